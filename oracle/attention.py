@@ -1,0 +1,312 @@
+"""Plain fp64 CPU oracle for exact softmax attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` use it.  It shares no code with the HIP library.
+
+What it computes is the textbook definition of softmax attention and of its
+gradient, written out per (batch, head) with no tiling, no fusion and no
+reordering beyond what the definition states.  A matrix product (numpy ``@``)
+is the only library primitive used.
+
+The backward follows the stage order of the Composable Kernel page
+"block_fmha_bwd_dq_dk_dv_pipeline_trload_kr_ktr_vr.hpp Source File"
+(``BlockFmhaBwdDQDKDVPipelineTrLoadKRKTRVR::run``):
+
+  STAGE 1  S = Q K^T, scaled by the softmax scale s
+  STAGE 2  P recomputed from S and the saved log-sum-exp (natural log; the page
+           multiplies it by log2(e) before taking exp2, which is the same value)
+  STAGE 4  dP = dO V^T
+  STAGE 3  dV = P^T dO
+  STAGE 5  dS = P * (dP - D), D the per-row sum of dO * O
+  STAGE 6  dK = dS^T Q, multiplied by s at the end ("Results Scale")
+  STAGE 7  dQ = dS K, multiplied by s ("QGrad Scale")
+
+Readings taken where the pages are silent (each is listed in the design notes):
+
+* Causal masking is aligned to the bottom-right corner: key j is visible to
+  query i iff ``j <= i + (Sk - Sq)``.  The pages only show that an
+  out-of-bound test exists (``mask.IsOutOfBound``), not its formula.
+* A query row that sees no key has LSE = -inf, O = 0 and contributes nothing
+  to any gradient.  The same page maps LSE = -inf to 0 (``get_validated_lse``)
+  so that such rows give P = exp(-inf) = 0.
+* D is computed from the O it is given (``D`` is only consumed on the pages).
+* GQA groups are contiguous: q-head h reads kv-head ``h // (Hq // Hkv)``, as in
+  the head mapping of ``CollectiveEpilogueBwdGQA::store`` on the
+  FlashAttention-3 page "flash-attention/hopper/epilogue_bwd.hpp"; dK and dV of
+  a kv-head are summed over its q-heads.
+
+Layouts (all numpy arrays, any float dtype, computed in float64):
+  dense : q, o, do [B, Sq, Hq, D];  k, v [B, Sk, Hkv, D];  lse, delta [B, Hq, Sq]
+  varlen: q, o, do [Tq, Hq, D];     k, v [Tk, Hkv, D];     lse, delta [Hq, Tq]
+          with ``cu_seqlens_q``/``cu_seqlens_k`` (length nseq + 1) giving the
+          row range of each sequence.
+"""
+
+import numpy as np
+
+__all__ = [
+    "visible",
+    "head_forward",
+    "head_backward",
+    "forward",
+    "backward",
+    "group_forward",
+    "group_backward",
+    "preprocess_delta",
+    "round_f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "postprocess_dq",
+]
+
+
+# --------------------------------------------------------------------------
+# one (batch, head) pair
+# --------------------------------------------------------------------------
+
+def visible(sq, sk, causal):
+    """Boolean [sq, sk]: True where query i may attend to key j.
+
+    Non-causal: every key.  Causal: ``j <= i + (sk - sq)`` (bottom-right
+    alignment; for sq == sk this is the usual lower triangle).
+    """
+    if not causal:
+        return np.ones((sq, sk), dtype=bool)
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return j <= i + (sk - sq)
+
+
+def head_forward(q, k, v, scale, causal):
+    """Softmax attention for one head.
+
+    q [sq, d], k [sk, d], v [sk, d] -> (o [sq, d], lse [sq]), float64.
+    ``lse_i = log(sum_j exp(s * q_i . k_j))`` over the visible keys,
+    ``o_i = sum_j softmax_ij v_j``.  Rows with no visible key give
+    lse = -inf and o = 0.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    sq, sk = q.shape[0], k.shape[0]
+    ok = visible(sq, sk, causal)
+    s = scale * (q @ k.T)
+    has_key = ok.any(axis=1)
+    # row maximum over visible keys (0 for empty rows, never used)
+    row_max = np.max(np.where(ok, s, -np.inf), axis=1, initial=-np.inf)
+    row_max = np.where(has_key, row_max, 0.0)
+    e = np.exp(np.where(ok, s - row_max[:, None], -np.inf))
+    total = e.sum(axis=1)
+    lse = np.full(sq, -np.inf)
+    lse[has_key] = row_max[has_key] + np.log(total[has_key])
+    p = np.zeros_like(s)
+    p[has_key] = e[has_key] / total[has_key, None]
+    o = p @ v
+    return o, lse
+
+
+def _probabilities(q, k, lse, scale, causal):
+    """P recomputed from the saved LSE (stages 1-2): exp(s q_i.k_j - lse_i)."""
+    sq, sk = q.shape[0], k.shape[0]
+    ok = visible(sq, sk, causal) & np.isfinite(lse)[:, None]
+    s = scale * (q @ k.T)
+    safe_lse = np.where(np.isfinite(lse), lse, 0.0)
+    return np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))
+
+
+def head_backward(q, k, v, o, do, lse, scale, causal, details=False):
+    """Gradient of attention for one head, given O and LSE as saved by a forward.
+
+    Returns (dq [sq, d], dk [sk, d], dv [sk, d]) in float64; with
+    ``details=True`` also a dict holding P, dP, dS and D.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    o = np.asarray(o, np.float64)
+    do = np.asarray(do, np.float64)
+    lse = np.asarray(lse, np.float64)
+    p = _probabilities(q, k, lse, scale, causal)          # stages 1-2
+    delta = np.sum(do * o, axis=1)                        # D = rowsum(dO * O)
+    dp = do @ v.T                                         # stage 4
+    dv = p.T @ do                                         # stage 3
+    ds = p * (dp - delta[:, None])                        # stage 5
+    dk = scale * (ds.T @ q)                               # stage 6 + final scale
+    dq = scale * (ds @ k)                                 # stage 7 + dQ scale
+    if details:
+        return dq, dk, dv, {"p": p, "dp": dp, "ds": ds, "delta": delta}
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# batched / grouped / varlen layouts
+# --------------------------------------------------------------------------
+
+def _ranges(nseq, sq, sk, cu_q, cu_k):
+    """Row ranges (q0, q1, k0, k1) of every sequence."""
+    if cu_q is None:
+        return [(b * sq, (b + 1) * sq, b * sk, (b + 1) * sk) for b in range(nseq)]
+    cu_q = np.asarray(cu_q, np.int64)
+    cu_k = np.asarray(cu_k, np.int64)
+    return [(int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])) for b in range(nseq)]
+
+
+def _flat(x, varlen):
+    """View [B, S, H, D] as [B*S, H, D]; varlen tensors already are [T, H, D]."""
+    x = np.asarray(x)
+    return x if varlen else x.reshape(-1, x.shape[2], x.shape[3])
+
+
+def _geometry(q, k, cu_q, cu_k):
+    varlen = cu_q is not None
+    if varlen:
+        nseq = len(cu_q) - 1
+        sq = sk = None
+        hq, hkv = q.shape[1], k.shape[1]
+    else:
+        nseq, sq, hq = q.shape[0], q.shape[1], q.shape[2]
+        sk, hkv = k.shape[1], k.shape[2]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return varlen, nseq, sq, sk, hq, hkv
+
+
+def _lse_view(lse, varlen, nseq, hq, sq):
+    """LSE/delta as [H, rows] over the flattened row index."""
+    lse = np.asarray(lse)
+    if varlen:
+        return lse
+    # [B, H, Sq] -> [H, B*Sq]
+    return np.transpose(lse, (1, 0, 2)).reshape(hq, nseq * sq)
+
+
+def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None):
+    """Forward for the q-heads of one kv-head group of one sequence.
+
+    Returns {q_head: (o [len_q, d], lse [len_q])}.
+    """
+    varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
+    g = hq // hkv
+    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)[seq]
+    qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
+    out = {}
+    for h in range(kv_head * g, (kv_head + 1) * g):
+        out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal)
+    return out
+
+
+def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
+                   cu_seqlens_q=None, cu_seqlens_k=None):
+    """Backward for one kv-head group of one sequence.
+
+    Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
+    are summed over the group's q-heads in ascending head order.
+    """
+    varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
+    g = hq // hkv
+    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)[seq]
+    qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
+    of, dof = _flat(o, varlen), _flat(do, varlen)
+    lf = _lse_view(lse, varlen, nseq, hq, sq)
+    d = qf.shape[2]
+    dk = np.zeros((k1 - k0, d))
+    dv = np.zeros((k1 - k0, d))
+    dq = {}
+    for h in range(kv_head * g, (kv_head + 1) * g):
+        dqh, dkh, dvh = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
+                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal)
+        dq[h] = dqh
+        dk += dkh
+        dv += dvh
+    return dq, dk, dv
+
+
+def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None):
+    """Full forward.  Returns (o, lse) in the layouts given in the module doc."""
+    varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
+    qf = _flat(q, varlen)
+    o = np.zeros(qf.shape, np.float64)
+    lse = np.zeros((hq, qf.shape[0]), np.float64)
+    for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)):
+        for g in range(hkv):
+            for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g,
+                                             cu_seqlens_q, cu_seqlens_k).items():
+                o[q0:q1, h] = oh
+                lse[h, q0:q1] = lh
+    if varlen:
+        return o, lse
+    return o.reshape(q.shape), np.transpose(lse.reshape(hq, nseq, sq), (1, 0, 2)).copy()
+
+
+def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None):
+    """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64)."""
+    varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
+    qf, kf = _flat(q, varlen), _flat(k, varlen)
+    dq = np.zeros(qf.shape, np.float64)
+    dk = np.zeros(kf.shape, np.float64)
+    dv = np.zeros(kf.shape, np.float64)
+    for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)):
+        for g in range(hkv):
+            dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g,
+                                           cu_seqlens_q, cu_seqlens_k)
+            for h, x in dqg.items():
+                dq[q0:q1, h] = x
+            dk[k0:k1, g] = dkg
+            dv[k0:k1, g] = dvg
+    if varlen:
+        return dq, dk, dv
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(k.shape)
+
+
+def preprocess_delta(o, do, cu_seqlens_q=None):
+    """D = rowsum(dO * O) per (head, row), in the LSE layout, float64."""
+    o = np.asarray(o, np.float64)
+    do = np.asarray(do, np.float64)
+    d = np.sum(o * do, axis=-1)              # [B, Sq, H] or [T, H]
+    if cu_seqlens_q is not None:
+        return d.T.copy()                    # [H, T]
+    return np.transpose(d, (0, 2, 1)).copy()  # [B, H, Sq]
+
+
+# --------------------------------------------------------------------------
+# dQ postprocess: fp32 accumulator -> output dtype, times the softmax scale
+# --------------------------------------------------------------------------
+
+def round_f32_to_bf16_bits(x):
+    """bfloat16 bit patterns (uint16) of float32 values, round to nearest even.
+
+    Written from the definition: bfloat16 keeps the top 16 bits of the binary32
+    pattern; the discarded low 16 bits round the kept part to the nearest
+    representable value, ties going to the even one.  NaN stays a (quiet) NaN.
+    """
+    u = np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    kept = u >> 16
+    half = 0x8000
+    round_up = (low > half) | ((low == half) & ((kept & 1) == 1))
+    out = (kept + round_up.astype(np.uint64)) & 0xFFFF
+    is_nan = ((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)
+    out = np.where(is_nan, (kept | 0x0040) & 0xFFFF, out)
+    return out.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """float32 values of bfloat16 bit patterns (exact)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def postprocess_dq(dq_accum, scale, out_dtype):
+    """dQ = out_dtype(scale * dQaccum), the product taken in float32.
+
+    Follows ``FlashAttentionBackwardPostprocess`` on the page
+    "flash_bwd_postprocess.py": the fp32 accumulator is multiplied by the
+    scale and converted to the output type.  ``out_dtype`` is "bf16" (returns
+    uint16 bit patterns) or "f32" (returns float32).
+    """
+    prod = np.asarray(dq_accum, np.float32) * np.float32(scale)
+    if out_dtype == "bf16":
+        return round_f32_to_bf16_bits(prod)
+    if out_dtype == "f32":
+        return prod.astype(np.float32)
+    raise ValueError(out_dtype)

@@ -1,0 +1,468 @@
+"""Pins of the fp64 CPU oracle to things other than itself (CPU only).
+
+Each test ties an oracle function to the mathematics: central finite
+differences of the forward loss, brute-force scalar loops, closed forms,
+invariants of the softmax gradient, an independent library routine (torch's
+attention and autograd in float64), and hand-derived worked examples stored
+under tests/golden/.  A planted-mistake test at the end checks that the pins
+catch the plausible slips (dropped term, wrong sign, transposed operand).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.max(np.abs(b))
+    return float(np.max(np.abs(a - b)) / (den if den > 0 else 1.0))
+
+
+def rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# forward: brute force, library routine, worked examples
+# --------------------------------------------------------------------------
+
+def brute_head_forward(q, k, v, scale, causal):
+    """Scalar loops with math.exp: the definition, no vectorisation."""
+    sq, sk, d = len(q), len(k), len(q[0])
+    o, lse = [], []
+    for i in range(sq):
+        vis = [j for j in range(sk) if (not causal) or j <= i + (sk - sq)]
+        if not vis:
+            o.append([0.0] * d)
+            lse.append(-math.inf)
+            continue
+        s = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in vis}
+        m = max(s.values())
+        z = sum(math.exp(s[j] - m) for j in vis)
+        lse.append(m + math.log(z))
+        o.append([sum(math.exp(s[j] - lse[-1]) * v[j][t] for j in vis) for t in range(d)])
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(5, 5, False), (5, 5, True), (4, 6, True), (6, 4, True), (3, 7, False)])
+def test_forward_matches_scalar_loops(sq, sk, causal):
+    rng = np.random.default_rng(10 + sq * 7 + sk)
+    q, k, v = rand(rng, sq, 3), rand(rng, sk, 3), rand(rng, sk, 3)
+    o, lse = A.head_forward(q, k, v, 0.7, causal)
+    bo, blse = brute_head_forward(q.tolist(), k.tolist(), v.tolist(), 0.7, causal)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(blse))
+    fin = np.isfinite(blse)
+    assert np.max(np.abs(lse[fin] - blse[fin])) <= 1e-12
+    assert np.max(np.abs(o - bo)) <= 1e-12
+
+
+def _torch_mask(sq, sk, causal):
+    import torch
+    i = torch.arange(sq)[:, None]
+    j = torch.arange(sk)[None, :]
+    return (j <= i + (sk - sq)) if causal else torch.ones(sq, sk, dtype=torch.bool)
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(33, 33, False), (33, 33, True), (20, 47, True), (47, 20, True)])
+def test_forward_matches_torch_sdpa_float64(sq, sk, causal):
+    """torch.nn.functional.scaled_dot_product_attention (CPU, float64) is an
+    independent implementation of the same definition."""
+    import torch
+    rng = np.random.default_rng(3)
+    q, k, v = rand(rng, 2, 3, sq, 8), rand(rng, 2, 3, sk, 8), rand(rng, 2, 3, sk, 8)
+    mask = _torch_mask(sq, sk, causal)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.4).numpy()
+    rows = mask.any(dim=1).numpy()
+    for b in range(2):
+        for h in range(3):
+            o, _ = A.head_forward(q[b, h], k[b, h], v[b, h], 0.4, causal)
+            assert np.max(np.abs(o[rows] - ref[b, h][rows])) <= 1e-12
+            assert np.all(o[~rows] == 0.0)
+
+
+def test_golden_worked_examples():
+    data = json.load(open(GOLDEN))
+    for ex in data["examples"]:
+        q, k, v, do = (np.array(ex[n], np.float64) for n in ("q", "k", "v", "do"))
+        o, lse = A.head_forward(q, k, v, ex["scale"], ex["causal"])
+        want_lse = np.array([-np.inf if x is None else x for x in ex["lse"]])
+        assert np.array_equal(np.isfinite(lse), np.isfinite(want_lse)), ex["name"]
+        fin = np.isfinite(want_lse)
+        assert np.max(np.abs(lse[fin] - want_lse[fin])) <= 1e-14, ex["name"]
+        assert np.max(np.abs(o - np.array(ex["o"]))) <= 1e-14, ex["name"]
+        dq, dk, dv = A.head_backward(q, k, v, o, do, lse, ex["scale"], ex["causal"])
+        for got, key in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            assert np.max(np.abs(got - np.array(ex[key]))) <= 1e-14, (ex["name"], key)
+
+
+# --------------------------------------------------------------------------
+# backward: central finite differences of L = sum(dO * O)
+# --------------------------------------------------------------------------
+
+def _fd_case(q, k, v, do, scale, causal, cu_q=None, cu_k=None):
+    """Analytic gradients vs central differences, h = 1e-5, every entry."""
+    o, lse = oracle.forward(q, k, v, scale, causal, cu_q, cu_k)
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, scale, causal, cu_q, cu_k)
+
+    def loss(qq, kk, vv):
+        oo, _ = oracle.forward(qq, kk, vv, scale, causal, cu_q, cu_k)
+        return float(np.sum(do * oo))
+
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            pos = "qkv".index(name)
+            args_p[pos], args_m[pos] = xp, xm
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = rel_err(g, fd)
+        assert err <= 1e-6, (name, err)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("sq,sk,causal,scale", [
+    (5, 5, False, 1 / math.sqrt(3)),
+    (5, 5, True, 1 / math.sqrt(3)),
+    (4, 6, True, 1 / math.sqrt(3)),
+    (6, 4, True, 1 / math.sqrt(3)),     # rows 0 and 1 see no key
+    (5, 5, True, 0.3),
+])
+def test_backward_finite_differences_dense(sq, sk, causal, scale):
+    rng = np.random.default_rng(100 + sq * 10 + sk)
+    q, k, v = rand(rng, 1, sq, 1, 3), rand(rng, 1, sk, 1, 3), rand(rng, 1, sk, 1, 3)
+    do = rand(rng, 1, sq, 1, 3)
+    _fd_case(q, k, v, do, scale, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences_gqa(causal):
+    rng = np.random.default_rng(7)
+    q, k, v = rand(rng, 1, 5, 4, 3), rand(rng, 1, 5, 2, 3), rand(rng, 1, 5, 2, 3)
+    do = rand(rng, 1, 5, 4, 3)
+    _fd_case(q, k, v, do, 0.5, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences_varlen(causal):
+    rng = np.random.default_rng(8)
+    lens = [1, 4, 7]
+    cu = np.array([0, 1, 5, 12], np.int32)
+    q, k, v = rand(rng, 12, 2, 3), rand(rng, 12, 1, 3), rand(rng, 12, 1, 3)
+    do = rand(rng, 12, 2, 3)
+    assert sum(lens) == 12
+    _fd_case(q, k, v, do, 0.6, causal, cu, cu)
+
+
+# --------------------------------------------------------------------------
+# backward: independent library autograd (torch, float64)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sq,sk,causal", [(40, 40, True), (40, 40, False), (25, 61, True)])
+def test_backward_matches_torch_autograd_float64(sq, sk, causal):
+    import torch
+    rng = np.random.default_rng(11)
+    q, k, v, do = rand(rng, sq, 16), rand(rng, sk, 16), rand(rng, sk, 16), rand(rng, sq, 16)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = _torch_mask(sq, sk, causal)
+    s = 0.25 * tq @ tk.T
+    s = s.masked_fill(~mask, float("-inf"))
+    out = torch.softmax(s, dim=-1) @ tv
+    out.backward(torch.from_numpy(do))
+    o, lse = A.head_forward(q, k, v, 0.25, causal)
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.25, causal)
+    assert rel_err(dq, tq.grad.numpy()) <= 1e-12
+    assert rel_err(dk, tk.grad.numpy()) <= 1e-12
+    assert rel_err(dv, tv.grad.numpy()) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# invariants and closed forms
+# --------------------------------------------------------------------------
+
+INVARIANT_SHAPES = [
+    # (label, sq, sk, d, causal, scale, do_scale) at the workloads' head dims and lengths
+    ("c1_like", 128, 128, 64, False, 1 / 8, 1.0),
+    ("c2_like", 1024, 1024, 64, True, 1 / 8, 1.0),
+    ("c3_like", 4096, 4096, 128, True, 1 / math.sqrt(128), 0.1),
+    ("c3nc_like", 4096, 4096, 128, False, 1 / math.sqrt(128), 0.1),
+    ("c4_like", 779, 779, 128, True, 1 / math.sqrt(128), 1.0),
+    ("c5_like", 2048, 2048, 128, True, 1 / math.sqrt(128), 1.0),
+]
+
+
+@pytest.mark.parametrize("label,sq,sk,d,causal,scale,do_scale", INVARIANT_SHAPES)
+def test_softmax_gradient_invariants(label, sq, sk, d, causal, scale, do_scale):
+    """With O and LSE from the oracle's own forward:
+    sum_j dS_ij = 0;  D_i = sum_j P_ij dP_ij;  sum_j dK_j = 0;
+    sum_j dV_j = sum of dO over rows that see a key."""
+    rng = np.random.default_rng(sq + d)
+    q, k, v = rand(rng, sq, d), rand(rng, sk, d), rand(rng, sk, d)
+    do = do_scale * rand(rng, sq, d)
+    o, lse = A.head_forward(q, k, v, scale, causal)
+    dq, dk, dv, x = A.head_backward(q, k, v, o, do, lse, scale, causal, details=True)
+    assert np.max(np.abs(x["ds"].sum(axis=1))) <= 1e-10, label
+    assert rel_err(x["delta"], (x["p"] * x["dp"]).sum(axis=1)) <= 1e-12, label
+    assert np.max(np.abs(dk.sum(axis=0))) <= 1e-10 * np.sum(np.abs(dk)), label
+    rows = np.isfinite(lse)
+    assert rel_err(dv.sum(axis=0), do[rows].sum(axis=0)) <= 1e-12, label
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(9, 9, False), (9, 9, True), (6, 11, True), (11, 6, True)])
+def test_closed_form_constant_keys(sq, sk, causal):
+    """All keys equal: P is uniform over the visible keys, so LSE = s q.k + ln n,
+    O = mean of the visible values, dV_j = sum over rows seeing j of dO_i / n_i,
+    and dQ = 0."""
+    rng = np.random.default_rng(5)
+    d = 4
+    kvec = rand(rng, d)
+    q, v, do = rand(rng, sq, d), rand(rng, sk, d), rand(rng, sq, d)
+    k = np.tile(kvec, (sk, 1))
+    o, lse = A.head_forward(q, k, v, 0.9, causal)
+    vis = A.visible(sq, sk, causal)
+    n = vis.sum(axis=1)
+    for i in range(sq):
+        if n[i] == 0:
+            assert lse[i] == -np.inf and np.all(o[i] == 0)
+            continue
+        assert abs(lse[i] - (0.9 * q[i] @ kvec + math.log(n[i]))) <= 1e-12
+        assert np.max(np.abs(o[i] - v[vis[i]].mean(axis=0))) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.9, causal)
+    want_dv = np.zeros((sk, d))
+    for i in range(sq):
+        for j in range(sk):
+            if vis[i, j]:
+                want_dv[j] += do[i] / n[i]
+    assert np.max(np.abs(dv - want_dv)) <= 1e-12
+    assert np.max(np.abs(dq)) <= 1e-12
+    if not causal and sq == sk:
+        # column mean of dO broadcast to every key
+        assert np.max(np.abs(dv - do.mean(axis=0)[None, :])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_closed_form_constant_values(causal):
+    """All values equal: O = v and dP is constant along each row, so dS = 0 and
+    dQ = dK = 0."""
+    rng = np.random.default_rng(6)
+    d = 5
+    vvec = rand(rng, d)
+    q, k, do = rand(rng, 8, d), rand(rng, 8, d), rand(rng, 8, d)
+    v = np.tile(vvec, (8, 1))
+    o, lse = A.head_forward(q, k, v, 0.5, causal)
+    assert np.max(np.abs(o - vvec)) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.5, causal)
+    assert np.max(np.abs(dq)) <= 1e-12
+    assert np.max(np.abs(dk)) <= 1e-12
+
+
+def test_single_key_special_case():
+    """Sk = 1: every row puts weight 1 on the only key, so dV_0 = sum_i dO_i and
+    dQ = dK = 0; LSE_i = s q_i . k_0."""
+    rng = np.random.default_rng(9)
+    q, k, v, do = rand(rng, 7, 3), rand(rng, 1, 3), rand(rng, 1, 3), rand(rng, 7, 3)
+    o, lse = A.head_forward(q, k, v, 0.8, False)
+    assert np.max(np.abs(lse - 0.8 * q @ k[0])) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.8, False)
+    assert np.max(np.abs(dv[0] - do.sum(axis=0))) <= 1e-12
+    assert np.max(np.abs(dq)) <= 1e-12 and np.max(np.abs(dk)) <= 1e-12
+
+
+def test_causal_first_row_and_last_key():
+    """Causal, Sq = Sk: query 0 sees only key 0 (so dQ_0 = 0) and the last key
+    is seen only by the last query (dV_last = P_last,last dO_last)."""
+    rng = np.random.default_rng(12)
+    q, k, v, do = rand(rng, 10, 4), rand(rng, 10, 4), rand(rng, 10, 4), rand(rng, 10, 4)
+    o, lse = A.head_forward(q, k, v, 0.5, True)
+    dq, dk, dv, x = A.head_backward(q, k, v, o, do, lse, 0.5, True, details=True)
+    assert np.max(np.abs(dq[0])) <= 1e-12
+    assert np.max(np.abs(dv[-1] - x["p"][-1, -1] * do[-1])) <= 1e-12
+
+
+def test_fully_masked_rows():
+    """Causal with Sq > Sk: rows i < Sq - Sk see no key; they get LSE = -inf,
+    O = 0 and dQ = 0, and do not touch dK or dV."""
+    rng = np.random.default_rng(13)
+    q, k, v, do = rand(rng, 9, 4), rand(rng, 5, 4), rand(rng, 5, 4), rand(rng, 9, 4)
+    o, lse = A.head_forward(q, k, v, 0.5, True)
+    assert np.all(lse[:4] == -np.inf) and np.all(np.isfinite(lse[4:]))
+    assert np.all(o[:4] == 0)
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.5, True)
+    assert np.all(dq[:4] == 0)
+    do2 = do.copy()
+    do2[:4] = 1e3 * rand(rng, 4, 4)        # changing dO on empty rows changes nothing
+    dq2, dk2, dv2 = A.head_backward(q, k, v, o, do2, lse, 0.5, True)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
+# --------------------------------------------------------------------------
+# layouts: GQA and varlen reduce to the plain per-head case
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_heads(causal):
+    rng = np.random.default_rng(14)
+    b, s, hq, hkv, d = 2, 23, 6, 2, 8
+    q, k, v, do = rand(rng, b, s, hq, d), rand(rng, b, s, hkv, d), rand(rng, b, s, hkv, d), rand(rng, b, s, hq, d)
+    g = hq // hkv
+    kr, vr = np.repeat(k, g, axis=2), np.repeat(v, g, axis=2)
+    o, lse = oracle.forward(q, k, v, 0.35, causal)
+    o_r, lse_r = oracle.forward(q, kr, vr, 0.35, causal)
+    assert np.max(np.abs(o - o_r)) <= 1e-12 and np.max(np.abs(lse - lse_r)) <= 1e-12
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, 0.35, causal)
+    dq_r, dk_r, dv_r = oracle.backward(q, kr, vr, o, do, lse, 0.35, causal)
+    assert np.max(np.abs(dq - dq_r)) <= 1e-12
+    assert np.max(np.abs(dk - dk_r.reshape(b, s, hkv, g, d).sum(axis=3))) <= 1e-12
+    assert np.max(np.abs(dv - dv_r.reshape(b, s, hkv, g, d).sum(axis=3))) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_per_sequence_dense(causal):
+    rng = np.random.default_rng(15)
+    lens = [1, 17, 40, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t, h, d = cu[-1], 3, 8
+    q, k, v, do = rand(rng, t, h, d), rand(rng, t, h, d), rand(rng, t, h, d), rand(rng, t, h, d)
+    o, lse = oracle.forward(q, k, v, 0.3, causal, cu, cu)
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, 0.3, causal, cu, cu)
+    for bi, L in enumerate(lens):
+        sl = slice(cu[bi], cu[bi + 1])
+        od, lsed = oracle.forward(q[None, sl], k[None, sl], v[None, sl], 0.3, causal)
+        assert np.max(np.abs(o[sl] - od[0])) <= 1e-12
+        assert np.max(np.abs(lse[:, sl] - lsed[0])) <= 1e-12
+        dqd, dkd, dvd = oracle.backward(q[None, sl], k[None, sl], v[None, sl], od, do[None, sl], lsed, 0.3, causal)
+        for a, bb in ((dq, dqd), (dk, dkd), (dv, dvd)):
+            assert np.max(np.abs(a[sl] - bb[0])) <= 1e-12
+
+
+def test_preprocess_delta_layouts_and_definition():
+    rng = np.random.default_rng(16)
+    o, do = rand(rng, 2, 5, 3, 4), rand(rng, 2, 5, 3, 4)
+    dl = oracle.preprocess_delta(o, do)
+    assert dl.shape == (2, 3, 5)
+    for b in range(2):
+        for i in range(5):
+            for h in range(3):
+                assert abs(dl[b, h, i] - sum(o[b, i, h, t] * do[b, i, h, t] for t in range(4))) <= 1e-13
+    ov, dov = o.reshape(10, 3, 4), do.reshape(10, 3, 4)
+    dlv = oracle.preprocess_delta(ov, dov, cu_seqlens_q=np.array([0, 5, 10]))
+    assert dlv.shape == (3, 10)
+    assert np.max(np.abs(dlv - np.transpose(dl, (1, 0, 2)).reshape(3, 10))) <= 1e-15
+
+
+# --------------------------------------------------------------------------
+# dQ postprocess: bfloat16 rounding
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_golden_bit_patterns():
+    data = json.load(open(GOLDEN))["bf16_rounding"]["cases"]
+    src = np.array([int(a, 16) for a, _, _ in data], np.uint32).view(np.float32)
+    want = np.array([int(b, 16) for _, b, _ in data], np.uint16)
+    got = A.round_f32_to_bf16_bits(src)
+    for (a, b, why), g in zip(data, got):
+        assert g == int(b, 16), (a, b, hex(int(g)), why)
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal(1 << 18) * np.exp(rng.uniform(-30, 30, 1 << 18))).astype(np.float32)
+    ties = ((rng.integers(0, 1 << 16, 4096).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties[np.isfinite(ties)]])
+    got = A.round_f32_to_bf16_bits(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    assert np.array_equal(A.bf16_bits_to_f32(got), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_postprocess_dq_product_in_float32():
+    import torch
+    rng = np.random.default_rng(18)
+    acc = rng.standard_normal((3, 7, 64)).astype(np.float32) * 50
+    s = 1 / math.sqrt(128)
+    got = oracle.postprocess_dq(acc, s, "bf16")
+    want = (torch.from_numpy(acc) * torch.tensor(s, dtype=torch.float32)).to(torch.bfloat16)
+    assert np.array_equal(got, want.view(torch.int16).numpy().view(np.uint16))
+    got32 = oracle.postprocess_dq(acc, s, "f32")
+    assert np.array_equal(got32, acc * np.float32(s))
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: the pins above must catch each of these
+# --------------------------------------------------------------------------
+
+def _mutants():
+    def drop_delta(q, k, v, o, do, lse, scale, causal):
+        p = A._probabilities(q, k, lse, scale, causal)
+        ds = p * (do @ v.T)
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+    def wrong_sign(q, k, v, o, do, lse, scale, causal):
+        p = A._probabilities(q, k, lse, scale, causal)
+        ds = p * ((do @ v.T) + np.sum(do * o, 1)[:, None])
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+    def no_dk_scale(q, k, v, o, do, lse, scale, causal):
+        dq, dk, dv = A.head_backward(q, k, v, o, do, lse, scale, causal)
+        return dq, dk / scale, dv
+
+    def transposed_p(q, k, v, o, do, lse, scale, causal):
+        dq, dk, dv = A.head_backward(q, k, v, o, do, lse, scale, causal)
+        p = A._probabilities(q, k, lse, scale, causal)
+        return dq, dk, p @ do
+
+    def causal_off_by_one(q, k, v, o, do, lse, scale, causal):
+        sq, sk = len(q), len(k)
+        ok = A.visible(sq, sk, causal)
+        ok = ok & ~np.eye(sq, sk, dtype=bool) if causal else ok
+        s = scale * q @ k.T
+        p = np.exp(np.where(ok, s - lse[:, None], -np.inf))
+        ds = p * ((do @ v.T) - np.sum(do * o, 1)[:, None])
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+    return [drop_delta, wrong_sign, no_dk_scale, transposed_p, causal_off_by_one]
+
+
+@pytest.mark.parametrize("mutant", _mutants(), ids=lambda f: f.__name__)
+def test_planted_mistakes_are_caught_by_finite_differences(mutant):
+    rng = np.random.default_rng(19)
+    q, k, v, do = rand(rng, 5, 3), rand(rng, 5, 3), rand(rng, 5, 3), rand(rng, 5, 3)
+    o, lse = A.head_forward(q, k, v, 0.6, True)
+    dq, dk, dv = mutant(q, k, v, o, do, lse, 0.6, True)
+    good = A.head_backward(q, k, v, o, do, lse, 0.6, True)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * A.head_forward(qq, kk, vv, 0.6, True)[0]))
+
+    h = 1e-5
+    worst = 0.0
+    for pos, g in enumerate((dq, dk, dv)):
+        base = [q, k, v]
+        fd = np.zeros_like(base[pos])
+        for idx in np.ndindex(fd.shape):
+            xp, xm = base[pos].copy(), base[pos].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(base), list(base)
+            ap[pos], am[pos] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert rel_err(good[pos], fd) <= 1e-6
+        worst = max(worst, rel_err(g, fd))
+    assert worst > 1e-3, mutant.__name__
