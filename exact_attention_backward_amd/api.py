@@ -1,0 +1,155 @@
+"""Python binding of the C ABI: the same entry points, taking torch tensors.
+
+PyTorch only supplies device memory and the current HIP stream; every step of
+the computation runs in the library's kernels.  Tensors must be contiguous
+and on the GPU; layouts are those of include/attn_bwd.h:
+
+  dense : q, o, do, dq [B, Sq, Hq, D];  k, v, dk, dv [B, Sk, Hkv, D];  lse, delta [B, Hq, Sq]
+  varlen: q, o, do, dq [Tq, Hq, D];     k, v, dk, dv [Tk, Hkv, D];     lse, delta [Hq, Tq]
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "make_shape",
+    "attn_bwd_workspace_bytes",
+    "attn_fwd",
+    "attn_bwd_preprocess",
+    "attn_bwd",
+    "attn_bwd_dq_postprocess",
+    "forward",
+    "backward",
+    "BackwardPlan",
+]
+
+_DTYPES = {torch.bfloat16: L.ATTN_DTYPE_BF16, torch.float32: L.ATTN_DTYPE_F32}
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
+               max_seqlen_q=None, max_seqlen_k=None):
+    """attn_shape_t for the given tensors (the dtype is q's)."""
+    s = L.AttnShape()
+    if q.dtype not in _DTYPES:
+        s.dtype = -1
+    else:
+        s.dtype = _DTYPES[q.dtype]
+    if cu_seqlens_q is None:
+        s.batch, s.seqlen_q, s.num_heads_q, s.head_dim = q.shape
+        s.seqlen_k, s.num_heads_kv = k.shape[1], k.shape[2]
+        s.total_q, s.total_k = s.batch * s.seqlen_q, s.batch * s.seqlen_k
+    else:
+        s.total_q, s.num_heads_q, s.head_dim = q.shape
+        s.total_k, s.num_heads_kv = k.shape[0], k.shape[1]
+        s.batch = cu_seqlens_q.numel() - 1
+        s.seqlen_q, s.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+        s.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        s.cu_seqlens_k = cu_seqlens_k.data_ptr()
+    s.softmax_scale = float(scale)
+    s.causal = int(bool(causal))
+    s.deterministic = int(bool(deterministic))
+    return s
+
+
+def attn_bwd_workspace_bytes(shape):
+    return int(L.lib().attn_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_fwd(shape, q, k, v, o, lse):
+    return L.check("attn_fwd", L.lib().attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                                   _ptr(lse), _stream()))
+
+
+def attn_bwd_preprocess(shape, o, do, delta, workspace):
+    return L.check("attn_bwd_preprocess", L.lib().attn_bwd_preprocess(
+        ctypes.byref(shape), _ptr(o), _ptr(do), _ptr(delta), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def attn_bwd(shape, q, k, v, do, lse, delta, workspace, dk, dv):
+    return L.check("attn_bwd", L.lib().attn_bwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
+        workspace.numel(), _ptr(dk), _ptr(dv), _stream()))
+
+
+def attn_bwd_dq_postprocess(shape, workspace, dq, scale):
+    return L.check("attn_bwd_dq_postprocess", L.lib().attn_bwd_dq_postprocess(
+        ctypes.byref(shape), _ptr(workspace), workspace.numel(), _ptr(dq), ctypes.c_float(scale), _stream()))
+
+
+def _lse_shape(shape, varlen):
+    if varlen:
+        return (shape.num_heads_q, shape.total_q)
+    return (shape.batch, shape.num_heads_q, shape.seqlen_q)
+
+
+def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
+    """Plain forward: returns (o, lse)."""
+    shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    o = torch.empty_like(q)
+    lse = torch.empty(_lse_shape(shape, cu_seqlens_q is not None), dtype=torch.float32, device=q.device)
+    attn_fwd(shape, q, k, v, o, lse)
+    return o, lse
+
+
+class BackwardPlan:
+    """Shape, workspace and D buffer of one backward problem, for repeated calls.
+
+    ``run`` enqueues the three backward kernels (preprocess, main, dQ
+    postprocess) on the current stream and writes dq, dk, dv.
+    """
+
+    def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
+                 max_seqlen_q=None, max_seqlen_k=None):
+        self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
+                                max_seqlen_q, max_seqlen_k)
+        self._keep = (cu_seqlens_q, cu_seqlens_k)
+        self.scale = float(scale)
+        nbytes = attn_bwd_workspace_bytes(self.shape)
+        if nbytes == 0:
+            raise L.AttnError("attn_bwd_workspace_bytes", L.ATTN_ERR_BAD_SHAPE, "invalid shape")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        self.delta = torch.empty(_lse_shape(self.shape, cu_seqlens_q is not None), dtype=torch.float32,
+                                 device=q.device)
+
+    def preprocess(self, o, do):
+        attn_bwd_preprocess(self.shape, o, do, self.delta, self.workspace)
+
+    def main(self, q, k, v, do, lse, dk, dv):
+        attn_bwd(self.shape, q, k, v, do, lse, self.delta, self.workspace, dk, dv)
+
+    def postprocess(self, dq):
+        attn_bwd_dq_postprocess(self.shape, self.workspace, dq, self.scale)
+
+    def run(self, q, k, v, o, do, lse, dq, dk, dv):
+        self.preprocess(o, do)
+        self.main(q, k, v, do, lse, dk, dv)
+        self.postprocess(dq)
+
+    def error_flag(self):
+        """Non-zero if an ordered (deterministic) wait gave up; reads the
+        workspace's status word (synchronises the stream)."""
+        return int(self.workspace[-256:].view(torch.int32)[0].item())
+
+
+def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None):
+    """Full backward: returns (dq, dk, dv)."""
+    plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    plan.run(q, k, v, o, do, lse, dq, dk, dv)
+    return dq, dk, dv

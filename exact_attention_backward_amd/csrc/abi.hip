@@ -1,0 +1,170 @@
+// C ABI of the library: argument validation, workspace layout and dispatch.
+// Every entry point validates before any HIP call, so the error paths run
+// (and are tested) on machines without a GPU.
+#include <stdint.h>
+#include <stddef.h>
+
+#include "launch.h"
+
+using namespace attn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kErrBytes = 256;   // status words of the deterministic mode
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_shape(const attn_shape_t* s) {
+    if (s == nullptr) return ATTN_ERR_NULL_ARG;
+    if (s->dtype != ATTN_DTYPE_F32 && s->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (s->batch <= 0 || s->num_heads_q <= 0 || s->num_heads_kv <= 0 || s->seqlen_q <= 0 || s->seqlen_k <= 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_BAD_SHAPE;
+    if ((s->cu_seqlens_q == nullptr) != (s->cu_seqlens_k == nullptr)) return ATTN_ERR_BAD_SHAPE;
+    if (s->cu_seqlens_q != nullptr) {
+        if (s->total_q <= 0 || s->total_k <= 0) return ATTN_ERR_BAD_SHAPE;
+        if ((reinterpret_cast<uintptr_t>(s->cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(s->cu_seqlens_k) & 3u))
+            return ATTN_ERR_MISALIGNED;
+    }
+    if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
+    if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
+    if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
+    // element counts must stay addressable with 64-bit offsets and 32-bit row counts
+    const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
+    const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
+    if (rows_q > 0x7fffffffLL || rows_k > 0x7fffffffLL) return ATTN_ERR_BAD_SHAPE;
+    return ATTN_OK;
+}
+
+bool varlen(const attn_shape_t* s) { return s->cu_seqlens_q != nullptr; }
+long long rows_q(const attn_shape_t* s) { return varlen(s) ? s->total_q : (long long)s->batch * s->seqlen_q; }
+
+size_t elem_bytes(const attn_shape_t* s) { return s->dtype == ATTN_DTYPE_BF16 ? 2 : 4; }
+
+// workspace = [dQ accumulator fp32][ordering counters int32][status words]
+size_t accum_bytes(const attn_shape_t* s) {
+    return align_up((size_t)rows_q(s) * s->num_heads_q * s->head_dim * sizeof(float));
+}
+int nblk_m(const attn_shape_t* s) {
+    const int bm = bwd_block_m(s->dtype, s->head_dim);
+    return (s->seqlen_q + bm - 1) / bm;
+}
+size_t sem_bytes(const attn_shape_t* s) {
+    return align_up((size_t)s->batch * s->num_heads_q * nblk_m(s) * sizeof(int32_t));
+}
+size_t workspace_bytes(const attn_shape_t* s) { return accum_bytes(s) + sem_bytes(s) + kErrBytes; }
+
+int check_launch() {
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL_ARG: return "null argument";
+        case ATTN_ERR_BAD_SHAPE: return "bad shape";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+        case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t attn_bwd_workspace_bytes(const attn_shape_t* shape) {
+    if (validate_shape(shape) != ATTN_OK) return 0;
+    return workspace_bytes(shape);
+}
+
+int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v, void* o, float* lse,
+             void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_MISALIGNED;
+    FwdArgs a{q, k, v, o, lse, s->cu_seqlens_q, s->cu_seqlens_k, s->batch, s->num_heads_q, s->num_heads_kv,
+              s->seqlen_q, s->seqlen_k, s->total_q, s->total_k, s->softmax_scale};
+    hipGetLastError();
+    launch_fwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
+                        size_t workspace_size, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!o || !dout || !delta || !workspace) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || !aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+    const size_t need = workspace_bytes(s);
+    if (workspace_size < need) return ATTN_ERR_BAD_SHAPE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipGetLastError();
+    launch_fill_zero(workspace, need, hs);
+    PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s)};
+    launch_preprocess(a, s->dtype, s->head_dim, hs);
+    return check_launch();
+}
+
+int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout, const float* lse,
+             const float* delta, void* workspace, size_t workspace_size, void* dk, void* dv, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dk || !dv) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+        !aligned16(delta) || !aligned16(workspace) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_MISALIGNED;
+    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+    char* ws = reinterpret_cast<char*>(workspace);
+    BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq_acc = reinterpret_cast<float*>(ws);
+    a.sem = reinterpret_cast<int*>(ws + accum_bytes(s));
+    a.err = reinterpret_cast<int*>(ws + accum_bytes(s) + sem_bytes(s));
+    a.dk = dk;
+    a.dv = dv;
+    a.cu_q = s->cu_seqlens_q;
+    a.cu_k = s->cu_seqlens_k;
+    a.batch = s->batch;
+    a.hq = s->num_heads_q;
+    a.hkv = s->num_heads_kv;
+    a.seqlen_q = s->seqlen_q;
+    a.seqlen_k = s->seqlen_k;
+    a.total_q = s->total_q;
+    a.total_k = s->total_k;
+    a.nblk_n = (s->seqlen_k + kBwdBlockN - 1) / kBwdBlockN;
+    a.nblk_m = nblk_m(s);
+    a.scale = s->softmax_scale;
+    a.deterministic = s->deterministic;
+    hipGetLastError();
+    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t workspace_size, void* dq,
+                            float scale, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!workspace || !dq) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(workspace) || !aligned16(dq)) return ATTN_ERR_MISALIGNED;
+    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+    PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
+               s->seqlen_q, s->total_q, varlen(s), scale};
+    hipGetLastError();
+    launch_postprocess(a, s->dtype, s->head_dim, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+}  // extern "C"

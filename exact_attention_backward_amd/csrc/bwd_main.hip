@@ -1,0 +1,444 @@
+// Main backward kernel of exact attention for gfx950.
+//
+// One workgroup (4 waves) owns a tile of 128 keys of one (sequence, kv-head)
+// and loops over the query tiles that can see it, for every q-head of the
+// kv-head's GQA group.  This is the key-stationary schedule of the
+// Composable Kernel page "block_fmha_bwd_dq_dk_dv_pipeline_trload_kr_ktr_vr.hpp
+// Source File" (one K/V tile per block, loop over Q tiles, five GEMMs):
+//
+//   stage 1  S  = Q K^T                 (MFMA, K from registers)
+//   stage 2  P  = exp2(S s log2e - LSE log2e), masked on edge tiles only
+//   stage 4  dP = dO V^T                (MFMA, V from registers)
+//   stage 3  dV += P^T dO               (MFMA, P^T straight from the S registers)
+//   stage 5  dS = P (dP - D)
+//   stage 6  dK += dS^T Q               (MFMA, dS^T straight from the registers)
+//   stage 7  dQ_tile = dS K             (MFMA, dS via LDS, K^T from registers)
+//            dQaccum += dQ_tile         (fp32 atomics, or ordered adds)
+//
+// Wave w owns keys 32w..32w+31 of the tile: it keeps those rows of K and V in
+// registers as MFMA B operands, accumulates their dK and dV rows in fp32 for
+// the whole loop, and, for the dQ product, holds a 32-column slice of K^T.
+// All transposed operands (dO and Q for stages 3 and 6, dS for stage 7, K^T)
+// come from LDS through the transposing read ds_read_b64_tr_b16, so every
+// tile is stored once, row-major and swizzled.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = kBwdBlockN;
+
+template <class T, int HD>
+struct BwdCfg {
+    static constexpr int BM = (sizeof(T) == 4 && HD == 128) ? 32 : 64;   // query rows per tile
+    static constexpr int ROWB = HD * (int)sizeof(T);                       // LDS bytes per Q/dO/K row
+    static constexpr int DSROWB = BM * (int)sizeof(T);                     // LDS bytes per dS^T row
+    static constexpr int TILE = BM * ROWB;
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_DO = TILE;
+    static constexpr int OFF_DS = 2 * TILE;
+    static constexpr int OFF_LSE = OFF_DS + kBN * DSROWB;
+    static constexpr int OFF_DL = OFF_LSE + BM * 4;
+    static constexpr int LOOP_BYTES = OFF_DL + BM * 4;
+    static constexpr int K_BYTES = kBN * ROWB;
+    static constexpr int LDS_BYTES = LOOP_BYTES > K_BYTES ? LOOP_BYTES : K_BYTES;
+    static constexpr int NC = HD / 16;     // 16-wide chunks of the head dim
+    static constexpr int NMB = BM / 32;    // 32-row blocks of a query tile
+    static constexpr int NDB = HD / 32;    // 32-column blocks of the head dim
+    static constexpr int NIC = BM / 16;    // 16-wide chunks of the query rows
+    static constexpr int NJC = kBN / 16;   // 16-wide chunks of the keys
+    static constexpr int DQB = NMB * NDB / kWaves;   // dQ 32x32 blocks per wave
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(NMB * NDB % kWaves == 0 && kWaves % NDB == 0, "dQ block split");
+};
+
+// --------------------------------------------------------------------------
+// operand loads
+// --------------------------------------------------------------------------
+
+// Row-major operand: lane gets M[row][col .. col+7] (col = 16c + 8h).
+template <class T, int ROWB>
+__device__ __forceinline__ typename Elem<T>::op_t read_op_row(const char* lds, int row, int col) {
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_bit_cast(bf16x8, lds_read16(lds, swz<ROWB>(row, col * 2)));
+    } else {
+        // whole-vector casts: a bit cast of a subscripted vector element is
+        // miscompiled (it reads element 0), so elements are never cast singly
+        const f32x4 a = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4)));
+        const f32x4 b = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4 + 16)));
+        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
+
+// Column operand: lane (l32 = lane % 32) gets M[r1 + t][c0 + l32] for t = 0..3
+// and M[r2 + t][c0 + l32] for t = 0..3, rows r1/r2 chosen per lane half.
+template <class T, int ROWB>
+__device__ __forceinline__ typename Elem<T>::op_t read_op_col(const char* lds, int r1, int r2, int c0, int lane) {
+    if constexpr (sizeof(T) == 2) {
+        const int s = lane & 15;
+        const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+        const u32x2 x = lds_read_tr(lds, swz<ROWB>(r1 + (s >> 2), col * 2));
+        const u32x2 y = lds_read_tr(lds, swz<ROWB>(r2 + (s >> 2), col * 2));
+        const u32x4 w = {x[0], x[1], y[0], y[1]};
+        return __builtin_bit_cast(bf16x8, w);
+    } else {
+        const int col = c0 + (lane & 31);
+        f32x8 r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            r[t] = *reinterpret_cast<const float*>(lds + swz<ROWB>(r1 + t, col * 4));
+            r[4 + t] = *reinterpret_cast<const float*>(lds + swz<ROWB>(r2 + t, col * 4));
+        }
+        return r;
+    }
+}
+
+// 8 consecutive elements of a global row as an MFMA operand (zero if !ok).
+template <class T>
+__device__ __forceinline__ typename Elem<T>::op_t load_op_global(const T* p, bool ok) {
+    if constexpr (sizeof(T) == 2) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ok) w = *reinterpret_cast<const u32x4*>(p);
+        return __builtin_bit_cast(bf16x8, w);
+    } else {
+        f32x8 r = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                r[t] = a[t];
+                r[4 + t] = b[t];
+            }
+        }
+        return r;
+    }
+}
+
+// Stage NROWS rows (row0 ..) of a global [rows, stride] tensor into a swizzled
+// LDS tile; rows at or past `valid` are written as zeros.
+template <class T, int ROWB, int NROWS>
+__device__ __forceinline__ void stage_rows(char* lds, const T* g, long long stride, int row0, int valid) {
+    constexpr int CPR = ROWB / 16;
+    constexpr int N = NROWS * CPR / kThreads;
+    static_assert(NROWS * CPR % kThreads == 0, "tile split");
+    u32x4 v[N];
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        const int c = threadIdx.x + t * kThreads;
+        const int r = c / CPR, ch = c % CPR;
+        v[t] = u32x4{0u, 0u, 0u, 0u};
+        if (row0 + r < valid)
+            v[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(g + (long long)(row0 + r) * stride) +
+                                                   ch * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+        const int c = threadIdx.x + t * kThreads;
+        const int r = c / CPR, ch = c % CPR;
+        lds_write(lds, swz<ROWB>(r, ch * 16), v[t]);
+    }
+}
+
+__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------------------------
+// the kernel
+// --------------------------------------------------------------------------
+template <class T, int HD, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
+    using C = BwdCfg<T, HD>;
+    using op_t = typename Elem<T>::op_t;
+    constexpr int BM = C::BM;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- which key tile: deterministic causal runs dispatch the highest key
+    // tile of a (sequence, kv-head) first, since it reaches every query tile
+    // first and so is first in the fixed summation order.
+    const int nb_lin = blockIdx.x % a.nblk_n;
+    const int rest = blockIdx.x / a.nblk_n;
+    const int hkv = rest % a.hkv;
+    const int b = rest / a.hkv;
+    const int n = (CAUSAL && a.deterministic) ? a.nblk_n - 1 - nb_lin : nb_lin;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    if (n * kBN >= si.len_k) return;
+    const bool varlen = a.cu_q != nullptr;
+    const int G = a.hq / a.hkv;
+    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+    const int m_end = (si.len_q + BM - 1) / BM;
+    int m_begin = 0;
+    if (CAUSAL) {
+        const int first_row = n * kBN - off;   // first query row that sees key n*kBN
+        m_begin = first_row > 0 ? first_row / BM : 0;
+    }
+    const int nblk_k = (si.len_k + kBN - 1) / kBN;
+
+    // ---- K and V of this wave's 32 keys in registers; K^T slice via LDS
+    const long long kstride = (long long)a.hkv * HD;
+    const T* kg = reinterpret_cast<const T*>(a.k) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    const T* vg = reinterpret_cast<const T*>(a.v) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    op_t kreg[C::NC], vreg[C::NC];
+    {
+        const int j = n * kBN + 32 * w + l32;
+        const bool ok = j < si.len_k;
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+            kreg[c] = load_op_global<T>(kg + (long long)j * kstride + 16 * c + 8 * h, ok);
+            vreg[c] = load_op_global<T>(vg + (long long)j * kstride + 16 * c + 8 * h, ok);
+        }
+    }
+    stage_rows<T, C::ROWB, kBN>(smem, kg, kstride, n * kBN, si.len_k);
+    __syncthreads();
+    // dQ blocks of this wave: column block db_w, row blocks mb_w0 + k * (kWaves / NDB)
+    const int db_w = w % C::NDB;
+    const int mb_w0 = w / C::NDB;
+    op_t ktreg[C::NJC];
+#pragma unroll
+    for (int c = 0; c < C::NJC; ++c)
+        ktreg[c] = read_op_col<T, C::ROWB>(smem, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * db_w, lane);
+    __syncthreads();
+
+    f32x16 dk[C::NDB], dv[C::NDB];
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            dk[d][v] = 0.f;
+            dv[d][v] = 0.f;
+        }
+    }
+
+    const float scale2 = a.scale * kLog2e;
+    const long long qstride = (long long)a.hq * HD;
+    char* lq = smem + C::OFF_Q;
+    char* ldo = smem + C::OFF_DO;
+    char* lds_ds = smem + C::OFF_DS;
+    float* llse = reinterpret_cast<float*>(smem + C::OFF_LSE);
+    float* ldl = reinterpret_cast<float*>(smem + C::OFF_DL);
+
+    for (int g = 0; g < G; ++g) {
+        const int hq = hkv * G + g;
+        const T* qg = reinterpret_cast<const T*>(a.q) + (long long)si.q0 * qstride + (long long)hq * HD;
+        const T* dog = reinterpret_cast<const T*>(a.dout) + (long long)si.q0 * qstride + (long long)hq * HD;
+        const long long row0 = varlen ? (long long)hq * a.total_q + si.q0
+                                      : ((long long)b * a.hq + hq) * a.seqlen_q;
+        const float* lse_g = a.lse + row0;
+        const float* dl_g = a.delta + row0;
+        float* dqa = a.dq_acc + row0 * HD;
+        int* sem_row = a.sem + ((long long)b * a.hq + hq) * a.nblk_m;
+
+        for (int m = m_begin; m < m_end; ++m) {
+            const int i0 = m * BM;
+            __syncthreads();   // previous tile's LDS reads are done
+            stage_rows<T, C::ROWB, BM>(lq, qg, qstride, i0, si.len_q);
+            stage_rows<T, C::ROWB, BM>(ldo, dog, qstride, i0, si.len_q);
+            if (threadIdx.x < BM) {
+                const int i = i0 + threadIdx.x;
+                float l2 = 0.f, dl = 0.f;
+                if (i < si.len_q) {
+                    const float lse = lse_g[i];
+                    l2 = lse == -INFINITY ? 0.f : lse * kLog2e;
+                    dl = dl_g[i];
+                }
+                llse[threadIdx.x] = l2;
+                ldl[threadIdx.x] = dl;
+            }
+            __syncthreads();
+
+            // ---- stages 1 and 4: S = Q K^T and dP = dO V^T for this wave's keys
+            f32x16 s[C::NMB], dp[C::NMB];
+#pragma unroll
+            for (int mb = 0; mb < C::NMB; ++mb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    s[mb][v] = 0.f;
+                    dp[mb][v] = 0.f;
+                }
+#pragma unroll
+                for (int c = 0; c < C::NC; ++c) {
+                    const op_t aq = read_op_row<T, C::ROWB>(lq, 32 * mb + l32, 16 * c + 8 * h);
+                    mma16(s[mb], aq, kreg[c]);
+                    const op_t ado = read_op_row<T, C::ROWB>(ldo, 32 * mb + l32, 16 * c + 8 * h);
+                    mma16(dp[mb], ado, vreg[c]);
+                }
+            }
+
+            // ---- stages 2 and 5: P = exp2(S s log2e - LSE log2e); dS = P (dP - D)
+            const bool edge = !((i0 + BM <= si.len_q) && (n * kBN + kBN <= si.len_k) &&
+                                (!CAUSAL || n * kBN + kBN - 1 <= i0 + off));
+            const int j = n * kBN + 32 * w + l32;
+#pragma unroll
+            for (int mb = 0; mb < C::NMB; ++mb) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int r = 32 * mb + 8 * q4 + 4 * h;
+                    const f32x4 l2 = *reinterpret_cast<const f32x4*>(llse + r);
+                    const f32x4 dl = *reinterpret_cast<const f32x4*>(ldl + r);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * q4 + e;
+                        float p = __builtin_amdgcn_exp2f(s[mb][v] * scale2 - l2[e]);
+                        if (edge) {
+                            const int i = i0 + r + e;
+                            const bool vis = i < si.len_q && j < si.len_k && (!CAUSAL || j <= i + off);
+                            p = vis ? p : 0.f;
+                        }
+                        s[mb][v] = p;
+                        dp[mb][v] = p * (dp[mb][v] - dl[e]);
+                    }
+                }
+            }
+
+            // ---- stages 3 and 6: dV += P^T dO, dK += dS^T Q
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) {
+                const int mb = c >> 1, vb = 8 * (c & 1);
+                op_t pa, dsa;
+                float tp[8], td[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    tp[t] = s[mb][vb + t];
+                    td[t] = dp[mb][vb + t];
+                }
+                to_op(pa, tp);
+                to_op(dsa, td);
+                const int r1 = 16 * c + 4 * h, r2 = 16 * c + 8 + 4 * h;
+#pragma unroll
+                for (int d = 0; d < C::NDB; ++d) {
+                    const op_t bdo = read_op_col<T, C::ROWB>(ldo, r1, r2, 32 * d, lane);
+                    mma16(dv[d], pa, bdo);
+                    const op_t bq = read_op_col<T, C::ROWB>(lq, r1, r2, 32 * d, lane);
+                    mma16(dk[d], dsa, bq);
+                }
+            }
+
+            // ---- dS^T to LDS (row = key, column = query row)
+            {
+                const int jr = 32 * w + l32;
+#pragma unroll
+                for (int mb = 0; mb < C::NMB; ++mb) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int col = 32 * mb + 8 * q4 + 4 * h;
+                        if constexpr (sizeof(T) == 2) {
+                            const u32x2 wv = {pack_bf16x2(dp[mb][4 * q4], dp[mb][4 * q4 + 1]),
+                                              pack_bf16x2(dp[mb][4 * q4 + 2], dp[mb][4 * q4 + 3])};
+                            lds_write(lds_ds, swz<C::DSROWB>(jr, col * 2), wv);
+                        } else {
+                            const f32x4 wv = {dp[mb][4 * q4], dp[mb][4 * q4 + 1], dp[mb][4 * q4 + 2],
+                                              dp[mb][4 * q4 + 3]};
+                            lds_write(lds_ds, swz<C::DSROWB>(jr, col * 4), wv);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+
+            // ---- stage 7: dQ tile = dS K for this wave's blocks
+            f32x16 dq[C::DQB];
+#pragma unroll
+            for (int x = 0; x < C::DQB; ++x) {
+                const int mb = mb_w0 + x * (kWaves / C::NDB);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dq[x][v] = 0.f;
+#pragma unroll
+                for (int c = 0; c < C::NJC; ++c) {
+                    const op_t ads =
+                        read_op_col<T, C::DSROWB>(lds_ds, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * mb, lane);
+                    mma16(dq[x], ads, ktreg[c]);
+                }
+            }
+
+            // ---- dQ accumulation: fp32 atomics, or in a fixed order per tile
+            int* sem = sem_row + m;
+            if (a.deterministic) {
+                int rank;
+                if (CAUSAL) {
+                    const int x = (m + 1) * BM + off;
+                    const int last = min(nblk_k - 1, (x + kBN - 1) / kBN - 1);
+                    rank = last - n;
+                } else {
+                    rank = n;
+                }
+                if (threadIdx.x == 0) {
+                    int spins = 0;
+                    while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != rank) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins > (1 << 24)) {
+                            __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
+                }
+                __syncthreads();
+                __atomic_thread_fence(__ATOMIC_ACQUIRE);
+            }
+#pragma unroll
+            for (int x = 0; x < C::DQB; ++x) {
+                const int mb = mb_w0 + x * (kWaves / C::NDB);
+                const int col = 32 * db_w + l32;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int i = i0 + 32 * mb + acc_row(v, h);
+                    if (i < si.len_q) atomic_add_f32(dqa + (long long)i * HD + col, dq[x][v]);
+                }
+            }
+            if (a.deterministic) {
+                __threadfence();
+                __syncthreads();
+                if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    // ---- epilogue: dK = s * sum dS^T Q, dV; rows past the sequence are not written
+    T* dkg = reinterpret_cast<T*>(a.dk) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    T* dvg = reinterpret_cast<T*>(a.dv) + (long long)si.k0 * kstride + (long long)hkv * HD;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int jj = n * kBN + 32 * w + acc_row(v, h);
+            if (jj < si.len_k) {
+                const long long idx = (long long)jj * kstride + 32 * d + l32;
+                store_elem(dkg, idx, dk[d][v] * a.scale);
+                store_elem(dvg, idx, dv[d][v]);
+            }
+        }
+    }
+}
+
+int bwd_block_m(int dtype, int head_dim) {
+    if (dtype == ATTN_DTYPE_F32 && head_dim == 128) return BwdCfg<float, 128>::BM;
+    return 64;
+}
+
+template <class T, int HD>
+static void launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
+    const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
+    if (causal)
+        bwd_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
+    else
+        bwd_kernel<T, HD, false><<<grid, kThreads, 0, st>>>(a);
+}
+
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, st);
+        else launch_bwd_t<bf16_t, 128>(a, causal, st);
+    } else {
+        if (hd == 64) launch_bwd_t<float, 64>(a, causal, st);
+        else launch_bwd_t<float, 128>(a, causal, st);
+    }
+}
+
+}  // namespace attn

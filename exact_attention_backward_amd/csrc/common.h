@@ -1,0 +1,148 @@
+// Shared device-side helpers of the gfx950 attention kernels: vector types,
+// MFMA wrappers, bf16 packing, the XOR-swizzled LDS tile addressing and the
+// transposing LDS read.  Written for CDNA4 (wave64, 160 KiB LDS per CU).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn_bwd.h"
+
+namespace attn {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// A bf16 value stored as its 16-bit pattern.  All bf16 vectors are moved as
+// integer words; the compiler's element access on __bf16 vectors is avoided,
+// and so is __builtin_bit_cast of a subscripted vector element (v[i]), which
+// this compiler lowers as a read of element 0: vectors are bit cast whole, or
+// the element is first copied into a scalar.
+typedef uint16_t bf16_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// element type traits: bf16 (MFMA 32x32x16 bf16) and fp32 (MFMA 32x32x2 f32)
+// ---------------------------------------------------------------------------
+template <class T> struct Elem;
+
+template <> struct Elem<bf16_t> {
+    // 8 consecutive-k operand values of one lane: 16 bytes
+    typedef bf16x8 op_t;
+    static constexpr int kBytes = 2;
+    static constexpr attn_dtype_t kDtype = ATTN_DTYPE_BF16;
+};
+template <> struct Elem<float> {
+    typedef f32x8 op_t;
+    static constexpr int kBytes = 4;
+    static constexpr attn_dtype_t kDtype = ATTN_DTYPE_F32;
+};
+
+// c += a * b over one 16-long slice of the contraction index.
+// Lane l holds a[i = l % 32][k = 8 * (l / 32) + t] and b[k = 8 * (l / 32) + t][j = l % 32]
+// for t = 0..7; c is the 32x32 fp32 accumulator in the MFMA output layout
+// (lane l, value v -> row 8 * (v / 4) + 4 * (l / 32) + v % 4, column l % 32).
+__device__ __forceinline__ void mma16(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& c, const f32x8& a, const f32x8& b) {
+    // step t pairs k = t (lanes 0-31) with k = 8 + t (lanes 32-63)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], c, 0, 0, 0);
+}
+
+// Row of the MFMA 32x32 output held by value v of lane half h (= lane / 32).
+__device__ __forceinline__ constexpr int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// ---------------------------------------------------------------------------
+// bf16 conversion (round to nearest even, the hardware v_cvt_pk_bf16_f32)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Eight fp32 values -> MFMA operand of type T.
+__device__ __forceinline__ void to_op(bf16x8& o, const float* x) {
+    u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+               pack_bf16x2(x[6], x[7])};
+    o = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void to_op(f32x8& o, const float* x) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = x[t];
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles: row-major with 16-byte chunks XOR-swizzled by the row index, so
+// that 16-byte reads of one column chunk across consecutive rows, and the
+// 8-byte transposing reads, fall in different banks.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row, int byte) {
+    constexpr int kChunks = ROW_BYTES / 16;
+    constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
+    return row * ROW_BYTES + ((((byte >> 4) ^ (row & kMask))) << 4) + (byte & 15);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane s supplies the address of 4 consecutive 16-bit elements; output
+// lane u receives element (u % 4) of source lanes 4e + u / 4, e = 0..3.  Used
+// on a row-major tile, where lane s points at row r0 + s / 4, columns
+// c0 + 4 (s % 4) .. +3, output lane u gets the column c0 + u of rows r0..r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* lds_base, int byte_off) {
+    bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_base + byte_off));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* lds_base, int byte_off) {
+    return *reinterpret_cast<const u32x4*>(lds_base + byte_off);
+}
+
+template <class V>
+__device__ __forceinline__ void lds_write(char* lds_base, int byte_off, const V& v) {
+    *reinterpret_cast<V*>(lds_base + byte_off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// problem geometry on the device
+// ---------------------------------------------------------------------------
+struct SeqInfo {
+    int q0, len_q;   // first row of the sequence in Q (flattened [rows, H, D]) and its length
+    int k0, len_k;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(int b, int seqlen_q, int seqlen_k, int total_q, int total_k,
+                                            const int32_t* cu_q, const int32_t* cu_k) {
+    SeqInfo s;
+    if (cu_q == nullptr) {
+        s.q0 = b * seqlen_q;
+        s.len_q = seqlen_q;
+        s.k0 = b * seqlen_k;
+        s.len_k = seqlen_k;
+    } else {
+        // offsets clamped into the buffers and lengths to the declared maxima,
+        // so malformed offsets cannot address outside the tensors
+        int a = min(max(cu_q[b], 0), total_q), e = min(max(cu_q[b + 1], a), total_q);
+        s.q0 = a;
+        s.len_q = min(e - a, seqlen_q);
+        a = min(max(cu_k[b], 0), total_k);
+        e = min(max(cu_k[b + 1], a), total_k);
+        s.k0 = a;
+        s.len_k = min(e - a, seqlen_k);
+    }
+    return s;
+}
+
+}  // namespace attn

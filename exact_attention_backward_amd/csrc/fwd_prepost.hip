@@ -1,0 +1,209 @@
+// Plain forward (input generator), backward preprocess (D = rowsum(dO * O),
+// workspace clear) and dQ postprocess (fp32 accumulator -> I/O type).
+//
+// The preprocess and postprocess are HBM-streaming kernels: every thread
+// moves 16-byte vectors, rows are read contiguously, and the only arithmetic
+// is a fused multiply-add chain (preprocess) or a scale + convert
+// (postprocess).
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+
+// Index of (sequence row r, head h) in the [B, H, S] / [H, total] layouts of
+// LSE, D and the dQ accumulator.  r is the flattened row of Q (b * Sq + i for
+// dense, the packed row for varlen).
+__device__ __forceinline__ long long lse_index(bool varlen, long long r, int h, int H, int S, long long total) {
+    if (varlen) return (long long)h * total + r;
+    long long b = r / S, i = r - b * S;
+    return (b * H + h) * S + i;
+}
+
+// ---------------------------------------------------------------------------
+// forward: one thread per query row, K/V tiles of 32 keys staged in LDS,
+// online softmax in base 2.  Not performance-tracked.
+// ---------------------------------------------------------------------------
+template <class T, int HD, bool CAUSAL>
+__global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
+    constexpr int BQ = 128, BK = 32;
+    __shared__ float ks[BK][HD];
+    __shared__ float vs[BK][HD];
+    const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    if (qb * BQ >= si.len_q) return;
+    const int hkv = hq / (a.hq / a.hkv);
+    const int i = qb * BQ + threadIdx.x;
+    const bool row_ok = i < si.len_q;
+    const int off = si.len_k - si.len_q;
+    const T* qp = reinterpret_cast<const T*>(a.q);
+    const T* kp = reinterpret_cast<const T*>(a.k);
+    const T* vp = reinterpret_cast<const T*>(a.v);
+
+    float q[HD], o[HD];
+    const float qs = a.scale * kLog2e;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        q[d] = row_ok ? (float)load_elem(qp, ((long long)(si.q0 + i) * a.hq + hq) * HD + d) * qs : 0.f;
+        o[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    int kend = si.len_k;
+    if (CAUSAL) kend = min(kend, min(qb * BQ + BQ, si.len_q) - 1 + off + 1);
+    for (int kt = 0; kt < kend; kt += BK) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < BK * HD; e += blockDim.x) {
+            const int jj = e / HD, d = e % HD, j = kt + jj;
+            const long long g = ((long long)(si.k0 + j) * a.hkv + hkv) * HD + d;
+            ks[jj][d] = j < si.len_k ? (float)load_elem(kp, g) : 0.f;
+            vs[jj][d] = j < si.len_k ? (float)load_elem(vp, g) : 0.f;
+        }
+        __syncthreads();
+        float s[BK];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < BK; ++jj) {
+            const int j = kt + jj;
+            const bool vis = row_ok && j < si.len_k && (!CAUSAL || j <= i + off);
+            float acc = 0.f;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) acc = fmaf(q[d], ks[jj][d], acc);
+            s[jj] = vis ? acc : -INFINITY;
+            tmax = fmaxf(tmax, s[jj]);
+        }
+        if (tmax > -INFINITY) {
+            const float mn = fmaxf(m, tmax);
+            const float corr = exp2f(m - mn);
+            l *= corr;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) o[d] *= corr;
+#pragma unroll
+            for (int jj = 0; jj < BK; ++jj) {
+                const float p = exp2f(s[jj] - mn);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < HD; ++d) o[d] = fmaf(p, vs[jj][d], o[d]);
+            }
+            m = mn;
+        }
+    }
+    if (!row_ok) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* op = reinterpret_cast<T*>(a.o);
+    const long long ob = ((long long)(si.q0 + i) * a.hq + hq) * HD;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) store_elem(op, ob + d, o[d] * inv);
+    const bool varlen = a.cu_q != nullptr;
+    const long long li = varlen ? (long long)hq * a.total_q + si.q0 + i
+                                : ((long long)b * a.hq + hq) * a.seqlen_q + i;
+    a.lse[li] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// preprocess: D = rowsum(dO * O); HD / 8 lanes per row, 8 elements per lane
+// ---------------------------------------------------------------------------
+template <class T, int HD>
+__global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
+    constexpr int LPR = HD / 8;
+    const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long row = gt / LPR;            // = flat_row * H + h, the memory order of O
+    const int part = (int)(gt % LPR);
+    float acc = 0.f;
+    if (row < a.rows) {
+        float x[8], y[8];
+        load8(reinterpret_cast<const T*>(a.o) + row * HD + part * 8, x);
+        load8(reinterpret_cast<const T*>(a.dout) + row * HD + part * 8, y);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc = fmaf(x[t], y[t], acc);
+    }
+#pragma unroll
+    for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
+    if (row < a.rows && part == 0) {
+        const long long r = row / a.h;
+        const int h = (int)(row - r * a.h);
+        a.delta[lse_index(a.varlen, r, h, a.h, a.s, a.total)] = acc;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, long long n16) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (long long)gridDim.x * blockDim.x)
+        p[i] = z;
+}
+
+// ---------------------------------------------------------------------------
+// postprocess: dQ[row, h, :] = T(scale * acc[h, row, :])
+// ---------------------------------------------------------------------------
+template <class T, int HD>
+__global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
+    constexpr int LPR = HD / 8;
+    const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long row = gt / LPR;
+    if (row >= a.rows) return;
+    const int part = (int)(gt % LPR);
+    const long long r = row / a.h;
+    const int h = (int)(row - r * a.h);
+    const float* src = a.acc + lse_index(a.varlen, r, h, a.h, a.s, a.total) * HD + part * 8;
+    const f32x4 u = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4);
+    float x[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] *= a.scale;
+    store8(reinterpret_cast<T*>(a.dq) + row * HD + part * 8, x);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <class T, int HD>
+static void launch_fwd_t(const FwdArgs& a, bool causal, hipStream_t st) {
+    dim3 grid((a.seqlen_q + 127) / 128, a.hq, a.batch);
+    if (causal)
+        fwd_kernel<T, HD, true><<<grid, 128, 0, st>>>(a);
+    else
+        fwd_kernel<T, HD, false><<<grid, 128, 0, st>>>(a);
+}
+
+void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) launch_fwd_t<bf16_t, 64>(a, causal, st);
+        else launch_fwd_t<bf16_t, 128>(a, causal, st);
+    } else {
+        if (hd == 64) launch_fwd_t<float, 64>(a, causal, st);
+        else launch_fwd_t<float, 128>(a, causal, st);
+    }
+}
+
+void launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+    const long long n16 = (long long)(bytes / 16);
+    if (n16 == 0) return;
+    long long blocks = (n16 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<u32x4*>(p), n16);
+}
+
+void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st) {
+    const long long threads = a.rows * (hd / 8);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) preprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
+        else preprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+    } else {
+        if (hd == 64) preprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
+        else preprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);
+    }
+}
+
+void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st) {
+    const long long threads = a.rows * (hd / 8);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) postprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
+        else postprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+    } else {
+        if (hd == 64) postprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
+        else postprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);
+    }
+}
+
+}  // namespace attn

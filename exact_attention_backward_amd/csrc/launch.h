@@ -1,0 +1,113 @@
+// Kernel argument blocks, element load/store helpers and launcher prototypes
+// shared by the kernel sources and the C ABI layer.
+#pragma once
+
+#include "common.h"
+
+namespace attn {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
+    float scale;
+};
+
+struct PreArgs {
+    const void* o;
+    const void* dout;
+    float* delta;
+    long long rows;      // flattened rows of O times heads
+    int h, s;            // heads, dense sequence length
+    long long total;     // varlen total rows
+    bool varlen;
+};
+
+struct PostArgs {
+    const float* acc;
+    void* dq;
+    long long rows;
+    int h, s;
+    long long total;
+    bool varlen;
+    float scale;
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    float* dq_acc;       // fp32 [B, Hq, Sq, D] or [Hq, total_q, D]
+    int* sem;            // deterministic mode: one counter per (sequence, q-head, query tile)
+    int* err;            // deterministic mode: set when an ordered wait gave up
+    void* dk;
+    void* dv;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
+    int nblk_n;          // key tiles per sequence (of the longest sequence)
+    int nblk_m;          // query tiles per sequence (of the longest sequence)
+    float scale;
+    int deterministic;
+};
+
+// Query rows per tile of the main kernel (keys per tile are fixed at 128).
+int bwd_block_m(int dtype, int head_dim);
+constexpr int kBwdBlockN = 128;
+
+void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
+void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// element access for the two I/O types
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float load_elem(const bf16_t* p, long long i) {
+    return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
+}
+__device__ __forceinline__ float load_elem(const float* p, long long i) { return p[i]; }
+__device__ __forceinline__ void store_elem(bf16_t* p, long long i, float x) {
+    p[i] = (bf16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+__device__ __forceinline__ void store_elem(float* p, long long i, float x) { p[i] = x; }
+
+__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[2 * t] = bf16_lo(w[t]);
+        x[2 * t + 1] = bf16_hi(w[t]);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[t] = u[t];
+        x[4 + t] = v[t];
+    }
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* x) {
+    const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+    *reinterpret_cast<u32x4*>(p) = w;
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+    const f32x4 u = {x[0], x[1], x[2], x[3]};
+    const f32x4 v = {x[4], x[5], x[6], x[7]};
+    *reinterpret_cast<f32x4*>(p) = u;
+    *reinterpret_cast<f32x4*>(p + 4) = v;
+}
+
+}  // namespace attn

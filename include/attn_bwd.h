@@ -1,0 +1,142 @@
+/*
+ * attn_bwd.h -- C ABI of the MI355X (gfx950) exact-attention backward library.
+ *
+ * The library computes the gradient of exact softmax attention,
+ *     O = softmax(s * Q K^T [+ causal mask]) V,
+ * i.e. dQ, dK and dV from Q, K, V, O, dO and the per-row log-sum-exp LSE,
+ * as a fused, tiled pass that recomputes the probabilities from LSE instead
+ * of storing them.  The operation and its stages are those of the
+ * Composable Kernel page "block_fmha_bwd_dq_dk_dv_pipeline_trload_kr_ktr_vr.hpp
+ * Source File" (BlockFmhaBwdDQDKDVPipelineTrLoadKRKTRVR, stages 1-7); the dK/dV
+ * epilogue and GQA reduction follow CollectiveEpilogueBwd /
+ * CollectiveEpilogueBwdGQA on "flash-attention/hopper/epilogue_bwd.hpp"; the dQ
+ * conversion follows FlashAttentionBackwardPostprocess on
+ * "flash_bwd_postprocess.py".
+ *
+ * One backward step is three calls on one stream, in this order:
+ *     attn_bwd_preprocess      D = rowsum(dO * O); clears the workspace
+ *     attn_bwd                 dK, dV; dQ accumulated in fp32 in the workspace
+ *     attn_bwd_dq_postprocess  dQ = scale * dQaccum, converted to the I/O type
+ * attn_fwd is a plain forward used only to produce O and LSE inputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, contiguous,
+ *    head dimension innermost.  The caller allocates and frees every buffer,
+ *    the workspace included; the library never allocates, frees or
+ *    synchronises.  Every call only enqueues work on `stream` (a hipStream_t,
+ *    NULL = the default stream) and returns.
+ *  - Layouts (element type = shape->dtype for Q K V O dO dQ dK dV; fp32 for
+ *    LSE and D):
+ *        dense : Q, O, dO, dQ [B, Sq, Hq, D];  K, V, dK, dV [B, Sk, Hkv, D]
+ *                LSE, D [B, Hq, Sq]
+ *        varlen: Q, O, dO, dQ [total_q, Hq, D]; K, V, dK, dV [total_k, Hkv, D]
+ *                LSE, D [Hq, total_q]
+ *    Varlen is selected by non-NULL cu_seqlens_q/cu_seqlens_k (device int32
+ *    arrays of batch+1 nondecreasing offsets starting at 0 and ending at
+ *    total_q/total_k); sequence b occupies rows [cu[b], cu[b+1]) and no
+ *    sequence may be longer than seqlen_q/seqlen_k.
+ *  - Causal masking is aligned to the bottom-right corner of each
+ *    (sequence, head) block: key j is visible to query i iff
+ *    j <= i + (len_k - len_q).  A query row that sees no key has LSE = -inf,
+ *    O = 0, and gets dQ = 0.
+ *  - GQA: Hq must be a multiple of Hkv; q-head h uses kv-head h / (Hq / Hkv)
+ *    (contiguous groups).  dK and dV of a kv-head are the sums over its
+ *    q-heads.
+ *  - Errors: every call validates its arguments before touching the GPU and
+ *    returns a status (attn_status_t); on error nothing is enqueued.  A launch
+ *    failure reported by the HIP runtime returns ATTN_ERR_HIP.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL (the workspace included) */
+    ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
+                                  cu_seqlens, workspace too small, ... */
+    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16, head_dim not 64 or 128 */
+    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} attn_status_t;
+
+typedef enum attn_dtype {
+    ATTN_DTYPE_F32 = 0,        /* fp32 I/O, fp32 MFMA contractions */
+    ATTN_DTYPE_BF16 = 1        /* bf16 I/O, bf16 MFMA operands, fp32 accumulation */
+} attn_dtype_t;
+
+/* Problem description, passed by pointer and only read.  Plain old data. */
+typedef struct attn_shape {
+    int32_t batch;           /* dense batch B, or number of sequences when varlen */
+    int32_t num_heads_q;     /* Hq */
+    int32_t num_heads_kv;    /* Hkv, divides Hq */
+    int32_t seqlen_q;        /* dense Sq, or the longest query sequence when varlen */
+    int32_t seqlen_k;        /* dense Sk, or the longest key sequence when varlen */
+    int32_t head_dim;        /* D: 64 or 128 */
+    int32_t total_q;         /* varlen only: rows of Q (= cu_seqlens_q[batch]) */
+    int32_t total_k;         /* varlen only: rows of K (= cu_seqlens_k[batch]) */
+    const int32_t* cu_seqlens_q;  /* device, [batch+1], or NULL for dense */
+    const int32_t* cu_seqlens_k;  /* device, [batch+1], or NULL for dense */
+    float softmax_scale;     /* s in softmax(s * Q K^T); always explicit */
+    int32_t causal;          /* 0 or 1 */
+    int32_t deterministic;   /* 1: dQ summed in a fixed order, bitwise reproducible */
+    int32_t dtype;           /* attn_dtype_t */
+} attn_shape_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_string(int status);
+
+/* Bytes of device workspace attn_bwd_preprocess/attn_bwd/attn_bwd_dq_postprocess
+ * need for this shape: the fp32 dQ accumulator ([B, Hq, Sq, D] dense,
+ * [Hq, total_q, D] varlen) followed by the int32 ordering counters of the
+ * deterministic mode, each part 256-byte aligned.  Returns 0 if the shape is
+ * invalid. */
+size_t attn_bwd_workspace_bytes(const attn_shape_t* shape);
+
+/* Plain forward: O = softmax(s Q K^T) V and LSE (natural log) per row.
+ * Not performance-tracked; used to make O/LSE inputs for the backward.
+ * q, k, v: inputs; o, lse: outputs (fully overwritten). */
+int attn_fwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+             void* o, float* lse, void* stream);
+
+/* Backward preprocess: D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d],
+ * accumulated in fp32 (D is consumed, never shown, by the pipeline page's
+ * stage 5).  Also zeroes the workspace, which attn_bwd accumulates into (the
+ * zero-initialised accumulator contract of CollectiveEpilogueBwdGQA::store_zero).
+ * o, dout: inputs; delta: output [LSE layout]; workspace: output, at least
+ * attn_bwd_workspace_bytes(shape) bytes (workspace_bytes says how many). */
+int attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* dout,
+                        float* delta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Main backward kernel.  Per K/V tile: recompute P = exp(s Q K^T - LSE),
+ * dP = dO V^T, dS = P (dP - D); dV = P^T dO and dK = s dS^T Q are written to
+ * dk/dv (fully overwritten, GQA groups summed, zero rows for keys no query
+ * sees); dQ partials dS K are added in fp32 into the workspace accumulator,
+ * with hardware atomics, or, when shape->deterministic, in a fixed order per
+ * dQ tile so that repeated runs are bitwise identical.  The workspace must
+ * have been cleared by attn_bwd_preprocess for this shape since the last
+ * attn_bwd (running attn_bwd twice without it adds dQ twice).
+ * q, k, v, dout, lse, delta: inputs; dk, dv: outputs; workspace: in/out. */
+int attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+             const void* dout, const float* lse, const float* delta,
+             void* workspace, size_t workspace_bytes, void* dk, void* dv, void* stream);
+
+/* dQ postprocess: dq = dtype(scale * dQaccum), the product in fp32, bf16
+ * rounded to nearest even (FlashAttentionBackwardPostprocess).  Pass
+ * scale = shape->softmax_scale.  workspace: input; dq: output. */
+int attn_bwd_dq_postprocess(const attn_shape_t* shape, const void* workspace,
+                            size_t workspace_bytes, void* dq, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

@@ -1,0 +1,104 @@
+"""Shared helpers of the GPU parity tests: run the HIP path and the oracle on
+the same seeded inputs and compare.  Test infrastructure only."""
+
+import math
+
+import numpy as np
+import torch
+
+import datagen
+import oracle
+from exact_attention_backward_amd import api
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(TORCH_DTYPE[dtype]).cuda()
+
+
+def to_host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def round_like(x, dtype):
+    """Values the GPU will hold for a float64 array stored in `dtype`."""
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    return datagen.round_to_bf16(x32).astype(np.float64) if dtype == "bf16" else x32.astype(np.float64)
+
+
+def small_problem(dtype, b, hq, hkv, sq, sk, d, causal, seed, lengths=None, deterministic=False, scale=None,
+                  do_scale=1.0):
+    if lengths is not None:
+        lengths = tuple(lengths)
+        sq = sk = max(lengths)
+    return datagen.Problem(dtype, len(lengths) if lengths else b, hq, hkv, sq, sk, d, causal,
+                           scale if scale is not None else 1 / math.sqrt(d), seed, do_scale=do_scale,
+                           lengths_q=lengths, lengths_k=lengths, deterministic=deterministic,
+                           name=f"test_{dtype}_{hq}_{hkv}_{sq}_{sk}_{d}_{int(causal)}")
+
+
+class Run:
+    """Inputs of a problem on host and device, with O/LSE from the oracle."""
+
+    def __init__(self, p, oracle_o_lse=True):
+        self.p = p
+        self.x = datagen.draw(p)
+        cq, ck = p.cu_seqlens()
+        self.cu_np = (cq, ck)
+        self.cu = (None, None) if cq is None else (torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda())
+        self.dev = {k: to_dev(v, p.dtype) for k, v in self.x.items()}
+        if oracle_o_lse:
+            o, lse = oracle.forward(self.x["q"], self.x["k"], self.x["v"], p.scale, p.causal, cq, ck)
+            self.set_o_lse(o, lse)
+
+    def kw(self):
+        p = self.p
+        if not p.varlen:
+            return {}
+        return dict(cu_seqlens_q=self.cu[0], cu_seqlens_k=self.cu[1], max_seqlen_q=p.seqlen_q,
+                    max_seqlen_k=p.seqlen_k)
+
+    def set_o_lse(self, o, lse):
+        """O rounded to the I/O type and LSE to fp32, the values both sides use."""
+        self.o = round_like(o, self.p.dtype)
+        self.lse = np.asarray(lse, np.float64).astype(np.float32).astype(np.float64)
+        self.dev["o"] = to_dev(self.o, self.p.dtype)
+        self.dev["lse"] = torch.from_numpy(self.lse.astype(np.float32)).cuda()
+
+    def gpu_forward(self):
+        d = self.dev
+        return api.forward(d["q"], d["k"], d["v"], self.p.scale, self.p.causal, **self.kw())
+
+    def plan(self, deterministic=None):
+        d = self.dev
+        det = self.p.deterministic if deterministic is None else deterministic
+        return api.BackwardPlan(d["q"], d["k"], self.p.scale, self.p.causal, det, **self.kw())
+
+    def gpu_backward(self, deterministic=None, plan=None):
+        d = self.dev
+        plan = plan or self.plan(deterministic)
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        plan.run(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq, dk, dv)
+        torch.cuda.synchronize()
+        return dq, dk, dv, plan
+
+    def oracle_backward(self):
+        cq, ck = self.cu_np
+        return oracle.backward(self.x["q"], self.x["k"], self.x["v"], self.o, self.x["do"], self.lse,
+                               self.p.scale, self.p.causal, cq, ck)
+
+
+def assert_close(name, got, ref, dtype):
+    err = rel_err(got, ref)
+    assert err <= TOL[dtype], f"{name}: max|gpu-ref|/max|ref| = {err:.3e} > {TOL[dtype]}"
+    return err

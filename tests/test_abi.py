@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_backward_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_bwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|size_t|int)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert L.status_string(L.ATTN_OK) == "ok"
+    for code in (1, 2, 3, 4, 5):
+        assert L.status_string(code) not in ("ok", "unknown status")
+    assert L.status_string(99) == "unknown status"
+
+
+def shape(**kw):
+    s = L.AttnShape()
+    base = dict(batch=2, num_heads_q=4, num_heads_kv=2, seqlen_q=100, seqlen_k=90, head_dim=128,
+                total_q=0, total_k=0, softmax_scale=0.125, causal=1, deterministic=0, dtype=L.ATTN_DTYPE_BF16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(s, k, v)
+    return s
+
+
+def ws_bytes(s):
+    return L.lib().attn_bwd_workspace_bytes(ctypes.byref(s))
+
+
+def test_workspace_size_formula():
+    s = shape()
+    # dQ accumulator [B, Hq, Sq, D] fp32, counters [B, Hq, ceil(Sq/64)] int32, 256 B status
+    acc = 2 * 4 * 100 * 128 * 4
+    acc = (acc + 255) // 256 * 256
+    sem = (2 * 4 * 2 * 4 + 255) // 256 * 256
+    assert ws_bytes(s) == acc + sem + 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=0), L.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.ATTN_ERR_UNSUPPORTED),
+    (dict(num_heads_kv=3), L.ATTN_ERR_BAD_SHAPE),
+    (dict(batch=0), L.ATTN_ERR_BAD_SHAPE),
+    (dict(seqlen_q=-1), L.ATTN_ERR_BAD_SHAPE),
+    (dict(causal=2), L.ATTN_ERR_BAD_SHAPE),
+    (dict(softmax_scale=float("nan")), L.ATTN_ERR_BAD_SHAPE),
+])
+def test_invalid_shapes_rejected(kw, status):
+    s = shape(**kw)
+    assert ws_bytes(s) == 0
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+    assert rc == status
+
+
+def test_varlen_needs_both_offsets_and_totals():
+    s = shape(cu_seqlens_q=0x1000)
+    assert ws_bytes(s) == 0
+    s = shape(cu_seqlens_q=0x1000, cu_seqlens_k=0x2000, total_q=0, total_k=5)
+    assert ws_bytes(s) == 0
+    s = shape(cu_seqlens_q=0x1000, cu_seqlens_k=0x2000, total_q=500, total_k=400)
+    assert ws_bytes(s) > 0
+
+
+def test_null_and_misaligned_pointers_rejected():
+    s = shape()
+    fake = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1004)
+    lib = L.lib()
+    assert lib.attn_bwd(ctypes.byref(s), None, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake,
+                        None) == L.ATTN_ERR_NULL_ARG
+    assert lib.attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, 1 << 40, fake, fake,
+                        None) == L.ATTN_ERR_NULL_ARG
+    assert lib.attn_bwd(ctypes.byref(s), bad, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake,
+                        None) == L.ATTN_ERR_MISALIGNED
+    assert lib.attn_bwd_preprocess(ctypes.byref(s), fake, fake, fake, fake, 16, None) == L.ATTN_ERR_BAD_SHAPE
+    assert lib.attn_bwd_dq_postprocess(ctypes.byref(s), None, 1 << 40, fake, ctypes.c_float(1.0),
+                                       None) == L.ATTN_ERR_NULL_ARG
+    assert lib.attn_fwd(ctypes.byref(s), fake, fake, fake, bad, fake, None) == L.ATTN_ERR_MISALIGNED
+    assert lib.attn_fwd(None, fake, fake, fake, fake, fake, None) == L.ATTN_ERR_NULL_ARG
