@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the attention backward hot path on one MI355X.
+
+A step is one full backward of the workload: preprocess (D = rowsum(dO * O)
+and workspace clear) -> main kernel -> dQ postprocess, with Q, K, V, O, dO and
+LSE already resident in HBM.  Inputs are seeded synthetic data of the
+workload's shape; O and LSE come from the library's plain forward.
+
+Prints ONE JSON line: whole-step TFLOP/s (10 * B * H * Sq * Sk * D FLOPs per
+step, halved when causal), the main kernel's roofline figures measured with HIP
+events on the stream the kernels run on, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention-backward TFLOP/s (bf16, causal, S=4096, D=128) and % of MFMA peak"
+# MI355X published dense peaks
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+MAIN_SRC = os.path.join(ROOT, "exact_attention_backward_amd", "csrc", "bwd_main.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_c3_causal.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="(sequence 0) heads of the workload in the CPU sample")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_entry(per_launch_flops):
+    """HBM bytes per main-kernel launch from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("kernel_source_sha256_16") != source_hash(MAIN_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(p, x, n_heads):
+    """The fp64 oracle backward on the first n_heads (sequence 0) of the
+    workload, given O and LSE from the oracle forward (not timed)."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n_heads = max(1, min(n_heads, p.heads_q))
+    g = p.heads_q // p.heads_kv
+    elapsed, flops = 0.0, 0.0
+    for h in range(n_heads):
+        if p.varlen:
+            L = p.lengths_q[0]
+            q, do = x["q"][:L, h], x["do"][:L, h]
+            k, v = x["k"][:L, h // g], x["v"][:L, h // g]
+            sq = sk = L
+        else:
+            q, do = x["q"][0, :, h], x["do"][0, :, h]
+            k, v = x["k"][0, :, h // g], x["v"][0, :, h // g]
+            sq, sk = p.seqlen_q, p.seqlen_k
+        o, lse = oracle.head_forward(q, k, v, p.scale, p.causal)
+        t0 = time.perf_counter()
+        oracle.head_backward(q, k, v, o, do, lse, p.scale, p.causal)
+        elapsed += time.perf_counter() - t0
+        f = 10.0 * sq * sk * p.head_dim
+        flops += f / 2 if p.causal else f
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle backward of {n_heads} of the {p.batch * p.heads_q} (sequence, head) "
+                  f"pairs (sequence 0, heads 0..{n_heads - 1}) at full length; {elapsed:.1f} s",
+        "seconds": elapsed,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by whole (batch, kv-head) groups, see the design notes)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import datagen
+    from exact_attention_backward_amd import api
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+    p = datagen.workload(args.workload, deterministic=args.deterministic)
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    x = datagen.draw(p)
+    dev = {k: torch.from_numpy(v).to(dt).cuda() for k, v in x.items()}
+    kw = {}
+    if p.varlen:
+        cq, ck = p.cu_seqlens()
+        kw = dict(cu_seqlens_q=torch.from_numpy(cq).cuda(), cu_seqlens_k=torch.from_numpy(ck).cuda(),
+                  max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, **kw)
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, **kw)
+    dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        plan.run(q, k, v, o, do, lse, dq, dk, dv)
+    torch.cuda.synchronize()
+
+    # per-kernel HIP events on the stream the kernels are launched on
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(st)
+        plan.preprocess(o, do)
+        e[1].record(st)
+        plan.main(q, k, v, do, lse, dk, dv)
+        e[2].record(st)
+        plan.postprocess(dq)
+        e[3].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    main_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    post_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    flops = p.flops()
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    main_avg = float(main_ms.mean())
+    achieved = flops / (main_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[p.dtype]
+
+    rows_q = p.total_q
+    elem = 2 if p.dtype == "bf16" else 4
+    pre_bytes = 2 * rows_q * p.heads_q * p.head_dim * elem + rows_q * p.heads_q * 4 + \
+        plan.workspace.numel()
+    post_bytes = rows_q * p.heads_q * p.head_dim * (4 + elem)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded normal Q, K, V, dO; O and LSE from the library forward)",
+        "config": {
+            "workload": f"{p.name}: B={p.batch} Hq={p.heads_q} Hkv={p.heads_kv} Sq={p.seqlen_q} "
+                        f"Sk={p.seqlen_k} D={p.head_dim} {'causal' if p.causal else 'non-causal'}"
+                        f"{' deterministic' if p.deterministic else ''}",
+            "batch": p.batch, "heads_q": p.heads_q, "heads_kv": p.heads_kv, "seqlen_q": p.seqlen_q,
+            "seqlen_k": p.seqlen_k, "head_dim": p.head_dim, "causal": p.causal,
+            "deterministic": p.deterministic, "flops_per_step": flops,
+        },
+        "roofline": {
+            "kernel": "bwd_kernel (main backward)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_entry(flops),
+            "avg_launch_ms": round(main_avg, 5),
+            "algorithmic_flops_per_launch": flops,
+        },
+        "kernels_ms": {
+            "preprocess": round(float(pre_ms.mean()), 5),
+            "main": round(main_avg, 5),
+            "postprocess": round(float(post_ms.mean()), 5),
+            "step_events": round(float(step_ms.mean()), 5),
+        },
+        "hbm_GBps": {
+            "preprocess": round(pre_bytes / (pre_ms.mean() * 1e-3) / 1e9, 1),
+            "postprocess": round(post_bytes / (post_ms.mean() * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+        },
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(p, x, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (BackwardPlan.run: preprocess -> main -> postprocess).
+
+The small workloads (fp32 B1 H2 S128 D64 and bf16 causal B2 H8 S1024 D64) are
+compared element by element in full.  For the large ones the oracle computes
+sampled (sequence, kv-head) groups one by one: their O and LSE come from the
+oracle forward (written into the device buffers, rounded to bf16 / fp32),
+every other head uses the library forward, and the sampled heads' dQ, dK and
+dV are compared with the oracle backward.  Every head is also checked against
+the identity sum_j dV_j = sum_i dO_i (rows of P sum to one), which holds at any
+size.  The deterministic mode is checked bit for bit across repeated runs."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from _harness import TOL, assert_close, rel_err, round_like, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def setup(p):
+    x = datagen.draw(p)
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(v).to(dt).cuda() for k, v in x.items()}
+    kw, cu = {}, (None, None)
+    if p.varlen:
+        cu = p.cu_seqlens()
+        kw = dict(cu_seqlens_q=torch.from_numpy(cu[0]).cuda(), cu_seqlens_k=torch.from_numpy(cu[1]).cuda(),
+                  max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
+    return x, dev, kw, cu
+
+
+def run_backward(p, dev, o, lse, kw, deterministic=None):
+    from exact_attention_backward_amd import api
+    det = p.deterministic if deterministic is None else deterministic
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, det, **kw)
+    dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+    plan.run(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv)
+    torch.cuda.synchronize()
+    if det:
+        assert plan.error_flag() == 0
+    return dq, dk, dv
+
+
+def sampled_check(p, samples, deterministic=None, repeats=1):
+    """samples: list of (sequence, kv_head)."""
+    from exact_attention_backward_amd import api
+    x, dev, kw, cu = setup(p)
+    print(f"{p.name}: inputs ready", flush=True)
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, **kw)
+    torch.cuda.synchronize()
+    g = p.heads_q // p.heads_kv
+    ranges = []
+    for b, hk in samples:
+        if p.varlen:
+            q0, q1 = int(cu[0][b]), int(cu[0][b + 1])
+        else:
+            q0, q1 = b * p.seqlen_q, (b + 1) * p.seqlen_q
+        ranges.append((q0, q1))
+        fw = oracle.group_forward(x["q"], x["k"], x["v"], p.scale, p.causal, b, hk, *cu)
+        for h, (oh, lh) in fw.items():
+            oh = round_like(oh, p.dtype).astype(np.float32)
+            lh = lh.astype(np.float32)
+            if p.varlen:
+                o[q0:q1, h] = torch.from_numpy(oh).to(o.dtype).cuda()
+                lse[h, q0:q1] = torch.from_numpy(lh).cuda()
+            else:
+                o[b, :, h] = torch.from_numpy(oh).to(o.dtype).cuda()
+                lse[b, h] = torch.from_numpy(lh).cuda()
+    torch.cuda.synchronize()
+    outs = [run_backward(p, dev, o, lse, kw, deterministic) for _ in range(repeats)]
+    print(f"{p.name}: backward done", flush=True)
+    for rep in outs[1:]:
+        for a, bb in zip(outs[0], rep):
+            assert torch.equal(a.view(torch.int16), bb.view(torch.int16)), "deterministic mode not reproducible"
+    dq, dk, dv = outs[0]
+    o_h = to_host(o)
+    lse_h = lse.cpu().numpy().astype(np.float64)
+    for (b, hk), (q0, q1) in zip(samples, ranges):
+        rdq, rdk, rdv = oracle.group_backward(x["q"], x["k"], x["v"], o_h, x["do"], lse_h, p.scale, p.causal, b, hk,
+                                              *cu)
+        if p.varlen:
+            k0, k1 = int(cu[1][b]), int(cu[1][b + 1])
+            gk, gv = to_host(dk[k0:k1, hk]), to_host(dv[k0:k1, hk])
+            gq = {h: to_host(dq[q0:q1, h]) for h in rdq}
+        else:
+            gk, gv = to_host(dk[b, :, hk]), to_host(dv[b, :, hk])
+            gq = {h: to_host(dq[b, :, h]) for h in rdq}
+        errs = {"dK": rel_err(gk, rdk), "dV": rel_err(gv, rdv)}
+        errs.update({f"dQ[h{h}]": rel_err(gq[h], rdq[h]) for h in rdq})
+        print(f"{p.name} seq {b} kv-head {hk}: {errs}", flush=True)
+        for n, e in errs.items():
+            assert e <= TOL[p.dtype], f"{n}: {e:.3e}"
+    # sum_j dV_j = sum of dO over rows that see a key, for every (sequence, kv-head)
+    dv_h, do_h = to_host(dv), x["do"].astype(np.float64)
+    if p.varlen:
+        for b in range(p.batch):
+            q0, q1 = int(cu[0][b]), int(cu[0][b + 1])
+            k0, k1 = int(cu[1][b]), int(cu[1][b + 1])
+            lhs = dv_h[k0:k1].sum(axis=0)                                  # [Hkv, D]
+            rhs = do_h[q0:q1].reshape(q1 - q0, p.heads_kv, g, p.head_dim).sum(axis=(0, 2))
+            assert rel_err(lhs, rhs) <= TOL[p.dtype]
+    else:
+        lhs = dv_h.sum(axis=1)                                             # [B, Hkv, D]
+        rhs = do_h.reshape(p.batch, p.seqlen_q, p.heads_kv, g, p.head_dim).sum(axis=(1, 3))
+        assert rel_err(lhs, rhs) <= TOL[p.dtype]
+
+
+def test_fp32_workload_full():
+    p = datagen.workload("c1")
+    x, dev, kw, cu = setup(p)
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], p.scale, p.causal)
+    o32, lse32 = o.astype(np.float32), lse.astype(np.float32)
+    dq, dk, dv = run_backward(p, dev, torch.from_numpy(o32).cuda(), torch.from_numpy(lse32).cuda(), kw)
+    rdq, rdk, rdv = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, p.scale, p.causal)
+    for n, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert_close(n, to_host(gg), r, "f32")
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_bf16_causal_d64_workload_full(deterministic):
+    p = datagen.workload("c2", deterministic=deterministic)
+    x, dev, kw, cu = setup(p)
+    o, lse = oracle.forward(x["q"], x["k"], x["v"], p.scale, p.causal)
+    o = round_like(o, "bf16")
+    lse = lse.astype(np.float32).astype(np.float64)
+    O = to_dev(o, "bf16")
+    L = torch.from_numpy(lse.astype(np.float32)).cuda()
+    reps = [run_backward(p, dev, O, L, kw) for _ in range(3 if deterministic else 1)]
+    for rep in reps[1:]:
+        for a, bb in zip(reps[0], rep):
+            assert torch.equal(a.view(torch.int16), bb.view(torch.int16))
+    dq, dk, dv = reps[0]
+    rdq, rdk, rdv = oracle.backward(x["q"], x["k"], x["v"], o, x["do"], lse, p.scale, p.causal)
+    for n, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert_close(n, to_host(gg), r, "bf16")
+
+
+def test_headline_causal_sampled():
+    sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)])
+
+
+def test_headline_noncausal_sampled():
+    sampled_check(datagen.workload("c3nc"), [(1, 7)])
+
+
+def test_varlen_sampled():
+    p = datagen.workload("c4")
+    longest = int(np.argmax(p.lengths_q))
+    shortest = int(np.argmin(p.lengths_q))
+    sampled_check(p, [(shortest, 0), (longest, 31)])
+
+
+def test_gqa_atomic_sampled():
+    sampled_check(datagen.workload("c5"), [(0, 0)])
+
+
+def test_gqa_deterministic_sampled_and_reproducible():
+    sampled_check(datagen.workload("c5", deterministic=True), [(0, 7)], repeats=3)
