@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
-    ap.add_argument("--cpu-heads", type=int, default=64, help="(sequence 0) heads of the workload in the CPU sample")
+    ap.add_argument("--cpu-pairs", type=int, default=64, help="(sequence, head) pairs in the CPU oracle sample")
     return ap.parse_args()
 
 
@@ -61,9 +61,10 @@ def traffic_entry(per_launch_flops):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(p, x, n_heads):
-    """The fp64 oracle backward on the first n_heads (sequence 0) of the
-    workload, given O and LSE from the oracle forward (not timed)."""
+def cpu_baseline(p, x, n_pairs):
+    """The fp64 oracle backward on the first n_pairs (sequence, q-head) pairs
+    of the workload (sequence-major), each at full length, given O and LSE
+    from the oracle forward (not timed)."""
     import numpy as np
     import oracle
     try:
@@ -71,18 +72,21 @@ def cpu_baseline(p, x, n_heads):
         threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    n_heads = max(1, min(n_heads, p.heads_q))
+    total = p.batch * p.heads_q
+    n_pairs = max(1, min(n_pairs, total))
     g = p.heads_q // p.heads_kv
+    cq, _ = p.cu_seqlens()
     elapsed, flops = 0.0, 0.0
-    for h in range(n_heads):
+    for idx in range(n_pairs):
+        b, h = divmod(idx, p.heads_q)
         if p.varlen:
-            L = p.lengths_q[0]
-            q, do = x["q"][:L, h], x["do"][:L, h]
-            k, v = x["k"][:L, h // g], x["v"][:L, h // g]
-            sq = sk = L
+            q0, q1 = int(cq[b]), int(cq[b + 1])
+            q, do = x["q"][q0:q1, h], x["do"][q0:q1, h]
+            k, v = x["k"][q0:q1, h // g], x["v"][q0:q1, h // g]
+            sq = sk = q1 - q0
         else:
-            q, do = x["q"][0, :, h], x["do"][0, :, h]
-            k, v = x["k"][0, :, h // g], x["v"][0, :, h // g]
+            q, do = x["q"][b, :, h], x["do"][b, :, h]
+            k, v = x["k"][b, :, h // g], x["v"][b, :, h // g]
             sq, sk = p.seqlen_q, p.seqlen_k
         o, lse = oracle.head_forward(q, k, v, p.scale, p.causal)
         t0 = time.perf_counter()
@@ -95,8 +99,8 @@ def cpu_baseline(p, x, n_heads):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle backward of {n_heads} of the {p.batch * p.heads_q} (sequence, head) "
-                  f"pairs (sequence 0, heads 0..{n_heads - 1}) at full length; {elapsed:.1f} s",
+        "sample": f"fp64 numpy oracle backward of {n_pairs} of the workload's {total} (sequence, head) pairs "
+                  f"at full length (O, LSE from the oracle forward, untimed); {elapsed:.1f} s of CPU time",
         "seconds": elapsed,
     }
 
@@ -221,7 +225,7 @@ def main():
         },
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(p, x, args.cpu_heads)
+        out["cpu_baseline"] = cpu_baseline(p, x, args.cpu_pairs)
     print(json.dumps(out), flush=True)
 
 

@@ -24,6 +24,9 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-munsafe-fp-atomics",
+    # MFMA accumulators in VGPRs: keeps the loop-carried dK/dV accumulators
+    # from being copied between register files every iteration
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

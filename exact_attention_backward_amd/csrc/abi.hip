@@ -92,7 +92,7 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
         return ATTN_ERR_MISALIGNED;
     FwdArgs a{q, k, v, o, lse, s->cu_seqlens_q, s->cu_seqlens_k, s->batch, s->num_heads_q, s->num_heads_kv,
               s->seqlen_q, s->seqlen_k, s->total_q, s->total_k, s->softmax_scale};
-    hipGetLastError();
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_fwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
@@ -106,7 +106,7 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
     const size_t need = workspace_bytes(s);
     if (workspace_size < need) return ATTN_ERR_BAD_SHAPE;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipGetLastError();
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_fill_zero(workspace, need, hs);
     PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s)};
     launch_preprocess(a, s->dtype, s->head_dim, hs);
@@ -148,7 +148,7 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.nblk_m = nblk_m(s);
     a.scale = s->softmax_scale;
     a.deterministic = s->deterministic;
-    hipGetLastError();
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
@@ -162,7 +162,7 @@ int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
                s->seqlen_q, s->total_q, varlen(s), scale};
-    hipGetLastError();
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_postprocess(a, s->dtype, s->head_dim, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }

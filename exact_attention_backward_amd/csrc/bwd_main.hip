@@ -24,26 +24,28 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = kBwdBlockN;
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X
 
 template <class T, int HD>
 struct BwdCfg {
-    static constexpr int BM = (sizeof(T) == 4 && HD == 128) ? 32 : 64;   // query rows per tile
+    static constexpr int BM = HD == 128 ? 32 : 64;   // query rows per tile
     static constexpr int ROWB = HD * (int)sizeof(T);                       // LDS bytes per Q/dO/K row
     static constexpr int DSROWB = BM * (int)sizeof(T);                     // LDS bytes per dS^T row
     static constexpr int TILE = BM * ROWB;
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_DO = TILE;
-    static constexpr int OFF_DS = 2 * TILE;
-    static constexpr int OFF_LSE = OFF_DS + kBN * DSROWB;
-    static constexpr int OFF_DL = OFF_LSE + BM * 4;
-    static constexpr int LOOP_BYTES = OFF_DL + BM * 4;
-    static constexpr int K_BYTES = kBN * ROWB;
-    static constexpr int LDS_BYTES = LOOP_BYTES > K_BYTES ? LOOP_BYTES : K_BYTES;
+    // LDS map: resident K tile | two buffers of (Q, dO, LSE, D) | dS^T
+    static constexpr int OFF_K = 0;
+    static constexpr int BUF_Q = 0, BUF_DO = TILE, BUF_LSE = 2 * TILE, BUF_DL = 2 * TILE + BM * 4;
+    static constexpr int BUF_BYTES = 2 * TILE + 2 * BM * 4;
+    static constexpr int OFF_BUF = kBN * ROWB;
+    static constexpr int OFF_DS = OFF_BUF + 2 * BUF_BYTES;
+    static constexpr int LDS_BYTES = OFF_DS + kBN * DSROWB;
     static constexpr int NC = HD / 16;     // 16-wide chunks of the head dim
     static constexpr int NMB = BM / 32;    // 32-row blocks of a query tile
     static constexpr int NDB = HD / 32;    // 32-column blocks of the head dim
@@ -52,6 +54,7 @@ struct BwdCfg {
     static constexpr int DQB = NMB * NDB / kWaves;   // dQ 32x32 blocks per wave
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(NMB * NDB % kWaves == 0 && kWaves % NDB == 0, "dQ block split");
+    static_assert(BM <= 64, "one load instruction per LSE/D tile");
 };
 
 // --------------------------------------------------------------------------
@@ -118,7 +121,9 @@ __device__ __forceinline__ typename Elem<T>::op_t load_op_global(const T* p, boo
 }
 
 // Stage NROWS rows (row0 ..) of a global [rows, stride] tensor into a swizzled
-// LDS tile; rows at or past `valid` are written as zeros.
+// LDS tile; rows at or past `valid` (>= 1) are written as zeros.  The loads
+// are unconditional (the row index is clamped into range) so that all of them
+// issue back to back and their latencies overlap.
 template <class T, int ROWB, int NROWS>
 __device__ __forceinline__ void stage_rows(char* lds, const T* g, long long stride, int row0, int valid) {
     constexpr int CPR = ROWB / 16;
@@ -129,22 +134,53 @@ __device__ __forceinline__ void stage_rows(char* lds, const T* g, long long stri
     for (int t = 0; t < N; ++t) {
         const int c = threadIdx.x + t * kThreads;
         const int r = c / CPR, ch = c % CPR;
-        v[t] = u32x4{0u, 0u, 0u, 0u};
-        if (row0 + r < valid)
-            v[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(g + (long long)(row0 + r) * stride) +
-                                                   ch * 16);
+        const int rr = min(row0 + r, valid - 1);
+        v[t] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(g + (long long)rr * stride) + ch * 16);
     }
 #pragma unroll
     for (int t = 0; t < N; ++t) {
         const int c = threadIdx.x + t * kThreads;
         const int r = c / CPR, ch = c % CPR;
-        lds_write(lds, swz<ROWB>(r, ch * 16), v[t]);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        lds_write(lds, swz<ROWB>(r, ch * 16), row0 + r < valid ? v[t] : z);
     }
 }
 
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Per-lane plan for copying a tile of NROWS rows (row length ROWB bytes in
+// LDS, rows stride_bytes apart in HBM) into its swizzled LDS image with
+// buffer_load ... lds: instruction t of wave w fills the 1 KiB LDS segment
+// w + t * kWaves, lane l writing 16-byte slot l of it; the lane fetches
+// whichever global chunk the swizzle puts in that slot.  The per-lane byte
+// offsets are computed once; a tile copy is then one descriptor (built with
+// scalar instructions) and N buffer loads per wave.  Rows outside the
+// descriptor's range arrive as zeros.
+template <int ROWB, int NROWS>
+struct TileCopy {
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int N = NROWS * CPR / 64 / kWaves;
+    static_assert(NROWS * CPR % (64 * kWaves) == 0, "segment split");
+    int voff[N];
+    __device__ __forceinline__ void init(int w, int lane, int stride_bytes) {
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            const int slot = (w + t * kWaves) * 64 + lane;
+            const int r = slot / CPR;
+            const int c = (slot % CPR) ^ swz_key<ROWB>(r);
+            voff[t] = r * stride_bytes + c * 16;
+        }
+    }
+    __device__ __forceinline__ void issue(rsrc_t src, char* lds, int w) const {
+#pragma unroll
+        for (int t = 0; t < N; ++t) buffer_to_lds16(src, lds + (w + t * kWaves) * 1024, voff[t]);
+    }
+};
+
+// s_waitcnt vmcnt(0) alone (lgkmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // --------------------------------------------------------------------------
 // the kernel
@@ -154,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     using C = BwdCfg<T, HD>;
     using op_t = typename Elem<T>::op_t;
     constexpr int BM = C::BM;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -164,10 +200,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     // ---- which key tile: deterministic causal runs dispatch the highest key
     // tile of a (sequence, kv-head) first, since it reaches every query tile
     // first and so is first in the fixed summation order.
-    const int nb_lin = blockIdx.x % a.nblk_n;
-    const int rest = blockIdx.x / a.nblk_n;
-    const int hkv = rest % a.hkv;
-    const int b = rest / a.hkv;
+    // Workgroups are dispatched round-robin over the 8 XCDs (each with its
+    // own L2).  All key tiles of one (sequence, kv-head) are put on the same
+    // XCD, in consecutive dispatch slots, so the dQ tiles they all add into
+    // and the Q/dO tiles they all read stay in one L2.  Within a group the
+    // dispatch order still follows the key-tile order.
+    int grp, nb_lin;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+            grp = (slot / a.nblk_n) * kXcds + xcd;
+            nb_lin = slot % a.nblk_n;
+        } else {
+            grp = blockIdx.x / a.nblk_n;
+            nb_lin = blockIdx.x % a.nblk_n;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
     const int n = (CAUSAL && a.deterministic) ? a.nblk_n - 1 - nb_lin : nb_lin;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
     if (n * kBN >= si.len_k) return;
@@ -180,12 +231,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         const int first_row = n * kBN - off;   // first query row that sees key n*kBN
         m_begin = first_row > 0 ? first_row / BM : 0;
     }
+    const int n_m = max(m_end - m_begin, 0);
+    const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
     const int nblk_k = (si.len_k + kBN - 1) / kBN;
 
-    // ---- K and V of this wave's 32 keys in registers; K^T slice via LDS
     const long long kstride = (long long)a.hkv * HD;
+    const long long qstride = (long long)a.hq * HD;
     const T* kg = reinterpret_cast<const T*>(a.k) + (long long)si.k0 * kstride + (long long)hkv * HD;
     const T* vg = reinterpret_cast<const T*>(a.v) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    char* lk = smem + C::OFF_K;
+    char* lds_ds = smem + C::OFF_DS;
+
+    // query-side tile t (q-head hkv*G + t / n_m, query tile m_begin + t % n_m)
+    auto tile_head = [&](int t) { return hkv * G + t / n_m; };
+    auto tile_row0 = [&](int t) { return (m_begin + t % n_m) * BM; };
+    auto lse_base = [&](int hq) -> long long {
+        return varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
+    };
+    TileCopy<C::ROWB, BM> qcopy;
+    qcopy.init(w, lane, (int)(qstride * sizeof(T)));
+    auto issue_tile = [&](int t, char* buf) {
+        const int hq = tile_head(t), i0 = tile_row0(t);
+        const int rows = min(si.len_q - i0, BM);
+        const long long row_elem = ((long long)(si.q0 + i0) * a.hq + hq) * HD;
+        const unsigned bytes = (unsigned)(rows * qstride * sizeof(T));
+        qcopy.issue(make_rsrc(reinterpret_cast<const T*>(a.q) + row_elem, bytes), buf + C::BUF_Q, w);
+        qcopy.issue(make_rsrc(reinterpret_cast<const T*>(a.dout) + row_elem, bytes), buf + C::BUF_DO, w);
+        const long long lb = lse_base(hq) + i0;
+        if (w == 0 && lane < BM) buffer_to_lds4(make_rsrc(a.lse + lb, rows * 4), buf + C::BUF_LSE, lane * 4);
+        if (w == 1 && lane < BM) buffer_to_lds4(make_rsrc(a.delta + lb, rows * 4), buf + C::BUF_DL, lane * 4);
+    };
+
+    // ---- prologue: first query tile, the resident K tile, K/V rows of this wave
+    if (n_tiles > 0) issue_tile(0, smem + C::OFF_BUF);
+    {
+        TileCopy<C::ROWB, kBN> kcopy;
+        kcopy.init(w, lane, (int)(kstride * sizeof(T)));
+        const int rows = min(si.len_k - n * kBN, kBN);
+        kcopy.issue(make_rsrc(kg + (long long)n * kBN * kstride, (unsigned)(rows * kstride * sizeof(T))), lk, w);
+    }
     op_t kreg[C::NC], vreg[C::NC];
     {
         const int j = n * kBN + 32 * w + l32;
@@ -196,16 +280,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             vreg[c] = load_op_global<T>(vg + (long long)j * kstride + 16 * c + 8 * h, ok);
         }
     }
-    stage_rows<T, C::ROWB, kBN>(smem, kg, kstride, n * kBN, si.len_k);
+    wait_vmem();
     __syncthreads();
-    // dQ blocks of this wave: column block db_w, row blocks mb_w0 + k * (kWaves / NDB)
+    // dQ blocks of this wave: column block db_w, row blocks mb_w0 + x * (kWaves / NDB)
     const int db_w = w % C::NDB;
     const int mb_w0 = w / C::NDB;
-    op_t ktreg[C::NJC];
-#pragma unroll
-    for (int c = 0; c < C::NJC; ++c)
-        ktreg[c] = read_op_col<T, C::ROWB>(smem, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * db_w, lane);
-    __syncthreads();
 
     f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
@@ -218,186 +297,202 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     }
 
     const float scale2 = a.scale * kLog2e;
-    const long long qstride = (long long)a.hq * HD;
-    char* lq = smem + C::OFF_Q;
-    char* ldo = smem + C::OFF_DO;
-    char* lds_ds = smem + C::OFF_DS;
-    float* llse = reinterpret_cast<float*>(smem + C::OFF_LSE);
-    float* ldl = reinterpret_cast<float*>(smem + C::OFF_DL);
+    const int j = n * kBN + 32 * w + l32;   // this lane's key (column of S)
 
-    for (int g = 0; g < G; ++g) {
-        const int hq = hkv * G + g;
-        const T* qg = reinterpret_cast<const T*>(a.q) + (long long)si.q0 * qstride + (long long)hq * HD;
-        const T* dog = reinterpret_cast<const T*>(a.dout) + (long long)si.q0 * qstride + (long long)hq * HD;
-        const long long row0 = varlen ? (long long)hq * a.total_q + si.q0
-                                      : ((long long)b * a.hq + hq) * a.seqlen_q;
-        const float* lse_g = a.lse + row0;
-        const float* dl_g = a.delta + row0;
-        float* dqa = a.dq_acc + row0 * HD;
-        int* sem_row = a.sem + ((long long)b * a.hq + hq) * a.nblk_m;
+    for (int t = 0; t < n_tiles; ++t) {
+        char* buf = smem + C::OFF_BUF + (t & 1) * C::BUF_BYTES;
+        char* nbuf = smem + C::OFF_BUF + ((t + 1) & 1) * C::BUF_BYTES;
+        const int hq = tile_head(t);
+        const int i0 = tile_row0(t);
+        const int m = i0 / BM;
+        // all waves are done with the other buffer and with dS^T of tile t-1;
+        // this tile's data has landed (each wave waited for its own copies)
+        __syncthreads();
+        if (t + 1 < n_tiles) issue_tile(t + 1, nbuf);
+        const char* lq = buf + C::BUF_Q;
+        const char* ldo = buf + C::BUF_DO;
+        const float* llse = reinterpret_cast<const float*>(buf + C::BUF_LSE);
+        const float* ldl = reinterpret_cast<const float*>(buf + C::BUF_DL);
 
-        for (int m = m_begin; m < m_end; ++m) {
-            const int i0 = m * BM;
-            __syncthreads();   // previous tile's LDS reads are done
-            stage_rows<T, C::ROWB, BM>(lq, qg, qstride, i0, si.len_q);
-            stage_rows<T, C::ROWB, BM>(ldo, dog, qstride, i0, si.len_q);
-            if (threadIdx.x < BM) {
-                const int i = i0 + threadIdx.x;
-                float l2 = 0.f, dl = 0.f;
-                if (i < si.len_q) {
-                    const float lse = lse_g[i];
-                    l2 = lse == -INFINITY ? 0.f : lse * kLog2e;
-                    dl = dl_g[i];
-                }
-                llse[threadIdx.x] = l2;
-                ldl[threadIdx.x] = dl;
+        // per-row key limits: key j is visible to row i iff j < lim(i)
+        const bool edge = !((i0 + BM <= si.len_q) && (n * kBN + kBN <= si.len_k) &&
+                            (!CAUSAL || n * kBN + kBN - 1 <= i0 + off));
+
+        // ---- stages 1 and 4: S = Q K^T and dP = dO V^T for this wave's keys
+        f32x16 s[C::NMB], dp[C::NMB];
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) {
+            op_t aq[C::NC], ado[C::NC];
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c) {
+                aq[c] = read_op_row<T, C::ROWB>(lq, 32 * mb + l32, 16 * c + 8 * h);
+                ado[c] = read_op_row<T, C::ROWB>(ldo, 32 * mb + l32, 16 * c + 8 * h);
             }
-            __syncthreads();
-
-            // ---- stages 1 and 4: S = Q K^T and dP = dO V^T for this wave's keys
-            f32x16 s[C::NMB], dp[C::NMB];
 #pragma unroll
-            for (int mb = 0; mb < C::NMB; ++mb) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    s[mb][v] = 0.f;
-                    dp[mb][v] = 0.f;
-                }
-#pragma unroll
-                for (int c = 0; c < C::NC; ++c) {
-                    const op_t aq = read_op_row<T, C::ROWB>(lq, 32 * mb + l32, 16 * c + 8 * h);
-                    mma16(s[mb], aq, kreg[c]);
-                    const op_t ado = read_op_row<T, C::ROWB>(ldo, 32 * mb + l32, 16 * c + 8 * h);
-                    mma16(dp[mb], ado, vreg[c]);
-                }
+            for (int v = 0; v < 16; ++v) {
+                s[mb][v] = 0.f;
+                dp[mb][v] = 0.f;
             }
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c) {
+                mma16(s[mb], aq[c], kreg[c]);
+                mma16(dp[mb], ado[c], vreg[c]);
+            }
+        }
 
-            // ---- stages 2 and 5: P = exp2(S s log2e - LSE log2e); dS = P (dP - D)
-            const bool edge = !((i0 + BM <= si.len_q) && (n * kBN + kBN <= si.len_k) &&
-                                (!CAUSAL || n * kBN + kBN - 1 <= i0 + off));
-            const int j = n * kBN + 32 * w + l32;
+        // ---- stages 2 and 5: P = exp2(S s log2e - LSE log2e); dS = P (dP - D).
+        // Only edge tiles test visibility (key j is visible to row i iff
+        // j < lim(i)); the branch is uniform.
+        auto softmax_grad = [&](auto masked) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int r = 32 * mb + 8 * q4 + 4 * h;
-                    const f32x4 l2 = *reinterpret_cast<const f32x4*>(llse + r);
+                    const f32x4 lse = *reinterpret_cast<const f32x4*>(llse + r);
                     const f32x4 dl = *reinterpret_cast<const f32x4*>(ldl + r);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * q4 + e;
-                        float p = __builtin_amdgcn_exp2f(s[mb][v] * scale2 - l2[e]);
-                        if (edge) {
+                        const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
+                        float p = __builtin_amdgcn_exp2f(s[mb][v] * scale2 - l2);
+                        if constexpr (decltype(masked)::value) {
                             const int i = i0 + r + e;
-                            const bool vis = i < si.len_q && j < si.len_k && (!CAUSAL || j <= i + off);
-                            p = vis ? p : 0.f;
+                            const int lim = i < si.len_q ? (CAUSAL ? min(si.len_k, i + off + 1) : si.len_k) : 0;
+                            p = j < lim ? p : 0.f;
                         }
                         s[mb][v] = p;
                         dp[mb][v] = p * (dp[mb][v] - dl[e]);
                     }
                 }
             }
+        };
+        if (edge)
+            softmax_grad(std::true_type{});
+        else
+            softmax_grad(std::false_type{});
 
-            // ---- stages 3 and 6: dV += P^T dO, dK += dS^T Q
+        // ---- stages 3 and 6: dV += P^T dO, dK += dS^T Q
 #pragma unroll
-            for (int c = 0; c < C::NIC; ++c) {
-                const int mb = c >> 1, vb = 8 * (c & 1);
-                op_t pa, dsa;
-                float tp[8], td[8];
+        for (int c = 0; c < C::NIC; ++c) {
+            const int mb = c >> 1, vb = 8 * (c & 1);
+            op_t pa, dsa;
+            float tp[8], td[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    tp[t] = s[mb][vb + t];
-                    td[t] = dp[mb][vb + t];
-                }
-                to_op(pa, tp);
-                to_op(dsa, td);
-                const int r1 = 16 * c + 4 * h, r2 = 16 * c + 8 + 4 * h;
+            for (int u = 0; u < 8; ++u) {
+                tp[u] = s[mb][vb + u];
+                td[u] = dp[mb][vb + u];
+            }
+            to_op(pa, tp);
+            to_op(dsa, td);
+            const int r1 = 16 * c + 4 * h, r2 = 16 * c + 8 + 4 * h;
+            op_t bdo[C::NDB], bq[C::NDB];
 #pragma unroll
-                for (int d = 0; d < C::NDB; ++d) {
-                    const op_t bdo = read_op_col<T, C::ROWB>(ldo, r1, r2, 32 * d, lane);
-                    mma16(dv[d], pa, bdo);
-                    const op_t bq = read_op_col<T, C::ROWB>(lq, r1, r2, 32 * d, lane);
-                    mma16(dk[d], dsa, bq);
+            for (int d = 0; d < C::NDB; ++d) {
+                bdo[d] = read_op_col<T, C::ROWB>(ldo, r1, r2, 32 * d, lane);
+                bq[d] = read_op_col<T, C::ROWB>(lq, r1, r2, 32 * d, lane);
+            }
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) {
+                mma16(dv[d], pa, bdo[d]);
+                mma16(dk[d], dsa, bq[d]);
+            }
+        }
+
+        // ---- dS^T to LDS (row = key, column = query row)
+        {
+            const int jr = 32 * w + l32;
+#pragma unroll
+            for (int mb = 0; mb < C::NMB; ++mb) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int col = 32 * mb + 8 * q4 + 4 * h;
+                    if constexpr (sizeof(T) == 2) {
+                        const u32x2 wv = {pack_bf16x2(dp[mb][4 * q4], dp[mb][4 * q4 + 1]),
+                                          pack_bf16x2(dp[mb][4 * q4 + 2], dp[mb][4 * q4 + 3])};
+                        lds_write(lds_ds, swz<C::DSROWB>(jr, col * 2), wv);
+                    } else {
+                        const f32x4 wv = {dp[mb][4 * q4], dp[mb][4 * q4 + 1], dp[mb][4 * q4 + 2],
+                                          dp[mb][4 * q4 + 3]};
+                        lds_write(lds_ds, swz<C::DSROWB>(jr, col * 4), wv);
+                    }
                 }
             }
+        }
+        __syncthreads();
 
-            // ---- dS^T to LDS (row = key, column = query row)
-            {
-                const int jr = 32 * w + l32;
+        // ---- stage 7: dQ tile = dS K for this wave's blocks
+        f32x16 dq[C::DQB];
 #pragma unroll
-                for (int mb = 0; mb < C::NMB; ++mb) {
+        for (int x = 0; x < C::DQB; ++x) {
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int col = 32 * mb + 8 * q4 + 4 * h;
-                        if constexpr (sizeof(T) == 2) {
-                            const u32x2 wv = {pack_bf16x2(dp[mb][4 * q4], dp[mb][4 * q4 + 1]),
-                                              pack_bf16x2(dp[mb][4 * q4 + 2], dp[mb][4 * q4 + 3])};
-                            lds_write(lds_ds, swz<C::DSROWB>(jr, col * 2), wv);
-                        } else {
-                            const f32x4 wv = {dp[mb][4 * q4], dp[mb][4 * q4 + 1], dp[mb][4 * q4 + 2],
-                                              dp[mb][4 * q4 + 3]};
-                            lds_write(lds_ds, swz<C::DSROWB>(jr, col * 4), wv);
-                        }
+            for (int v = 0; v < 16; ++v) dq[x][v] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < C::NJC; ++c) {
+            op_t ads[C::DQB];
+#pragma unroll
+            for (int x = 0; x < C::DQB; ++x) {
+                const int mb = mb_w0 + x * (kWaves / C::NDB);
+                ads[x] = read_op_col<T, C::DSROWB>(lds_ds, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * mb, lane);
+            }
+            const op_t kt = read_op_col<T, C::ROWB>(lk, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * db_w, lane);
+#pragma unroll
+            for (int x = 0; x < C::DQB; ++x) mma16(dq[x], ads[x], kt);
+        }
+
+        // ---- dQ accumulation: fp32 atomics, or in a fixed order per tile
+        const long long row0 = lse_base(hq);
+        float* dqa = a.dq_acc + row0 * HD;
+        int* sem = a.sem + ((long long)b * a.hq + hq) * a.nblk_m + m;
+        if (a.deterministic) {
+            int rank;
+            if (CAUSAL) {
+                const int x = (m + 1) * BM + off;
+                const int last = min(nblk_k - 1, (x + kBN - 1) / kBN - 1);
+                rank = last - n;
+            } else {
+                rank = n;
+            }
+            if (threadIdx.x == 0) {
+                int spins = 0;
+                while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != rank) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > (1 << 24)) {
+                        __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
                     }
                 }
             }
             __syncthreads();
-
-            // ---- stage 7: dQ tile = dS K for this wave's blocks
-            f32x16 dq[C::DQB];
+            __atomic_thread_fence(__ATOMIC_ACQUIRE);
+        }
+        {
+            float* dq_tile = dqa + (long long)i0 * HD;   // uniform base of this query tile
+            auto add_dq = [&](auto ragged) {
 #pragma unroll
-            for (int x = 0; x < C::DQB; ++x) {
-                const int mb = mb_w0 + x * (kWaves / C::NDB);
+                for (int x = 0; x < C::DQB; ++x) {
+                    const int mb = mb_w0 + x * (kWaves / C::NDB);
+                    const int col = 32 * db_w + l32;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) dq[x][v] = 0.f;
-#pragma unroll
-                for (int c = 0; c < C::NJC; ++c) {
-                    const op_t ads =
-                        read_op_col<T, C::DSROWB>(lds_ds, 16 * c + 8 * h, 16 * c + 8 * h + 4, 32 * mb, lane);
-                    mma16(dq[x], ads, ktreg[c]);
-                }
-            }
-
-            // ---- dQ accumulation: fp32 atomics, or in a fixed order per tile
-            int* sem = sem_row + m;
-            if (a.deterministic) {
-                int rank;
-                if (CAUSAL) {
-                    const int x = (m + 1) * BM + off;
-                    const int last = min(nblk_k - 1, (x + kBN - 1) / kBN - 1);
-                    rank = last - n;
-                } else {
-                    rank = n;
-                }
-                if (threadIdx.x == 0) {
-                    int spins = 0;
-                    while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != rank) {
-                        __builtin_amdgcn_s_sleep(2);
-                        if (++spins > (1 << 24)) {
-                            __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = 32 * mb + acc_row(v, h);
+                        const unsigned o = (unsigned)(r * HD + col);
+                        if (!decltype(ragged)::value || i0 + r < si.len_q) atomic_add_f32(dq_tile + o, dq[x][v]);
                     }
                 }
-                __syncthreads();
-                __atomic_thread_fence(__ATOMIC_ACQUIRE);
-            }
-#pragma unroll
-            for (int x = 0; x < C::DQB; ++x) {
-                const int mb = mb_w0 + x * (kWaves / C::NDB);
-                const int col = 32 * db_w + l32;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int i = i0 + 32 * mb + acc_row(v, h);
-                    if (i < si.len_q) atomic_add_f32(dqa + (long long)i * HD + col, dq[x][v]);
-                }
-            }
-            if (a.deterministic) {
-                __threadfence();
-                __syncthreads();
-                if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            };
+            if (i0 + BM <= si.len_q)
+                add_dq(std::false_type{});
+            else
+                add_dq(std::true_type{});
         }
+        if (a.deterministic) {
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmem();   // the next tile's copies (and this tile's atomics) are complete
     }
 
     // ---- epilogue: dK = s * sum dS^T Q, dV; rows past the sequence are not written
@@ -418,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 }
 
 int bwd_block_m(int dtype, int head_dim) {
-    if (dtype == ATTN_DTYPE_F32 && head_dim == 128) return BwdCfg<float, 128>::BM;
-    return 64;
+    if (head_dim == 128) return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 128>::BM : BwdCfg<bf16_t, 128>::BM;
+    return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 64>::BM : BwdCfg<bf16_t, 64>::BM;
 }
 
 template <class T, int HD>

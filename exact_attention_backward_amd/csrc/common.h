@@ -85,15 +85,26 @@ __device__ __forceinline__ void to_op(f32x8& o, const float* x) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: row-major with 16-byte chunks XOR-swizzled by the row index, so
-// that 16-byte reads of one column chunk across consecutive rows, and the
-// 8-byte transposing reads, fall in different banks.
+// LDS tiles: row-major, 16-byte chunks XOR-swizzled by a function of the row.
+// LDS serves 256 bytes per cycle from 64 four-byte banks, so a 16-byte chunk
+// slot is (row * ROW_BYTES / 16 + chunk) mod 16.  The swizzle keeps both
+// access patterns of the kernels conflict-free:
+//  - 16-byte reads of one logical chunk by 16 consecutive rows;
+//  - transposing reads of 4 consecutive rows (starting at a multiple of 4)
+//    by 4 consecutive chunks (a 64-byte column group).
+// A plain XOR with the low row bits only permutes chunks inside a 64-byte
+// group and leaves the second pattern 4-way conflicted.
 // ---------------------------------------------------------------------------
 template <int ROW_BYTES>
-__device__ __forceinline__ int swz(int row, int byte) {
+__device__ __forceinline__ int swz_key(int row) {
     constexpr int kChunks = ROW_BYTES / 16;
-    constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
-    return row * ROW_BYTES + ((((byte >> 4) ^ (row & kMask))) << 4) + (byte & 15);
+    if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (kChunks == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else return (row >> 2) & (kChunks - 1);
+}
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row, int byte) {
+    return row * ROW_BYTES + (((byte >> 4) ^ swz_key<ROW_BYTES>(row)) << 4) + (byte & 15);
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
@@ -113,6 +124,32 @@ __device__ __forceinline__ u32x4 lds_read16(const char* lds_base, int byte_off) 
 template <class V>
 __device__ __forceinline__ void lds_write(char* lds_base, int byte_off, const V& v) {
     *reinterpret_cast<V*>(lds_base + byte_off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// buffer resources: base address, byte range and the gfx9 raw-buffer format
+// word.  Loads past the range return zeros and stores/atomics past it are
+// dropped; only the per-lane offset and the instruction offset take part in
+// that check, so every variable part of an address goes into the descriptor
+// base or the per-lane offset, never into the scalar offset.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void buffer_to_lds16(rsrc_t r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+// 4 bytes per lane from buffer offset voff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void buffer_to_lds4(rsrc_t r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_atomic_add(float v, rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
