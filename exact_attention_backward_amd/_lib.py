@@ -21,6 +21,9 @@ ATTN_ERR_HIP = 5
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
 
+ATTN_DQ_SEPARATE = 0
+ATTN_DQ_ATOMIC = 1
+
 EXPORTS = (
     "attn_status_string",
     "attn_bwd_workspace_bytes",
@@ -48,6 +51,7 @@ class AttnShape(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("dq_algo", ctypes.c_int32),
     ]
 
 

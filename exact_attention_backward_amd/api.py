@@ -41,9 +41,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC}
+
+
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-               max_seqlen_q=None, max_seqlen_k=None):
-    """attn_shape_t for the given tensors (the dtype is q's)."""
+               max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
+    """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
+    "separate" (query-stationary dQ pass, no atomics) or "atomic"."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -63,6 +67,7 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
+    s.dq_algo = DQ_ALGOS[dq_algo] if isinstance(dq_algo, str) else int(dq_algo)
     return s
 
 
@@ -114,9 +119,9 @@ class BackwardPlan:
     """
 
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-                 max_seqlen_q=None, max_seqlen_k=None):
+                 max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
-                                max_seqlen_q, max_seqlen_k)
+                                max_seqlen_q, max_seqlen_k, dq_algo)
         self._keep = (cu_seqlens_q, cu_seqlens_k)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
@@ -147,9 +152,10 @@ class BackwardPlan:
 
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-             max_seqlen_q=None, max_seqlen_k=None):
+             max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
     """Full backward: returns (dq, dk, dv)."""
-    plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                        dq_algo)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     plan.run(q, k, v, o, do, lse, dq, dk, dv)
     return dq, dk, dv

@@ -33,6 +33,7 @@ int validate_shape(const attn_shape_t* s) {
     if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
     if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
     if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
+    if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC) return ATTN_ERR_UNSUPPORTED;
     // element counts must stay addressable with 64-bit offsets and 32-bit row counts
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
@@ -107,7 +108,12 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
     if (workspace_size < need) return ATTN_ERR_BAD_SHAPE;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    launch_fill_zero(workspace, need, hs);
+    // the separate dQ pass overwrites every accumulator row; only the atomic
+    // modes add into it
+    if (s->dq_algo == ATTN_DQ_ATOMIC)
+        launch_fill_zero(workspace, need, hs);
+    else
+        launch_fill_zero(reinterpret_cast<char*>(workspace) + accum_bytes(s), need - accum_bytes(s), hs);
     PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s)};
     launch_preprocess(a, s->dtype, s->head_dim, hs);
     return check_launch();
@@ -149,7 +155,14 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.scale = s->softmax_scale;
     a.deterministic = s->deterministic;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const bool atomic = s->dq_algo == ATTN_DQ_ATOMIC;
+    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, atomic, hs);
+    if (!atomic) {
+        BwdArgs d = a;
+        d.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
+        launch_bwd_dq(d, s->dtype, s->head_dim, s->causal != 0, hs);
+    }
     return check_launch();
 }
 

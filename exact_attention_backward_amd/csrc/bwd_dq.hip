@@ -1,0 +1,325 @@
+// Query-stationary dQ pass of the attention backward for gfx950.
+//
+// One workgroup (4 waves) owns 128 query rows of one (sequence, q-head) and
+// loops over 64-key tiles of K and V, recomputing for each tile
+//   S^T  = K Q^T           (MFMA; K rows from LDS, Q rows of the wave in registers)
+//   dP^T = V dO^T          (MFMA; V rows from LDS, dO rows in registers)
+//   P    = exp2(S s log2e - LSE log2e),  dS = P (dP - D)
+//   dQ  += dS K            (MFMA; dS straight from the S^T registers, K^T via
+//                           transposing LDS reads)
+// and writes its dQ rows once, with plain stores, into the fp32 accumulator
+// (scaled and converted by the dQ postprocess).  This is the dQ half of the
+// per-tile work of the Composable Kernel pipeline page
+// "block_fmha_bwd_dq_dk_dv_pipeline_trload_kr_ktr_vr.hpp Source File" (stages
+// 1, 2, 4, 5, 7), scheduled over keys instead of over queries so that no two
+// workgroups add into the same dQ row: on MI355X fp32 atomics to device
+// memory are executed memory-side, at about 1.3 TB/s, which bounds the
+// key-stationary schedule's dQ accumulation far below the MFMA rate.
+//
+// Computing S^T (keys as rows) makes the lane of an accumulator own one query
+// row and hold 8 keys per 16-key slice, which is exactly the layout of the dQ
+// product's A operand (rows = queries, contraction over keys), so P and dS
+// never leave the registers.
+#include "common.h"
+#include "launch.h"
+
+#include <type_traits>
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;
+
+template <class T, int HD>
+struct DqCfg {
+    static constexpr int BQ = 32 * kWaves;   // query rows per workgroup
+    static constexpr int BN = 64;            // keys per K/V tile
+    static constexpr int ROWB = HD * (int)sizeof(T);
+    static constexpr int TILE = BN * ROWB;
+    static constexpr int BUF_K = 0, BUF_V = TILE;
+    static constexpr int BUF_BYTES = 2 * TILE;
+    static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+    static constexpr int NC = HD / 16;       // 16-wide chunks of the head dim
+    static constexpr int NDB = HD / 32;      // 32-column blocks of the head dim
+    static constexpr int NJB = BN / 32;      // 32-key blocks of a K tile
+    static constexpr int NJC = BN / 16;      // 16-key chunks of a K tile
+};
+
+template <class T, int HD>
+using DqOp = typename Elem<T>::op_t;
+
+// Row-major operand: lane gets M[row][col .. col+7].
+template <class T, int ROWB>
+__device__ __forceinline__ DqOp<T, 0> dq_read_row(const char* lds, int row, int col) {
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_bit_cast(bf16x8, lds_read16(lds, swz<ROWB>(row, col * 2)));
+    } else {
+        const f32x4 a = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4)));
+        const f32x4 b = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4 + 16)));
+        return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+}
+
+// Column operand: lane (l32) gets M[r1 + t][c0 + l32] and M[r2 + t][c0 + l32], t = 0..3.
+template <class T, int ROWB>
+__device__ __forceinline__ DqOp<T, 0> dq_read_col(const char* lds, int r1, int r2, int c0, int lane) {
+    if constexpr (sizeof(T) == 2) {
+        const int s = lane & 15;
+        const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+        const u32x2 x = lds_read_tr(lds, swz<ROWB>(r1 + (s >> 2), col * 2));
+        const u32x2 y = lds_read_tr(lds, swz<ROWB>(r2 + (s >> 2), col * 2));
+        const u32x4 w = {x[0], x[1], y[0], y[1]};
+        return __builtin_bit_cast(bf16x8, w);
+    } else {
+        const int col = c0 + (lane & 31);
+        f32x8 r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            r[t] = *reinterpret_cast<const float*>(lds + swz<ROWB>(r1 + t, col * 4));
+            r[4 + t] = *reinterpret_cast<const float*>(lds + swz<ROWB>(r2 + t, col * 4));
+        }
+        return r;
+    }
+}
+
+template <class T>
+__device__ __forceinline__ DqOp<T, 0> dq_load_global(const T* p, bool ok) {
+    if constexpr (sizeof(T) == 2) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ok) w = *reinterpret_cast<const u32x4*>(p);
+        return __builtin_bit_cast(bf16x8, w);
+    } else {
+        f32x8 r = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (ok) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+            r = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        }
+        return r;
+    }
+}
+
+// Per-lane plan of a K or V tile copy into its swizzled LDS image (see the
+// key-stationary kernel): each wave fills 1 KiB segments with buffer loads
+// whose lanes fetch the global chunk the swizzle puts in their slot.
+template <int ROWB, int NROWS>
+struct DqTileCopy {
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int N = NROWS * CPR / 64 / kWaves;
+    static_assert(NROWS * CPR % (64 * kWaves) == 0, "segment split");
+    int voff[N];
+    __device__ __forceinline__ void init(int w, int lane, int stride_bytes) {
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+            const int slot = (w + t * kWaves) * 64 + lane;
+            const int r = slot / CPR;
+            const int c = (slot % CPR) ^ swz_key<ROWB>(r);
+            voff[t] = r * stride_bytes + c * 16;
+        }
+    }
+    __device__ __forceinline__ void issue(i32x4 src, const char* lds, int w) const {
+#pragma unroll
+        for (int t = 0; t < N; ++t) dma_to_lds16(src, lds_addr(lds + (w + t * kWaves) * 1024), voff[t]);
+    }
+};
+
+__device__ __forceinline__ void dq_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace
+
+template <class T, int HD, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+    using C = DqCfg<T, HD>;
+    using op_t = typename Elem<T>::op_t;
+    constexpr int BQ = C::BQ, BN = C::BN;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- which query tile: all query tiles of all q-heads of one
+    // (sequence, kv-head) run on one XCD, so their K/V reads share an L2
+    const int G = a.hq / a.hkv;
+    const int per_group = a.nblk_m * G;          // workgroups of one (sequence, kv-head)
+    int grp, slot;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
+            grp = (s / per_group) * kXcds + xcd;
+            slot = s % per_group;
+        } else {
+            grp = blockIdx.x / per_group;
+            slot = blockIdx.x % per_group;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const int hq = hkv * G + slot / a.nblk_m;
+    // heaviest (last) query tiles first: under a causal mask they see the most keys
+    const int m = CAUSAL ? a.nblk_m - 1 - slot % a.nblk_m : slot % a.nblk_m;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    const int i0 = m * BQ;
+    if (i0 >= si.len_q) return;
+    const bool varlen = a.cu_q != nullptr;
+    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+
+    // keys any row of this tile can see
+    int key_end = si.len_k;
+    if (CAUSAL) key_end = min(key_end, min(i0 + BQ, si.len_q) - 1 + off + 1);
+    const int n_kt = key_end > 0 ? (key_end + BN - 1) / BN : 0;
+
+    const long long qstride = (long long)a.hq * HD;
+    const long long kstride = (long long)a.hkv * HD;
+    const T* kg = reinterpret_cast<const T*>(a.k) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    const T* vg = reinterpret_cast<const T*>(a.v) + (long long)si.k0 * kstride + (long long)hkv * HD;
+
+    DqTileCopy<C::ROWB, BN> kvcopy;
+    kvcopy.init(w, lane, (int)(kstride * sizeof(T)));
+    auto issue_tile = [&](int kt, char* buf) {
+        const int rows = min(si.len_k - kt * BN, BN);
+        const unsigned bytes = (unsigned)(rows * kstride * sizeof(T));
+        kvcopy.issue(rsrc_words(kg + (long long)kt * BN * kstride, bytes), buf + C::BUF_K, w);
+        kvcopy.issue(rsrc_words(vg + (long long)kt * BN * kstride, bytes), buf + C::BUF_V, w);
+    };
+    if (n_kt > 0) issue_tile(0, smem);
+
+    // ---- this lane's query row: Q and dO rows as MFMA B operands, LSE and D
+    const int i = i0 + 32 * w + l32;
+    const bool row_ok = i < si.len_q;
+    op_t qreg[C::NC], doreg[C::NC];
+    {
+        const T* qg = reinterpret_cast<const T*>(a.q) + ((long long)(si.q0 + i) * a.hq + hq) * HD;
+        const T* dog = reinterpret_cast<const T*>(a.dout) + ((long long)(si.q0 + i) * a.hq + hq) * HD;
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+            qreg[c] = dq_load_global<T>(qg + 16 * c + 8 * h, row_ok);
+            doreg[c] = dq_load_global<T>(dog + 16 * c + 8 * h, row_ok);
+        }
+    }
+    const long long row0 = varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
+    float l2 = 0.f, dl = 0.f;
+    if (row_ok) {
+        const float lse = a.lse[row0 + i];
+        l2 = lse == -INFINITY ? 0.f : lse * kLog2e;
+        dl = a.delta[row0 + i];
+    }
+    const float scale2 = a.scale * kLog2e;
+    // key j is visible to this lane's row iff j < lim
+    const int lim = row_ok ? (CAUSAL ? min(si.len_k, i + off + 1) : si.len_k) : 0;
+
+    f32x16 dq[C::NDB];
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dq[d][v] = 0.f;
+    }
+
+    dq_wait_vmem();
+    for (int kt = 0; kt < n_kt; ++kt) {
+        char* buf = smem + (kt & 1) * C::BUF_BYTES;
+        char* nbuf = smem + ((kt + 1) & 1) * C::BUF_BYTES;
+        __syncthreads();   // tile kt landed (each wave waited for its copies); tile kt-1 is no longer read
+        if (kt + 1 < n_kt) issue_tile(kt + 1, nbuf);
+        const char* lk = buf + C::BUF_K;
+        const char* lv = buf + C::BUF_V;
+        const int j0 = kt * BN;
+        const bool edge = !((j0 + BN <= si.len_k) && (i0 + BQ <= si.len_q) &&
+                            (!CAUSAL || j0 + BN - 1 <= i0 + off));
+
+        // ---- S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = this wave's queries)
+        f32x16 st[C::NJB], dpt[C::NJB];
+#pragma unroll
+        for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                st[jb][v] = 0.f;
+                dpt[jb][v] = 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c) {
+                const op_t ak = dq_read_row<T, C::ROWB>(lk, 32 * jb + l32, 16 * c + 8 * h);
+                const op_t av = dq_read_row<T, C::ROWB>(lv, 32 * jb + l32, 16 * c + 8 * h);
+                mma16(st[jb], ak, qreg[c]);
+                mma16(dpt[jb], av, doreg[c]);
+            }
+        }
+
+        // ---- P = exp2(S s log2e - LSE log2e), dS = P (dP - D); edge tiles test visibility
+        auto softmax_grad = [&](auto masked) {
+#pragma unroll
+            for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float p = __builtin_amdgcn_exp2f(st[jb][v] * scale2 - l2);
+                    if constexpr (decltype(masked)::value) {
+                        const int j = j0 + 32 * jb + acc_row(v, h);
+                        p = j < lim ? p : 0.f;
+                    }
+                    dpt[jb][v] = p * (dpt[jb][v] - dl);
+                }
+            }
+        };
+        if (edge)
+            softmax_grad(std::true_type{});
+        else
+            softmax_grad(std::false_type{});
+
+        // ---- dQ += dS K: A = dS (this lane's row, 8 keys per slice), B = K^T via transposing reads
+#pragma unroll
+        for (int c = 0; c < C::NJC; ++c) {
+            const int jb = c >> 1, vb = 8 * (c & 1);
+            op_t ads;
+            float td[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) td[u] = dpt[jb][vb + u];
+            to_op(ads, td);
+            const int r1 = 16 * c + 4 * h, r2 = 16 * c + 8 + 4 * h;
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) {
+                const op_t bk = dq_read_col<T, C::ROWB>(lk, r1, r2, 32 * d, lane);
+                mma16(dq[d], ads, bk);
+            }
+        }
+        dq_wait_vmem();   // the next tile's copies are complete
+    }
+
+    // ---- write this tile's dQ rows once (unscaled; the postprocess applies s)
+    float* dqa = a.dq_acc + (row0 + i0 + 32 * w) * HD;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = acc_row(v, h);
+            if (i0 + 32 * w + r < si.len_q) dqa[(long long)r * HD + 32 * d + l32] = dq[d][v];
+        }
+    }
+}
+
+template <class T, int HD>
+static void launch_dq_t(const BwdArgs& a, bool causal, hipStream_t st) {
+    const unsigned grid = (unsigned)(a.nblk_m * a.hq * a.batch);
+    if (causal)
+        bwd_dq_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
+    else
+        bwd_dq_kernel<T, HD, false><<<grid, kThreads, 0, st>>>(a);
+}
+
+int bwd_dq_block_m() { return 32 * kWaves; }
+
+void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) launch_dq_t<bf16_t, 64>(a, causal, st);
+        else launch_dq_t<bf16_t, 128>(a, causal, st);
+    } else {
+        if (hd == 64) launch_dq_t<float, 64>(a, causal, st);
+        else launch_dq_t<float, 128>(a, causal, st);
+    }
+}
+
+}  // namespace attn

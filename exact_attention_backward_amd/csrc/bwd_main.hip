@@ -177,15 +177,28 @@ struct TileCopy {
 #pragma unroll
         for (int t = 0; t < N; ++t) buffer_to_lds16(src, lds + (w + t * kWaves) * 1024, voff[t]);
     }
+    // untracked copies (see dma_to_lds16); returns the VMEM instructions issued
+    __device__ __forceinline__ void issue_untracked(i32x4 src, const char* lds, int w) const {
+#pragma unroll
+        for (int t = 0; t < N; ++t) dma_to_lds16(src, lds_addr(lds + (w + t * kWaves) * 1024), voff[t]);
+    }
 };
 
 // s_waitcnt vmcnt(0) alone (lgkmcnt and expcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recently issued VMEM operations are
+// complete (the counter retires in issue order).  gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // --------------------------------------------------------------------------
 // the kernel
 // --------------------------------------------------------------------------
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     using C = BwdCfg<T, HD>;
     using op_t = typename Elem<T>::op_t;
@@ -255,11 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         const int rows = min(si.len_q - i0, BM);
         const long long row_elem = ((long long)(si.q0 + i0) * a.hq + hq) * HD;
         const unsigned bytes = (unsigned)(rows * qstride * sizeof(T));
-        qcopy.issue(make_rsrc(reinterpret_cast<const T*>(a.q) + row_elem, bytes), buf + C::BUF_Q, w);
-        qcopy.issue(make_rsrc(reinterpret_cast<const T*>(a.dout) + row_elem, bytes), buf + C::BUF_DO, w);
+        qcopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.q) + row_elem, bytes), buf + C::BUF_Q, w);
+        qcopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.dout) + row_elem, bytes), buf + C::BUF_DO, w);
         const long long lb = lse_base(hq) + i0;
-        if (w == 0 && lane < BM) buffer_to_lds4(make_rsrc(a.lse + lb, rows * 4), buf + C::BUF_LSE, lane * 4);
-        if (w == 1 && lane < BM) buffer_to_lds4(make_rsrc(a.delta + lb, rows * 4), buf + C::BUF_DL, lane * 4);
+        if (w == 0 && lane < BM) dma_to_lds4(rsrc_words(a.lse + lb, rows * 4), lds_addr(buf + C::BUF_LSE), lane * 4);
+        if (w == 1 && lane < BM) dma_to_lds4(rsrc_words(a.delta + lb, rows * 4), lds_addr(buf + C::BUF_DL), lane * 4);
     };
 
     // ---- prologue: first query tile, the resident K tile, K/V rows of this wave
@@ -399,6 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             }
         }
 
+        if constexpr (DQ_ATOMIC) {
         // ---- dS^T to LDS (row = key, column = query row)
         {
             const int jr = 32 * w + l32;
@@ -492,7 +506,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             __syncthreads();
             if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
-        wait_vmem();   // the next tile's copies (and this tile's atomics) are complete
+        }
+        // the next tile's copies are complete; on full tiles of the atomic
+        // mode this tile's 16 * DQB atomics, issued after them, may still fly
+        if (DQ_ATOMIC && !a.deterministic && i0 + BM <= si.len_q)
+            wait_vmem_but<16 * C::DQB>();
+        else
+            wait_vmem();
     }
 
     // ---- epilogue: dK = s * sum dS^T Q, dV; rows past the sequence are not written
@@ -518,21 +538,24 @@ int bwd_block_m(int dtype, int head_dim) {
 }
 
 template <class T, int HD>
-static void launch_bwd_t(const BwdArgs& a, bool causal, hipStream_t st) {
+static void launch_bwd_t(const BwdArgs& a, bool causal, bool dq_atomic, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
-    if (causal)
-        bwd_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
-    else
-        bwd_kernel<T, HD, false><<<grid, kThreads, 0, st>>>(a);
+    if (causal) {
+        if (dq_atomic) bwd_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
+        else bwd_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
+    } else {
+        if (dq_atomic) bwd_kernel<T, HD, false, true><<<grid, kThreads, 0, st>>>(a);
+        else bwd_kernel<T, HD, false, false><<<grid, kThreads, 0, st>>>(a);
+    }
 }
 
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, bool dq_atomic, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, st);
-        else launch_bwd_t<bf16_t, 128>(a, causal, st);
+        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, dq_atomic, st);
+        else launch_bwd_t<bf16_t, 128>(a, causal, dq_atomic, st);
     } else {
-        if (hd == 64) launch_bwd_t<float, 64>(a, causal, st);
-        else launch_bwd_t<float, 128>(a, causal, st);
+        if (hd == 64) launch_bwd_t<float, 64>(a, causal, dq_atomic, st);
+        else launch_bwd_t<float, 128>(a, causal, dq_atomic, st);
     }
 }
 

@@ -152,6 +152,35 @@ __device__ __forceinline__ void buffer_atomic_add(float v, rsrc_t r, int voff) {
     __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, 0, 0);
 }
 
+// The same copies issued from inline assembly, for the main loop's prefetch.
+// The compiler's wait-count pass cannot tell which LDS bytes an LDS-DMA copy
+// writes, so after a tracked copy it waits for it before the next LDS read,
+// even one of a different buffer; that serialises the prefetch with the
+// compute it should overlap.  These copies are invisible to that pass: the
+// caller waits for them explicitly (vmcnt) before the barrier that publishes
+// the buffer.  Extra untracked VMEM operations only make the compiler's own
+// in-order vmcnt waits more conservative.  The descriptor words are
+// {base[31:0], base[47:32] (stride 0), byte range, raw-buffer format}.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
+    const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+    i32x4 r = {__builtin_amdgcn_readfirstlane((int)(unsigned)b),
+               __builtin_amdgcn_readfirstlane((int)((unsigned)(b >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+    return r;
+}
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(size_t)((__attribute__((address_space(3))) const char*)p));
+}
+__device__ __forceinline__ void dma_to_lds16(i32x4 r, unsigned lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
+
 // ---------------------------------------------------------------------------
 // problem geometry on the device
 // ---------------------------------------------------------------------------

@@ -67,7 +67,10 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st
 void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, bool dq_atomic, hipStream_t st);
+// query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
+void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+int bwd_dq_block_m();
 
 // ---------------------------------------------------------------------------
 // element access for the two I/O types

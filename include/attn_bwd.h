@@ -73,6 +73,19 @@ typedef enum attn_dtype {
     ATTN_DTYPE_BF16 = 1        /* bf16 I/O, bf16 MFMA operands, fp32 accumulation */
 } attn_dtype_t;
 
+/* How attn_bwd produces dQ (both reach the same result up to fp32 summation
+ * order; see attn_bwd).
+ *  ATTN_DQ_SEPARATE: a query-stationary second pass recomputes S and dP per
+ *    (query tile, key tile) and writes each dQ row once: no atomics, bitwise
+ *    reproducible; seven contractions per tile pair instead of five.
+ *  ATTN_DQ_ATOMIC: the key-stationary kernel adds dS K for each tile pair
+ *    into the fp32 accumulator with global atomics (with deterministic = 1,
+ *    in a fixed order per dQ tile). */
+typedef enum attn_dq_algo {
+    ATTN_DQ_SEPARATE = 0,
+    ATTN_DQ_ATOMIC = 1
+} attn_dq_algo_t;
+
 /* Problem description, passed by pointer and only read.  Plain old data. */
 typedef struct attn_shape {
     int32_t batch;           /* dense batch B, or number of sequences when varlen */
@@ -89,6 +102,7 @@ typedef struct attn_shape {
     int32_t causal;          /* 0 or 1 */
     int32_t deterministic;   /* 1: dQ summed in a fixed order, bitwise reproducible */
     int32_t dtype;           /* attn_dtype_t */
+    int32_t dq_algo;         /* attn_dq_algo_t: how attn_bwd accumulates dQ */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -109,21 +123,28 @@ int attn_fwd(const attn_shape_t* shape, const void* q, const void* k, const void
 
 /* Backward preprocess: D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d],
  * accumulated in fp32 (D is consumed, never shown, by the pipeline page's
- * stage 5).  Also zeroes the workspace, which attn_bwd accumulates into (the
- * zero-initialised accumulator contract of CollectiveEpilogueBwdGQA::store_zero).
+ * stage 5).  Also clears the workspace parts attn_bwd accumulates into (the
+ * zero-initialised accumulator contract of CollectiveEpilogueBwdGQA::store_zero):
+ * the ordering counters and status words always, the dQ accumulator for
+ * ATTN_DQ_ATOMIC (the separate pass overwrites it).
  * o, dout: inputs; delta: output [LSE layout]; workspace: output, at least
  * attn_bwd_workspace_bytes(shape) bytes (workspace_bytes says how many). */
 int attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* dout,
                         float* delta, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Main backward kernel.  Per K/V tile: recompute P = exp(s Q K^T - LSE),
- * dP = dO V^T, dS = P (dP - D); dV = P^T dO and dK = s dS^T Q are written to
- * dk/dv (fully overwritten, GQA groups summed, zero rows for keys no query
- * sees); dQ partials dS K are added in fp32 into the workspace accumulator,
- * with hardware atomics, or, when shape->deterministic, in a fixed order per
- * dQ tile so that repeated runs are bitwise identical.  The workspace must
- * have been cleared by attn_bwd_preprocess for this shape since the last
- * attn_bwd (running attn_bwd twice without it adds dQ twice).
+/* Main backward.  Per K/V tile (key-stationary kernel): recompute
+ * P = exp(s Q K^T - LSE), dP = dO V^T, dS = P (dP - D); dV = P^T dO and
+ * dK = s dS^T Q are written to dk/dv (fully overwritten, GQA groups summed,
+ * zero rows for keys no query sees).  dQ / s = dS K goes to the workspace's
+ * fp32 accumulator:
+ *  - shape->dq_algo == ATTN_DQ_SEPARATE: a second, query-stationary kernel
+ *    writes every accumulator row once (no atomics; bitwise reproducible
+ *    whatever shape->deterministic says);
+ *  - shape->dq_algo == ATTN_DQ_ATOMIC: the partials are added with fp32
+ *    atomics, or, when shape->deterministic, in a fixed order per dQ tile so
+ *    that repeated runs are bitwise identical.  The accumulator must then
+ *    have been cleared by attn_bwd_preprocess for this shape since the last
+ *    attn_bwd (running attn_bwd twice without it adds dQ twice).
  * q, k, v, dout, lse, delta: inputs; dk, dv: outputs; workspace: in/out. */
 int attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
              const void* dout, const float* lse, const float* delta,

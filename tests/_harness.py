@@ -79,14 +79,14 @@ class Run:
         d = self.dev
         return api.forward(d["q"], d["k"], d["v"], self.p.scale, self.p.causal, **self.kw())
 
-    def plan(self, deterministic=None):
+    def plan(self, deterministic=None, dq_algo="separate"):
         d = self.dev
         det = self.p.deterministic if deterministic is None else deterministic
-        return api.BackwardPlan(d["q"], d["k"], self.p.scale, self.p.causal, det, **self.kw())
+        return api.BackwardPlan(d["q"], d["k"], self.p.scale, self.p.causal, det, dq_algo=dq_algo, **self.kw())
 
-    def gpu_backward(self, deterministic=None, plan=None):
+    def gpu_backward(self, deterministic=None, plan=None, dq_algo="separate"):
         d = self.dev
-        plan = plan or self.plan(deterministic)
+        plan = plan or self.plan(deterministic, dq_algo)
         dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
         plan.run(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq, dk, dv)
         torch.cuda.synchronize()

@@ -33,10 +33,10 @@ def setup(p):
     return x, dev, kw, cu
 
 
-def run_backward(p, dev, o, lse, kw, deterministic=None):
+def run_backward(p, dev, o, lse, kw, deterministic=None, dq_algo="separate"):
     from exact_attention_backward_amd import api
     det = p.deterministic if deterministic is None else deterministic
-    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, det, **kw)
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, det, dq_algo=dq_algo, **kw)
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     plan.run(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv)
     torch.cuda.synchronize()
@@ -45,7 +45,7 @@ def run_backward(p, dev, o, lse, kw, deterministic=None):
     return dq, dk, dv
 
 
-def sampled_check(p, samples, deterministic=None, repeats=1):
+def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate"):
     """samples: list of (sequence, kv_head)."""
     from exact_attention_backward_amd import api
     x, dev, kw, cu = setup(p)
@@ -71,7 +71,7 @@ def sampled_check(p, samples, deterministic=None, repeats=1):
                 o[b, :, h] = torch.from_numpy(oh).to(o.dtype).cuda()
                 lse[b, h] = torch.from_numpy(lh).cuda()
     torch.cuda.synchronize()
-    outs = [run_backward(p, dev, o, lse, kw, deterministic) for _ in range(repeats)]
+    outs = [run_backward(p, dev, o, lse, kw, deterministic, dq_algo) for _ in range(repeats)]
     print(f"{p.name}: backward done", flush=True)
     for rep in outs[1:]:
         for a, bb in zip(outs[0], rep):
@@ -120,8 +120,8 @@ def test_fp32_workload_full():
         assert_close(n, to_host(gg), r, "f32")
 
 
-@pytest.mark.parametrize("deterministic", [False, True])
-def test_bf16_causal_d64_workload_full(deterministic):
+@pytest.mark.parametrize("dq_algo,deterministic", [("separate", False), ("atomic", False), ("atomic", True)])
+def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
     p = datagen.workload("c2", deterministic=deterministic)
     x, dev, kw, cu = setup(p)
     o, lse = oracle.forward(x["q"], x["k"], x["v"], p.scale, p.causal)
@@ -129,7 +129,7 @@ def test_bf16_causal_d64_workload_full(deterministic):
     lse = lse.astype(np.float32).astype(np.float64)
     O = to_dev(o, "bf16")
     L = torch.from_numpy(lse.astype(np.float32)).cuda()
-    reps = [run_backward(p, dev, O, L, kw) for _ in range(3 if deterministic else 1)]
+    reps = [run_backward(p, dev, O, L, kw, dq_algo=dq_algo) for _ in range(3 if deterministic else 1)]
     for rep in reps[1:]:
         for a, bb in zip(reps[0], rep):
             assert torch.equal(a.view(torch.int16), bb.view(torch.int16))
@@ -139,8 +139,9 @@ def test_bf16_causal_d64_workload_full(deterministic):
         assert_close(n, to_host(gg), r, "bf16")
 
 
-def test_headline_causal_sampled():
-    sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)])
+@pytest.mark.parametrize("dq_algo", ["separate", "atomic"])
+def test_headline_causal_sampled(dq_algo):
+    sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)], dq_algo=dq_algo)
 
 
 def test_headline_noncausal_sampled():
@@ -155,8 +156,13 @@ def test_varlen_sampled():
 
 
 def test_gqa_atomic_sampled():
-    sampled_check(datagen.workload("c5"), [(0, 0)])
+    sampled_check(datagen.workload("c5"), [(0, 0)], dq_algo="atomic")
 
 
 def test_gqa_deterministic_sampled_and_reproducible():
-    sampled_check(datagen.workload("c5", deterministic=True), [(0, 7)], repeats=3)
+    """Ordered atomic dQ adds: bitwise identical over three runs."""
+    sampled_check(datagen.workload("c5", deterministic=True), [(0, 7)], repeats=3, dq_algo="atomic")
+
+
+def test_gqa_separate_pass_sampled_and_reproducible():
+    sampled_check(datagen.workload("c5"), [(0, 3)], repeats=2, dq_algo="separate")

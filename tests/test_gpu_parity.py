@@ -65,12 +65,13 @@ def test_forward_matches_oracle(case):
     assert np.max(np.abs(g[fin] - rlse[fin])) <= (1e-5 if p.dtype == "f32" else 1e-4)
 
 
+@pytest.mark.parametrize("dq_algo", ["separate", "atomic"])
 @pytest.mark.parametrize("case", CASES, ids=_id)
-def test_backward_matches_oracle(case):
+def test_backward_matches_oracle(case, dq_algo):
     p = problem(case)
     r = Run(p)
-    print(f"backward {_id(case)}", flush=True)
-    dq, dk, dv, plan = r.gpu_backward()
+    print(f"backward {_id(case)} dq={dq_algo}", flush=True)
+    dq, dk, dv, plan = r.gpu_backward(dq_algo=dq_algo)
     rdq, rdk, rdv = r.oracle_backward()
     errs = {n: rel_err(to_host(g), ref) for n, g, ref in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv))}
     print("rel errs", errs, flush=True)
@@ -85,14 +86,17 @@ def test_backward_matches_oracle(case):
 DET_CASES = [CASES[0], CASES[6], CASES[8], CASES[1]]
 
 
+@pytest.mark.parametrize("dq_algo", ["atomic", "separate"])
 @pytest.mark.parametrize("case", DET_CASES, ids=_id)
-def test_deterministic_mode_is_bitwise_reproducible(case):
+def test_deterministic_mode_is_bitwise_reproducible(case, dq_algo):
+    """Ordered atomic adds (deterministic atomic mode) and the separate dQ
+    pass both give bitwise identical results on repeated runs."""
     p = problem(case, deterministic=True)
     r = Run(p)
-    print(f"deterministic {_id(case)}", flush=True)
+    print(f"deterministic {_id(case)} dq={dq_algo}", flush=True)
     outs = []
     for _ in range(3):
-        dq, dk, dv, plan = r.gpu_backward()
+        dq, dk, dv, plan = r.gpu_backward(dq_algo=dq_algo)
         assert plan.error_flag() == 0
         outs.append([t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu() for t in (dq, dk, dv)])
     for rep in outs[1:]:
@@ -127,12 +131,12 @@ def test_dq_postprocess_bit_exact(dtype, d):
 
 
 def test_preprocess_clears_workspace_and_main_accumulates():
-    """Running the main kernel twice without the preprocess adds dQ twice (the
-    documented contract); with it in between, results repeat."""
+    """Atomic mode: running the main kernel twice without the preprocess adds
+    dQ twice (the documented contract); with it in between, results repeat."""
     p = small_problem("bf16", 1, 2, 2, 150, 150, 64, True, 9)
     r = Run(p)
     d = r.dev
-    plan = r.plan()
+    plan = r.plan(dq_algo="atomic")
     dq1, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
     plan.run(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq1, dk, dv)
     plan.main(d["q"], d["k"], d["v"], d["do"], d["lse"], dk, dv)
