@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--dq-algo", default="separate", choices=["separate", "atomic"],
+                    help="dQ by a query-stationary second pass (default) or fp32 atomics")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
@@ -137,7 +139,7 @@ def main():
         kw = dict(cu_seqlens_q=torch.from_numpy(cq).cuda(), cu_seqlens_k=torch.from_numpy(ck).cuda(),
                   max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k)
     o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, **kw)
-    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, **kw)
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, dq_algo=args.dq_algo, **kw)
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
@@ -176,8 +178,11 @@ def main():
 
     rows_q = p.total_q
     elem = 2 if p.dtype == "bf16" else 4
+    # preprocess: read O and dO, write D; the dQ accumulator is cleared only
+    # in the atomic dQ mode (the separate pass overwrites it)
+    accum = rows_q * p.heads_q * p.head_dim * 4
     pre_bytes = 2 * rows_q * p.heads_q * p.head_dim * elem + rows_q * p.heads_q * 4 + \
-        plan.workspace.numel()
+        (accum if args.dq_algo == "atomic" else 0)
     post_bytes = rows_q * p.heads_q * p.head_dim * (4 + elem)
 
     out = {
@@ -199,10 +204,11 @@ def main():
                         f"{' deterministic' if p.deterministic else ''}",
             "batch": p.batch, "heads_q": p.heads_q, "heads_kv": p.heads_kv, "seqlen_q": p.seqlen_q,
             "seqlen_k": p.seqlen_k, "head_dim": p.head_dim, "causal": p.causal,
-            "deterministic": p.deterministic, "flops_per_step": flops,
+            "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
         },
         "roofline": {
-            "kernel": "bwd_kernel (main backward)",
+            "kernel": "attn_bwd (key-stationary dK/dV kernel + query-stationary dQ kernel)"
+                      if args.dq_algo == "separate" else "attn_bwd (key-stationary kernel with dQ atomics)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,

@@ -36,12 +36,14 @@ constexpr int kXcds = 8;
 template <class T, int HD>
 struct DqCfg {
     static constexpr int BQ = 32 * kWaves;   // query rows per workgroup
-    static constexpr int BN = 64;            // keys per K/V tile
+    static constexpr int BN = 32;            // keys per K/V tile
+    static constexpr int NS = sizeof(T) == 2 ? 4 : 2;   // K/V tiles in flight (LDS ring)
     static constexpr int ROWB = HD * (int)sizeof(T);
     static constexpr int TILE = BN * ROWB;
     static constexpr int BUF_K = 0, BUF_V = TILE;
     static constexpr int BUF_BYTES = 2 * TILE;
-    static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+    static constexpr int LDS_BYTES = NS * BUF_BYTES;
+    static_assert(LDS_BYTES <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for bf16)");
     static constexpr int NC = HD / 16;       // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;      // 32-column blocks of the head dim
     static constexpr int NJB = BN / 32;      // 32-key blocks of a K tile
@@ -128,6 +130,20 @@ struct DqTileCopy {
 
 __device__ __forceinline__ void dq_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(n) for a run-time n in [0, 16): all but the n most
+// recently issued VMEM operations are complete (gfx9 field layout).
+__device__ __forceinline__ void dq_wait_vmem_but(int n) {
+    switch (n) {
+#define ATTN_VMCNT_CASE(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | 0x0F70); break;
+        ATTN_VMCNT_CASE(0) ATTN_VMCNT_CASE(1) ATTN_VMCNT_CASE(2) ATTN_VMCNT_CASE(3)
+        ATTN_VMCNT_CASE(4) ATTN_VMCNT_CASE(5) ATTN_VMCNT_CASE(6) ATTN_VMCNT_CASE(7)
+        ATTN_VMCNT_CASE(8) ATTN_VMCNT_CASE(9) ATTN_VMCNT_CASE(10) ATTN_VMCNT_CASE(11)
+        ATTN_VMCNT_CASE(12) ATTN_VMCNT_CASE(13) ATTN_VMCNT_CASE(14) ATTN_VMCNT_CASE(15)
+#undef ATTN_VMCNT_CASE
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
 }  // namespace
 
 template <class T, int HD, bool CAUSAL>
@@ -181,13 +197,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 
     DqTileCopy<C::ROWB, BN> kvcopy;
     kvcopy.init(w, lane, (int)(kstride * sizeof(T)));
-    auto issue_tile = [&](int kt, char* buf) {
+    constexpr int kOpsPerTile = 2 * DqTileCopy<C::ROWB, BN>::N;   // copies one wave issues per tile
+    static_assert(kOpsPerTile * (C::NS - 2) < 16, "vmcnt range");
+    auto buf_of = [&](int kt) { return smem + (kt % C::NS) * C::BUF_BYTES; };
+    auto issue_tile = [&](int kt) {
         const int rows = min(si.len_k - kt * BN, BN);
         const unsigned bytes = (unsigned)(rows * kstride * sizeof(T));
+        char* buf = buf_of(kt);
         kvcopy.issue(rsrc_words(kg + (long long)kt * BN * kstride, bytes), buf + C::BUF_K, w);
         kvcopy.issue(rsrc_words(vg + (long long)kt * BN * kstride, bytes), buf + C::BUF_V, w);
     };
-    if (n_kt > 0) issue_tile(0, smem);
 
     // ---- this lane's query row: Q and dO rows as MFMA B operands, LSE and D
     const int i = i0 + 32 * w + l32;
@@ -220,12 +239,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         for (int v = 0; v < 16; ++v) dq[d][v] = 0.f;
     }
 
-    dq_wait_vmem();
+    // prologue: the first NS - 1 tiles in flight
+    for (int kt = 0; kt < C::NS - 1 && kt < n_kt; ++kt) issue_tile(kt);
     for (int kt = 0; kt < n_kt; ++kt) {
-        char* buf = smem + (kt & 1) * C::BUF_BYTES;
-        char* nbuf = smem + ((kt + 1) & 1) * C::BUF_BYTES;
-        __syncthreads();   // tile kt landed (each wave waited for its copies); tile kt-1 is no longer read
-        if (kt + 1 < n_kt) issue_tile(kt + 1, nbuf);
+        const char* buf = buf_of(kt);
+        // tile kt has landed once only the tiles issued after it may be in flight
+        dq_wait_vmem_but(kOpsPerTile * (min(kt + C::NS - 2, n_kt - 1) - kt));
+        __syncthreads();   // tile kt is visible to all waves; tile kt-1's buffer is free
+        if (kt + C::NS - 1 < n_kt) issue_tile(kt + C::NS - 1);
         const char* lk = buf + C::BUF_K;
         const char* lv = buf + C::BUF_V;
         const int j0 = kt * BN;
@@ -286,7 +307,6 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
                 mma16(dq[d], ads, bk);
             }
         }
-        dq_wait_vmem();   // the next tile's copies are complete
     }
 
     // ---- write this tile's dQ rows once (unscaled; the postprocess applies s)

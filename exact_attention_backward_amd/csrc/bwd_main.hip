@@ -33,19 +33,22 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = kBwdBlockN;
 constexpr int kXcds = 8;   // accelerator complex dies of an MI355X
 
-template <class T, int HD>
+template <class T, int HD, bool DQ_ATOMIC = true>
 struct BwdCfg {
     static constexpr int BM = HD == 128 ? 32 : 64;   // query rows per tile
     static constexpr int ROWB = HD * (int)sizeof(T);                       // LDS bytes per Q/dO/K row
     static constexpr int DSROWB = BM * (int)sizeof(T);                     // LDS bytes per dS^T row
     static constexpr int TILE = BM * ROWB;
-    // LDS map: resident K tile | two buffers of (Q, dO, LSE, D) | dS^T
+    // LDS map: [resident K tile] | buffers of (Q, dO, LSE, D) | [dS^T]; the
+    // K tile and dS^T are only needed when dQ is accumulated here
+    static constexpr int K_BYTES = DQ_ATOMIC ? kBN * ROWB : 0;
+    static constexpr int DS_BYTES = DQ_ATOMIC ? kBN * DSROWB : 0;
     static constexpr int OFF_K = 0;
     static constexpr int BUF_Q = 0, BUF_DO = TILE, BUF_LSE = 2 * TILE, BUF_DL = 2 * TILE + BM * 4;
     static constexpr int BUF_BYTES = 2 * TILE + 2 * BM * 4;
-    static constexpr int OFF_BUF = kBN * ROWB;
+    static constexpr int OFF_BUF = K_BYTES;
     static constexpr int OFF_DS = OFF_BUF + 2 * BUF_BYTES;
-    static constexpr int LDS_BYTES = OFF_DS + kBN * DSROWB;
+    static constexpr int LDS_BYTES = OFF_DS + (DS_BYTES > 0 ? DS_BYTES : 16);
     static constexpr int NC = HD / 16;     // 16-wide chunks of the head dim
     static constexpr int NMB = BM / 32;    // 32-row blocks of a query tile
     static constexpr int NDB = HD / 32;    // 32-column blocks of the head dim
@@ -200,7 +203,7 @@ __device__ __forceinline__ void wait_vmem_but() {
 // --------------------------------------------------------------------------
 template <class T, int HD, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
-    using C = BwdCfg<T, HD>;
+    using C = BwdCfg<T, HD, DQ_ATOMIC>;
     using op_t = typename Elem<T>::op_t;
     constexpr int BM = C::BM;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 
     // ---- prologue: first query tile, the resident K tile, K/V rows of this wave
     if (n_tiles > 0) issue_tile(0, smem + C::OFF_BUF);
-    {
+    if constexpr (DQ_ATOMIC) {
         TileCopy<C::ROWB, kBN> kcopy;
         kcopy.init(w, lane, (int)(kstride * sizeof(T)));
         const int rows = min(si.len_k - n * kBN, kBN);
@@ -534,6 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 
 int bwd_block_m(int dtype, int head_dim) {
     if (head_dim == 128) return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 128>::BM : BwdCfg<bf16_t, 128>::BM;
+    static_assert(BwdCfg<bf16_t, 128, true>::BM == BwdCfg<bf16_t, 128, false>::BM, "one query tiling");
     return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 64>::BM : BwdCfg<bf16_t, 64>::BM;
 }
 
