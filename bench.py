@@ -28,7 +28,7 @@ METRIC = "attention-backward TFLOP/s (bf16, causal, S=4096, D=128) and % of MFMA
 # MI355X published dense peaks
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-MAIN_SRC = os.path.join(ROOT, "exact_attention_backward_amd", "csrc", "bwd_main.hip")
+MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f) for f in ("bwd_main.hip", "bwd_dq.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_c3_causal.json")
 
 
@@ -52,13 +52,14 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_entry(per_launch_flops):
-    """HBM bytes per main-kernel launch from the committed counter summary,
-    or None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(dq_algo):
+    """HBM bytes per attn_bwd call from the committed counter summary (taken
+    with the separate dQ pass), or None when a kernel source changed since the
+    counters were taken or another dQ algorithm runs."""
+    if not os.path.exists(TRAFFIC_FILE) or dq_algo != "separate":
         return None
     t = json.load(open(TRAFFIC_FILE))
-    if t.get("kernel_source_sha256_16") != source_hash(MAIN_SRC):
+    if t.get("kernel_source_sha256_16") != "+".join(source_hash(p) for p in MAIN_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -214,7 +215,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": traffic_entry(flops),
+            "traffic": traffic_entry(args.dq_algo),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,
         },
