@@ -38,6 +38,9 @@ int validate_shape(const attn_shape_t* s) {
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
     if (rows_q > 0x7fffffffLL || rows_k > 0x7fffffffLL) return ATTN_ERR_BAD_SHAPE;
+    // one-dimensional grids of the streaming kernels: (row, head) pairs times
+    // lanes per pair must stay below 2^32 threads
+    if (rows_q * s->num_heads_q > (1LL << 27) || rows_k * s->num_heads_kv > (1LL << 27)) return ATTN_ERR_BAD_SHAPE;
     return ATTN_OK;
 }
 

@@ -155,22 +155,22 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
 
 // Per-lane plan for copying a tile of NROWS rows (row length ROWB bytes in
 // LDS, rows stride_bytes apart in HBM) into its swizzled LDS image with
-// buffer_load ... lds: instruction t of wave w fills the 1 KiB LDS segment
-// w + t * kWaves, lane l writing 16-byte slot l of it; the lane fetches
-// whichever global chunk the swizzle puts in that slot.  The per-lane byte
-// offsets are computed once; a tile copy is then one descriptor (built with
-// scalar instructions) and N buffer loads per wave.  Rows outside the
-// descriptor's range arrive as zeros.
-template <int ROWB, int NROWS>
+// buffer_load ... lds, by a workgroup of WAVES waves: instruction t of wave w
+// fills the 1 KiB LDS segment w + t * WAVES, lane l writing 16-byte slot l of
+// it; the lane fetches whichever global chunk the swizzle puts in that slot.
+// The per-lane byte offsets are computed once; a tile copy is then one
+// descriptor (built with scalar instructions) and N buffer loads per wave.
+// Rows outside the descriptor's range arrive as zeros.
+template <int ROWB, int NROWS, int WAVES = kWaves>
 struct TileCopy {
     static constexpr int CPR = ROWB / 16;
-    static constexpr int N = NROWS * CPR / 64 / kWaves;
-    static_assert(NROWS * CPR % (64 * kWaves) == 0, "segment split");
+    static constexpr int N = NROWS * CPR / 64 / WAVES;
+    static_assert(NROWS * CPR % (64 * WAVES) == 0, "segment split");
     int voff[N];
     __device__ __forceinline__ void init(int w, int lane, int stride_bytes) {
 #pragma unroll
         for (int t = 0; t < N; ++t) {
-            const int slot = (w + t * kWaves) * 64 + lane;
+            const int slot = (w + t * WAVES) * 64 + lane;
             const int r = slot / CPR;
             const int c = (slot % CPR) ^ swz_key<ROWB>(r);
             voff[t] = r * stride_bytes + c * 16;
@@ -178,12 +178,12 @@ struct TileCopy {
     }
     __device__ __forceinline__ void issue(rsrc_t src, char* lds, int w) const {
 #pragma unroll
-        for (int t = 0; t < N; ++t) buffer_to_lds16(src, lds + (w + t * kWaves) * 1024, voff[t]);
+        for (int t = 0; t < N; ++t) buffer_to_lds16(src, lds + (w + t * WAVES) * 1024, voff[t]);
     }
-    // untracked copies (see dma_to_lds16); returns the VMEM instructions issued
+    // untracked copies (see dma_to_lds16)
     __device__ __forceinline__ void issue_untracked(i32x4 src, const char* lds, int w) const {
 #pragma unroll
-        for (int t = 0; t < N; ++t) dma_to_lds16(src, lds_addr(lds + (w + t * kWaves) * 1024), voff[t]);
+        for (int t = 0; t < N; ++t) dma_to_lds16(src, lds_addr(lds + (w + t * WAVES) * 1024), voff[t]);
     }
 };
 
@@ -535,6 +535,345 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     }
 }
 
+// --------------------------------------------------------------------------
+// dK/dV kernel with split wave roles (bf16, dQ left to the query-stationary
+// pass).  Same key tiling and dispatch as bwd_kernel, but eight waves per
+// workgroup, two per SIMD: the 32 keys of pair p (keys 32p..32p+31) are
+// shared by a "P wave" (waves 0-3) and a "dS wave" (waves 4-7).  Per query
+// tile t:
+//
+//   P wave : X = Q K^T (stage 1), P = exp2(X s log2e - LSE log2e) (stage 2),
+//            P to LDS for its partner, dV += P^T dO (stage 3)
+//   dS wave: X = dO V^T (stage 4) for tile t; for tile t-1, with the P its
+//            partner left in LDS: dS = P (dP - D) (stage 5), dK += dS^T Q (stage 6)
+//
+// Each wave holds one K or V slice (its B operand) and one accumulator, so
+// both fit in the register budget of two waves per SIMD, and the two waves
+// of a SIMD overlap each other's MFMA, exponential and LDS work.  The dS wave
+// runs one tile behind so that a single barrier per tile publishes P.
+// Query-side tiles (Q, dO, LSE, D) are prefetched three tiles ahead into a
+// ring of five LDS buffers (the dS wave still reads tile t-1).
+//
+// The loop body is kept lean: LDS addresses are per-lane constants combined
+// with the buffer offset by one add and an XOR per operand (the swizzle only
+// permutes address bits the loop indices touch), tile coordinates advance
+// incrementally, and every wave issues the same three copies per tile (past
+// the last tile with an empty range), so each wait count is a constant.
+//
+// Masking: a padded query row (past the sequence) has Q = dO = 0 and
+// LSE = D = 0 in LDS, so its P is finite and its P dO and dS terms are zero;
+// a padded key only affects its own dK/dV rows, which are not stored.  Only
+// the causal diagonal tiles need a mask.
+// --------------------------------------------------------------------------
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = 64 * kKvWaves;
+
+template <int HD>
+struct KvCfg {
+    static constexpr int BM = HD == 128 ? 32 : 64;   // query rows per tile
+    static constexpr int ROWB = HD * 2;
+    static constexpr int TILE = BM * ROWB;
+    static constexpr int NBUF = 5;                   // ring of query-side tile buffers
+    static constexpr int PD = NBUF - 2;              // prefetch distance in tiles
+    static constexpr int BUF_Q = 0, BUF_DO = TILE, BUF_LSE = 2 * TILE, BUF_DL = 2 * TILE + 256;
+    static constexpr int BUF_BYTES = 2 * TILE + 512;
+    static constexpr int NMB = BM / 32;              // 32-row blocks of a query tile
+    static constexpr int PSLOT = NMB * 16 * 64 * 4;  // P of one pair: 16 fp32 per lane per row block
+    static constexpr int OFF_P = NBUF * BUF_BYTES;   // [pair][tile parity] P slots
+    static constexpr int OFF_DUMP = OFF_P + 4 * 2 * PSLOT;   // target of the empty copies
+    static constexpr int LDS_BYTES = OFF_DUMP + 256;
+    static constexpr int NC = HD / 16;               // 16-wide chunks of the head dim
+    static constexpr int NDB = HD / 32;              // 32-column blocks of the head dim
+    static constexpr int NIC = BM / 16;              // 16-wide chunks of the query rows
+    static constexpr int OPS = 3;                    // copy instructions per tile and wave
+    static_assert(TileCopy<ROWB, BM, kKvWaves>::N == 1, "one segment per wave and tensor");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(BUF_BYTES % 256 == 0 && TILE % 256 == 0, "XOR addressing needs 256-byte aligned tiles");
+    static_assert(BM * 4 <= 256, "LSE/D tile in one 256-byte slot");
+};
+
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
+    using C = KvCfg<HD>;
+    using T = bf16_t;
+    using op_t = bf16x8;
+    constexpr int BM = C::BM, NMB = C::NMB, ROWB = C::ROWB;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int role = w >> 2;   // 0: P wave (S, P, dV), 1: dS wave (dP, dS, dK)
+    const int pair = w & 3;    // keys 32 * pair .. + 31 of the tile
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- key tile: all key tiles of one (sequence, kv-head) on one XCD
+    int grp, n;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+            grp = (slot / a.nblk_n) * kXcds + xcd;
+            n = slot % a.nblk_n;
+        } else {
+            grp = blockIdx.x / a.nblk_n;
+            n = blockIdx.x % a.nblk_n;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    if (n * kBN >= si.len_k) return;
+    const bool varlen = a.cu_q != nullptr;
+    const int G = a.hq / a.hkv;
+    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+    const int m_end = (si.len_q + BM - 1) / BM;
+    int m_begin = 0;
+    if (CAUSAL) {
+        const int first_row = n * kBN - off;   // first query row that sees key n*kBN
+        m_begin = first_row > 0 ? first_row / BM : 0;
+    }
+    const int n_m = max(m_end - m_begin, 0);
+    const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
+
+    const long long kstride = (long long)a.hkv * HD;
+    const long long qstride = (long long)a.hq * HD;
+    const long long kv_base = (long long)si.k0 * kstride + (long long)hkv * HD;
+
+    // ---- per-lane LDS offsets, fixed for the whole kernel
+    const unsigned lds0 = lds_addr(smem);
+    // row operand of the first product: row 32 mb + l32, chunk 2c + h at (rbase ^ 32c) + mb * 32 ROWB
+    const int rbase = swz<ROWB>(l32, 16 * h);
+    // column operand of the second product: rows 16c + 8e + 4h + (lane % 16) / 4,
+    // columns 32d + 16 ((lane / 16) % 2) + 4 (lane % 4), at (tbase[e] ^ 64d) + c * 16 ROWB
+    const int s16 = lane & 15;
+    const int tcol = 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+    const int tbase0 = swz<ROWB>(4 * h + (s16 >> 2), tcol);
+    const int tbase1 = swz<ROWB>(8 + 4 * h + (s16 >> 2), tcol);
+    const int tile_off = role == 0 ? C::BUF_Q : C::BUF_DO;    // row operand of the first product
+    const int col_off = role == 0 ? C::BUF_DO : C::BUF_Q;     // column operand of the second
+    const int pslots = C::OFF_P + pair * 2 * C::PSLOT;
+
+    // ---- copies: this wave's 1 KiB segment of the Q and dO tiles, then LSE
+    // (wave 0), D (wave 1) or an empty copy (the others)
+    const int seg_voff = [&] {
+        constexpr int CPR = ROWB / 16;
+        const int slot = w * 64 + lane;
+        const int r = slot / CPR;
+        return r * (int)(qstride * sizeof(T)) + ((slot % CPR) ^ swz_key<ROWB>(r)) * 16;
+    }();
+    const long long tile_step = (long long)BM * qstride * (long long)sizeof(T);   // bytes between query tiles
+    const long long lse_head = (long long)(varlen ? a.total_q : a.seqlen_q) * 4;  // bytes between heads
+    const long long q_g0 = ((long long)(si.q0 + m_begin * BM) * a.hq + (long long)hkv * G) * HD * (long long)sizeof(T);
+    const long long l_g0 =
+        ((varlen ? (long long)hkv * G * a.total_q + si.q0 : ((long long)b * a.hq + (long long)hkv * G) * a.seqlen_q) +
+         m_begin * BM) * 4;
+    const char* qbytes = reinterpret_cast<const char*>(a.q);
+    const char* dobytes = reinterpret_cast<const char*>(a.dout);
+    const char* sbytes = w == 0 ? reinterpret_cast<const char*>(a.lse) : reinterpret_cast<const char*>(a.delta);
+    // issue cursor: coordinates of the next tile to copy
+    int is_t = 0, is_m = m_begin, is_g = 0;
+    long long is_q = q_g0, is_l = l_g0;
+    unsigned is_buf = 0;   // ring offset of the next tile
+    auto issue_next = [&] {
+        const bool real = is_t < n_tiles;
+        const int rows = real ? min(si.len_q - is_m * BM, BM) : 0;
+        const unsigned qb = (unsigned)(rows * qstride * (long long)sizeof(T));
+        const unsigned dst = lds0 + is_buf;
+        dma_to_lds16(rsrc_words(qbytes + is_q, qb), dst + C::BUF_Q + w * 1024, seg_voff);
+        dma_to_lds16(rsrc_words(dobytes + is_q, qb), dst + C::BUF_DO + w * 1024, seg_voff);
+        const unsigned sdst = w == 0 ? dst + C::BUF_LSE : w == 1 ? dst + C::BUF_DL : lds0 + C::OFF_DUMP;
+        if (lane < BM) dma_to_lds4(rsrc_words(sbytes + is_l, w < 2 ? rows * 4 : 0), sdst, lane * 4);
+        ++is_t;
+        is_buf = is_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : is_buf + C::BUF_BYTES;
+        if (++is_m == m_end) {
+            is_m = m_begin;
+            ++is_g;
+            is_q = q_g0 + (long long)is_g * HD * (long long)sizeof(T);
+            is_l = l_g0 + is_g * lse_head;
+        } else {
+            is_q += tile_step;
+            is_l += BM * 4;
+        }
+    };
+
+    // ---- prologue: the first query-side tiles, then this wave's K (P wave)
+    // or V (dS wave) rows as B operands.  The wait for all of them here tells
+    // the compiler that the K/V registers are ready; otherwise it would wait
+    // for them (vmcnt(0), the prefetches included) inside the loop.
+#pragma unroll
+    for (int t = 0; t < C::PD; ++t) issue_next();
+    op_t wreg[C::NC];
+    {
+        const T* src = reinterpret_cast<const T*>(role == 0 ? a.k : a.v) + kv_base;
+        const int j = n * kBN + 32 * pair + l32;
+        const bool ok = j < si.len_k;
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) wreg[c] = load_op_global<T>(src + (long long)j * kstride + 16 * c + 8 * h, ok);
+    }
+    wait_vmem();
+
+    f32x16 acc[C::NDB];   // dV rows (P wave) or unscaled dK rows (dS wave) of this pair's keys
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
+    }
+    const float scale2 = a.scale * kLog2e;
+    const int j = n * kBN + 32 * pair + l32;   // this lane's key (column of S)
+    const int diag = n * kBN + kBN - 1 - off;  // tiles starting at or below this row are unmasked
+    unsigned cur_buf = 0;                      // ring offset of tile t
+    int cur_m = m_begin;                       // query tile of tile t
+
+    // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
+    auto step = [&](int t, f32x16* xc, f32x16* xp) {
+        // this wave's copies of tile t have landed (those of the PD - 1 later
+        // tiles may still fly); after the barrier all waves' have, P of tile
+        // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
+        // receives tile t+3
+        wait_vmem_but<C::OPS * (C::PD - 1)>();
+        __syncthreads();
+        const unsigned prev_buf = cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES;
+        const int i0 = cur_m * BM;
+        // row statistics of the tile whose second product comes in this step,
+        // read now so their latency hides behind the first product: LSE of
+        // tile t (P wave), or D and the partner's P of tile t-1 (dS wave)
+        const float* lst = reinterpret_cast<const float*>(
+            smem + (role == 0 ? cur_buf + C::BUF_LSE : prev_buf + C::BUF_DL) + 16 * h);
+        f32x4 stat[NMB * 4], pin[NMB * 4];
+#pragma unroll
+        for (int q = 0; q < NMB * 4; ++q) stat[q] = *reinterpret_cast<const f32x4*>(lst + 8 * q);
+        if (role == 1) {
+            const int psr = pslots + ((t - 1) & 1) * C::PSLOT + lane * 16;
+#pragma unroll
+            for (int q = 0; q < NMB * 4; ++q) pin[q] = *reinterpret_cast<const f32x4*>(smem + psr + q * 1024);
+        }
+
+        // ---- X = Q K^T (P wave) or dO V^T (dS wave) for tile t
+        if (t < n_tiles) {
+            const int rb = (int)cur_buf + tile_off + rbase;
+            op_t ra[C::NC];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+                for (int c = 0; c < C::NC; ++c)
+                    ra[c] = __builtin_bit_cast(op_t, lds_read16(smem, ((rb ^ (32 * c)) + mb * 32 * ROWB)));
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xc[mb][v] = 0.f;
+#pragma unroll
+                for (int c = 0; c < C::NC; ++c) mma16(xc[mb], ra[c], wreg[c]);
+            }
+            // all operand reads first, so the MFMA chain does not wait on LDS latency
+            __builtin_amdgcn_sched_group_barrier(0x100, NMB * C::NC, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NMB * C::NC, 0);
+        }
+        issue_next();
+        cur_buf = cur_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : cur_buf + C::BUF_BYTES;
+        if (++cur_m == m_end) cur_m = m_begin;
+
+        // the tile whose second product this wave computes now
+        const int tt = role == 0 ? t : t - 1;
+        if (tt < 0 || tt >= n_tiles) return;
+        const unsigned buf = role == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
+                                       : prev_buf;
+        const int ps = pslots + (tt & 1) * C::PSLOT + lane * 16;
+        op_t opa[C::NIC];
+        if (role == 0) {
+            // ---- P = exp2(S s log2e - LSE log2e), masked on causal diagonal tiles
+            auto softmax = [&](auto masked) {
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int r = 32 * mb + 8 * q4;   // + 4h + e
+                        const f32x4 lse = stat[mb * 4 + q4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = 4 * q4 + e;
+                            float p;
+                            if constexpr (decltype(masked)::value) {
+                                const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
+                                p = __builtin_amdgcn_exp2f(xc[mb][v] * scale2 - l2);
+                                p = j <= i0 + r + 4 * h + e + off ? p : 0.f;
+                            } else {
+                                p = __builtin_amdgcn_exp2f(fmaf(xc[mb][v], scale2, -lse[e] * kLog2e));
+                            }
+                            xc[mb][v] = p;
+                        }
+                        const f32x4 pv = {xc[mb][4 * q4], xc[mb][4 * q4 + 1], xc[mb][4 * q4 + 2], xc[mb][4 * q4 + 3]};
+                        lds_write(smem, ps + (mb * 4 + q4) * 1024, pv);
+                    }
+                }
+            };
+            if (CAUSAL && i0 < diag)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) {
+                float tp[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) tp[u] = xc[c >> 1][8 * (c & 1) + u];
+                to_op(opa[c], tp);
+            }
+        } else {
+            // ---- dS = P (dP - D) with P from the partner wave
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 dl = stat[mb * 4 + q4];
+                    const f32x4 pv = pin[mb * 4 + q4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xp[mb][4 * q4 + e] = pv[e] * (xp[mb][4 * q4 + e] - dl[e]);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) {
+                float td[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) td[u] = xp[c >> 1][8 * (c & 1) + u];
+                to_op(opa[c], td);
+            }
+        }
+        // ---- dV += P^T dO (P wave) or dK += dS^T Q (dS wave)
+        const int cb = (int)buf + col_off;
+        const int t0 = cb + tbase0, t1 = cb + tbase1;
+#pragma unroll
+        for (int c = 0; c < C::NIC; ++c) {
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) {
+                const u32x2 x = lds_read_tr(smem, (t0 ^ (64 * d)) + c * 16 * ROWB);
+                const u32x2 y = lds_read_tr(smem, (t1 ^ (64 * d)) + c * 16 * ROWB);
+                const u32x4 wv = {x[0], x[1], y[0], y[1]};
+                mma16(acc[d], opa[c], __builtin_bit_cast(op_t, wv));
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
+    };
+
+    // the dS wave keeps X of tile t until step t+1: two register sets, unrolled by two
+    f32x16 xA[NMB], xB[NMB];
+    for (int t = 0; t <= n_tiles; t += 2) {
+        step(t, xA, xB);
+        if (t + 1 <= n_tiles) step(t + 1, xB, xA);
+    }
+
+    // ---- epilogue: dV (P wave) or dK = s * sum dS^T Q (dS wave); rows past
+    // the sequence are not written
+    T* dst = reinterpret_cast<T*>(role == 0 ? a.dv : a.dk) + kv_base;
+    const float f = role == 0 ? 1.f : a.scale;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int jj = n * kBN + 32 * pair + acc_row(v, h);
+            if (jj < si.len_k) store_elem(dst, (long long)jj * kstride + 32 * d + l32, acc[d][v] * f);
+        }
+    }
+}
+
 int bwd_block_m(int dtype, int head_dim) {
     if (head_dim == 128) return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 128>::BM : BwdCfg<bf16_t, 128>::BM;
     static_assert(BwdCfg<bf16_t, 128, true>::BM == BwdCfg<bf16_t, 128, false>::BM, "one query tiling");
@@ -544,6 +883,14 @@ int bwd_block_m(int dtype, int head_dim) {
 template <class T, int HD>
 static void launch_bwd_t(const BwdArgs& a, bool causal, bool dq_atomic, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
+    if constexpr (sizeof(T) == 2) {
+        static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
+        if (!dq_atomic) {
+            if (causal) bwd_kv_kernel<HD, true><<<grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<HD, false><<<grid, kKvThreads, 0, st>>>(a);
+            return;
+        }
+    }
     if (causal) {
         if (dq_atomic) bwd_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
         else bwd_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);

@@ -172,13 +172,14 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(size_t)((__attribute__((address_space(3))) const char*)p));
 }
+// M0 (the LDS base of the copy) is an input operand bound to that register,
+// so the compiler sets it, knows it changed, and never sees it clobbered; the
+// s_nop is the wait state required between an M0 write and an LDS-DMA load.
 __device__ __forceinline__ void dma_to_lds16(i32x4 r, unsigned lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+    asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 
 // ---------------------------------------------------------------------------

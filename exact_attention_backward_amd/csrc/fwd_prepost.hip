@@ -99,29 +99,45 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// preprocess: D = rowsum(dO * O); HD / 8 lanes per row, 8 elements per lane
+// preprocess: D = rowsum(dO * O).  One workgroup takes one head and 64
+// consecutive token rows: HD / 8 lanes per row read 16 bytes each of O and dO
+// (a contiguous head row), reduce by shuffles, and the 64 sums leave through
+// LDS as one contiguous 256-byte run of D, so no D line is shared between
+// workgroups (they would sit in different L2s and be written back partially).
 // ---------------------------------------------------------------------------
+constexpr int kPreTokens = 64;
+
 template <class T, int HD>
 __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
     constexpr int LPR = HD / 8;
-    const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long row = gt / LPR;            // = flat_row * H + h, the memory order of O
-    const int part = (int)(gt % LPR);
-    float acc = 0.f;
-    if (row < a.rows) {
-        float x[8], y[8];
-        load8(reinterpret_cast<const T*>(a.o) + row * HD + part * 8, x);
-        load8(reinterpret_cast<const T*>(a.dout) + row * HD + part * 8, y);
+    constexpr int RPP = 256 / LPR;                 // rows per pass
+    constexpr int PASSES = kPreTokens / RPP;
+    __shared__ float dsum[kPreTokens];
+    const long long tokens = a.rows / a.h;
+    const int h = (int)(blockIdx.x % (unsigned)a.h);
+    const long long r0 = (long long)(blockIdx.x / (unsigned)a.h) * kPreTokens;
+    const int part = threadIdx.x % LPR, slot = threadIdx.x / LPR;
+    float x[PASSES][8], y[PASSES][8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc = fmaf(x[t], y[t], acc);
+    for (int p = 0; p < PASSES; ++p) {
+        const long long r = min(r0 + p * RPP + slot, tokens - 1);
+        const long long e = (r * a.h + h) * HD + part * 8;
+        load8(reinterpret_cast<const T*>(a.o) + e, x[p]);
+        load8(reinterpret_cast<const T*>(a.dout) + e, y[p]);
     }
 #pragma unroll
-    for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
-    if (row < a.rows && part == 0) {
-        const long long r = row / a.h;
-        const int h = (int)(row - r * a.h);
-        a.delta[lse_index(a.varlen, r, h, a.h, a.s, a.total)] = acc;
+    for (int p = 0; p < PASSES; ++p) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc = fmaf(x[p][t], y[p][t], acc);
+#pragma unroll
+        for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
+        if (part == 0) dsum[p * RPP + slot] = acc;
     }
+    __syncthreads();
+    const long long r = r0 + threadIdx.x;
+    if (threadIdx.x < kPreTokens && r < tokens)
+        a.delta[lse_index(a.varlen, r, h, a.h, a.s, a.total)] = dsum[threadIdx.x];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, long long n16) {
@@ -183,8 +199,8 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 }
 
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st) {
-    const long long threads = a.rows * (hd / 8);
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const long long tokens = a.rows / a.h;
+    const unsigned blocks = (unsigned)((tokens + kPreTokens - 1) / kPreTokens * a.h);
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) preprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
         else preprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);

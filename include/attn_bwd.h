@@ -62,7 +62,8 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL (the workspace included) */
     ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
-                                  cu_seqlens, workspace too small, ... */
+                                  cu_seqlens, workspace too small, more than 2^27
+                                  (row, head) pairs in Q or K, ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16, head_dim not 64 or 128 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */

@@ -67,6 +67,8 @@ def test_workspace_size_formula():
     (dict(seqlen_q=-1), L.ATTN_ERR_BAD_SHAPE),
     (dict(causal=2), L.ATTN_ERR_BAD_SHAPE),
     (dict(softmax_scale=float("nan")), L.ATTN_ERR_BAD_SHAPE),
+    (dict(batch=1, seqlen_q=(1 << 23) + 1, num_heads_q=16, num_heads_kv=16), L.ATTN_ERR_BAD_SHAPE),
+    (dict(dq_algo=5), L.ATTN_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, status):
     s = shape(**kw)
