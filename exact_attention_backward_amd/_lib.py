@@ -23,6 +23,7 @@ ATTN_DTYPE_BF16 = 1
 
 ATTN_DQ_SEPARATE = 0
 ATTN_DQ_ATOMIC = 1
+ATTN_DQ_STORED_DS = 2
 
 EXPORTS = (
     "attn_status_string",

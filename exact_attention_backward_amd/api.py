@@ -41,13 +41,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC}
+DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_ds": L.ATTN_DQ_STORED_DS}
 
 
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
-    "separate" (query-stationary dQ pass, no atomics) or "atomic"."""
+    "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
+    "stored_ds" (dS stored in bf16 by the dK/dV kernel, then dQ = dS K; bf16
+    only, workspace grows with Sq x Sk) or "atomic"."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -147,8 +149,13 @@ class BackwardPlan:
 
     def error_flag(self):
         """Non-zero if an ordered (deterministic) wait gave up; reads the
-        workspace's status word (synchronises the stream)."""
-        return int(self.workspace[-256:].view(torch.int32)[0].item())
+        workspace's status word (synchronises the stream).  The status words
+        are the last 256 bytes of the workspace prefix every dQ mode shares,
+        which is the whole workspace of the separate mode."""
+        base = L.AttnShape.from_buffer_copy(self.shape)
+        base.dq_algo = L.ATTN_DQ_SEPARATE
+        end = attn_bwd_workspace_bytes(base)
+        return int(self.workspace[end - 256:end].view(torch.int32)[0].item())
 
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,

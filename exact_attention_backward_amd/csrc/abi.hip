@@ -33,7 +33,9 @@ int validate_shape(const attn_shape_t* s) {
     if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
     if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
     if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
-    if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC) return ATTN_ERR_UNSUPPORTED;
+    if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC && s->dq_algo != ATTN_DQ_STORED_DS)
+        return ATTN_ERR_UNSUPPORTED;
+    if (s->dq_algo == ATTN_DQ_STORED_DS && s->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
     // element counts must stay addressable with 64-bit offsets and 32-bit row counts
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
@@ -60,7 +62,22 @@ int nblk_m(const attn_shape_t* s) {
 size_t sem_bytes(const attn_shape_t* s) {
     return align_up((size_t)s->batch * s->num_heads_q * nblk_m(s) * sizeof(int32_t));
 }
-size_t workspace_bytes(const attn_shape_t* s) { return accum_bytes(s) + sem_bytes(s) + kErrBytes; }
+// stored-dS mode: [first query block of each sequence, int32][dS blocks]
+long long ds_qb(const attn_shape_t* s) {
+    if (varlen(s)) return (long long)(s->total_q + kDsRows - 1) / kDsRows + s->batch;
+    return (long long)s->batch * ((s->seqlen_q + kDsRows - 1) / kDsRows);
+}
+int ds_nn(const attn_shape_t* s) { return (s->seqlen_k + kDsKeys - 1) / kDsKeys; }
+size_t ds_table_bytes(const attn_shape_t* s) {
+    return s->dq_algo == ATTN_DQ_STORED_DS ? align_up((size_t)(s->batch + 1) * sizeof(int32_t)) : 0;
+}
+size_t ds_bytes(const attn_shape_t* s) {
+    if (s->dq_algo != ATTN_DQ_STORED_DS) return 0;
+    return (size_t)s->num_heads_q * (size_t)ds_qb(s) * (size_t)ds_nn(s) * kDsBlockBytes;
+}
+size_t workspace_bytes(const attn_shape_t* s) {
+    return accum_bytes(s) + sem_bytes(s) + kErrBytes + ds_table_bytes(s) + ds_bytes(s);
+}
 
 int check_launch() {
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -111,14 +128,19 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
     if (workspace_size < need) return ATTN_ERR_BAD_SHAPE;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    // the separate dQ pass overwrites every accumulator row; only the atomic
-    // modes add into it
+    // the counters and status words always; the accumulator only where it is
+    // added into (atomic modes); the dS blocks are written before they are read
     if (s->dq_algo == ATTN_DQ_ATOMIC)
-        launch_fill_zero(workspace, need, hs);
+        launch_fill_zero(workspace, accum_bytes(s) + sem_bytes(s) + kErrBytes, hs);
     else
-        launch_fill_zero(reinterpret_cast<char*>(workspace) + accum_bytes(s), need - accum_bytes(s), hs);
+        launch_fill_zero(reinterpret_cast<char*>(workspace) + accum_bytes(s), sem_bytes(s) + kErrBytes, hs);
     PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s)};
     launch_preprocess(a, s->dtype, s->head_dim, hs);
+    if (s->dq_algo == ATTN_DQ_STORED_DS && varlen(s))
+        launch_ds_table(s->cu_seqlens_q, s->batch, s->seqlen_q, s->total_q,
+                        reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + accum_bytes(s) + sem_bytes(s) +
+                                               kErrBytes),
+                        hs);
     return check_launch();
 }
 
@@ -157,14 +179,22 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.nblk_m = nblk_m(s);
     a.scale = s->softmax_scale;
     a.deterministic = s->deterministic;
+    if (s->dq_algo == ATTN_DQ_STORED_DS) {
+        char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
+        a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
+        a.ds = reinterpret_cast<bf16_t*>(tab + ds_table_bytes(s));
+        a.ds_qb = ds_qb(s);
+        a.ds_nn = ds_nn(s);
+    }
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    const bool atomic = s->dq_algo == ATTN_DQ_ATOMIC;
-    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, atomic, hs);
-    if (!atomic) {
+    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, s->dq_algo, hs);
+    if (s->dq_algo == ATTN_DQ_SEPARATE) {
         BwdArgs d = a;
         d.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
         launch_bwd_dq(d, s->dtype, s->head_dim, s->causal != 0, hs);
+    } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
+        launch_bwd_dq_gemm(a, s->head_dim, s->causal != 0, hs);
     }
     return check_launch();
 }

@@ -592,7 +592,7 @@ struct KvCfg {
     static_assert(BM * 4 <= 256, "LSE/D tile in one 256-byte slot");
 };
 
-template <int HD, bool CAUSAL>
+template <int HD, bool CAUSAL, bool STORE_DS>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     using C = KvCfg<HD>;
     using T = bf16_t;
@@ -724,6 +724,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     const int diag = n * kBN + kBN - 1 - off;  // tiles starting at or below this row are unmasked
     unsigned cur_buf = 0;                      // ring offset of tile t
     int cur_m = m_begin;                       // query tile of tile t
+    int cur_g = 0;                             // q-head (within the group) of tile t
+    int last_m = m_begin, last_g = 0;          // the same for tile t-1
+    // stored-dS mode: first 32-row query block of this sequence, and whether
+    // the key tile reaches past the sequence (its dS columns are then zeroed)
+    const long long ds_qb0 = STORE_DS ? (varlen ? (long long)a.ds_qb_base[b]
+                                                : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows))
+                                      : 0;
+    const bool ragged_k = n * kBN + kBN > si.len_k;
+    constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
     auto step = [&](int t, f32x16* xc, f32x16* xp) {
@@ -731,7 +740,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         // tiles may still fly); after the barrier all waves' have, P of tile
         // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
         // receives tile t+3
-        wait_vmem_but<C::OPS * (C::PD - 1)>();
+        // in the stored-dS mode each dS-wave step also issues NST stores after
+        // its copies, so the tiles' copies are counted past them (the first
+        // step has no dS; it stores an empty range instead, to keep the count)
+        if (STORE_DS && role == 1)
+            wait_vmem_but<C::OPS * (C::PD - 1) + NST * C::PD>();
+        else
+            wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
         const unsigned prev_buf = cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES;
         const int i0 = cur_m * BM;
@@ -769,11 +784,28 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         }
         issue_next();
         cur_buf = cur_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : cur_buf + C::BUF_BYTES;
-        if (++cur_m == m_end) cur_m = m_begin;
+        const int tile_m = cur_m, tile_g = cur_g;   // coordinates of tile t
+        if (++cur_m == m_end) {
+            cur_m = m_begin;
+            ++cur_g;
+        }
+        const int prev_m = last_m, prev_g = last_g;   // coordinates of tile t-1
+        last_m = tile_m;
+        last_g = tile_g;
+        (void)prev_m;
+        (void)prev_g;
 
         // the tile whose second product this wave computes now
         const int tt = role == 0 ? t : t - 1;
-        if (tt < 0 || tt >= n_tiles) return;
+        if (tt < 0 || tt >= n_tiles) {
+            if (STORE_DS && role == 1) {   // the dS wave's first step: empty stores
+                const rsrc_t none = make_rsrc(a.ds, 0);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < NST; ++k) __builtin_amdgcn_raw_buffer_store_b128(z, none, lane * 16, 0, 0);
+            }
+            return;
+        }
         const unsigned buf = role == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
                                        : prev_buf;
         const int ps = pslots + (tt & 1) * C::PSLOT + lane * 16;
@@ -828,6 +860,15 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
                     for (int e = 0; e < 4; ++e) xp[mb][4 * q4 + e] = pv[e] * (xp[mb][4 * q4 + e] - dl[e]);
                 }
             }
+            if (STORE_DS && ragged_k && j >= si.len_k) {
+                // a key past the sequence meets zero K rows in dQ = dS K; its
+                // dS is zeroed so that a non-finite value cannot reach them
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) xp[mb][v] = 0.f;
+                }
+            }
 #pragma unroll
             for (int c = 0; c < C::NIC; ++c) {
                 float td[8];
@@ -851,6 +892,38 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
+        if (STORE_DS && role == 1) {
+            // dS (bf16) of this pair's 32 keys to the dS blocks, in MFMA
+            // A-operand order: transposed through this pair's P slot of tile
+            // t-1 (that P is already in registers) as [key][row].  Issued
+            // after the dK MFMAs, which run meanwhile.
+            constexpr int TROWB = BM * 2;
+            char* tr = smem + pslots + (tt & 1) * C::PSLOT;
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) {
+                const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+                lds_write(tr, swz<TROWB>(l32, (16 * c + 4 * h) * 2), u32x2{wv[0], wv[1]});
+                lds_write(tr, swz<TROWB>(l32, (16 * c + 8 + 4 * h) * 2), u32x2{wv[2], wv[3]});
+            }
+            const int hq = hkv * G + prev_g;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const int lq = prev_m * (BM / kDsRows) + mb;   // 32-row block within the sequence
+                // blocks past the sequence get an empty range (the second
+                // test only fails for overlapping, malformed cu_seqlens)
+                const bool ok = lq * kDsRows < si.len_q && ds_qb0 + lq < a.ds_qb;
+                const rsrc_t dst = make_rsrc(
+                    reinterpret_cast<char*>(a.ds) + (((long long)hq * a.ds_qb + ds_qb0 + lq) * a.ds_nn + n) *
+                                                        kDsBlockBytes,
+                    ok ? kDsBlockBytes : 0);
+#pragma unroll
+                for (int cs = 0; cs < 2; ++cs) {
+                    const op_t f = read_op_col<T, TROWB>(tr, 16 * cs + 8 * h, 16 * cs + 8 * h + 4, 32 * mb, lane);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f), dst,
+                                                           (2 * pair + cs) * 1024 + lane * 16, 0, 0);
+                }
+            }
+        }
     };
 
     // the dS wave keeps X of tile t until step t+1: two register sets, unrolled by two
@@ -881,16 +954,23 @@ int bwd_block_m(int dtype, int head_dim) {
 }
 
 template <class T, int HD>
-static void launch_bwd_t(const BwdArgs& a, bool causal, bool dq_atomic, hipStream_t st) {
+static void launch_bwd_t(const BwdArgs& a, bool causal, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
-        if (!dq_atomic) {
-            if (causal) bwd_kv_kernel<HD, true><<<grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<HD, false><<<grid, kKvThreads, 0, st>>>(a);
+        static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
+        if (dq_algo == ATTN_DQ_SEPARATE) {
+            if (causal) bwd_kv_kernel<HD, true, false><<<grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<HD, false, false><<<grid, kKvThreads, 0, st>>>(a);
+            return;
+        }
+        if (dq_algo == ATTN_DQ_STORED_DS) {
+            if (causal) bwd_kv_kernel<HD, true, true><<<grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<HD, false, true><<<grid, kKvThreads, 0, st>>>(a);
             return;
         }
     }
+    const bool dq_atomic = dq_algo == ATTN_DQ_ATOMIC;
     if (causal) {
         if (dq_atomic) bwd_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
         else bwd_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
@@ -900,13 +980,13 @@ static void launch_bwd_t(const BwdArgs& a, bool causal, bool dq_atomic, hipStrea
     }
 }
 
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, bool dq_atomic, hipStream_t st) {
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, dq_atomic, st);
-        else launch_bwd_t<bf16_t, 128>(a, causal, dq_atomic, st);
+        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, dq_algo, st);
+        else launch_bwd_t<bf16_t, 128>(a, causal, dq_algo, st);
     } else {
-        if (hd == 64) launch_bwd_t<float, 64>(a, causal, dq_atomic, st);
-        else launch_bwd_t<float, 128>(a, causal, dq_atomic, st);
+        if (hd == 64) launch_bwd_t<float, 64>(a, causal, dq_algo, st);
+        else launch_bwd_t<float, 128>(a, causal, dq_algo, st);
     }
 }
 

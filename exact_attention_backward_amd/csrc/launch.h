@@ -57,7 +57,20 @@ struct BwdArgs {
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
     int deterministic;
+    // stored-dS mode: dS blocks [Hq][ds_qb][ds_nn][32 x 128 bf16] and, for
+    // varlen, each sequence's first 32-row query block
+    bf16_t* ds;
+    const int* ds_qb_base;
+    long long ds_qb;     // 32-row query blocks per q-head
+    int ds_nn;           // 128-key blocks per query block
 };
+
+// dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16, held as
+// eight 16-key slices of 1 KiB, each in the lane order of an MFMA A operand
+// (lane l: row l % 32, keys 8 (l / 32) .. + 7 of the slice, 16 bytes).
+constexpr int kDsRows = 32;
+constexpr int kDsKeys = 128;
+constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
 
 // Query rows per tile of the main kernel (keys per tile are fixed at 128).
 int bwd_block_m(int dtype, int head_dim);
@@ -67,7 +80,11 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st
 void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, bool dq_atomic, hipStream_t st);
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, hipStream_t st);
+// stored-dS mode: dQ = dS K from the stored blocks (bf16), and the per-sequence
+// block table of varlen problems
+void launch_bwd_dq_gemm(const BwdArgs& a, int hd, bool causal, hipStream_t st);
+void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, int* out, hipStream_t st);
 // query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
 int bwd_dq_block_m();

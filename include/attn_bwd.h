@@ -64,7 +64,8 @@ typedef enum attn_status {
     ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
                                   cu_seqlens, workspace too small, more than 2^27
                                   (row, head) pairs in Q or K, ... */
-    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16, head_dim not 64 or 128 */
+    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16, head_dim not 64 or 128, unknown
+                                  dq_algo, ATTN_DQ_STORED_DS with F32 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status_t;
@@ -81,10 +82,17 @@ typedef enum attn_dtype {
  *    reproducible; seven contractions per tile pair instead of five.
  *  ATTN_DQ_ATOMIC: the key-stationary kernel adds dS K for each tile pair
  *    into the fp32 accumulator with global atomics (with deterministic = 1,
- *    in a fixed order per dQ tile). */
+ *    in a fixed order per dQ tile).
+ *  ATTN_DQ_STORED_DS (bf16 only): the key-stationary kernel stores dS, in
+ *    bf16 (the operand type the pages' dQ = dS K product uses), in the
+ *    workspace; a second pass forms dQ = dS K from it and writes every
+ *    accumulator row once: five contractions per tile pair, no atomics,
+ *    bitwise reproducible, at the cost of a workspace that grows with
+ *    Sq x Sk (2 bytes per query row and key, per q-head). */
 typedef enum attn_dq_algo {
     ATTN_DQ_SEPARATE = 0,
-    ATTN_DQ_ATOMIC = 1
+    ATTN_DQ_ATOMIC = 1,
+    ATTN_DQ_STORED_DS = 2
 } attn_dq_algo_t;
 
 /* Problem description, passed by pointer and only read.  Plain old data. */
@@ -112,8 +120,11 @@ const char* attn_status_string(int status);
 /* Bytes of device workspace attn_bwd_preprocess/attn_bwd/attn_bwd_dq_postprocess
  * need for this shape: the fp32 dQ accumulator ([B, Hq, Sq, D] dense,
  * [Hq, total_q, D] varlen) followed by the int32 ordering counters of the
- * deterministic mode, each part 256-byte aligned.  Returns 0 if the shape is
- * invalid. */
+ * deterministic mode and, for ATTN_DQ_STORED_DS, a table of per-sequence
+ * offsets and the dS blocks (32 query rows x 128 keys of bf16 each, for every
+ * q-head, 32-row query block and 128-key block; varlen sizes the query
+ * blocks by total_q / 32 + batch and the key blocks by seqlen_k), each part
+ * 256-byte aligned.  Returns 0 if the shape is invalid. */
 size_t attn_bwd_workspace_bytes(const attn_shape_t* shape);
 
 /* Plain forward: O = softmax(s Q K^T) V and LSE (natural log) per row.
@@ -127,7 +138,9 @@ int attn_fwd(const attn_shape_t* shape, const void* q, const void* k, const void
  * stage 5).  Also clears the workspace parts attn_bwd accumulates into (the
  * zero-initialised accumulator contract of CollectiveEpilogueBwdGQA::store_zero):
  * the ordering counters and status words always, the dQ accumulator for
- * ATTN_DQ_ATOMIC (the separate pass overwrites it).
+ * ATTN_DQ_ATOMIC (the other modes overwrite it).  For ATTN_DQ_STORED_DS with
+ * varlen it also writes the table of each sequence's first 32-row query
+ * block.
  * o, dout: inputs; delta: output [LSE layout]; workspace: output, at least
  * attn_bwd_workspace_bytes(shape) bytes (workspace_bytes says how many). */
 int attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* dout,
@@ -141,6 +154,9 @@ int attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* do
  *  - shape->dq_algo == ATTN_DQ_SEPARATE: a second, query-stationary kernel
  *    writes every accumulator row once (no atomics; bitwise reproducible
  *    whatever shape->deterministic says);
+ *  - shape->dq_algo == ATTN_DQ_STORED_DS: the key-stationary kernel stores
+ *    dS (bf16) in the workspace and a second kernel writes every accumulator
+ *    row once as the sum of dS K over the key blocks the row can see;
  *  - shape->dq_algo == ATTN_DQ_ATOMIC: the partials are added with fp32
  *    atomics, or, when shape->deterministic, in a fixed order per dQ tile so
  *    that repeated runs are bitwise identical.  The accumulator must then

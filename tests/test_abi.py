@@ -56,6 +56,11 @@ def test_workspace_size_formula():
     acc = (acc + 255) // 256 * 256
     sem = (2 * 4 * 2 * 4 + 255) // 256 * 256
     assert ws_bytes(s) == acc + sem + 256
+    # stored dS: + table of (batch + 1) int32 + Hq x (B ceil(Sq/32)) x ceil(Sk/128) blocks of 32 x 128 bf16
+    s = shape(dq_algo=L.ATTN_DQ_STORED_DS)
+    table = 256
+    blocks = 4 * (2 * 4) * 1 * 32 * 128 * 2
+    assert ws_bytes(s) == acc + sem + 256 + table + blocks
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -69,6 +74,7 @@ def test_workspace_size_formula():
     (dict(softmax_scale=float("nan")), L.ATTN_ERR_BAD_SHAPE),
     (dict(batch=1, seqlen_q=(1 << 23) + 1, num_heads_q=16, num_heads_kv=16), L.ATTN_ERR_BAD_SHAPE),
     (dict(dq_algo=5), L.ATTN_ERR_UNSUPPORTED),
+    (dict(dq_algo=L.ATTN_DQ_STORED_DS, dtype=L.ATTN_DTYPE_F32), L.ATTN_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, status):
     s = shape(**kw)

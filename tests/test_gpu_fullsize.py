@@ -120,7 +120,8 @@ def test_fp32_workload_full():
         assert_close(n, to_host(gg), r, "f32")
 
 
-@pytest.mark.parametrize("dq_algo,deterministic", [("separate", False), ("atomic", False), ("atomic", True)])
+@pytest.mark.parametrize("dq_algo,deterministic",
+                         [("separate", False), ("stored_ds", False), ("atomic", False), ("atomic", True)])
 def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
     p = datagen.workload("c2", deterministic=deterministic)
     x, dev, kw, cu = setup(p)
@@ -139,20 +140,22 @@ def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
         assert_close(n, to_host(gg), r, "bf16")
 
 
-@pytest.mark.parametrize("dq_algo", ["separate", "atomic"])
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
 def test_headline_causal_sampled(dq_algo):
     sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)], dq_algo=dq_algo)
 
 
-def test_headline_noncausal_sampled():
-    sampled_check(datagen.workload("c3nc"), [(1, 7)])
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
+def test_headline_noncausal_sampled(dq_algo):
+    sampled_check(datagen.workload("c3nc"), [(1, 7)], dq_algo=dq_algo)
 
 
-def test_varlen_sampled():
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
+def test_varlen_sampled(dq_algo):
     p = datagen.workload("c4")
     longest = int(np.argmax(p.lengths_q))
     shortest = int(np.argmin(p.lengths_q))
-    sampled_check(p, [(shortest, 0), (longest, 31)])
+    sampled_check(p, [(shortest, 0), (longest, 31)], dq_algo=dq_algo)
 
 
 def test_gqa_atomic_sampled():
@@ -164,5 +167,6 @@ def test_gqa_deterministic_sampled_and_reproducible():
     sampled_check(datagen.workload("c5", deterministic=True), [(0, 7)], repeats=3, dq_algo="atomic")
 
 
-def test_gqa_separate_pass_sampled_and_reproducible():
-    sampled_check(datagen.workload("c5"), [(0, 3)], repeats=2, dq_algo="separate")
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
+def test_gqa_atomic_free_modes_sampled_and_reproducible(dq_algo):
+    sampled_check(datagen.workload("c5"), [(0, 3)], repeats=2, dq_algo=dq_algo)
