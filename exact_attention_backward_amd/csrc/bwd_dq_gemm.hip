@@ -3,14 +3,15 @@
 // Source File" (stage 7), as a pass of its own over the dS blocks the dK/dV
 // kernel stored, so that no partial dQ is ever added with atomics.
 //
-// One workgroup (4 waves) owns 128 query rows of one (sequence, q-head); wave
-// w owns the 32-row dS block 4m + w.  Per 64-key stage the workgroup copies
-// the K rows into LDS and each wave its half of its dS block (both with
-// buffer_load ... lds, three stages in flight in a ring of four), then each
-// wave adds the 32 x 64 product dS K into its fp32 dQ rows: the A operand comes in the stored lane
-// order (one conflict-free 16-byte LDS read per 16-key slice), the B operand
-// K^T through the transposing LDS read.  The pass streams dS from HBM once:
-// it is bound by HBM bandwidth, not by the matrix cores.
+// One workgroup (4 waves) owns 256 query rows of one (sequence, q-head); wave
+// w owns the two 32-row dS blocks 8m + 2w and 8m + 2w + 1.  Per 64-key stage
+// the workgroup copies the K rows into LDS and each wave its part of its two
+// dS blocks (both with buffer_load ... lds, two stages in flight in a ring of
+// three), then each wave adds the 64 x 64 product dS K into its fp32 dQ rows:
+// the A operands come in the stored lane order (one conflict-free 16-byte
+// LDS read per 16-key slice and block), the B operand K^T through the
+// transposing LDS read, each B read feeding both blocks' MFMAs.  LDS traffic
+// per MFMA, not the matrix cores, bounds this pass besides HBM.
 #include "common.h"
 #include "launch.h"
 
@@ -20,22 +21,24 @@ namespace {
 constexpr int kGWaves = 4;
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int kGXcds = 8;
+constexpr int kGRB = 2;   // 32-row dS blocks per wave
 
 template <int HD>
 struct DqgCfg {
-    static constexpr int BQ = kGWaves * kDsRows;    // query rows per workgroup
+    static constexpr int BQ = kGWaves * kGRB * kDsRows;   // query rows per workgroup
     static constexpr int BN = kDsKeys;              // keys per dS block
-    static constexpr int BS = BN / 2;               // keys per pipeline stage (half a block)
+    static constexpr int BS = 64;                   // keys per pipeline stage
+    static constexpr int SPB = BN / BS;             // stages per dS block
     static constexpr int ROWB = HD * 2;
     static constexpr int K_BYTES = BS * ROWB;
-    static constexpr int DS_HALF = kDsBlockBytes / 2;   // one wave's half block
-    static constexpr int STAGE = K_BYTES + kGWaves * DS_HALF;
-    static constexpr int NS = 4;                    // ring of stages
+    static constexpr int DS_PART = kDsBlockBytes / SPB;   // one block's part per stage
+    static constexpr int STAGE = K_BYTES + kGWaves * kGRB * DS_PART;
+    static constexpr int NS = 3;                    // ring of stages
     static constexpr int PD = NS - 1;               // stages in flight ahead
     static constexpr int LDS_BYTES = NS * STAGE;
     static constexpr int NDB = HD / 32;
     static constexpr int KOPS = BS * (ROWB / 16) / 64 / kGWaves;   // K copy instructions per wave and stage
-    static constexpr int OPS = KOPS + DS_HALF / 1024;               // copy instructions per wave and stage
+    static constexpr int OPS = KOPS + kGRB * DS_PART / 1024;        // copy instructions per wave and stage
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(BS * (ROWB / 16) % (64 * kGWaves) == 0, "K tile split");
     static_assert(OPS * (PD - 1) < 64, "vmcnt range");
@@ -63,22 +66,149 @@ __device__ __forceinline__ void g_wait_vmem_but() {
 
 }  // namespace
 
+// dQ rows of query tile m (256 rows) of q-head hq in sequence b.
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
+__device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
+                                          char* smem) {
     using C = DqgCfg<HD>;
     constexpr int BQ = C::BQ, BN = C::BN;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;
     const int l32 = lane & 31;
+    const int i0 = m * BQ;
+    if (i0 >= si.len_q) return;
+    const bool varlen = a.cu_q != nullptr;
+    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+    const int nblk_k = (si.len_k + BN - 1) / BN;
+    const long long qb0 = varlen ? (long long)a.ds_qb_base[b] : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows);
 
-    // ---- which query tile: all tiles of all q-heads of one (sequence,
-    // kv-head) on one XCD, so their K reads share an L2; heaviest first
+    // last key block a 32-row block can see (-1: none, or no stored block:
+    // a block past the table only comes from overlapping, malformed cu_seqlens)
+    auto last_block = [&](int lq) {
+        if (lq * kDsRows >= si.len_q || qb0 + lq >= a.ds_qb) return -1;
+        if (!CAUSAL) return nblk_k - 1;
+        const int x = min((lq + 1) * kDsRows, si.len_q) - 1 + off;   // last visible key of the block's last row
+        return x < 0 ? -1 : min(nblk_k - 1, x / BN);
+    };
+    const int lq0 = m * (BQ / kDsRows) + kGRB * w;   // this wave's first 32-row block within the sequence
+    int n_last_b[kGRB];
+#pragma unroll
+    for (int r = 0; r < kGRB; ++r) n_last_b[r] = last_block(lq0 + r);
+    const int n_last_w = max(n_last_b[0], n_last_b[kGRB - 1]);
+    int n_last = -1;   // the workgroup's last key block: that of its last block with rows
+    for (int lq = m * (BQ / kDsRows); lq < (m + 1) * (BQ / kDsRows); ++lq) n_last = max(n_last, last_block(lq));
+
+    const long long kstride = (long long)a.hkv * HD;
+    const char* kbytes = reinterpret_cast<const char*>(a.k) + ((long long)si.k0 * kstride + (long long)hkv * HD) * 2;
+    const char* dsb = reinterpret_cast<const char*>(a.ds) + ((long long)hq * a.ds_qb + qb0 + lq0) * a.ds_nn * kDsBlockBytes;
+    const long long blk_stride = (long long)a.ds_nn * kDsBlockBytes;   // next 32-row block
+
+    const unsigned lds0 = lds_addr(smem);
+    // K copy plan: instruction t of wave w fills LDS segment w + 4t of a stage
+    int kvoff[C::KOPS];
+#pragma unroll
+    for (int t = 0; t < C::KOPS; ++t) {
+        constexpr int CPR = C::ROWB / 16;
+        const int sl = (w + t * kGWaves) * 64 + lane;
+        const int r = sl / CPR;
+        kvoff[t] = r * (int)(kstride * 2) + ((sl % CPR) ^ swz_key<C::ROWB>(r)) * 16;
+    }
+    // stage u holds keys BS u .. BS u + BS - 1 (part hf = u % SPB of key block
+    // u / SPB) and the matching parts of every wave's dS blocks (zeros for a
+    // block whose rows see none of these keys); every wave issues OPS copies
+    // per stage, empty ones past the last stage, so that one wait count
+    // serves the whole loop
+    const int n_stage = C::SPB * (n_last + 1);
+    auto issue = [&](int u) {
+        const unsigned base = lds0 + (u % C::NS) * C::STAGE;
+        const int n = u / C::SPB, hf = u % C::SPB;
+        const bool live = u < n_stage;
+        const int rows = live ? max(min(si.len_k - u * C::BS, C::BS), 0) : 0;
+        const i32x4 kr = rsrc_words(kbytes + (long long)u * C::BS * kstride * 2, (unsigned)(rows * kstride * 2));
+#pragma unroll
+        for (int t = 0; t < C::KOPS; ++t) dma_to_lds16(kr, base + (w + t * kGWaves) * 1024, kvoff[t]);
+#pragma unroll
+        for (int r = 0; r < kGRB; ++r) {
+            const bool mine = live && n <= n_last_b[r];
+            const i32x4 dr = rsrc_words(dsb + r * blk_stride + (long long)n * kDsBlockBytes + hf * C::DS_PART,
+                                        mine ? C::DS_PART : 0);
+#pragma unroll
+            for (int t = 0; t < C::DS_PART / 1024; ++t)
+                dma_to_lds16_nt(dr, base + C::K_BYTES + (kGRB * w + r) * C::DS_PART + t * 1024, t * 1024 + lane * 16);
+        }
+    };
+
+    f32x16 acc[kGRB][C::NDB];
+#pragma unroll
+    for (int r = 0; r < kGRB; ++r) {
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[r][d][v] = 0.f;
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < C::PD; ++u) issue(u);
+    for (int u = 0; u < n_stage; ++u) {
+        // stage u has landed for this wave (the PD - 1 later ones may still
+        // fly); after the barrier for all, and every wave is done with stage
+        // u - 1, whose buffer receives stage u + PD
+        g_wait_vmem_but<C::OPS * (C::PD - 1)>();
+        __syncthreads();
+        issue(u + C::PD);
+        if (u / C::SPB <= n_last_w) {
+            const char* stage = smem + (u % C::NS) * C::STAGE;
+            const char* ds = stage + C::K_BYTES + kGRB * w * C::DS_PART;
+#pragma unroll
+            for (int sl = 0; sl < C::BS / 16; ++sl) {
+                bf16x8 av[kGRB];
+#pragma unroll
+                for (int r = 0; r < kGRB; ++r)
+                    av[r] = __builtin_bit_cast(bf16x8, lds_read16(ds, r * C::DS_PART + sl * 1024 + lane * 16));
+#pragma unroll
+                for (int d = 0; d < C::NDB; ++d) {
+                    const bf16x8 bk = g_read_col<C::ROWB>(stage, 16 * sl + 8 * h, 16 * sl + 8 * h + 4, 32 * d, lane);
+#pragma unroll
+                    for (int r = 0; r < kGRB; ++r) mma16(acc[r][d], av[r], bk);
+                }
+            }
+        }
+    }
+    g_wait_vmem_but<0>();   // the empty copies past the end have retired before the waves exit
+
+    // ---- this wave's dQ rows, written once (unscaled; the postprocess applies s)
+    const long long row0 = varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
+#pragma unroll
+    for (int r = 0; r < kGRB; ++r) {
+        const int r0 = (lq0 + r) * kDsRows;
+        float* dqa = a.dq_acc + (row0 + r0) * HD;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rr = acc_row(v, h);
+                if (r0 + rr < si.len_q) dqa[(long long)rr * HD + 32 * d + l32] = acc[r][d][v];
+            }
+        }
+    }
+}
+
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
+    using C = DqgCfg<HD>;
+    constexpr int BQ = C::BQ;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    // ---- which query tiles: all tiles of all q-heads of one (sequence,
+    // kv-head) on one XCD, so their K reads share an L2
     const int G = a.hq / a.hkv;
     const int nblk_q = (a.seqlen_q + BQ - 1) / BQ;
-    const int per_group = nblk_q * G;
+    // causal: workgroup p takes query tiles p and nblk_q - 1 - p, whose key
+    // ranges add up to the same length for every p (balanced work)
+    const int n_pair = CAUSAL ? (nblk_q + 1) / 2 : nblk_q;
+    const int per_group = n_pair * G;
     int grp, slot;
     {
         const int groups = a.hkv * a.batch;
@@ -93,104 +223,21 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     }
     const int hkv = grp % a.hkv;
     const int b = grp / a.hkv;
-    const int hq = hkv * G + slot / nblk_q;
-    const int m = CAUSAL ? nblk_q - 1 - slot % nblk_q : slot % nblk_q;
+    const int hq = hkv * G + slot / n_pair;
+    const int p = slot % n_pair;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
-    const int i0 = m * BQ;
-    if (i0 >= si.len_q) return;
-    const bool varlen = a.cu_q != nullptr;
-    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
-    const int nblk_k = (si.len_k + BN - 1) / BN;
-
-    // last key block each wave's rows can see (-1: none), and the workgroup's
-    auto last_block = [&](int r0) {
-        if (r0 >= si.len_q) return -1;
-        if (!CAUSAL) return nblk_k - 1;
-        const int x = min(r0 + kDsRows, si.len_q) - 1 + off;   // last visible key of the block's last row
-        return x < 0 ? -1 : min(nblk_k - 1, x / BN);
-    };
-    const int lq = m * (BQ / kDsRows) + w;   // this wave's 32-row block within the sequence
-    const long long qb0 = varlen ? (long long)a.ds_qb_base[b] : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows);
-    // (a block past the table only comes from overlapping, malformed cu_seqlens)
-    const int n_last_w = qb0 + lq < a.ds_qb ? last_block(lq * kDsRows) : -1;
-    const int n_last = last_block(i0 + BQ - kDsRows < si.len_q ? i0 + BQ - kDsRows
-                                                               : ((si.len_q - 1) / kDsRows) * kDsRows);
-
-    const long long kstride = (long long)a.hkv * HD;
-    const char* kbytes = reinterpret_cast<const char*>(a.k) + ((long long)si.k0 * kstride + (long long)hkv * HD) * 2;
-    const char* dsb = reinterpret_cast<const char*>(a.ds) + ((long long)hq * a.ds_qb + qb0 + lq) * a.ds_nn * kDsBlockBytes;
-
-    const unsigned lds0 = lds_addr(smem);
-    // K copy plan: instruction t of wave w fills LDS segment w + 4t of a stage
-    int kvoff[C::KOPS];
-#pragma unroll
-    for (int t = 0; t < C::KOPS; ++t) {
-        constexpr int CPR = C::ROWB / 16;
-        const int sl = (w + t * kGWaves) * 64 + lane;
-        const int r = sl / CPR;
-        kvoff[t] = r * (int)(kstride * 2) + ((sl % CPR) ^ swz_key<C::ROWB>(r)) * 16;
-    }
-    // stage u holds keys 64u .. 64u + 63 (half hf = u % 2 of key block u / 2)
-    // and every wave's matching half of its dS block; every wave issues OPS
-    // copies per stage, empty ones past the last stage, so that one wait
-    // count serves the whole loop
-    const int n_stage = 2 * (n_last + 1);
-    auto issue = [&](int u) {
-        const unsigned base = lds0 + (u % C::NS) * C::STAGE;
-        const int n = u >> 1, hf = u & 1;
-        const bool live = u < n_stage;
-        const int rows = live ? max(min(si.len_k - u * C::BS, C::BS), 0) : 0;
-        const i32x4 kr = rsrc_words(kbytes + (long long)u * C::BS * kstride * 2, (unsigned)(rows * kstride * 2));
-#pragma unroll
-        for (int t = 0; t < C::KOPS; ++t) dma_to_lds16(kr, base + (w + t * kGWaves) * 1024, kvoff[t]);
-        const bool mine = live && n <= n_last_w;
-        const i32x4 dr = rsrc_words(dsb + (long long)n * kDsBlockBytes + hf * C::DS_HALF, mine ? C::DS_HALF : 0);
-#pragma unroll
-        for (int t = 0; t < C::DS_HALF / 1024; ++t)
-            dma_to_lds16(dr, base + C::K_BYTES + w * C::DS_HALF + t * 1024, t * 1024 + lane * 16);
-    };
-
-    f32x16 acc[C::NDB];
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[d][v] = 0.f;
-    }
-
-#pragma unroll
-    for (int u = 0; u < C::PD; ++u) issue(u);
-    for (int u = 0; u < n_stage; ++u) {
-        // stage u has landed for this wave (the PD - 1 later ones may still
-        // fly); after the barrier for all, and every wave is done with stage
-        // u - 1, whose buffer receives stage u + PD
-        g_wait_vmem_but<C::OPS * (C::PD - 1)>();
-        __syncthreads();
-        issue(u + C::PD);
-        if ((u >> 1) <= n_last_w) {
-            const char* stage = smem + (u % C::NS) * C::STAGE;
-            const char* ds = stage + C::K_BYTES + w * C::DS_HALF;
-#pragma unroll
-            for (int sl = 0; sl < C::BS / 16; ++sl) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, lds_read16(ds, sl * 1024 + lane * 16));
-#pragma unroll
-                for (int d = 0; d < C::NDB; ++d)
-                    mma16(acc[d], av, g_read_col<C::ROWB>(stage, 16 * sl + 8 * h, 16 * sl + 8 * h + 4, 32 * d, lane));
-            }
+    const int nblk_q_seq = (si.len_q + BQ - 1) / BQ;   // this sequence's query tiles
+    if (CAUSAL) {
+        // the longer tile first, then its partner (once the first tile's LDS
+        // stages are no longer read)
+        const int m2 = nblk_q_seq - 1 - p;
+        if (m2 > p) {
+            gemm_tile<HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);
+            __syncthreads();
         }
-    }
-    g_wait_vmem_but<0>();   // the empty copies past the end have retired before the waves exit
-
-    // ---- this wave's dQ rows, written once (unscaled; the postprocess applies s)
-    const long long row0 = varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
-    const int r0 = lq * kDsRows;
-    float* dqa = a.dq_acc + (row0 + r0) * HD;
-#pragma unroll
-    for (int d = 0; d < C::NDB; ++d) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = acc_row(v, h);
-            if (r0 + r < si.len_q) dqa[(long long)r * HD + 32 * d + l32] = acc[d][v];
-        }
+        if (p < nblk_q_seq && p <= m2) gemm_tile<HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+    } else {
+        gemm_tile<HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
     }
 }
 
@@ -229,8 +276,10 @@ void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, 
 }
 
 void launch_bwd_dq_gemm(const BwdArgs& a, int hd, bool causal, hipStream_t st) {
-    const int nblk_q = (a.seqlen_q + kGWaves * kDsRows - 1) / (kGWaves * kDsRows);
-    const unsigned grid = (unsigned)(nblk_q * a.hq * a.batch);
+    const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;
+    static_assert(DqgCfg<128>::BQ == DqgCfg<64>::BQ, "one query tiling");
+    const int n_pair = causal ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
+    const unsigned grid = (unsigned)(n_pair * a.hq * a.batch);
     if (hd == 64) {
         if (causal) bwd_dq_gemm_kernel<64, true><<<grid, kGThreads, 0, st>>>(a);
         else bwd_dq_gemm_kernel<64, false><<<grid, kGThreads, 0, st>>>(a);

@@ -592,13 +592,13 @@ struct KvCfg {
     static_assert(BM * 4 <= 256, "LSE/D tile in one 256-byte slot");
 };
 
+// All work of one key tile n of sequence b, kv-head hkv (the body of bwd_kv_kernel).
 template <int HD, bool CAUSAL, bool STORE_DS>
-__global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
+__device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
     using C = KvCfg<HD>;
     using T = bf16_t;
     using op_t = bf16x8;
     constexpr int BM = C::BM, NMB = C::NMB, ROWB = C::ROWB;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -606,23 +606,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     const int pair = w & 3;    // keys 32 * pair .. + 31 of the tile
     const int h = lane >> 5;
     const int l32 = lane & 31;
-
-    // ---- key tile: all key tiles of one (sequence, kv-head) on one XCD
-    int grp, n;
-    {
-        const int groups = a.hkv * a.batch;
-        if (groups % kXcds == 0) {
-            const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-            grp = (slot / a.nblk_n) * kXcds + xcd;
-            n = slot % a.nblk_n;
-        } else {
-            grp = blockIdx.x / a.nblk_n;
-            n = blockIdx.x % a.nblk_n;
-        }
-    }
-    const int hkv = grp % a.hkv;
-    const int b = grp / a.hkv;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
     if (n * kBN >= si.len_k) return;
     const bool varlen = a.cu_q != nullptr;
     const int G = a.hq / a.hkv;
@@ -919,8 +902,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs) {
                     const op_t f = read_op_col<T, TROWB>(tr, 16 * cs + 8 * h, 16 * cs + 8 * h + 4, 32 * mb, lane);
+                    // non-temporal: dS is read once, by the next pass, and must not
+                    // displace the Q/dO tiles the key tiles share in the L2
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f), dst,
-                                                           (2 * pair + cs) * 1024 + lane * 16, 0, 0);
+                                                           (2 * pair + cs) * 1024 + lane * 16, 0, 2);
                 }
             }
         }
@@ -947,6 +932,43 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     }
 }
 
+
+template <int HD, bool CAUSAL, bool STORE_DS>
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[KvCfg<HD>::LDS_BYTES];
+    // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
+    // a causal mask key tile n is seen by a number of query tiles that falls
+    // linearly with n, so workgroup p takes the tiles p and (last - p), which
+    // together always cost about the same.
+    const int per_group = CAUSAL ? (a.nblk_n + 1) / 2 : a.nblk_n;
+    int grp, p;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+            grp = (slot / per_group) * kXcds + xcd;
+            p = slot % per_group;
+        } else {
+            grp = blockIdx.x / per_group;
+            p = blockIdx.x % per_group;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    if (CAUSAL) {
+        const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
+        const int n2 = nk - 1 - p;
+        if (p <= n2) kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
+        if (n2 > p) {
+            __syncthreads();   // the first tile's LDS ring and P slots are free again
+            kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, n2, si, smem);
+        }
+    } else {
+        kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
+    }
+}
+
 int bwd_block_m(int dtype, int head_dim) {
     if (head_dim == 128) return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 128>::BM : BwdCfg<bf16_t, 128>::BM;
     static_assert(BwdCfg<bf16_t, 128, true>::BM == BwdCfg<bf16_t, 128, false>::BM, "one query tiling");
@@ -957,16 +979,18 @@ template <class T, int HD>
 static void launch_bwd_t(const BwdArgs& a, bool causal, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
+        // causal: one workgroup per pair of key tiles
+        const unsigned kv_grid = causal ? (unsigned)((a.nblk_n + 1) / 2 * a.hkv * a.batch) : grid;
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE) {
-            if (causal) bwd_kv_kernel<HD, true, false><<<grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<HD, false, false><<<grid, kKvThreads, 0, st>>>(a);
+            if (causal) bwd_kv_kernel<HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<HD, false, false><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
         if (dq_algo == ATTN_DQ_STORED_DS) {
-            if (causal) bwd_kv_kernel<HD, true, true><<<grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<HD, false, true><<<grid, kKvThreads, 0, st>>>(a);
+            if (causal) bwd_kv_kernel<HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<HD, false, true><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
     }

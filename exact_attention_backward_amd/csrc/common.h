@@ -178,6 +178,11 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 __device__ __forceinline__ void dma_to_lds16(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
+// The same with the non-temporal hint, for data read once (streams that
+// should not displace reused tiles from the L2).
+__device__ __forceinline__ void dma_to_lds16_nt(i32x4 r, unsigned lds, int voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
+}
 __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
