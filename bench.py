@@ -28,8 +28,14 @@ METRIC = "attention-backward TFLOP/s (bf16, causal, S=4096, D=128) and % of MFMA
 # MI355X published dense peaks
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f) for f in ("bwd_main.hip", "bwd_dq.hip")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_c3_causal.json")
+MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f)
+             for f in ("bwd_main.hip", "bwd_dq.hip", "bwd_dq_gemm.hip")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_c3_causal_{}.json")
+KERNEL_DESC = {
+    "stored_ds": "attn_bwd (key-stationary dK/dV kernel storing dS + dQ = dS K pass)",
+    "separate": "attn_bwd (key-stationary dK/dV kernel + query-stationary dQ kernel)",
+    "atomic": "attn_bwd (key-stationary kernel with dQ atomics)",
+}
 
 
 def parse():
@@ -39,8 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--deterministic", action="store_true")
-    ap.add_argument("--dq-algo", default="separate", choices=["separate", "atomic"],
-                    help="dQ by a query-stationary second pass (default) or fp32 atomics")
+    ap.add_argument("--dq-algo", default=None, choices=["stored_ds", "separate", "atomic"],
+                    help="dQ from dS stored by the dK/dV kernel (default for bf16), by a query-stationary "
+                         "pass that recomputes S and dP (default for fp32), or by fp32 atomics")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
@@ -52,13 +59,14 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_entry(dq_algo):
-    """HBM bytes per attn_bwd call from the committed counter summary (taken
-    with the separate dQ pass), or None when a kernel source changed since the
-    counters were taken or another dQ algorithm runs."""
-    if not os.path.exists(TRAFFIC_FILE) or dq_algo != "separate":
+def traffic_entry(dq_algo, workload):
+    """HBM bytes per attn_bwd call from the committed counter summary of this
+    dQ algorithm on the headline workload, or None when there is none or a
+    kernel source changed since the counters were taken."""
+    path = TRAFFIC_FILE.format(dq_algo)
+    if workload != "c3" or not os.path.exists(path):
         return None
-    t = json.load(open(TRAFFIC_FILE))
+    t = json.load(open(path))
     if t.get("kernel_source_sha256_16") != "+".join(source_hash(p) for p in MAIN_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
@@ -131,6 +139,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
     p = datagen.workload(args.workload, deterministic=args.deterministic)
+    if args.dq_algo is None:
+        args.dq_algo = "stored_ds" if p.dtype == "bf16" else "separate"
     dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
     x = datagen.draw(p)
     dev = {k: torch.from_numpy(v).to(dt).cuda() for k, v in x.items()}
@@ -180,7 +190,7 @@ def main():
     rows_q = p.total_q
     elem = 2 if p.dtype == "bf16" else 4
     # preprocess: read O and dO, write D; the dQ accumulator is cleared only
-    # in the atomic dQ mode (the separate pass overwrites it)
+    # in the atomic dQ mode (the other modes overwrite it)
     accum = rows_q * p.heads_q * p.head_dim * 4
     pre_bytes = 2 * rows_q * p.heads_q * p.head_dim * elem + rows_q * p.heads_q * 4 + \
         (accum if args.dq_algo == "atomic" else 0)
@@ -208,14 +218,13 @@ def main():
             "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
         },
         "roofline": {
-            "kernel": "attn_bwd (key-stationary dK/dV kernel + query-stationary dQ kernel)"
-                      if args.dq_algo == "separate" else "attn_bwd (key-stationary kernel with dQ atomics)",
+            "kernel": KERNEL_DESC[args.dq_algo],
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": traffic_entry(args.dq_algo),
+            "traffic": traffic_entry(args.dq_algo, args.workload),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,
         },
