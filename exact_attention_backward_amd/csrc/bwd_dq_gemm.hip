@@ -8,9 +8,9 @@
 // the workgroup copies the K rows into LDS and each wave its part of its two
 // dS blocks (both with buffer_load ... lds, two stages in flight in a ring of
 // three), then each wave adds the 64 x 64 product dS K into its fp32 dQ rows:
-// the A operands come in the stored lane order (one conflict-free 16-byte
-// LDS read per 16-key slice and block), the B operand K^T through the
-// transposing LDS read, each B read feeding both blocks' MFMAs.  LDS traffic
+// the A operands come from the stored operand-register order through two
+// transposing LDS reads per 16-key slice and block, the B operand K^T through
+// the transposing LDS read too, each B read feeding both blocks' MFMAs.  LDS traffic
 // per MFMA, not the matrix cores, bounds this pass besides HBM.
 #include "common.h"
 #include "launch.h"
@@ -139,6 +139,16 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
         }
     };
 
+    // A operand of a 16-key slice from the stored chunks (see ds_chunk): two
+    // transposing reads; in each group of 16 lanes, source lane s points at
+    // rows 16c + 4 (s % 4) .. + 3 of key k0 + s / 4 (those rows sit in chunk
+    // lane 32 ((s % 4) & 1) + key, bytes 8 ((s % 4) >> 1) ..), so output lane
+    // u receives row 16c + u of keys k0 .. k0 + 3 (c = (lane / 16) % 2,
+    // k0 = 8 (lane / 32) for the first read, + 4 for the second)
+    const int ts = lane & 15, te = ts >> 2, tq = ts & 3;
+    const int abase = (((lane >> 4) & 1) * 64 + 32 * (tq & 1) + 8 * (lane >> 5) + te) * 16 + 8 * (tq >> 1);
+    const int aoff0 = abase + 64 * (tq & 1), aoff1 = abase + 64 * ((tq & 1) ^ 1);
+
     f32x16 acc[kGRB][C::NDB];
 #pragma unroll
     for (int r = 0; r < kGRB; ++r) {
@@ -163,10 +173,16 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
             const char* ds = stage + C::K_BYTES + kGRB * w * C::DS_PART;
 #pragma unroll
             for (int sl = 0; sl < C::BS / 16; ++sl) {
+                // keys 16 sl .. 16 sl + 15 of the stage: pair sl / 2 of its part, keys 16 (sl % 2) ..
+                const int so = (2 * (sl >> 1) * 64 + 16 * (sl & 1)) * 16;
                 bf16x8 av[kGRB];
 #pragma unroll
-                for (int r = 0; r < kGRB; ++r)
-                    av[r] = __builtin_bit_cast(bf16x8, lds_read16(ds, r * C::DS_PART + sl * 1024 + lane * 16));
+                for (int r = 0; r < kGRB; ++r) {
+                    const u32x2 x = lds_read_tr(ds, r * C::DS_PART + aoff0 + so);
+                    const u32x2 y = lds_read_tr(ds, r * C::DS_PART + aoff1 + so);
+                    const u32x4 wv = {x[0], x[1], y[0], y[1]};
+                    av[r] = __builtin_bit_cast(bf16x8, wv);
+                }
 #pragma unroll
                 for (int d = 0; d < C::NDB; ++d) {
                     const bf16x8 bk = g_read_col<C::ROWB>(stage, 16 * sl + 8 * h, 16 * sl + 8 * h + 4, 32 * d, lane);

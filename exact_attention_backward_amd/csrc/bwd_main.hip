@@ -709,14 +709,13 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     int cur_m = m_begin;                       // query tile of tile t
     int cur_g = 0;                             // q-head (within the group) of tile t
     int last_m = m_begin, last_g = 0;          // the same for tile t-1
-    int last2_m = m_begin, last2_g = 0;        // the same for tile t-2
     // stored-dS mode: first 32-row query block of this sequence, and whether
     // the key tile reaches past the sequence (its dS columns are then zeroed)
     const long long ds_qb0 = STORE_DS ? (varlen ? (long long)a.ds_qb_base[b]
                                                 : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows))
                                       : 0;
     const bool ragged_k = n * kBN + kBN > si.len_k;
-    constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per P-wave step
+    constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
     auto step = [&](int t, f32x16* xc, f32x16* xp) {
@@ -724,10 +723,10 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // tiles may still fly); after the barrier all waves' have, P of tile
         // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
         // receives tile t+3
-        // in the stored-dS mode each P-wave step also issues NST stores after
-        // its copies, so the tiles' copies are counted past them (steps with
-        // no dS to store store an empty range instead, to keep the count)
-        if (STORE_DS && role == 0)
+        // in the stored-dS mode each dS-wave step also issues NST stores after
+        // its copies, so the tiles' copies are counted past them (the first
+        // step has no dS; it stores an empty range instead, to keep the count)
+        if (STORE_DS && role == 1)
             wait_vmem_but<C::OPS * (C::PD - 1) + NST * C::PD>();
         else
             wait_vmem_but<C::OPS * (C::PD - 1)>();
@@ -773,46 +772,23 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             cur_m = m_begin;
             ++cur_g;
         }
-        const int prev2_m = last2_m, prev2_g = last2_g;   // coordinates of tile t-2
-        last2_m = last_m;
-        last2_g = last_g;
+        const int prev_m = last_m, prev_g = last_g;   // coordinates of tile t-1
         last_m = tile_m;
         last_g = tile_g;
-        (void)prev2_m;
-        (void)prev2_g;
-
-        if (STORE_DS && role == 0) {
-            // dS (bf16) of tile t-2, which the partner dS wave left transposed
-            // as [key][row] in this pair's P slot t % 2 during the last step,
-            // to the dS blocks in MFMA A-operand order (read before this
-            // step's P overwrites the slot)
-            constexpr int TROWB = BM * 2;
-            const char* tr = smem + pslots + (t & 1) * C::PSLOT;
-            const bool have = t >= 2;   // t - 2 < n_tiles holds for every step
-            const int hq = hkv * G + prev2_g;
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                const int lq = prev2_m * (BM / kDsRows) + mb;   // 32-row block within the sequence
-                // no block yet, or blocks past the sequence: an empty range
-                // (the last test only fails for overlapping, malformed cu_seqlens)
-                const bool ok = have && lq * kDsRows < si.len_q && ds_qb0 + lq < a.ds_qb;
-                const rsrc_t dst = make_rsrc(
-                    reinterpret_cast<char*>(a.ds) + (((long long)hq * a.ds_qb + ds_qb0 + lq) * a.ds_nn + n) *
-                                                        kDsBlockBytes,
-                    ok ? kDsBlockBytes : 0);
-#pragma unroll
-                for (int cs = 0; cs < 2; ++cs) {
-                    const op_t f = read_op_col<T, TROWB>(tr, 16 * cs + 8 * h, 16 * cs + 8 * h + 4, 32 * mb, lane);
-                    // non-temporal: read once, by the dQ pass
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f), dst,
-                                                           (2 * pair + cs) * 1024 + lane * 16, 0, 2);
-                }
-            }
-        }
+        (void)prev_m;
+        (void)prev_g;
 
         // the tile whose second product this wave computes now
         const int tt = role == 0 ? t : t - 1;
-        if (tt < 0 || tt >= n_tiles) return;
+        if (tt < 0 || tt >= n_tiles) {
+            if (STORE_DS && role == 1) {   // the dS wave's first step: empty stores
+                const rsrc_t none = make_rsrc(a.ds, 0);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int k = 0; k < NST; ++k) __builtin_amdgcn_raw_buffer_store_b128(z, none, lane * 16, 0, 2);
+            }
+            return;
+        }
         const unsigned buf = role == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
                                        : prev_buf;
         const int ps = pslots + (tt & 1) * C::PSLOT + lane * 16;
@@ -900,28 +876,37 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
         if (STORE_DS && role == 1) {
-            // dS (bf16) of this pair's 32 keys, transposed to [key][row] in
-            // this pair's P slot of tile t-1 (that P is already in registers);
-            // the P wave stores it to the dS blocks in the next step.  Written
-            // after the dK MFMAs are issued, which run meanwhile.
-            constexpr int TROWB = BM * 2;
-            char* tr = smem + pslots + (tt & 1) * C::PSLOT;
+            // dS (bf16) of this pair's 32 keys straight from the MFMA operand
+            // registers to the dS block: chunk (pair, c, lane) holds, for key
+            // 32 pair + lane % 32, the rows 16c + 4 (lane / 32) + 0..3 and
+            // 16c + 8 + 4 (lane / 32) + 0..3 (the dQ pass reads it back with
+            // transposing reads).  Issued after the dK MFMAs, which run meanwhile.
+            const int hq = hkv * G + prev_g;
 #pragma unroll
-            for (int c = 0; c < C::NIC; ++c) {
-                const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
-                lds_write(tr, swz<TROWB>(l32, (16 * c + 4 * h) * 2), u32x2{wv[0], wv[1]});
-                lds_write(tr, swz<TROWB>(l32, (16 * c + 8 + 4 * h) * 2), u32x2{wv[2], wv[3]});
+            for (int mb = 0; mb < NMB; ++mb) {
+                const int lq = prev_m * (BM / kDsRows) + mb;   // 32-row block within the sequence
+                // blocks past the sequence get an empty range (the second test
+                // only fails for overlapping, malformed cu_seqlens)
+                const bool ok = lq * kDsRows < si.len_q && ds_qb0 + lq < a.ds_qb;
+                const rsrc_t dst = make_rsrc(
+                    reinterpret_cast<char*>(a.ds) + (((long long)hq * a.ds_qb + ds_qb0 + lq) * a.ds_nn + n) *
+                                                        kDsBlockBytes,
+                    ok ? kDsBlockBytes : 0);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    // non-temporal: read once, by the dQ pass
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, opa[2 * mb + c]), dst,
+                                                           ds_chunk(2 * pair + c, lane) * 16, 0, 2);
+                }
             }
         }
     };
 
-    // the dS wave keeps X of tile t until step t+1: two register sets, unrolled
-    // by two; in the stored-dS mode one more step stores the last dS
+    // the dS wave keeps X of tile t until step t+1: two register sets, unrolled by two
     f32x16 xA[NMB], xB[NMB];
-    const int t_last = n_tiles + (STORE_DS ? 1 : 0);
-    for (int t = 0; t <= t_last; t += 2) {
+    for (int t = 0; t <= n_tiles; t += 2) {
         step(t, xA, xB);
-        if (t + 1 <= t_last) step(t + 1, xB, xA);
+        if (t + 1 <= n_tiles) step(t + 1, xB, xA);
     }
 
     // ---- epilogue: dV (P wave) or dK = s * sum dS^T Q (dS wave); rows past

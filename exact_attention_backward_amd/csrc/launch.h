@@ -65,12 +65,17 @@ struct BwdArgs {
     int ds_nn;           // 128-key blocks per query block
 };
 
-// dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16, held as
-// eight 16-key slices of 1 KiB, each in the lane order of an MFMA A operand
-// (lane l: row l % 32, keys 8 (l / 32) .. + 7 of the slice, 16 bytes).
+// dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16 (8 KiB),
+// in the register order of the key-stationary kernel's MFMA operands: 16-byte
+// chunk (g, l) for g = 2 p + c (keys 32p .. 32p + 31, rows 16c .. 16c + 15)
+// holds key 32 p + l % 32, rows 16c + 4 (l / 32) + 0..3 and
+// 16c + 8 + 4 (l / 32) + 0..3.  The chunk of lane l sits at slot ds_chunk(g, l)
+// (lanes 32..63 are moved by four chunks, so that the dQ pass's transposing
+// reads of keys k and k + 32 lanes apart hit different LDS banks).
 constexpr int kDsRows = 32;
 constexpr int kDsKeys = 128;
 constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
+__host__ __device__ constexpr int ds_chunk(int g, int l) { return g * 64 + (l ^ ((l >> 5) << 2)); }
 
 // Query rows per tile of the main kernel (keys per tile are fixed at 128).
 int bwd_block_m(int dtype, int head_dim);
