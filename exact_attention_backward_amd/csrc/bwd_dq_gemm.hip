@@ -4,10 +4,11 @@
 // kernel stored, so that no partial dQ is ever added with atomics.
 //
 // One workgroup (4 waves) owns 256 query rows of one (sequence, q-head); wave
-// w owns the two 32-row dS blocks 8m + 2w and 8m + 2w + 1.  Per 64-key stage
+// w owns the two 32-row dS blocks 8m + 2w and 8m + 2w + 1.  Per 32-key stage
 // the workgroup copies the K rows into LDS and each wave its part of its two
 // dS blocks (both with buffer_load ... lds, two stages in flight in a ring of
-// three), then each wave adds the 64 x 64 product dS K into its fp32 dQ rows:
+// three; 72 KiB of LDS, so two workgroups share a CU), then each wave adds the
+// 64 x 32 product dS K into its fp32 dQ rows:
 // the A operands come from the stored operand-register order through two
 // transposing LDS reads per 16-key slice and block, the B operand K^T through
 // the transposing LDS read too, each B read feeding both blocks' MFMAs.  LDS traffic
@@ -27,7 +28,7 @@ template <int HD>
 struct DqgCfg {
     static constexpr int BQ = kGWaves * kGRB * kDsRows;   // query rows per workgroup
     static constexpr int BN = kDsKeys;              // keys per dS block
-    static constexpr int BS = 64;                   // keys per pipeline stage
+    static constexpr int BS = 32;                   // keys per pipeline stage
     static constexpr int SPB = BN / BS;             // stages per dS block
     static constexpr int ROWB = HD * 2;
     static constexpr int K_BYTES = BS * ROWB;
@@ -173,7 +174,8 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
             const char* ds = stage + C::K_BYTES + kGRB * w * C::DS_PART;
 #pragma unroll
             for (int sl = 0; sl < C::BS / 16; ++sl) {
-                // keys 16 sl .. 16 sl + 15 of the stage: pair sl / 2 of its part, keys 16 (sl % 2) ..
+                // keys 16 sl .. 16 sl + 15 of the stage: pair sl / 2 of its part (one pair
+                // when a stage holds 32 keys), keys 16 (sl % 2) ..
                 const int so = (2 * (sl >> 1) * 64 + 16 * (sl & 1)) * 16;
                 bf16x8 av[kGRB];
 #pragma unroll
