@@ -146,40 +146,17 @@ __device__ __forceinline__ void dq_wait_vmem_but(int n) {
 
 }  // namespace
 
+// dQ rows of query tile m (128 rows) of q-head hq in sequence b.
 template <class T, int HD, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
+                                        char* smem) {
     using C = DqCfg<T, HD>;
     using op_t = typename Elem<T>::op_t;
     constexpr int BQ = C::BQ, BN = C::BN;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int h = lane >> 5;
     const int l32 = lane & 31;
-
-    // ---- which query tile: all query tiles of all q-heads of one
-    // (sequence, kv-head) run on one XCD, so their K/V reads share an L2
-    const int G = a.hq / a.hkv;
-    const int per_group = a.nblk_m * G;          // workgroups of one (sequence, kv-head)
-    int grp, slot;
-    {
-        const int groups = a.hkv * a.batch;
-        if (groups % kXcds == 0) {
-            const int xcd = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
-            grp = (s / per_group) * kXcds + xcd;
-            slot = s % per_group;
-        } else {
-            grp = blockIdx.x / per_group;
-            slot = blockIdx.x % per_group;
-        }
-    }
-    const int hkv = grp % a.hkv;
-    const int b = grp / a.hkv;
-    const int hq = hkv * G + slot / a.nblk_m;
-    // heaviest (last) query tiles first: under a causal mask they see the most keys
-    const int m = CAUSAL ? a.nblk_m - 1 - slot % a.nblk_m : slot % a.nblk_m;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
     const int i0 = m * BQ;
     if (i0 >= si.len_q) return;
     const bool varlen = a.cu_q != nullptr;
@@ -270,6 +247,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
                 mma16(dpt[jb], av, doreg[c]);
             }
         }
+        if constexpr (sizeof(T) == 2) {
+            // all operand reads first, so the MFMA chains do not wait on LDS latency
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NJB * C::NC, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::NJB * C::NC, 0);
+        }
 
         // ---- P = exp2(S s log2e - LSE log2e), dS = P (dP - D); edge tiles test visibility
         auto softmax_grad = [&](auto masked) {
@@ -307,6 +289,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
                 mma16(dq[d], ads, bk);
             }
         }
+        if constexpr (sizeof(T) == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NJC * C::NDB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NJC * C::NDB, 0);
+        }
     }
 
     // ---- write this tile's dQ rows once (unscaled; the postprocess applies s)
@@ -321,9 +307,50 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
     }
 }
 
+
+template <class T, int HD, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
+    // ---- which query tiles: all query tiles of all q-heads of one (sequence,
+    // kv-head) run on one XCD, so their K/V reads share an L2.  Under a causal
+    // mask the keys a query tile sees grow linearly with its index, so
+    // workgroup p takes the tiles p and (last - p).
+    const int G = a.hq / a.hkv;
+    const int n_pair = CAUSAL ? (a.nblk_m + 1) / 2 : a.nblk_m;
+    const int per_group = n_pair * G;          // workgroups of one (sequence, kv-head)
+    int grp, slot;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
+            grp = (s / per_group) * kXcds + xcd;
+            slot = s % per_group;
+        } else {
+            grp = blockIdx.x / per_group;
+            slot = blockIdx.x % per_group;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const int hq = hkv * G + slot / n_pair;
+    const int p = slot % n_pair;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    if (CAUSAL) {
+        const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
+        const int m2 = nq - 1 - p;
+        if (m2 > p) {
+            dq_tile<T, HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            __syncthreads();   // its LDS ring is free again
+        }
+        if (p < nq && p <= m2) dq_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+    } else {
+        dq_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+    }
+}
+
 template <class T, int HD>
 static void launch_dq_t(const BwdArgs& a, bool causal, hipStream_t st) {
-    const unsigned grid = (unsigned)(a.nblk_m * a.hq * a.batch);
+    const unsigned grid = (unsigned)((causal ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
     if (causal)
         bwd_dq_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
     else
