@@ -4,9 +4,9 @@ oracle side and the HIP side of every test and of the benchmark.
 It holds no attention arithmetic: it draws normal samples, rounds them to the
 storage type, and packs varlen sequences.  Inputs are drawn with numpy's PCG64
 generator (``numpy.random.default_rng(seed)``) in the order Q, K, V, dO (for
-varlen, the sequence lengths first), as float32, then rounded to bfloat16 with
-round-to-nearest-even for the bf16 workloads, so both sides see identical
-values.
+varlen, the sequence lengths first), as float32, then rounded to bfloat16 or
+IEEE binary16 with round-to-nearest-even for the bf16 and fp16 workloads, so
+both sides see identical values.
 
 Workloads (sizes of the five configurations the method is measured on):
   c1  fp32, non-causal, B=1 H=2 S=128 D=64
@@ -14,6 +14,7 @@ Workloads (sizes of the five configurations the method is measured on):
   c3  bf16, B=4 H=16 S=4096 D=128, causal and non-causal; dO scaled by 0.1
   c4  bf16, causal, varlen: 8 sequences, lengths uniform in [128, 8192], H=32 D=128
   c5  bf16, causal, GQA: B=1 Hq=32 Hkv=8 S=8192 D=128
+  c3h the c3 causal shape with fp16 I/O (the same draws, rounded to fp16)
 """
 
 import math
@@ -22,13 +23,13 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Problem", "WORKLOADS", "workload", "draw", "round_to_bf16", "varlen_lengths"]
+__all__ = ["Problem", "WORKLOADS", "workload", "draw", "round_to_bf16", "round_to_f16", "varlen_lengths"]
 
 
 @dataclass(frozen=True)
 class Problem:
     """Shape and flags of one attention-backward problem."""
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "f16"
     batch: int            # dense batch, or number of sequences when varlen
     heads_q: int
     heads_kv: int
@@ -98,6 +99,8 @@ WORKLOADS = {
     "c4": _c4(),
     "c5": Problem("bf16", 1, 32, 8, 8192, 8192, 128, True, 1 / math.sqrt(128), 5,
                   name="c5_bf16_gqa_causal"),
+    "c3h": Problem("f16", 4, 16, 16, 4096, 4096, 128, True, 1 / math.sqrt(128), 3, do_scale=0.1,
+                   name="c3_f16_causal"),
 }
 
 
@@ -113,6 +116,14 @@ def round_to_bf16(x):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def round_to_f16(x):
+    """float32 array -> float32 array holding the nearest binary16 values
+    (RNE), using torch's conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float16).to(torch.float32).numpy()
 
 
 def draw(p: Problem):
@@ -141,4 +152,6 @@ def draw(p: Problem):
         do = do * np.float32(p.do_scale)
     if p.dtype == "bf16":
         q, k, v, do = (round_to_bf16(x) for x in (q, k, v, do))
+    elif p.dtype == "f16":
+        q, k, v, do = (round_to_f16(x) for x in (q, k, v, do))
     return {"q": q, "k": k, "v": v, "do": do}

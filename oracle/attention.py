@@ -56,6 +56,8 @@ __all__ = [
     "preprocess_delta",
     "round_f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "round_f32_to_f16_bits",
+    "f16_bits_to_f32",
     "postprocess_dq",
 ]
 
@@ -296,17 +298,64 @@ def bf16_bits_to_f32(bits):
     return b.view(np.float32)
 
 
+def round_f32_to_f16_bits(x):
+    """IEEE 754 binary16 bit patterns (uint16) of float32 values, round to
+    nearest, ties to even.
+
+    Written from the format's definition: 1 sign bit, 5 exponent bits (bias
+    15), 10 fraction bits; normal numbers from 2^-14 have a last-place unit of
+    2^(e - 10) for |x| in [2^e, 2^(e+1)), subnormals a unit of 2^-24.  The
+    value is rounded to a whole number of its unit (float64 holds every
+    float32 exactly, and scaling by a power of two is exact, so ``rint`` sees
+    the exact quotient); a result of 2^16 or more is infinity.  NaN becomes a
+    quiet NaN keeping the top fraction bits.
+    """
+    x32 = np.ascontiguousarray(np.asarray(x, np.float32))
+    u = x32.view(np.uint32)
+    a = np.abs(x32.astype(np.float64))
+    sign = ((u >> 16) & 0x8000).astype(np.uint32)
+    _, ex = np.frexp(a)                         # a = f 2^ex, f in [0.5, 1)
+    e = ex.astype(np.int64) - 1                 # a in [2^e, 2^(e+1)) for a > 0
+    unit = np.where(e >= -14, e - 10, -24)      # exponent of the last-place unit
+    val = np.ldexp(np.rint(np.ldexp(a, -unit)), unit)
+    over = ~(val < 65536.0)                     # overflow, infinities and NaN
+    val = np.where(over, 0.0, val)
+    normal = val >= 2.0 ** -14
+    fn, en = np.frexp(np.where(normal, val, 1.0))
+    bits_normal = ((en.astype(np.int64) - 1 + 15) << 10) + (np.ldexp(fn, 11).astype(np.int64) - 1024)
+    bits_sub = np.ldexp(val, 24).astype(np.int64)          # whole units of 2^-24 (1024 = 2^-14)
+    mag = np.where(normal, bits_normal, bits_sub)
+    mag = np.where(over, 0x7C00, mag)
+    is_nan = np.isnan(a)
+    mag = np.where(is_nan, 0x7E00 | ((u >> 13) & 0x3FF), mag)
+    return (sign | mag.astype(np.uint32)).astype(np.uint16)
+
+
+def f16_bits_to_f32(bits):
+    """float32 values of binary16 bit patterns (exact), from the definition."""
+    b = np.asarray(bits, np.uint16).astype(np.int64)
+    sgn = np.where(b & 0x8000, -1.0, 1.0)
+    ex = (b >> 10) & 0x1F
+    fr = b & 0x3FF
+    val = np.where(ex == 0, np.ldexp(fr.astype(np.float64), -24),
+                   np.ldexp((1024 + fr).astype(np.float64), ex - 25))
+    val = np.where(ex == 31, np.where(fr == 0, np.inf, np.nan), val)
+    return (sgn * val).astype(np.float32)
+
+
 def postprocess_dq(dq_accum, scale, out_dtype):
     """dQ = out_dtype(scale * dQaccum), the product taken in float32.
 
     Follows ``FlashAttentionBackwardPostprocess`` on the page
     "flash_bwd_postprocess.py": the fp32 accumulator is multiplied by the
-    scale and converted to the output type.  ``out_dtype`` is "bf16" (returns
-    uint16 bit patterns) or "f32" (returns float32).
+    scale and converted to the output type.  ``out_dtype`` is "bf16" or "f16"
+    (returns uint16 bit patterns) or "f32" (returns float32).
     """
     prod = np.asarray(dq_accum, np.float32) * np.float32(scale)
     if out_dtype == "bf16":
         return round_f32_to_bf16_bits(prod)
+    if out_dtype == "f16":
+        return round_f32_to_f16_bits(prod)
     if out_dtype == "f32":
         return prod.astype(np.float32)
     raise ValueError(out_dtype)

@@ -392,6 +392,34 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(A.bf16_bits_to_f32(got), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
 
 
+def test_f16_rounding_golden_bit_patterns():
+    data = json.load(open(GOLDEN))["f16_rounding"]["cases"]
+    src = np.array([int(a, 16) for a, _, _ in data], np.uint32).view(np.float32)
+    got = A.round_f32_to_f16_bits(src)
+    for (a, b, why), g in zip(data, got):
+        assert g == int(b, 16), (a, b, hex(int(g)), why)
+
+
+def test_f16_rounding_matches_numpy():
+    """numpy's float32 -> float16 conversion is IEEE round-to-nearest-even:
+    agreement over normal, subnormal, overflowing and exact-tie inputs."""
+    rng = np.random.default_rng(19)
+    x = (rng.standard_normal(1 << 18) * np.exp(rng.uniform(-25, 13, 1 << 18))).astype(np.float32)
+    # exact ties: odd multiples of half a unit, in normal binades and among subnormals
+    e = rng.integers(-14, 16, 4096)
+    k = rng.integers(0, 1024, 4096)
+    ties_n = np.ldexp(1024.0 + k + 0.5, e - 10).astype(np.float32)
+    ties_s = np.ldexp(rng.integers(0, 1024, 4096) + 0.5, -24).astype(np.float32)
+    x = np.concatenate([x, ties_n, ties_s, -ties_n, np.float32([np.inf, -np.inf, 0.0, -0.0])])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16)
+    got = A.round_f32_to_f16_bits(x)
+    assert np.array_equal(got, want.view(np.uint16))
+    assert np.array_equal(A.f16_bits_to_f32(got), want.astype(np.float32))
+    nan = np.float32([np.nan, -np.nan])
+    assert np.all(np.isnan(A.f16_bits_to_f32(A.round_f32_to_f16_bits(nan))))
+
+
 def test_postprocess_dq_product_in_float32():
     import torch
     rng = np.random.default_rng(18)
@@ -400,6 +428,8 @@ def test_postprocess_dq_product_in_float32():
     got = oracle.postprocess_dq(acc, s, "bf16")
     want = (torch.from_numpy(acc) * torch.tensor(s, dtype=torch.float32)).to(torch.bfloat16)
     assert np.array_equal(got, want.view(torch.int16).numpy().view(np.uint16))
+    got16 = oracle.postprocess_dq(acc, s, "f16")
+    assert np.array_equal(got16, (acc * np.float32(s)).astype(np.float16).view(np.uint16))
     got32 = oracle.postprocess_dq(acc, s, "f32")
     assert np.array_equal(got32, acc * np.float32(s))
 
