@@ -26,11 +26,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention-backward TFLOP/s (bf16, causal, S=4096, D=128) and % of MFMA peak"
 # MI355X published dense peaks
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+TORCH_DT = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
 PEAK_HBM_GBS = 8000.0
 MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f)
              for f in ("bwd_main.hip", "bwd_dq.hip", "bwd_dq_gemm.hip")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_c3_causal_{}.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_{}_causal_{}.json")
 KERNEL_DESC = {
     "stored_ds": "attn_bwd (key-stationary dK/dV kernel storing dS + dQ = dS K pass)",
     "separate": "attn_bwd (key-stationary dK/dV kernel + query-stationary dQ kernel)",
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--dq-algo", default=None, choices=["stored_ds", "separate", "atomic"],
-                    help="dQ from dS stored by the dK/dV kernel (default for bf16), by a query-stationary "
+                    help="dQ from dS stored by the dK/dV kernel (default for bf16/fp16), by a query-stationary "
                          "pass that recomputes S and dP (default for fp32), or by fp32 atomics")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -61,10 +62,10 @@ def source_hash(path):
 
 def traffic_entry(dq_algo, workload):
     """HBM bytes per attn_bwd call from the committed counter summary of this
-    dQ algorithm on the headline workload, or None when there is none or a
-    kernel source changed since the counters were taken."""
-    path = TRAFFIC_FILE.format(dq_algo)
-    if workload != "c3" or not os.path.exists(path):
+    dQ algorithm on this workload, or None when there is none or a kernel
+    source changed since the counters were taken."""
+    path = TRAFFIC_FILE.format(workload, dq_algo)
+    if not os.path.exists(path):
         return None
     t = json.load(open(path))
     if t.get("kernel_source_sha256_16") != "+".join(source_hash(p) for p in MAIN_SRCS):
@@ -140,8 +141,8 @@ def main():
         return
     p = datagen.workload(args.workload, deterministic=args.deterministic)
     if args.dq_algo is None:
-        args.dq_algo = "stored_ds" if p.dtype == "bf16" else "separate"
-    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+        args.dq_algo = "separate" if p.dtype == "f32" else "stored_ds"
+    dt = getattr(torch, TORCH_DT[p.dtype])
     x = datagen.draw(p)
     dev = {k: torch.from_numpy(v).to(dt).cuda() for k, v in x.items()}
     kw = {}
@@ -188,7 +189,7 @@ def main():
     peak = PEAK_TFLOPS[p.dtype]
 
     rows_q = p.total_q
-    elem = 2 if p.dtype == "bf16" else 4
+    elem = 4 if p.dtype == "f32" else 2
     # preprocess: read O and dO, write D; the dQ accumulator is cleared only
     # in the atomic dQ mode (the other modes overwrite it)
     accum = rows_q * p.heads_q * p.head_dim * 4
@@ -197,7 +198,8 @@ def main():
     post_bytes = rows_q * p.heads_q * p.head_dim * (4 + elem)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "c3" else
+        f"attention-backward TFLOP/s ({p.dtype}, {p.name}) and % of MFMA peak",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,

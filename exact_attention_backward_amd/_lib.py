@@ -20,6 +20,7 @@ ATTN_ERR_HIP = 5
 
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
+ATTN_DTYPE_F16 = 2
 
 ATTN_DQ_SEPARATE = 0
 ATTN_DQ_ATOMIC = 1

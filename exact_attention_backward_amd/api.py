@@ -26,7 +26,7 @@ __all__ = [
     "BackwardPlan",
 ]
 
-_DTYPES = {torch.bfloat16: L.ATTN_DTYPE_BF16, torch.float32: L.ATTN_DTYPE_F32}
+_DTYPES = {torch.bfloat16: L.ATTN_DTYPE_BF16, torch.float16: L.ATTN_DTYPE_F16, torch.float32: L.ATTN_DTYPE_F32}
 
 
 def _ptr(t):
@@ -48,8 +48,8 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
-    "stored_ds" (dS stored in bf16 by the dK/dV kernel, then dQ = dS K; bf16
-    only, workspace grows with Sq x Sk) or "atomic"."""
+    "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
+    dQ = dS K; bf16 and fp16 only, workspace grows with Sq x Sk) or "atomic"."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1

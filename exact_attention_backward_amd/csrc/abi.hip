@@ -19,7 +19,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int validate_shape(const attn_shape_t* s) {
     if (s == nullptr) return ATTN_ERR_NULL_ARG;
-    if (s->dtype != ATTN_DTYPE_F32 && s->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (s->dtype != ATTN_DTYPE_F32 && s->dtype != ATTN_DTYPE_BF16 && s->dtype != ATTN_DTYPE_F16)
+        return ATTN_ERR_UNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
     if (s->batch <= 0 || s->num_heads_q <= 0 || s->num_heads_kv <= 0 || s->seqlen_q <= 0 || s->seqlen_k <= 0)
         return ATTN_ERR_BAD_SHAPE;
@@ -35,7 +36,7 @@ int validate_shape(const attn_shape_t* s) {
     if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
     if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC && s->dq_algo != ATTN_DQ_STORED_DS)
         return ATTN_ERR_UNSUPPORTED;
-    if (s->dq_algo == ATTN_DQ_STORED_DS && s->dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (s->dq_algo == ATTN_DQ_STORED_DS && s->dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
     // element counts must stay addressable with 64-bit offsets and 32-bit row counts
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
@@ -49,7 +50,7 @@ int validate_shape(const attn_shape_t* s) {
 bool varlen(const attn_shape_t* s) { return s->cu_seqlens_q != nullptr; }
 long long rows_q(const attn_shape_t* s) { return varlen(s) ? s->total_q : (long long)s->batch * s->seqlen_q; }
 
-size_t elem_bytes(const attn_shape_t* s) { return s->dtype == ATTN_DTYPE_BF16 ? 2 : 4; }
+size_t elem_bytes(const attn_shape_t* s) { return s->dtype == ATTN_DTYPE_F32 ? 4 : 2; }
 
 // workspace = [dQ accumulator fp32][ordering counters int32][status words]
 size_t accum_bytes(const attn_shape_t* s) {
@@ -182,7 +183,7 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
-        a.ds = reinterpret_cast<bf16_t*>(tab + ds_table_bytes(s));
+        a.ds = tab + ds_table_bytes(s);
         a.ds_qb = ds_qb(s);
         a.ds_nn = ds_nn(s);
     }
@@ -194,7 +195,7 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
         d.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
         launch_bwd_dq(d, s->dtype, s->head_dim, s->causal != 0, hs);
     } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
-        launch_bwd_dq_gemm(a, s->head_dim, s->causal != 0, hs);
+        launch_bwd_dq_gemm(a, s->dtype, s->head_dim, s->causal != 0, hs);
     }
     return check_launch();
 }

@@ -43,7 +43,7 @@ struct DqCfg {
     static constexpr int BUF_K = 0, BUF_V = TILE;
     static constexpr int BUF_BYTES = 2 * TILE;
     static constexpr int LDS_BYTES = NS * BUF_BYTES;
-    static_assert(LDS_BYTES <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for bf16)");
+    static_assert(LDS_BYTES <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for 16-bit types)");
     static constexpr int NC = HD / 16;       // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;      // 32-column blocks of the head dim
     static constexpr int NJB = BN / 32;      // 32-key blocks of a K tile
@@ -57,7 +57,7 @@ using DqOp = typename Elem<T>::op_t;
 template <class T, int ROWB>
 __device__ __forceinline__ DqOp<T, 0> dq_read_row(const char* lds, int row, int col) {
     if constexpr (sizeof(T) == 2) {
-        return __builtin_bit_cast(bf16x8, lds_read16(lds, swz<ROWB>(row, col * 2)));
+        return __builtin_bit_cast(typename Elem<T>::op_t, lds_read16(lds, swz<ROWB>(row, col * 2)));
     } else {
         const f32x4 a = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4)));
         const f32x4 b = __builtin_bit_cast(f32x4, lds_read16(lds, swz<ROWB>(row, col * 4 + 16)));
@@ -74,7 +74,7 @@ __device__ __forceinline__ DqOp<T, 0> dq_read_col(const char* lds, int r1, int r
         const u32x2 x = lds_read_tr(lds, swz<ROWB>(r1 + (s >> 2), col * 2));
         const u32x2 y = lds_read_tr(lds, swz<ROWB>(r2 + (s >> 2), col * 2));
         const u32x4 w = {x[0], x[1], y[0], y[1]};
-        return __builtin_bit_cast(bf16x8, w);
+        return __builtin_bit_cast(typename Elem<T>::op_t, w);
     } else {
         const int col = c0 + (lane & 31);
         f32x8 r;
@@ -92,7 +92,7 @@ __device__ __forceinline__ DqOp<T, 0> dq_load_global(const T* p, bool ok) {
     if constexpr (sizeof(T) == 2) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (ok) w = *reinterpret_cast<const u32x4*>(p);
-        return __builtin_bit_cast(bf16x8, w);
+        return __builtin_bit_cast(typename Elem<T>::op_t, w);
     } else {
         f32x8 r = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (ok) {
@@ -363,6 +363,9 @@ void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_dq_t<bf16_t, 64>(a, causal, st);
         else launch_dq_t<bf16_t, 128>(a, causal, st);
+    } else if (dtype == ATTN_DTYPE_F16) {
+        if (hd == 64) launch_dq_t<f16_t, 64>(a, causal, st);
+        else launch_dq_t<f16_t, 128>(a, causal, st);
     } else {
         if (hd == 64) launch_dq_t<float, 64>(a, causal, st);
         else launch_dq_t<float, 128>(a, causal, st);

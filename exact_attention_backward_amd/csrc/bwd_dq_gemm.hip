@@ -1,4 +1,4 @@
-// dQ from stored dS (bf16): dQ / s = dS K, the fifth product of the
+// dQ from stored dS (bf16 or fp16): dQ / s = dS K, the fifth product of the
 // Composable Kernel page "block_fmha_bwd_dq_dk_dv_pipeline_trload_kr_ktr_vr.hpp
 // Source File" (stage 7), as a pass of its own over the dS blocks the dK/dV
 // kernel stored, so that no partial dQ is ever added with atomics.
@@ -45,16 +45,16 @@ struct DqgCfg {
     static_assert(OPS * (PD - 1) < 64, "vmcnt range");
 };
 
-// Transposing read of a row-major bf16 tile (see lds_read_tr): lane gets
+// Transposing read of a row-major 16-bit tile (see lds_read_tr): lane gets
 // M[r1 + t][c0 + lane % 32] and M[r2 + t][c0 + lane % 32], t = 0..3.
-template <int ROWB>
-__device__ __forceinline__ bf16x8 g_read_col(const char* lds, int r1, int r2, int c0, int lane) {
+template <class T, int ROWB>
+__device__ __forceinline__ typename Elem<T>::op_t g_read_col(const char* lds, int r1, int r2, int c0, int lane) {
     const int s = lane & 15;
     const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
     const u32x2 x = lds_read_tr(lds, swz<ROWB>(r1 + (s >> 2), col * 2));
     const u32x2 y = lds_read_tr(lds, swz<ROWB>(r2 + (s >> 2), col * 2));
     const u32x4 w = {x[0], x[1], y[0], y[1]};
-    return __builtin_bit_cast(bf16x8, w);
+    return __builtin_bit_cast(typename Elem<T>::op_t, w);
 }
 
 // s_waitcnt vmcnt(N) alone (lgkmcnt and expcnt left at their maxima): all but
@@ -68,7 +68,7 @@ __device__ __forceinline__ void g_wait_vmem_but() {
 }  // namespace
 
 // dQ rows of query tile m (256 rows) of q-head hq in sequence b.
-template <int HD, bool CAUSAL>
+template <class T, int HD, bool CAUSAL>
 __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                           char* smem) {
     using C = DqgCfg<HD>;
@@ -177,17 +177,17 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
                 // keys 16 sl .. 16 sl + 15 of the stage: pair sl / 2 of its part (one pair
                 // when a stage holds 32 keys), keys 16 (sl % 2) ..
                 const int so = (2 * (sl >> 1) * 64 + 16 * (sl & 1)) * 16;
-                bf16x8 av[kGRB];
+                typename Elem<T>::op_t av[kGRB];
 #pragma unroll
                 for (int r = 0; r < kGRB; ++r) {
                     const u32x2 x = lds_read_tr(ds, r * C::DS_PART + aoff0 + so);
                     const u32x2 y = lds_read_tr(ds, r * C::DS_PART + aoff1 + so);
                     const u32x4 wv = {x[0], x[1], y[0], y[1]};
-                    av[r] = __builtin_bit_cast(bf16x8, wv);
+                    av[r] = __builtin_bit_cast(typename Elem<T>::op_t, wv);
                 }
 #pragma unroll
                 for (int d = 0; d < C::NDB; ++d) {
-                    const bf16x8 bk = g_read_col<C::ROWB>(stage, 16 * sl + 8 * h, 16 * sl + 8 * h + 4, 32 * d, lane);
+                    const typename Elem<T>::op_t bk = g_read_col<T, C::ROWB>(stage, 16 * sl + 8 * h, 16 * sl + 8 * h + 4, 32 * d, lane);
 #pragma unroll
                     for (int r = 0; r < kGRB; ++r) mma16(acc[r][d], av[r], bk);
                 }
@@ -213,7 +213,7 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     }
 }
 
-template <int HD, bool CAUSAL>
+template <class T, int HD, bool CAUSAL>
 __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     using C = DqgCfg<HD>;
     constexpr int BQ = C::BQ;
@@ -250,12 +250,12 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
         // stages are no longer read)
         const int m2 = nblk_q_seq - 1 - p;
         if (m2 > p) {
-            gemm_tile<HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);
+            gemm_tile<T, HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);
             __syncthreads();
         }
-        if (p < nblk_q_seq && p <= m2) gemm_tile<HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        if (p < nblk_q_seq && p <= m2) gemm_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
     } else {
-        gemm_tile<HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        gemm_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
     }
 }
 
@@ -293,18 +293,24 @@ void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, 
     ds_table_kernel<<<1, 256, 0, st>>>(cu_q, batch, seqlen_q, total_q, out);
 }
 
-void launch_bwd_dq_gemm(const BwdArgs& a, int hd, bool causal, hipStream_t st) {
+template <class T>
+static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool causal, hipStream_t st) {
     const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;
     static_assert(DqgCfg<128>::BQ == DqgCfg<64>::BQ, "one query tiling");
     const int n_pair = causal ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
     const unsigned grid = (unsigned)(n_pair * a.hq * a.batch);
     if (hd == 64) {
-        if (causal) bwd_dq_gemm_kernel<64, true><<<grid, kGThreads, 0, st>>>(a);
-        else bwd_dq_gemm_kernel<64, false><<<grid, kGThreads, 0, st>>>(a);
+        if (causal) bwd_dq_gemm_kernel<T, 64, true><<<grid, kGThreads, 0, st>>>(a);
+        else bwd_dq_gemm_kernel<T, 64, false><<<grid, kGThreads, 0, st>>>(a);
     } else {
-        if (causal) bwd_dq_gemm_kernel<128, true><<<grid, kGThreads, 0, st>>>(a);
-        else bwd_dq_gemm_kernel<128, false><<<grid, kGThreads, 0, st>>>(a);
+        if (causal) bwd_dq_gemm_kernel<T, 128, true><<<grid, kGThreads, 0, st>>>(a);
+        else bwd_dq_gemm_kernel<T, 128, false><<<grid, kGThreads, 0, st>>>(a);
     }
+}
+
+void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_F16) launch_dq_gemm_t<f16_t>(a, hd, causal, st);
+    else launch_dq_gemm_t<bf16_t>(a, hd, causal, st);
 }
 
 }  // namespace attn

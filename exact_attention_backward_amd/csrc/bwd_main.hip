@@ -68,7 +68,7 @@ struct BwdCfg {
 template <class T, int ROWB>
 __device__ __forceinline__ typename Elem<T>::op_t read_op_row(const char* lds, int row, int col) {
     if constexpr (sizeof(T) == 2) {
-        return __builtin_bit_cast(bf16x8, lds_read16(lds, swz<ROWB>(row, col * 2)));
+        return __builtin_bit_cast(typename Elem<T>::op_t, lds_read16(lds, swz<ROWB>(row, col * 2)));
     } else {
         // whole-vector casts: a bit cast of a subscripted vector element is
         // miscompiled (it reads element 0), so elements are never cast singly
@@ -88,7 +88,7 @@ __device__ __forceinline__ typename Elem<T>::op_t read_op_col(const char* lds, i
         const u32x2 x = lds_read_tr(lds, swz<ROWB>(r1 + (s >> 2), col * 2));
         const u32x2 y = lds_read_tr(lds, swz<ROWB>(r2 + (s >> 2), col * 2));
         const u32x4 w = {x[0], x[1], y[0], y[1]};
-        return __builtin_bit_cast(bf16x8, w);
+        return __builtin_bit_cast(typename Elem<T>::op_t, w);
     } else {
         const int col = c0 + (lane & 31);
         f32x8 r;
@@ -107,7 +107,7 @@ __device__ __forceinline__ typename Elem<T>::op_t load_op_global(const T* p, boo
     if constexpr (sizeof(T) == 2) {
         u32x4 w = {0u, 0u, 0u, 0u};
         if (ok) w = *reinterpret_cast<const u32x4*>(p);
-        return __builtin_bit_cast(bf16x8, w);
+        return __builtin_bit_cast(typename Elem<T>::op_t, w);
     } else {
         f32x8 r = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (ok) {
@@ -425,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int col = 32 * mb + 8 * q4 + 4 * h;
                     if constexpr (sizeof(T) == 2) {
-                        const u32x2 wv = {pack_bf16x2(dp[mb][4 * q4], dp[mb][4 * q4 + 1]),
-                                          pack_bf16x2(dp[mb][4 * q4 + 2], dp[mb][4 * q4 + 3])};
+                        const u32x2 wv = {pack2<T>(dp[mb][4 * q4], dp[mb][4 * q4 + 1]),
+                                          pack2<T>(dp[mb][4 * q4 + 2], dp[mb][4 * q4 + 3])};
                         lds_write(lds_ds, swz<C::DSROWB>(jr, col * 2), wv);
                     } else {
                         const f32x4 wv = {dp[mb][4 * q4], dp[mb][4 * q4 + 1], dp[mb][4 * q4 + 2],
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// dK/dV kernel with split wave roles (bf16, dQ left to the query-stationary
+// dK/dV kernel with split wave roles (16-bit types, dQ left to another
 // pass).  Same key tiling and dispatch as bwd_kernel, but eight waves per
 // workgroup, two per SIMD: the 32 keys of pair p (keys 32p..32p+31) are
 // shared by a "P wave" (waves 0-3) and a "dS wave" (waves 4-7).  Per query
@@ -593,11 +593,11 @@ struct KvCfg {
 };
 
 // All work of one key tile n of sequence b, kv-head hkv (the body of bwd_kv_kernel).
-template <int HD, bool CAUSAL, bool STORE_DS>
+template <class T, int HD, bool CAUSAL, bool STORE_DS>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
+    static_assert(sizeof(T) == 2, "16-bit operand types");
     using C = KvCfg<HD>;
-    using T = bf16_t;
-    using op_t = bf16x8;
+    using op_t = typename Elem<T>::op_t;
     constexpr int BM = C::BM, NMB = C::NMB, ROWB = C::ROWB;
 
     const int lane = threadIdx.x & 63;
@@ -876,7 +876,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
         if (STORE_DS && role == 1) {
-            // dS (bf16) of this pair's 32 keys straight from the MFMA operand
+            // dS (16-bit) of this pair's 32 keys straight from the MFMA operand
             // registers to the dS block: chunk (pair, c, lane) holds, for key
             // 32 pair + lane % 32, the rows 16c + 4 (lane / 32) + 0..3 and
             // 16c + 8 + 4 (lane / 32) + 0..3 (the dQ pass reads it back with
@@ -924,7 +924,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-template <int HD, bool CAUSAL, bool STORE_DS>
+template <class T, int HD, bool CAUSAL, bool STORE_DS>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[KvCfg<HD>::LDS_BYTES];
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
@@ -950,13 +950,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     if (CAUSAL) {
         const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
         const int n2 = nk - 1 - p;
-        if (p <= n2) kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
+        if (p <= n2) kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
         if (n2 > p) {
             __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, n2, si, smem);
+            kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, n2, si, smem);
         }
     } else {
-        kv_tile<HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
+        kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
     }
 }
 
@@ -975,13 +975,13 @@ static void launch_bwd_t(const BwdArgs& a, bool causal, int dq_algo, hipStream_t
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE) {
-            if (causal) bwd_kv_kernel<HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<HD, false, false><<<kv_grid, kKvThreads, 0, st>>>(a);
+            if (causal) bwd_kv_kernel<T, HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<T, HD, false, false><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
         if (dq_algo == ATTN_DQ_STORED_DS) {
-            if (causal) bwd_kv_kernel<HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<HD, false, true><<<kv_grid, kKvThreads, 0, st>>>(a);
+            if (causal) bwd_kv_kernel<T, HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
+            else bwd_kv_kernel<T, HD, false, true><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
     }
@@ -999,6 +999,9 @@ void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, h
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, dq_algo, st);
         else launch_bwd_t<bf16_t, 128>(a, causal, dq_algo, st);
+    } else if (dtype == ATTN_DTYPE_F16) {
+        if (hd == 64) launch_bwd_t<f16_t, 64>(a, causal, dq_algo, st);
+        else launch_bwd_t<f16_t, 128>(a, causal, dq_algo, st);
     } else {
         if (hd == 64) launch_bwd_t<float, 64>(a, causal, dq_algo, st);
         else launch_bwd_t<float, 128>(a, causal, dq_algo, st);

@@ -1,5 +1,5 @@
 // Shared device-side helpers of the gfx950 attention kernels: vector types,
-// MFMA wrappers, bf16 packing, the XOR-swizzled LDS tile addressing and the
+// MFMA wrappers, bf16/fp16 packing, the XOR-swizzled LDS tile addressing and the
 // transposing LDS read.  Written for CDNA4 (wave64, 160 KiB LDS per CU).
 #pragma once
 
@@ -25,12 +25,17 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // this compiler lowers as a read of element 0: vectors are bit cast whole, or
 // the element is first copied into a scalar.
 typedef uint16_t bf16_t;
+// IEEE binary16, stored and converted natively (v_cvt_f16_f32 rounds to nearest even).
+typedef _Float16 f16_t;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
-// element type traits: bf16 (MFMA 32x32x16 bf16) and fp32 (MFMA 32x32x2 f32)
+// element type traits: bf16 and fp16 (MFMA 32x32x16 of that type) and fp32
+// (MFMA 32x32x2 f32)
 // ---------------------------------------------------------------------------
 template <class T> struct Elem;
 
@@ -39,6 +44,11 @@ template <> struct Elem<bf16_t> {
     typedef bf16x8 op_t;
     static constexpr int kBytes = 2;
     static constexpr attn_dtype_t kDtype = ATTN_DTYPE_BF16;
+};
+template <> struct Elem<f16_t> {
+    typedef f16x8 op_t;
+    static constexpr int kBytes = 2;
+    static constexpr attn_dtype_t kDtype = ATTN_DTYPE_F16;
 };
 template <> struct Elem<float> {
     typedef f32x8 op_t;
@@ -52,6 +62,9 @@ template <> struct Elem<float> {
 // (lane l, value v -> row 8 * (v / 4) + 4 * (l / 32) + v % 4, column l % 32).
 __device__ __forceinline__ void mma16(f32x16& c, const bf16x8& a, const bf16x8& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& c, const f16x8& a, const f16x8& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma16(f32x16& c, const f32x8& a, const f32x8& b) {
     // step t pairs k = t (lanes 0-31) with k = 8 + t (lanes 32-63)
@@ -73,11 +86,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Two fp32 values -> one word of two 16-bit values of type T (low = first).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) { return pack_bf16x2(lo, hi); }
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) { return pack_f16x2(lo, hi); }
+
 // Eight fp32 values -> MFMA operand of type T.
 __device__ __forceinline__ void to_op(bf16x8& o, const float* x) {
     u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                pack_bf16x2(x[6], x[7])};
     o = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ void to_op(f16x8& o, const float* x) {
+    u32x4 w = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
+               pack_f16x2(x[6], x[7])};
+    o = __builtin_bit_cast(f16x8, w);
 }
 __device__ __forceinline__ void to_op(f32x8& o, const float* x) {
 #pragma unroll

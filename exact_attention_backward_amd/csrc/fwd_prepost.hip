@@ -163,8 +163,13 @@ __global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
     const f32x4 u = *reinterpret_cast<const f32x4*>(src);
     const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4);
     float x[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+    {
+        // the product is rounded to fp32 before the conversion to T: no
+        // fused multiply-and-convert (v_fma_mix) for fp16
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) x[t] *= a.scale;
+        for (int t = 0; t < 8; ++t) x[t] *= a.scale;
+    }
     store8(reinterpret_cast<T*>(a.dq) + row * HD + part * 8, x);
 }
 
@@ -184,6 +189,9 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_fwd_t<bf16_t, 64>(a, causal, st);
         else launch_fwd_t<bf16_t, 128>(a, causal, st);
+    } else if (dtype == ATTN_DTYPE_F16) {
+        if (hd == 64) launch_fwd_t<f16_t, 64>(a, causal, st);
+        else launch_fwd_t<f16_t, 128>(a, causal, st);
     } else {
         if (hd == 64) launch_fwd_t<float, 64>(a, causal, st);
         else launch_fwd_t<float, 128>(a, causal, st);
@@ -204,6 +212,9 @@ void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) preprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
         else preprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+    } else if (dtype == ATTN_DTYPE_F16) {
+        if (hd == 64) preprocess_kernel<f16_t, 64><<<blocks, 256, 0, st>>>(a);
+        else preprocess_kernel<f16_t, 128><<<blocks, 256, 0, st>>>(a);
     } else {
         if (hd == 64) preprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
         else preprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);
@@ -216,6 +227,9 @@ void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) postprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
         else postprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+    } else if (dtype == ATTN_DTYPE_F16) {
+        if (hd == 64) postprocess_kernel<f16_t, 64><<<blocks, 256, 0, st>>>(a);
+        else postprocess_kernel<f16_t, 128><<<blocks, 256, 0, st>>>(a);
     } else {
         if (hd == 64) postprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
         else postprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);

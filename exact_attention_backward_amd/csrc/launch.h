@@ -57,15 +57,15 @@ struct BwdArgs {
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
     int deterministic;
-    // stored-dS mode: dS blocks [Hq][ds_qb][ds_nn][32 x 128 bf16] and, for
-    // varlen, each sequence's first 32-row query block
-    bf16_t* ds;
+    // stored-dS mode: dS blocks [Hq][ds_qb][ds_nn][32 x 128 of the 16-bit I/O
+    // type] and, for varlen, each sequence's first 32-row query block
+    void* ds;
     const int* ds_qb_base;
     long long ds_qb;     // 32-row query blocks per q-head
     int ds_nn;           // 128-key blocks per query block
 };
 
-// dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16 (8 KiB),
+// dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16 or fp16 (8 KiB),
 // in the register order of the key-stationary kernel's MFMA operands: 16-byte
 // chunk (g, l) for g = 2 p + c (keys 32p .. 32p + 31, rows 16c .. 16c + 15)
 // holds key 32 p + l % 32, rows 16c + 4 (l / 32) + 0..3 and
@@ -86,17 +86,29 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
 void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, hipStream_t st);
-// stored-dS mode: dQ = dS K from the stored blocks (bf16), and the per-sequence
-// block table of varlen problems
-void launch_bwd_dq_gemm(const BwdArgs& a, int hd, bool causal, hipStream_t st);
+// stored-dS mode: dQ = dS K from the stored blocks (16-bit types), and the
+// per-sequence block table of varlen problems
+void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
 void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, int* out, hipStream_t st);
 // query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
 int bwd_dq_block_m();
 
 // ---------------------------------------------------------------------------
-// element access for the two I/O types
+// element access for the three I/O types
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float load_elem(const f16_t* p, long long i) { return (float)p[i]; }
+__device__ __forceinline__ void store_elem(f16_t* p, long long i, float x) { p[i] = (f16_t)x; }
+__device__ __forceinline__ void load8(const f16_t* p, float* x) {
+    const f16x8 h = *reinterpret_cast<const f16x8*>(p);
+    const f32x8 f = __builtin_convertvector(h, f32x8);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = f[t];
+}
+__device__ __forceinline__ void store8(f16_t* p, const float* x) {
+    const f32x8 f = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    *reinterpret_cast<f16x8*>(p) = __builtin_convertvector(f, f16x8);
+}
 __device__ __forceinline__ float load_elem(const bf16_t* p, long long i) {
     return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
 }

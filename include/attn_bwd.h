@@ -64,15 +64,19 @@ typedef enum attn_status {
     ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
                                   cu_seqlens, workspace too small, more than 2^27
                                   (row, head) pairs in Q or K, ... */
-    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16, head_dim not 64 or 128, unknown
-                                  dq_algo, ATTN_DQ_STORED_DS with F32 */
+    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not 64 or 128,
+                                  unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status_t;
 
 typedef enum attn_dtype {
     ATTN_DTYPE_F32 = 0,        /* fp32 I/O, fp32 MFMA contractions */
-    ATTN_DTYPE_BF16 = 1        /* bf16 I/O, bf16 MFMA operands, fp32 accumulation */
+    ATTN_DTYPE_BF16 = 1,       /* bf16 I/O, bf16 MFMA operands, fp32 accumulation */
+    ATTN_DTYPE_F16 = 2         /* IEEE binary16 I/O, fp16 MFMA operands, fp32
+                                  accumulation (the kernels' fp16/bf16 element-type
+                                  choice on the composable-kernel backward page);
+                                  P and dS are rounded to fp16 like they are to bf16 */
 } attn_dtype_t;
 
 /* How attn_bwd produces dQ (both reach the same result up to fp32 summation
@@ -83,9 +87,9 @@ typedef enum attn_dtype {
  *  ATTN_DQ_ATOMIC: the key-stationary kernel adds dS K for each tile pair
  *    into the fp32 accumulator with global atomics (with deterministic = 1,
  *    in a fixed order per dQ tile).
- *  ATTN_DQ_STORED_DS (bf16 only): the key-stationary kernel stores dS, in
- *    bf16 (the operand type the pages' dQ = dS K product uses), in the
- *    workspace; a second pass forms dQ = dS K from it and writes every
+ *  ATTN_DQ_STORED_DS (bf16 and fp16): the key-stationary kernel stores dS
+ *    in the 16-bit I/O type (the operand type the pages' dQ = dS K product
+ *    uses) in the workspace; a second pass forms dQ = dS K from it and writes every
  *    accumulator row once: five contractions per tile pair, no atomics,
  *    bitwise reproducible, at the cost of a workspace that grows with
  *    Sq x Sk (2 bytes per query row and key, per q-head). */
@@ -121,7 +125,7 @@ const char* attn_status_string(int status);
  * need for this shape: the fp32 dQ accumulator ([B, Hq, Sq, D] dense,
  * [Hq, total_q, D] varlen) followed by the int32 ordering counters of the
  * deterministic mode and, for ATTN_DQ_STORED_DS, a table of per-sequence
- * offsets and the dS blocks (32 query rows x 128 keys of bf16 each, for every
+ * offsets and the dS blocks (32 query rows x 128 keys of 16-bit dS each, for every
  * q-head, 32-row query block and 128-key block; varlen sizes the query
  * blocks by total_q / 32 + batch and the key blocks by seqlen_k), each part
  * 256-byte aligned.  Returns 0 if the shape is invalid. */
@@ -167,8 +171,8 @@ int attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void
              const void* dout, const float* lse, const float* delta,
              void* workspace, size_t workspace_bytes, void* dk, void* dv, void* stream);
 
-/* dQ postprocess: dq = dtype(scale * dQaccum), the product in fp32, bf16
- * rounded to nearest even (FlashAttentionBackwardPostprocess).  Pass
+/* dQ postprocess: dq = dtype(scale * dQaccum), the product in fp32, bf16 and
+ * fp16 rounded to nearest even (FlashAttentionBackwardPostprocess).  Pass
  * scale = shape->softmax_scale.  workspace: input; dq: output. */
 int attn_bwd_dq_postprocess(const attn_shape_t* shape, const void* workspace,
                             size_t workspace_bytes, void* dq, float scale, void* stream);

@@ -10,8 +10,13 @@ import datagen
 import oracle
 from exact_attention_backward_amd import api
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+# max|gpu - oracle| / max|oracle|.  The 16-bit paths round P and dS to the
+# operand type before their products and the outputs once more, each a
+# relative error of at most u (2^-8 for bf16, 2^-11 for fp16), so the bound
+# is five units of the type: 2e-2 for bf16, 2.5e-3 for fp16.  fp32 keeps
+# only summation-order differences.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2.5e-3}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def rel_err(got, ref):
@@ -33,7 +38,11 @@ def to_host(t):
 def round_like(x, dtype):
     """Values the GPU will hold for a float64 array stored in `dtype`."""
     x32 = np.asarray(x, np.float64).astype(np.float32)
-    return datagen.round_to_bf16(x32).astype(np.float64) if dtype == "bf16" else x32.astype(np.float64)
+    if dtype == "bf16":
+        return datagen.round_to_bf16(x32).astype(np.float64)
+    if dtype == "f16":
+        return datagen.round_to_f16(x32).astype(np.float64)
+    return x32.astype(np.float64)
 
 
 def small_problem(dtype, b, hq, hkv, sq, sk, d, causal, seed, lengths=None, deterministic=False, scale=None,

@@ -61,6 +61,9 @@ def test_workspace_size_formula():
     table = 256
     blocks = 4 * (2 * 4) * 1 * 32 * 128 * 2
     assert ws_bytes(s) == acc + sem + 256 + table + blocks
+    # fp16 I/O: the same sizes (the accumulator is fp32, dS blocks 16-bit)
+    assert ws_bytes(shape(dtype=L.ATTN_DTYPE_F16)) == acc + sem + 256
+    assert ws_bytes(shape(dq_algo=L.ATTN_DQ_STORED_DS, dtype=L.ATTN_DTYPE_F16)) == acc + sem + 256 + table + blocks
 
 
 @pytest.mark.parametrize("kw,status", [

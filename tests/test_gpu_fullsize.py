@@ -4,7 +4,7 @@ benchmark times (BackwardPlan.run: preprocess -> main -> postprocess).
 The small workloads (fp32 B1 H2 S128 D64 and bf16 causal B2 H8 S1024 D64) are
 compared element by element in full.  For the large ones the oracle computes
 sampled (sequence, kv-head) groups one by one: their O and LSE come from the
-oracle forward (written into the device buffers, rounded to bf16 / fp32),
+oracle forward (written into the device buffers, rounded to the I/O type),
 every other head uses the library forward, and the sampled heads' dQ, dK and
 dV are compared with the oracle backward.  Every head is also checked against
 the identity sum_j dV_j = sum_i dO_i (rows of P sum to one), which holds at any
@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 def setup(p):
     x = datagen.draw(p)
-    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[p.dtype]
     dev = {k: torch.from_numpy(v).to(dt).cuda() for k, v in x.items()}
     kw, cu = {}, (None, None)
     if p.varlen:
@@ -143,6 +143,12 @@ def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
 def test_headline_causal_sampled(dq_algo):
     sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)], dq_algo=dq_algo)
+
+
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
+def test_headline_shape_fp16_sampled(dq_algo):
+    """The causal B=4 H=16 S=4096 D=128 shape with fp16 I/O."""
+    sampled_check(datagen.workload("c3h"), [(0, 0), (2, 9)], dq_algo=dq_algo)
 
 
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
