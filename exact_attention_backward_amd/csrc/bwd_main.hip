@@ -715,6 +715,18 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                                                 : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows))
                                       : 0;
     const bool ragged_k = n * kBN + kBN > si.len_k;
+    // dS block cursors: the block (q-head, first 32-row block of the tile,
+    // key tile n) of tile t and of tile t-1; blocks from ds_lim on lie past
+    // the sequence (or, for malformed overlapping cu_seqlens, past the buffer)
+    // and get an empty range
+    const int ds_lim = STORE_DS ? (int)min((long long)(si.len_q + kDsRows - 1) / kDsRows, a.ds_qb - ds_qb0) : 0;
+    const long long ds_blk_n = STORE_DS ? (long long)a.ds_nn * kDsBlockBytes : 0;   // bytes per 32-row block
+    const char* ds_p0 = STORE_DS ? reinterpret_cast<const char*>(a.ds) +
+                                       (((long long)hkv * G * a.ds_qb + ds_qb0 + m_begin * (BM / kDsRows)) * a.ds_nn + n) *
+                                           kDsBlockBytes
+                                 : nullptr;
+    const char* ds_cur = ds_p0;   // tile t
+    const char* ds_last = ds_p0;  // tile t-1
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
@@ -768,9 +780,14 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         issue_next();
         cur_buf = cur_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : cur_buf + C::BUF_BYTES;
         const int tile_m = cur_m, tile_g = cur_g;   // coordinates of tile t
+        const char* ds_prev = ds_last;              // dS blocks of tile t-1
+        if (STORE_DS) ds_last = ds_cur;
         if (++cur_m == m_end) {
             cur_m = m_begin;
             ++cur_g;
+            if (STORE_DS) ds_cur = ds_p0 + (long long)cur_g * a.ds_qb * ds_blk_n;
+        } else if (STORE_DS) {
+            ds_cur += (BM / kDsRows) * ds_blk_n;
         }
         const int prev_m = last_m, prev_g = last_g;   // coordinates of tile t-1
         last_m = tile_m;
@@ -843,15 +860,6 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                     for (int e = 0; e < 4; ++e) xp[mb][4 * q4 + e] = pv[e] * (xp[mb][4 * q4 + e] - dl[e]);
                 }
             }
-            if (STORE_DS && ragged_k && j >= si.len_k) {
-                // a key past the sequence meets zero K rows in dQ = dS K; its
-                // dS is zeroed so that a non-finite value cannot reach them
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) xp[mb][v] = 0.f;
-                }
-            }
 #pragma unroll
             for (int c = 0; c < C::NIC; ++c) {
                 float td[8];
@@ -859,39 +867,58 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                 for (int u = 0; u < 8; ++u) td[u] = xp[c >> 1][8 * (c & 1) + u];
                 to_op(opa[c], td);
             }
+            if (STORE_DS && ragged_k) {
+                // a key past the sequence meets zero K rows in dQ = dS K; its
+                // stored dS is zero so that a non-finite value cannot reach them
+                // (its dK row is not stored either)
+                const bool kill = j >= si.len_k;
+#pragma unroll
+                for (int c = 0; c < C::NIC; ++c) {
+                    u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wv[q] = kill ? 0u : wv[q];
+                    opa[c] = __builtin_bit_cast(op_t, wv);
+                }
+            }
         }
         // ---- dV += P^T dO (P wave) or dK += dS^T Q (dS wave)
         const int cb = (int)buf + col_off;
         const int t0 = cb + tbase0, t1 = cb + tbase1;
+        // every transposing read is issued before the first MFMA.  With the
+        // dS stores in the block, the compiler sinks the reads to their uses
+        // (exposing the LDS latency once per MFMA) unless a scheduling
+        // barrier separates them; without the stores the grouping hints below
+        // give a better interleaving.
+        u32x4 bop[C::NIC][C::NDB];
 #pragma unroll
         for (int c = 0; c < C::NIC; ++c) {
 #pragma unroll
             for (int d = 0; d < C::NDB; ++d) {
                 const u32x2 x = lds_read_tr(smem, (t0 ^ (64 * d)) + c * 16 * ROWB);
                 const u32x2 y = lds_read_tr(smem, (t1 ^ (64 * d)) + c * 16 * ROWB);
-                const u32x4 wv = {x[0], x[1], y[0], y[1]};
-                mma16(acc[d], opa[c], __builtin_bit_cast(op_t, wv));
+                bop[c][d] = u32x4{x[0], x[1], y[0], y[1]};
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
+        if constexpr (STORE_DS) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < C::NIC; ++c) {
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) mma16(acc[d], opa[c], __builtin_bit_cast(op_t, bop[c][d]));
+        }
+        if constexpr (!STORE_DS) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
+        }
         if (STORE_DS && role == 1) {
             // dS (16-bit) of this pair's 32 keys straight from the MFMA operand
             // registers to the dS block: chunk (pair, c, lane) holds, for key
             // 32 pair + lane % 32, the rows 16c + 4 (lane / 32) + 0..3 and
             // 16c + 8 + 4 (lane / 32) + 0..3 (the dQ pass reads it back with
             // transposing reads).  Issued after the dK MFMAs, which run meanwhile.
-            const int hq = hkv * G + prev_g;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
                 const int lq = prev_m * (BM / kDsRows) + mb;   // 32-row block within the sequence
-                // blocks past the sequence get an empty range (the second test
-                // only fails for overlapping, malformed cu_seqlens)
-                const bool ok = lq * kDsRows < si.len_q && ds_qb0 + lq < a.ds_qb;
-                const rsrc_t dst = make_rsrc(
-                    reinterpret_cast<char*>(a.ds) + (((long long)hq * a.ds_qb + ds_qb0 + lq) * a.ds_nn + n) *
-                                                        kDsBlockBytes,
-                    ok ? kDsBlockBytes : 0);
+                const rsrc_t dst = make_rsrc(ds_prev + mb * ds_blk_n, lq < ds_lim ? kDsBlockBytes : 0);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     // non-temporal: read once, by the dQ pass
