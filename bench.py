@@ -11,7 +11,11 @@ step, halved when causal), the main kernel's roofline figures measured with HIP
 events on the stream the kernels run on, and the fp64 CPU oracle timed on a
 bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu]
+Before the W warm-up steps the bench runs untimed steps for --settle seconds
+(0.5 s by default): after idle the GPU needs about twenty calls to reach its
+steady clock, and the first calls run up to 30% slower.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--settle S]
 """
 
 import argparse
@@ -53,6 +57,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
     ap.add_argument("--cpu-pairs", type=int, default=64, help="(sequence, head) pairs in the CPU oracle sample")
+    ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
+                    help="untimed steps before the warm-up, until this much time has passed: after idle the GPU "
+                         "takes about 20 calls (~25 ms) to reach its steady clock")
     return ap.parse_args()
 
 
@@ -156,6 +163,13 @@ def main():
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
 
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            plan.run(q, k, v, o, do, lse, dq, dk, dv)
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         plan.run(q, k, v, o, do, lse, dq, dk, dv)
     torch.cuda.synchronize()
@@ -205,6 +219,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
