@@ -144,13 +144,33 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False):
 # batched / grouped / varlen layouts
 # --------------------------------------------------------------------------
 
-def _ranges(nseq, sq, sk, cu_q, cu_k):
-    """Row ranges (q0, q1, k0, k1) of every sequence."""
+def _ranges(nseq, sq, sk, cu_q, cu_k, used_q=None, used_k=None):
+    """Row ranges (q0, q1, k0, k1) of every sequence.
+
+    Varlen only: ``used_q``/``used_k`` (one length per sequence) replace the
+    length cu[b+1] - cu[b] while the sequence still starts at cu[b], as the
+    sequence-length helper of the FlashAttention-3 backward epilogue page does
+    with ``seqused``; rows past the used length take no part in anything.
+    """
     if cu_q is None:
+        if used_q is not None or used_k is not None:
+            raise ValueError("seqused needs cu_seqlens")
         return [(b * sq, (b + 1) * sq, b * sk, (b + 1) * sk) for b in range(nseq)]
     cu_q = np.asarray(cu_q, np.int64)
     cu_k = np.asarray(cu_k, np.int64)
-    return [(int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])) for b in range(nseq)]
+    out = []
+    for b in range(nseq):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if used_q is not None:
+            if not 0 <= int(used_q[b]) <= q1 - q0:
+                raise ValueError("seqused_q out of range")
+            q1 = q0 + int(used_q[b])
+        if used_k is not None:
+            if not 0 <= int(used_k[b]) <= k1 - k0:
+                raise ValueError("seqused_k out of range")
+            k1 = k0 + int(used_k[b])
+        out.append((q0, q1, k0, k1))
+    return out
 
 
 def _flat(x, varlen):
@@ -182,14 +202,15 @@ def _lse_view(lse, varlen, nseq, hq, sq):
     return np.transpose(lse, (1, 0, 2)).reshape(hq, nseq * sq)
 
 
-def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None):
+def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None,
+                  seqused_q=None, seqused_k=None):
     """Forward for the q-heads of one kv-head group of one sequence.
 
     Returns {q_head: (o [len_q, d], lse [len_q])}.
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
-    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)[seq]
+    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)[seq]
     qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
     out = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
@@ -198,7 +219,7 @@ def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_se
 
 
 def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
-                   cu_seqlens_q=None, cu_seqlens_k=None):
+                   cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None):
     """Backward for one kv-head group of one sequence.
 
     Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
@@ -206,7 +227,7 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
-    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)[seq]
+    q0, q1, k0, k1 = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)[seq]
     qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
     of, dof = _flat(o, varlen), _flat(do, varlen)
     lf = _lse_view(lse, varlen, nseq, hq, sq)
@@ -223,16 +244,17 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
     return dq, dk, dv
 
 
-def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None):
-    """Full forward.  Returns (o, lse) in the layouts given in the module doc."""
+def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None):
+    """Full forward.  Returns (o, lse) in the layouts given in the module doc
+    (rows past a sequence's used length are left at zero)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     qf = _flat(q, varlen)
     o = np.zeros(qf.shape, np.float64)
     lse = np.zeros((hq, qf.shape[0]), np.float64)
-    for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)):
+    for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g,
-                                             cu_seqlens_q, cu_seqlens_k).items():
+                                             cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k).items():
                 o[q0:q1, h] = oh
                 lse[h, q0:q1] = lh
     if varlen:
@@ -240,17 +262,19 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None):
     return o.reshape(q.shape), np.transpose(lse.reshape(hq, nseq, sq), (1, 0, 2)).copy()
 
 
-def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None):
-    """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64)."""
+def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
+             seqused_q=None, seqused_k=None):
+    """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64);
+    rows past a sequence's used length are left at zero."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     qf, kf = _flat(q, varlen), _flat(k, varlen)
     dq = np.zeros(qf.shape, np.float64)
     dk = np.zeros(kf.shape, np.float64)
     dv = np.zeros(kf.shape, np.float64)
-    for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k)):
+    for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g,
-                                           cu_seqlens_q, cu_seqlens_k)
+                                           cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)
             for h, x in dqg.items():
                 dq[q0:q1, h] = x
             dk[k0:k1, g] = dkg

@@ -352,6 +352,44 @@ def test_varlen_equals_per_sequence_dense(causal):
             assert np.max(np.abs(a[sl] - bb[0])) <= 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_seqused_equals_truncated_sequences(causal):
+    """seqused keeps each sequence's start (cu_seqlens) and shortens it: the
+    result on the used rows is the per-sequence dense result of the first
+    used rows (causal alignment from the used lengths), and every unused row
+    is left at zero."""
+    rng = np.random.default_rng(25)
+    lens_q, lens_k = [9, 30, 4, 21], [12, 25, 7, 21]
+    used_q, used_k = np.array([9, 17, 0, 5], np.int32), np.array([3, 25, 7, 21], np.int32)
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    h, hkv, d = 4, 2, 8
+    q, do = rand(rng, cq[-1], h, d), rand(rng, cq[-1], h, d)
+    k, v = rand(rng, ck[-1], hkv, d), rand(rng, ck[-1], hkv, d)
+    o, lse = oracle.forward(q, k, v, 0.4, causal, cq, ck, used_q, used_k)
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, 0.4, causal, cq, ck, used_q, used_k)
+    for bi in range(4):
+        sq = slice(cq[bi], cq[bi] + used_q[bi])
+        sk = slice(ck[bi], ck[bi] + used_k[bi])
+        if used_q[bi] and used_k[bi]:
+            od, lsed = oracle.forward(q[None, sq], k[None, sk], v[None, sk], 0.4, causal)
+            assert np.max(np.abs(o[sq] - od[0])) <= 1e-12
+            fin = np.isfinite(lsed[0])
+            assert np.array_equal(np.isfinite(lse[:, sq]), fin)
+            assert np.max(np.abs(lse[:, sq][fin] - lsed[0][fin]), initial=0) <= 1e-12
+            dqd, dkd, dvd = oracle.backward(q[None, sq], k[None, sk], v[None, sk], od, do[None, sq], lsed, 0.4, causal)
+            assert np.max(np.abs(dq[sq] - dqd[0])) <= 1e-12
+            assert np.max(np.abs(dk[sk] - dkd[0])) <= 1e-12
+            assert np.max(np.abs(dv[sk] - dvd[0])) <= 1e-12
+        for arr, cu, used in ((dq, cq, used_q), (o, cq, used_q), (dk, ck, used_k), (dv, ck, used_k)):
+            assert not np.any(arr[cu[bi] + used[bi]:cu[bi + 1]])
+    # seqused equal to the full lengths changes nothing
+    full = oracle.backward(q, k, v, o, do, lse, 0.4, causal, cq, ck, np.diff(cq), np.diff(ck))
+    plain = oracle.backward(q, k, v, o, do, lse, 0.4, causal, cq, ck)
+    for a, bb in zip(full, plain):
+        assert np.array_equal(a, bb)
+
+
 def test_preprocess_delta_layouts_and_definition():
     rng = np.random.default_rng(16)
     o, do = rand(rng, 2, 5, 3, 4), rand(rng, 2, 5, 3, 4)
