@@ -54,6 +54,8 @@ class AttnShape(ctypes.Structure):
         ("deterministic", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("dq_algo", ctypes.c_int32),
+        ("seqused_q", ctypes.c_void_p),
+        ("seqused_k", ctypes.c_void_p),
     ]
 
 

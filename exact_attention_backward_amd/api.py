@@ -45,11 +45,13 @@ DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_
 
 
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-               max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
+               max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
     "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
-    dQ = dS K; bf16 and fp16 only, workspace grows with Sq x Sk) or "atomic"."""
+    dQ = dS K; bf16 and fp16 only, workspace grows with Sq x Sk) or "atomic".
+    seqused_q / seqused_k (varlen only): int32 device tensors of per-sequence
+    used lengths."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -66,6 +68,10 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
         s.seqlen_q, s.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
         s.cu_seqlens_q = cu_seqlens_q.data_ptr()
         s.cu_seqlens_k = cu_seqlens_k.data_ptr()
+    if seqused_q is not None:
+        s.seqused_q = seqused_q.data_ptr()
+    if seqused_k is not None:
+        s.seqused_k = seqused_k.data_ptr()
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
@@ -104,11 +110,17 @@ def _lse_shape(shape, varlen):
     return (shape.batch, shape.num_heads_q, shape.seqlen_q)
 
 
-def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
-    """Plain forward: returns (o, lse)."""
-    shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
-    o = torch.empty_like(q)
-    lse = torch.empty(_lse_shape(shape, cu_seqlens_q is not None), dtype=torch.float32, device=q.device)
+def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+            seqused_q=None, seqused_k=None, out=None):
+    """Plain forward: returns (o, lse).  ``out`` = (o, lse) writes into given
+    buffers (rows past the used lengths keep their contents)."""
+    shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                       seqused_q=seqused_q, seqused_k=seqused_k)
+    if out is not None:
+        o, lse = out
+    else:
+        o = torch.empty_like(q)
+        lse = torch.empty(_lse_shape(shape, cu_seqlens_q is not None), dtype=torch.float32, device=q.device)
     attn_fwd(shape, q, k, v, o, lse)
     return o, lse
 
@@ -121,10 +133,10 @@ class BackwardPlan:
     """
 
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-                 max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
+                 max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None):
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
-                                max_seqlen_q, max_seqlen_k, dq_algo)
-        self._keep = (cu_seqlens_q, cu_seqlens_k)
+                                max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k)
+        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
         if nbytes == 0:
@@ -159,10 +171,10 @@ class BackwardPlan:
 
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
-             max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate"):
+             max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None):
     """Full backward: returns (dq, dk, dv)."""
     plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                        dq_algo)
+                        dq_algo, seqused_q, seqused_k)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     plan.run(q, k, v, o, do, lse, dq, dk, dv)
     return dq, dk, dv

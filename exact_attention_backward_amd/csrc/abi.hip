@@ -30,7 +30,11 @@ int validate_shape(const attn_shape_t* s) {
         if (s->total_q <= 0 || s->total_k <= 0) return ATTN_ERR_BAD_SHAPE;
         if ((reinterpret_cast<uintptr_t>(s->cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(s->cu_seqlens_k) & 3u))
             return ATTN_ERR_MISALIGNED;
+    } else if (s->seqused_q != nullptr || s->seqused_k != nullptr) {
+        return ATTN_ERR_BAD_SHAPE;   // used lengths are a varlen feature
     }
+    if ((reinterpret_cast<uintptr_t>(s->seqused_q) & 3u) || (reinterpret_cast<uintptr_t>(s->seqused_k) & 3u))
+        return ATTN_ERR_MISALIGNED;
     if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
     if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
     if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
@@ -112,7 +116,8 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_MISALIGNED;
-    FwdArgs a{q, k, v, o, lse, s->cu_seqlens_q, s->cu_seqlens_k, s->batch, s->num_heads_q, s->num_heads_kv,
+    FwdArgs a{q, k, v, o, lse, s->cu_seqlens_q, s->cu_seqlens_k, s->seqused_q, s->seqused_k, s->batch,
+              s->num_heads_q, s->num_heads_kv,
               s->seqlen_q, s->seqlen_k, s->total_q, s->total_k, s->softmax_scale};
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_fwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
@@ -169,6 +174,8 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.dv = dv;
     a.cu_q = s->cu_seqlens_q;
     a.cu_k = s->cu_seqlens_k;
+    a.used_q = s->seqused_q;
+    a.used_k = s->seqused_k;
     a.batch = s->batch;
     a.hq = s->num_heads_q;
     a.hkv = s->num_heads_kv;
@@ -208,7 +215,7 @@ int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t
     if (!aligned16(workspace) || !aligned16(dq)) return ATTN_ERR_MISALIGNED;
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
-               s->seqlen_q, s->total_q, varlen(s), scale};
+               s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch};
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     launch_postprocess(a, s->dtype, s->head_dim, reinterpret_cast<hipStream_t>(stream));
     return check_launch();

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const int b = grp / a.hkv;
     const int hq = hkv * G + slot / n_pair;
     const int p = slot % n_pair;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     const int nblk_q_seq = (si.len_q + BQ - 1) / BQ;   // this sequence's query tiles
     if (CAUSAL) {
         // the longer tile first, then its partner (once the first tile's LDS

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     const int hkv = grp % a.hkv;
     const int b = grp / a.hkv;
     const int n = (CAUSAL && a.deterministic) ? a.nblk_n - 1 - nb_lin : nb_lin;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (n * kBN >= si.len_k) return;
     const bool varlen = a.cu_q != nullptr;
     const int G = a.hq / a.hkv;
@@ -973,7 +973,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     }
     const int hkv = grp % a.hkv;
     const int b = grp / a.hkv;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (CAUSAL) {
         const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
         const int n2 = nk - 1 - p;

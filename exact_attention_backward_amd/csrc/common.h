@@ -222,8 +222,11 @@ struct SeqInfo {
     int k0, len_k;
 };
 
+// used_q / used_k (varlen only, may be null): per-sequence used lengths that
+// replace the offset difference; the sequence still starts at cu[b].
 __device__ __forceinline__ SeqInfo seq_info(int b, int seqlen_q, int seqlen_k, int total_q, int total_k,
-                                            const int32_t* cu_q, const int32_t* cu_k) {
+                                            const int32_t* cu_q, const int32_t* cu_k,
+                                            const int32_t* used_q = nullptr, const int32_t* used_k = nullptr) {
     SeqInfo s;
     if (cu_q == nullptr) {
         s.q0 = b * seqlen_q;
@@ -240,6 +243,8 @@ __device__ __forceinline__ SeqInfo seq_info(int b, int seqlen_q, int seqlen_k, i
         e = min(max(cu_k[b + 1], a), total_k);
         s.k0 = a;
         s.len_k = min(e - a, seqlen_k);
+        if (used_q != nullptr) s.len_q = min(s.len_q, max(used_q[b], 0));
+        if (used_k != nullptr) s.len_k = min(s.len_k, max(used_k[b], 0));
     }
     return s;
 }

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     __shared__ float ks[BK][HD];
     __shared__ float vs[BK][HD];
     const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k);
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (qb * BQ >= si.len_q) return;
     const int hkv = hq / (a.hq / a.hkv);
     const int i = qb * BQ + threadIdx.x;
@@ -159,6 +159,19 @@ __global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
     const int part = (int)(gt % LPR);
     const long long r = row / a.h;
     const int h = (int)(row - r * a.h);
+    if (a.used_q != nullptr) {
+        // the sequence holding token r (the last b with cu[b] <= r); tokens
+        // past its used length, or past every sequence, keep their dQ
+        int lo = 0, hi = a.batch;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.cu_q[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        if (lo >= a.batch) return;
+        const int len = min(a.cu_q[lo + 1] - a.cu_q[lo], max(a.used_q[lo], 0));
+        if (r >= (long long)a.cu_q[lo] + len) return;
+    }
     const float* src = a.acc + lse_index(a.varlen, r, h, a.h, a.s, a.total) * HD + part * 8;
     const f32x4 u = *reinterpret_cast<const f32x4*>(src);
     const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4);

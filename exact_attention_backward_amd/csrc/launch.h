@@ -14,6 +14,8 @@ struct FwdArgs {
     float* lse;
     const int32_t* cu_q;
     const int32_t* cu_k;
+    const int32_t* used_q;   // varlen: per-sequence used lengths, or null
+    const int32_t* used_k;
     int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
     float scale;
 };
@@ -36,6 +38,10 @@ struct PostArgs {
     long long total;
     bool varlen;
     float scale;
+    // varlen with used lengths: rows past a sequence's used length are skipped
+    const int32_t* cu_q;
+    const int32_t* used_q;
+    int batch;
 };
 
 struct BwdArgs {
@@ -52,6 +58,8 @@ struct BwdArgs {
     void* dv;
     const int32_t* cu_q;
     const int32_t* cu_k;
+    const int32_t* used_q;   // varlen: per-sequence used lengths, or null
+    const int32_t* used_k;
     int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)

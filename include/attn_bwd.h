@@ -36,6 +36,12 @@
  *    arrays of batch+1 nondecreasing offsets starting at 0 and ending at
  *    total_q/total_k); sequence b occupies rows [cu[b], cu[b+1]) and no
  *    sequence may be longer than seqlen_q/seqlen_k.
+ *  - Used lengths (varlen only; the `seqused` arrays of the FlashAttention-3
+ *    backward epilogue page): when seqused_q (seqused_k) is non-NULL,
+ *    sequence b has min(seqused[b], cu[b+1] - cu[b]) query (key) rows
+ *    starting at cu[b]; the rows after them take no part and their outputs
+ *    (O, LSE of attn_fwd; dQ, dK, dV) are left untouched.  Given without
+ *    cu_seqlens they are rejected (ATTN_ERR_BAD_SHAPE).
  *  - Causal masking is aligned to the bottom-right corner of each
  *    (sequence, head) block: key j is visible to query i iff
  *    j <= i + (len_k - len_q).  A query row that sees no key has LSE = -inf,
@@ -66,7 +72,8 @@ typedef enum attn_status {
                                   (row, head) pairs in Q or K, ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not 64 or 128,
                                   unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
-    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned (cu_seqlens and
+                                  seqused: 4-byte) */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status_t;
 
@@ -116,6 +123,8 @@ typedef struct attn_shape {
     int32_t deterministic;   /* 1: dQ summed in a fixed order, bitwise reproducible */
     int32_t dtype;           /* attn_dtype_t */
     int32_t dq_algo;         /* attn_dq_algo_t: how attn_bwd accumulates dQ */
+    const int32_t* seqused_q;     /* varlen only: device [batch] used query lengths, or NULL */
+    const int32_t* seqused_k;     /* varlen only: device [batch] used key lengths, or NULL */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -87,6 +87,20 @@ def test_invalid_shapes_rejected(kw, status):
     assert rc == status
 
 
+def test_seqused_needs_varlen_and_alignment():
+    assert ws_bytes(shape(seqused_q=0x1000)) == 0
+    assert ws_bytes(shape(seqused_k=0x1000)) == 0
+    s = shape(cu_seqlens_q=0x1000, cu_seqlens_k=0x2000, total_q=500, total_k=400, seqused_q=0x3000, seqused_k=0x4000)
+    assert ws_bytes(s) == ws_bytes(shape(cu_seqlens_q=0x1000, cu_seqlens_k=0x2000, total_q=500, total_k=400))
+    fake = ctypes.c_void_p(0x1000)
+    s = shape(cu_seqlens_q=0x1000, cu_seqlens_k=0x2000, total_q=500, total_k=400, seqused_q=0x3002)
+    rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+    assert rc == L.ATTN_ERR_MISALIGNED
+    s = shape(seqused_k=0x3000)
+    rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+    assert rc == L.ATTN_ERR_BAD_SHAPE
+
+
 def test_varlen_needs_both_offsets_and_totals():
     s = shape(cu_seqlens_q=0x1000)
     assert ws_bytes(s) == 0

@@ -155,3 +155,73 @@ def test_preprocess_clears_workspace_and_main_accumulates():
     plan.run(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq2, dk, dv)
     torch.cuda.synchronize()
     assert rel_err(to_host(dq2), to_host(dq1)) <= 1e-2
+
+
+SEQUSED_CASES = [
+    # (dtype, Hq, Hkv, D, causal, lengths_q, lengths_k, used_q, used_k)
+    ("bf16", 4, 2, 128, True, (70, 300, 129, 1), (90, 260, 129, 40), (70, 211, 0, 1), (33, 260, 100, 40)),
+    ("bf16", 2, 2, 64, False, (200, 65, 130), (150, 300, 130), (199, 1, 130), (150, 129, 64)),
+    ("f16", 4, 1, 128, True, (257, 40), (257, 300), (250, 40), (257, 170)),
+]
+
+
+def _sequsedid(c):
+    dt, hq, hkv, d, causal, lq, lk, uq, uk = c
+    return f"{dt}-h{hq}/{hkv}-d{d}-{'causal' if causal else 'full'}-uq{'-'.join(map(str, uq))}-uk{'-'.join(map(str, uk))}"
+
+
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
+@pytest.mark.parametrize("case", SEQUSED_CASES, ids=_sequsedid)
+def test_seqused_matches_oracle_and_leaves_unused_rows(case, dq_algo):
+    """Varlen with used lengths: the used rows of O, LSE, dQ, dK, dV match the
+    oracle; every row past a used length keeps what the buffer held."""
+    import datagen
+    from _harness import TORCH_DTYPE, to_dev
+    dt, hq, hkv, d, causal, lq, lk, uq, uk = case
+    p = datagen.Problem(dt, len(lq), hq, hkv, max(lq), max(lk), d, causal, 1 / math.sqrt(d), 77,
+                        lengths_q=tuple(lq), lengths_k=tuple(lk), name="seqused")
+    x = datagen.draw(p)
+    cq, ck = p.cu_seqlens()
+    uq_np, uk_np = np.array(uq, np.int32), np.array(uk, np.int32)
+    dev = {n: to_dev(v, dt) for n, v in x.items()}
+    cu = dict(cu_seqlens_q=torch.from_numpy(cq).cuda(), cu_seqlens_k=torch.from_numpy(ck).cuda(),
+              max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k,
+              seqused_q=torch.from_numpy(uq_np).cuda(), seqused_k=torch.from_numpy(uk_np).cuda())
+    used_q = np.zeros(cq[-1], bool)
+    used_k = np.zeros(ck[-1], bool)
+    for b in range(len(lq)):
+        used_q[cq[b]:cq[b] + uq[b]] = True
+        used_k[ck[b]:ck[b] + uk[b]] = True
+    print(f"seqused {_sequsedid(case)} dq={dq_algo}", flush=True)
+    sentinel = 3.0
+    # forward: used rows against the oracle, unused rows untouched
+    o_buf = torch.full_like(dev["q"], sentinel)
+    lse_buf = torch.full((hq, cq[-1]), sentinel, dtype=torch.float32, device="cuda")
+    api.forward(dev["q"], dev["k"], dev["v"], p.scale, causal, out=(o_buf, lse_buf), **cu)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.forward(x["q"], x["k"], x["v"], p.scale, causal, cq, ck, uq_np, uk_np)
+    go = to_host(o_buf)
+    assert_close("O", go[used_q], ro[used_q], dt)
+    assert np.all(go[~used_q] == sentinel)
+    gl = lse_buf.cpu().numpy().astype(np.float64)
+    assert np.all(gl[:, ~used_q] == sentinel)
+    fin = np.isfinite(rlse[:, used_q])
+    assert np.array_equal(np.isfinite(gl[:, used_q]), fin)
+    assert np.max(np.abs(gl[:, used_q][fin] - rlse[:, used_q][fin]), initial=0) <= 1e-4
+    # backward with the oracle's O and LSE on the used rows
+    o_in = round_like(np.where(used_q[:, None, None], ro, 0.0), dt)
+    lse_in = np.where(used_q[None, :], rlse, 0.0).astype(np.float32)
+    dev_o = to_dev(o_in, dt)
+    dev_lse = torch.from_numpy(lse_in).cuda()
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, causal, False, dq_algo=dq_algo, **cu)
+    dq = torch.full_like(dev["q"], sentinel)
+    dk = torch.full_like(dev["k"], sentinel)
+    dv = torch.full_like(dev["v"], sentinel)
+    plan.run(dev["q"], dev["k"], dev["v"], dev_o, dev["do"], dev_lse, dq, dk, dv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.backward(x["q"], x["k"], x["v"], o_in, x["do"], lse_in.astype(np.float64), p.scale, causal,
+                                    cq, ck, uq_np, uk_np)
+    for n, g, ref, used in (("dQ", dq, rdq, used_q), ("dK", dk, rdk, used_k), ("dV", dv, rdv, used_k)):
+        gh = to_host(g)
+        assert_close(n, gh[used], ref[used], dt)
+        assert np.all(gh[~used] == sentinel), f"{n}: a row past the used length was written"
