@@ -48,6 +48,10 @@ int validate_shape(const attn_shape_t* s) {
     // one-dimensional grids of the streaming kernels: (row, head) pairs times
     // lanes per pair must stay below 2^32 threads
     if (rows_q * s->num_heads_q > (1LL << 27) || rows_k * s->num_heads_kv > (1LL << 27)) return ATTN_ERR_BAD_SHAPE;
+    // a tile's byte offset within one sequence's Q/dO rows travels in a
+    // 32-bit scalar offset
+    if ((long long)s->seqlen_q * s->num_heads_q * s->head_dim * (s->dtype == ATTN_DTYPE_F32 ? 4 : 2) >= (1LL << 31))
+        return ATTN_ERR_BAD_SHAPE;
     return ATTN_OK;
 }
 

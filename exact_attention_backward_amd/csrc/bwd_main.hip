@@ -654,29 +654,41 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     const char* qbytes = reinterpret_cast<const char*>(a.q);
     const char* dobytes = reinterpret_cast<const char*>(a.dout);
     const char* sbytes = w == 0 ? reinterpret_cast<const char*>(a.lse) : reinterpret_cast<const char*>(a.delta);
-    // issue cursor: coordinates of the next tile to copy
+    // issue cursor: the next tile to copy.  The descriptors point at the
+    // current q-head's first tile; a tile's offset from there goes into the
+    // scalar offset, and the range word ends at the tile's last valid row,
+    // so a step only updates two offsets and two range words.
     int is_t = 0, is_m = m_begin, is_g = 0;
-    long long is_q = q_g0, is_l = l_g0;
-    unsigned is_buf = 0;   // ring offset of the next tile
+    int is_so = 0, is_lo = 0;   // byte offsets of the tile from the head's first tile (Q/dO, LSE/D)
+    unsigned is_buf = 0;        // ring offset of the next tile
+    const int full_q = (int)(BM * qstride * (long long)sizeof(T));
+    const int last_rows = si.len_q - (m_end - 1) * BM;   // rows of the last query tile
+    i32x4 rq = rsrc_words(qbytes + q_g0, 0), rdo = rsrc_words(dobytes + q_g0, 0), rs = rsrc_words(sbytes + l_g0, 0);
+    const unsigned sdst0 = w == 0 ? lds0 + C::BUF_LSE : w == 1 ? lds0 + C::BUF_DL : lds0 + C::OFF_DUMP;
+    const unsigned sstep = w < 2 ? 1u : 0u;   // the empty copies all land in the one dump slot
     auto issue_next = [&] {
-        const bool real = is_t < n_tiles;
-        const int rows = real ? min(si.len_q - is_m * BM, BM) : 0;
-        const unsigned qb = (unsigned)(rows * qstride * (long long)sizeof(T));
+        const int rows = is_t < n_tiles ? (is_m == m_end - 1 ? last_rows : BM) : 0;
+        // the range check covers scalar + per-lane offset: the range is the
+        // tile's offset plus its valid bytes
+        rq[2] = rdo[2] = __builtin_amdgcn_readfirstlane(is_so + rows * (int)(qstride * (long long)sizeof(T)));
+        rs[2] = __builtin_amdgcn_readfirstlane(w < 2 ? is_lo + rows * 4 : 0);
         const unsigned dst = lds0 + is_buf;
-        dma_to_lds16(rsrc_words(qbytes + is_q, qb), dst + C::BUF_Q + w * 1024, seg_voff);
-        dma_to_lds16(rsrc_words(dobytes + is_q, qb), dst + C::BUF_DO + w * 1024, seg_voff);
-        const unsigned sdst = w == 0 ? dst + C::BUF_LSE : w == 1 ? dst + C::BUF_DL : lds0 + C::OFF_DUMP;
-        if (lane < BM) dma_to_lds4(rsrc_words(sbytes + is_l, w < 2 ? rows * 4 : 0), sdst, lane * 4);
+        dma_to_lds16_so(rq, dst + C::BUF_Q + w * 1024, seg_voff, is_so);
+        dma_to_lds16_so(rdo, dst + C::BUF_DO + w * 1024, seg_voff, is_so);
+        dma_to_lds4_so(rs, sdst0 + sstep * is_buf, lane * 4, is_lo);
         ++is_t;
         is_buf = is_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : is_buf + C::BUF_BYTES;
         if (++is_m == m_end) {
             is_m = m_begin;
             ++is_g;
-            is_q = q_g0 + (long long)is_g * HD * (long long)sizeof(T);
-            is_l = l_g0 + is_g * lse_head;
+            is_so = 0;
+            is_lo = 0;
+            rq = rsrc_words(qbytes + q_g0 + (long long)is_g * HD * (long long)sizeof(T), 0);
+            rdo = rsrc_words(dobytes + q_g0 + (long long)is_g * HD * (long long)sizeof(T), 0);
+            rs = rsrc_words(sbytes + l_g0 + is_g * lse_head, 0);
         } else {
-            is_q += tile_step;
-            is_l += BM * 4;
+            is_so += full_q;
+            is_lo += BM * 4;
         }
     };
 

@@ -156,9 +156,9 @@ __device__ __forceinline__ void lds_write(char* lds_base, int byte_off, const V&
 // ---------------------------------------------------------------------------
 // buffer resources: base address, byte range and the gfx9 raw-buffer format
 // word.  Loads past the range return zeros and stores/atomics past it are
-// dropped; only the per-lane offset and the instruction offset take part in
-// that check, so every variable part of an address goes into the descriptor
-// base or the per-lane offset, never into the scalar offset.
+// dropped.  The check is on the sum of the per-lane, instruction and scalar
+// offsets (measured: a scalar offset past the range reads zeros), so a range
+// that should end at a tile's last valid byte includes the scalar offset.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -209,6 +209,16 @@ __device__ __forceinline__ void dma_to_lds16(i32x4 r, unsigned lds, int voff) {
 // should not displace reused tiles from the L2).
 __device__ __forceinline__ void dma_to_lds16_nt(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
+}
+// The same with a scalar offset added to the address; the range check
+// applies to the scalar plus the per-lane offset.
+__device__ __forceinline__ void dma_to_lds16_so(i32x4 r, unsigned lds, int voff, int soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
+}
+__device__ __forceinline__ void dma_to_lds4_so(i32x4 r, unsigned lds, int voff, int soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory");
 }
 __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");

@@ -69,7 +69,8 @@ typedef enum attn_status {
     ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL (the workspace included) */
     ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
                                   cu_seqlens, workspace too small, more than 2^27
-                                  (row, head) pairs in Q or K, ... */
+                                  (row, head) pairs in Q or K, 2 GiB or more of Q
+                                  in one sequence (seqlen_q x Hq x D elements), ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not 64 or 128,
                                   unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned (cu_seqlens and
