@@ -742,7 +742,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
-    auto step = [&](int t, f32x16* xc, f32x16* xp) {
+    auto step = [&](auto role_c, auto first_c, int t, f32x16* xc, f32x16* xp) {
+        constexpr int R = decltype(role_c)::value;   // this wave's role, a constant per loop
+        constexpr bool FIRST = decltype(first_c)::value;   // the dS wave's first step (no tile t-1)
         // this wave's copies of tile t have landed (those of the PD - 1 later
         // tiles may still fly); after the barrier all waves' have, P of tile
         // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
@@ -750,7 +752,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // in the stored-dS mode each dS-wave step also issues NST stores after
         // its copies, so the tiles' copies are counted past them (the first
         // step has no dS; it stores an empty range instead, to keep the count)
-        if (STORE_DS && role == 1)
+        if (STORE_DS && R == 1)
             wait_vmem_but<C::OPS * (C::PD - 1) + NST * C::PD>();
         else
             wait_vmem_but<C::OPS * (C::PD - 1)>();
@@ -761,11 +763,11 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // read now so their latency hides behind the first product: LSE of
         // tile t (P wave), or D and the partner's P of tile t-1 (dS wave)
         const float* lst = reinterpret_cast<const float*>(
-            smem + (role == 0 ? cur_buf + C::BUF_LSE : prev_buf + C::BUF_DL) + 16 * h);
+            smem + (R == 0 ? cur_buf + C::BUF_LSE : prev_buf + C::BUF_DL) + 16 * h);
         f32x4 stat[NMB * 4], pin[NMB * 4];
 #pragma unroll
         for (int q = 0; q < NMB * 4; ++q) stat[q] = *reinterpret_cast<const f32x4*>(lst + 8 * q);
-        if (role == 1) {
+        if constexpr (R == 1) {
             const int psr = pslots + ((t - 1) & 1) * C::PSLOT + lane * 16;
 #pragma unroll
             for (int q = 0; q < NMB * 4; ++q) pin[q] = *reinterpret_cast<const f32x4*>(smem + psr + q * 1024);
@@ -808,9 +810,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         (void)prev_g;
 
         // the tile whose second product this wave computes now
-        const int tt = role == 0 ? t : t - 1;
-        if (tt < 0 || tt >= n_tiles) {
-            if (STORE_DS && role == 1) {   // the dS wave's first step: empty stores
+        const int tt = R == 0 ? t : t - 1;   // the dS wave's later steps always have a tile t-1
+        if (FIRST || (R == 0 && tt >= n_tiles)) {
+            if (STORE_DS && FIRST) {   // the dS wave's first step: empty stores
                 const rsrc_t none = make_rsrc(a.ds, 0);
                 const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -818,11 +820,11 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             }
             return;
         }
-        const unsigned buf = role == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
+        const unsigned buf = R == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
                                        : prev_buf;
         const int ps = pslots + (tt & 1) * C::PSLOT + lane * 16;
         op_t opa[C::NIC];
-        if (role == 0) {
+        if constexpr (R == 0) {
             // ---- P = exp2(S s log2e - LSE log2e), masked on causal diagonal tiles
             auto softmax = [&](auto masked) {
 #pragma unroll
@@ -911,17 +913,31 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                 bop[c][d] = u32x4{x[0], x[1], y[0], y[1]};
             }
         }
-        if constexpr (STORE_DS) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < C::NIC; ++c) {
 #pragma unroll
             for (int d = 0; d < C::NDB; ++d) mma16(acc[d], opa[c], __builtin_bit_cast(op_t, bop[c][d]));
         }
         if constexpr (!STORE_DS) {
+            // every read first
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NIC * C::NDB, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, C::NIC * C::NDB, 0);
+        } else {
+            // one slice ahead (fewer registers held by the dS wave, which
+            // also keeps its store offsets): the reads of slice c + 1 go
+            // between the MFMAs of slice c
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NDB, 0);
+#pragma unroll
+            for (int c = 1; c < C::NIC; ++c) {
+#pragma unroll
+                for (int d = 0; d < C::NDB; ++d) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NDB, 0);
         }
-        if (STORE_DS && role == 1) {
+        if (STORE_DS && R == 1) {
             // dS (16-bit) of this pair's 32 keys straight from the MFMA operand
             // registers to the dS block: chunk (pair, c, lane) holds, for key
             // 32 pair + lane % 32, the rows 16c + 4 (lane / 32) + 0..3 and
@@ -941,11 +957,25 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         }
     };
 
-    // the dS wave keeps X of tile t until step t+1: two register sets, unrolled by two
+    // the dS wave keeps X of tile t until step t+1: two register sets, unrolled
+    // by two.  Each role runs its own copy of the loop (the same number of
+    // steps and barriers), compiled for that role alone.
     f32x16 xA[NMB], xB[NMB];
-    for (int t = 0; t <= n_tiles; t += 2) {
-        step(t, xA, xB);
-        if (t + 1 <= n_tiles) step(t + 1, xB, xA);
+    // The dS wave's first step (no tile t-1 yet) is peeled off its loop.
+    const std::false_type later;
+    if (role == 0) {
+        const std::integral_constant<int, 0> r0;
+        for (int t = 0; t <= n_tiles; t += 2) {
+            step(r0, later, t, xA, xB);
+            if (t + 1 <= n_tiles) step(r0, later, t + 1, xB, xA);
+        }
+    } else {
+        const std::integral_constant<int, 1> r1;
+        step(r1, std::true_type{}, 0, xA, xB);
+        for (int t = 1; t <= n_tiles; t += 2) {
+            step(r1, later, t, xB, xA);
+            if (t + 1 <= n_tiles) step(r1, later, t + 1, xA, xB);
+        }
     }
 
     // ---- epilogue: dV (P wave) or dK = s * sum dS^T Q (dS wave); rows past
