@@ -573,7 +573,7 @@ struct KvCfg {
     static constexpr int BM = HD == 128 ? 32 : 64;   // query rows per tile
     static constexpr int ROWB = HD * 2;
     static constexpr int TILE = BM * ROWB;
-    static constexpr int NBUF = 5;                   // ring of query-side tile buffers
+    static constexpr int NBUF = 4;                   // ring of query-side tile buffers
     static constexpr int PD = NBUF - 2;              // prefetch distance in tiles
     static constexpr int BUF_Q = 0, BUF_DO = TILE, BUF_LSE = 2 * TILE, BUF_DL = 2 * TILE + 256;
     static constexpr int BUF_BYTES = 2 * TILE + 512;
@@ -660,13 +660,12 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // so a step only updates two offsets and two range words.
     int is_t = 0, is_m = m_begin, is_g = 0;
     int is_so = 0, is_lo = 0;   // byte offsets of the tile from the head's first tile (Q/dO, LSE/D)
-    unsigned is_buf = 0;        // ring offset of the next tile
     const int full_q = (int)(BM * qstride * (long long)sizeof(T));
     const int last_rows = si.len_q - (m_end - 1) * BM;   // rows of the last query tile
     i32x4 rq = rsrc_words(qbytes + q_g0, 0), rdo = rsrc_words(dobytes + q_g0, 0), rs = rsrc_words(sbytes + l_g0, 0);
     const unsigned sdst0 = w == 0 ? lds0 + C::BUF_LSE : w == 1 ? lds0 + C::BUF_DL : lds0 + C::OFF_DUMP;
     const unsigned sstep = w < 2 ? 1u : 0u;   // the empty copies all land in the one dump slot
-    auto issue_next = [&] {
+    auto issue_next = [&](unsigned is_buf) {   // is_buf: ring offset of the tile's buffer
         const int rows = is_t < n_tiles ? (is_m == m_end - 1 ? last_rows : BM) : 0;
         // the range check covers scalar + per-lane offset: the range is the
         // tile's offset plus its valid bytes
@@ -677,7 +676,6 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         dma_to_lds16_so(rdo, dst + C::BUF_DO + w * 1024, seg_voff, is_so);
         dma_to_lds4_so(rs, sdst0 + sstep * is_buf, lane * 4, is_lo);
         ++is_t;
-        is_buf = is_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : is_buf + C::BUF_BYTES;
         if (++is_m == m_end) {
             is_m = m_begin;
             ++is_g;
@@ -697,7 +695,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // the compiler that the K/V registers are ready; otherwise it would wait
     // for them (vmcnt(0), the prefetches included) inside the loop.
 #pragma unroll
-    for (int t = 0; t < C::PD; ++t) issue_next();
+    for (int t = 0; t < C::PD; ++t) issue_next(t * C::BUF_BYTES);
     op_t wreg[C::NC];
     {
         const T* src = reinterpret_cast<const T*>(role == 0 ? a.k : a.v) + kv_base;
@@ -717,7 +715,6 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     const float scale2 = a.scale * kLog2e;
     const int j = n * kBN + 32 * pair + l32;   // this lane's key (column of S)
     const int diag = n * kBN + kBN - 1 - off;  // tiles starting at or below this row are unmasked
-    unsigned cur_buf = 0;                      // ring offset of tile t
     int cur_m = m_begin;                       // query tile of tile t
     int cur_g = 0;                             // q-head (within the group) of tile t
     int last_m = m_begin, last_g = 0;          // the same for tile t-1
@@ -742,9 +739,15 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
-    auto step = [&](auto role_c, auto first_c, int t, f32x16* xc, f32x16* xp) {
+    auto step = [&](auto role_c, auto first_c, auto k_c, int t, f32x16* xc, f32x16* xp) {
         constexpr int R = decltype(role_c)::value;   // this wave's role, a constant per loop
         constexpr bool FIRST = decltype(first_c)::value;   // the dS wave's first step (no tile t-1)
+        // ring buffers of tiles t, t-1 and t+PD (t = K mod NBUF), compile-time
+        // constants: LDS addresses are per-lane constants plus immediate offsets
+        constexpr int K = decltype(k_c)::value;
+        constexpr unsigned CUR = K * C::BUF_BYTES;
+        constexpr unsigned PREV = ((K + C::NBUF - 1) % C::NBUF) * C::BUF_BYTES;
+        constexpr unsigned ISS = ((K + C::PD) % C::NBUF) * C::BUF_BYTES;
         // this wave's copies of tile t have landed (those of the PD - 1 later
         // tiles may still fly); after the barrier all waves' have, P of tile
         // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
@@ -757,31 +760,32 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         else
             wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
-        const unsigned prev_buf = cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES;
         const int i0 = cur_m * BM;
         // row statistics of the tile whose second product comes in this step,
         // read now so their latency hides behind the first product: LSE of
         // tile t (P wave), or D and the partner's P of tile t-1 (dS wave)
         const float* lst = reinterpret_cast<const float*>(
-            smem + (R == 0 ? cur_buf + C::BUF_LSE : prev_buf + C::BUF_DL) + 16 * h);
+            smem + (R == 0 ? CUR + C::BUF_LSE : PREV + C::BUF_DL) + 16 * h);
         f32x4 stat[NMB * 4], pin[NMB * 4];
 #pragma unroll
         for (int q = 0; q < NMB * 4; ++q) stat[q] = *reinterpret_cast<const f32x4*>(lst + 8 * q);
         if constexpr (R == 1) {
-            const int psr = pslots + ((t - 1) & 1) * C::PSLOT + lane * 16;
+            const int psr = pslots + ((K + 1) & 1) * C::PSLOT + lane * 16;   // slot of tile t-1
 #pragma unroll
             for (int q = 0; q < NMB * 4; ++q) pin[q] = *reinterpret_cast<const f32x4*>(smem + psr + q * 1024);
         }
 
         // ---- X = Q K^T (P wave) or dO V^T (dS wave) for tile t
         if (t < n_tiles) {
-            const int rb = (int)cur_buf + tile_off + rbase;
+            // the swizzle XOR touches only address bits 5-7, which are zero
+            // in the ring offset, so the offset is an immediate
+            const int rb = tile_off + rbase;
             op_t ra[C::NC];
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
                 for (int c = 0; c < C::NC; ++c)
-                    ra[c] = __builtin_bit_cast(op_t, lds_read16(smem, ((rb ^ (32 * c)) + mb * 32 * ROWB)));
+                    ra[c] = __builtin_bit_cast(op_t, lds_read16(smem, (rb ^ (32 * c)) + (int)CUR + mb * 32 * ROWB));
 #pragma unroll
                 for (int v = 0; v < 16; ++v) xc[mb][v] = 0.f;
 #pragma unroll
@@ -791,8 +795,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             __builtin_amdgcn_sched_group_barrier(0x100, NMB * C::NC, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NMB * C::NC, 0);
         }
-        issue_next();
-        cur_buf = cur_buf == (C::NBUF - 1) * C::BUF_BYTES ? 0 : cur_buf + C::BUF_BYTES;
+        issue_next(ISS);
         const int tile_m = cur_m, tile_g = cur_g;   // coordinates of tile t
         const char* ds_prev = ds_last;              // dS blocks of tile t-1
         if (STORE_DS) ds_last = ds_cur;
@@ -820,12 +823,12 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             }
             return;
         }
-        const unsigned buf = R == 0 ? (cur_buf == 0 ? (C::NBUF - 1) * C::BUF_BYTES : cur_buf - C::BUF_BYTES)
-                                       : prev_buf;
-        const int ps = pslots + (tt & 1) * C::PSLOT + lane * 16;
+        constexpr unsigned buf = R == 0 ? CUR : PREV;
+        const int ps = pslots + ((R == 0 ? K : K + 1) & 1) * C::PSLOT + lane * 16;   // slot of tile tt
         op_t opa[C::NIC];
         if constexpr (R == 0) {
             // ---- P = exp2(S s log2e - LSE log2e), masked on causal diagonal tiles
+            const int dj = j - (i0 + off + 4 * h);   // key column relative to this lane's first row
             auto softmax = [&](auto masked) {
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
@@ -840,7 +843,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                             if constexpr (decltype(masked)::value) {
                                 const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
                                 p = __builtin_amdgcn_exp2f(xc[mb][v] * scale2 - l2);
-                                p = j <= i0 + r + 4 * h + e + off ? p : 0.f;
+                                p = dj <= r + e ? p : 0.f;   // j <= i0 + r + 4h + e + off
                             } else {
                                 p = __builtin_amdgcn_exp2f(fmaf(xc[mb][v], scale2, -lse[e] * kLog2e));
                             }
@@ -896,8 +899,8 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             }
         }
         // ---- dV += P^T dO (P wave) or dK += dS^T Q (dS wave)
-        const int cb = (int)buf + col_off;
-        const int t0 = cb + tbase0, t1 = cb + tbase1;
+        // the XOR touches address bits 6-7 only, zero in the ring offset
+        const int t0 = col_off + tbase0, t1 = col_off + tbase1;
         // every transposing read is issued before the first MFMA.  With the
         // dS stores in the block, the compiler sinks the reads to their uses
         // (exposing the LDS latency once per MFMA) unless a scheduling
@@ -908,8 +911,8 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         for (int c = 0; c < C::NIC; ++c) {
 #pragma unroll
             for (int d = 0; d < C::NDB; ++d) {
-                const u32x2 x = lds_read_tr(smem, (t0 ^ (64 * d)) + c * 16 * ROWB);
-                const u32x2 y = lds_read_tr(smem, (t1 ^ (64 * d)) + c * 16 * ROWB);
+                const u32x2 x = lds_read_tr(smem, (t0 ^ (64 * d)) + (int)buf + c * 16 * ROWB);
+                const u32x2 y = lds_read_tr(smem, (t1 ^ (64 * d)) + (int)buf + c * 16 * ROWB);
                 bop[c][d] = u32x4{x[0], x[1], y[0], y[1]};
             }
         }
@@ -962,19 +965,36 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // steps and barriers), compiled for that role alone.
     f32x16 xA[NMB], xB[NMB];
     // The dS wave's first step (no tile t-1 yet) is peeled off its loop.
+    // The loops are unrolled by the ring length, so each step's buffers are
+    // constants (NBUF is even, which also fixes the tile parity per step).
+    static_assert(C::NBUF == 4, "the unrolled loops below assume a ring of four");
     const std::false_type later;
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
     if (role == 0) {
         const std::integral_constant<int, 0> r0;
-        for (int t = 0; t <= n_tiles; t += 2) {
-            step(r0, later, t, xA, xB);
-            if (t + 1 <= n_tiles) step(r0, later, t + 1, xB, xA);
+        for (int t = 0; t <= n_tiles; t += 4) {
+            step(r0, later, K0{}, t, xA, xB);
+            if (t + 1 > n_tiles) break;
+            step(r0, later, K1{}, t + 1, xB, xA);
+            if (t + 2 > n_tiles) break;
+            step(r0, later, K2{}, t + 2, xA, xB);
+            if (t + 3 > n_tiles) break;
+            step(r0, later, K3{}, t + 3, xB, xA);
         }
     } else {
         const std::integral_constant<int, 1> r1;
-        step(r1, std::true_type{}, 0, xA, xB);
-        for (int t = 1; t <= n_tiles; t += 2) {
-            step(r1, later, t, xB, xA);
-            if (t + 1 <= n_tiles) step(r1, later, t + 1, xA, xB);
+        step(r1, std::true_type{}, K0{}, 0, xA, xB);
+        for (int t = 1; t <= n_tiles; t += 4) {
+            step(r1, later, K1{}, t, xB, xA);
+            if (t + 1 > n_tiles) break;
+            step(r1, later, K2{}, t + 1, xA, xB);
+            if (t + 2 > n_tiles) break;
+            step(r1, later, K3{}, t + 2, xB, xA);
+            if (t + 3 > n_tiles) break;
+            step(r1, later, K0{}, t + 3, xA, xB);
         }
     }
 
@@ -1019,10 +1039,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     if (CAUSAL) {
         const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
         const int n2 = nk - 1 - p;
-        if (p <= n2) kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
-        if (n2 > p) {
-            __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, n2, si, smem);
+        // one call site in a loop: a single copy of the (large) tile body
+        const int cnt = (p <= n2) + (n2 > p);
+        for (int k = 0; k < cnt; ++k) {
+            if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
+            kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
         kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
