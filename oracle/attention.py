@@ -66,20 +66,35 @@ __all__ = [
 # one (batch, head) pair
 # --------------------------------------------------------------------------
 
-def visible(sq, sk, causal):
+def visible(sq, sk, causal, window=None):
     """Boolean [sq, sk]: True where query i may attend to key j.
 
     Non-causal: every key.  Causal: ``j <= i + (sk - sq)`` (bottom-right
     alignment; for sq == sk this is the usual lower triangle).
+
+    ``window = (left, right)``: a local (sliding-window) mask on the same
+    bottom-right-aligned diagonal, ``i + off - left <= j <= i + off + right``
+    with off = sk - sq; a negative side is unbounded.  The composable-kernel
+    page only shows that the pipeline asks the mask for each tile's key range
+    and for out-of-bound elements; these bounds are the reading taken, and
+    they combine with the causal bound by intersection.
     """
-    if not causal:
-        return np.ones((sq, sk), dtype=bool)
     i = np.arange(sq)[:, None]
     j = np.arange(sk)[None, :]
-    return j <= i + (sk - sq)
+    off = sk - sq
+    ok = np.ones((sq, sk), dtype=bool)
+    if causal:
+        ok &= j <= i + off
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok &= j >= i + off - left
+        if right >= 0:
+            ok &= j <= i + off + right
+    return ok
 
 
-def head_forward(q, k, v, scale, causal):
+def head_forward(q, k, v, scale, causal, window=None):
     """Softmax attention for one head.
 
     q [sq, d], k [sk, d], v [sk, d] -> (o [sq, d], lse [sq]), float64.
@@ -91,7 +106,7 @@ def head_forward(q, k, v, scale, causal):
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     sq, sk = q.shape[0], k.shape[0]
-    ok = visible(sq, sk, causal)
+    ok = visible(sq, sk, causal, window)
     s = scale * (q @ k.T)
     has_key = ok.any(axis=1)
     # row maximum over visible keys (0 for empty rows, never used)
@@ -107,16 +122,16 @@ def head_forward(q, k, v, scale, causal):
     return o, lse
 
 
-def _probabilities(q, k, lse, scale, causal):
+def _probabilities(q, k, lse, scale, causal, window=None):
     """P recomputed from the saved LSE (stages 1-2): exp(s q_i.k_j - lse_i)."""
     sq, sk = q.shape[0], k.shape[0]
-    ok = visible(sq, sk, causal) & np.isfinite(lse)[:, None]
+    ok = visible(sq, sk, causal, window) & np.isfinite(lse)[:, None]
     s = scale * (q @ k.T)
     safe_lse = np.where(np.isfinite(lse), lse, 0.0)
     return np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))
 
 
-def head_backward(q, k, v, o, do, lse, scale, causal, details=False):
+def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None):
     """Gradient of attention for one head, given O and LSE as saved by a forward.
 
     Returns (dq [sq, d], dk [sk, d], dv [sk, d]) in float64; with
@@ -128,7 +143,7 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False):
     o = np.asarray(o, np.float64)
     do = np.asarray(do, np.float64)
     lse = np.asarray(lse, np.float64)
-    p = _probabilities(q, k, lse, scale, causal)          # stages 1-2
+    p = _probabilities(q, k, lse, scale, causal, window)  # stages 1-2
     delta = np.sum(do * o, axis=1)                        # D = rowsum(dO * O)
     dp = do @ v.T                                         # stage 4
     dv = p.T @ do                                         # stage 3
@@ -203,7 +218,7 @@ def _lse_view(lse, varlen, nseq, hq, sq):
 
 
 def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None,
-                  seqused_q=None, seqused_k=None):
+                  seqused_q=None, seqused_k=None, window=None):
     """Forward for the q-heads of one kv-head group of one sequence.
 
     Returns {q_head: (o [len_q, d], lse [len_q])}.
@@ -214,12 +229,12 @@ def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_se
     qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
     out = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
-        out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal)
+        out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal, window)
     return out
 
 
 def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
-                   cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None):
+                   cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None, window=None):
     """Backward for one kv-head group of one sequence.
 
     Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
@@ -237,14 +252,15 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
     dq = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
         dqh, dkh, dvh = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
-                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal)
+                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, window=window)
         dq[h] = dqh
         dk += dkh
         dv += dvh
     return dq, dk, dv
 
 
-def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None):
+def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None,
+            window=None):
     """Full forward.  Returns (o, lse) in the layouts given in the module doc
     (rows past a sequence's used length are left at zero)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -254,7 +270,7 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
     for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g,
-                                             cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k).items():
+                                             cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, window).items():
                 o[q0:q1, h] = oh
                 lse[h, q0:q1] = lh
     if varlen:
@@ -263,7 +279,7 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
 
 
 def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-             seqused_q=None, seqused_k=None):
+             seqused_q=None, seqused_k=None, window=None):
     """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64);
     rows past a sequence's used length are left at zero."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -274,7 +290,7 @@ def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k
     for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g,
-                                           cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)
+                                           cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, window)
             for h, x in dqg.items():
                 dq[q0:q1, h] = x
             dk[k0:k1, g] = dkg

@@ -110,13 +110,13 @@ def test_golden_worked_examples():
 # backward: central finite differences of L = sum(dO * O)
 # --------------------------------------------------------------------------
 
-def _fd_case(q, k, v, do, scale, causal, cu_q=None, cu_k=None):
+def _fd_case(q, k, v, do, scale, causal, cu_q=None, cu_k=None, window=None):
     """Analytic gradients vs central differences, h = 1e-5, every entry."""
-    o, lse = oracle.forward(q, k, v, scale, causal, cu_q, cu_k)
-    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, scale, causal, cu_q, cu_k)
+    o, lse = oracle.forward(q, k, v, scale, causal, cu_q, cu_k, window=window)
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, scale, causal, cu_q, cu_k, window=window)
 
     def loss(qq, kk, vv):
-        oo, _ = oracle.forward(qq, kk, vv, scale, causal, cu_q, cu_k)
+        oo, _ = oracle.forward(qq, kk, vv, scale, causal, cu_q, cu_k, window=window)
         return float(np.sum(do * oo))
 
     h = 1e-5
@@ -172,8 +172,106 @@ def test_backward_finite_differences_varlen(causal):
 
 
 # --------------------------------------------------------------------------
+# local (sliding-window) masks
+# --------------------------------------------------------------------------
+
+def _window_mask_loops(sq, sk, causal, left, right):
+    """The visibility rule written as scalar loops (independent of the oracle's
+    vectorised form)."""
+    off = sk - sq
+    m = np.zeros((sq, sk), bool)
+    for i in range(sq):
+        for j in range(sk):
+            ok = True
+            if causal and j > i + off:
+                ok = False
+            if left >= 0 and j < i + off - left:
+                ok = False
+            if right >= 0 and j > i + off + right:
+                ok = False
+            m[i, j] = ok
+    return m
+
+
+@pytest.mark.parametrize("sq,sk", [(9, 9), (6, 11), (11, 6)])
+@pytest.mark.parametrize("causal,left,right", [(False, 3, 2), (True, 2, -1), (False, -1, 0), (False, 0, 0),
+                                               (True, 4, 1), (False, 1, -1), (False, 40, 40)])
+def test_window_visibility_and_special_cases(sq, sk, causal, left, right):
+    want = _window_mask_loops(sq, sk, causal, left, right)
+    assert np.array_equal(A.visible(sq, sk, causal, (left, right)), want)
+    # no window == (-1, -1); causal == the window (-1, 0); a window wider
+    # than the keys == no window
+    assert np.array_equal(A.visible(sq, sk, causal, (-1, -1)), A.visible(sq, sk, causal))
+    assert np.array_equal(A.visible(sq, sk, False, (-1, 0)), A.visible(sq, sk, True))
+    assert np.array_equal(A.visible(sq, sk, causal, (sq + sk, sq + sk)), A.visible(sq, sk, causal))
+
+
+def test_window_zero_width_closed_form():
+    """window (0, 0): row i sees only key i + off, so P is one-hot: O_i = V_j,
+    dV_j = dO_i, and dQ = dK = 0 (dS = P (dO.V_j - dO.O_i) = 0)."""
+    rng = np.random.default_rng(31)
+    sq, sk = 7, 10
+    q, k, v, do = rand(rng, sq, 5), rand(rng, sk, 5), rand(rng, sk, 5), rand(rng, sq, 5)
+    o, lse = A.head_forward(q, k, v, 0.7, False, window=(0, 0))
+    off = sk - sq
+    assert np.max(np.abs(o - v[off:off + sq])) <= 1e-14
+    assert np.max(np.abs(lse - 0.7 * np.sum(q * k[off:off + sq], axis=1))) <= 1e-13
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.7, False, window=(0, 0))
+    assert np.max(np.abs(dq)) <= 1e-13 and np.max(np.abs(dk)) <= 1e-13
+    want_dv = np.zeros_like(v)
+    want_dv[off:off + sq] = do
+    assert np.max(np.abs(dv - want_dv)) <= 1e-14
+
+
+@pytest.mark.parametrize("causal,window", [(False, (2, 1)), (True, (3, -1)), (False, (0, 4))])
+def test_backward_finite_differences_window(causal, window):
+    rng = np.random.default_rng(41)
+    q, k, v = rand(rng, 1, 9, 2, 3), rand(rng, 1, 7, 1, 3), rand(rng, 1, 7, 1, 3)
+    do = rand(rng, 1, 9, 2, 3)
+    _fd_case(q, k, v, do, 0.45, causal, window=window)
+
+
+def test_window_varlen_equals_per_sequence():
+    rng = np.random.default_rng(42)
+    lens = [5, 1, 12]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v, do = rand(rng, cu[-1], 2, 4), rand(rng, cu[-1], 2, 4), rand(rng, cu[-1], 2, 4), rand(rng, cu[-1], 2, 4)
+    o, lse = oracle.forward(q, k, v, 0.5, True, cu, cu, window=(3, -1))
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, 0.5, True, cu, cu, window=(3, -1))
+    for bi in range(3):
+        sl = slice(cu[bi], cu[bi + 1])
+        od, lsed = oracle.forward(q[None, sl], k[None, sl], v[None, sl], 0.5, True, window=(3, -1))
+        assert np.max(np.abs(o[sl] - od[0])) <= 1e-12
+        dd = oracle.backward(q[None, sl], k[None, sl], v[None, sl], od, do[None, sl], lsed, 0.5, True, window=(3, -1))
+        for a_, b_ in zip((dq, dk, dv), dd):
+            assert np.max(np.abs(a_[sl] - b_[0])) <= 1e-12
+
+
+# --------------------------------------------------------------------------
 # backward: independent library autograd (torch, float64)
 # --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sq,sk,left,right", [(30, 30, 5, 3), (20, 37, 9, -1), (37, 20, 2, 6)])
+def test_window_backward_matches_torch_autograd_float64(sq, sk, left, right):
+    """A windowed mask as an explicit boolean mask in torch float64 autograd."""
+    import torch
+    rng = np.random.default_rng(12)
+    q, k, v, do = rand(rng, sq, 8), rand(rng, sk, 8), rand(rng, sk, 8), rand(rng, sq, 8)
+    mask = torch.from_numpy(_window_mask_loops(sq, sk, False, left, right))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = (0.3 * tq @ tk.T).masked_fill(~mask, float("-inf"))
+    rows = mask.any(dim=1)
+    pr = torch.where(rows[:, None], torch.softmax(torch.where(rows[:, None], s, torch.zeros_like(s)), dim=-1)
+                     * mask, torch.zeros_like(s))
+    out = pr @ tv
+    out.backward(torch.from_numpy(do))
+    o, lse = A.head_forward(q, k, v, 0.3, False, window=(left, right))
+    assert np.max(np.abs(o - out.detach().numpy())) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.3, False, window=(left, right))
+    assert rel_err(dq, tq.grad.numpy()) <= 1e-12
+    assert rel_err(dk, tk.grad.numpy()) <= 1e-12
+    assert rel_err(dv, tv.grad.numpy()) <= 1e-12
+
 
 @pytest.mark.parametrize("sq,sk,causal", [(40, 40, True), (40, 40, False), (25, 61, True)])
 def test_backward_matches_torch_autograd_float64(sq, sk, causal):
