@@ -56,6 +56,9 @@ class AttnShape(ctypes.Structure):
         ("dq_algo", ctypes.c_int32),
         ("seqused_q", ctypes.c_void_p),
         ("seqused_k", ctypes.c_void_p),
+        ("local", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 

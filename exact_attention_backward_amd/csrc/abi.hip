@@ -37,6 +37,8 @@ int validate_shape(const attn_shape_t* s) {
         return ATTN_ERR_MISALIGNED;
     if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
     if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
+    if (s->local != 0 && s->local != 1) return ATTN_ERR_BAD_SHAPE;
+    if (s->local && (s->window_left < -1 || s->window_right < -1)) return ATTN_ERR_BAD_SHAPE;
     if (s->deterministic != 0 && s->deterministic != 1) return ATTN_ERR_BAD_SHAPE;
     if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC && s->dq_algo != ATTN_DQ_STORED_DS)
         return ATTN_ERR_UNSUPPORTED;
@@ -56,6 +58,21 @@ int validate_shape(const attn_shape_t* s) {
 }
 
 bool varlen(const attn_shape_t* s) { return s->cu_seqlens_q != nullptr; }
+
+// Window bounds of the kernels: key j visible to query i iff
+// i + off - lo <= j <= i + off + hi (kNoWindow: unbounded side).  Sequences
+// hold fewer than 2^27 rows, so a window of kNoWindow or more already spans
+// every key and is clamped there (keeping i + off + hi inside 32 bits).
+int win_lo(const attn_shape_t* s) {
+    return s->local && s->window_left >= 0 ? (s->window_left < kNoWindow ? s->window_left : kNoWindow) : kNoWindow;
+}
+int win_hi(const attn_shape_t* s) {
+    if (s->causal) return 0;   // the causal bound is the tighter one (window_right >= 0)
+    return s->local && s->window_right >= 0 ? (s->window_right < kNoWindow ? s->window_right : kNoWindow)
+                                            : kNoWindow;
+}
+// whether any bound applies (the kernels' masked instantiation)
+bool masked(const attn_shape_t* s) { return win_lo(s) < kNoWindow || win_hi(s) < kNoWindow; }
 long long rows_q(const attn_shape_t* s) { return varlen(s) ? s->total_q : (long long)s->batch * s->seqlen_q; }
 
 size_t elem_bytes(const attn_shape_t* s) { return s->dtype == ATTN_DTYPE_F32 ? 4 : 2; }
@@ -124,7 +141,9 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
               s->num_heads_q, s->num_heads_kv,
               s->seqlen_q, s->seqlen_k, s->total_q, s->total_k, s->softmax_scale};
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    launch_fwd(a, s->dtype, s->head_dim, s->causal != 0, reinterpret_cast<hipStream_t>(stream));
+    a.win_lo = win_lo(s);
+    a.win_hi = win_hi(s);
+    launch_fwd(a, s->dtype, s->head_dim, masked(s), reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -191,6 +210,8 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.nblk_m = nblk_m(s);
     a.scale = s->softmax_scale;
     a.deterministic = s->deterministic;
+    a.win_lo = win_lo(s);
+    a.win_hi = win_hi(s);
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
@@ -200,13 +221,13 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     }
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    launch_bwd(a, s->dtype, s->head_dim, s->causal != 0, s->dq_algo, hs);
+    launch_bwd(a, s->dtype, s->head_dim, masked(s), s->dq_algo, hs);
     if (s->dq_algo == ATTN_DQ_SEPARATE) {
         BwdArgs d = a;
         d.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
-        launch_bwd_dq(d, s->dtype, s->head_dim, s->causal != 0, hs);
+        launch_bwd_dq(d, s->dtype, s->head_dim, masked(s), hs);
     } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
-        launch_bwd_dq_gemm(a, s->dtype, s->head_dim, s->causal != 0, hs);
+        launch_bwd_dq_gemm(a, s->dtype, s->head_dim, masked(s), hs);
     }
     return check_launch();
 }

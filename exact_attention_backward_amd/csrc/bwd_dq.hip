@@ -147,7 +147,7 @@ __device__ __forceinline__ void dq_wait_vmem_but(int n) {
 }  // namespace
 
 // dQ rows of query tile m (128 rows) of q-head hq in sequence b.
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool MASKED>
 __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                         char* smem) {
     using C = DqCfg<T, HD>;
@@ -160,12 +160,16 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     const int i0 = m * BQ;
     if (i0 >= si.len_q) return;
     const bool varlen = a.cu_q != nullptr;
-    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+    const int off = si.len_k - si.len_q;   // bottom-right alignment of the mask
 
-    // keys any row of this tile can see
-    int key_end = si.len_k;
-    if (CAUSAL) key_end = min(key_end, min(i0 + BQ, si.len_q) - 1 + off + 1);
-    const int n_kt = key_end > 0 ? (key_end + BN - 1) / BN : 0;
+    // key tiles any row of this tile can see: kt_b .. kt_b + n_kt - 1
+    int key_end = si.len_k, kt_b = 0;
+    if (MASKED) {
+        key_end = min(key_end, min(i0 + BQ, si.len_q) - 1 + off + a.win_hi + 1);
+        const int key_beg = i0 + off - a.win_lo;   // the first row's lower bound
+        kt_b = key_beg > 0 ? key_beg / BN : 0;
+    }
+    const int n_kt = key_end > 0 ? max((key_end + BN - 1) / BN - kt_b, 0) : 0;
 
     const long long qstride = (long long)a.hq * HD;
     const long long kstride = (long long)a.hkv * HD;
@@ -176,11 +180,13 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     kvcopy.init(w, lane, (int)(kstride * sizeof(T)));
     constexpr int kOpsPerTile = 2 * DqTileCopy<C::ROWB, BN>::N;   // copies one wave issues per tile
     static_assert(kOpsPerTile * (C::NS - 2) < 16, "vmcnt range");
-    auto buf_of = [&](int kt) { return smem + (kt % C::NS) * C::BUF_BYTES; };
-    auto issue_tile = [&](int kt) {
+    // the u-th tile of the run (key tile kt_b + u) goes to ring buffer u % NS
+    auto buf_of = [&](int u) { return smem + (u % C::NS) * C::BUF_BYTES; };
+    auto issue_tile = [&](int u) {
+        const int kt = kt_b + u;
         const int rows = min(si.len_k - kt * BN, BN);
         const unsigned bytes = (unsigned)(rows * kstride * sizeof(T));
-        char* buf = buf_of(kt);
+        char* buf = buf_of(u);
         kvcopy.issue(rsrc_words(kg + (long long)kt * BN * kstride, bytes), buf + C::BUF_K, w);
         kvcopy.issue(rsrc_words(vg + (long long)kt * BN * kstride, bytes), buf + C::BUF_V, w);
     };
@@ -206,8 +212,9 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         dl = a.delta[row0 + i];
     }
     const float scale2 = a.scale * kLog2e;
-    // key j is visible to this lane's row iff j < lim
-    const int lim = row_ok ? (CAUSAL ? min(si.len_k, i + off + 1) : si.len_k) : 0;
+    // key j is visible to this lane's row iff lim_lo <= j < lim
+    const int lim = row_ok ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
+    const int lim_lo = MASKED ? i + off - a.win_lo : 0;
 
     f32x16 dq[C::NDB];
 #pragma unroll
@@ -217,18 +224,18 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     }
 
     // prologue: the first NS - 1 tiles in flight
-    for (int kt = 0; kt < C::NS - 1 && kt < n_kt; ++kt) issue_tile(kt);
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const char* buf = buf_of(kt);
-        // tile kt has landed once only the tiles issued after it may be in flight
-        dq_wait_vmem_but(kOpsPerTile * (min(kt + C::NS - 2, n_kt - 1) - kt));
-        __syncthreads();   // tile kt is visible to all waves; tile kt-1's buffer is free
-        if (kt + C::NS - 1 < n_kt) issue_tile(kt + C::NS - 1);
+    for (int u = 0; u < C::NS - 1 && u < n_kt; ++u) issue_tile(u);
+    for (int u = 0; u < n_kt; ++u) {
+        const char* buf = buf_of(u);
+        // tile u has landed once only the tiles issued after it may be in flight
+        dq_wait_vmem_but(kOpsPerTile * (min(u + C::NS - 2, n_kt - 1) - u));
+        __syncthreads();   // tile u is visible to all waves; tile u-1's buffer is free
+        if (u + C::NS - 1 < n_kt) issue_tile(u + C::NS - 1);
         const char* lk = buf + C::BUF_K;
         const char* lv = buf + C::BUF_V;
-        const int j0 = kt * BN;
+        const int j0 = (kt_b + u) * BN;
         const bool edge = !((j0 + BN <= si.len_k) && (i0 + BQ <= si.len_q) &&
-                            (!CAUSAL || j0 + BN - 1 <= i0 + off));
+                            (!MASKED || (j0 + BN - 1 <= i0 + off + a.win_hi && j0 >= i0 + BQ - 1 + off - a.win_lo)));
 
         // ---- S^T = K Q^T and dP^T = V dO^T (rows = keys, columns = this wave's queries)
         f32x16 st[C::NJB], dpt[C::NJB];
@@ -262,7 +269,7 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
                     float p = __builtin_amdgcn_exp2f(st[jb][v] * scale2 - l2);
                     if constexpr (decltype(masked)::value) {
                         const int j = j0 + 32 * jb + acc_row(v, h);
-                        p = j < lim ? p : 0.f;
+                        p = (j < lim && j >= lim_lo) ? p : 0.f;
                     }
                     dpt[jb][v] = p * (dpt[jb][v] - dl);
                 }
@@ -308,15 +315,15 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 }
 
 
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool MASKED>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
     // kv-head) run on one XCD, so their K/V reads share an L2.  Under a causal
     // mask the keys a query tile sees grow linearly with its index, so
-    // workgroup p takes the tiles p and (last - p).
+    // workgroup p takes the tiles p and (last - p) (also under a window).
     const int G = a.hq / a.hkv;
-    const int n_pair = CAUSAL ? (a.nblk_m + 1) / 2 : a.nblk_m;
+    const int n_pair = MASKED ? (a.nblk_m + 1) / 2 : a.nblk_m;
     const int per_group = n_pair * G;          // workgroups of one (sequence, kv-head)
     int grp, slot;
     {
@@ -335,23 +342,23 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
     const int hq = hkv * G + slot / n_pair;
     const int p = slot % n_pair;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
-    if (CAUSAL) {
+    if (MASKED) {
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
         const int m2 = nq - 1 - p;
         if (m2 > p) {
-            dq_tile<T, HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            dq_tile<T, HD, MASKED>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
             __syncthreads();   // its LDS ring is free again
         }
-        if (p < nq && p <= m2) dq_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        if (p < nq && p <= m2) dq_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     } else {
-        dq_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        dq_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
-static void launch_dq_t(const BwdArgs& a, bool causal, hipStream_t st) {
-    const unsigned grid = (unsigned)((causal ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
-    if (causal)
+static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
+    const unsigned grid = (unsigned)((masked ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
+    if (masked)
         bwd_dq_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
     else
         bwd_dq_kernel<T, HD, false><<<grid, kThreads, 0, st>>>(a);
@@ -359,16 +366,16 @@ static void launch_dq_t(const BwdArgs& a, bool causal, hipStream_t st) {
 
 int bwd_dq_block_m() { return 32 * kWaves; }
 
-void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) launch_dq_t<bf16_t, 64>(a, causal, st);
-        else launch_dq_t<bf16_t, 128>(a, causal, st);
+        if (hd == 64) launch_dq_t<bf16_t, 64>(a, masked, st);
+        else launch_dq_t<bf16_t, 128>(a, masked, st);
     } else if (dtype == ATTN_DTYPE_F16) {
-        if (hd == 64) launch_dq_t<f16_t, 64>(a, causal, st);
-        else launch_dq_t<f16_t, 128>(a, causal, st);
+        if (hd == 64) launch_dq_t<f16_t, 64>(a, masked, st);
+        else launch_dq_t<f16_t, 128>(a, masked, st);
     } else {
-        if (hd == 64) launch_dq_t<float, 64>(a, causal, st);
-        else launch_dq_t<float, 128>(a, causal, st);
+        if (hd == 64) launch_dq_t<float, 64>(a, masked, st);
+        else launch_dq_t<float, 128>(a, masked, st);
     }
 }
 

@@ -68,7 +68,7 @@ __device__ __forceinline__ void g_wait_vmem_but() {
 }  // namespace
 
 // dQ rows of query tile m (256 rows) of q-head hq in sequence b.
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool MASKED>
 __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                           char* smem) {
     using C = DqgCfg<HD>;
@@ -80,25 +80,47 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     const int i0 = m * BQ;
     if (i0 >= si.len_q) return;
     const bool varlen = a.cu_q != nullptr;
-    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
+    const int off = si.len_k - si.len_q;   // bottom-right alignment of the mask
     const int nblk_k = (si.len_k + BN - 1) / BN;
     const long long qb0 = varlen ? (long long)a.ds_qb_base[b] : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows);
 
-    // last key block a 32-row block can see (-1: none, or no stored block:
-    // a block past the table only comes from overlapping, malformed cu_seqlens)
+    // key blocks a 32-row block can see: first_block .. last_block (last < 0:
+    // none, also for a block with no stored dS: a block past the table only
+    // comes from overlapping, malformed cu_seqlens).  The dK/dV kernel has
+    // stored exactly the blocks of each query tile that some row of it sees,
+    // a superset of these.
     auto last_block = [&](int lq) {
         if (lq * kDsRows >= si.len_q || qb0 + lq >= a.ds_qb) return -1;
-        if (!CAUSAL) return nblk_k - 1;
-        const int x = min((lq + 1) * kDsRows, si.len_q) - 1 + off;   // last visible key of the block's last row
-        return x < 0 ? -1 : min(nblk_k - 1, x / BN);
+        if (!MASKED) return nblk_k - 1;
+        // the last key the block's last row sees
+        const int x = min((lq + 1) * kDsRows, si.len_q) - 1 + off + a.win_hi;
+        if (x < 0) return -1;
+        const int y = lq * kDsRows + off - a.win_lo;   // the first key its first row sees
+        if (y > si.len_k - 1) return -1;
+        return min(nblk_k - 1, x / BN);
+    };
+    auto first_block = [&](int lq) {
+        if (!MASKED) return 0;
+        const int y = lq * kDsRows + off - a.win_lo;
+        return y > 0 ? y / BN : 0;
     };
     const int lq0 = m * (BQ / kDsRows) + kGRB * w;   // this wave's first 32-row block within the sequence
-    int n_last_b[kGRB];
+    int n_first_b[kGRB], n_last_b[kGRB];
 #pragma unroll
-    for (int r = 0; r < kGRB; ++r) n_last_b[r] = last_block(lq0 + r);
+    for (int r = 0; r < kGRB; ++r) {
+        n_last_b[r] = last_block(lq0 + r);
+        n_first_b[r] = n_last_b[r] < 0 ? nblk_k : first_block(lq0 + r);
+    }
+    const int n_first_w = min(n_first_b[0], n_first_b[kGRB - 1]);
     const int n_last_w = max(n_last_b[0], n_last_b[kGRB - 1]);
-    int n_last = -1;   // the workgroup's last key block: that of its last block with rows
-    for (int lq = m * (BQ / kDsRows); lq < (m + 1) * (BQ / kDsRows); ++lq) n_last = max(n_last, last_block(lq));
+    // the workgroup's key blocks: n_first .. n_last over its blocks with rows
+    int n_first = nblk_k, n_last = -1;
+    for (int lq = m * (BQ / kDsRows); lq < (m + 1) * (BQ / kDsRows); ++lq) {
+        const int l = last_block(lq);
+        if (l < 0) continue;
+        n_last = max(n_last, l);
+        n_first = min(n_first, first_block(lq));
+    }
 
     const long long kstride = (long long)a.hkv * HD;
     const char* kbytes = reinterpret_cast<const char*>(a.k) + ((long long)si.k0 * kstride + (long long)hkv * HD) * 2;
@@ -117,21 +139,25 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     }
     // stage u holds keys BS u .. BS u + BS - 1 (part hf = u % SPB of key block
     // u / SPB) and the matching parts of every wave's dS blocks (zeros for a
-    // block whose rows see none of these keys); every wave issues OPS copies
-    // per stage, empty ones past the last stage, so that one wait count
-    // serves the whole loop
-    const int n_stage = C::SPB * (n_last + 1);
-    auto issue = [&](int u) {
-        const unsigned base = lds0 + (u % C::NS) * C::STAGE;
+    // block whose rows see none of these keys); the stages run from u_beg
+    // (the first key block's) to u_end, the v-th of them in ring buffer
+    // v % NS.  Every wave issues OPS copies per stage, empty ones past the
+    // last stage, so that one wait count serves the whole loop
+    const int u_beg = C::SPB * n_first;
+    const int u_end = C::SPB * (n_last + 1);
+    const int n_stage = max(u_end - u_beg, 0);
+    auto issue = [&](int v) {
+        const unsigned base = lds0 + (v % C::NS) * C::STAGE;
+        const int u = u_beg + v;
         const int n = u / C::SPB, hf = u % C::SPB;
-        const bool live = u < n_stage;
+        const bool live = v < n_stage;
         const int rows = live ? max(min(si.len_k - u * C::BS, C::BS), 0) : 0;
         const i32x4 kr = rsrc_words(kbytes + (long long)u * C::BS * kstride * 2, (unsigned)(rows * kstride * 2));
 #pragma unroll
         for (int t = 0; t < C::KOPS; ++t) dma_to_lds16(kr, base + (w + t * kGWaves) * 1024, kvoff[t]);
 #pragma unroll
         for (int r = 0; r < kGRB; ++r) {
-            const bool mine = live && n <= n_last_b[r];
+            const bool mine = live && n >= n_first_b[r] && n <= n_last_b[r];
             const i32x4 dr = rsrc_words(dsb + r * blk_stride + (long long)n * kDsBlockBytes + hf * C::DS_PART,
                                         mine ? C::DS_PART : 0);
 #pragma unroll
@@ -161,16 +187,17 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     }
 
 #pragma unroll
-    for (int u = 0; u < C::PD; ++u) issue(u);
-    for (int u = 0; u < n_stage; ++u) {
-        // stage u has landed for this wave (the PD - 1 later ones may still
+    for (int v = 0; v < C::PD; ++v) issue(v);
+    for (int v = 0; v < n_stage; ++v) {
+        // stage v has landed for this wave (the PD - 1 later ones may still
         // fly); after the barrier for all, and every wave is done with stage
-        // u - 1, whose buffer receives stage u + PD
+        // v - 1, whose buffer receives stage v + PD
         g_wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
-        issue(u + C::PD);
-        if (u / C::SPB <= n_last_w) {
-            const char* stage = smem + (u % C::NS) * C::STAGE;
+        issue(v + C::PD);
+        const int kb = (u_beg + v) / C::SPB;   // key block of the stage
+        if (kb >= n_first_w && kb <= n_last_w) {
+            const char* stage = smem + (v % C::NS) * C::STAGE;
             const char* ds = stage + C::K_BYTES + kGRB * w * C::DS_PART;
 #pragma unroll
             for (int sl = 0; sl < C::BS / 16; ++sl) {
@@ -213,7 +240,7 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     }
 }
 
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool MASKED>
 __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     using C = DqgCfg<HD>;
     constexpr int BQ = C::BQ;
@@ -223,9 +250,9 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     // kv-head) on one XCD, so their K reads share an L2
     const int G = a.hq / a.hkv;
     const int nblk_q = (a.seqlen_q + BQ - 1) / BQ;
-    // causal: workgroup p takes query tiles p and nblk_q - 1 - p, whose key
+    // masked: workgroup p takes query tiles p and nblk_q - 1 - p, whose key
     // ranges add up to the same length for every p (balanced work)
-    const int n_pair = CAUSAL ? (nblk_q + 1) / 2 : nblk_q;
+    const int n_pair = MASKED ? (nblk_q + 1) / 2 : nblk_q;
     const int per_group = n_pair * G;
     int grp, slot;
     {
@@ -245,17 +272,17 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const int p = slot % n_pair;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     const int nblk_q_seq = (si.len_q + BQ - 1) / BQ;   // this sequence's query tiles
-    if (CAUSAL) {
+    if (MASKED) {
         // the longer tile first, then its partner (once the first tile's LDS
         // stages are no longer read)
         const int m2 = nblk_q_seq - 1 - p;
         if (m2 > p) {
-            gemm_tile<T, HD, CAUSAL>(m2, a, b, hq, hkv, si, smem);
+            gemm_tile<T, HD, MASKED>(m2, a, b, hq, hkv, si, smem);
             __syncthreads();
         }
-        if (p < nblk_q_seq && p <= m2) gemm_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        if (p < nblk_q_seq && p <= m2) gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     } else {
-        gemm_tile<T, HD, CAUSAL>(p, a, b, hq, hkv, si, smem);
+        gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     }
 }
 
@@ -294,23 +321,23 @@ void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, 
 }
 
 template <class T>
-static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool causal, hipStream_t st) {
+static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool masked, hipStream_t st) {
     const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;
     static_assert(DqgCfg<128>::BQ == DqgCfg<64>::BQ, "one query tiling");
-    const int n_pair = causal ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
+    const int n_pair = masked ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
     const unsigned grid = (unsigned)(n_pair * a.hq * a.batch);
     if (hd == 64) {
-        if (causal) bwd_dq_gemm_kernel<T, 64, true><<<grid, kGThreads, 0, st>>>(a);
+        if (masked) bwd_dq_gemm_kernel<T, 64, true><<<grid, kGThreads, 0, st>>>(a);
         else bwd_dq_gemm_kernel<T, 64, false><<<grid, kGThreads, 0, st>>>(a);
     } else {
-        if (causal) bwd_dq_gemm_kernel<T, 128, true><<<grid, kGThreads, 0, st>>>(a);
+        if (masked) bwd_dq_gemm_kernel<T, 128, true><<<grid, kGThreads, 0, st>>>(a);
         else bwd_dq_gemm_kernel<T, 128, false><<<grid, kGThreads, 0, st>>>(a);
     }
 }
 
-void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
-    if (dtype == ATTN_DTYPE_F16) launch_dq_gemm_t<f16_t>(a, hd, causal, st);
-    else launch_dq_gemm_t<bf16_t>(a, hd, causal, st);
+void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_F16) launch_dq_gemm_t<f16_t>(a, hd, masked, st);
+    else launch_dq_gemm_t<bf16_t>(a, hd, masked, st);
 }
 
 }  // namespace attn

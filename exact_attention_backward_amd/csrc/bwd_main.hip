@@ -201,7 +201,7 @@ __device__ __forceinline__ void wait_vmem_but() {
 // --------------------------------------------------------------------------
 // the kernel
 // --------------------------------------------------------------------------
-template <class T, int HD, bool CAUSAL, bool DQ_ATOMIC>
+template <class T, int HD, bool MASKED, bool DQ_ATOMIC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     using C = BwdCfg<T, HD, DQ_ATOMIC>;
     using op_t = typename Elem<T>::op_t;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    // ---- which key tile: deterministic causal runs dispatch the highest key
+    // ---- which key tile: deterministic masked runs dispatch the highest key
     // tile of a (sequence, kv-head) first, since it reaches every query tile
     // first and so is first in the fixed summation order.
     // Workgroups are dispatched round-robin over the 8 XCDs (each with its
@@ -235,17 +235,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     }
     const int hkv = grp % a.hkv;
     const int b = grp / a.hkv;
-    const int n = (CAUSAL && a.deterministic) ? a.nblk_n - 1 - nb_lin : nb_lin;
+    const int n = (MASKED && a.deterministic) ? a.nblk_n - 1 - nb_lin : nb_lin;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (n * kBN >= si.len_k) return;
     const bool varlen = a.cu_q != nullptr;
     const int G = a.hq / a.hkv;
-    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
-    const int m_end = (si.len_q + BM - 1) / BM;
-    int m_begin = 0;
-    if (CAUSAL) {
-        const int first_row = n * kBN - off;   // first query row that sees key n*kBN
+    const int off = si.len_k - si.len_q;   // bottom-right alignment of the mask
+    int m_begin = 0, m_end = (si.len_q + BM - 1) / BM;
+    if (MASKED) {
+        // query rows that see some key of the tile: from the first row whose
+        // upper bound reaches key n*kBN to the last row whose lower bound
+        // still admits the tile's last key
+        const int first_row = n * kBN - off - a.win_hi;
+        const int last_row = min(n * kBN + kBN, si.len_k) - 1 - off + a.win_lo;
         m_begin = first_row > 0 ? first_row / BM : 0;
+        m_end = last_row < 0 ? 0 : min(last_row, si.len_q - 1) / BM + 1;
     }
     const int n_m = max(m_end - m_begin, 0);
     const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
@@ -330,9 +334,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         const float* llse = reinterpret_cast<const float*>(buf + C::BUF_LSE);
         const float* ldl = reinterpret_cast<const float*>(buf + C::BUF_DL);
 
-        // per-row key limits: key j is visible to row i iff j < lim(i)
+        // per-row key limits: key j is visible to row i iff lo(i) <= j < lim(i)
         const bool edge = !((i0 + BM <= si.len_q) && (n * kBN + kBN <= si.len_k) &&
-                            (!CAUSAL || n * kBN + kBN - 1 <= i0 + off));
+                            (!MASKED || (n * kBN + kBN - 1 <= i0 + off + a.win_hi &&
+                                         n * kBN >= i0 + BM - 1 + off - a.win_lo)));
 
         // ---- stages 1 and 4: S = Q K^T and dP = dO V^T for this wave's keys
         f32x16 s[C::NMB], dp[C::NMB];
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 
         // ---- stages 2 and 5: P = exp2(S s log2e - LSE log2e); dS = P (dP - D).
         // Only edge tiles test visibility (key j is visible to row i iff
-        // j < lim(i)); the branch is uniform.
+        // lo(i) <= j < lim(i)); the branch is uniform.
         auto softmax_grad = [&](auto masked) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
@@ -374,8 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                         float p = __builtin_amdgcn_exp2f(s[mb][v] * scale2 - l2);
                         if constexpr (decltype(masked)::value) {
                             const int i = i0 + r + e;
-                            const int lim = i < si.len_q ? (CAUSAL ? min(si.len_k, i + off + 1) : si.len_k) : 0;
-                            p = j < lim ? p : 0.f;
+                            const int lim =
+                                i < si.len_q ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
+                            const int lo = MASKED ? i + off - a.win_lo : 0;
+                            p = (j < lim && j >= lo) ? p : 0.f;
                         }
                         s[mb][v] = p;
                         dp[mb][v] = p * (dp[mb][v] - dl[e]);
@@ -464,8 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         int* sem = a.sem + ((long long)b * a.hq + hq) * a.nblk_m + m;
         if (a.deterministic) {
             int rank;
-            if (CAUSAL) {
-                const int x = (m + 1) * BM + off;
+            if (MASKED) {
+                // the key tiles that visit query tile m are a contiguous run
+                // ending at the last one whose first key some row of the tile
+                // sees; they come in descending order
+                const int x = (m + 1) * BM + off + a.win_hi;
                 const int last = min(nblk_k - 1, (x + kBN - 1) / kBN - 1);
                 rank = last - n;
             } else {
@@ -563,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 // Masking: a padded query row (past the sequence) has Q = dO = 0 and
 // LSE = D = 0 in LDS, so its P is finite and its P dO and dS terms are zero;
 // a padded key only affects its own dK/dV rows, which are not stored.  Only
-// the causal diagonal tiles need a mask.
+// the tiles a causal or window bound crosses need a mask.
 // --------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
@@ -593,7 +603,7 @@ struct KvCfg {
 };
 
 // All work of one key tile n of sequence b, kv-head hkv (the body of bwd_kv_kernel).
-template <class T, int HD, bool CAUSAL, bool STORE_DS>
+template <class T, int HD, bool MASKED, bool STORE_DS>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
     static_assert(sizeof(T) == 2, "16-bit operand types");
     using C = KvCfg<HD>;
@@ -609,12 +619,16 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     if (n * kBN >= si.len_k) return;
     const bool varlen = a.cu_q != nullptr;
     const int G = a.hq / a.hkv;
-    const int off = si.len_k - si.len_q;   // bottom-right causal alignment
-    const int m_end = (si.len_q + BM - 1) / BM;
-    int m_begin = 0;
-    if (CAUSAL) {
-        const int first_row = n * kBN - off;   // first query row that sees key n*kBN
+    const int off = si.len_k - si.len_q;   // bottom-right alignment of the mask
+    int m_begin = 0, m_end = (si.len_q + BM - 1) / BM;
+    if (MASKED) {
+        // query rows that see some key of the tile: from the first row whose
+        // upper bound reaches key n*kBN to the last row whose lower bound
+        // still admits the tile's last key
+        const int first_row = n * kBN - off - a.win_hi;
+        const int last_row = min(n * kBN + kBN, si.len_k) - 1 - off + a.win_lo;
         m_begin = first_row > 0 ? first_row / BM : 0;
+        m_end = last_row < 0 ? 0 : min(last_row, si.len_q - 1) / BM + 1;
     }
     const int n_m = max(m_end - m_begin, 0);
     const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
@@ -661,7 +675,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     int is_t = 0, is_m = m_begin, is_g = 0;
     int is_so = 0, is_lo = 0;   // byte offsets of the tile from the head's first tile (Q/dO, LSE/D)
     const int full_q = (int)(BM * qstride * (long long)sizeof(T));
-    const int last_rows = si.len_q - (m_end - 1) * BM;   // rows of the last query tile
+    const int last_rows = min(si.len_q - (m_end - 1) * BM, BM);   // rows of the last query tile
     i32x4 rq = rsrc_words(qbytes + q_g0, 0), rdo = rsrc_words(dobytes + q_g0, 0), rs = rsrc_words(sbytes + l_g0, 0);
     const unsigned sdst0 = w == 0 ? lds0 + C::BUF_LSE : w == 1 ? lds0 + C::BUF_DL : lds0 + C::OFF_DUMP;
     const unsigned sstep = w < 2 ? 1u : 0u;   // the empty copies all land in the one dump slot
@@ -714,7 +728,11 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     }
     const float scale2 = a.scale * kLog2e;
     const int j = n * kBN + 32 * pair + l32;   // this lane's key (column of S)
-    const int diag = n * kBN + kBN - 1 - off;  // tiles starting at or below this row are unmasked
+    // a query tile starting at row i0 needs the mask iff i0 < diag_hi (some
+    // key past a row's upper bound) or i0 > diag_lo (some key before a
+    // row's lower bound)
+    const int diag_hi = n * kBN + kBN - 1 - off - a.win_hi;
+    const int diag_lo = n * kBN - off + a.win_lo - BM + 1;
     int cur_m = m_begin;                       // query tile of tile t
     int cur_g = 0;                             // q-head (within the group) of tile t
     int last_m = m_begin, last_g = 0;          // the same for tile t-1
@@ -827,8 +845,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         const int ps = pslots + ((R == 0 ? K : K + 1) & 1) * C::PSLOT + lane * 16;   // slot of tile tt
         op_t opa[C::NIC];
         if constexpr (R == 0) {
-            // ---- P = exp2(S s log2e - LSE log2e), masked on causal diagonal tiles
+            // ---- P = exp2(S s log2e - LSE log2e), masked on the tiles the mask crosses
             const int dj = j - (i0 + off + 4 * h);   // key column relative to this lane's first row
+            const int dj_hi = dj - a.win_hi, dj_lo = dj + a.win_lo;
             auto softmax = [&](auto masked) {
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
@@ -843,7 +862,8 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                             if constexpr (decltype(masked)::value) {
                                 const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
                                 p = __builtin_amdgcn_exp2f(xc[mb][v] * scale2 - l2);
-                                p = dj <= r + e ? p : 0.f;   // j <= i0 + r + 4h + e + off
+                                // i + off - lo <= j <= i + off + hi, i = i0 + r + 4h + e
+                                p = (dj_hi <= r + e && dj_lo >= r + e) ? p : 0.f;
                             } else {
                                 p = __builtin_amdgcn_exp2f(fmaf(xc[mb][v], scale2, -lse[e] * kLog2e));
                             }
@@ -854,7 +874,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                     }
                 }
             };
-            if (CAUSAL && i0 < diag)
+            if (MASKED && (i0 < diag_hi || i0 > diag_lo))
                 softmax(std::true_type{});
             else
                 softmax(std::false_type{});
@@ -1013,14 +1033,15 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-template <class T, int HD, bool CAUSAL, bool STORE_DS>
+template <class T, int HD, bool MASKED, bool STORE_DS>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[KvCfg<HD>::LDS_BYTES];
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
     // a causal mask key tile n is seen by a number of query tiles that falls
     // linearly with n, so workgroup p takes the tiles p and (last - p), which
-    // together always cost about the same.
-    const int per_group = CAUSAL ? (a.nblk_n + 1) / 2 : a.nblk_n;
+    // together always cost about the same (under a window alone the pairs
+    // cost about the same anyway).
+    const int per_group = MASKED ? (a.nblk_n + 1) / 2 : a.nblk_n;
     int grp, p;
     {
         const int groups = a.hkv * a.batch;
@@ -1036,17 +1057,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     const int hkv = grp % a.hkv;
     const int b = grp / a.hkv;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
-    if (CAUSAL) {
+    if (MASKED) {
         const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
         const int n2 = nk - 1 - p;
         // one call site in a loop: a single copy of the (large) tile body
         const int cnt = (p <= n2) + (n2 > p);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
+            kv_tile<T, HD, MASKED, STORE_DS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
-        kv_tile<T, HD, CAUSAL, STORE_DS>(a, b, hkv, p, si, smem);
+        kv_tile<T, HD, MASKED, STORE_DS>(a, b, hkv, p, si, smem);
     }
 }
 
@@ -1057,26 +1078,26 @@ int bwd_block_m(int dtype, int head_dim) {
 }
 
 template <class T, int HD>
-static void launch_bwd_t(const BwdArgs& a, bool causal, int dq_algo, hipStream_t st) {
+static void launch_bwd_t(const BwdArgs& a, bool masked, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
-        // causal: one workgroup per pair of key tiles
-        const unsigned kv_grid = causal ? (unsigned)((a.nblk_n + 1) / 2 * a.hkv * a.batch) : grid;
+        // masked: one workgroup per pair of key tiles
+        const unsigned kv_grid = masked ? (unsigned)((a.nblk_n + 1) / 2 * a.hkv * a.batch) : grid;
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE) {
-            if (causal) bwd_kv_kernel<T, HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
+            if (masked) bwd_kv_kernel<T, HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
             else bwd_kv_kernel<T, HD, false, false><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
         if (dq_algo == ATTN_DQ_STORED_DS) {
-            if (causal) bwd_kv_kernel<T, HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
+            if (masked) bwd_kv_kernel<T, HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
             else bwd_kv_kernel<T, HD, false, true><<<kv_grid, kKvThreads, 0, st>>>(a);
             return;
         }
     }
     const bool dq_atomic = dq_algo == ATTN_DQ_ATOMIC;
-    if (causal) {
+    if (masked) {
         if (dq_atomic) bwd_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
         else bwd_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
     } else {
@@ -1085,16 +1106,16 @@ static void launch_bwd_t(const BwdArgs& a, bool causal, int dq_algo, hipStream_t
     }
 }
 
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, hipStream_t st) {
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, causal, dq_algo, st);
-        else launch_bwd_t<bf16_t, 128>(a, causal, dq_algo, st);
+        if (hd == 64) launch_bwd_t<bf16_t, 64>(a, masked, dq_algo, st);
+        else launch_bwd_t<bf16_t, 128>(a, masked, dq_algo, st);
     } else if (dtype == ATTN_DTYPE_F16) {
-        if (hd == 64) launch_bwd_t<f16_t, 64>(a, causal, dq_algo, st);
-        else launch_bwd_t<f16_t, 128>(a, causal, dq_algo, st);
+        if (hd == 64) launch_bwd_t<f16_t, 64>(a, masked, dq_algo, st);
+        else launch_bwd_t<f16_t, 128>(a, masked, dq_algo, st);
     } else {
-        if (hd == 64) launch_bwd_t<float, 64>(a, causal, dq_algo, st);
-        else launch_bwd_t<float, 128>(a, causal, dq_algo, st);
+        if (hd == 64) launch_bwd_t<float, 64>(a, masked, dq_algo, st);
+        else launch_bwd_t<float, 128>(a, masked, dq_algo, st);
     }
 }
 

@@ -23,7 +23,7 @@ __device__ __forceinline__ long long lse_index(bool varlen, long long r, int h, 
 // forward: one thread per query row, K/V tiles of 32 keys staged in LDS,
 // online softmax in base 2.  Not performance-tracked.
 // ---------------------------------------------------------------------------
-template <class T, int HD, bool CAUSAL>
+template <class T, int HD, bool MASKED>
 __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     constexpr int BQ = 128, BK = 32;
     __shared__ float ks[BK][HD];
@@ -47,9 +47,16 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
         o[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    int kend = si.len_k;
-    if (CAUSAL) kend = min(kend, min(qb * BQ + BQ, si.len_q) - 1 + off + 1);
-    for (int kt = 0; kt < kend; kt += BK) {
+    // keys any row of the block can see: with a mask, from the first row's
+    // lower bound (aligned down to a tile) to the last row's upper bound
+    const int whi = a.win_hi, wlo = a.win_lo;
+    int kbeg = 0, kend = si.len_k;
+    if (MASKED) {
+        kend = min(kend, min(qb * BQ + BQ, si.len_q) - 1 + off + a.win_hi + 1);
+        const int first = qb * BQ + off - a.win_lo;
+        kbeg = first > 0 ? first / BK * BK : 0;
+    }
+    for (int kt = kbeg; kt < kend; kt += BK) {
         __syncthreads();
         for (int e = threadIdx.x; e < BK * HD; e += blockDim.x) {
             const int jj = e / HD, d = e % HD, j = kt + jj;
@@ -63,7 +70,8 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int jj = 0; jj < BK; ++jj) {
             const int j = kt + jj;
-            const bool vis = row_ok && j < si.len_k && (!CAUSAL || j <= i + off);
+            const int dj = j - i - off;   // i + off - lo <= j <= i + off + hi
+            const bool vis = row_ok && j < si.len_k && (!MASKED || (dj <= whi && dj >= -wlo));
             float acc = 0.f;
 #pragma unroll
             for (int d = 0; d < HD; ++d) acc = fmaf(q[d], ks[jj][d], acc);
@@ -190,24 +198,24 @@ __global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 template <class T, int HD>
-static void launch_fwd_t(const FwdArgs& a, bool causal, hipStream_t st) {
+static void launch_fwd_t(const FwdArgs& a, bool masked, hipStream_t st) {
     dim3 grid((a.seqlen_q + 127) / 128, a.hq, a.batch);
-    if (causal)
+    if (masked)
         fwd_kernel<T, HD, true><<<grid, 128, 0, st>>>(a);
     else
         fwd_kernel<T, HD, false><<<grid, 128, 0, st>>>(a);
 }
 
-void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st) {
+void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) launch_fwd_t<bf16_t, 64>(a, causal, st);
-        else launch_fwd_t<bf16_t, 128>(a, causal, st);
+        if (hd == 64) launch_fwd_t<bf16_t, 64>(a, masked, st);
+        else launch_fwd_t<bf16_t, 128>(a, masked, st);
     } else if (dtype == ATTN_DTYPE_F16) {
-        if (hd == 64) launch_fwd_t<f16_t, 64>(a, causal, st);
-        else launch_fwd_t<f16_t, 128>(a, causal, st);
+        if (hd == 64) launch_fwd_t<f16_t, 64>(a, masked, st);
+        else launch_fwd_t<f16_t, 128>(a, masked, st);
     } else {
-        if (hd == 64) launch_fwd_t<float, 64>(a, causal, st);
-        else launch_fwd_t<float, 128>(a, causal, st);
+        if (hd == 64) launch_fwd_t<float, 64>(a, masked, st);
+        else launch_fwd_t<float, 128>(a, masked, st);
     }
 }
 

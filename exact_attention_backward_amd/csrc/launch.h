@@ -18,6 +18,7 @@ struct FwdArgs {
     const int32_t* used_k;
     int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
     float scale;
+    int win_lo, win_hi;      // visibility: i + off - win_lo <= j <= i + off + win_hi
 };
 
 struct PreArgs {
@@ -61,6 +62,11 @@ struct BwdArgs {
     const int32_t* used_q;   // varlen: per-sequence used lengths, or null
     const int32_t* used_k;
     int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
+    // visibility of key j to query i (off = len_k - len_q, bottom-right
+    // aligned): i + off - win_lo <= j <= i + off + win_hi; kNoWindow on an
+    // unbounded side.  Kernels instantiated with MASKED = false (no bound at
+    // all) ignore them.
+    int win_lo, win_hi;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
@@ -85,21 +91,24 @@ constexpr int kDsKeys = 128;
 constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
 __host__ __device__ constexpr int ds_chunk(int g, int l) { return g * 64 + (l ^ ((l >> 5) << 2)); }
 
+// An unbounded side of the visibility window (far beyond any sequence length).
+constexpr int kNoWindow = 1 << 29;
+
 // Query rows per tile of the main kernel (keys per tile are fixed at 128).
 int bwd_block_m(int dtype, int head_dim);
 constexpr int kBwdBlockN = 128;
 
-void launch_fwd(const FwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
-void launch_bwd(const BwdArgs& a, int dtype, int hd, bool causal, int dq_algo, hipStream_t st);
+void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, hipStream_t st);
 // stored-dS mode: dQ = dS K from the stored blocks (16-bit types), and the
 // per-sequence block table of varlen problems
-void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, int* out, hipStream_t st);
 // query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
-void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool causal, hipStream_t st);
+void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 int bwd_dq_block_m();
 
 // ---------------------------------------------------------------------------

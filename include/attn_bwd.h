@@ -46,6 +46,13 @@
  *    (sequence, head) block: key j is visible to query i iff
  *    j <= i + (len_k - len_q).  A query row that sees no key has LSE = -inf,
  *    O = 0, and gets dQ = 0.
+ *  - Local (sliding-window) masks, with local = 1, use the same diagonal:
+ *    key j is visible to query i iff
+ *        i + off - window_left <= j <= i + off + window_right,
+ *    off = len_k - len_q, a side of -1 being unbounded, intersected with the
+ *    causal bound when causal = 1.  (The composable-kernel pipeline page
+ *    leaves the mask's rule to its mask object; this is the reading taken.)
+ *    local = 0 (a zero-initialised shape) means no window.
  *  - GQA: Hq must be a multiple of Hkv; q-head h uses kv-head h / (Hq / Hkv)
  *    (contiguous groups).  dK and dV of a kv-head are the sums over its
  *    q-heads.
@@ -67,7 +74,8 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL (the workspace included) */
-    ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, varlen without both
+    ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, causal/local not 0 or 1,
+                                  window sizes below -1, varlen without both
                                   cu_seqlens, workspace too small, more than 2^27
                                   (row, head) pairs in Q or K, 2 GiB or more of Q
                                   in one sequence (seqlen_q x Hq x D elements), ... */
@@ -126,6 +134,9 @@ typedef struct attn_shape {
     int32_t dq_algo;         /* attn_dq_algo_t: how attn_bwd accumulates dQ */
     const int32_t* seqused_q;     /* varlen only: device [batch] used query lengths, or NULL */
     const int32_t* seqused_k;     /* varlen only: device [batch] used key lengths, or NULL */
+    int32_t local;           /* 1: local (sliding-window) mask, see window_left/right */
+    int32_t window_left;     /* local: keys at most this many before the diagonal, -1 = any */
+    int32_t window_right;    /* local: keys at most this many after the diagonal, -1 = any */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -2,6 +2,7 @@
 header declares, and rejects invalid arguments before any HIP call."""
 
 import ctypes
+from pathlib import Path
 import os
 import re
 
@@ -77,6 +78,9 @@ def test_workspace_size_formula():
     (dict(softmax_scale=float("nan")), L.ATTN_ERR_BAD_SHAPE),
     (dict(batch=1, seqlen_q=(1 << 23) + 1, num_heads_q=16, num_heads_kv=16), L.ATTN_ERR_BAD_SHAPE),
     (dict(dq_algo=5), L.ATTN_ERR_UNSUPPORTED),
+    (dict(local=2), L.ATTN_ERR_BAD_SHAPE),
+    (dict(local=1, window_left=-2, window_right=3), L.ATTN_ERR_BAD_SHAPE),
+    (dict(local=1, window_left=3, window_right=-7), L.ATTN_ERR_BAD_SHAPE),
     (dict(dq_algo=L.ATTN_DQ_STORED_DS, dtype=L.ATTN_DTYPE_F32), L.ATTN_ERR_UNSUPPORTED),
 ])
 def test_invalid_shapes_rejected(kw, status):
@@ -99,6 +103,35 @@ def test_seqused_needs_varlen_and_alignment():
     s = shape(seqused_k=0x3000)
     rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
     assert rc == L.ATTN_ERR_BAD_SHAPE
+
+
+def test_window_sizes_accepted():
+    base = ws_bytes(shape())
+    for left, right in [(-1, -1), (0, 0), (5, -1), (-1, 7), (1 << 30, (1 << 31) - 1)]:
+        for causal in (0, 1):
+            assert ws_bytes(shape(local=1, window_left=left, window_right=right, causal=causal)) == base
+    # the window fields are ignored without local
+    assert ws_bytes(shape(local=0, window_left=-9, window_right=-9)) == base
+
+
+def test_shape_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of attn_shape_t has the C layout (compiled from the header)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in L.AttnShape._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "attn_bwd.h"\nint main(void) {\n'
+                   '    printf("%zu\\n", sizeof(attn_shape_t));\n'
+                   + "".join(f'    printf("%zu\\n", offsetof(attn_shape_t, {f}));\n' for f in fields)
+                   + "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    inc = Path(__file__).resolve().parents[1] / "include"
+    subprocess.run(["gcc", "-std=c99", "-I", str(inc), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(L.AttnShape)
+    assert out[1:] == [getattr(L.AttnShape, f).offset for f in fields]
 
 
 def test_varlen_needs_both_offsets_and_totals():
