@@ -31,6 +31,13 @@ Readings taken where the pages are silent (each is listed in the design notes):
   to any gradient.  The same page maps LSE = -inf to 0 (``get_validated_lse``)
   so that such rows give P = exp(-inf) = 0.
 * D is computed from the O it is given (``D`` is only consumed on the pages).
+* ALiBi: the composable-kernel page applies a position encoding to each
+  scaled logit from its (row, column) position only (``position_encoding.
+  update`` after ``s_acc *= scale``, before the exponential), without its
+  formula.  Reading taken: the linear-bias definition on the same
+  bottom-right-aligned diagonal as the masks, ``-slope_h * |i + off - j|``
+  (off = Sk - Sq) added to ``s * q_i . k_j`` in natural-log units, one slope
+  per q-head.
 * GQA groups are contiguous: q-head h reads kv-head ``h // (Hq // Hkv)``, as in
   the head mapping of ``CollectiveEpilogueBwdGQA::store`` on the
   FlashAttention-3 page "flash-attention/hopper/epilogue_bwd.hpp"; dK and dV of
@@ -47,6 +54,7 @@ import numpy as np
 
 __all__ = [
     "visible",
+    "alibi_bias",
     "head_forward",
     "head_backward",
     "forward",
@@ -94,20 +102,37 @@ def visible(sq, sk, causal, window=None):
     return ok
 
 
-def head_forward(q, k, v, scale, causal, window=None):
+def alibi_bias(sq, sk, slope):
+    """[sq, sk] float64 ALiBi bias of one head: ``-slope * |i + (sk - sq) - j|``
+    (zero on the bottom-right-aligned diagonal, falling linearly with the
+    distance from it on both sides)."""
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return -float(slope) * np.abs(i + (sk - sq) - j).astype(np.float64)
+
+
+def _logits(q, k, scale, alibi):
+    """Stage 1: s * Q K^T, plus the ALiBi bias when a slope is given."""
+    s = scale * (q @ k.T)
+    if alibi is not None:
+        s = s + alibi_bias(q.shape[0], k.shape[0], alibi)
+    return s
+
+
+def head_forward(q, k, v, scale, causal, window=None, alibi=None):
     """Softmax attention for one head.
 
     q [sq, d], k [sk, d], v [sk, d] -> (o [sq, d], lse [sq]), float64.
-    ``lse_i = log(sum_j exp(s * q_i . k_j))`` over the visible keys,
-    ``o_i = sum_j softmax_ij v_j``.  Rows with no visible key give
-    lse = -inf and o = 0.
+    ``lse_i = log(sum_j exp(s * q_i . k_j + b_ij))`` over the visible keys
+    (b the ALiBi bias of slope ``alibi``, or 0), ``o_i = sum_j softmax_ij
+    v_j``.  Rows with no visible key give lse = -inf and o = 0.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     sq, sk = q.shape[0], k.shape[0]
     ok = visible(sq, sk, causal, window)
-    s = scale * (q @ k.T)
+    s = _logits(q, k, scale, alibi)
     has_key = ok.any(axis=1)
     # row maximum over visible keys (0 for empty rows, never used)
     row_max = np.max(np.where(ok, s, -np.inf), axis=1, initial=-np.inf)
@@ -122,20 +147,21 @@ def head_forward(q, k, v, scale, causal, window=None):
     return o, lse
 
 
-def _probabilities(q, k, lse, scale, causal, window=None):
-    """P recomputed from the saved LSE (stages 1-2): exp(s q_i.k_j - lse_i)."""
+def _probabilities(q, k, lse, scale, causal, window=None, alibi=None):
+    """P recomputed from the saved LSE (stages 1-2): exp(s q_i.k_j + b_ij - lse_i)."""
     sq, sk = q.shape[0], k.shape[0]
     ok = visible(sq, sk, causal, window) & np.isfinite(lse)[:, None]
-    s = scale * (q @ k.T)
+    s = _logits(q, k, scale, alibi)
     safe_lse = np.where(np.isfinite(lse), lse, 0.0)
     return np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))
 
 
-def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None):
+def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None, alibi=None):
     """Gradient of attention for one head, given O and LSE as saved by a forward.
 
     Returns (dq [sq, d], dk [sk, d], dv [sk, d]) in float64; with
-    ``details=True`` also a dict holding P, dP, dS and D.
+    ``details=True`` also a dict holding P, dP, dS and D.  The ALiBi bias
+    only enters through P (it does not depend on Q or K).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -143,7 +169,7 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None
     o = np.asarray(o, np.float64)
     do = np.asarray(do, np.float64)
     lse = np.asarray(lse, np.float64)
-    p = _probabilities(q, k, lse, scale, causal, window)  # stages 1-2
+    p = _probabilities(q, k, lse, scale, causal, window, alibi)  # stages 1-2
     delta = np.sum(do * o, axis=1)                        # D = rowsum(dO * O)
     dp = do @ v.T                                         # stage 4
     dv = p.T @ do                                         # stage 3
@@ -217,11 +243,16 @@ def _lse_view(lse, varlen, nseq, hq, sq):
     return np.transpose(lse, (1, 0, 2)).reshape(hq, nseq * sq)
 
 
+def _slope(alibi_slopes, h):
+    return None if alibi_slopes is None else float(np.asarray(alibi_slopes, np.float64)[h])
+
+
 def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None,
-                  seqused_q=None, seqused_k=None, window=None):
+                  seqused_q=None, seqused_k=None, window=None, alibi_slopes=None):
     """Forward for the q-heads of one kv-head group of one sequence.
 
-    Returns {q_head: (o [len_q, d], lse [len_q])}.
+    Returns {q_head: (o [len_q, d], lse [len_q])}.  ``alibi_slopes``: one
+    slope per q-head, or None.
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
@@ -229,12 +260,14 @@ def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_se
     qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
     out = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
-        out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal, window)
+        out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal, window,
+                              _slope(alibi_slopes, h))
     return out
 
 
 def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
-                   cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None, window=None):
+                   cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None, window=None,
+                   alibi_slopes=None):
     """Backward for one kv-head group of one sequence.
 
     Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
@@ -252,7 +285,8 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
     dq = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
         dqh, dkh, dvh = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
-                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, window=window)
+                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, window=window,
+                                      alibi=_slope(alibi_slopes, h))
         dq[h] = dqh
         dk += dkh
         dv += dvh
@@ -260,7 +294,7 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None,
-            window=None):
+            window=None, alibi_slopes=None):
     """Full forward.  Returns (o, lse) in the layouts given in the module doc
     (rows past a sequence's used length are left at zero)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -269,8 +303,8 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
     lse = np.zeros((hq, qf.shape[0]), np.float64)
     for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
-            for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g,
-                                             cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, window).items():
+            for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
+                                             seqused_q, seqused_k, window, alibi_slopes).items():
                 o[q0:q1, h] = oh
                 lse[h, q0:q1] = lh
     if varlen:
@@ -279,7 +313,7 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
 
 
 def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-             seqused_q=None, seqused_k=None, window=None):
+             seqused_q=None, seqused_k=None, window=None, alibi_slopes=None):
     """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64);
     rows past a sequence's used length are left at zero."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -289,8 +323,8 @@ def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k
     dv = np.zeros(kf.shape, np.float64)
     for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
-            dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g,
-                                           cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, window)
+            dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
+                                           seqused_q, seqused_k, window, alibi_slopes)
             for h, x in dqg.items():
                 dq[q0:q1, h] = x
             dk[k0:k1, g] = dkg

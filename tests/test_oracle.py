@@ -248,6 +248,229 @@ def test_window_varlen_equals_per_sequence():
 
 
 # --------------------------------------------------------------------------
+# ALiBi: -slope * |i + off - j| added to the scaled logits
+# --------------------------------------------------------------------------
+
+def brute_alibi_forward(q, k, v, scale, causal, slope):
+    """Scalar loops: logit_ij = scale q_i.k_j - slope |i + (sk - sq) - j| over
+    the visible keys, softmax with math.exp."""
+    sq, sk, d = len(q), len(k), len(q[0])
+    o, lse = [], []
+    for i in range(sq):
+        vis = [j for j in range(sk) if (not causal) or j <= i + (sk - sq)]
+        if not vis:
+            o.append([0.0] * d)
+            lse.append(-math.inf)
+            continue
+        s = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) - slope * abs(i + (sk - sq) - j) for j in vis}
+        m = max(s.values())
+        lse.append(m + math.log(sum(math.exp(s[j] - m) for j in vis)))
+        o.append([sum(math.exp(s[j] - lse[-1]) * v[j][t] for j in vis) for t in range(d)])
+    return np.array(o), np.array(lse)
+
+
+ALIBI_LOOP_CASES = [(5, 5, False, 0.5), (5, 5, True, 0.25), (4, 7, True, 1.0), (7, 4, True, 0.125),
+                    (3, 6, False, 2.0), (6, 3, False, 0.75)]
+
+
+def _alibi_scalar_loop_pin(sq, sk, causal, slope):
+    rng = np.random.default_rng(40 + sq * 7 + sk)
+    q, k, v = rand(rng, sq, 3), rand(rng, sk, 3), rand(rng, sk, 3)
+    o, lse = A.head_forward(q, k, v, 0.7, causal, alibi=slope)
+    bo, blse = brute_alibi_forward(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, slope)
+    fin = np.isfinite(blse)
+    return (np.array_equal(np.isfinite(lse), fin) and np.max(np.abs(lse[fin] - blse[fin])) <= 1e-12
+            and np.max(np.abs(o - bo)) <= 1e-12)
+
+
+@pytest.mark.parametrize("sq,sk,causal,slope", ALIBI_LOOP_CASES)
+def test_alibi_forward_matches_scalar_loops(sq, sk, causal, slope):
+    assert _alibi_scalar_loop_pin(sq, sk, causal, slope)
+
+
+def _alibi_zero_query_pin(sq, sk, causal, slope):
+    """Q = 0: the logits are the bias alone, so P_ij = r^|c - j| / Z_i with
+    r = exp(-slope), c = i + off the diagonal key, and Z_i the sum of two
+    geometric series (keys left and right of c).  dK = s dS^T Q = 0."""
+    rng = np.random.default_rng(5)
+    q = np.zeros((sq, 4))
+    k, v, do = rand(rng, sk, 4), rand(rng, sk, 4), rand(rng, sq, 4)
+    o, lse = A.head_forward(q, k, v, 0.9, causal, alibi=slope)
+    r = math.exp(-slope)
+    ok = True
+    for i in range(sq):
+        c = i + sk - sq
+        lo_key, hi_key = 0, (min(c, sk - 1) if causal else sk - 1)
+        if hi_key < lo_key:
+            ok &= lse[i] == -math.inf and np.all(o[i] == 0)
+            continue
+        def run(d0, d1):   # sum of r^d for d = d0 .. d1
+            return 0.0 if d1 < d0 else (r ** d0 - r ** (d1 + 1)) / (1 - r)
+        # keys at or left of c have distances c - j, those right of it j - c
+        l0, l1 = lo_key, min(hi_key, c)
+        r0, r1 = max(lo_key, c + 1), hi_key
+        z = run(c - l1, c - l0) + run(r0 - c, r1 - c)
+        ok &= abs(lse[i] - math.log(z)) <= 1e-12
+        w = np.array([r ** abs(c - j) / z if lo_key <= j <= hi_key else 0.0 for j in range(sk)])
+        ok &= np.max(np.abs(o[i] - w @ v)) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.9, causal, alibi=slope)
+    ok &= np.all(dk == 0.0)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("sq,sk,causal,slope", [(6, 6, False, 0.3), (6, 6, True, 0.7), (4, 9, False, 1.5),
+                                                (9, 4, True, 0.2), (9, 4, False, 0.9)])
+def test_alibi_zero_query_closed_form(sq, sk, causal, slope):
+    assert _alibi_zero_query_pin(sq, sk, causal, slope)
+
+
+def _alibi_augmented_pin(sq, sk, slope, right_side):
+    """On one side of the diagonal |i + off - j| is linear in j, so the bias
+    splits into a row constant (cancels in the softmax, shifts LSE) and a
+    column term that one extra head dimension carries: [q, 1] . [k, +-slope
+    j / s].  The plain path (no ALiBi code) then gives the same O, dQ, dK,
+    dV, and LSE shifted by -+slope (i + off).  Left side: causal; right side:
+    the window (0, -1)."""
+    rng = np.random.default_rng(8)
+    d, sc = 5, 0.6
+    q, k, v, do = rand(rng, sq, d), rand(rng, sk, d), rand(rng, sk, d), rand(rng, sq, d)
+    causal, window = (False, (0, -1)) if right_side else (True, None)
+    sign = -1.0 if right_side else 1.0
+    jcol = sign * slope * np.arange(sk)[:, None] / sc
+    qa = np.concatenate([q, np.ones((sq, 1))], axis=1)
+    ka = np.concatenate([k, jcol], axis=1)
+    o, lse = A.head_forward(q, k, v, sc, causal, window=window, alibi=slope)
+    oa, lsea = A.head_forward(qa, ka, v, sc, causal, window=window)
+    c = np.arange(sq) + (sk - sq)
+    fin = np.isfinite(lsea)
+    ok = np.array_equal(np.isfinite(lse), fin)
+    ok &= np.max(np.abs(o - oa)) <= 1e-12
+    ok &= np.max(np.abs(lse[fin] - (lsea[fin] - sign * slope * c[fin])), initial=0) <= 1e-11
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, sc, causal, window=window, alibi=slope)
+    dqa, dka, dva = A.head_backward(qa, ka, v, oa, do, lsea, sc, causal, window=window)
+    ok &= rel_err(dq, dqa[:, :d]) <= 1e-12 and rel_err(dk, dka[:, :d]) <= 1e-12 and rel_err(dv, dva) <= 1e-12
+    return bool(ok)
+
+
+@pytest.mark.parametrize("sq,sk,slope,right_side", [(9, 9, 0.4, False), (6, 11, 1.1, False), (11, 6, 0.3, False),
+                                                    (9, 9, 0.4, True), (6, 11, 0.8, True), (11, 6, 0.5, True)])
+def test_alibi_augmented_dimension_equivalence(sq, sk, slope, right_side):
+    assert _alibi_augmented_pin(sq, sk, slope, right_side)
+
+
+def test_alibi_zero_slope_is_plain_attention():
+    rng = np.random.default_rng(6)
+    q, k, v, do = rand(rng, 7, 4), rand(rng, 9, 4), rand(rng, 9, 4), rand(rng, 7, 4)
+    for causal in (False, True):
+        o, lse = A.head_forward(q, k, v, 0.5, causal)
+        oz, lsez = A.head_forward(q, k, v, 0.5, causal, alibi=0.0)
+        assert np.array_equal(o, oz) and np.array_equal(lse, lsez)
+        g = A.head_backward(q, k, v, o, do, lse, 0.5, causal)
+        gz = A.head_backward(q, k, v, o, do, lse, 0.5, causal, alibi=0.0)
+        for a, b in zip(g, gz):
+            assert np.array_equal(a, b)
+
+
+def _fd_alibi(q, k, v, do, scale, causal, slopes, cu=None, window=None):
+    o, lse = oracle.forward(q, k, v, scale, causal, cu, cu, window=window, alibi_slopes=slopes)
+    dq, dk, dv = oracle.backward(q, k, v, o, do, lse, scale, causal, cu, cu, window=window, alibi_slopes=slopes)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * oracle.forward(qq, kk, vv, scale, causal, cu, cu, window=window,
+                                                alibi_slopes=slopes)[0]))
+
+    h = 1e-5
+    for pos, g in enumerate((dq, dk, dv)):
+        base = [q, k, v]
+        fd = np.zeros_like(base[pos])
+        for idx in np.ndindex(fd.shape):
+            xp, xm = base[pos].copy(), base[pos].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(base), list(base)
+            ap[pos], am[pos] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert rel_err(g, fd) <= 1e-6
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (False, (3, 2))])
+def test_alibi_backward_finite_differences(causal, window):
+    """Dense GQA (4 q-heads on 2 kv-heads, each q-head its own slope)."""
+    rng = np.random.default_rng(21)
+    q, k, v, do = rand(rng, 1, 6, 4, 3), rand(rng, 1, 7, 2, 3), rand(rng, 1, 7, 2, 3), rand(rng, 1, 6, 4, 3)
+    _fd_alibi(q, k, v, do, 0.5, causal, np.array([0.5, 0.25, 1.0, 0.125]), window=window)
+
+
+def test_alibi_backward_finite_differences_varlen():
+    rng = np.random.default_rng(22)
+    cu = np.array([0, 3, 8], np.int32)
+    q, k, v, do = rand(rng, 8, 2, 3), rand(rng, 8, 2, 3), rand(rng, 8, 2, 3), rand(rng, 8, 2, 3)
+    _fd_alibi(q, k, v, do, 0.6, True, np.array([0.3, 0.9]), cu=cu)
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(30, 30, False), (20, 37, True), (37, 20, False)])
+def test_alibi_backward_matches_torch_autograd_float64(sq, sk, causal):
+    """The bias as an explicit float matrix added to the logits in torch float64 autograd."""
+    import torch
+    rng = np.random.default_rng(13)
+    slope = 0.37
+    q, k, v, do = rand(rng, sq, 8), rand(rng, sk, 8), rand(rng, sk, 8), rand(rng, sq, 8)
+    i = torch.arange(sq, dtype=torch.float64)[:, None]
+    j = torch.arange(sk, dtype=torch.float64)[None, :]
+    bias = -slope * torch.abs(i + (sk - sq) - j)
+    mask = (j <= i + (sk - sq)) if causal else torch.ones(sq, sk, dtype=torch.bool)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = (0.3 * tq @ tk.T + bias).masked_fill(~mask, float("-inf"))
+    rows = mask.any(dim=1)
+    pr = torch.where(rows[:, None], torch.softmax(torch.where(rows[:, None], s, torch.zeros_like(s)), dim=-1),
+                     torch.zeros_like(s))
+    out = pr @ tv
+    out.backward(torch.from_numpy(do))
+    o, lse = A.head_forward(q, k, v, 0.3, causal, alibi=slope)
+    assert np.max(np.abs(o - out.detach().numpy())) <= 1e-12
+    dq, dk, dv = A.head_backward(q, k, v, o, do, lse, 0.3, causal, alibi=slope)
+    assert rel_err(dq, tq.grad.numpy()) <= 1e-12
+    assert rel_err(dk, tk.grad.numpy()) <= 1e-12
+    assert rel_err(dv, tv.grad.numpy()) <= 1e-12
+
+
+def _alibi_sign_flipped(sq, sk, slope):
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return float(slope) * np.abs(i + (sk - sq) - j).astype(np.float64)
+
+
+def _alibi_top_left(sq, sk, slope):
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return -float(slope) * np.abs(i - j).astype(np.float64)
+
+
+def _alibi_no_abs(sq, sk, slope):
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return -float(slope) * (i + (sk - sq) - j).astype(np.float64)
+
+
+def _alibi_transposed_distance(sq, sk, slope):
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    return -float(slope) * np.abs(j + (sk - sq) - i).astype(np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_alibi_sign_flipped, _alibi_top_left, _alibi_no_abs, _alibi_transposed_distance],
+                         ids=lambda f: f.__name__)
+def test_planted_alibi_mistakes_are_caught(mutant, monkeypatch):
+    """Each plausible slip in the bias fails at least one of the ALiBi pins."""
+    monkeypatch.setattr(A, "alibi_bias", mutant)
+    caught = not all(_alibi_scalar_loop_pin(*c) for c in ALIBI_LOOP_CASES)
+    caught |= not _alibi_zero_query_pin(4, 9, False, 1.5)
+    caught |= not _alibi_augmented_pin(6, 11, 1.1, False)
+    caught |= not _alibi_augmented_pin(6, 11, 0.8, True)
+    assert caught, mutant.__name__
+
+
+# --------------------------------------------------------------------------
 # backward: independent library autograd (torch, float64)
 # --------------------------------------------------------------------------
 
