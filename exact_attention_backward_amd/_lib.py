@@ -59,6 +59,7 @@ class AttnShape(ctypes.Structure):
         ("local", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 

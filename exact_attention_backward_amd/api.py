@@ -46,7 +46,7 @@ DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_
 
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-               window=None):
+               window=None, alibi_slopes=None):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
     "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
@@ -54,7 +54,8 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     seqused_q / seqused_k (varlen only): int32 device tensors of per-sequence
     used lengths.  window = (left, right) selects the local mask: query i sees
     key j iff i + off - left <= j <= i + off + right (off = len_k - len_q, -1
-    for an unbounded side), intersected with the causal bound when causal."""
+    for an unbounded side), intersected with the causal bound when causal.
+    alibi_slopes: fp32 device tensor [Hq]; the logits get -slope_h |i + off - j|."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -78,6 +79,10 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     if window is not None:
         s.local = 1
         s.window_left, s.window_right = int(window[0]), int(window[1])
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != q.shape[-2]:
+            raise ValueError("alibi_slopes must be a float32 tensor with one slope per q-head")
+        s.alibi_slopes = alibi_slopes.data_ptr()
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
@@ -117,11 +122,11 @@ def _lse_shape(shape, varlen):
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            seqused_q=None, seqused_k=None, out=None, window=None):
+            seqused_q=None, seqused_k=None, out=None, window=None, alibi_slopes=None):
     """Plain forward: returns (o, lse).  ``out`` = (o, lse) writes into given
     buffers (rows past the used lengths keep their contents)."""
     shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                       seqused_q=seqused_q, seqused_k=seqused_k, window=window)
+                       seqused_q=seqused_q, seqused_k=seqused_k, window=window, alibi_slopes=alibi_slopes)
     if out is not None:
         o, lse = out
     else:
@@ -140,10 +145,10 @@ class BackwardPlan:
 
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                  max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-                 window=None):
+                 window=None, alibi_slopes=None):
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
-                                max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window)
-        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)
+                                max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window, alibi_slopes)
+        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
         if nbytes == 0:
@@ -179,10 +184,10 @@ class BackwardPlan:
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-             window=None):
+             window=None, alibi_slopes=None):
     """Full backward: returns (dq, dk, dv)."""
     plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                        dq_algo, seqused_q, seqused_k, window)
+                        dq_algo, seqused_q, seqused_k, window, alibi_slopes)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     plan.run(q, k, v, o, do, lse, dq, dk, dv)
     return dq, dk, dv

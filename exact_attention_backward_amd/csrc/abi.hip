@@ -33,7 +33,8 @@ int validate_shape(const attn_shape_t* s) {
     } else if (s->seqused_q != nullptr || s->seqused_k != nullptr) {
         return ATTN_ERR_BAD_SHAPE;   // used lengths are a varlen feature
     }
-    if ((reinterpret_cast<uintptr_t>(s->seqused_q) & 3u) || (reinterpret_cast<uintptr_t>(s->seqused_k) & 3u))
+    if ((reinterpret_cast<uintptr_t>(s->seqused_q) & 3u) || (reinterpret_cast<uintptr_t>(s->seqused_k) & 3u) ||
+        (reinterpret_cast<uintptr_t>(s->alibi_slopes) & 3u))
         return ATTN_ERR_MISALIGNED;
     if (!(s->softmax_scale == s->softmax_scale)) return ATTN_ERR_BAD_SHAPE;   // NaN scale
     if (s->causal != 0 && s->causal != 1) return ATTN_ERR_BAD_SHAPE;
@@ -143,6 +144,7 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     a.win_lo = win_lo(s);
     a.win_hi = win_hi(s);
+    a.alibi = s->alibi_slopes;
     launch_fwd(a, s->dtype, s->head_dim, masked(s), reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
@@ -212,6 +214,7 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.deterministic = s->deterministic;
     a.win_lo = win_lo(s);
     a.win_hi = win_hi(s);
+    a.alibi = s->alibi_slopes;
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;

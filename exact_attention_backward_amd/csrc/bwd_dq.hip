@@ -147,7 +147,7 @@ __device__ __forceinline__ void dq_wait_vmem_but(int n) {
 }  // namespace
 
 // dQ rows of query tile m (128 rows) of q-head hq in sequence b.
-template <class T, int HD, bool MASKED>
+template <class T, int HD, bool MASKED, bool ALIBI>
 __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                         char* smem) {
     using C = DqCfg<T, HD>;
@@ -212,6 +212,8 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         dl = a.delta[row0 + i];
     }
     const float scale2 = a.scale * kLog2e;
+    // ALiBi slope of this q-head, negated, in log2 units
+    const float nsl2 = ALIBI ? -a.alibi[hq] * kLog2e : 0.f;
     // key j is visible to this lane's row iff lim_lo <= j < lim
     const int lim = row_ok ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
     const int lim_lo = MASKED ? i + off - a.win_lo : 0;
@@ -261,12 +263,18 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         }
 
         // ---- P = exp2(S s log2e - LSE log2e), dS = P (dP - D); edge tiles test visibility
+        // ALiBi distance of key j0 + 32 jb + acc_row(v, h) from this lane's
+        // diagonal key i + off: fdist + 32 jb + 8 (v / 4) + v % 4
+        const float fdist = (float)(j0 + 4 * h - i - off);
         auto softmax_grad = [&](auto masked) {
 #pragma unroll
             for (int jb = 0; jb < C::NJB; ++jb) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float p = __builtin_amdgcn_exp2f(st[jb][v] * scale2 - l2);
+                    float x = st[jb][v] * scale2 - l2;
+                    if constexpr (ALIBI)
+                        x = fmaf(nsl2, fabsf(fdist + (float)(32 * jb + 8 * (v >> 2) + (v & 3))), x);
+                    float p = __builtin_amdgcn_exp2f(x);
                     if constexpr (decltype(masked)::value) {
                         const int j = j0 + 32 * jb + acc_row(v, h);
                         p = (j < lim && j >= lim_lo) ? p : 0.f;
@@ -315,7 +323,7 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 }
 
 
-template <class T, int HD, bool MASKED>
+template <class T, int HD, bool MASKED, bool ALIBI>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
@@ -346,22 +354,26 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
         const int m2 = nq - 1 - p;
         if (m2 > p) {
-            dq_tile<T, HD, MASKED>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            dq_tile<T, HD, MASKED, ALIBI>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
             __syncthreads();   // its LDS ring is free again
         }
-        if (p < nq && p <= m2) dq_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
+        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
     } else {
-        dq_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
+        dq_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
 static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
     const unsigned grid = (unsigned)((masked ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
-    if (masked)
-        bwd_dq_kernel<T, HD, true><<<grid, kThreads, 0, st>>>(a);
-    else
-        bwd_dq_kernel<T, HD, false><<<grid, kThreads, 0, st>>>(a);
+    const bool alibi = a.alibi != nullptr;
+    if (masked) {
+        if (alibi) bwd_dq_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
+    } else {
+        if (alibi) bwd_dq_kernel<T, HD, false, true><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, false, false><<<grid, kThreads, 0, st>>>(a);
+    }
 }
 
 int bwd_dq_block_m() { return 32 * kWaves; }

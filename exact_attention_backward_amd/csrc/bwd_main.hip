@@ -364,7 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         // ---- stages 2 and 5: P = exp2(S s log2e - LSE log2e); dS = P (dP - D).
         // Only edge tiles test visibility (key j is visible to row i iff
         // lo(i) <= j < lim(i)); the branch is uniform.
-        auto softmax_grad = [&](auto masked) {
+        // ALiBi slope of this tile's q-head, negated, in log2 units
+        const float nsl2 = a.alibi != nullptr ? -a.alibi[hq] * kLog2e : 0.f;
+        auto softmax_grad = [&](auto masked, auto alibi) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
 #pragma unroll
@@ -376,7 +378,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * q4 + e;
                         const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
-                        float p = __builtin_amdgcn_exp2f(s[mb][v] * scale2 - l2);
+                        float x = s[mb][v] * scale2 - l2;
+                        if constexpr (decltype(alibi)::value)
+                            x = fmaf(nsl2, fabsf((float)(j - (i0 + r + e) - off)), x);
+                        float p = __builtin_amdgcn_exp2f(x);
                         if constexpr (decltype(masked)::value) {
                             const int i = i0 + r + e;
                             const int lim =
@@ -390,10 +395,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                 }
             }
         };
-        if (edge)
-            softmax_grad(std::true_type{});
-        else
-            softmax_grad(std::false_type{});
+        if (a.alibi != nullptr) {
+            if (edge)
+                softmax_grad(std::true_type{}, std::true_type{});
+            else
+                softmax_grad(std::false_type{}, std::true_type{});
+        } else {
+            if (edge)
+                softmax_grad(std::true_type{}, std::false_type{});
+            else
+                softmax_grad(std::false_type{}, std::false_type{});
+        }
 
         // ---- stages 3 and 6: dV += P^T dO, dK += dS^T Q
 #pragma unroll
@@ -603,7 +615,7 @@ struct KvCfg {
 };
 
 // All work of one key tile n of sequence b, kv-head hkv (the body of bwd_kv_kernel).
-template <class T, int HD, bool MASKED, bool STORE_DS>
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
     static_assert(sizeof(T) == 2, "16-bit operand types");
     using C = KvCfg<HD>;
@@ -718,6 +730,10 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) wreg[c] = load_op_global<T>(src + (long long)j * kstride + 16 * c + 8 * h, ok);
     }
+    // ALiBi: lane g holds the slope of the group's q-head g (groups of up to
+    // 64 q-heads; larger ones read the slope per tile)
+    float slope_v = 0.f;
+    if (ALIBI && lane < G) slope_v = a.alibi[hkv * G + lane];
     wait_vmem();
 
     f32x16 acc[C::NDB];   // dV rows (P wave) or unscaled dK rows (dS wave) of this pair's keys
@@ -779,6 +795,14 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
         const int i0 = cur_m * BM;
+        // ALiBi slope of tile t's q-head, negated, in log2 units
+        float nsl2 = 0.f;
+        if constexpr (ALIBI && R == 0) {
+            const float sl = G <= 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                     __builtin_bit_cast(int, slope_v), cur_g))
+                                     : a.alibi[hkv * G + cur_g];
+            nsl2 = -sl * kLog2e;
+        }
         // row statistics of the tile whose second product comes in this step,
         // read now so their latency hides behind the first product: LSE of
         // tile t (P wave), or D and the partner's P of tile t-1 (dS wave)
@@ -848,6 +872,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             // ---- P = exp2(S s log2e - LSE log2e), masked on the tiles the mask crosses
             const int dj = j - (i0 + off + 4 * h);   // key column relative to this lane's first row
             const int dj_hi = dj - a.win_hi, dj_lo = dj + a.win_lo;
+            const float fdj = (float)dj;   // ALiBi distance of row r + e: |fdj - (r + e)|
             auto softmax = [&](auto masked) {
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
@@ -861,11 +886,15 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                             float p;
                             if constexpr (decltype(masked)::value) {
                                 const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
-                                p = __builtin_amdgcn_exp2f(xc[mb][v] * scale2 - l2);
+                                float x = xc[mb][v] * scale2 - l2;
+                                if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                p = __builtin_amdgcn_exp2f(x);
                                 // i + off - lo <= j <= i + off + hi, i = i0 + r + 4h + e
                                 p = (dj_hi <= r + e && dj_lo >= r + e) ? p : 0.f;
                             } else {
-                                p = __builtin_amdgcn_exp2f(fmaf(xc[mb][v], scale2, -lse[e] * kLog2e));
+                                float x = fmaf(xc[mb][v], scale2, -lse[e] * kLog2e);
+                                if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                p = __builtin_amdgcn_exp2f(x);
                             }
                             xc[mb][v] = p;
                         }
@@ -1033,7 +1062,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-template <class T, int HD, bool MASKED, bool STORE_DS>
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[KvCfg<HD>::LDS_BYTES];
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
@@ -1064,10 +1093,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         const int cnt = (p <= n2) + (n2 > p);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, MASKED, STORE_DS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
+            kv_tile<T, HD, MASKED, STORE_DS, ALIBI>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
-        kv_tile<T, HD, MASKED, STORE_DS>(a, b, hkv, p, si, smem);
+        kv_tile<T, HD, MASKED, STORE_DS, ALIBI>(a, b, hkv, p, si, smem);
     }
 }
 
@@ -1075,6 +1104,27 @@ int bwd_block_m(int dtype, int head_dim) {
     if (head_dim == 128) return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 128>::BM : BwdCfg<bf16_t, 128>::BM;
     static_assert(BwdCfg<bf16_t, 128, true>::BM == BwdCfg<bf16_t, 128, false>::BM, "one query tiling");
     return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 64>::BM : BwdCfg<bf16_t, 64>::BM;
+}
+
+// the dK/dV kernel's instantiation for (mask, stored dS, ALiBi)
+template <class T, int HD, bool M, bool S, bool A>
+static void launch_kv3(const BwdArgs& a, unsigned grid, hipStream_t st) {
+    bwd_kv_kernel<T, HD, M, S, A><<<grid, kKvThreads, 0, st>>>(a);
+}
+template <class T, int HD, bool M, bool S>
+static void launch_kv2(const BwdArgs& a, bool alibi, unsigned grid, hipStream_t st) {
+    if (alibi) launch_kv3<T, HD, M, S, true>(a, grid, st);
+    else launch_kv3<T, HD, M, S, false>(a, grid, st);
+}
+template <class T, int HD, bool M>
+static void launch_kv1(const BwdArgs& a, bool store_ds, bool alibi, unsigned grid, hipStream_t st) {
+    if (store_ds) launch_kv2<T, HD, M, true>(a, alibi, grid, st);
+    else launch_kv2<T, HD, M, false>(a, alibi, grid, st);
+}
+template <class T, int HD>
+static void launch_kv(const BwdArgs& a, bool masked, bool store_ds, bool alibi, unsigned grid, hipStream_t st) {
+    if (masked) launch_kv1<T, HD, true>(a, store_ds, alibi, grid, st);
+    else launch_kv1<T, HD, false>(a, store_ds, alibi, grid, st);
 }
 
 template <class T, int HD>
@@ -1085,14 +1135,8 @@ static void launch_bwd_t(const BwdArgs& a, bool masked, int dq_algo, hipStream_t
         const unsigned kv_grid = masked ? (unsigned)((a.nblk_n + 1) / 2 * a.hkv * a.batch) : grid;
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
-        if (dq_algo == ATTN_DQ_SEPARATE) {
-            if (masked) bwd_kv_kernel<T, HD, true, false><<<kv_grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<T, HD, false, false><<<kv_grid, kKvThreads, 0, st>>>(a);
-            return;
-        }
-        if (dq_algo == ATTN_DQ_STORED_DS) {
-            if (masked) bwd_kv_kernel<T, HD, true, true><<<kv_grid, kKvThreads, 0, st>>>(a);
-            else bwd_kv_kernel<T, HD, false, true><<<kv_grid, kKvThreads, 0, st>>>(a);
+        if (dq_algo == ATTN_DQ_SEPARATE || dq_algo == ATTN_DQ_STORED_DS) {
+            launch_kv<T, HD>(a, masked, dq_algo == ATTN_DQ_STORED_DS, a.alibi != nullptr, kv_grid, st);
             return;
         }
     }

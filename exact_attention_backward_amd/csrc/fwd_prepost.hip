@@ -47,6 +47,8 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
         o[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
+    // ALiBi slope in the log2 units of the scaled logits (0: no bias)
+    const float sl2 = a.alibi != nullptr ? a.alibi[hq] * kLog2e : 0.f;
     // keys any row of the block can see: with a mask, from the first row's
     // lower bound (aligned down to a tile) to the last row's upper bound
     const int whi = a.win_hi, wlo = a.win_lo;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
             float acc = 0.f;
 #pragma unroll
             for (int d = 0; d < HD; ++d) acc = fmaf(q[d], ks[jj][d], acc);
-            s[jj] = vis ? acc : -INFINITY;
+            s[jj] = vis ? acc - sl2 * fabsf((float)dj) : -INFINITY;
             tmax = fmaxf(tmax, s[jj]);
         }
         if (tmax > -INFINITY) {

@@ -19,6 +19,7 @@ struct FwdArgs {
     int batch, hq, hkv, seqlen_q, seqlen_k, total_q, total_k;
     float scale;
     int win_lo, win_hi;      // visibility: i + off - win_lo <= j <= i + off + win_hi
+    const float* alibi;      // per q-head ALiBi slopes, or null
 };
 
 struct PreArgs {
@@ -67,6 +68,8 @@ struct BwdArgs {
     // unbounded side.  Kernels instantiated with MASKED = false (no bound at
     // all) ignore them.
     int win_lo, win_hi;
+    // ALiBi: logit - slope[q-head] |i + off - j| (natural-log units), or null
+    const float* alibi;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;

@@ -53,6 +53,13 @@
  *    causal bound when causal = 1.  (The composable-kernel pipeline page
  *    leaves the mask's rule to its mask object; this is the reading taken.)
  *    local = 0 (a zero-initialised shape) means no window.
+ *  - ALiBi: when alibi_slopes is non-NULL (device, fp32 [num_heads_q],
+ *    4-byte aligned, read only), the logit of query i and key j under q-head
+ *    h becomes s * q_i . k_j - alibi_slopes[h] * |i + off - j| (natural-log
+ *    units, the masks' diagonal).  The composable-kernel pipeline page adds a
+ *    position encoding per (row, column) after the scale without its formula;
+ *    this linear bias is the reading taken.  attn_fwd's LSE includes it and
+ *    attn_bwd must get the same slopes.
  *  - GQA: Hq must be a multiple of Hkv; q-head h uses kv-head h / (Hq / Hkv)
  *    (contiguous groups).  dK and dV of a kv-head are the sums over its
  *    q-heads.
@@ -81,8 +88,8 @@ typedef enum attn_status {
                                   in one sequence (seqlen_q x Hq x D elements), ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not 64 or 128,
                                   unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
-    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned (cu_seqlens and
-                                  seqused: 4-byte) */
+    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned (cu_seqlens,
+                                  seqused and alibi_slopes: 4-byte) */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status_t;
 
@@ -137,6 +144,7 @@ typedef struct attn_shape {
     int32_t local;           /* 1: local (sliding-window) mask, see window_left/right */
     int32_t window_left;     /* local: keys at most this many before the diagonal, -1 = any */
     int32_t window_right;    /* local: keys at most this many after the diagonal, -1 = any */
+    const float* alibi_slopes;    /* device [num_heads_q] fp32 ALiBi slopes, or NULL for none */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

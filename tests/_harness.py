@@ -58,19 +58,22 @@ def small_problem(dtype, b, hq, hkv, sq, sk, d, causal, seed, lengths=None, dete
 
 class Run:
     """Inputs of a problem on host and device, with O/LSE from the oracle.
-    window = (left, right) applies a local mask on both sides."""
+    window = (left, right) applies a local mask on both sides; alibi (fp32
+    array, one slope per q-head) the ALiBi bias."""
 
-    def __init__(self, p, oracle_o_lse=True, window=None):
+    def __init__(self, p, oracle_o_lse=True, window=None, alibi=None):
         self.p = p
         self.window = window
+        self.alibi = None if alibi is None else np.asarray(alibi, np.float32)
         self.x = datagen.draw(p)
         cq, ck = p.cu_seqlens()
         self.cu_np = (cq, ck)
         self.cu = (None, None) if cq is None else (torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda())
         self.dev = {k: to_dev(v, p.dtype) for k, v in self.x.items()}
+        self.slopes = None if self.alibi is None else torch.from_numpy(self.alibi).cuda()
         if oracle_o_lse:
             o, lse = oracle.forward(self.x["q"], self.x["k"], self.x["v"], p.scale, p.causal, cq, ck,
-                                    window=window)
+                                    window=window, alibi_slopes=self.alibi)
             self.set_o_lse(o, lse)
 
     def kw(self):
@@ -89,13 +92,14 @@ class Run:
 
     def gpu_forward(self):
         d = self.dev
-        return api.forward(d["q"], d["k"], d["v"], self.p.scale, self.p.causal, window=self.window, **self.kw())
+        return api.forward(d["q"], d["k"], d["v"], self.p.scale, self.p.causal, window=self.window,
+                           alibi_slopes=self.slopes, **self.kw())
 
     def plan(self, deterministic=None, dq_algo="separate"):
         d = self.dev
         det = self.p.deterministic if deterministic is None else deterministic
         return api.BackwardPlan(d["q"], d["k"], self.p.scale, self.p.causal, det, dq_algo=dq_algo,
-                                window=self.window, **self.kw())
+                                window=self.window, alibi_slopes=self.slopes, **self.kw())
 
     def gpu_backward(self, deterministic=None, plan=None, dq_algo="separate"):
         d = self.dev
@@ -108,7 +112,7 @@ class Run:
     def oracle_backward(self):
         cq, ck = self.cu_np
         return oracle.backward(self.x["q"], self.x["k"], self.x["v"], self.o, self.x["do"], self.lse,
-                               self.p.scale, self.p.causal, cq, ck, window=self.window)
+                               self.p.scale, self.p.causal, cq, ck, window=self.window, alibi_slopes=self.alibi)
 
 
 def assert_close(name, got, ref, dtype):

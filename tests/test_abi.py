@@ -114,6 +114,16 @@ def test_window_sizes_accepted():
     assert ws_bytes(shape(local=0, window_left=-9, window_right=-9)) == base
 
 
+def test_alibi_slopes_alignment():
+    base = ws_bytes(shape())
+    assert ws_bytes(shape(alibi_slopes=0x1000)) == base
+    s = shape(alibi_slopes=0x1002)
+    assert ws_bytes(s) == 0
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+    assert rc == L.ATTN_ERR_MISALIGNED
+
+
 def test_shape_struct_layout_matches_header(tmp_path):
     """The ctypes mirror of attn_shape_t has the C layout (compiled from the header)."""
     import shutil
