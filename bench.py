@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the attention backward hot path on one MI355X.
 
-A step is one full backward of the workload: preprocess (D = rowsum(dO * O)
-and workspace clear) -> main kernel -> dQ postprocess, with Q, K, V, O, dO and
-LSE already resident in HBM.  Inputs are seeded synthetic data of the
+A step is one full backward of the workload: attn_bwd_preprocess (D =
+rowsum(dO * O) and workspace clear) -> attn_bwd_full (dK, dV and dQ; the
+dQ pass writes dQ in the I/O type), with Q, K, V, O, dO and LSE already
+resident in HBM.  --api three times the three-call path instead
+(attn_bwd_preprocess -> attn_bwd -> attn_bwd_dq_postprocess).  Inputs are seeded synthetic data of the
 workload's shape; O and LSE come from the library's plain forward.
 
 Prints ONE JSON line: whole-step TFLOP/s (10 * B * H * Sq * Sk * D FLOPs per
@@ -15,7 +17,7 @@ Before the W warm-up steps the bench runs untimed steps for --settle seconds
 (0.5 s by default): after idle the GPU needs about twenty calls to reach its
 steady clock, and the first calls run up to 30% slower.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--settle S]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu] [--settle S] [--api full|three]
 """
 
 import argparse
@@ -37,9 +39,9 @@ MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f)
              for f in ("bwd_main.hip", "bwd_dq.hip", "bwd_dq_gemm.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_{}_causal_{}.json")
 KERNEL_DESC = {
-    "stored_ds": "attn_bwd (key-stationary dK/dV kernel storing dS + dQ = dS K pass)",
-    "separate": "attn_bwd (key-stationary dK/dV kernel + query-stationary dQ kernel)",
-    "atomic": "attn_bwd (key-stationary kernel with dQ atomics)",
+    "stored_ds": "key-stationary dK/dV kernel storing dS + dQ = dS K pass",
+    "separate": "key-stationary dK/dV kernel + query-stationary dQ kernel",
+    "atomic": "key-stationary kernel with dQ atomics",
 }
 
 
@@ -57,6 +59,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
     ap.add_argument("--cpu-pairs", type=int, default=64, help="(sequence, head) pairs in the CPU oracle sample")
+    ap.add_argument("--api", default="full", choices=["full", "three"],
+                    help="full: attn_bwd_preprocess + attn_bwd_full (default); three: attn_bwd_preprocess + "
+                         "attn_bwd + attn_bwd_dq_postprocess")
     ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
                     help="untimed steps before the warm-up, until this much time has passed: after idle the GPU "
                          "takes about 20 calls (~25 ms) to reach its steady clock")
@@ -67,10 +72,13 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_entry(dq_algo, workload):
-    """HBM bytes per attn_bwd call from the committed counter summary of this
-    dQ algorithm on this workload, or None when there is none or a kernel
-    source changed since the counters were taken."""
+def traffic_entry(dq_algo, workload, api):
+    """HBM bytes per attn_bwd_full call from the committed counter summary of
+    this dQ algorithm on this workload, or None when there is none, a kernel
+    source changed since the counters were taken, or the three-call path is
+    timed (its counters are not kept)."""
+    if api != "full":
+        return None
     path = TRAFFIC_FILE.format(workload, dq_algo)
     if not os.path.exists(path):
         return None
@@ -163,18 +171,20 @@ def main():
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
 
+    three = args.api == "three"
+    run = plan.run if three else plan.run_full
     settle_steps = 0
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle:
         for _ in range(10):
-            plan.run(q, k, v, o, do, lse, dq, dk, dv)
+            run(q, k, v, o, do, lse, dq, dk, dv)
         settle_steps += 10
         torch.cuda.synchronize()
     for _ in range(args.warmup):
-        plan.run(q, k, v, o, do, lse, dq, dk, dv)
+        run(q, k, v, o, do, lse, dq, dk, dv)
     torch.cuda.synchronize()
 
-    # per-kernel HIP events on the stream the kernels are launched on
+    # per-call HIP events on the stream the kernels are launched on
     st = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -184,9 +194,13 @@ def main():
         e[0].record(st)
         plan.preprocess(o, do)
         e[1].record(st)
-        plan.main(q, k, v, do, lse, dk, dv)
-        e[2].record(st)
-        plan.postprocess(dq)
+        if three:
+            plan.main(q, k, v, do, lse, dk, dv)
+            e[2].record(st)
+            plan.postprocess(dq)
+        else:
+            plan.main_full(q, k, v, do, lse, dq, dk, dv)
+            e[2].record(st)
         e[3].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -235,25 +249,28 @@ def main():
             "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
         },
         "roofline": {
-            "kernel": KERNEL_DESC[args.dq_algo],
+            "kernel": ("attn_bwd (" if three else "attn_bwd_full (") + KERNEL_DESC[args.dq_algo] +
+                      ("" if three or args.dq_algo != "atomic" else " + dQ postprocess") + ")",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": traffic_entry(args.dq_algo, args.workload),
+            "traffic": traffic_entry(args.dq_algo, args.workload, args.api),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,
         },
+        "api": "attn_bwd_preprocess + attn_bwd + attn_bwd_dq_postprocess" if three else
+               "attn_bwd_preprocess + attn_bwd_full",
         "kernels_ms": {
             "preprocess": round(float(pre_ms.mean()), 5),
             "main": round(main_avg, 5),
-            "postprocess": round(float(post_ms.mean()), 5),
+            "postprocess": round(float(post_ms.mean()), 5) if three else None,
             "step_events": round(float(step_ms.mean()), 5),
         },
         "hbm_GBps": {
             "preprocess": round(pre_bytes / (pre_ms.mean() * 1e-3) / 1e9, 1),
-            "postprocess": round(post_bytes / (post_ms.mean() * 1e-3) / 1e9, 1),
+            "postprocess": round(post_bytes / (post_ms.mean() * 1e-3) / 1e9, 1) if three else None,
             "peak": PEAK_HBM_GBS,
         },
     }

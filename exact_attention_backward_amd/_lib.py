@@ -33,6 +33,7 @@ EXPORTS = (
     "attn_bwd_preprocess",
     "attn_bwd",
     "attn_bwd_dq_postprocess",
+    "attn_bwd_full",
 )
 
 
@@ -93,6 +94,8 @@ def lib():
         L.attn_bwd.restype = i32
         L.attn_bwd_dq_postprocess.argtypes = [sp, vp, sz, vp, ctypes.c_float, vp]
         L.attn_bwd_dq_postprocess.restype = i32
+        L.attn_bwd_full.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
+        L.attn_bwd_full.restype = i32
         _lib = L
     return _lib
 

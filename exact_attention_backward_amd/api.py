@@ -115,6 +115,12 @@ def attn_bwd_dq_postprocess(shape, workspace, dq, scale):
         ctypes.byref(shape), _ptr(workspace), workspace.numel(), _ptr(dq), ctypes.c_float(scale), _stream()))
 
 
+def attn_bwd_full(shape, q, k, v, do, lse, delta, workspace, dq, dk, dv):
+    return L.check("attn_bwd_full", L.lib().attn_bwd_full(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
+        workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _stream()))
+
+
 def _lse_shape(shape, varlen):
     if varlen:
         return (shape.num_heads_q, shape.total_q)
@@ -167,9 +173,20 @@ class BackwardPlan:
         attn_bwd_dq_postprocess(self.shape, self.workspace, dq, self.scale)
 
     def run(self, q, k, v, o, do, lse, dq, dk, dv):
+        """The three calls in order (dQ through the fp32 accumulator)."""
         self.preprocess(o, do)
         self.main(q, k, v, do, lse, dk, dv)
         self.postprocess(dq)
+
+    def main_full(self, q, k, v, do, lse, dq, dk, dv):
+        """attn_bwd_full: dK, dV and dQ in one call (dQ written straight in the
+        I/O type by the separate and stored-dS modes)."""
+        attn_bwd_full(self.shape, q, k, v, do, lse, self.delta, self.workspace, dq, dk, dv)
+
+    def run_full(self, q, k, v, o, do, lse, dq, dk, dv):
+        """Two calls: attn_bwd_preprocess, then attn_bwd_full."""
+        self.preprocess(o, do)
+        self.main_full(q, k, v, do, lse, dq, dk, dv)
 
     def error_flag(self):
         """Non-zero if an ordered (deterministic) wait gave up; reads the

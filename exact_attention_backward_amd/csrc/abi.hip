@@ -149,16 +149,13 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     return check_launch();
 }
 
-int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
-                        size_t workspace_size, void* stream) {
-    int st = validate_shape(s);
-    if (st) return st;
-    if (!o || !dout || !delta || !workspace) return ATTN_ERR_NULL_ARG;
-    if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || !aligned16(workspace)) return ATTN_ERR_MISALIGNED;
-    const size_t need = workspace_bytes(s);
-    if (workspace_size < need) return ATTN_ERR_BAD_SHAPE;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    (void)hipGetLastError();   // clear a stale error so the check below is ours
+}  // extern "C"
+
+namespace {
+
+// The enqueue steps behind the entry points; arguments already validated.
+void enqueue_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
+                        hipStream_t hs) {
     // the counters and status words always; the accumulator only where it is
     // added into (atomic modes); the dS blocks are written before they are read
     if (s->dq_algo == ATTN_DQ_ATOMIC)
@@ -172,18 +169,13 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
                         reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + accum_bytes(s) + sem_bytes(s) +
                                                kErrBytes),
                         hs);
-    return check_launch();
 }
 
-int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout, const float* lse,
-             const float* delta, void* workspace, size_t workspace_size, void* dk, void* dv, void* stream) {
-    int st = validate_shape(s);
-    if (st) return st;
-    if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dk || !dv) return ATTN_ERR_NULL_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
-        !aligned16(delta) || !aligned16(workspace) || !aligned16(dk) || !aligned16(dv))
-        return ATTN_ERR_MISALIGNED;
-    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+// dq_out: the separate and stored-dS modes write dQ = T(dq_scale * sum)
+// there instead of to the accumulator (null: the accumulator)
+void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout,
+                 const float* lse, const float* delta, void* workspace, void* dk, void* dv, void* dq_out,
+                 float dq_scale, hipStream_t hs) {
     char* ws = reinterpret_cast<char*>(workspace);
     BwdArgs a{};
     a.q = q;
@@ -215,6 +207,8 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.win_lo = win_lo(s);
     a.win_hi = win_hi(s);
     a.alibi = s->alibi_slopes;
+    a.dq_out = s->dq_algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
+    a.dq_scale = dq_scale;
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
@@ -222,8 +216,6 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
         a.ds_qb = ds_qb(s);
         a.ds_nn = ds_nn(s);
     }
-    (void)hipGetLastError();   // clear a stale error so the check below is ours
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     launch_bwd(a, s->dtype, s->head_dim, masked(s), s->dq_algo, hs);
     if (s->dq_algo == ATTN_DQ_SEPARATE) {
         BwdArgs d = a;
@@ -232,6 +224,41 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
         launch_bwd_dq_gemm(a, s->dtype, s->head_dim, masked(s), hs);
     }
+}
+
+void enqueue_postprocess(const attn_shape_t* s, const void* workspace, void* dq, float scale, hipStream_t hs) {
+    PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
+               s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch};
+    launch_postprocess(a, s->dtype, s->head_dim, hs);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
+                        size_t workspace_size, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!o || !dout || !delta || !workspace) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || !aligned16(workspace)) return ATTN_ERR_MISALIGNED;
+    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
+    enqueue_preprocess(s, o, dout, delta, workspace, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout, const float* lse,
+             const float* delta, void* workspace, size_t workspace_size, void* dk, void* dv, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dk || !dv) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+        !aligned16(delta) || !aligned16(workspace) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_MISALIGNED;
+    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
+    enqueue_bwd(s, q, k, v, dout, lse, delta, workspace, dk, dv, nullptr, 0.f, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -242,10 +269,25 @@ int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t
     if (!workspace || !dq) return ATTN_ERR_NULL_ARG;
     if (!aligned16(workspace) || !aligned16(dq)) return ATTN_ERR_MISALIGNED;
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
-    PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
-               s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch};
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    launch_postprocess(a, s->dtype, s->head_dim, reinterpret_cast<hipStream_t>(stream));
+    enqueue_postprocess(s, workspace, dq, scale, reinterpret_cast<hipStream_t>(stream));
+    return check_launch();
+}
+
+int attn_bwd_full(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse, const float* delta, void* workspace, size_t workspace_size, void* dq, void* dk,
+                  void* dv, void* stream) {
+    int st = validate_shape(s);
+    if (st) return st;
+    if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dq || !dk || !dv) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+        !aligned16(delta) || !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_MISALIGNED;
+    if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
+    enqueue_bwd(s, q, k, v, dout, lse, delta, workspace, dk, dv, dq, s->softmax_scale, hs);
+    if (s->dq_algo == ATTN_DQ_ATOMIC) enqueue_postprocess(s, workspace, dq, s->softmax_scale, hs);
     return check_launch();
 }
 

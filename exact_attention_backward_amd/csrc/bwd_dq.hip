@@ -310,7 +310,26 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         }
     }
 
-    // ---- write this tile's dQ rows once (unscaled; the postprocess applies s)
+    // ---- write this tile's dQ rows once: scaled and converted into dq, or
+    // unscaled into the accumulator (the postprocess applies s)
+    if (a.dq_out != nullptr) {
+        const long long ostride = (long long)a.hq * HD;
+        T* o = reinterpret_cast<T*>(a.dq_out) + ((long long)(si.q0 + i0 + 32 * w) * a.hq + hq) * HD;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = acc_row(v, h);
+                float y;
+                {
+#pragma clang fp contract(off)
+                    y = dq[d][v] * a.dq_scale;   // rounded to fp32, then to T
+                }
+                if (i0 + 32 * w + r < si.len_q) store_elem(o, (long long)r * ostride + 32 * d + l32, y);
+            }
+        }
+        return;
+    }
     float* dqa = a.dq_acc + (row0 + i0 + 32 * w) * HD;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {

@@ -223,7 +223,30 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     }
     g_wait_vmem_but<0>();   // the empty copies past the end have retired before the waves exit
 
-    // ---- this wave's dQ rows, written once (unscaled; the postprocess applies s)
+    // ---- this wave's dQ rows, written once: scaled and converted into dq,
+    // or unscaled into the accumulator (the postprocess applies s)
+    if (a.dq_out != nullptr) {
+        const long long ostride = (long long)a.hq * HD;
+#pragma unroll
+        for (int r = 0; r < kGRB; ++r) {
+            const int r0 = (lq0 + r) * kDsRows;
+            T* o = reinterpret_cast<T*>(a.dq_out) + ((long long)(si.q0 + r0) * a.hq + hq) * HD;
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rr = acc_row(v, h);
+                    float y;
+                    {
+#pragma clang fp contract(off)
+                        y = acc[r][d][v] * a.dq_scale;   // rounded to fp32, then to T
+                    }
+                    if (r0 + rr < si.len_q) store_elem(o, (long long)rr * ostride + 32 * d + l32, y);
+                }
+            }
+        }
+        return;
+    }
     const long long row0 = varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
 #pragma unroll
     for (int r = 0; r < kGRB; ++r) {

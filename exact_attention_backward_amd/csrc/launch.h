@@ -70,6 +70,12 @@ struct BwdArgs {
     int win_lo, win_hi;
     // ALiBi: logit - slope[q-head] |i + off - j| (natural-log units), or null
     const float* alibi;
+    // dQ passes that own whole rows (separate, stored dS): when set, dQ goes
+    // straight to this [rows, Hq, D] tensor of the I/O type as
+    // T(dq_scale * sum), the product rounded to fp32 first, instead of to
+    // the fp32 accumulator
+    void* dq_out;
+    float dq_scale;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;

@@ -17,6 +17,9 @@
  *     attn_bwd_preprocess      D = rowsum(dO * O); clears the workspace
  *     attn_bwd                 dK, dV; dQ accumulated in fp32 in the workspace
  *     attn_bwd_dq_postprocess  dQ = scale * dQaccum, converted to the I/O type
+ * or two: attn_bwd_preprocess, then attn_bwd_full (dK, dV and dQ, the latter
+ * written in the I/O type by the dQ pass itself where that pass owns whole
+ * rows).
  * attn_fwd is a plain forward used only to produce O and LSE inputs.
  *
  * Conventions shared by every entry point
@@ -205,6 +208,24 @@ int attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void
  * scale = shape->softmax_scale.  workspace: input; dq: output. */
 int attn_bwd_dq_postprocess(const attn_shape_t* shape, const void* workspace,
                             size_t workspace_bytes, void* dq, float scale, void* stream);
+
+/* attn_bwd and the dQ conversion in one call (after attn_bwd_preprocess, in
+ * place of attn_bwd + attn_bwd_dq_postprocess), with scale =
+ * shape->softmax_scale and the same results bit for bit (the non-
+ * deterministic atomic mode: up to the order of its atomic additions, as
+ * between any two runs).  The separate and stored-dS modes, whose dQ pass
+ * owns whole rows, write dq = dtype(scale * dS K) straight from that pass
+ * (the product rounded to fp32, then to nearest even, as the postprocess
+ * does), skipping the fp32 accumulator and the conversion pass; the atomic
+ * mode runs the postprocess.  Only rows of the sequences are written (with
+ * seqused, rows past the used lengths keep their contents).  Same layouts,
+ * workspace and errors as attn_bwd; the accumulator's contents afterwards
+ * are unspecified.
+ * q, k, v, dout, lse, delta: inputs; dq, dk, dv: outputs; workspace: in/out. */
+int attn_bwd_full(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                  const void* dout, const float* lse, const float* delta,
+                  void* workspace, size_t workspace_bytes, void* dq, void* dk, void* dv,
+                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -169,3 +169,10 @@ def test_null_and_misaligned_pointers_rejected():
                                        None) == L.ATTN_ERR_NULL_ARG
     assert lib.attn_fwd(ctypes.byref(s), fake, fake, fake, bad, fake, None) == L.ATTN_ERR_MISALIGNED
     assert lib.attn_fwd(None, fake, fake, fake, fake, fake, None) == L.ATTN_ERR_NULL_ARG
+    # attn_bwd_full: dq is required and aligned like the other tensors
+    assert lib.attn_bwd_full(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, None, fake, fake,
+                             None) == L.ATTN_ERR_NULL_ARG
+    assert lib.attn_bwd_full(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, bad, fake, fake,
+                             None) == L.ATTN_ERR_MISALIGNED
+    assert lib.attn_bwd_full(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 16, fake, fake, fake,
+                             None) == L.ATTN_ERR_BAD_SHAPE

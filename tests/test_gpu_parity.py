@@ -309,6 +309,54 @@ def test_alibi_zero_slopes_equal_plain(dq_algo):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+# attn_bwd_full against the three-call path: (case, window, alibi)
+FULL_CASES = [
+    (CASES[0], None, False),      # bf16 dense causal D128
+    (CASES[3], None, False),      # bf16 Sq < Sk causal
+    (CASES[9], None, False),      # bf16 varlen + GQA D64
+    (CASES[15], None, False),     # fp16 Sq < Sk causal D64
+    (CASES[17], None, False),     # fp16 varlen + GQA causal
+    (CASES[11], None, False),     # fp32 Sq > Sk causal
+    (CASES[13], None, False),     # fp32 varlen
+    (CASES[6], (100, -1), True),  # bf16 GQA causal window + ALiBi
+]
+
+
+def _fullid(c):
+    case, win, alibi = c
+    return _id(case) + (f"-w{win[0]}/{win[1]}" if win else "") + ("-alibi" if alibi else "")
+
+
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
+@pytest.mark.parametrize("fc", FULL_CASES, ids=_fullid)
+def test_bwd_full_matches_three_calls_bitwise(fc, dq_algo):
+    """attn_bwd_full (dQ written by the dQ pass in the I/O type, or through
+    the postprocess in the atomic mode) gives the three-call results bit for
+    bit (the atomic mode in its deterministic order), and the oracle's."""
+    case, win, alibi = fc
+    if dq_algo == "stored_ds" and case[0] == "f32":
+        pytest.skip("the stored-dS mode is for 16-bit types only (the ABI rejects fp32)")
+    p = problem(case, deterministic=dq_algo == "atomic")
+    r = Run(p, window=win, alibi=_alibi_slopes(case[2]) if alibi else None)
+    print(f"full {_fullid(fc)} dq={dq_algo}", flush=True)
+    d = r.dev
+    plan = r.plan(dq_algo=dq_algo)
+    sentinel = 7.0
+    three = [torch.full_like(d[n], sentinel) for n in ("q", "k", "v")]
+    plan.run(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], *three)
+    full = [torch.full_like(d[n], sentinel) for n in ("q", "k", "v")]
+    plan.run_full(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], *full)
+    torch.cuda.synchronize()
+    if p.deterministic:
+        assert plan.error_flag() == 0
+    iview = torch.int16 if full[0].element_size() == 2 else torch.int32
+    for n, a, b in zip(("dQ", "dK", "dV"), three, full):
+        assert torch.equal(a.view(iview), b.view(iview)), n
+    rdq, rdk, rdv = r.oracle_backward()
+    for n, g, ref in (("dQ", full[0], rdq), ("dK", full[1], rdk), ("dV", full[2], rdv)):
+        assert_close(n, to_host(g), ref, p.dtype)
+
+
 SEQUSED_CASES = [
     # (dtype, Hq, Hkv, D, causal, lengths_q, lengths_k, used_q, used_k)
     ("bf16", 4, 2, 128, True, (70, 300, 129, 1), (90, 260, 129, 40), (70, 211, 0, 1), (33, 260, 100, 40)),
@@ -322,11 +370,13 @@ def _sequsedid(c):
     return f"{dt}-h{hq}/{hkv}-d{d}-{'causal' if causal else 'full'}-uq{'-'.join(map(str, uq))}-uk{'-'.join(map(str, uk))}"
 
 
+@pytest.mark.parametrize("full", [False, True], ids=["three_calls", "bwd_full"])
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
 @pytest.mark.parametrize("case", SEQUSED_CASES, ids=_sequsedid)
-def test_seqused_matches_oracle_and_leaves_unused_rows(case, dq_algo):
+def test_seqused_matches_oracle_and_leaves_unused_rows(case, dq_algo, full):
     """Varlen with used lengths: the used rows of O, LSE, dQ, dK, dV match the
-    oracle; every row past a used length keeps what the buffer held."""
+    oracle; every row past a used length keeps what the buffer held (through
+    the three calls and through attn_bwd_full)."""
     import datagen
     from _harness import TORCH_DTYPE, to_dev
     dt, hq, hkv, d, causal, lq, lk, uq, uk = case
@@ -344,7 +394,7 @@ def test_seqused_matches_oracle_and_leaves_unused_rows(case, dq_algo):
     for b in range(len(lq)):
         used_q[cq[b]:cq[b] + uq[b]] = True
         used_k[ck[b]:ck[b] + uk[b]] = True
-    print(f"seqused {_sequsedid(case)} dq={dq_algo}", flush=True)
+    print(f"seqused {_sequsedid(case)} dq={dq_algo} full={full}", flush=True)
     sentinel = 3.0
     # forward: used rows against the oracle, unused rows untouched
     o_buf = torch.full_like(dev["q"], sentinel)
@@ -369,7 +419,8 @@ def test_seqused_matches_oracle_and_leaves_unused_rows(case, dq_algo):
     dq = torch.full_like(dev["q"], sentinel)
     dk = torch.full_like(dev["k"], sentinel)
     dv = torch.full_like(dev["v"], sentinel)
-    plan.run(dev["q"], dev["k"], dev["v"], dev_o, dev["do"], dev_lse, dq, dk, dv)
+    runner = plan.run_full if full else plan.run
+    runner(dev["q"], dev["k"], dev["v"], dev_o, dev["do"], dev_lse, dq, dk, dv)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle.backward(x["q"], x["k"], x["v"], o_in, x["do"], lse_in.astype(np.float64), p.scale, causal,
                                     cq, ck, uq_np, uk_np)
