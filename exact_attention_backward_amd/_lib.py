@@ -37,6 +37,19 @@ EXPORTS = (
 )
 
 
+class TensorStrides(ctypes.Structure):
+    """Mirror of attn_tensor_strides_t (elements)."""
+    _fields_ = [("batch", ctypes.c_int64), ("row", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+STRIDE_TENSORS = ("q", "k", "v", "o", "dout", "dq", "dk", "dv")
+
+
+class Strides(ctypes.Structure):
+    """Mirror of attn_strides_t."""
+    _fields_ = [(n, TensorStrides) for n in STRIDE_TENSORS]
+
+
 class AttnShape(ctypes.Structure):
     """Mirror of attn_shape_t."""
     _fields_ = [
@@ -61,6 +74,7 @@ class AttnShape(ctypes.Structure):
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
+        ("strides", ctypes.c_void_p),
     ]
 
 

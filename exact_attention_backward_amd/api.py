@@ -1,11 +1,16 @@
 """Python binding of the C ABI: the same entry points, taking torch tensors.
 
 PyTorch only supplies device memory and the current HIP stream; every step of
-the computation runs in the library's kernels.  Tensors must be contiguous
-and on the GPU; layouts are those of include/attn_bwd.h:
+the computation runs in the library's kernels.  Tensors must be on the GPU
+with the index order of include/attn_bwd.h:
 
   dense : q, o, do, dq [B, Sq, Hq, D];  k, v, dk, dv [B, Sk, Hkv, D];  lse, delta [B, Hq, Sq]
   varlen: q, o, do, dq [Tq, Hq, D];     k, v, dk, dv [Tk, Hkv, D];     lse, delta [Hq, Tq]
+
+The head dimension must be contiguous; the batch, row and head strides of
+every tensor are passed to the library as they are (views such as the q, k
+and v slices of a packed [B, S, 3, H, D] tensor need no copy).  LSE, D and
+the workspace must be contiguous.
 """
 
 import ctypes
@@ -21,6 +26,7 @@ __all__ = [
     "attn_bwd_preprocess",
     "attn_bwd",
     "attn_bwd_dq_postprocess",
+    "attn_bwd_full",
     "forward",
     "backward",
     "BackwardPlan",
@@ -30,10 +36,19 @@ _DTYPES = {torch.bfloat16: L.ATTN_DTYPE_BF16, torch.float16: L.ATTN_DTYPE_F16, t
 
 
 def _ptr(t):
+    """Pointer of a tensor the library reads or writes with its own
+    (contiguous) layout: LSE, D, the workspace."""
     if t is None:
         return None
     if not t.is_contiguous():
-        raise ValueError("tensors must be contiguous")
+        raise ValueError("lse, delta and the workspace must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _tptr(t):
+    """Pointer of a strided Q/K/V/O/dO/dQ/dK/dV tensor (head dim contiguous)."""
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError("the head dimension must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -90,35 +105,68 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     return s
 
 
+def _strides(shape, tensors):
+    """attn_strides_t of the given tensors (the others keep the contiguous
+    layout)."""
+    varlen = bool(shape.cu_seqlens_q)
+    st = L.Strides()
+    d = shape.head_dim
+    for name in L.STRIDE_TENSORS:
+        is_k = name in ("k", "v", "dk", "dv")
+        heads = shape.num_heads_kv if is_k else shape.num_heads_q
+        seq = shape.seqlen_k if is_k else shape.seqlen_q
+        t = tensors.get(name)
+        x = getattr(st, name)
+        if t is None:
+            x.row, x.head = heads * d, d
+            x.batch = 0 if varlen else seq * heads * d
+        elif varlen:
+            x.batch, x.row, x.head = 0, t.stride(0), t.stride(1)
+        else:
+            x.batch, x.row, x.head = t.stride(0), t.stride(1), t.stride(2)
+    return st
+
+
+def _call(name, shape, tensors, *args):
+    """Call entry point `name` with shape.strides pointing at the strides of
+    `tensors` for the duration of the call only."""
+    st = _strides(shape, tensors)
+    shape.strides = ctypes.addressof(st)
+    try:
+        return L.check(name, getattr(L.lib(), name)(ctypes.byref(shape), *args))
+    finally:
+        shape.strides = None
+
+
 def attn_bwd_workspace_bytes(shape):
     return int(L.lib().attn_bwd_workspace_bytes(ctypes.byref(shape)))
 
 
 def attn_fwd(shape, q, k, v, o, lse):
-    return L.check("attn_fwd", L.lib().attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                                   _ptr(lse), _stream()))
+    return _call("attn_fwd", shape, dict(q=q, k=k, v=v, o=o),
+                 _tptr(q), _tptr(k), _tptr(v), _tptr(o), _ptr(lse), _stream())
 
 
 def attn_bwd_preprocess(shape, o, do, delta, workspace):
-    return L.check("attn_bwd_preprocess", L.lib().attn_bwd_preprocess(
-        ctypes.byref(shape), _ptr(o), _ptr(do), _ptr(delta), _ptr(workspace), workspace.numel(), _stream()))
+    return _call("attn_bwd_preprocess", shape, dict(o=o, dout=do),
+                 _tptr(o), _tptr(do), _ptr(delta), _ptr(workspace), workspace.numel(), _stream())
 
 
 def attn_bwd(shape, q, k, v, do, lse, delta, workspace, dk, dv):
-    return L.check("attn_bwd", L.lib().attn_bwd(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
-        workspace.numel(), _ptr(dk), _ptr(dv), _stream()))
+    return _call("attn_bwd", shape, dict(q=q, k=k, v=v, dout=do, dk=dk, dv=dv),
+                 _tptr(q), _tptr(k), _tptr(v), _tptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
+                 workspace.numel(), _tptr(dk), _tptr(dv), _stream())
 
 
 def attn_bwd_dq_postprocess(shape, workspace, dq, scale):
-    return L.check("attn_bwd_dq_postprocess", L.lib().attn_bwd_dq_postprocess(
-        ctypes.byref(shape), _ptr(workspace), workspace.numel(), _ptr(dq), ctypes.c_float(scale), _stream()))
+    return _call("attn_bwd_dq_postprocess", shape, dict(dq=dq),
+                 _ptr(workspace), workspace.numel(), _tptr(dq), ctypes.c_float(scale), _stream())
 
 
 def attn_bwd_full(shape, q, k, v, do, lse, delta, workspace, dq, dk, dv):
-    return L.check("attn_bwd_full", L.lib().attn_bwd_full(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
-        workspace.numel(), _ptr(dq), _ptr(dk), _ptr(dv), _stream()))
+    return _call("attn_bwd_full", shape, dict(q=q, k=k, v=v, dout=do, dq=dq, dk=dk, dv=dv),
+                 _tptr(q), _tptr(k), _tptr(v), _tptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
+                 workspace.numel(), _tptr(dq), _tptr(dk), _tptr(dv), _stream())
 
 
 def _lse_shape(shape, varlen):

@@ -17,11 +17,20 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// the caller's strides, or those of the contiguous layouts
+attn_strides_t strides_of(const attn_shape_t* s) {
+    if (s->strides != nullptr) return *s->strides;
+    const long long d = s->head_dim;
+    const attn_tensor_strides_t qs{(long long)s->seqlen_q * s->num_heads_q * d, (long long)s->num_heads_q * d, d};
+    const attn_tensor_strides_t ks{(long long)s->seqlen_k * s->num_heads_kv * d, (long long)s->num_heads_kv * d, d};
+    return attn_strides_t{qs, ks, ks, qs, qs, qs, ks, ks};
+}
+
 int validate_shape(const attn_shape_t* s) {
     if (s == nullptr) return ATTN_ERR_NULL_ARG;
     if (s->dtype != ATTN_DTYPE_F32 && s->dtype != ATTN_DTYPE_BF16 && s->dtype != ATTN_DTYPE_F16)
         return ATTN_ERR_UNSUPPORTED;
-    if (s->head_dim != 64 && s->head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (s->head_dim < 8 || s->head_dim > 128 || s->head_dim % 8 != 0) return ATTN_ERR_UNSUPPORTED;
     if (s->batch <= 0 || s->num_heads_q <= 0 || s->num_heads_kv <= 0 || s->seqlen_q <= 0 || s->seqlen_k <= 0)
         return ATTN_ERR_BAD_SHAPE;
     if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_BAD_SHAPE;
@@ -51,14 +60,30 @@ int validate_shape(const attn_shape_t* s) {
     // one-dimensional grids of the streaming kernels: (row, head) pairs times
     // lanes per pair must stay below 2^32 threads
     if (rows_q * s->num_heads_q > (1LL << 27) || rows_k * s->num_heads_kv > (1LL << 27)) return ATTN_ERR_BAD_SHAPE;
-    // a tile's byte offset within one sequence's Q/dO rows travels in a
-    // 32-bit scalar offset
-    if ((long long)s->seqlen_q * s->num_heads_q * s->head_dim * (s->dtype == ATTN_DTYPE_F32 ? 4 : 2) >= (1LL << 31))
-        return ATTN_ERR_BAD_SHAPE;
+    // strides: non-negative and 16-byte multiples (rows and heads start on
+    // 16-byte boundaries); a tile's byte offset within one sequence's rows
+    // travels in a 32-bit offset, and all buffer ranges stay below kOobOff
+    const long long esz = s->dtype == ATTN_DTYPE_F32 ? 4 : 2;
+    const attn_strides_t d = strides_of(s);
+    const attn_tensor_strides_t* all[] = {&d.q, &d.k, &d.v, &d.o, &d.dout, &d.dq, &d.dk, &d.dv};
+    for (int t = 0; t < 8; ++t) {
+        const attn_tensor_strides_t* x = all[t];
+        if (x->batch < 0 || x->row < 0 || x->head < 0) return ATTN_ERR_BAD_SHAPE;
+        if ((x->batch * esz) % 16 || (x->row * esz) % 16 || (x->head * esz) % 16) return ATTN_ERR_MISALIGNED;
+        // rows of q, k, v, o, dout, dq, dk, dv in one sequence
+        const long long len = (t == 1 || t == 2 || t >= 6) ? s->seqlen_k : s->seqlen_q;
+        if ((len + 1) * x->row * esz >= kOobOff - (1LL << 20)) return ATTN_ERR_BAD_SHAPE;
+        if (x->head * esz >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;   // 32-bit head steps
+    }
     return ATTN_OK;
 }
 
 bool varlen(const attn_shape_t* s) { return s->cu_seqlens_q != nullptr; }
+
+// the head dim the kernels tile with: head_dim rounded up to 64 or 128
+int padded_hd(const attn_shape_t* s) { return s->head_dim <= 64 ? 64 : 128; }
+
+Strides to_kernel(const attn_tensor_strides_t& t) { return Strides{t.batch, t.row, t.head}; }
 
 // Window bounds of the kernels: key j visible to query i iff
 // i + off - lo <= j <= i + off + hi (kNoWindow: unbounded side).  Sequences
@@ -80,10 +105,10 @@ size_t elem_bytes(const attn_shape_t* s) { return s->dtype == ATTN_DTYPE_F32 ? 4
 
 // workspace = [dQ accumulator fp32][ordering counters int32][status words]
 size_t accum_bytes(const attn_shape_t* s) {
-    return align_up((size_t)rows_q(s) * s->num_heads_q * s->head_dim * sizeof(float));
+    return align_up((size_t)rows_q(s) * s->num_heads_q * padded_hd(s) * sizeof(float));
 }
 int nblk_m(const attn_shape_t* s) {
-    const int bm = bwd_block_m(s->dtype, s->head_dim);
+    const int bm = bwd_block_m(s->dtype, padded_hd(s));
     return (s->seqlen_q + bm - 1) / bm;
 }
 size_t sem_bytes(const attn_shape_t* s) {
@@ -119,7 +144,7 @@ const char* attn_status_string(int status) {
         case ATTN_OK: return "ok";
         case ATTN_ERR_NULL_ARG: return "null argument";
         case ATTN_ERR_BAD_SHAPE: return "bad shape";
-        case ATTN_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or dq_algo";
         case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case ATTN_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
@@ -145,7 +170,13 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.win_lo = win_lo(s);
     a.win_hi = win_hi(s);
     a.alibi = s->alibi_slopes;
-    launch_fwd(a, s->dtype, s->head_dim, masked(s), reinterpret_cast<hipStream_t>(stream));
+    const attn_strides_t d = strides_of(s);
+    a.d = s->head_dim;
+    a.sq = to_kernel(d.q);
+    a.sk = to_kernel(d.k);
+    a.sv = to_kernel(d.v);
+    a.so = to_kernel(d.o);
+    launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -162,8 +193,10 @@ void enqueue_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
         launch_fill_zero(workspace, accum_bytes(s) + sem_bytes(s) + kErrBytes, hs);
     else
         launch_fill_zero(reinterpret_cast<char*>(workspace) + accum_bytes(s), sem_bytes(s) + kErrBytes, hs);
-    PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s)};
-    launch_preprocess(a, s->dtype, s->head_dim, hs);
+    const attn_strides_t d = strides_of(s);
+    PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s),
+              s->head_dim, to_kernel(d.o), to_kernel(d.dout)};
+    launch_preprocess(a, s->dtype, padded_hd(s), hs);
     if (s->dq_algo == ATTN_DQ_STORED_DS && varlen(s))
         launch_ds_table(s->cu_seqlens_q, s->batch, s->seqlen_q, s->total_q,
                         reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + accum_bytes(s) + sem_bytes(s) +
@@ -209,6 +242,15 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
     a.alibi = s->alibi_slopes;
     a.dq_out = s->dq_algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
     a.dq_scale = dq_scale;
+    const attn_strides_t d = strides_of(s);
+    a.d = s->head_dim;
+    a.sq = to_kernel(d.q);
+    a.sk = to_kernel(d.k);
+    a.sv = to_kernel(d.v);
+    a.sdo = to_kernel(d.dout);
+    a.sdq = to_kernel(d.dq);
+    a.sdk = to_kernel(d.dk);
+    a.sdv = to_kernel(d.dv);
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
@@ -216,20 +258,21 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
         a.ds_qb = ds_qb(s);
         a.ds_nn = ds_nn(s);
     }
-    launch_bwd(a, s->dtype, s->head_dim, masked(s), s->dq_algo, hs);
+    launch_bwd(a, s->dtype, padded_hd(s), masked(s), s->dq_algo, hs);
     if (s->dq_algo == ATTN_DQ_SEPARATE) {
-        BwdArgs d = a;
-        d.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
-        launch_bwd_dq(d, s->dtype, s->head_dim, masked(s), hs);
+        BwdArgs e = a;
+        e.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
+        launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), hs);
     } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
-        launch_bwd_dq_gemm(a, s->dtype, s->head_dim, masked(s), hs);
+        launch_bwd_dq_gemm(a, s->dtype, padded_hd(s), masked(s), hs);
     }
 }
 
 void enqueue_postprocess(const attn_shape_t* s, const void* workspace, void* dq, float scale, hipStream_t hs) {
     PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
-               s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch};
-    launch_postprocess(a, s->dtype, s->head_dim, hs);
+               s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch,
+               s->head_dim, to_kernel(strides_of(s).dq)};
+    launch_postprocess(a, s->dtype, padded_hd(s), hs);
 }
 
 }  // namespace

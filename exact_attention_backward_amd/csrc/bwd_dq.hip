@@ -113,13 +113,15 @@ struct DqTileCopy {
     static constexpr int N = NROWS * CPR / 64 / kWaves;
     static_assert(NROWS * CPR % (64 * kWaves) == 0, "segment split");
     int voff[N];
-    __device__ __forceinline__ void init(int w, int lane, int stride_bytes) {
+    // stride_bytes: between rows in memory; valid: 16-byte chunks of a row
+    // inside the head dim (the others read zeros)
+    __device__ __forceinline__ void init(int w, int lane, int stride_bytes, int valid) {
 #pragma unroll
         for (int t = 0; t < N; ++t) {
             const int slot = (w + t * kWaves) * 64 + lane;
             const int r = slot / CPR;
             const int c = (slot % CPR) ^ swz_key<ROWB>(r);
-            voff[t] = r * stride_bytes + c * 16;
+            voff[t] = c < valid ? r * stride_bytes + c * 16 : kOobOff;
         }
     }
     __device__ __forceinline__ void issue(i32x4 src, const char* lds, int w) const {
@@ -171,13 +173,13 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     }
     const int n_kt = key_end > 0 ? max((key_end + BN - 1) / BN - kt_b, 0) : 0;
 
-    const long long qstride = (long long)a.hq * HD;
-    const long long kstride = (long long)a.hkv * HD;
-    const T* kg = reinterpret_cast<const T*>(a.k) + (long long)si.k0 * kstride + (long long)hkv * HD;
-    const T* vg = reinterpret_cast<const T*>(a.v) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    const T* kg = reinterpret_cast<const T*>(a.k) + seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h;
+    const T* vg = reinterpret_cast<const T*>(a.v) + seq_off(a.sv, varlen, b, si.k0) + (long long)hkv * a.sv.h;
 
-    DqTileCopy<C::ROWB, BN> kvcopy;
-    kvcopy.init(w, lane, (int)(kstride * sizeof(T)));
+    const int valid = a.d * (int)sizeof(T) / 16;   // 16-byte chunks of a row inside the head dim
+    DqTileCopy<C::ROWB, BN> kcopy, vcopy;
+    kcopy.init(w, lane, (int)(a.sk.r * (long long)sizeof(T)), valid);
+    vcopy.init(w, lane, (int)(a.sv.r * (long long)sizeof(T)), valid);
     constexpr int kOpsPerTile = 2 * DqTileCopy<C::ROWB, BN>::N;   // copies one wave issues per tile
     static_assert(kOpsPerTile * (C::NS - 2) < 16, "vmcnt range");
     // the u-th tile of the run (key tile kt_b + u) goes to ring buffer u % NS
@@ -185,10 +187,11 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     auto issue_tile = [&](int u) {
         const int kt = kt_b + u;
         const int rows = min(si.len_k - kt * BN, BN);
-        const unsigned bytes = (unsigned)(rows * kstride * sizeof(T));
         char* buf = buf_of(u);
-        kvcopy.issue(rsrc_words(kg + (long long)kt * BN * kstride, bytes), buf + C::BUF_K, w);
-        kvcopy.issue(rsrc_words(vg + (long long)kt * BN * kstride, bytes), buf + C::BUF_V, w);
+        kcopy.issue(rsrc_words(kg + (long long)kt * BN * a.sk.r, (unsigned)(rows * a.sk.r * (long long)sizeof(T))),
+                    buf + C::BUF_K, w);
+        vcopy.issue(rsrc_words(vg + (long long)kt * BN * a.sv.r, (unsigned)(rows * a.sv.r * (long long)sizeof(T))),
+                    buf + C::BUF_V, w);
     };
 
     // ---- this lane's query row: Q and dO rows as MFMA B operands, LSE and D
@@ -196,12 +199,15 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     const bool row_ok = i < si.len_q;
     op_t qreg[C::NC], doreg[C::NC];
     {
-        const T* qg = reinterpret_cast<const T*>(a.q) + ((long long)(si.q0 + i) * a.hq + hq) * HD;
-        const T* dog = reinterpret_cast<const T*>(a.dout) + ((long long)(si.q0 + i) * a.hq + hq) * HD;
+        const T* qg = reinterpret_cast<const T*>(a.q) + seq_off(a.sq, varlen, b, si.q0) + (long long)hq * a.sq.h +
+                      (long long)i * a.sq.r;
+        const T* dog = reinterpret_cast<const T*>(a.dout) + seq_off(a.sdo, varlen, b, si.q0) +
+                       (long long)hq * a.sdo.h + (long long)i * a.sdo.r;
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) {
-            qreg[c] = dq_load_global<T>(qg + 16 * c + 8 * h, row_ok);
-            doreg[c] = dq_load_global<T>(dog + 16 * c + 8 * h, row_ok);
+            const bool ok = row_ok && 16 * c + 8 * h < a.d;
+            qreg[c] = dq_load_global<T>(qg + 16 * c + 8 * h, ok);
+            doreg[c] = dq_load_global<T>(dog + 16 * c + 8 * h, ok);
         }
     }
     const long long row0 = varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
@@ -313,19 +319,17 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     // ---- write this tile's dQ rows once: scaled and converted into dq, or
     // unscaled into the accumulator (the postprocess applies s)
     if (a.dq_out != nullptr) {
-        const long long ostride = (long long)a.hq * HD;
-        T* o = reinterpret_cast<T*>(a.dq_out) + ((long long)(si.q0 + i0 + 32 * w) * a.hq + hq) * HD;
+        const long long ostride = a.sdq.r;
+        T* o = reinterpret_cast<T*>(a.dq_out) + seq_off(a.sdq, varlen, b, si.q0) + (long long)hq * a.sdq.h +
+               (long long)(i0 + 32 * w) * ostride;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = acc_row(v, h);
-                float y;
-                {
-#pragma clang fp contract(off)
-                    y = dq[d][v] * a.dq_scale;   // rounded to fp32, then to T
-                }
-                if (i0 + 32 * w + r < si.len_q) store_elem(o, (long long)r * ostride + 32 * d + l32, y);
+                const float y = mul_f32(dq[d][v], a.dq_scale);   // rounded to fp32, then to T
+                if (i0 + 32 * w + r < si.len_q && 32 * d + l32 < a.d)
+                    store_elem(o, (long long)r * ostride + 32 * d + l32, y);
             }
         }
         return;

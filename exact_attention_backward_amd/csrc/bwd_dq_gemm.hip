@@ -122,20 +122,23 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
         n_first = min(n_first, first_block(lq));
     }
 
-    const long long kstride = (long long)a.hkv * HD;
-    const char* kbytes = reinterpret_cast<const char*>(a.k) + ((long long)si.k0 * kstride + (long long)hkv * HD) * 2;
+    const long long kstride = a.sk.r;   // elements between K rows
+    const char* kbytes = reinterpret_cast<const char*>(a.k) +
+                         (seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h) * 2;
     const char* dsb = reinterpret_cast<const char*>(a.ds) + ((long long)hq * a.ds_qb + qb0 + lq0) * a.ds_nn * kDsBlockBytes;
     const long long blk_stride = (long long)a.ds_nn * kDsBlockBytes;   // next 32-row block
 
     const unsigned lds0 = lds_addr(smem);
-    // K copy plan: instruction t of wave w fills LDS segment w + 4t of a stage
+    // K copy plan: instruction t of wave w fills LDS segment w + 4t of a
+    // stage; chunks past the head dim read zeros
     int kvoff[C::KOPS];
 #pragma unroll
     for (int t = 0; t < C::KOPS; ++t) {
         constexpr int CPR = C::ROWB / 16;
         const int sl = (w + t * kGWaves) * 64 + lane;
         const int r = sl / CPR;
-        kvoff[t] = r * (int)(kstride * 2) + ((sl % CPR) ^ swz_key<C::ROWB>(r)) * 16;
+        const int c = (sl % CPR) ^ swz_key<C::ROWB>(r);
+        kvoff[t] = c * 8 < a.d ? r * (int)(kstride * 2) + c * 16 : kOobOff;
     }
     // stage u holds keys BS u .. BS u + BS - 1 (part hf = u % SPB of key block
     // u / SPB) and the matching parts of every wave's dS blocks (zeros for a
@@ -226,22 +229,20 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     // ---- this wave's dQ rows, written once: scaled and converted into dq,
     // or unscaled into the accumulator (the postprocess applies s)
     if (a.dq_out != nullptr) {
-        const long long ostride = (long long)a.hq * HD;
+        const long long ostride = a.sdq.r;
 #pragma unroll
         for (int r = 0; r < kGRB; ++r) {
             const int r0 = (lq0 + r) * kDsRows;
-            T* o = reinterpret_cast<T*>(a.dq_out) + ((long long)(si.q0 + r0) * a.hq + hq) * HD;
+            T* o = reinterpret_cast<T*>(a.dq_out) + seq_off(a.sdq, varlen, b, si.q0) + (long long)hq * a.sdq.h +
+                   (long long)r0 * ostride;
 #pragma unroll
             for (int d = 0; d < C::NDB; ++d) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int rr = acc_row(v, h);
-                    float y;
-                    {
-#pragma clang fp contract(off)
-                        y = acc[r][d][v] * a.dq_scale;   // rounded to fp32, then to T
-                    }
-                    if (r0 + rr < si.len_q) store_elem(o, (long long)rr * ostride + 32 * d + l32, y);
+                    const float y = mul_f32(acc[r][d][v], a.dq_scale);   // rounded to fp32, then to T
+                    if (r0 + rr < si.len_q && 32 * d + l32 < a.d)
+                        store_elem(o, (long long)rr * ostride + 32 * d + l32, y);
                 }
             }
         }

@@ -167,13 +167,15 @@ struct TileCopy {
     static constexpr int N = NROWS * CPR / 64 / WAVES;
     static_assert(NROWS * CPR % (64 * WAVES) == 0, "segment split");
     int voff[N];
-    __device__ __forceinline__ void init(int w, int lane, int stride_bytes) {
+    // stride_bytes: between rows in memory; valid: 16-byte chunks of a row
+    // inside the head dim (the others read zeros)
+    __device__ __forceinline__ void init(int w, int lane, int stride_bytes, int valid) {
 #pragma unroll
         for (int t = 0; t < N; ++t) {
             const int slot = (w + t * WAVES) * 64 + lane;
             const int r = slot / CPR;
             const int c = (slot % CPR) ^ swz_key<ROWB>(r);
-            voff[t] = r * stride_bytes + c * 16;
+            voff[t] = c < valid ? r * stride_bytes + c * 16 : kOobOff;
         }
     }
     __device__ __forceinline__ void issue(rsrc_t src, char* lds, int w) const {
@@ -255,10 +257,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
     const int nblk_k = (si.len_k + kBN - 1) / kBN;
 
-    const long long kstride = (long long)a.hkv * HD;
-    const long long qstride = (long long)a.hq * HD;
-    const T* kg = reinterpret_cast<const T*>(a.k) + (long long)si.k0 * kstride + (long long)hkv * HD;
-    const T* vg = reinterpret_cast<const T*>(a.v) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    const T* kg = reinterpret_cast<const T*>(a.k) + seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h;
+    const T* vg = reinterpret_cast<const T*>(a.v) + seq_off(a.sv, varlen, b, si.k0) + (long long)hkv * a.sv.h;
+    const int valid = a.d * (int)sizeof(T) / 16;   // 16-byte chunks of a row inside the head dim
     char* lk = smem + C::OFF_K;
     char* lds_ds = smem + C::OFF_DS;
 
@@ -268,15 +269,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     auto lse_base = [&](int hq) -> long long {
         return varlen ? (long long)hq * a.total_q + si.q0 : ((long long)b * a.hq + hq) * a.seqlen_q;
     };
-    TileCopy<C::ROWB, BM> qcopy;
-    qcopy.init(w, lane, (int)(qstride * sizeof(T)));
+    TileCopy<C::ROWB, BM> qcopy, docopy;
+    qcopy.init(w, lane, (int)(a.sq.r * (long long)sizeof(T)), valid);
+    docopy.init(w, lane, (int)(a.sdo.r * (long long)sizeof(T)), valid);
+    const long long q_seq = seq_off(a.sq, varlen, b, si.q0), do_seq = seq_off(a.sdo, varlen, b, si.q0);
     auto issue_tile = [&](int t, char* buf) {
         const int hq = tile_head(t), i0 = tile_row0(t);
         const int rows = min(si.len_q - i0, BM);
-        const long long row_elem = ((long long)(si.q0 + i0) * a.hq + hq) * HD;
-        const unsigned bytes = (unsigned)(rows * qstride * sizeof(T));
-        qcopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.q) + row_elem, bytes), buf + C::BUF_Q, w);
-        qcopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.dout) + row_elem, bytes), buf + C::BUF_DO, w);
+        const long long q_elem = q_seq + (long long)hq * a.sq.h + (long long)i0 * a.sq.r;
+        const long long do_elem = do_seq + (long long)hq * a.sdo.h + (long long)i0 * a.sdo.r;
+        qcopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.q) + q_elem,
+                                         (unsigned)(rows * a.sq.r * (long long)sizeof(T))), buf + C::BUF_Q, w);
+        docopy.issue_untracked(rsrc_words(reinterpret_cast<const T*>(a.dout) + do_elem,
+                                          (unsigned)(rows * a.sdo.r * (long long)sizeof(T))), buf + C::BUF_DO, w);
         const long long lb = lse_base(hq) + i0;
         if (w == 0 && lane < BM) dma_to_lds4(rsrc_words(a.lse + lb, rows * 4), lds_addr(buf + C::BUF_LSE), lane * 4);
         if (w == 1 && lane < BM) dma_to_lds4(rsrc_words(a.delta + lb, rows * 4), lds_addr(buf + C::BUF_DL), lane * 4);
@@ -286,9 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     if (n_tiles > 0) issue_tile(0, smem + C::OFF_BUF);
     if constexpr (DQ_ATOMIC) {
         TileCopy<C::ROWB, kBN> kcopy;
-        kcopy.init(w, lane, (int)(kstride * sizeof(T)));
+        kcopy.init(w, lane, (int)(a.sk.r * (long long)sizeof(T)), valid);
         const int rows = min(si.len_k - n * kBN, kBN);
-        kcopy.issue(make_rsrc(kg + (long long)n * kBN * kstride, (unsigned)(rows * kstride * sizeof(T))), lk, w);
+        kcopy.issue(make_rsrc(kg + (long long)n * kBN * a.sk.r, (unsigned)(rows * a.sk.r * (long long)sizeof(T))), lk,
+                    w);
     }
     op_t kreg[C::NC], vreg[C::NC];
     {
@@ -296,8 +302,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         const bool ok = j < si.len_k;
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) {
-            kreg[c] = load_op_global<T>(kg + (long long)j * kstride + 16 * c + 8 * h, ok);
-            vreg[c] = load_op_global<T>(vg + (long long)j * kstride + 16 * c + 8 * h, ok);
+            const int col = 16 * c + 8 * h;   // first of this lane's 8 columns of chunk c
+            kreg[c] = load_op_global<T>(kg + (long long)j * a.sk.r + col, ok && col < a.d);
+            vreg[c] = load_op_global<T>(vg + (long long)j * a.sv.r + col, ok && col < a.d);
         }
     }
     wait_vmem();
@@ -541,17 +548,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
     }
 
     // ---- epilogue: dK = s * sum dS^T Q, dV; rows past the sequence are not written
-    T* dkg = reinterpret_cast<T*>(a.dk) + (long long)si.k0 * kstride + (long long)hkv * HD;
-    T* dvg = reinterpret_cast<T*>(a.dv) + (long long)si.k0 * kstride + (long long)hkv * HD;
+    T* dkg = reinterpret_cast<T*>(a.dk) + seq_off(a.sdk, varlen, b, si.k0) + (long long)hkv * a.sdk.h;
+    T* dvg = reinterpret_cast<T*>(a.dv) + seq_off(a.sdv, varlen, b, si.k0) + (long long)hkv * a.sdv.h;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int jj = n * kBN + 32 * w + acc_row(v, h);
-            if (jj < si.len_k) {
-                const long long idx = (long long)jj * kstride + 32 * d + l32;
-                store_elem(dkg, idx, dk[d][v] * a.scale);
-                store_elem(dvg, idx, dv[d][v]);
+            if (jj < si.len_k && 32 * d + l32 < a.d) {
+                store_elem(dkg, (long long)jj * a.sdk.r + 32 * d + l32, dk[d][v] * a.scale);
+                store_elem(dvg, (long long)jj * a.sdv.r + 32 * d + l32, dv[d][v]);
             }
         }
     }
@@ -598,12 +604,13 @@ struct KvCfg {
     static constexpr int NBUF = 4;                   // ring of query-side tile buffers
     static constexpr int PD = NBUF - 2;              // prefetch distance in tiles
     static constexpr int BUF_Q = 0, BUF_DO = TILE, BUF_LSE = 2 * TILE, BUF_DL = 2 * TILE + 256;
-    static constexpr int BUF_BYTES = 2 * TILE + 512;
+    static constexpr int BUF_DUMP = 2 * TILE + 512;   // target of the empty statistic copies
+    static constexpr int BUF_BYTES = 2 * TILE + 768;
     static constexpr int NMB = BM / 32;              // 32-row blocks of a query tile
     static constexpr int PSLOT = NMB * 16 * 64 * 4;  // P of one pair: 16 fp32 per lane per row block
     static constexpr int OFF_P = NBUF * BUF_BYTES;   // [pair][tile parity] P slots
-    static constexpr int OFF_DUMP = OFF_P + 4 * 2 * PSLOT;   // target of the empty copies
-    static constexpr int LDS_BYTES = OFF_DUMP + 256;
+    static constexpr int OFF_CONST = OFF_P + 4 * 2 * PSLOT;   // 16 bytes per wave, see kv_tile
+    static constexpr int LDS_BYTES = OFF_CONST + kKvWaves * 16;
     static constexpr int NC = HD / 16;               // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;              // 32-column blocks of the head dim
     static constexpr int NIC = BM / 16;              // 16-wide chunks of the query rows
@@ -645,9 +652,13 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     const int n_m = max(m_end - m_begin, 0);
     const int n_tiles = G * n_m;            // (q-head, query tile) pairs, q-head major
 
-    const long long kstride = (long long)a.hkv * HD;
-    const long long qstride = (long long)a.hq * HD;
-    const long long kv_base = (long long)si.k0 * kstride + (long long)hkv * HD;
+    // this wave's K (P wave) or V (dS wave) rows, and the dV (P wave) or dK
+    // (dS wave) rows it writes: element offsets of the kv-head's first row
+    // and the row strides
+    const Strides& s_in = role == 0 ? a.sk : a.sv;
+    const long long in_base = seq_off(s_in, varlen, b, si.k0) + (long long)hkv * s_in.h;
+    const Strides& s_out = role == 0 ? a.sdv : a.sdk;
+    const long long out_base = seq_off(s_out, varlen, b, si.k0) + (long long)hkv * s_out.h;
 
     // ---- per-lane LDS offsets, fixed for the whole kernel
     const unsigned lds0 = lds_addr(smem);
@@ -664,55 +675,73 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     const int pslots = C::OFF_P + pair * 2 * C::PSLOT;
 
     // ---- copies: this wave's 1 KiB segment of the Q and dO tiles, then LSE
-    // (wave 0), D (wave 1) or an empty copy (the others)
-    const int seg_voff = [&] {
+    // (wave 0), D (wave 1) or an empty copy (the others).  Row strides in
+    // bytes; chunks past the head dim read zeros.
+    const int qrow_b = (int)(a.sq.r * (long long)sizeof(T)), dorow_b = (int)(a.sdo.r * (long long)sizeof(T));
+    int seg_voff_q, seg_voff_do;
+    {
         constexpr int CPR = ROWB / 16;
         const int slot = w * 64 + lane;
         const int r = slot / CPR;
-        return r * (int)(qstride * sizeof(T)) + ((slot % CPR) ^ swz_key<ROWB>(r)) * 16;
-    }();
-    const long long tile_step = (long long)BM * qstride * (long long)sizeof(T);   // bytes between query tiles
-    const long long lse_head = (long long)(varlen ? a.total_q : a.seqlen_q) * 4;  // bytes between heads
-    const long long q_g0 = ((long long)(si.q0 + m_begin * BM) * a.hq + (long long)hkv * G) * HD * (long long)sizeof(T);
-    const long long l_g0 =
+        const int c = (slot % CPR) ^ swz_key<ROWB>(r);
+        const bool ok = c * 16 < a.d * (int)sizeof(T);
+        seg_voff_q = ok ? r * qrow_b + c * 16 : kOobOff;
+        seg_voff_do = ok ? r * dorow_b + c * 16 : kOobOff;
+    }
+    // bytes between q-heads (the ABI keeps head strides below 2 GiB), needed
+    // once per n_m tiles: each wave parks them in its own LDS slot and reads
+    // them back at a head change, so they do not occupy scalar registers
+    // across the loops
+    char* wconst = smem + C::OFF_CONST + w * 16;
+    if (lane == 0) {
+        const u32x4 hb = {(unsigned)(a.sq.h * (long long)sizeof(T)), (unsigned)(a.sdo.h * (long long)sizeof(T)),
+                          (unsigned)(varlen ? a.total_q : a.seqlen_q) * 4u, 0u};
+        *reinterpret_cast<u32x4*>(wconst) = hb;
+    }
+    // the group's first q-head, first query tile in Q, dO and LSE/D (this
+    // wave's statistic); the descriptors step from there one head at a time
+    const char* q_head = reinterpret_cast<const char*>(a.q) +
+                         (seq_off(a.sq, varlen, b, si.q0) + (long long)m_begin * BM * a.sq.r +
+                          (long long)hkv * G * a.sq.h) * (long long)sizeof(T);
+    const char* do_head = reinterpret_cast<const char*>(a.dout) +
+                          (seq_off(a.sdo, varlen, b, si.q0) + (long long)m_begin * BM * a.sdo.r +
+                           (long long)hkv * G * a.sdo.h) * (long long)sizeof(T);
+    const char* l_head =
+        (w == 0 ? reinterpret_cast<const char*>(a.lse) : reinterpret_cast<const char*>(a.delta)) +
         ((varlen ? (long long)hkv * G * a.total_q + si.q0 : ((long long)b * a.hq + (long long)hkv * G) * a.seqlen_q) +
          m_begin * BM) * 4;
-    const char* qbytes = reinterpret_cast<const char*>(a.q);
-    const char* dobytes = reinterpret_cast<const char*>(a.dout);
-    const char* sbytes = w == 0 ? reinterpret_cast<const char*>(a.lse) : reinterpret_cast<const char*>(a.delta);
     // issue cursor: the next tile to copy.  The descriptors point at the
     // current q-head's first tile; a tile's offset from there goes into the
-    // scalar offset, and the range word ends at the tile's last valid row,
-    // so a step only updates two offsets and two range words.
-    int is_t = 0, is_m = m_begin, is_g = 0;
-    int is_so = 0, is_lo = 0;   // byte offsets of the tile from the head's first tile (Q/dO, LSE/D)
-    const int full_q = (int)(BM * qstride * (long long)sizeof(T));
-    const int last_rows = min(si.len_q - (m_end - 1) * BM, BM);   // rows of the last query tile
-    i32x4 rq = rsrc_words(qbytes + q_g0, 0), rdo = rsrc_words(dobytes + q_g0, 0), rs = rsrc_words(sbytes + l_g0, 0);
-    const unsigned sdst0 = w == 0 ? lds0 + C::BUF_LSE : w == 1 ? lds0 + C::BUF_DL : lds0 + C::OFF_DUMP;
-    const unsigned sstep = w < 2 ? 1u : 0u;   // the empty copies all land in the one dump slot
-    auto issue_next = [&](unsigned is_buf) {   // is_buf: ring offset of the tile's buffer
-        const int rows = is_t < n_tiles ? (is_m == m_end - 1 ? last_rows : BM) : 0;
-        // the range check covers scalar + per-lane offset: the range is the
-        // tile's offset plus its valid bytes
-        rq[2] = rdo[2] = __builtin_amdgcn_readfirstlane(is_so + rows * (int)(qstride * (long long)sizeof(T)));
-        rs[2] = __builtin_amdgcn_readfirstlane(w < 2 ? is_lo + rows * 4 : 0);
-        const unsigned dst = lds0 + is_buf;
-        dma_to_lds16_so(rq, dst + C::BUF_Q + w * 1024, seg_voff, is_so);
-        dma_to_lds16_so(rdo, dst + C::BUF_DO + w * 1024, seg_voff, is_so);
-        dma_to_lds4_so(rs, sdst0 + sstep * is_buf, lane * 4, is_lo);
+    // scalar offset.  The range word (which the scalar offset counts against)
+    // ends at the sequence's last row, the same for every head, so rows past
+    // the sequence read zeros; the empty copies past the last tile take a
+    // scalar offset past every range.
+    int is_t = 0, is_m = m_begin;
+    const int full_q = BM * qrow_b, full_do = BM * dorow_b;   // bytes between query tiles
+    const int rows_left = max(si.len_q - m_begin * BM, 0);   // rows from the first tile to the sequence end
+    i32x4 rq = rsrc_words(q_head, (unsigned)(rows_left * qrow_b));
+    i32x4 rdo = rsrc_words(do_head, (unsigned)(rows_left * dorow_b));
+    i32x4 rs = rsrc_words(l_head, w < 2 ? (unsigned)rows_left * 4u : 0u);
+    // LDS bases of this wave's copies: its 1 KiB segment of the Q tile (dO
+    // follows at a constant distance) and its statistic slot (LSE, D, or the
+    // dump slot of the other waves); a buffer's ring offset is an immediate
+    const unsigned seg_base = lds0 + C::BUF_Q + w * 1024;
+    const unsigned stat_base = lds0 + (w == 0 ? C::BUF_LSE : w == 1 ? C::BUF_DL : C::BUF_DUMP);
+    auto issue_next = [&](auto iss_c) {   // iss_c: ring offset of the tile's buffer (a constant)
+        constexpr unsigned ISB = decltype(iss_c)::value;
+        const bool live = is_t < n_tiles;
+        const int rel = is_m - m_begin;   // the tile's offset from the head's first tile, in tiles
+        dma_to_lds16_at<ISB>(rq, seg_base, seg_voff_q, live ? rel * full_q : kOobOff);
+        dma_to_lds16_at<ISB + C::BUF_DO - C::BUF_Q>(rdo, seg_base, seg_voff_do, live ? rel * full_do : kOobOff);
+        dma_to_lds4_at<ISB>(rs, stat_base, lane * 4, live ? rel * (BM * 4) : kOobOff);
         ++is_t;
         if (++is_m == m_end) {
             is_m = m_begin;
-            ++is_g;
-            is_so = 0;
-            is_lo = 0;
-            rq = rsrc_words(qbytes + q_g0 + (long long)is_g * HD * (long long)sizeof(T), 0);
-            rdo = rsrc_words(dobytes + q_g0 + (long long)is_g * HD * (long long)sizeof(T), 0);
-            rs = rsrc_words(sbytes + l_g0 + is_g * lse_head, 0);
-        } else {
-            is_so += full_q;
-            is_lo += BM * 4;
+            // the next q-head (once per n_m tiles)
+            const u32x4 hb = *reinterpret_cast<const u32x4*>(wconst);
+            rsrc_advance(rq, __builtin_amdgcn_readfirstlane(hb[0]));
+            rsrc_advance(rdo, __builtin_amdgcn_readfirstlane(hb[1]));
+            rsrc_advance(rs, __builtin_amdgcn_readfirstlane(hb[2]));
         }
     };
 
@@ -720,15 +749,17 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // or V (dS wave) rows as B operands.  The wait for all of them here tells
     // the compiler that the K/V registers are ready; otherwise it would wait
     // for them (vmcnt(0), the prefetches included) inside the loop.
-#pragma unroll
-    for (int t = 0; t < C::PD; ++t) issue_next(t * C::BUF_BYTES);
+    static_assert(C::PD == 2, "the prologue issues two tiles");
+    issue_next(std::integral_constant<unsigned, 0>{});
+    issue_next(std::integral_constant<unsigned, C::BUF_BYTES>{});
     op_t wreg[C::NC];
     {
-        const T* src = reinterpret_cast<const T*>(role == 0 ? a.k : a.v) + kv_base;
+        const T* src = reinterpret_cast<const T*>(role == 0 ? a.k : a.v) + in_base;
         const int j = n * kBN + 32 * pair + l32;
         const bool ok = j < si.len_k;
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) wreg[c] = load_op_global<T>(src + (long long)j * kstride + 16 * c + 8 * h, ok);
+        for (int c = 0; c < C::NC; ++c)
+            wreg[c] = load_op_global<T>(src + (long long)j * s_in.r + 16 * c + 8 * h, ok && 16 * c + 8 * h < a.d);
     }
     // ALiBi: lane g holds the slope of the group's q-head g (groups of up to
     // 64 q-heads; larger ones read the slope per tile)
@@ -837,7 +868,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             __builtin_amdgcn_sched_group_barrier(0x100, NMB * C::NC, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NMB * C::NC, 0);
         }
-        issue_next(ISS);
+        issue_next(std::integral_constant<unsigned, ISS>{});
         const int tile_m = cur_m, tile_g = cur_g;   // coordinates of tile t
         const char* ds_prev = ds_last;              // dS blocks of tile t-1
         if (STORE_DS) ds_last = ds_cur;
@@ -1049,14 +1080,14 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 
     // ---- epilogue: dV (P wave) or dK = s * sum dS^T Q (dS wave); rows past
     // the sequence are not written
-    T* dst = reinterpret_cast<T*>(role == 0 ? a.dv : a.dk) + kv_base;
+    T* dst = reinterpret_cast<T*>(role == 0 ? a.dv : a.dk) + out_base;
     const float f = role == 0 ? 1.f : a.scale;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int jj = n * kBN + 32 * pair + acc_row(v, h);
-            if (jj < si.len_k) store_elem(dst, (long long)jj * kstride + 32 * d + l32, acc[d][v] * f);
+            if (jj < si.len_k && 32 * d + l32 < a.d) store_elem(dst, (long long)jj * s_out.r + 32 * d + l32, acc[d][v] * f);
         }
     }
 }

@@ -161,6 +161,11 @@ __device__ __forceinline__ void lds_write(char* lds_base, int byte_off, const V&
 // that should end at a tile's last valid byte includes the scalar offset.
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// A per-lane buffer offset past every range the kernels build (the ranges,
+// scalar offsets included, stay below it): the lane's load returns zeros.
+// It fills the tile columns past the head dim.
+constexpr int kOobOff = 0x7FFFFFF0;
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
@@ -196,6 +201,14 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
                __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
     return r;
 }
+// Move a descriptor's base address by `bytes` (the 48-bit address of words
+// 0-1; the stride field above it is zero and an address never carries into it).
+__device__ __forceinline__ void rsrc_advance(i32x4& r, unsigned bytes) {
+    const unsigned long long base =
+        (((unsigned long long)(unsigned)r[1] << 32) | (unsigned)r[0]) + (unsigned long long)bytes;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)base);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(base >> 32));
+}
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(size_t)((__attribute__((address_space(3))) const char*)p));
 }
@@ -219,6 +232,21 @@ __device__ __forceinline__ void dma_to_lds16_so(i32x4 r, unsigned lds, int voff,
 __device__ __forceinline__ void dma_to_lds4_so(i32x4 r, unsigned lds, int voff, int soff) {
     asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory");
+}
+// The scalar-offset copies to an LDS address given as an SGPR base plus a
+// constant.  The base passes through an empty asm at every call, so the
+// compiler cannot precompute base + OFF for each ring buffer of an unrolled
+// loop and keep all those addresses live; the add itself stays visible to
+// it (it writes SCC).
+template <unsigned OFF>
+__device__ __forceinline__ void dma_to_lds16_at(i32x4 r, unsigned base, int voff, int soff) {
+    asm volatile("" : "+s"(base));
+    dma_to_lds16_so(r, base + OFF, voff, soff);
+}
+template <unsigned OFF>
+__device__ __forceinline__ void dma_to_lds4_at(i32x4 r, unsigned base, int voff, int soff) {
+    asm volatile("" : "+s"(base));
+    dma_to_lds4_so(r, base + OFF, voff, soff);
 }
 __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");

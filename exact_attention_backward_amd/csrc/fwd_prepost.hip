@@ -35,15 +35,20 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     const int i = qb * BQ + threadIdx.x;
     const bool row_ok = i < si.len_q;
     const int off = si.len_k - si.len_q;
+    const bool varlen = a.cu_q != nullptr;
     const T* qp = reinterpret_cast<const T*>(a.q);
     const T* kp = reinterpret_cast<const T*>(a.k);
     const T* vp = reinterpret_cast<const T*>(a.v);
+    const long long qrow = seq_off(a.sq, varlen, b, si.q0) + (long long)hq * a.sq.h + (long long)i * a.sq.r;
+    const long long kbase = seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h;
+    const long long vbase = seq_off(a.sv, varlen, b, si.k0) + (long long)hkv * a.sv.h;
 
+    // columns from a.d on are zero (the head dim padded to HD)
     float q[HD], o[HD];
     const float qs = a.scale * kLog2e;
 #pragma unroll
     for (int d = 0; d < HD; ++d) {
-        q[d] = row_ok ? (float)load_elem(qp, ((long long)(si.q0 + i) * a.hq + hq) * HD + d) * qs : 0.f;
+        q[d] = row_ok && d < a.d ? (float)load_elem(qp, qrow + d) * qs : 0.f;
         o[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -62,9 +67,9 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
         __syncthreads();
         for (int e = threadIdx.x; e < BK * HD; e += blockDim.x) {
             const int jj = e / HD, d = e % HD, j = kt + jj;
-            const long long g = ((long long)(si.k0 + j) * a.hkv + hkv) * HD + d;
-            ks[jj][d] = j < si.len_k ? (float)load_elem(kp, g) : 0.f;
-            vs[jj][d] = j < si.len_k ? (float)load_elem(vp, g) : 0.f;
+            const bool ok = j < si.len_k && d < a.d;
+            ks[jj][d] = ok ? (float)load_elem(kp, kbase + (long long)j * a.sk.r + d) : 0.f;
+            vs[jj][d] = ok ? (float)load_elem(vp, vbase + (long long)j * a.sv.r + d) : 0.f;
         }
         __syncthreads();
         float s[BK];
@@ -99,10 +104,11 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     if (!row_ok) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     T* op = reinterpret_cast<T*>(a.o);
-    const long long ob = ((long long)(si.q0 + i) * a.hq + hq) * HD;
+    const long long ob = seq_off(a.so, varlen, b, si.q0) + (long long)hq * a.so.h + (long long)i * a.so.r;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) store_elem(op, ob + d, o[d] * inv);
-    const bool varlen = a.cu_q != nullptr;
+    for (int d = 0; d < HD; ++d) {
+        if (d < a.d) store_elem(op, ob + d, o[d] * inv);
+    }
     const long long li = varlen ? (long long)hq * a.total_q + si.q0 + i
                                 : ((long long)b * a.hq + hq) * a.seqlen_q + i;
     a.lse[li] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
@@ -127,13 +133,20 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
     const int h = (int)(blockIdx.x % (unsigned)a.h);
     const long long r0 = (long long)(blockIdx.x / (unsigned)a.h) * kPreTokens;
     const int part = threadIdx.x % LPR, slot = threadIdx.x / LPR;
+    const bool live = part * 8 < a.d;   // this lane's 8 columns lie within the head dim
     float x[PASSES][8], y[PASSES][8];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const long long r = min(r0 + p * RPP + slot, tokens - 1);
-        const long long e = (r * a.h + h) * HD + part * 8;
-        load8(reinterpret_cast<const T*>(a.o) + e, x[p]);
-        load8(reinterpret_cast<const T*>(a.dout) + e, y[p]);
+        if (live) {
+            load8(reinterpret_cast<const T*>(a.o) + flat_row_off(a.so, a.varlen, r, a.s) + (long long)h * a.so.h +
+                      part * 8, x[p]);
+            load8(reinterpret_cast<const T*>(a.dout) + flat_row_off(a.sdo, a.varlen, r, a.s) +
+                      (long long)h * a.sdo.h + part * 8, y[p]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[p][t] = y[p][t] = 0.f;
+        }
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -182,18 +195,15 @@ __global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
         const int len = min(a.cu_q[lo + 1] - a.cu_q[lo], max(a.used_q[lo], 0));
         if (r >= (long long)a.cu_q[lo] + len) return;
     }
+    if (part * 8 >= a.d) return;   // padding columns of the accumulator
     const float* src = a.acc + lse_index(a.varlen, r, h, a.h, a.s, a.total) * HD + part * 8;
     const f32x4 u = *reinterpret_cast<const f32x4*>(src);
     const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4);
     float x[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
-    {
-        // the product is rounded to fp32 before the conversion to T: no
-        // fused multiply-and-convert (v_fma_mix) for fp16
-#pragma clang fp contract(off)
+    // the product is rounded to fp32 before the conversion to T
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] *= a.scale;
-    }
-    store8(reinterpret_cast<T*>(a.dq) + row * HD + part * 8, x);
+    for (int t = 0; t < 8; ++t) x[t] = mul_f32(x[t], a.scale);
+    store8(reinterpret_cast<T*>(a.dq) + flat_row_off(a.sdq, a.varlen, r, a.s) + (long long)h * a.sdq.h + part * 8, x);
 }
 
 // ---------------------------------------------------------------------------

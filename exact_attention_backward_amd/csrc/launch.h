@@ -6,6 +6,24 @@
 
 namespace attn {
 
+// Element strides of one tensor: between batch entries (dense layouts only),
+// rows (tokens) and heads; the head dimension is contiguous.
+struct Strides {
+    long long b, r, h;
+};
+
+// Offset of a sequence's first row: its batch entry (dense) or its packed
+// first row q0 (varlen).
+__host__ __device__ __forceinline__ long long seq_off(const Strides& s, bool varlen, int b, int q0) {
+    return varlen ? (long long)q0 * s.r : (long long)b * s.b;
+}
+// Offset of flattened row r (b * S + i dense, the packed row varlen).
+__host__ __device__ __forceinline__ long long flat_row_off(const Strides& s, bool varlen, long long r, int S) {
+    if (varlen) return r * s.r;
+    const long long b = r / S;
+    return b * s.b + (r - b * S) * s.r;
+}
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -20,6 +38,8 @@ struct FwdArgs {
     float scale;
     int win_lo, win_hi;      // visibility: i + off - win_lo <= j <= i + off + win_hi
     const float* alibi;      // per q-head ALiBi slopes, or null
+    int d;                   // head dim (the kernels' HD is this rounded up to 64 or 128)
+    Strides sq, sk, sv, so;
 };
 
 struct PreArgs {
@@ -30,6 +50,8 @@ struct PreArgs {
     int h, s;            // heads, dense sequence length
     long long total;     // varlen total rows
     bool varlen;
+    int d;               // head dim
+    Strides so, sdo;
 };
 
 struct PostArgs {
@@ -44,6 +66,8 @@ struct PostArgs {
     const int32_t* cu_q;
     const int32_t* used_q;
     int batch;
+    int d;               // head dim
+    Strides sdq;
 };
 
 struct BwdArgs {
@@ -76,6 +100,9 @@ struct BwdArgs {
     // the fp32 accumulator
     void* dq_out;
     float dq_scale;
+    int d;               // head dim (the kernels' HD is this rounded up to 64 or 128;
+                         // columns from d on are zero in every tile)
+    Strides sq, sk, sv, sdo, sdq, sdk, sdv;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
@@ -99,6 +126,16 @@ constexpr int kDsRows = 32;
 constexpr int kDsKeys = 128;
 constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
 __host__ __device__ constexpr int ds_chunk(int g, int l) { return g * 64 + (l ^ ((l >> 5) << 2)); }
+
+// x * s rounded to fp32 and held in a register, so that a following
+// conversion to fp16 rounds that fp32 value: the empty asm keeps the
+// compiler from fusing the multiply into a mixed-precision
+// multiply-and-convert (one rounding of the exact product instead of two).
+__device__ __forceinline__ float mul_f32(float x, float s) {
+    float y = x * s;
+    asm volatile("" : "+v"(y));
+    return y;
+}
 
 // An unbounded side of the visibility window (far beyond any sequence length).
 constexpr int kNoWindow = 1 << 29;

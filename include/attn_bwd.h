@@ -24,8 +24,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - All tensor pointers are DEVICE pointers, 16-byte aligned, contiguous,
- *    head dimension innermost.  The caller allocates and frees every buffer,
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, head
+ *    dimension innermost and contiguous; rows, heads and batch entries are
+ *    contiguous too unless shape->strides gives their strides.  The caller allocates and frees every buffer,
  *    the workspace included; the library never allocates, frees or
  *    synchronises.  Every call only enqueues work on `stream` (a hipStream_t,
  *    NULL = the default stream) and returns.
@@ -35,6 +36,9 @@
  *                LSE, D [B, Hq, Sq]
  *        varlen: Q, O, dO, dQ [total_q, Hq, D]; K, V, dK, dV [total_k, Hkv, D]
  *                LSE, D [Hq, total_q]
+ *    (index order; with shape->strides, element (b, i, h, d) of a dense
+ *    tensor sits at b * batch + i * row + h * head + d, and row r of a
+ *    varlen one at r * row + h * head + d).
  *    Varlen is selected by non-NULL cu_seqlens_q/cu_seqlens_k (device int32
  *    arrays of batch+1 nondecreasing offsets starting at 0 and ending at
  *    total_q/total_k); sequence b occupies rows [cu[b], cu[b+1]) and no
@@ -87,12 +91,13 @@ typedef enum attn_status {
     ATTN_ERR_BAD_SHAPE = 2,    /* non-positive size, Hq % Hkv != 0, causal/local not 0 or 1,
                                   window sizes below -1, varlen without both
                                   cu_seqlens, workspace too small, more than 2^27
-                                  (row, head) pairs in Q or K, 2 GiB or more of Q
-                                  in one sequence (seqlen_q x Hq x D elements), ... */
-    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not 64 or 128,
-                                  unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
-    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned (cu_seqlens,
-                                  seqused and alibi_slopes: 4-byte) */
+                                  (row, head) pairs in Q or K, a negative stride,
+                                  about 2 GiB or more of one sequence's rows of a
+                                  tensor (seqlen x row stride), ... */
+    ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not a multiple of 8 in
+                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
+    ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer or stride is not 16-byte aligned
+                                  (cu_seqlens, seqused and alibi_slopes: 4-byte) */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } attn_status_t;
 
@@ -125,6 +130,23 @@ typedef enum attn_dq_algo {
     ATTN_DQ_STORED_DS = 2
 } attn_dq_algo_t;
 
+/* Element strides of one tensor (FA3's (row, d, head, batch) tensor strides
+ * with d contiguous): between batch entries (dense layouts; ignored for
+ * varlen, whose rows are packed), between rows (tokens) and between heads.
+ * All non-negative and 16-byte multiples (8 elements for bf16/fp16, 4 for
+ * fp32). */
+typedef struct attn_tensor_strides {
+    int64_t batch;
+    int64_t row;
+    int64_t head;
+} attn_tensor_strides_t;
+
+/* Strides of every tensor the calls read or write (LSE and D are always
+ * contiguous).  Outputs must not overlap one another or the inputs. */
+typedef struct attn_strides {
+    attn_tensor_strides_t q, k, v, o, dout, dq, dk, dv;
+} attn_strides_t;
+
 /* Problem description, passed by pointer and only read.  Plain old data. */
 typedef struct attn_shape {
     int32_t batch;           /* dense batch B, or number of sequences when varlen */
@@ -132,7 +154,8 @@ typedef struct attn_shape {
     int32_t num_heads_kv;    /* Hkv, divides Hq */
     int32_t seqlen_q;        /* dense Sq, or the longest query sequence when varlen */
     int32_t seqlen_k;        /* dense Sk, or the longest key sequence when varlen */
-    int32_t head_dim;        /* D: 64 or 128 */
+    int32_t head_dim;        /* D: a multiple of 8, 8..128 (the kernels pad it with zeros
+                                to 64 or 128 and compute at that size) */
     int32_t total_q;         /* varlen only: rows of Q (= cu_seqlens_q[batch]) */
     int32_t total_k;         /* varlen only: rows of K (= cu_seqlens_k[batch]) */
     const int32_t* cu_seqlens_q;  /* device, [batch+1], or NULL for dense */
@@ -148,6 +171,8 @@ typedef struct attn_shape {
     int32_t window_left;     /* local: keys at most this many before the diagonal, -1 = any */
     int32_t window_right;    /* local: keys at most this many after the diagonal, -1 = any */
     const float* alibi_slopes;    /* device [num_heads_q] fp32 ALiBi slopes, or NULL for none */
+    const attn_strides_t* strides; /* HOST pointer, read during each call; NULL = the
+                                      contiguous layouts above */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -68,7 +68,8 @@ def test_workspace_size_formula():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=96), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=100), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=136), L.ATTN_ERR_UNSUPPORTED),
     (dict(head_dim=0), L.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), L.ATTN_ERR_UNSUPPORTED),
     (dict(num_heads_kv=3), L.ATTN_ERR_BAD_SHAPE),
@@ -103,6 +104,51 @@ def test_seqused_needs_varlen_and_alignment():
     s = shape(seqused_k=0x3000)
     rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
     assert rc == L.ATTN_ERR_BAD_SHAPE
+
+
+def test_head_dims_accepted_and_workspace_padded():
+    """Any multiple of 8 up to 128; the accumulator is sized for the padded
+    head dim (64 or 128)."""
+    for d, pad in ((8, 64), (40, 64), (64, 64), (72, 128), (96, 128), (128, 128)):
+        assert ws_bytes(shape(head_dim=d)) == ws_bytes(shape(head_dim=pad))
+
+
+def _strides(**over):
+    st = L.Strides()
+    for name in L.STRIDE_TENSORS:
+        x = getattr(st, name)
+        heads = 2 if name in ("k", "v", "dk", "dv") else 4
+        seq = 90 if name in ("k", "v", "dk", "dv") else 100
+        x.batch, x.row, x.head = seq * heads * 128, heads * 128, 128
+    for key, (b, r, h) in over.items():
+        x = getattr(st, key)
+        x.batch, x.row, x.head = b, r, h
+    return st
+
+
+def test_strides_validated():
+    fake = ctypes.c_void_p(0x1000)
+    lib = L.lib()
+
+    def call(st):
+        s = shape()
+        s.strides = ctypes.addressof(st)
+        return lib.attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+
+    def ws(st):
+        s = shape()
+        s.strides = ctypes.addressof(st)
+        return ws_bytes(s)
+
+    base = ws_bytes(shape())
+    # packed QKV rows (3 H D) and a head-major dO: accepted, same workspace
+    assert ws(_strides(q=(100 * 3 * 4 * 128, 3 * 4 * 128, 128), dout=(4 * 100 * 128, 128, 100 * 128))) == base
+    assert call(_strides(q=(-8, 512, 128))) == L.ATTN_ERR_BAD_SHAPE
+    assert call(_strides(dk=(8, -512, 128))) == L.ATTN_ERR_BAD_SHAPE
+    assert call(_strides(v=(100, 256, 128))) == L.ATTN_ERR_MISALIGNED     # batch stride not 16-byte aligned
+    assert call(_strides(dq=(0, 516, 128))) == L.ATTN_ERR_MISALIGNED      # row stride not 16-byte aligned
+    assert call(_strides(o=(0, 512, 132))) == L.ATTN_ERR_MISALIGNED       # head stride not 16-byte aligned
+    assert call(_strides(q=(0, 1 << 24, 128))) == L.ATTN_ERR_BAD_SHAPE    # a sequence's rows past 2 GiB
 
 
 def test_window_sizes_accepted():

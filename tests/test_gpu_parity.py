@@ -314,6 +314,7 @@ FULL_CASES = [
     (CASES[0], None, False),      # bf16 dense causal D128
     (CASES[3], None, False),      # bf16 Sq < Sk causal
     (CASES[9], None, False),      # bf16 varlen + GQA D64
+    (CASES[14], None, False),     # fp16 dense causal D128
     (CASES[15], None, False),     # fp16 Sq < Sk causal D64
     (CASES[17], None, False),     # fp16 varlen + GQA causal
     (CASES[11], None, False),     # fp32 Sq > Sk causal
@@ -355,6 +356,130 @@ def test_bwd_full_matches_three_calls_bitwise(fc, dq_algo):
     rdq, rdk, rdv = r.oracle_backward()
     for n, g, ref in (("dQ", full[0], rdq), ("dK", full[1], rdk), ("dV", full[2], rdv)):
         assert_close(n, to_host(g), ref, p.dtype)
+
+
+# head dims other than 64 and 128 (padded with zeros to 64 or 128 inside the kernels)
+HEADDIM_CASES = [
+    ("bf16", 1, 2, 2, 200, 200, 8, True, None),
+    ("bf16", 1, 3, 3, 150, 260, 40, False, None),
+    ("bf16", 2, 4, 2, 130, 130, 72, True, None),     # GQA
+    ("bf16", 1, 2, 2, 300, 300, 96, True, None),
+    ("f16", 1, 2, 2, 170, 170, 120, False, None),
+    ("f16", 0, 4, 2, 0, 0, 80, True, (7, 128, 129, 300)),   # varlen + GQA
+    ("f32", 1, 2, 2, 100, 150, 48, True, None),
+    ("f32", 1, 2, 2, 100, 100, 112, False, None),
+]
+
+
+@pytest.mark.parametrize("case", HEADDIM_CASES, ids=_id)
+def test_head_dim_forward_matches_oracle(case):
+    p = problem(case)
+    r = Run(p, oracle_o_lse=False)
+    print(f"head dim forward {_id(case)}", flush=True)
+    o, lse = r.gpu_forward()
+    torch.cuda.synchronize()
+    cq, ck = r.cu_np
+    ro, rlse = oracle.forward(r.x["q"], r.x["k"], r.x["v"], p.scale, p.causal, cq, ck)
+    assert_close("O", to_host(o), ro, p.dtype)
+    g = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.max(np.abs(g[fin] - rlse[fin]), initial=0) <= (1e-5 if p.dtype == "f32" else 1e-4)
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["three_calls", "bwd_full"])
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
+@pytest.mark.parametrize("case", HEADDIM_CASES, ids=_id)
+def test_head_dim_backward_matches_oracle(case, dq_algo, full):
+    if dq_algo == "stored_ds" and case[0] == "f32":
+        pytest.skip("the stored-dS mode is for 16-bit types only (the ABI rejects fp32)")
+    p = problem(case)
+    r = Run(p)
+    print(f"head dim backward {_id(case)} dq={dq_algo} full={full}", flush=True)
+    d = r.dev
+    plan = r.plan(dq_algo=dq_algo)
+    dq, dk, dv = (torch.full_like(d[n], 5.0) for n in ("q", "k", "v"))
+    (plan.run_full if full else plan.run)(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq, dk, dv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = r.oracle_backward()
+    for n, g, ref in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert_close(n, to_host(g), ref, p.dtype)
+
+
+# strided layouts: (dtype, B, H, S, D, varlen lengths) with packed QKV rows
+STRIDE_CASES = [
+    ("bf16", 2, 3, 260, 128, None),
+    ("bf16", 1, 4, 333, 64, None),
+    ("f16", 2, 2, 200, 72, None),
+    ("bf16", 0, 2, 0, 128, (1, 64, 300, 129)),
+    ("f32", 1, 2, 150, 64, None),
+]
+
+
+def _strideid(c):
+    dt, b, h, s, d, lens = c
+    return f"{dt}-{'lens' + '-'.join(map(str, lens)) if lens else f'b{b}s{s}'}-h{h}-d{d}"
+
+
+@pytest.mark.parametrize("dq_algo", ["stored_ds", "separate", "atomic"])
+@pytest.mark.parametrize("case", STRIDE_CASES, ids=_strideid)
+def test_strided_layouts_match_contiguous_bitwise(case, dq_algo):
+    """Q, K, V as views of one packed [.., S, 3, H, D] tensor, dO head-major
+    ([B, H, S, D] permuted), O in a row-padded buffer, dQ/dK/dV written into
+    a packed gradient tensor: every output equals the contiguous run's bit
+    for bit (the kernels only address differently), the padding and the
+    other slots of the packed outputs are untouched, and dQ/dK/dV match the
+    oracle."""
+    dt, b, h, s_len, d, lens = case
+    if dq_algo == "stored_ds" and dt == "f32":
+        pytest.skip("the stored-dS mode is for 16-bit types only (the ABI rejects fp32)")
+    causal = True
+    p = small_problem(dt, b, h, h, s_len, s_len, d, causal, 61, lengths=lens, deterministic=dq_algo == "atomic")
+    r = Run(p, oracle_o_lse=False)
+    print(f"strided {_strideid(case)} dq={dq_algo}", flush=True)
+    dev, kw = r.dev, r.kw()
+    varlen = lens is not None
+    # contiguous reference run
+    o_c, lse_c = api.forward(dev["q"], dev["k"], dev["v"], p.scale, causal, **kw)
+    plan_c = api.BackwardPlan(dev["q"], dev["k"], p.scale, causal, p.deterministic, dq_algo=dq_algo, **kw)
+    ref = [torch.empty_like(dev[n]) for n in ("q", "k", "v")]
+    plan_c.run_full(dev["q"], dev["k"], dev["v"], o_c, dev["do"], lse_c, *ref)
+    # strided copies of the same values
+    lead = dev["q"].shape[:-2]                 # (B, S) or (T,)
+    nl = len(lead)
+    qkv = torch.empty(*lead, 3, h, d, dtype=dev["q"].dtype, device="cuda")
+    for slot, n in enumerate(("q", "k", "v")):
+        qkv.select(nl, slot).copy_(dev[n])
+    q, k, v = (qkv.select(nl, slot) for slot in range(3))
+    do_hm = dev["do"].movedim(nl, 0).contiguous()   # [H, B, S, D] or [H, T, D]
+    do = do_hm.movedim(0, nl)
+    sentinel = -3.0
+    o_pad = torch.full((*lead, h, d + 8), sentinel, dtype=dev["q"].dtype, device="cuda")
+    o = o_pad[..., :d]
+    lse = torch.empty_like(lse_c)
+    api.forward(q, k, v, p.scale, causal, out=(o, lse), **kw)
+    dqkv = torch.full((*lead, 3, h, d), sentinel, dtype=dev["q"].dtype, device="cuda")
+    grads = [dqkv.select(nl, slot) for slot in range(3)]
+    plan = api.BackwardPlan(q, k, p.scale, causal, p.deterministic, dq_algo=dq_algo, **kw)
+    plan.run_full(q, k, v, o, do, lse, *grads)
+    torch.cuda.synchronize()
+    iview = torch.int16 if o_c.element_size() == 2 else torch.int32
+    assert torch.equal(o.contiguous().view(iview), o_c.view(iview))
+    assert torch.equal(lse, lse_c)
+    assert bool((o_pad[..., d:] == sentinel).all())
+    for n, g, c in zip(("dQ", "dK", "dV"), grads, ref):
+        assert torch.equal(g.contiguous().view(iview), c.view(iview)), n
+    # the three-call path through the same strided views
+    grads3 = [torch.full_like(dev[n], sentinel).movedim(nl, 0).contiguous().movedim(0, nl) for n in ("q", "k", "v")]
+    plan.run(q, k, v, o, do, lse, *grads3)
+    torch.cuda.synchronize()
+    for n, g, c in zip(("dQ", "dK", "dV"), grads3, ref):
+        assert torch.equal(g.contiguous().view(iview), c.view(iview)), n + " (three calls)"
+    # and the oracle, from the strided run's own O and LSE
+    r.set_o_lse(to_host(o.contiguous()), lse.cpu().numpy().astype(np.float64))
+    rdq, rdk, rdv = r.oracle_backward()
+    for n, g, rr in (("dQ", grads[0], rdq), ("dK", grads[1], rdk), ("dV", grads[2], rdv)):
+        assert_close(n, to_host(g.contiguous()), rr, p.dtype)
 
 
 SEQUSED_CASES = [
