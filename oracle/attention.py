@@ -38,6 +38,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
   bottom-right-aligned diagonal as the masks, ``-slope_h * |i + off - j|``
   (off = Sk - Sq) added to ``s * q_i . k_j`` in natural-log units, one slope
   per q-head.
+* Elementwise bias: the composable-kernel page adds a bias tile to the scaled
+  logits (times log2e in its base-2 arithmetic, i.e. in natural-log units)
+  and writes dBias as dS cast to the bias type.  The gradient of the loss
+  with respect to the logit s q_i . k_j + bias_ij is exactly dS_ij, so dBias
+  = dS; a bias broadcast over batch or heads is not summed here (the page
+  writes one dBias tile per (batch, head) tile).
 * GQA groups are contiguous: q-head h reads kv-head ``h // (Hq // Hkv)``, as in
   the head mapping of ``CollectiveEpilogueBwdGQA::store`` on the
   FlashAttention-3 page "flash-attention/hopper/epilogue_bwd.hpp"; dK and dV of
@@ -111,15 +117,18 @@ def alibi_bias(sq, sk, slope):
     return -float(slope) * np.abs(i + (sk - sq) - j).astype(np.float64)
 
 
-def _logits(q, k, scale, alibi):
-    """Stage 1: s * Q K^T, plus the ALiBi bias when a slope is given."""
+def _logits(q, k, scale, alibi, bias=None):
+    """Stage 1: s * Q K^T, plus the ALiBi bias when a slope is given and the
+    elementwise bias [sq, sk] when one is given."""
     s = scale * (q @ k.T)
     if alibi is not None:
         s = s + alibi_bias(q.shape[0], k.shape[0], alibi)
+    if bias is not None:
+        s = s + np.asarray(bias, np.float64)
     return s
 
 
-def head_forward(q, k, v, scale, causal, window=None, alibi=None):
+def head_forward(q, k, v, scale, causal, window=None, alibi=None, bias=None):
     """Softmax attention for one head.
 
     q [sq, d], k [sk, d], v [sk, d] -> (o [sq, d], lse [sq]), float64.
@@ -132,7 +141,7 @@ def head_forward(q, k, v, scale, causal, window=None, alibi=None):
     v = np.asarray(v, np.float64)
     sq, sk = q.shape[0], k.shape[0]
     ok = visible(sq, sk, causal, window)
-    s = _logits(q, k, scale, alibi)
+    s = _logits(q, k, scale, alibi, bias)
     has_key = ok.any(axis=1)
     # row maximum over visible keys (0 for empty rows, never used)
     row_max = np.max(np.where(ok, s, -np.inf), axis=1, initial=-np.inf)
@@ -147,21 +156,22 @@ def head_forward(q, k, v, scale, causal, window=None, alibi=None):
     return o, lse
 
 
-def _probabilities(q, k, lse, scale, causal, window=None, alibi=None):
+def _probabilities(q, k, lse, scale, causal, window=None, alibi=None, bias=None):
     """P recomputed from the saved LSE (stages 1-2): exp(s q_i.k_j + b_ij - lse_i)."""
     sq, sk = q.shape[0], k.shape[0]
     ok = visible(sq, sk, causal, window) & np.isfinite(lse)[:, None]
-    s = _logits(q, k, scale, alibi)
+    s = _logits(q, k, scale, alibi, bias)
     safe_lse = np.where(np.isfinite(lse), lse, 0.0)
     return np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))
 
 
-def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None, alibi=None):
+def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None, alibi=None, bias=None):
     """Gradient of attention for one head, given O and LSE as saved by a forward.
 
     Returns (dq [sq, d], dk [sk, d], dv [sk, d]) in float64; with
-    ``details=True`` also a dict holding P, dP, dS and D.  The ALiBi bias
-    only enters through P (it does not depend on Q or K).
+    ``details=True`` also a dict holding P, dP, dS and D.  The ALiBi and
+    elementwise biases only enter through P (they do not depend on Q or K);
+    the gradient of the elementwise bias is dS (``details["ds"]``).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -169,7 +179,7 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None
     o = np.asarray(o, np.float64)
     do = np.asarray(do, np.float64)
     lse = np.asarray(lse, np.float64)
-    p = _probabilities(q, k, lse, scale, causal, window, alibi)  # stages 1-2
+    p = _probabilities(q, k, lse, scale, causal, window, alibi, bias)  # stages 1-2
     delta = np.sum(do * o, axis=1)                        # D = rowsum(dO * O)
     dp = do @ v.T                                         # stage 4
     dv = p.T @ do                                         # stage 3
@@ -247,12 +257,18 @@ def _slope(alibi_slopes, h):
     return None if alibi_slopes is None else float(np.asarray(alibi_slopes, np.float64)[h])
 
 
+def _bias_block(bias, seq, h, len_q, len_k):
+    """The [len_q, len_k] bias of one (sequence, q-head), or None."""
+    return None if bias is None else np.asarray(bias)[seq, h, :len_q, :len_k]
+
+
 def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None,
-                  seqused_q=None, seqused_k=None, window=None, alibi_slopes=None):
+                  seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None):
     """Forward for the q-heads of one kv-head group of one sequence.
 
     Returns {q_head: (o [len_q, d], lse [len_q])}.  ``alibi_slopes``: one
-    slope per q-head, or None.
+    slope per q-head, or None.  ``bias``: [nseq, Hq, Sq, Sk] (Sq, Sk the
+    longest lengths), each sequence's block at its top left, or None.
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
@@ -261,17 +277,19 @@ def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_se
     out = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
         out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal, window,
-                              _slope(alibi_slopes, h))
+                              _slope(alibi_slopes, h), _bias_block(bias, seq, h, q1 - q0, k1 - k0))
     return out
 
 
 def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
                    cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None, window=None,
-                   alibi_slopes=None):
+                   alibi_slopes=None, bias=None, dbias_out=None):
     """Backward for one kv-head group of one sequence.
 
     Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
-    are summed over the group's q-heads in ascending head order.
+    are summed over the group's q-heads in ascending head order.  With
+    ``dbias_out`` ([nseq, Hq, Sq, Sk]) each q-head's dS is written into its
+    block (top left of the sequence's slot).
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
@@ -284,9 +302,12 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
     dv = np.zeros((k1 - k0, d))
     dq = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
-        dqh, dkh, dvh = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
-                                      of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, window=window,
-                                      alibi=_slope(alibi_slopes, h))
+        dqh, dkh, dvh, det = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
+                                           of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, details=True,
+                                           window=window, alibi=_slope(alibi_slopes, h),
+                                           bias=_bias_block(bias, seq, h, q1 - q0, k1 - k0))
+        if dbias_out is not None:
+            dbias_out[seq, h, :q1 - q0, :k1 - k0] = det["ds"]
         dq[h] = dqh
         dk += dkh
         dv += dvh
@@ -294,7 +315,7 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None,
-            window=None, alibi_slopes=None):
+            window=None, alibi_slopes=None, bias=None):
     """Full forward.  Returns (o, lse) in the layouts given in the module doc
     (rows past a sequence's used length are left at zero)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -304,7 +325,7 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
     for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
-                                             seqused_q, seqused_k, window, alibi_slopes).items():
+                                             seqused_q, seqused_k, window, alibi_slopes, bias).items():
                 o[q0:q1, h] = oh
                 lse[h, q0:q1] = lh
     if varlen:
@@ -313,25 +334,37 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
 
 
 def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-             seqused_q=None, seqused_k=None, window=None, alibi_slopes=None):
+             seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None, want_dbias=False):
     """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64);
-    rows past a sequence's used length are left at zero."""
+    rows past a sequence's used length are left at zero.  With
+    ``want_dbias`` also dBias [nseq, Hq, Sq, Sk] (dS of each head; zero
+    outside each sequence's block)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     qf, kf = _flat(q, varlen), _flat(k, varlen)
     dq = np.zeros(qf.shape, np.float64)
     dk = np.zeros(kf.shape, np.float64)
     dv = np.zeros(kf.shape, np.float64)
-    for b, (q0, q1, k0, k1) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
+    ranges = _ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)
+    dbias = None
+    if want_dbias:
+        msq = max(r[1] - r[0] for r in ranges) if varlen else sq
+        msk = max(r[3] - r[2] for r in ranges) if varlen else sk
+        if bias is not None:
+            msq, msk = np.asarray(bias).shape[2], np.asarray(bias).shape[3]
+        dbias = np.zeros((nseq, hq, msq, msk), np.float64)
+    for b, (q0, q1, k0, k1) in enumerate(ranges):
         for g in range(hkv):
             dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
-                                           seqused_q, seqused_k, window, alibi_slopes)
+                                           seqused_q, seqused_k, window, alibi_slopes, bias, dbias)
             for h, x in dqg.items():
                 dq[q0:q1, h] = x
             dk[k0:k1, g] = dkg
             dv[k0:k1, g] = dvg
     if varlen:
-        return dq, dk, dv
-    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(k.shape)
+        out = (dq, dk, dv)
+    else:
+        out = (dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(k.shape))
+    return out + (dbias,) if want_dbias else out
 
 
 def preprocess_delta(o, do, cu_seqlens_q=None):

@@ -471,6 +471,130 @@ def test_planted_alibi_mistakes_are_caught(mutant, monkeypatch):
 
 
 # --------------------------------------------------------------------------
+# elementwise bias: added to the scaled logits; dBias = dS
+# --------------------------------------------------------------------------
+
+def brute_bias_forward(q, k, v, scale, causal, bias):
+    """Scalar loops: logit_ij = scale q_i.k_j + bias_ij over the visible keys."""
+    sq, sk, d = len(q), len(k), len(q[0])
+    o, lse = [], []
+    for i in range(sq):
+        vis = [j for j in range(sk) if (not causal) or j <= i + (sk - sq)]
+        if not vis:
+            o.append([0.0] * d)
+            lse.append(-math.inf)
+            continue
+        s = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) + bias[i][j] for j in vis}
+        m = max(s.values())
+        lse.append(m + math.log(sum(math.exp(s[j] - m) for j in vis)))
+        o.append([sum(math.exp(s[j] - lse[-1]) * v[j][t] for j in vis) for t in range(d)])
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(5, 5, False), (4, 7, True), (7, 4, True), (3, 6, False)])
+def test_bias_forward_matches_scalar_loops(sq, sk, causal):
+    rng = np.random.default_rng(70 + sq * 7 + sk)
+    q, k, v, bias = rand(rng, sq, 3), rand(rng, sk, 3), rand(rng, sk, 3), 2.0 * rand(rng, sq, sk)
+    o, lse = A.head_forward(q, k, v, 0.7, causal, bias=bias)
+    bo, blse = brute_bias_forward(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, bias.tolist())
+    fin = np.isfinite(blse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - blse[fin])) <= 1e-12
+    assert np.max(np.abs(o - bo)) <= 1e-12
+
+
+def _fd_bias(q, k, v, do, bias, scale, causal, cu=None):
+    """Every gradient, dBias included, against central differences of sum(dO * O)."""
+    o, lse = oracle.forward(q, k, v, scale, causal, cu, cu, bias=bias)
+    dq, dk, dv, db = oracle.backward(q, k, v, o, do, lse, scale, causal, cu, cu, bias=bias, want_dbias=True)
+
+    def loss(qq, kk, vv, bb):
+        return float(np.sum(do * oracle.forward(qq, kk, vv, scale, causal, cu, cu, bias=bb)[0]))
+
+    h = 1e-5
+    base = [q, k, v, bias]
+    for pos, g in enumerate((dq, dk, dv, db)):
+        fd = np.zeros_like(base[pos])
+        for idx in np.ndindex(fd.shape):
+            xp, xm = base[pos].copy(), base[pos].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(base), list(base)
+            ap[pos], am[pos] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        # (bias entries outside a sequence's block take no part: both are zero)
+        assert rel_err(g, fd) <= 1e-6, ("dq", "dk", "dv", "dbias")[pos]
+    return db
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_backward_finite_differences(causal):
+    """Dense GQA (4 q-heads on 2 kv-heads): dQ, dK, dV and dBias."""
+    rng = np.random.default_rng(31)
+    q, k, v, do = rand(rng, 1, 5, 4, 3), rand(rng, 1, 6, 2, 3), rand(rng, 1, 6, 2, 3), rand(rng, 1, 5, 4, 3)
+    bias = rand(rng, 1, 4, 5, 6)
+    _fd_bias(q, k, v, do, bias, 0.5, causal)
+
+
+def test_bias_backward_finite_differences_varlen():
+    rng = np.random.default_rng(32)
+    cu = np.array([0, 2, 6], np.int32)
+    q, k, v, do = rand(rng, 6, 2, 3), rand(rng, 6, 2, 3), rand(rng, 6, 2, 3), rand(rng, 6, 2, 3)
+    bias = rand(rng, 2, 2, 4, 4)
+    db = _fd_bias(q, k, v, do, bias, 0.6, True, cu)
+    assert np.all(db[0, :, 2:, :] == 0) and np.all(db[0, :, :, 2:] == 0)   # outside sequence 0's 2 x 2 block
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(30, 30, False), (20, 37, True), (37, 20, False)])
+def test_bias_backward_matches_torch_autograd_float64(sq, sk, causal):
+    """The bias as a leaf tensor in torch float64 autograd: dQ, dK, dV and dBias."""
+    import torch
+    rng = np.random.default_rng(14)
+    q, k, v, do, bias = (rand(rng, sq, 8), rand(rng, sk, 8), rand(rng, sk, 8), rand(rng, sq, 8),
+                         rand(rng, sq, sk))
+    i = torch.arange(sq)[:, None]
+    j = torch.arange(sk)[None, :]
+    mask = (j <= i + (sk - sq)) if causal else torch.ones(sq, sk, dtype=torch.bool)
+    tq, tk, tv, tb = (torch.tensor(x, requires_grad=True) for x in (q, k, v, bias))
+    s = (0.3 * tq @ tk.T + tb).masked_fill(~mask, float("-inf"))
+    rows = mask.any(dim=1)
+    pr = torch.where(rows[:, None], torch.softmax(torch.where(rows[:, None], s, torch.zeros_like(s)), dim=-1),
+                     torch.zeros_like(s))
+    out = pr @ tv
+    out.backward(torch.from_numpy(do))
+    o, lse = A.head_forward(q, k, v, 0.3, causal, bias=bias)
+    assert np.max(np.abs(o - out.detach().numpy())) <= 1e-12
+    dq, dk, dv, det = A.head_backward(q, k, v, o, do, lse, 0.3, causal, details=True, bias=bias)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad), (det["ds"], tb.grad)):
+        assert rel_err(got, want.numpy()) <= 1e-12
+
+
+def test_bias_invariants():
+    """A per-row constant bias leaves P (so O, dQ, dK, dV) unchanged and shifts
+    LSE by the constant; every row of dBias = dS sums to zero; the ALiBi bias
+    given as an elementwise bias gives the ALiBi results."""
+    rng = np.random.default_rng(15)
+    q, k, v, do = rand(rng, 9, 4), rand(rng, 11, 4), rand(rng, 11, 4), rand(rng, 9, 4)
+    c = rand(rng, 9)
+    for causal in (False, True):
+        o, lse = A.head_forward(q, k, v, 0.5, causal)
+        ob, lseb = A.head_forward(q, k, v, 0.5, causal, bias=np.repeat(c[:, None], 11, axis=1))
+        assert np.max(np.abs(o - ob)) <= 1e-12
+        assert np.max(np.abs((lseb - lse) - c)) <= 1e-12
+        g = A.head_backward(q, k, v, o, do, lse, 0.5, causal)
+        gb = A.head_backward(q, k, v, ob, do, lseb, 0.5, causal, bias=np.repeat(c[:, None], 11, axis=1))
+        for x, y in zip(g, gb):
+            assert rel_err(y, x) <= 1e-10
+        bias = rand(rng, 9, 11)
+        ob, lseb = A.head_forward(q, k, v, 0.5, causal, bias=bias)
+        *_, det = A.head_backward(q, k, v, ob, do, lseb, 0.5, causal, details=True, bias=bias)
+        assert np.max(np.abs(det["ds"].sum(axis=1))) <= 1e-12
+        oa, lsea = A.head_forward(q, k, v, 0.5, causal, alibi=0.3)
+        ob, lseb = A.head_forward(q, k, v, 0.5, causal, bias=A.alibi_bias(9, 11, 0.3))
+        assert np.max(np.abs(oa - ob)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
 # backward: independent library autograd (torch, float64)
 # --------------------------------------------------------------------------
 
