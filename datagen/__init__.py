@@ -155,3 +155,18 @@ def draw(p: Problem):
     elif p.dtype == "f16":
         q, k, v, do = (round_to_f16(x) for x in (q, k, v, do))
     return {"q": q, "k": k, "v": v, "do": do}
+
+
+def draw_bias(p: Problem, seed, heads=None, batch=None):
+    """A seeded elementwise bias [nseq or B, H, Sq, Sk] (Sq, Sk the longest
+    lengths) of standard normal values times 2, exactly representable in the
+    problem's dtype.  heads / batch = 1 give a bias to broadcast over them."""
+    rng = np.random.default_rng(seed)
+    shape = (batch if batch is not None else p.batch, heads if heads is not None else p.heads_q,
+             p.seqlen_q, p.seqlen_k)
+    b = (2.0 * rng.standard_normal(shape)).astype(np.float32)
+    if p.dtype == "bf16":
+        b = round_to_bf16(b)
+    elif p.dtype == "f16":
+        b = round_to_f16(b)
+    return b

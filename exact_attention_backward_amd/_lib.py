@@ -75,6 +75,10 @@ class AttnShape(ctypes.Structure):
         ("window_right", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
         ("strides", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("bias_strides", TensorStrides),
+        ("dbias", ctypes.c_void_p),
+        ("dbias_strides", TensorStrides),
     ]
 
 

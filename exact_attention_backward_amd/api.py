@@ -61,7 +61,7 @@ DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_
 
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-               window=None, alibi_slopes=None):
+               window=None, alibi_slopes=None, bias=None, dbias=None):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
     "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
@@ -70,7 +70,11 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     used lengths.  window = (left, right) selects the local mask: query i sees
     key j iff i + off - left <= j <= i + off + right (off = len_k - len_q, -1
     for an unbounded side), intersected with the causal bound when causal.
-    alibi_slopes: fp32 device tensor [Hq]; the logits get -slope_h |i + off - j|."""
+    alibi_slopes: fp32 device tensor [Hq]; the logits get -slope_h |i + off - j|.
+    bias / dbias (atomic dQ mode): tensors indexed [b, h, i, j] (b the
+    sequence for varlen; keys contiguous, any batch/head/row strides, 0 to
+    broadcast the bias); the bias is added to the logits and dbias receives
+    dS."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -98,6 +102,14 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
         if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != q.shape[-2]:
             raise ValueError("alibi_slopes must be a float32 tensor with one slope per q-head")
         s.alibi_slopes = alibi_slopes.data_ptr()
+    for name, t in (("bias", bias), ("dbias", dbias)):
+        if t is None:
+            continue
+        if t.dim() != 4 or (t.stride(3) != 1 and t.shape[3] > 1) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a 4-d [b, h, i, j] tensor of q's dtype with contiguous keys")
+        setattr(s, name, t.data_ptr())
+        st = getattr(s, name + "_strides")
+        st.batch, st.head, st.row = t.stride(0), t.stride(1), t.stride(2)
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
@@ -176,11 +188,12 @@ def _lse_shape(shape, varlen):
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            seqused_q=None, seqused_k=None, out=None, window=None, alibi_slopes=None):
+            seqused_q=None, seqused_k=None, out=None, window=None, alibi_slopes=None, bias=None):
     """Plain forward: returns (o, lse).  ``out`` = (o, lse) writes into given
     buffers (rows past the used lengths keep their contents)."""
     shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                       seqused_q=seqused_q, seqused_k=seqused_k, window=window, alibi_slopes=alibi_slopes)
+                       seqused_q=seqused_q, seqused_k=seqused_k, window=window, alibi_slopes=alibi_slopes,
+                       bias=bias)
     if out is not None:
         o, lse = out
     else:
@@ -199,10 +212,11 @@ class BackwardPlan:
 
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                  max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-                 window=None, alibi_slopes=None):
+                 window=None, alibi_slopes=None, bias=None, dbias=None):
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
-                                max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window, alibi_slopes)
-        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes)
+                                max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window, alibi_slopes,
+                                bias, dbias)
+        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes, bias, dbias)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
         if nbytes == 0:
@@ -249,10 +263,10 @@ class BackwardPlan:
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-             window=None, alibi_slopes=None):
-    """Full backward: returns (dq, dk, dv)."""
+             window=None, alibi_slopes=None, bias=None, dbias=None):
+    """Full backward: returns (dq, dk, dv) (and fills dbias when given)."""
     plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                        dq_algo, seqused_q, seqused_k, window, alibi_slopes)
+                        dq_algo, seqused_q, seqused_k, window, alibi_slopes, bias, dbias)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     plan.run(q, k, v, o, do, lse, dq, dk, dv)
     return dq, dk, dv

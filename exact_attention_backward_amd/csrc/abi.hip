@@ -75,6 +75,22 @@ int validate_shape(const attn_shape_t* s) {
         if ((len + 1) * x->row * esz >= kOobOff - (1LL << 20)) return ATTN_ERR_BAD_SHAPE;
         if (x->head * esz >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;   // 32-bit head steps
     }
+    const attn_tensor_strides_t* bs[] = {&s->bias_strides, &s->dbias_strides};
+    const void* bp[] = {s->bias, s->dbias};
+    for (int t = 0; t < 2; ++t) {
+        if (bp[t] == nullptr) continue;
+        if (bs[t]->batch < 0 || bs[t]->row < 0 || bs[t]->head < 0) return ATTN_ERR_BAD_SHAPE;
+        if (reinterpret_cast<uintptr_t>(bp[t]) % esz) return ATTN_ERR_MISALIGNED;
+    }
+    return ATTN_OK;
+}
+
+// the backward entry points: an elementwise bias or its gradient needs the
+// atomic dQ mode (the forward takes a bias whatever dq_algo says)
+int validate_bwd(const attn_shape_t* s) {
+    const int st = validate_shape(s);
+    if (st) return st;
+    if ((s->bias != nullptr || s->dbias != nullptr) && s->dq_algo != ATTN_DQ_ATOMIC) return ATTN_ERR_UNSUPPORTED;
     return ATTN_OK;
 }
 
@@ -152,7 +168,7 @@ const char* attn_status_string(int status) {
 }
 
 size_t attn_bwd_workspace_bytes(const attn_shape_t* shape) {
-    if (validate_shape(shape) != ATTN_OK) return 0;
+    if (validate_bwd(shape) != ATTN_OK) return 0;
     return workspace_bytes(shape);
 }
 
@@ -176,6 +192,8 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.sk = to_kernel(d.k);
     a.sv = to_kernel(d.v);
     a.so = to_kernel(d.o);
+    a.bias = s->bias;
+    a.sbias = to_kernel(s->bias_strides);
     launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
@@ -251,6 +269,10 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
     a.sdq = to_kernel(d.dq);
     a.sdk = to_kernel(d.dk);
     a.sdv = to_kernel(d.dv);
+    a.bias = s->bias;
+    a.dbias = s->dbias;
+    a.sbias = to_kernel(s->bias_strides);
+    a.sdbias = to_kernel(s->dbias_strides);
     if (s->dq_algo == ATTN_DQ_STORED_DS) {
         char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
         a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
@@ -258,6 +280,8 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
         a.ds_qb = ds_qb(s);
         a.ds_nn = ds_nn(s);
     }
+    // dBias blocks the kernel does not visit (masked tiles) must read zero
+    if (s->dbias != nullptr) launch_zero_blocks(s->dbias, a.sdbias, s->dtype, a, hs);
     launch_bwd(a, s->dtype, padded_hd(s), masked(s), s->dq_algo, hs);
     if (s->dq_algo == ATTN_DQ_SEPARATE) {
         BwdArgs e = a;
@@ -293,7 +317,7 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
 
 int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout, const float* lse,
              const float* delta, void* workspace, size_t workspace_size, void* dk, void* dv, void* stream) {
-    int st = validate_shape(s);
+    int st = validate_bwd(s);
     if (st) return st;
     if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dk || !dv) return ATTN_ERR_NULL_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
@@ -320,7 +344,7 @@ int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t
 int attn_bwd_full(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout,
                   const float* lse, const float* delta, void* workspace, size_t workspace_size, void* dq, void* dk,
                   void* dv, void* stream) {
-    int st = validate_shape(s);
+    int st = validate_bwd(s);
     if (st) return st;
     if (!q || !k || !v || !dout || !lse || !delta || !workspace || !dq || !dk || !dv) return ATTN_ERR_NULL_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||

@@ -373,7 +373,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         // lo(i) <= j < lim(i)); the branch is uniform.
         // ALiBi slope of this tile's q-head, negated, in log2 units
         const float nsl2 = a.alibi != nullptr ? -a.alibi[hq] * kLog2e : 0.f;
-        auto softmax_grad = [&](auto masked, auto alibi) {
+        // this (sequence, q-head)'s elementwise bias and dBias, or null
+        const T* bias_h = a.bias != nullptr ? reinterpret_cast<const T*>(a.bias) + (long long)b * a.sbias.b +
+                                                  (long long)hq * a.sbias.h
+                                            : nullptr;
+        T* dbias_h = a.dbias != nullptr ? reinterpret_cast<T*>(a.dbias) + (long long)b * a.sdbias.b +
+                                              (long long)hq * a.sdbias.h
+                                        : nullptr;
+        // extra: ALiBi and the bias (each present or not); rows and keys past
+        // the sequence read no bias
+        auto softmax_grad = [&](auto masked, auto extra) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
 #pragma unroll
@@ -386,8 +395,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                         const int v = 4 * q4 + e;
                         const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
                         float x = s[mb][v] * scale2 - l2;
-                        if constexpr (decltype(alibi)::value)
-                            x = fmaf(nsl2, fabsf((float)(j - (i0 + r + e) - off)), x);
+                        if constexpr (decltype(extra)::value) {
+                            const int ib = i0 + r + e;
+                            x = fmaf(nsl2, fabsf((float)(j - ib - off)), x);
+                            if (bias_h != nullptr && ib < si.len_q && j < si.len_k)
+                                x = fmaf(load_elem(bias_h, (long long)ib * a.sbias.r + j), kLog2e, x);
+                        }
                         float p = __builtin_amdgcn_exp2f(x);
                         if constexpr (decltype(masked)::value) {
                             const int i = i0 + r + e;
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                 }
             }
         };
-        if (a.alibi != nullptr) {
+        if (a.alibi != nullptr || a.bias != nullptr) {
             if (edge)
                 softmax_grad(std::true_type{}, std::true_type{});
             else
@@ -463,6 +476,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
+        if (dbias_h != nullptr) {
+            // dBias = dS of this tile (rows and keys inside the sequence),
+            // copied from its LDS image (already in the I/O type); consecutive
+            // threads take consecutive keys of a row
+            for (int e = threadIdx.x; e < BM * kBN; e += kThreads) {
+                const int ii = e / kBN, jj = e % kBN;
+                const int ib = i0 + ii, jb = n * kBN + jj;
+                if (ib < si.len_q && jb < si.len_k)
+                    dbias_h[(long long)ib * a.sdbias.r + jb] =
+                        *reinterpret_cast<const T*>(lds_ds + swz<C::DSROWB>(jj, ii * (int)sizeof(T)));
+            }
+        }
 
         // ---- stage 7: dQ tile = dS K for this wave's blocks
         f32x16 dq[C::DQB];

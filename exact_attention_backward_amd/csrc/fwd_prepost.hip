@@ -54,6 +54,11 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     float m = -INFINITY, l = 0.f;
     // ALiBi slope in the log2 units of the scaled logits (0: no bias)
     const float sl2 = a.alibi != nullptr ? a.alibi[hq] * kLog2e : 0.f;
+    // this row of the elementwise bias (log2 units at use), or null
+    const T* brow = a.bias != nullptr && row_ok
+                        ? reinterpret_cast<const T*>(a.bias) + (long long)b * a.sbias.b + (long long)hq * a.sbias.h +
+                              (long long)i * a.sbias.r
+                        : nullptr;
     // keys any row of the block can see: with a mask, from the first row's
     // lower bound (aligned down to a tile) to the last row's upper bound
     const int whi = a.win_hi, wlo = a.win_lo;
@@ -82,7 +87,9 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
             float acc = 0.f;
 #pragma unroll
             for (int d = 0; d < HD; ++d) acc = fmaf(q[d], ks[jj][d], acc);
-            s[jj] = vis ? acc - sl2 * fabsf((float)dj) : -INFINITY;
+            float x = acc - sl2 * fabsf((float)dj);
+            if (brow != nullptr && vis) x = fmaf((float)load_elem(brow, j), kLog2e, x);
+            s[jj] = vis ? x : -INFINITY;
             tmax = fmaxf(tmax, s[jj]);
         }
         if (tmax > -INFINITY) {
@@ -163,6 +170,16 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
         a.delta[lse_index(a.varlen, r, h, a.h, a.s, a.total)] = dsum[threadIdx.x];
 }
 
+// zero row i of (sequence b, q-head h) of a [b, h, i, j] tensor: its len_k elements
+template <class T>
+__global__ __launch_bounds__(256) void zero_blocks_kernel(T* p, Strides s, BwdArgs a) {
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
+    if (i >= si.len_q) return;
+    T* row = p + (long long)b * s.b + (long long)h * s.h + (long long)i * s.r;
+    for (int j = threadIdx.x; j < si.len_k; j += blockDim.x) store_elem(row, j, 0.f);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, long long n16) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
@@ -237,6 +254,13 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
     long long blocks = (n16 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<u32x4*>(p), n16);
+}
+
+void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st) {
+    const dim3 grid((unsigned)a.seqlen_q, (unsigned)a.hq, (unsigned)a.batch);
+    if (dtype == ATTN_DTYPE_BF16) zero_blocks_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<bf16_t*>(p), s, a);
+    else if (dtype == ATTN_DTYPE_F16) zero_blocks_kernel<f16_t><<<grid, 256, 0, st>>>(reinterpret_cast<f16_t*>(p), s, a);
+    else zero_blocks_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<float*>(p), s, a);
 }
 
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st) {

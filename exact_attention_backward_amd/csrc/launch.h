@@ -40,6 +40,8 @@ struct FwdArgs {
     const float* alibi;      // per q-head ALiBi slopes, or null
     int d;                   // head dim (the kernels' HD is this rounded up to 64 or 128)
     Strides sq, sk, sv, so;
+    const void* bias;        // elementwise bias [b, h, i, j] (I/O type), or null
+    Strides sbias;           // its batch, row and head strides (columns contiguous)
 };
 
 struct PreArgs {
@@ -103,6 +105,11 @@ struct BwdArgs {
     int d;               // head dim (the kernels' HD is this rounded up to 64 or 128;
                          // columns from d on are zero in every tile)
     Strides sq, sk, sv, sdo, sdq, sdk, sdv;
+    // elementwise bias [b, h, i, j] added to the logits and its gradient dS
+    // (atomic dQ mode), or null; batch, row and head strides
+    const void* bias;
+    void* dbias;
+    Strides sbias, sdbias;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
@@ -146,6 +153,8 @@ constexpr int kBwdBlockN = 128;
 
 void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// zero every sequence's [Hq, len_q, len_k] block of a [b, h, i, j] tensor with strides s
+void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
 void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, hipStream_t st);

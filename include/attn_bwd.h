@@ -67,6 +67,16 @@
  *    position encoding per (row, column) after the scale without its formula;
  *    this linear bias is the reading taken.  attn_fwd's LSE includes it and
  *    attn_bwd must get the same slopes.
+ *  - Elementwise bias (ATTN_DQ_ATOMIC only; other modes return
+ *    ATTN_ERR_UNSUPPORTED): with bias non-NULL the logit of query i, key j
+ *    under q-head h of sequence b gets + bias[b * batch + h * head + i * row
+ *    + j] (bias_strides, in elements; 0 broadcasts; keys contiguous), in
+ *    natural-log units, in attn_fwd and attn_bwd alike.  With dbias non-NULL,
+ *    attn_bwd / attn_bwd_full write dBias = dS (the gradient of the logit,
+ *    rounded to the I/O type, as the composable-kernel pipeline's dBias
+ *    tile) at the same positions with dbias_strides: every (i, j) of each
+ *    sequence's len_q x len_k block of every q-head, zero where masked.
+ *    dbias must not overlap other tensors or itself.
  *  - GQA: Hq must be a multiple of Hkv; q-head h uses kv-head h / (Hq / Hkv)
  *    (contiguous groups).  dK and dV of a kv-head are the sums over its
  *    q-heads.
@@ -95,7 +105,8 @@ typedef enum attn_status {
                                   about 2 GiB or more of one sequence's rows of a
                                   tensor (seqlen x row stride), ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not a multiple of 8 in
-                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
+                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32,
+                                  bias or dbias without ATTN_DQ_ATOMIC */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer or stride is not 16-byte aligned
                                   (cu_seqlens, seqused and alibi_slopes: 4-byte) */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
@@ -173,6 +184,10 @@ typedef struct attn_shape {
     const float* alibi_slopes;    /* device [num_heads_q] fp32 ALiBi slopes, or NULL for none */
     const attn_strides_t* strides; /* HOST pointer, read during each call; NULL = the
                                       contiguous layouts above */
+    const void* bias;        /* device elementwise bias (dtype), or NULL: see below */
+    attn_tensor_strides_t bias_strides;
+    void* dbias;             /* device output dBias (dtype), or NULL: see below */
+    attn_tensor_strides_t dbias_strides;
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

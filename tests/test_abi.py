@@ -170,6 +170,23 @@ def test_alibi_slopes_alignment():
     assert rc == L.ATTN_ERR_MISALIGNED
 
 
+def test_bias_needs_the_atomic_mode():
+    fake = ctypes.c_void_p(0x1000)
+    for algo, want in ((L.ATTN_DQ_SEPARATE, L.ATTN_ERR_UNSUPPORTED), (L.ATTN_DQ_STORED_DS, L.ATTN_ERR_UNSUPPORTED)):
+        for field in ("bias", "dbias"):
+            s = shape(dq_algo=algo, **{field: 0x1000})
+            assert ws_bytes(s) == 0
+            rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
+            assert rc == want
+    s = shape(dq_algo=L.ATTN_DQ_ATOMIC, bias=0x1000, dbias=0x2000)
+    assert ws_bytes(s) == ws_bytes(shape(dq_algo=L.ATTN_DQ_ATOMIC))
+    s = shape(dq_algo=L.ATTN_DQ_ATOMIC, bias=0x1001)
+    assert ws_bytes(s) == 0   # misaligned for bf16
+    s = shape(dq_algo=L.ATTN_DQ_ATOMIC, dbias=0x1000)
+    s.dbias_strides.row = -4
+    assert ws_bytes(s) == 0
+
+
 def test_shape_struct_layout_matches_header(tmp_path):
     """The ctypes mirror of attn_shape_t has the C layout (compiled from the header)."""
     import shutil
@@ -177,17 +194,21 @@ def test_shape_struct_layout_matches_header(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("no C compiler")
     fields = [f[0] for f in L.AttnShape._fields_]
+    sub = {"bias_strides": ("batch", "row", "head"), "dbias_strides": ("batch", "row", "head")}
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "attn_bwd.h"\nint main(void) {\n'
                    '    printf("%zu\\n", sizeof(attn_shape_t));\n'
                    + "".join(f'    printf("%zu\\n", offsetof(attn_shape_t, {f}));\n' for f in fields)
+                   + "".join(f'    printf("%zu\\n", offsetof(attn_shape_t, {f}.{g}));\n' for f in sub for g in sub[f])
                    + "    return 0;\n}\n")
     exe = tmp_path / "layout"
     inc = Path(__file__).resolve().parents[1] / "include"
     subprocess.run(["gcc", "-std=c99", "-I", str(inc), str(src), "-o", str(exe)], check=True)
     out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert out[0] == ctypes.sizeof(L.AttnShape)
-    assert out[1:] == [getattr(L.AttnShape, f).offset for f in fields]
+    want = [getattr(L.AttnShape, f).offset for f in fields]
+    want += [getattr(L.AttnShape, f).offset + getattr(L.TensorStrides, g).offset for f in sub for g in sub[f]]
+    assert out[1:] == want
 
 
 def test_varlen_needs_both_offsets_and_totals():

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from _harness import Run, assert_close, rel_err, round_like, small_problem, to_host, TOL
+from _harness import Run, assert_close, rel_err, round_like, small_problem, to_dev, to_host, TOL
 from exact_attention_backward_amd import api
 
 pytestmark = pytest.mark.gpu
@@ -480,6 +480,70 @@ def test_strided_layouts_match_contiguous_bitwise(case, dq_algo):
     rdq, rdk, rdv = r.oracle_backward()
     for n, g, rr in (("dQ", grads[0], rdq), ("dK", grads[1], rdk), ("dV", grads[2], rdv)):
         assert_close(n, to_host(g.contiguous()), rr, p.dtype)
+
+
+# elementwise bias + dBias (atomic dQ mode): (dtype, B, Hq, Hkv, Sq, Sk, D, causal, lengths, window, broadcast)
+BIAS_CASES = [
+    ("bf16", 2, 3, 3, 200, 200, 128, True, None, None, None),
+    ("bf16", 1, 4, 2, 170, 260, 64, False, None, None, "heads"),     # one bias for every q-head
+    ("bf16", 2, 2, 2, 130, 130, 64, True, None, None, "batch"),      # one bias for every batch entry
+    ("f16", 1, 2, 2, 300, 300, 128, True, None, (50, -1), None),
+    ("f32", 1, 2, 2, 150, 200, 64, True, None, None, None),
+    ("bf16", 0, 4, 2, 0, 0, 128, True, (1, 64, 300), None, None),    # varlen
+]
+
+
+def _biasid(c):
+    bc = f"-bcast_{c[10]}" if c[10] else ""
+    w = f"-w{c[9][0]}/{c[9][1]}" if c[9] else ""
+    return f"{_id(c[:9])}{w}{bc}"
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["three_calls", "bwd_full"])
+@pytest.mark.parametrize("case", BIAS_CASES, ids=_biasid)
+def test_bias_and_dbias_match_oracle(case, full):
+    """O and LSE with the bias, dQ/dK/dV and dBias = dS against the oracle;
+    dBias outside each sequence's block keeps its contents."""
+    import datagen
+    p = problem(case[:9])
+    win, bcast = case[9], case[10]
+    r = Run(p, oracle_o_lse=False, window=win)
+    nb = len(case[8]) if case[8] else case[1]
+    bias_np = datagen.draw_bias(p, 91, heads=1 if bcast == "heads" else None, batch=1 if bcast == "batch" else nb)
+    bias_dev = to_dev(bias_np, p.dtype).expand(nb, p.heads_q, p.seqlen_q, p.seqlen_k)
+    bias_full = np.broadcast_to(bias_np, (nb, p.heads_q, p.seqlen_q, p.seqlen_k))
+    print(f"bias {_biasid(case)} full={full}", flush=True)
+    d, kw = r.dev, r.kw()
+    cq, ck = r.cu_np
+    o, lse = api.forward(d["q"], d["k"], d["v"], p.scale, p.causal, window=win, bias=bias_dev, **kw)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.forward(r.x["q"], r.x["k"], r.x["v"], p.scale, p.causal, cq, ck, window=win, bias=bias_full)
+    assert_close("O", to_host(o), ro, p.dtype)
+    fin = np.isfinite(rlse)
+    g = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.max(np.abs(g[fin] - rlse[fin]), initial=0) <= (1e-4 if p.dtype == "f32" else 2e-4)
+    # backward from the oracle's O and LSE
+    r.set_o_lse(ro, rlse)
+    sentinel = 9.0
+    dbias = torch.full((nb, p.heads_q, p.seqlen_q, p.seqlen_k), sentinel, dtype=d["q"].dtype, device="cuda")
+    plan = api.BackwardPlan(d["q"], d["k"], p.scale, p.causal, False, dq_algo="atomic", window=win,
+                            bias=bias_dev, dbias=dbias, **kw)
+    dq, dk, dv = (torch.empty_like(d[n]) for n in ("q", "k", "v"))
+    (plan.run_full if full else plan.run)(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq, dk, dv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rdb = oracle.backward(r.x["q"], r.x["k"], r.x["v"], r.o, r.x["do"], r.lse, p.scale, p.causal,
+                                         cq, ck, window=win, bias=bias_full, want_dbias=True)
+    for n, gg, ref in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert_close(n, to_host(gg), ref, p.dtype)
+    gdb = to_host(dbias)
+    inside = np.zeros(gdb.shape, bool)
+    lq = [cq[i + 1] - cq[i] for i in range(nb)] if cq is not None else [p.seqlen_q] * nb
+    lk = [ck[i + 1] - ck[i] for i in range(nb)] if ck is not None else [p.seqlen_k] * nb
+    for bb in range(nb):
+        inside[bb, :, :lq[bb], :lk[bb]] = True
+    assert_close("dBias", gdb[inside], rdb[inside], p.dtype)
+    assert np.all(gdb[~inside] == sentinel)
 
 
 SEQUSED_CASES = [
