@@ -205,15 +205,16 @@ namespace {
 // The enqueue steps behind the entry points; arguments already validated.
 void enqueue_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
                         hipStream_t hs) {
-    // the counters and status words always; the accumulator only where it is
-    // added into (atomic modes); the dS blocks are written before they are read
-    if (s->dq_algo == ATTN_DQ_ATOMIC)
-        launch_fill_zero(workspace, accum_bytes(s) + sem_bytes(s) + kErrBytes, hs);
-    else
-        launch_fill_zero(reinterpret_cast<char*>(workspace) + accum_bytes(s), sem_bytes(s) + kErrBytes, hs);
+    // the preprocess kernel also clears the counters and status words, and
+    // the accumulator where it is added into (atomic modes); the dS blocks
+    // are written before they are read
+    const bool atomic = s->dq_algo == ATTN_DQ_ATOMIC;
+    char* zero = reinterpret_cast<char*>(workspace) + (atomic ? 0 : accum_bytes(s));
+    const size_t zero_bytes = (atomic ? accum_bytes(s) : 0) + sem_bytes(s) + kErrBytes;
     const attn_strides_t d = strides_of(s);
     PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s),
-              s->head_dim, to_kernel(d.o), to_kernel(d.dout)};
+              s->head_dim, to_kernel(d.o), to_kernel(d.dout), reinterpret_cast<u32x4*>(zero),
+              (long long)(zero_bytes / 16)};
     launch_preprocess(a, s->dtype, padded_hd(s), hs);
     if (s->dq_algo == ATTN_DQ_STORED_DS && varlen(s))
         launch_ds_table(s->cu_seqlens_q, s->batch, s->seqlen_q, s->total_q,

@@ -136,6 +136,13 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
     constexpr int RPP = 256 / LPR;                 // rows per pass
     constexpr int PASSES = kPreTokens / RPP;
     __shared__ float dsum[kPreTokens];
+    {
+        // the workspace words attn_bwd accumulates into (grid-stride)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < a.n16;
+             i += (long long)gridDim.x * blockDim.x)
+            a.zero[i] = z;
+    }
     const long long tokens = a.rows / a.h;
     const int h = (int)(blockIdx.x % (unsigned)a.h);
     const long long r0 = (long long)(blockIdx.x / (unsigned)a.h) * kPreTokens;

@@ -54,6 +54,8 @@ struct PreArgs {
     bool varlen;
     int d;               // head dim
     Strides so, sdo;
+    u32x4* zero;         // workspace words the kernel also clears (16-byte units), n16 of them
+    long long n16;
 };
 
 struct PostArgs {
