@@ -194,7 +194,12 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.so = to_kernel(d.o);
     a.bias = s->bias;
     a.sbias = to_kernel(s->bias_strides);
-    launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
+    // the MFMA forward for the 16-bit types; fp32 and the elementwise bias
+    // take the plain one
+    if (s->dtype != ATTN_DTYPE_F32 && s->bias == nullptr)
+        launch_fwd_mfma(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
+    else
+        launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 

@@ -401,6 +401,258 @@ static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
 
 int bwd_dq_block_m() { return 32 * kWaves; }
 
+// ---------------------------------------------------------------------------
+// MFMA forward (bf16 / fp16): the same query-stationary schedule.  Per key
+// tile, S^T = K Q^T (this lane's query in its accumulator column), an online
+// softmax in base 2 (a running row maximum shared with the partner lane that
+// holds the tile's other keys, and a running partial row sum), and
+// O^T += V^T P^T: V^T through the transposing reads the dQ pass uses for K,
+// P (rounded to the operand type) straight from the S^T registers.  The O^T
+// accumulator's column is again this lane's query, so the rescale by the
+// change of the row maximum is one scalar per lane.  Not part of the
+// backward; it produces O and LSE for it.
+// ---------------------------------------------------------------------------
+template <class T, int HD, bool MASKED, bool ALIBI>
+__device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
+                                         char* smem) {
+    using C = DqCfg<T, HD>;
+    using op_t = typename Elem<T>::op_t;
+    constexpr int BQ = C::BQ, BN = C::BN;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int i0 = m * BQ;
+    if (i0 >= si.len_q) return;
+    const bool varlen = a.cu_q != nullptr;
+    const int off = si.len_k - si.len_q;
+
+    int key_end = si.len_k, kt_b = 0;
+    if (MASKED) {
+        key_end = min(key_end, min(i0 + BQ, si.len_q) - 1 + off + a.win_hi + 1);
+        const int key_beg = i0 + off - a.win_lo;
+        kt_b = key_beg > 0 ? key_beg / BN : 0;
+    }
+    const int n_kt = key_end > 0 ? max((key_end + BN - 1) / BN - kt_b, 0) : 0;
+
+    const T* kg = reinterpret_cast<const T*>(a.k) + seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h;
+    const T* vg = reinterpret_cast<const T*>(a.v) + seq_off(a.sv, varlen, b, si.k0) + (long long)hkv * a.sv.h;
+    const int valid = a.d * (int)sizeof(T) / 16;
+    DqTileCopy<C::ROWB, BN> kcopy, vcopy;
+    kcopy.init(w, lane, (int)(a.sk.r * (long long)sizeof(T)), valid);
+    vcopy.init(w, lane, (int)(a.sv.r * (long long)sizeof(T)), valid);
+    constexpr int kOpsPerTile = 2 * DqTileCopy<C::ROWB, BN>::N;
+    auto buf_of = [&](int u) { return smem + (u % C::NS) * C::BUF_BYTES; };
+    auto issue_tile = [&](int u) {
+        const int kt = kt_b + u;
+        const int rows = min(si.len_k - kt * BN, BN);
+        char* buf = buf_of(u);
+        kcopy.issue(rsrc_words(kg + (long long)kt * BN * a.sk.r, (unsigned)(rows * a.sk.r * (long long)sizeof(T))),
+                    buf + C::BUF_K, w);
+        vcopy.issue(rsrc_words(vg + (long long)kt * BN * a.sv.r, (unsigned)(rows * a.sv.r * (long long)sizeof(T))),
+                    buf + C::BUF_V, w);
+    };
+
+    // ---- this lane's query row as the B operand of S^T = K Q^T
+    const int i = i0 + 32 * w + l32;
+    const bool row_ok = i < si.len_q;
+    op_t qreg[C::NC];
+    {
+        const T* qg = reinterpret_cast<const T*>(a.q) + seq_off(a.sq, varlen, b, si.q0) + (long long)hq * a.sq.h +
+                      (long long)i * a.sq.r;
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) qreg[c] = dq_load_global<T>(qg + 16 * c + 8 * h, row_ok && 16 * c + 8 * h < a.d);
+    }
+    const float scale2 = a.scale * kLog2e;
+    const float nsl2 = ALIBI ? -a.alibi[hq] * kLog2e : 0.f;
+    const int lim = row_ok ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
+    const int lim_lo = MASKED ? i + off - a.win_lo : 0;
+
+    f32x16 o[C::NDB];   // O^T: rows = head-dim columns, column = this lane's query
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[d][v] = 0.f;
+    }
+    float mrow = -INFINITY, lsum = 0.f;   // running maximum (log2 units) and this lane's partial sum
+
+    for (int u = 0; u < C::NS - 1 && u < n_kt; ++u) issue_tile(u);
+    for (int u = 0; u < n_kt; ++u) {
+        const char* buf = buf_of(u);
+        dq_wait_vmem_but(kOpsPerTile * (min(u + C::NS - 2, n_kt - 1) - u));
+        __syncthreads();
+        if (u + C::NS - 1 < n_kt) issue_tile(u + C::NS - 1);
+        const char* lk = buf + C::BUF_K;
+        const char* lv = buf + C::BUF_V;
+        const int j0 = (kt_b + u) * BN;
+        const bool edge = !((j0 + BN <= si.len_k) && (i0 + BQ <= si.len_q) &&
+                            (!MASKED || (j0 + BN - 1 <= i0 + off + a.win_hi && j0 >= i0 + BQ - 1 + off - a.win_lo)));
+
+        f32x16 st[C::NJB];
+#pragma unroll
+        for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st[jb][v] = 0.f;
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c)
+                mma16(st[jb], dq_read_row<T, C::ROWB>(lk, 32 * jb + l32, 16 * c + 8 * h), qreg[c]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, C::NJB * C::NC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NJB * C::NC, 0);
+
+        // ---- logits in log2 units; keys this row does not see are -inf
+        const float fdist = (float)(j0 + 4 * h - i - off);
+        auto logits = [&](auto masked) {
+#pragma unroll
+            for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float x = st[jb][v] * scale2;
+                    if constexpr (ALIBI)
+                        x = fmaf(nsl2, fabsf(fdist + (float)(32 * jb + 8 * (v >> 2) + (v & 3))), x);
+                    if constexpr (decltype(masked)::value) {
+                        const int j = j0 + 32 * jb + acc_row(v, h);
+                        x = (j < lim && j >= lim_lo) ? x : -INFINITY;
+                    }
+                    st[jb][v] = x;
+                }
+            }
+        };
+        if (edge)
+            logits(std::true_type{});
+        else
+            logits(std::false_type{});
+
+        // ---- online softmax: the tile's maximum over both lanes of the row
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, st[jb][v]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(mrow, tmax);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;   // a row with no key yet keeps P = 0
+        const float corr = __builtin_amdgcn_exp2f(mrow - mref);
+        lsum *= corr;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[d][v] *= corr;
+        }
+#pragma unroll
+        for (int jb = 0; jb < C::NJB; ++jb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(st[jb][v] - mref);
+                lsum += p;
+                st[jb][v] = p;
+            }
+        }
+        mrow = mnew;
+
+        // ---- O^T += V^T P^T: A = V^T via transposing reads, B = P (this lane's query, 8 keys per slice)
+#pragma unroll
+        for (int c = 0; c < C::NJC; ++c) {
+            const int jb = c >> 1, vb = 8 * (c & 1);
+            op_t pb;
+            float tp[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) tp[t] = st[jb][vb + t];
+            to_op(pb, tp);
+            const int r1 = 16 * c + 4 * h, r2 = 16 * c + 8 + 4 * h;
+#pragma unroll
+            for (int d = 0; d < C::NDB; ++d) mma16(o[d], dq_read_col<T, C::ROWB>(lv, r1, r2, 32 * d, lane), pb);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NJC * C::NDB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NJC * C::NDB, 0);
+    }
+
+    // ---- epilogue: O = O^T / l (this lane's query row), LSE = (m + log2 l) ln 2
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (!row_ok) return;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    T* orow = reinterpret_cast<T*>(a.o) + seq_off(a.so, varlen, b, si.q0) + (long long)hq * a.so.h +
+              (long long)i * a.so.r;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int col = 32 * d + acc_row(v, h);
+            if (col < a.d) store_elem(orow, col, o[d][v] * inv);
+        }
+    }
+    if (h == 0) {
+        const long long li = varlen ? (long long)hq * a.total_q + si.q0 + i : ((long long)b * a.hq + hq) * a.seqlen_q + i;
+        a.lse[li] = ltot > 0.f ? (mrow + log2f(ltot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <class T, int HD, bool MASKED, bool ALIBI>
+__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
+    // all query tiles of all q-heads of one (sequence, kv-head) on one XCD;
+    // masked: workgroup p takes the tiles p and (last - p)
+    constexpr int BQ = DqCfg<T, HD>::BQ;
+    const int G = a.hq / a.hkv;
+    const int nblk_m = (a.seqlen_q + BQ - 1) / BQ;
+    const int n_pair = MASKED ? (nblk_m + 1) / 2 : nblk_m;
+    const int per_group = n_pair * G;
+    int grp, slot;
+    {
+        const int groups = a.hkv * a.batch;
+        if (groups % kXcds == 0) {
+            const int xcd = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
+            grp = (s / per_group) * kXcds + xcd;
+            slot = s % per_group;
+        } else {
+            grp = blockIdx.x / per_group;
+            slot = blockIdx.x % per_group;
+        }
+    }
+    const int hkv = grp % a.hkv;
+    const int b = grp / a.hkv;
+    const int hq = hkv * G + slot / n_pair;
+    const int p = slot % n_pair;
+    const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
+    if (MASKED) {
+        const int nq = (si.len_q + BQ - 1) / BQ;
+        const int m2 = nq - 1 - p;
+        if (m2 > p) {
+            fwd_tile<T, HD, MASKED, ALIBI>(m2, a, b, hq, hkv, si, smem);
+            __syncthreads();
+        }
+        if (p < nq && p <= m2) fwd_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+    } else {
+        fwd_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+    }
+}
+
+template <class T, int HD>
+static void launch_fwd_mfma_t(const FwdArgs& a, bool masked, hipStream_t st) {
+    constexpr int BQ = DqCfg<T, HD>::BQ;
+    const int nblk_m = (a.seqlen_q + BQ - 1) / BQ;
+    const unsigned grid = (unsigned)((masked ? (nblk_m + 1) / 2 : nblk_m) * a.hq * a.batch);
+    const bool alibi = a.alibi != nullptr;
+    if (masked) {
+        if (alibi) fwd_mfma_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
+        else fwd_mfma_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
+    } else {
+        if (alibi) fwd_mfma_kernel<T, HD, false, true><<<grid, kThreads, 0, st>>>(a);
+        else fwd_mfma_kernel<T, HD, false, false><<<grid, kThreads, 0, st>>>(a);
+    }
+}
+
+void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
+    if (dtype == ATTN_DTYPE_BF16) {
+        if (hd == 64) launch_fwd_mfma_t<bf16_t, 64>(a, masked, st);
+        else launch_fwd_mfma_t<bf16_t, 128>(a, masked, st);
+    } else {
+        if (hd == 64) launch_fwd_mfma_t<f16_t, 64>(a, masked, st);
+        else launch_fwd_mfma_t<f16_t, 128>(a, masked, st);
+    }
+}
+
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_dq_t<bf16_t, 64>(a, masked, st);
