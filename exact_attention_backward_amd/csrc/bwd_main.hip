@@ -604,14 +604,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
 // both fit in the register budget of two waves per SIMD, and the two waves
 // of a SIMD overlap each other's MFMA, exponential and LDS work.  The dS wave
 // runs one tile behind so that a single barrier per tile publishes P.
-// Query-side tiles (Q, dO, LSE, D) are prefetched three tiles ahead into a
-// ring of five LDS buffers (the dS wave still reads tile t-1).
+// Query-side tiles (Q, dO, LSE, D) are prefetched two tiles ahead into a
+// ring of four LDS buffers (the dS wave still reads tile t-1).
 //
-// The loop body is kept lean: LDS addresses are per-lane constants combined
-// with the buffer offset by one add and an XOR per operand (the swizzle only
-// permutes address bits the loop indices touch), tile coordinates advance
-// incrementally, and every wave issues the same three copies per tile (past
-// the last tile with an empty range), so each wait count is a constant.
+// The loop body is kept lean: the loops are unrolled by the ring length, so
+// every LDS address is a per-lane constant plus an immediate (the swizzle
+// only permutes address bits the ring offsets leave zero), tile coordinates
+// advance incrementally, and every wave issues the same three copies per
+// tile (past the last tile with a scalar offset beyond every range), so each
+// wait count is a constant.
 //
 // Masking: a padded query row (past the sequence) has Q = dO = 0 and
 // LSE = D = 0 in LDS, so its P is finite and its P dO and dS terms are zero;
@@ -817,7 +818,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // dS block cursors: the block (q-head, first 32-row block of the tile,
     // key tile n) of tile t and of tile t-1; blocks from ds_lim on lie past
     // the sequence (or, for malformed overlapping cu_seqlens, past the buffer)
-    // and get an empty range
+    // and get an empty range (their stores are dropped)
     const int ds_lim = STORE_DS ? (int)min((long long)(si.len_q + kDsRows - 1) / kDsRows, a.ds_qb - ds_qb0) : 0;
     const long long ds_blk_n = STORE_DS ? (long long)a.ds_nn * kDsBlockBytes : 0;   // bytes per 32-row block
     const char* ds_p0 = STORE_DS ? reinterpret_cast<const char*>(a.ds) +

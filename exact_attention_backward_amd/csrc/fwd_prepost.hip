@@ -187,13 +187,6 @@ __global__ __launch_bounds__(256) void zero_blocks_kernel(T* p, Strides s, BwdAr
     for (int j = threadIdx.x; j < si.len_k; j += blockDim.x) store_elem(row, j, 0.f);
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* p, long long n16) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-         i += (long long)gridDim.x * blockDim.x)
-        p[i] = z;
-}
-
 // ---------------------------------------------------------------------------
 // postprocess: dQ[row, h, :] = T(scale * acc[h, row, :])
 // ---------------------------------------------------------------------------
@@ -253,14 +246,6 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st
         if (hd == 64) launch_fwd_t<float, 64>(a, masked, st);
         else launch_fwd_t<float, 128>(a, masked, st);
     }
-}
-
-void launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
-    const long long n16 = (long long)(bytes / 16);
-    if (n16 == 0) return;
-    long long blocks = (n16 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<u32x4*>(p), n16);
 }
 
 void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st) {

@@ -156,7 +156,6 @@ constexpr int kBwdBlockN = 128;
 void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 // the MFMA forward (bf16 and fp16, no elementwise bias)
 void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
-void launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // zero every sequence's [Hq, len_q, len_k] block of a [b, h, i, j] tensor with strides s
 void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st);
 void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
