@@ -33,10 +33,10 @@ def setup(p):
     return x, dev, kw, cu
 
 
-def run_backward(p, dev, o, lse, kw, deterministic=None, dq_algo="separate"):
+def run_backward(p, dev, o, lse, kw, deterministic=None, dq_algo="separate", extra=None):
     from exact_attention_backward_amd import api
     det = p.deterministic if deterministic is None else deterministic
-    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, det, dq_algo=dq_algo, **kw)
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, det, dq_algo=dq_algo, **kw, **(extra or {}))
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     # the two calls the benchmark times: attn_bwd_preprocess, attn_bwd_full
     plan.run_full(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv)
@@ -46,12 +46,22 @@ def run_backward(p, dev, o, lse, kw, deterministic=None, dq_algo="separate"):
     return dq, dk, dv
 
 
-def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate"):
-    """samples: list of (sequence, kv_head)."""
+def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate", window=None, alibi=None,
+                  packed=False):
+    """samples: list of (sequence, kv_head).  window / alibi (slopes, one per
+    q-head): local mask and ALiBi on both sides; packed: Q, K, V as views of
+    one [B, S, 3, H, D] tensor (dense, Hq == Hkv)."""
     from exact_attention_backward_amd import api
     x, dev, kw, cu = setup(p)
+    if packed:
+        qkv = torch.empty(p.batch, p.seqlen_q, 3, p.heads_q, p.head_dim, dtype=dev["q"].dtype, device="cuda")
+        for slot, n in enumerate(("q", "k", "v")):
+            qkv[:, :, slot].copy_(dev[n])
+            dev[n] = qkv[:, :, slot]
+    slopes = None if alibi is None else np.asarray(alibi, np.float32)
+    extra = dict(window=window, alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda())
     print(f"{p.name}: inputs ready", flush=True)
-    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, **kw)
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, **kw, **extra)
     torch.cuda.synchronize()
     g = p.heads_q // p.heads_kv
     ranges = []
@@ -61,7 +71,8 @@ def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate")
         else:
             q0, q1 = b * p.seqlen_q, (b + 1) * p.seqlen_q
         ranges.append((q0, q1))
-        fw = oracle.group_forward(x["q"], x["k"], x["v"], p.scale, p.causal, b, hk, *cu)
+        fw = oracle.group_forward(x["q"], x["k"], x["v"], p.scale, p.causal, b, hk, *cu, window=window,
+                                  alibi_slopes=slopes)
         for h, (oh, lh) in fw.items():
             oh = round_like(oh, p.dtype).astype(np.float32)
             lh = lh.astype(np.float32)
@@ -72,7 +83,7 @@ def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate")
                 o[b, :, h] = torch.from_numpy(oh).to(o.dtype).cuda()
                 lse[b, h] = torch.from_numpy(lh).cuda()
     torch.cuda.synchronize()
-    outs = [run_backward(p, dev, o, lse, kw, deterministic, dq_algo) for _ in range(repeats)]
+    outs = [run_backward(p, dev, o, lse, kw, deterministic, dq_algo, extra) for _ in range(repeats)]
     print(f"{p.name}: backward done", flush=True)
     for rep in outs[1:]:
         for a, bb in zip(outs[0], rep):
@@ -82,7 +93,7 @@ def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate")
     lse_h = lse.cpu().numpy().astype(np.float64)
     for (b, hk), (q0, q1) in zip(samples, ranges):
         rdq, rdk, rdv = oracle.group_backward(x["q"], x["k"], x["v"], o_h, x["do"], lse_h, p.scale, p.causal, b, hk,
-                                              *cu)
+                                              *cu, window=window, alibi_slopes=slopes)
         if p.varlen:
             k0, k1 = int(cu[1][b]), int(cu[1][b + 1])
             gk, gv = to_host(dk[k0:k1, hk]), to_host(dv[k0:k1, hk])
@@ -108,6 +119,19 @@ def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate")
         lhs = dv_h.sum(axis=1)                                             # [B, Hkv, D]
         rhs = do_h.reshape(p.batch, p.seqlen_q, p.heads_kv, g, p.head_dim).sum(axis=(1, 3))
         assert rel_err(lhs, rhs) <= TOL[p.dtype]
+
+
+@pytest.mark.parametrize("dq_algo", ["stored_ds", "separate"])
+def test_headline_window_alibi_sampled(dq_algo):
+    """The headline shape with a causal sliding window of 1024 keys and ALiBi."""
+    slopes = [2.0 ** (-8.0 * (h + 1) / 16) for h in range(16)]
+    sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)], dq_algo=dq_algo, window=(1024, -1), alibi=slopes)
+
+
+@pytest.mark.parametrize("dq_algo", ["stored_ds", "atomic"])
+def test_headline_packed_qkv_sampled(dq_algo):
+    """The headline shape with Q, K and V read from one packed [B, S, 3, H, D] tensor."""
+    sampled_check(datagen.workload("c3"), [(1, 4)], dq_algo=dq_algo, packed=True)
 
 
 def test_fp32_workload_full():
