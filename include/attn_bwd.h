@@ -2,7 +2,7 @@
  * attn_bwd.h -- C ABI of the MI355X (gfx950) exact-attention backward library.
  *
  * The library computes the gradient of exact softmax attention,
- *     O = softmax(s * Q K^T [+ causal mask]) V,
+ *     O = softmax(s * Q K^T [+ ALiBi] [+ bias] [+ causal / local mask]) V,
  * i.e. dQ, dK and dV from Q, K, V, O, dO and the per-row log-sum-exp LSE,
  * as a fused, tiled pass that recomputes the probabilities from LSE instead
  * of storing them.  The operation and its stages are those of the
@@ -231,14 +231,17 @@ int attn_bwd_preprocess(const attn_shape_t* shape, const void* o, const void* do
  *    writes every accumulator row once (no atomics; bitwise reproducible
  *    whatever shape->deterministic says);
  *  - shape->dq_algo == ATTN_DQ_STORED_DS: the key-stationary kernel stores
- *    dS (bf16) in the workspace and a second kernel writes every accumulator
- *    row once as the sum of dS K over the key blocks the row can see;
+ *    dS (bf16 or fp16) in the workspace and a second kernel writes every
+ *    accumulator row once as the sum of dS K over the key blocks the row can
+ *    see;
  *  - shape->dq_algo == ATTN_DQ_ATOMIC: the partials are added with fp32
  *    atomics, or, when shape->deterministic, in a fixed order per dQ tile so
  *    that repeated runs are bitwise identical.  The accumulator must then
  *    have been cleared by attn_bwd_preprocess for this shape since the last
- *    attn_bwd (running attn_bwd twice without it adds dQ twice).
- * q, k, v, dout, lse, delta: inputs; dk, dv: outputs; workspace: in/out. */
+ *    attn_bwd (running attn_bwd twice without it adds dQ twice).  This is
+ *    the mode of the elementwise bias: it also writes dBias when asked.
+ * q, k, v, dout, lse, delta: inputs; dk, dv (and shape->dbias): outputs;
+ * workspace: in/out. */
 int attn_bwd(const attn_shape_t* shape, const void* q, const void* k, const void* v,
              const void* dout, const float* lse, const float* delta,
              void* workspace, size_t workspace_bytes, void* dk, void* dv, void* stream);
