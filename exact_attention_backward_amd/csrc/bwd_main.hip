@@ -633,13 +633,13 @@ struct KvCfg {
     static constexpr int BUF_DUMP = 2 * TILE + 512;   // target of the empty statistic copies
     static constexpr int BUF_BYTES = 2 * TILE + 768;
     static constexpr int NMB = BM / 32;              // 32-row blocks of a query tile
-    static constexpr int PSLOT = NMB * 16 * 64 * 4;  // P of one pair: 16 fp32 per lane per row block
+    static constexpr int NIC = BM / 16;              // 16-wide chunks of the query rows
+    static constexpr int PSLOT = NIC * 16 * 64;      // P of one pair: its NIC operand chunks per lane
     static constexpr int OFF_P = NBUF * BUF_BYTES;   // [pair][tile parity] P slots
     static constexpr int OFF_CONST = OFF_P + 4 * 2 * PSLOT;   // 16 bytes per wave, see kv_tile
     static constexpr int LDS_BYTES = OFF_CONST + kKvWaves * 16;
     static constexpr int NC = HD / 16;               // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;              // 32-column blocks of the head dim
-    static constexpr int NIC = BM / 16;              // 16-wide chunks of the query rows
     static constexpr int OPS = 3;                    // copy instructions per tile and wave
     static_assert(TileCopy<ROWB, BM, kKvWaves>::N == 1, "one segment per wave and tensor");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -865,13 +865,14 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // tile t (P wave), or D and the partner's P of tile t-1 (dS wave)
         const float* lst = reinterpret_cast<const float*>(
             smem + (R == 0 ? CUR + C::BUF_LSE : PREV + C::BUF_DL) + 16 * h);
-        f32x4 stat[NMB * 4], pin[NMB * 4];
+        f32x4 stat[NMB * 4];
+        u32x4 pin[C::NIC];
 #pragma unroll
         for (int q = 0; q < NMB * 4; ++q) stat[q] = *reinterpret_cast<const f32x4*>(lst + 8 * q);
         if constexpr (R == 1) {
             const int psr = pslots + ((K + 1) & 1) * C::PSLOT + lane * 16;   // slot of tile t-1
 #pragma unroll
-            for (int q = 0; q < NMB * 4; ++q) pin[q] = *reinterpret_cast<const f32x4*>(smem + psr + q * 1024);
+            for (int c = 0; c < C::NIC; ++c) pin[c] = *reinterpret_cast<const u32x4*>(smem + psr + c * 1024);
         }
 
         // ---- X = Q K^T (P wave) or dO V^T (dS wave) for tile t
@@ -955,8 +956,6 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                             }
                             xc[mb][v] = p;
                         }
-                        const f32x4 pv = {xc[mb][4 * q4], xc[mb][4 * q4 + 1], xc[mb][4 * q4 + 2], xc[mb][4 * q4 + 3]};
-                        lds_write(smem, ps + (mb * 4 + q4) * 1024, pv);
                     }
                 }
             };
@@ -970,17 +969,26 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tp[u] = xc[c >> 1][8 * (c & 1) + u];
                 to_op(opa[c], tp);
+                // P goes to the partner in the operand type it already has
+                // for P^T dO (half the LDS bytes of fp32)
+                lds_write(smem, ps + c * 1024, __builtin_bit_cast(u32x4, opa[c]));
             }
         } else {
-            // ---- dS = P (dP - D) with P from the partner wave
+            // ---- dS = P (dP - D) with P from the partner wave (the value
+            // its dV product used, rounded to the operand type)
+            float pf[C::NIC][8];
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) from_op(__builtin_bit_cast(op_t, pin[c]), pf[c]);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 dl = stat[mb * 4 + q4];
-                    const f32x4 pv = pin[mb * 4 + q4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) xp[mb][4 * q4 + e] = pv[e] * (xp[mb][4 * q4 + e] - dl[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * q4 + e;
+                        xp[mb][v] = pf[2 * mb + (v >> 3)][v & 7] * (xp[mb][v] - dl[e]);
+                    }
                 }
             }
 #pragma unroll

@@ -111,6 +111,21 @@ __device__ __forceinline__ void to_op(f32x8& o, const float* x) {
     for (int t = 0; t < 8; ++t) o[t] = x[t];
 }
 
+// MFMA operand of a 16-bit type -> its eight values in fp32 (exact).
+__device__ __forceinline__ void from_op(const bf16x8& o, float* x) {
+    const u32x4 w = __builtin_bit_cast(u32x4, o);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        x[2 * t] = bf16_lo(w[t]);
+        x[2 * t + 1] = bf16_hi(w[t]);
+    }
+}
+__device__ __forceinline__ void from_op(const f16x8& o, float* x) {
+    const f32x8 f = __builtin_convertvector(o, f32x8);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = f[t];
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles: row-major, 16-byte chunks XOR-swizzled by a function of the row.
 // LDS serves 256 bytes per cycle from 64 four-byte banks, so a 16-byte chunk
