@@ -121,8 +121,11 @@ typedef enum attn_dtype {
                                   P and dS are rounded to fp16 like they are to bf16 */
 } attn_dtype_t;
 
-/* How attn_bwd produces dQ (both reach the same result up to fp32 summation
- * order; see attn_bwd).
+/* How attn_bwd produces dQ (the modes agree up to fp32 summation order and
+ * one rounding point: for bf16/fp16, the dK/dV kernel of the separate and
+ * stored-dS modes forms dS = P (dP - D) from P after its rounding to the I/O
+ * type, the operand its dV product uses, where the atomic kernel and the
+ * separate dQ pass use P in fp32; see attn_bwd).
  *  ATTN_DQ_SEPARATE: a query-stationary second pass recomputes S and dP per
  *    (query tile, key tile) and writes each dQ row once: no atomics, bitwise
  *    reproducible; seven contractions per tile pair instead of five.
