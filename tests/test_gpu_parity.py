@@ -551,6 +551,9 @@ SEQUSED_CASES = [
     ("bf16", 4, 2, 128, True, (70, 300, 129, 1), (90, 260, 129, 40), (70, 211, 0, 1), (33, 260, 100, 40)),
     ("bf16", 2, 2, 64, False, (200, 65, 130), (150, 300, 130), (199, 1, 130), (150, 129, 64)),
     ("f16", 4, 1, 128, True, (257, 40), (257, 300), (250, 40), (257, 170)),
+    # a sequence with no used keys (its rows: LSE -inf, O = dQ = 0) and an
+    # empty sequence (cu_seqlens repeats an offset) between two others
+    ("bf16", 2, 2, 128, True, (100, 0, 64), (120, 0, 200), (100, 0, 64), (0, 0, 150)),
 ]
 
 
