@@ -525,9 +525,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             } else {
                 rank = n;
             }
+            // The counter and the dQ adds are device-scope atomics, which the
+            // memory side performs (they bypass the per-XCD L2s), and the
+            // tile's adds only write: observing the count with a coherent
+            // relaxed load, then issuing the adds, orders them after the
+            // previous contributor's.  No acquire fence: on this chip one
+            // invalidates the XCD's whole L2, for every step of every
+            // workgroup (measured ten times slower overall).
             if (threadIdx.x == 0) {
                 int spins = 0;
-                while (__hip_atomic_load(sem, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != rank) {
+                while (__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != rank) {
                     __builtin_amdgcn_s_sleep(2);
                     if (++spins > (1 << 24)) {
                         __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -536,7 +543,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                 }
             }
             __syncthreads();
-            __atomic_thread_fence(__ATOMIC_ACQUIRE);
         }
         {
             float* dq_tile = dqa + (long long)i0 * HD;   // uniform base of this query tile
@@ -559,9 +565,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                 add_dq(std::true_type{});
         }
         if (a.deterministic) {
-            __threadfence();
+            // every wave's adds have been performed (vmcnt counts atomics
+            // until the memory side acknowledges them) before the next
+            // contributor is let in; a release fence would also write back
+            // the whole L2, which holds nothing the next contributor reads
+            wait_vmem();
             __syncthreads();
-            if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         }
         // the next tile's copies are complete; on full tiles of the atomic
