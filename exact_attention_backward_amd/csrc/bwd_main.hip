@@ -952,6 +952,10 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             const int dj = j - (i0 + off + 4 * h);   // key column relative to this lane's first row
             const int dj_hi = dj - a.win_hi, dj_lo = dj + a.win_lo;
             const float fdj = (float)dj;   // ALiBi distance of row r + e: |fdj - (r + e)|
+            // rows past the sequence (Q = dO = 0, LSE = D = 0): zero P with
+            // ALiBi, whose term a negative slope makes grow with the distance
+            // (an infinite P would turn 0 * P into NaN for real keys)
+            const int row_lim = si.len_q - i0 - 4 * h;
             auto softmax = [&](auto masked) {
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
@@ -969,7 +973,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                                 if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
                                 p = __builtin_amdgcn_exp2f(x);
                                 // i + off - lo <= j <= i + off + hi, i = i0 + r + 4h + e
-                                p = (dj_hi <= r + e && dj_lo >= r + e) ? p : 0.f;
+                                bool vis = dj_hi <= r + e && dj_lo >= r + e;
+                                if constexpr (ALIBI) vis = vis && r + e < row_lim;
+                                p = vis ? p : 0.f;
                             } else {
                                 float x = fmaf(xc[mb][v], scale2, -lse[e] * kLog2e);
                                 if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
@@ -980,7 +986,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                     }
                 }
             };
-            if (MASKED && (i0 < diag_hi || i0 > diag_lo))
+            if ((MASKED && (i0 < diag_hi || i0 > diag_lo)) || (ALIBI && i0 + BM > si.len_q))
                 softmax(std::true_type{});
             else
                 softmax(std::false_type{});

@@ -309,6 +309,27 @@ def test_alibi_zero_slopes_equal_plain(dq_algo):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
+@pytest.mark.parametrize("d,s,causal", [(128, 700, False), (128, 700, True), (64, 650, False)])
+def test_alibi_negative_slopes_with_padded_rows(d, s, causal, dq_algo):
+    """Negative slopes (the logit grows with the distance from the diagonal)
+    on a length that leaves padded rows in the last query tile: those rows
+    must not reach real keys' gradients (their ALiBi term alone would
+    overflow exp2; 0 * inf would be NaN)."""
+    p = small_problem("bf16", 1, 4, 2, s, s, d, causal, 44)
+    slopes = np.array([-0.075, -0.15, -0.225, -0.3], np.float32)
+    assert s % (32 if d == 128 else 64) != 0
+    assert float(np.max(-slopes)) * s * 1.4427 > 128      # exp2 of the padded rows' term overflows
+    r = Run(p, alibi=slopes)
+    print(f"negative alibi d{d} s{s} causal={causal} dq={dq_algo}", flush=True)
+    dq, dk, dv, plan = r.gpu_backward(dq_algo=dq_algo)
+    rdq, rdk, rdv = r.oracle_backward()
+    for n, g, ref in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        h = to_host(g)
+        assert np.all(np.isfinite(h)), f"{n} has non-finite values"
+        assert_close(n, h, ref, p.dtype)
+
+
 # attn_bwd_full against the three-call path: (case, window, alibi)
 FULL_CASES = [
     (CASES[0], None, False),      # bf16 dense causal D128
