@@ -9,7 +9,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattnbwd.so")
+# the in-tree build; ATTN_BWD_LIB may name another build of the same sources
+LIB_PATH = os.environ.get("ATTN_BWD_LIB") or os.path.join(_PKG, "libattnbwd.so")
 
 ATTN_OK = 0
 ATTN_ERR_NULL_ARG = 1
@@ -79,6 +80,9 @@ class AttnShape(ctypes.Structure):
         ("bias_strides", TensorStrides),
         ("dbias", ctypes.c_void_p),
         ("dbias_strides", TensorStrides),
+        ("max_workspace_bytes", ctypes.c_int64),
+        ("cu_seqlens_q_host", ctypes.c_void_p),
+        ("cu_seqlens_k_host", ctypes.c_void_p),
     ]
 
 

@@ -61,7 +61,8 @@ DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_
 
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-               window=None, alibi_slopes=None, bias=None, dbias=None):
+               window=None, alibi_slopes=None, bias=None, dbias=None, max_workspace_bytes=0,
+               cu_seqlens_host=None):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
     "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
@@ -74,7 +75,11 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     bias / dbias (atomic dQ mode): tensors indexed [b, h, i, j] (b the
     sequence for varlen; keys contiguous, any batch/head/row strides, 0 to
     broadcast the bias); the bias is added to the logits and dbias receives
-    dS."""
+    dS.  max_workspace_bytes caps the stored-dS workspace (kv-head groups in
+    chunks, or the separate mode when not even one fits).  cu_seqlens_host =
+    (cu_q, cu_k): contiguous int32 CPU tensors holding the offsets, kept
+    alive by the caller while the shape is used; with them the stored-dS
+    workspace is sized exactly."""
     s = L.AttnShape()
     if q.dtype not in _DTYPES:
         s.dtype = -1
@@ -110,6 +115,12 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
         setattr(s, name, t.data_ptr())
         st = getattr(s, name + "_strides")
         st.batch, st.head, st.row = t.stride(0), t.stride(1), t.stride(2)
+    if cu_seqlens_host is not None:
+        for name, t in zip(("cu_seqlens_q_host", "cu_seqlens_k_host"), cu_seqlens_host):
+            if t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("host cu_seqlens must be contiguous int32 CPU tensors")
+            setattr(s, name, t.data_ptr())
+    s.max_workspace_bytes = int(max_workspace_bytes)
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
@@ -212,11 +223,16 @@ class BackwardPlan:
 
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                  max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-                 window=None, alibi_slopes=None, bias=None, dbias=None):
+                 window=None, alibi_slopes=None, bias=None, dbias=None, max_workspace_bytes=0,
+                 host_offsets=True):
+        # host copies of the offsets size the stored-dS workspace exactly
+        host = None
+        if cu_seqlens_q is not None and host_offsets:
+            host = (cu_seqlens_q.to("cpu", torch.int32).contiguous(), cu_seqlens_k.to("cpu", torch.int32).contiguous())
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
                                 max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window, alibi_slopes,
-                                bias, dbias)
-        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes, bias, dbias)
+                                bias, dbias, max_workspace_bytes, host)
+        self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes, bias, dbias, host)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
         if nbytes == 0:

@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "launch.h"
 
 using namespace attn;
@@ -53,6 +56,7 @@ int validate_shape(const attn_shape_t* s) {
     if (s->dq_algo != ATTN_DQ_SEPARATE && s->dq_algo != ATTN_DQ_ATOMIC && s->dq_algo != ATTN_DQ_STORED_DS)
         return ATTN_ERR_UNSUPPORTED;
     if (s->dq_algo == ATTN_DQ_STORED_DS && s->dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+    if (s->max_workspace_bytes < 0) return ATTN_ERR_BAD_SHAPE;
     // element counts must stay addressable with 64-bit offsets and 32-bit row counts
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
@@ -130,21 +134,106 @@ int nblk_m(const attn_shape_t* s) {
 size_t sem_bytes(const attn_shape_t* s) {
     return align_up((size_t)s->batch * s->num_heads_q * nblk_m(s) * sizeof(int32_t));
 }
-// stored-dS mode: [first query block of each sequence, int32][dS blocks]
-long long ds_qb(const attn_shape_t* s) {
-    if (varlen(s)) return (long long)(s->total_q + kDsRows - 1) / kDsRows + s->batch;
-    return (long long)s->batch * ((s->seqlen_q + kDsRows - 1) / kDsRows);
+// ---- stored-dS mode: [block table][dS blocks]
+// Query rows per tile of the dK/dV kernel (its dS blocks come per tile).
+int ds_bm(const attn_shape_t* s) { return kv_block_m(padded_hd(s)); }
+// Entries of the per-query-tile table: every sequence's tiles.
+long long ds_tiles(const attn_shape_t* s) {
+    const int bm = ds_bm(s);
+    if (varlen(s)) return (long long)s->total_q / bm + s->batch;
+    return (long long)s->batch * ((s->seqlen_q + bm - 1) / bm);
 }
-int ds_nn(const attn_shape_t* s) { return (s->seqlen_k + kDsKeys - 1) / kDsKeys; }
-size_t ds_table_bytes(const attn_shape_t* s) {
-    return s->dq_algo == ATTN_DQ_STORED_DS ? align_up((size_t)(s->batch + 1) * sizeof(int32_t)) : 0;
+// dS blocks of one sequence: the blocks of each query tile's visiting key tiles
+long long ds_seq_blocks(const attn_shape_t* s, int len_q, int len_k) {
+    const int bm = ds_bm(s);
+    long long n = 0;
+    for (int m = 0; m * bm < len_q; ++m) n += ds_tile_blocks(m, bm, len_q, len_k, win_lo(s), win_hi(s), masked(s));
+    return n;
 }
-size_t ds_bytes(const attn_shape_t* s) {
-    if (s->dq_algo != ATTN_DQ_STORED_DS) return 0;
-    return (size_t)s->num_heads_q * (size_t)ds_qb(s) * (size_t)ds_nn(s) * kDsBlockBytes;
+// dS blocks per q-head: exact for dense problems and for varlen ones whose
+// offsets the caller also gave in host memory (without used lengths); else
+// the bound of every sequence's full rectangle of 32-row and 128-key blocks,
+// sum_b (len_b / 32 + blocks per tile) * ceil(seqlen_k / 128)
+long long ds_head_blocks(const attn_shape_t* s) {
+    if (!varlen(s)) return (long long)s->batch * ds_seq_blocks(s, s->seqlen_q, s->seqlen_k);
+    if (s->cu_seqlens_q_host != nullptr && s->cu_seqlens_k_host != nullptr && s->seqused_q == nullptr &&
+        s->seqused_k == nullptr) {
+        long long n = 0;
+        for (int b = 0; b < s->batch; ++b) {
+            // clamped as the kernels clamp the device offsets
+            const int* cq = s->cu_seqlens_q_host;
+            const int* ck = s->cu_seqlens_k_host;
+            int q0 = std::min(std::max(cq[b], 0), s->total_q), q1 = std::min(std::max(cq[b + 1], q0), s->total_q);
+            int k0 = std::min(std::max(ck[b], 0), s->total_k), k1 = std::min(std::max(ck[b + 1], k0), s->total_k);
+            n += ds_seq_blocks(s, std::min(q1 - q0, s->seqlen_q), std::min(k1 - k0, s->seqlen_k));
+        }
+        return n;
+    }
+    const long long per_tile = ds_bm(s) / kDsRows;
+    return ((long long)s->total_q / kDsRows + per_tile * s->batch) * ((s->seqlen_k + kDsKeys - 1) / kDsKeys);
+}
+
+// How attn_bwd runs for a shape: the dQ mode after the workspace cap
+// (max_workspace_bytes) and, for the stored-dS mode, the kv-heads per
+// launch (their q-heads' dS fits the workspace at once).
+struct Plan {
+    int algo;
+    int chunk;            // kv-heads per launch (stored dS), else all
+    long long head_blocks;   // stored dS: blocks per q-head
+};
+size_t base_bytes(const attn_shape_t* s, int algo, bool with_accum);
+Plan plan(const attn_shape_t* s) {
+    Plan p{s->dq_algo, s->num_heads_kv, 0};
+    if (s->dq_algo != ATTN_DQ_STORED_DS) return p;
+    p.head_blocks = ds_head_blocks(s);
+    // block indices are int32 in the table (a q-head's dS past 2^31 blocks,
+    // 16 TiB, could not be allocated anyway): the separate mode instead
+    if (p.head_blocks > 0x7fffffffLL) return Plan{ATTN_DQ_SEPARATE, s->num_heads_kv, 0};
+    const int G = s->num_heads_q / s->num_heads_kv;
+    const double per_kv = (double)G * (double)p.head_blocks * kDsBlockBytes;   // bytes of one kv-head group
+    if (s->max_workspace_bytes > 0) {
+        const double avail = (double)s->max_workspace_bytes - (double)base_bytes(s, ATTN_DQ_STORED_DS, true);
+        const double fit = avail > 0 ? std::floor(avail / std::max(per_kv, 1.0)) : 0.0;
+        p.chunk = (int)std::min<double>(s->num_heads_kv, fit);
+        if (p.chunk < 1) p = Plan{ATTN_DQ_SEPARATE, s->num_heads_kv, 0};   // not even one group fits
+    }
+    return p;
+}
+size_t ds_table_bytes(const attn_shape_t* s, int algo) {
+    return algo == ATTN_DQ_STORED_DS ? align_up((size_t)(s->batch + 1 + ds_tiles(s)) * sizeof(int32_t)) : 0;
+}
+size_t ds_bytes(const attn_shape_t* s, const Plan& p) {
+    if (p.algo != ATTN_DQ_STORED_DS) return 0;
+    const int G = s->num_heads_q / s->num_heads_kv;
+    return (size_t)p.chunk * G * (size_t)p.head_blocks * kDsBlockBytes;
+}
+// everything but the dS blocks
+size_t base_bytes(const attn_shape_t* s, int algo, bool with_accum) {
+    return (with_accum ? accum_bytes(s) : 0) + sem_bytes(s) + kErrBytes + ds_table_bytes(s, algo);
 }
 size_t workspace_bytes(const attn_shape_t* s) {
-    return accum_bytes(s) + sem_bytes(s) + kErrBytes + ds_table_bytes(s) + ds_bytes(s);
+    const Plan p = plan(s);
+    return base_bytes(s, p.algo, true) + ds_bytes(s, p);
+}
+
+// Byte offsets of the workspace parts from the workspace base.  The entry
+// points that take a workspace use the full layout; the no-allocation entry
+// point (attn_bwd_full only) leaves the accumulator out unless dQ is added
+// atomically, since the other dQ passes write dQ straight to the output.
+struct Layout {
+    Plan p;
+    size_t accum, sem, err, tab, ds, total;
+};
+Layout layout(const attn_shape_t* s, bool with_accum) {
+    Layout l;
+    l.p = plan(s);
+    l.accum = 0;
+    l.sem = with_accum ? accum_bytes(s) : 0;
+    l.err = l.sem + sem_bytes(s);
+    l.tab = l.err + kErrBytes;
+    l.ds = l.tab + ds_table_bytes(s, l.p.algo);
+    l.total = l.ds + ds_bytes(s, l.p);
+    return l;
 }
 
 int check_launch() {
@@ -208,44 +297,15 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
 namespace {
 
 // The enqueue steps behind the entry points; arguments already validated.
-void enqueue_preprocess(const attn_shape_t* s, const void* o, const void* dout, float* delta, void* workspace,
-                        hipStream_t hs) {
-    // the preprocess kernel also clears the counters and status words, and
-    // the accumulator where it is added into (atomic modes); the dS blocks
-    // are written before they are read
-    const bool atomic = s->dq_algo == ATTN_DQ_ATOMIC;
-    char* zero = reinterpret_cast<char*>(workspace) + (atomic ? 0 : accum_bytes(s));
-    const size_t zero_bytes = (atomic ? accum_bytes(s) : 0) + sem_bytes(s) + kErrBytes;
-    const attn_strides_t d = strides_of(s);
-    PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s),
-              s->head_dim, to_kernel(d.o), to_kernel(d.dout), reinterpret_cast<u32x4*>(zero),
-              (long long)(zero_bytes / 16)};
-    launch_preprocess(a, s->dtype, padded_hd(s), hs);
-    if (s->dq_algo == ATTN_DQ_STORED_DS && varlen(s))
-        launch_ds_table(s->cu_seqlens_q, s->batch, s->seqlen_q, s->total_q,
-                        reinterpret_cast<int*>(reinterpret_cast<char*>(workspace) + accum_bytes(s) + sem_bytes(s) +
-                                               kErrBytes),
-                        hs);
-}
 
-// dq_out: the separate and stored-dS modes write dQ = T(dq_scale * sum)
-// there instead of to the accumulator (null: the accumulator)
-void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* dout,
-                 const float* lse, const float* delta, void* workspace, void* dk, void* dv, void* dq_out,
-                 float dq_scale, hipStream_t hs) {
+// Kernel arguments shared by the backward kernels and the dS table kernel:
+// problem, workspace parts and, for the stored-dS mode, its table and blocks.
+BwdArgs bwd_args(const attn_shape_t* s, const Layout& l, void* workspace) {
     char* ws = reinterpret_cast<char*>(workspace);
     BwdArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.dout = dout;
-    a.lse = lse;
-    a.delta = delta;
-    a.dq_acc = reinterpret_cast<float*>(ws);
-    a.sem = reinterpret_cast<int*>(ws + accum_bytes(s));
-    a.err = reinterpret_cast<int*>(ws + accum_bytes(s) + sem_bytes(s));
-    a.dk = dk;
-    a.dv = dv;
+    a.dq_acc = reinterpret_cast<float*>(ws + l.accum);
+    a.sem = reinterpret_cast<int*>(ws + l.sem);
+    a.err = reinterpret_cast<int*>(ws + l.err);
     a.cu_q = s->cu_seqlens_q;
     a.cu_k = s->cu_seqlens_k;
     a.used_q = s->seqused_q;
@@ -253,6 +313,8 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
     a.batch = s->batch;
     a.hq = s->num_heads_q;
     a.hkv = s->num_heads_kv;
+    a.hkv0 = 0;
+    a.hkv_n = s->num_heads_kv;
     a.seqlen_q = s->seqlen_q;
     a.seqlen_k = s->seqlen_k;
     a.total_q = s->total_q;
@@ -264,8 +326,6 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
     a.win_lo = win_lo(s);
     a.win_hi = win_hi(s);
     a.alibi = s->alibi_slopes;
-    a.dq_out = s->dq_algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
-    a.dq_scale = dq_scale;
     const attn_strides_t d = strides_of(s);
     a.d = s->head_dim;
     a.sq = to_kernel(d.q);
@@ -279,27 +339,72 @@ void enqueue_bwd(const attn_shape_t* s, const void* q, const void* k, const void
     a.dbias = s->dbias;
     a.sbias = to_kernel(s->bias_strides);
     a.sdbias = to_kernel(s->dbias_strides);
-    if (s->dq_algo == ATTN_DQ_STORED_DS) {
-        char* tab = ws + accum_bytes(s) + sem_bytes(s) + kErrBytes;
-        a.ds_qb_base = varlen(s) ? reinterpret_cast<const int*>(tab) : nullptr;
-        a.ds = tab + ds_table_bytes(s);
-        a.ds_qb = ds_qb(s);
-        a.ds_nn = ds_nn(s);
+    if (l.p.algo == ATTN_DQ_STORED_DS) {
+        a.ds_tile_base = reinterpret_cast<const int*>(ws + l.tab);
+        a.ds_prefix = a.ds_tile_base + s->batch + 1;
+        a.ds_ntiles = (int)ds_tiles(s);
+        a.ds_head_blocks = l.p.head_blocks;
+        a.ds = ws + l.ds;
     }
+    return a;
+}
+
+void enqueue_preprocess(const attn_shape_t* s, const Layout& l, const void* o, const void* dout, float* delta,
+                        void* workspace, hipStream_t hs) {
+    // the preprocess kernel also clears the counters and status words, and
+    // the accumulator where it is added into (atomic modes); the dS blocks
+    // are written before they are read
+    const bool atomic = l.p.algo == ATTN_DQ_ATOMIC;
+    char* zero = reinterpret_cast<char*>(workspace) + (atomic ? l.accum : l.sem);
+    const size_t zero_bytes = l.tab - (atomic ? l.accum : l.sem);
+    const attn_strides_t d = strides_of(s);
+    PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s),
+              s->head_dim, to_kernel(d.o), to_kernel(d.dout), reinterpret_cast<u32x4*>(zero),
+              (long long)(zero_bytes / 16)};
+    launch_preprocess(a, s->dtype, padded_hd(s), hs);
+    if (l.p.algo == ATTN_DQ_STORED_DS) launch_ds_table(bwd_args(s, l, workspace), ds_bm(s), masked(s), hs);
+}
+
+// dq_out: the separate and stored-dS modes write dQ = T(dq_scale * sum)
+// there instead of to the accumulator (null: the accumulator)
+void enqueue_bwd(const attn_shape_t* s, const Layout& l, const void* q, const void* k, const void* v,
+                 const void* dout, const float* lse, const float* delta, void* workspace, void* dk, void* dv,
+                 void* dq_out, float dq_scale, hipStream_t hs) {
+    BwdArgs a = bwd_args(s, l, workspace);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dk = dk;
+    a.dv = dv;
+    a.dq_out = l.p.algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
+    a.dq_scale = dq_scale;
     // dBias blocks the kernel does not visit (masked tiles) must read zero
     if (s->dbias != nullptr) launch_zero_blocks(s->dbias, a.sdbias, s->dtype, a, hs);
-    launch_bwd(a, s->dtype, padded_hd(s), masked(s), s->dq_algo, hs);
-    if (s->dq_algo == ATTN_DQ_SEPARATE) {
+    if (l.p.algo == ATTN_DQ_STORED_DS) {
+        // kv-head groups in chunks whose dS fits the workspace: the dK/dV
+        // kernel stores the chunk's dS, the dQ pass consumes it
+        for (int h0 = 0; h0 < s->num_heads_kv; h0 += l.p.chunk) {
+            a.hkv0 = h0;
+            a.hkv_n = std::min(l.p.chunk, s->num_heads_kv - h0);
+            launch_bwd(a, s->dtype, padded_hd(s), masked(s), ATTN_DQ_STORED_DS, hs);
+            launch_bwd_dq_gemm(a, s->dtype, padded_hd(s), masked(s), hs);
+        }
+        return;
+    }
+    launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
+    if (l.p.algo == ATTN_DQ_SEPARATE) {
         BwdArgs e = a;
         e.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
         launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), hs);
-    } else if (s->dq_algo == ATTN_DQ_STORED_DS) {
-        launch_bwd_dq_gemm(a, s->dtype, padded_hd(s), masked(s), hs);
     }
 }
 
-void enqueue_postprocess(const attn_shape_t* s, const void* workspace, void* dq, float scale, hipStream_t hs) {
-    PostArgs a{reinterpret_cast<const float*>(workspace), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
+void enqueue_postprocess(const attn_shape_t* s, const Layout& l, const void* workspace, void* dq, float scale,
+                         hipStream_t hs) {
+    PostArgs a{reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + l.accum), dq, rows_q(s) * s->num_heads_q, s->num_heads_q,
                s->seqlen_q, s->total_q, varlen(s), scale, s->cu_seqlens_q, s->seqused_q, s->batch,
                s->head_dim, to_kernel(strides_of(s).dq)};
     launch_postprocess(a, s->dtype, padded_hd(s), hs);
@@ -317,7 +422,7 @@ int attn_bwd_preprocess(const attn_shape_t* s, const void* o, const void* dout, 
     if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || !aligned16(workspace)) return ATTN_ERR_MISALIGNED;
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    enqueue_preprocess(s, o, dout, delta, workspace, reinterpret_cast<hipStream_t>(stream));
+    enqueue_preprocess(s, layout(s, true), o, dout, delta, workspace, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -331,7 +436,8 @@ int attn_bwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
         return ATTN_ERR_MISALIGNED;
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    enqueue_bwd(s, q, k, v, dout, lse, delta, workspace, dk, dv, nullptr, 0.f, reinterpret_cast<hipStream_t>(stream));
+    enqueue_bwd(s, layout(s, true), q, k, v, dout, lse, delta, workspace, dk, dv, nullptr, 0.f,
+                reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -343,7 +449,7 @@ int attn_bwd_dq_postprocess(const attn_shape_t* s, const void* workspace, size_t
     if (!aligned16(workspace) || !aligned16(dq)) return ATTN_ERR_MISALIGNED;
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    enqueue_postprocess(s, workspace, dq, scale, reinterpret_cast<hipStream_t>(stream));
+    enqueue_postprocess(s, layout(s, true), workspace, dq, scale, reinterpret_cast<hipStream_t>(stream));
     return check_launch();
 }
 
@@ -359,8 +465,9 @@ int attn_bwd_full(const attn_shape_t* s, const void* q, const void* k, const voi
     if (workspace_size < workspace_bytes(s)) return ATTN_ERR_BAD_SHAPE;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    enqueue_bwd(s, q, k, v, dout, lse, delta, workspace, dk, dv, dq, s->softmax_scale, hs);
-    if (s->dq_algo == ATTN_DQ_ATOMIC) enqueue_postprocess(s, workspace, dq, s->softmax_scale, hs);
+    const Layout l = layout(s, true);
+    enqueue_bwd(s, l, q, k, v, dout, lse, delta, workspace, dk, dv, dq, s->softmax_scale, hs);
+    if (l.p.algo == ATTN_DQ_ATOMIC) enqueue_postprocess(s, l, workspace, dq, s->softmax_scale, hs);
     return check_launch();
 }
 

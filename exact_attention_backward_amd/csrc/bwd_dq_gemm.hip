@@ -82,15 +82,21 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     const bool varlen = a.cu_q != nullptr;
     const int off = si.len_k - si.len_q;   // bottom-right alignment of the mask
     const int nblk_k = (si.len_k + BN - 1) / BN;
-    const long long qb0 = varlen ? (long long)a.ds_qb_base[b] : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows);
+    // the dK/dV kernel's query tiles: KBM rows, KR 32-row blocks each
+    constexpr int KBM = kv_block_m(HD), KR = KBM / kDsRows;
+    const int G = a.hq / a.hkv;
+    // first stored block of query tile mm of this sequence (-1: none stored)
+    auto tile_first = [&](int mm) {
+        const int idx = a.ds_tile_base[b] + mm;
+        return idx < a.ds_tile_base[b + 1] && idx < a.ds_ntiles ? a.ds_prefix[idx] : -1;
+    };
 
     // key blocks a 32-row block can see: first_block .. last_block (last < 0:
-    // none, also for a block with no stored dS: a block past the table only
-    // comes from overlapping, malformed cu_seqlens).  The dK/dV kernel has
-    // stored exactly the blocks of each query tile that some row of it sees,
-    // a superset of these.
+    // none, also for a block with no stored dS, which only malformed
+    // cu_seqlens produce).  The dK/dV kernel has stored exactly the blocks of
+    // each query tile that some row of it sees, a superset of these.
     auto last_block = [&](int lq) {
-        if (lq * kDsRows >= si.len_q || qb0 + lq >= a.ds_qb) return -1;
+        if (lq * kDsRows >= si.len_q || tile_first(lq / KR) < 0) return -1;
         if (!MASKED) return nblk_k - 1;
         // the last key the block's last row sees
         const int x = min((lq + 1) * kDsRows, si.len_q) - 1 + off + a.win_hi;
@@ -125,8 +131,19 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
     const long long kstride = a.sk.r;   // elements between K rows
     const char* kbytes = reinterpret_cast<const char*>(a.k) +
                          (seq_off(a.sk, varlen, b, si.k0) + (long long)hkv * a.sk.h) * 2;
-    const char* dsb = reinterpret_cast<const char*>(a.ds) + ((long long)hq * a.ds_qb + qb0 + lq0) * a.ds_nn * kDsBlockBytes;
-    const long long blk_stride = (long long)a.ds_nn * kDsBlockBytes;   // next 32-row block
+    // this wave's dS blocks: block r's key block n sits at dsr[r] + n blocks
+    // (the tile's first block, + its 32-row block times the tile's key
+    // blocks, - the tile's first key block)
+    const char* dsr[kGRB];
+#pragma unroll
+    for (int r = 0; r < kGRB; ++r) {
+        const int lq = lq0 + r, mm = lq / KR;
+        const KeyRange kr = ds_key_range(mm, KBM, si.len_q, si.len_k, a.win_lo, a.win_hi, MASKED);
+        const long long first = n_last_b[r] < 0 ? 0 : tile_first(mm);
+        dsr[r] = reinterpret_cast<const char*>(a.ds) +
+                 ((long long)(hq - a.hkv0 * G) * a.ds_head_blocks + first + (long long)(lq % KR) * (kr.n1 - kr.n0 + 1) -
+                  kr.n0) * kDsBlockBytes;
+    }
 
     const unsigned lds0 = lds_addr(smem);
     // K copy plan: instruction t of wave w fills LDS segment w + 4t of a
@@ -161,7 +178,7 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
 #pragma unroll
         for (int r = 0; r < kGRB; ++r) {
             const bool mine = live && n >= n_first_b[r] && n <= n_last_b[r];
-            const i32x4 dr = rsrc_words(dsb + r * blk_stride + (long long)n * kDsBlockBytes + hf * C::DS_PART,
+            const i32x4 dr = rsrc_words(dsr[r] + (long long)(mine ? n : 0) * kDsBlockBytes + hf * C::DS_PART,
                                         mine ? C::DS_PART : 0);
 #pragma unroll
             for (int t = 0; t < C::DS_PART / 1024; ++t)
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const int per_group = n_pair * G;
     int grp, slot;
     {
-        const int groups = a.hkv * a.batch;
+        const int groups = a.hkv_n * a.batch;
         if (groups % kGXcds == 0) {
             const int xcd = blockIdx.x % kGXcds, s = blockIdx.x / kGXcds;
             grp = (s / per_group) * kGXcds + xcd;
@@ -290,8 +307,8 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
             slot = blockIdx.x % per_group;
         }
     }
-    const int hkv = grp % a.hkv;
-    const int b = grp / a.hkv;
+    const int hkv = a.hkv0 + grp % a.hkv_n;
+    const int b = grp / a.hkv_n;
     const int hq = hkv * G + slot / n_pair;
     const int p = slot % n_pair;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
@@ -310,38 +327,74 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     }
 }
 
-// First 32-row query block of every sequence (exclusive prefix sum of
-// ceil(len_q / 32)), for the stored-dS layout of varlen problems.  One
-// workgroup; the sequence lengths are clamped as the kernels clamp them.
-__global__ __launch_bounds__(256) void ds_table_kernel(const int32_t* cu_q, int batch, int seqlen_q, int total_q,
-                                                       int* out) {
-    __shared__ int part[256];
-    int carry = 0;
-    for (int c0 = 0; c0 < batch; c0 += 256) {
-        const int bb = c0 + (int)threadIdx.x;
-        int v = 0;
-        if (bb < batch) {
-            const int s0 = min(max(cu_q[bb], 0), total_q);
-            const int e0 = min(max(cu_q[bb + 1], s0), total_q);
-            v = (min(e0 - s0, seqlen_q) + kDsRows - 1) / kDsRows;
-        }
+// The stored-dS block table, one workgroup: first the exclusive prefix sum
+// of each sequence's query tiles (tile_base, batch + 1 entries), then that of
+// the dS blocks of every query tile over all sequences (prefix, one entry
+// per tile): the tile's first block within a q-head's region.  A tile whose
+// blocks would end past ds_head_blocks (only with malformed cu_seqlens,
+// whose clamped lengths can add up to more rows than total_q) gets -1: no dS
+// is stored or read for it.  Lengths are clamped as the kernels clamp them.
+__global__ __launch_bounds__(256) void ds_table_kernel(BwdArgs a, int bm, bool masked) {
+    __shared__ long long part[256];
+    int* tile_base = const_cast<int*>(a.ds_tile_base);
+    int* prefix = const_cast<int*>(a.ds_prefix);
+    auto scan = [&](long long v) {   // inclusive scan of v over the workgroup
         part[threadIdx.x] = v;
         __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {   // inclusive scan
-            const int x = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
+        for (int o = 1; o < 256; o <<= 1) {
+            const long long x = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
             __syncthreads();
             part[threadIdx.x] += x;
             __syncthreads();
         }
-        if (bb < batch) out[bb] = carry + part[threadIdx.x] - v;
-        carry += part[255];
+        const long long r = part[threadIdx.x];
+        const long long total = part[255];
         __syncthreads();
+        return make_longlong2(r, total);
+    };
+    long long carry = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += 256) {
+        const int b = c0 + (int)threadIdx.x;
+        long long v = 0;
+        if (b < a.batch) {
+            const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
+                                        a.used_k);
+            v = (si.len_q + bm - 1) / bm;
+        }
+        const longlong2 r = scan(v);
+        if (b < a.batch) tile_base[b] = (int)min(carry + r.x - v, (long long)a.ds_ntiles);
+        carry += r.y;
     }
-    if (threadIdx.x == 0) out[batch] = carry;
+    if (threadIdx.x == 0) tile_base[a.batch] = (int)min(carry, (long long)a.ds_ntiles);
+    __syncthreads();
+    const int ntiles = (int)min(carry, (long long)a.ds_ntiles);
+    long long blocks = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += 256) {
+        const int t = t0 + (int)threadIdx.x;
+        long long v = 0;
+        if (t < ntiles) {
+            // the sequence of tile t: the last b with tile_base[b] <= t
+            int lo = 0, hi = a.batch - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tile_base[mid] <= t) lo = mid;
+                else hi = mid - 1;
+            }
+            const SeqInfo si = seq_info(lo, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
+                                        a.used_k);
+            v = ds_tile_blocks(t - tile_base[lo], bm, si.len_q, si.len_k, a.win_lo, a.win_hi, masked);
+        }
+        const longlong2 r = scan(v);
+        if (t < ntiles) {
+            const long long first = blocks + r.x - v;
+            prefix[t] = first + v <= a.ds_head_blocks ? (int)first : -1;
+        }
+        blocks += r.y;
+    }
 }
 
-void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, int* out, hipStream_t st) {
-    ds_table_kernel<<<1, 256, 0, st>>>(cu_q, batch, seqlen_q, total_q, out);
+void launch_ds_table(const BwdArgs& a, int bm, bool masked, hipStream_t st) {
+    ds_table_kernel<<<1, 256, 0, st>>>(a, bm, masked);
 }
 
 template <class T>
@@ -349,7 +402,7 @@ static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool masked, hipStream_t 
     const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;
     static_assert(DqgCfg<128>::BQ == DqgCfg<64>::BQ, "one query tiling");
     const int n_pair = masked ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
-    const unsigned grid = (unsigned)(n_pair * a.hq * a.batch);
+    const unsigned grid = (unsigned)(n_pair * (a.hq / a.hkv) * a.hkv_n * a.batch);
     if (hd == 64) {
         if (masked) bwd_dq_gemm_kernel<T, 64, true><<<grid, kGThreads, 0, st>>>(a);
         else bwd_dq_gemm_kernel<T, 64, false><<<grid, kGThreads, 0, st>>>(a);

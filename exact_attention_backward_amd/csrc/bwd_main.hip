@@ -818,25 +818,62 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     const int diag_lo = n * kBN - off + a.win_lo - BM + 1;
     int cur_m = m_begin;                       // query tile of tile t
     int cur_g = 0;                             // q-head (within the group) of tile t
-    int last_m = m_begin, last_g = 0;          // the same for tile t-1
-    // stored-dS mode: first 32-row query block of this sequence, and whether
-    // the key tile reaches past the sequence (its dS columns are then zeroed)
-    const long long ds_qb0 = STORE_DS ? (varlen ? (long long)a.ds_qb_base[b]
-                                                : (long long)b * ((a.seqlen_q + kDsRows - 1) / kDsRows))
-                                      : 0;
+    // stored-dS mode: whether the key tile reaches past the sequence (its dS
+    // columns are then zeroed), and the dS blocks of tile t and of tile t-1:
+    // block (32-row block r, this key tile) of a tile at ptr + r * stride, or
+    // none (ptr null: the table stores nothing for the tile, which only
+    // malformed cu_seqlens produce; its stores get an empty range).  A tile's
+    // first block (the same in every q-head's region) comes from the table
+    // for the range's first tile only and then advances by each tile's
+    // blocks: a table read inside the loop would wait for every copy in
+    // flight (vmcnt counts both)
     const bool ragged_k = n * kBN + kBN > si.len_k;
-    // dS block cursors: the block (q-head, first 32-row block of the tile,
-    // key tile n) of tile t and of tile t-1; blocks from ds_lim on lie past
-    // the sequence (or, for malformed overlapping cu_seqlens, past the buffer)
-    // and get an empty range (their stores are dropped)
-    const int ds_lim = STORE_DS ? (int)min((long long)(si.len_q + kDsRows - 1) / kDsRows, a.ds_qb - ds_qb0) : 0;
-    const long long ds_blk_n = STORE_DS ? (long long)a.ds_nn * kDsBlockBytes : 0;   // bytes per 32-row block
-    const char* ds_p0 = STORE_DS ? reinterpret_cast<const char*>(a.ds) +
-                                       (((long long)hkv * G * a.ds_qb + ds_qb0 + m_begin * (BM / kDsRows)) * a.ds_nn + n) *
-                                           kDsBlockBytes
-                                 : nullptr;
-    const char* ds_cur = ds_p0;   // tile t
-    const char* ds_last = ds_p0;  // tile t-1
+    const int ds_t0 = STORE_DS ? a.ds_tile_base[b] : 0;
+    const int ds_t1 = STORE_DS ? min(a.ds_tile_base[b + 1], a.ds_ntiles) : 0;
+    // A tile's first block is the same in every q-head's region.  The table
+    // gives the range's first tile's; the others follow by adding each
+    // tile's blocks (a table read inside the loop would wait for every copy
+    // in flight: vmcnt counts both).  The table's entries only grow along a
+    // sequence, and a tile whose blocks would overflow the region is -1
+    // (only malformed cu_seqlens make one), so checking the range's first and
+    // last tiles once covers every tile; a key tile that fails stores nothing.
+    const int ds_first0 = STORE_DS && n_m > 0 && ds_t0 + m_end <= ds_t1 && a.ds_prefix[ds_t0 + m_end - 1] >= 0
+                              ? a.ds_prefix[ds_t0 + m_begin]
+                              : -1;
+    const char* ds_head0 = STORE_DS ? reinterpret_cast<const char*>(a.ds) +
+                                          (long long)(hkv - a.hkv0) * G * a.ds_head_blocks * kDsBlockBytes
+                                    : nullptr;
+    // Cursor over the query tiles of one q-head: the key range n0 .. n1 of
+    // tile m (ds_key_range's, here never empty: every tile visited sees key
+    // tile n; from one tile to the next both bounds' arguments x, y grow by
+    // BM) and blk, the index of block (0, key tile n) in the q-head's region
+    struct DsCursor {
+        int x, y, n0, cnt, blk;
+    };
+    const int ds_nblk = (si.len_k + kDsKeys - 1) / kDsKeys;
+    auto ds_range = [&](DsCursor& c) {
+        int n1 = ds_nblk - 1;
+        c.n0 = 0;
+        if (MASKED) {
+            c.n0 = c.x <= kDsKeys ? 0 : (c.x + kDsKeys - 1) / kDsKeys - 1;
+            n1 = min(ds_nblk - 1, c.y / kDsKeys);
+        }
+        c.cnt = n1 - c.n0 + 1;
+    };
+    auto ds_start = [&](DsCursor& c) {   // the q-head's first tile
+        c.x = m_begin * BM + off - a.win_lo + 1;
+        c.y = (m_begin + 1) * BM - 1 + off + a.win_hi;
+        ds_range(c);
+        c.blk = ds_first0 + n - c.n0;
+    };
+    DsCursor ds_cur{};   // tile t
+    if (STORE_DS) ds_start(ds_cur);
+    const char* ds_head = ds_first0 >= 0 ? ds_head0 : nullptr;   // region of tile t's q-head (null: no stores)
+    struct DsBlocks {
+        const char* head;
+        int blk, cnt;
+    };
+    DsBlocks ds_last{ds_head, ds_cur.blk, ds_cur.cnt};   // tile t-1: what its stores need
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
@@ -916,22 +953,30 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         issue_next(std::integral_constant<unsigned, ISS>{});
         };
         if constexpr (!DS_LATE) first_product();
-        const int tile_m = cur_m, tile_g = cur_g;   // coordinates of tile t
-        const char* ds_prev = ds_last;              // dS blocks of tile t-1
-        if (STORE_DS) ds_last = ds_cur;
+        const DsBlocks ds_prev = ds_last;           // dS blocks of tile t-1
+        if (STORE_DS) ds_last = DsBlocks{ds_head, ds_cur.blk, ds_cur.cnt};
+        bool new_head = false;
         if (++cur_m == m_end) {
             cur_m = m_begin;
             ++cur_g;
-            if (STORE_DS) ds_cur = ds_p0 + (long long)cur_g * a.ds_qb * ds_blk_n;
-        } else if (STORE_DS) {
-            ds_cur += (BM / kDsRows) * ds_blk_n;
+            new_head = true;
         }
-        const int prev_m = last_m, prev_g = last_g;   // coordinates of tile t-1
-        last_m = tile_m;
-        last_g = tile_g;
-        (void)prev_m;
-        (void)prev_g;
-
+        // the dS blocks of tile t+1, worked out at the end of the step, while
+        // its last MFMAs run (here, after the barrier, they delayed the step)
+        auto advance_ds = [&]() {
+            if (STORE_DS && R == 1) {
+                if (new_head) {
+                    if (ds_head) ds_head += (long long)a.ds_head_blocks * kDsBlockBytes;
+                    ds_start(ds_cur);
+                } else {
+                    const int n0 = ds_cur.n0, blocks = (BM / kDsRows) * ds_cur.cnt;
+                    ds_cur.x += BM;
+                    ds_cur.y += BM;
+                    ds_range(ds_cur);
+                    ds_cur.blk += blocks + n0 - ds_cur.n0;
+                }
+            }
+        };
         // the tile whose second product this wave computes now
         const int tt = R == 0 ? t : t - 1;   // the dS wave's later steps always have a tile t-1
         if (FIRST || (R == 0 && tt >= n_tiles)) {
@@ -942,6 +987,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                 for (int k = 0; k < NST; ++k) __builtin_amdgcn_raw_buffer_store_b128(z, none, lane * 16, 0, 2);
             }
             if constexpr (DS_LATE) first_product();
+            advance_ds();
             return;
         }
         constexpr unsigned buf = R == 0 ? CUR : PREV;
@@ -1089,8 +1135,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             // transposing reads).  Issued after the dK MFMAs, which run meanwhile.
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
-                const int lq = prev_m * (BM / kDsRows) + mb;   // 32-row block within the sequence
-                const rsrc_t dst = make_rsrc(ds_prev + mb * ds_blk_n, lq < ds_lim ? kDsBlockBytes : 0);
+                const rsrc_t dst = make_rsrc(
+                    ds_prev.head + (long long)(ds_prev.blk + mb * ds_prev.cnt) * kDsBlockBytes,
+                    ds_prev.head ? kDsBlockBytes : 0);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     // non-temporal: read once, by the dQ pass
@@ -1103,6 +1150,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             __builtin_amdgcn_sched_barrier(0);
             first_product();
         }
+        advance_ds();
     };
 
     // the dS wave keeps X of tile t until step t+1: two register sets, unrolled
@@ -1169,7 +1217,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     const int per_group = MASKED ? (a.nblk_n + 1) / 2 : a.nblk_n;
     int grp, p;
     {
-        const int groups = a.hkv * a.batch;
+        const int groups = a.hkv_n * a.batch;
         if (groups % kXcds == 0) {
             const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
             grp = (slot / per_group) * kXcds + xcd;
@@ -1179,8 +1227,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
             p = blockIdx.x % per_group;
         }
     }
-    const int hkv = grp % a.hkv;
-    const int b = grp / a.hkv;
+    const int hkv = a.hkv0 + grp % a.hkv_n;
+    const int b = grp / a.hkv_n;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (MASKED) {
         const int nk = (si.len_k + kBN - 1) / kBN;   // this sequence's key tiles
@@ -1227,8 +1275,8 @@ template <class T, int HD>
 static void launch_bwd_t(const BwdArgs& a, bool masked, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
-        // masked: one workgroup per pair of key tiles
-        const unsigned kv_grid = masked ? (unsigned)((a.nblk_n + 1) / 2 * a.hkv * a.batch) : grid;
+        // masked: one workgroup per pair of key tiles; the launch's kv-heads only
+        const unsigned kv_grid = (unsigned)((masked ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE || dq_algo == ATTN_DQ_STORED_DS) {

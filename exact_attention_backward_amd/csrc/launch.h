@@ -116,12 +116,21 @@ struct BwdArgs {
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;
     int deterministic;
-    // stored-dS mode: dS blocks [Hq][ds_qb][ds_nn][32 x 128 of the 16-bit I/O
-    // type] and, for varlen, each sequence's first 32-row query block
+    // stored-dS mode: the dS blocks (32 x 128 of the 16-bit I/O type each) of
+    // the q-heads of this launch's kv-head chunk, ds_head_blocks blocks per
+    // q-head; within a q-head, query tile m of sequence b holds its
+    // (BM / 32) x cnt(m) blocks (see ds_key_range) from block
+    // ds_prefix[ds_tile_base[b] + m] on (-1: none stored), 32-row block r
+    // and key tile n at + r * cnt(m) + n - N0(m)
     void* ds;
-    const int* ds_qb_base;
-    long long ds_qb;     // 32-row query blocks per q-head
-    int ds_nn;           // 128-key blocks per query block
+    const int* ds_tile_base;   // [batch + 1]: each sequence's first entry of ds_prefix
+    const int* ds_prefix;      // [ds_ntiles]
+    int ds_ntiles;
+    long long ds_head_blocks;
+    // kv-heads hkv0 .. hkv0 + hkv_n - 1 only (a chunk of the problem's
+    // kv-heads: the launch's grid covers these groups; the stored-dS region
+    // starts at q-head hkv0 * Hq / Hkv)
+    int hkv0, hkv_n;
 };
 
 // dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16 or fp16 (8 KiB),
@@ -135,6 +144,39 @@ constexpr int kDsRows = 32;
 constexpr int kDsKeys = 128;
 constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
 __host__ __device__ constexpr int ds_chunk(int g, int l) { return g * 64 + (l ^ ((l >> 5) << 2)); }
+
+// Query rows per tile of the stored-dS dK/dV kernel (kDsRows-row blocks each).
+__host__ __device__ constexpr int kv_block_m(int hd) { return hd == 128 ? 32 : 64; }
+
+// The key tiles (kDsKeys keys each) whose dS the key-stationary kernel stores
+// for query tile m (bm rows) of a sequence with len_q query and len_k key
+// rows: exactly those that visit the tile, a contiguous run n0 .. n1 (n1 <
+// n0: none).  Visibility: key j to row i iff i + off - lo <= j <= i + off +
+// hi, off = len_k - len_q (masked); every key when !masked.  Shared by the
+// host's workspace sizing, the table kernel and both dS kernels.
+struct KeyRange {
+    int n0, n1;
+};
+// 32-bit arithmetic: the ABI keeps every sequence below 2^27 rows and clamps
+// window sizes to 2^29, so |x| and |y| below stay under 2^30.
+__host__ __device__ inline KeyRange ds_key_range(int m, int bm, int len_q, int len_k, int lo, int hi, bool masked) {
+    const int nblk = (len_k + kDsKeys - 1) / kDsKeys;
+    if (!masked) return KeyRange{0, nblk - 1};
+    const int off = len_k - len_q;
+    // first: the smallest n whose last visible row reaches the tile's first row
+    const int x = m * bm + off - lo + 1;   // need min((n + 1) kDsKeys, len_k) >= x
+    if (x > len_k) return KeyRange{0, -1};
+    const int n0 = x <= kDsKeys ? 0 : (x + kDsKeys - 1) / kDsKeys - 1;
+    // last: the largest n whose first visible row is in or before the tile
+    const int y = (m + 1) * bm - 1 + off + hi;   // need n kDsKeys <= y
+    if (y < 0) return KeyRange{0, -1};
+    return KeyRange{n0, y / kDsKeys < nblk - 1 ? y / kDsKeys : nblk - 1};
+}
+// dS blocks of query tile m: 32-row blocks per tile times the tile's key tiles
+__host__ __device__ inline long long ds_tile_blocks(int m, int bm, int len_q, int len_k, int lo, int hi, bool masked) {
+    const KeyRange r = ds_key_range(m, bm, len_q, len_k, lo, hi, masked);
+    return r.n1 >= r.n0 ? (long long)(bm / kDsRows) * (r.n1 - r.n0 + 1) : 0;
+}
 
 // x * s rounded to fp32 and held in a register, so that a following
 // conversion to fp16 rounds that fp32 value: the empty asm keeps the
@@ -164,7 +206,10 @@ void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, h
 // stored-dS mode: dQ = dS K from the stored blocks (16-bit types), and the
 // per-sequence block table of varlen problems
 void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
-void launch_ds_table(const int32_t* cu_q, int batch, int seqlen_q, int total_q, int* out, hipStream_t st);
+// the stored-dS block table: a.ds_tile_base and a.ds_prefix from the
+// sequence lengths (cu_seqlens / seqused of a, or the dense lengths), for
+// query tiles of bm rows
+void launch_ds_table(const BwdArgs& a, int bm, bool masked, hipStream_t st);
 // query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 int bwd_dq_block_m();

@@ -191,6 +191,15 @@ typedef struct attn_shape {
     attn_tensor_strides_t bias_strides;
     void* dbias;             /* device output dBias (dtype), or NULL: see below */
     attn_tensor_strides_t dbias_strides;
+    int64_t max_workspace_bytes;  /* 0 = no cap.  Else ATTN_DQ_STORED_DS keeps its workspace
+                                     within this many bytes where it can: it runs the
+                                     kv-head groups in chunks whose dS blocks fit, and,
+                                     when not even one group's fit, behaves as
+                                     ATTN_DQ_SEPARATE (attn_bwd_workspace_bytes reports
+                                     the size of the mode taken).  Other modes ignore it */
+    const int32_t* cu_seqlens_q_host;  /* varlen, optional: HOST copies of cu_seqlens_q/_k, read */
+    const int32_t* cu_seqlens_k_host;  /* during each call; with both (and no seqused) the
+                                          stored-dS workspace is sized exactly from them */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -199,11 +208,16 @@ const char* attn_status_string(int status);
 /* Bytes of device workspace attn_bwd_preprocess/attn_bwd/attn_bwd_dq_postprocess
  * need for this shape: the fp32 dQ accumulator ([B, Hq, Sq, D] dense,
  * [Hq, total_q, D] varlen) followed by the int32 ordering counters of the
- * deterministic mode and, for ATTN_DQ_STORED_DS, a table of per-sequence
- * offsets and the dS blocks (32 query rows x 128 keys of 16-bit dS each, for every
- * q-head, 32-row query block and 128-key block; varlen sizes the query
- * blocks by total_q / 32 + batch and the key blocks by seqlen_k), each part
- * 256-byte aligned.  Returns 0 if the shape is invalid. */
+ * deterministic mode and, for ATTN_DQ_STORED_DS, a table of per-query-tile
+ * offsets and the dS blocks: 32 query rows x 128 keys of 16-bit dS each, for
+ * every q-head, only for the (query tile, key tile) pairs the causal or
+ * window mask leaves visible (the tiles hold 32 query rows for head dims
+ * above 64, else 64).  Dense problems and varlen ones with host copies of
+ * cu_seqlens are sized exactly; other varlen problems by the bound
+ * (total_q / 32 + 2 batch) x ceil(seqlen_k / 128) blocks per q-head.  With
+ * max_workspace_bytes the dS blocks are those of one chunk of kv-head groups
+ * (or none, see attn_shape_t).  Each part is 256-byte aligned.  Returns 0 if
+ * the shape is invalid. */
 size_t attn_bwd_workspace_bytes(const attn_shape_t* shape);
 
 /* Plain forward: O = softmax(s Q K^T) V and LSE (natural log) per row.

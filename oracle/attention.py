@@ -63,6 +63,8 @@ __all__ = [
     "alibi_bias",
     "head_forward",
     "head_backward",
+    "head_forward_rows",
+    "head_backward_rows",
     "forward",
     "backward",
     "group_forward",
@@ -188,6 +190,109 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None
     dq = scale * (ds @ k)                                 # stage 7 + dQ scale
     if details:
         return dq, dk, dv, {"p": p, "dp": dp, "ds": ds, "delta": delta}
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
+# one head at lengths where the [sq, sk] matrices do not fit: the same
+# definitions, evaluated a slice of rows (or single rows / keys) at a time
+# --------------------------------------------------------------------------
+
+def _row_logits(q_rows, rows, k, scale, causal, window, alibi, sq):
+    """Logits s q_i . k_j (+ ALiBi) of the given global rows i (q_rows their
+    queries) against every key, and their visibility mask."""
+    sk = k.shape[0]
+    i = np.asarray(rows)[:, None]
+    j = np.arange(sk)[None, :]
+    off = sk - sq
+    ok = np.ones((len(rows), sk), dtype=bool)
+    if causal:
+        ok &= j <= i + off
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok &= j >= i + off - left
+        if right >= 0:
+            ok &= j <= i + off + right
+    s = scale * (q_rows @ k.T)
+    if alibi is not None:
+        s = s - float(alibi) * np.abs(i + off - j).astype(np.float64)
+    return s, ok
+
+
+def head_forward_rows(q, k, v, scale, causal, window=None, alibi=None, block=1024):
+    """head_forward for one head, computed ``block`` query rows at a time
+    (each row's logits, LSE and output are those of head_forward: rows are
+    independent).  Returns (o [sq, d], lse [sq]) in float64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    sq = q.shape[0]
+    o = np.zeros((sq, v.shape[1]))
+    lse = np.full(sq, -np.inf)
+    for r0 in range(0, sq, block):
+        rows = np.arange(r0, min(r0 + block, sq))
+        s, ok = _row_logits(q[rows], rows, k, scale, causal, window, alibi, sq)
+        has_key = ok.any(axis=1)
+        row_max = np.max(np.where(ok, s, -np.inf), axis=1, initial=-np.inf)
+        row_max = np.where(has_key, row_max, 0.0)
+        e = np.exp(np.where(ok, s - row_max[:, None], -np.inf))
+        total = e.sum(axis=1)
+        lse[rows[has_key]] = row_max[has_key] + np.log(total[has_key])
+        p = np.zeros_like(s)
+        p[has_key] = e[has_key] / total[has_key, None]
+        o[rows] = p @ v
+    return o, lse
+
+
+def head_backward_rows(q, k, v, o, do, lse, scale, causal, q_rows, k_rows, window=None, alibi=None):
+    """head_backward's dQ at the query rows ``q_rows`` and dK, dV at the keys
+    ``k_rows``, each from its definition: dQ_i = s sum_j dS_ij k_j needs row i
+    of P and dP; dK_j = s sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i need
+    column j, i.e. P_ij = exp(s q_i . k_j - LSE_i) and dP_ij = dO_i . v_j for
+    every row i (and D_i = dO_i . O_i).  Returns (dq [len(q_rows), d],
+    dk [len(k_rows), d], dv [len(k_rows), d]) in float64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    o = np.asarray(o, np.float64)
+    do = np.asarray(do, np.float64)
+    lse = np.asarray(lse, np.float64)
+    sq, sk = q.shape[0], k.shape[0]
+    delta = np.sum(do * o, axis=1)                 # D for every row
+    finite = np.isfinite(lse)
+    safe_lse = np.where(finite, lse, 0.0)
+    # dQ rows
+    rows = np.asarray(q_rows)
+    s, ok = _row_logits(q[rows], rows, k, scale, causal, window, alibi, sq)
+    ok &= finite[rows][:, None]
+    p = np.exp(np.where(ok, s - safe_lse[rows][:, None], -np.inf))
+    dp = do[rows] @ v.T
+    ds = p * (dp - delta[rows][:, None])
+    dq = scale * (ds @ k)
+    # dK, dV keys: their columns of P and dP over every row
+    keys = np.asarray(k_rows)
+    all_rows = np.arange(sq)
+    s, ok = _row_logits(q, all_rows, k[keys], scale, False, None, None, sq)   # s q_i . k_j, no mask yet
+    i = all_rows[:, None]
+    j = keys[None, :]
+    off = sk - sq
+    if causal:
+        ok &= j <= i + off
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok &= j >= i + off - left
+        if right >= 0:
+            ok &= j <= i + off + right
+    if alibi is not None:
+        s = s - float(alibi) * np.abs(i + off - j).astype(np.float64)
+    ok &= finite[:, None]
+    p = np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))     # [sq, len(keys)]
+    dp = do @ v[keys].T
+    ds = p * (dp - delta[:, None])
+    dk = scale * (ds.T @ q)
+    dv = p.T @ do
     return dq, dk, dv
 
 

@@ -57,14 +57,96 @@ def test_workspace_size_formula():
     acc = (acc + 255) // 256 * 256
     sem = (2 * 4 * 2 * 4 + 255) // 256 * 256
     assert ws_bytes(s) == acc + sem + 256
-    # stored dS: + table of (batch + 1) int32 + Hq x (B ceil(Sq/32)) x ceil(Sk/128) blocks of 32 x 128 bf16
+    # stored dS: + the block table + Hq x (visible (query tile, key tile) pairs) blocks of 32 x 128 bf16
     s = shape(dq_algo=L.ATTN_DQ_STORED_DS)
-    table = 256
+    table = 256                       # (batch + 1 + query tiles) int32
+    # Sq = 100, Sk = 90 causal (off = -10): each 32-row tile's rows 10.. see key tile 0
     blocks = 4 * (2 * 4) * 1 * 32 * 128 * 2
     assert ws_bytes(s) == acc + sem + 256 + table + blocks
     # fp16 I/O: the same sizes (the accumulator is fp32, dS blocks 16-bit)
     assert ws_bytes(shape(dtype=L.ATTN_DTYPE_F16)) == acc + sem + 256
     assert ws_bytes(shape(dq_algo=L.ATTN_DQ_STORED_DS, dtype=L.ATTN_DTYPE_F16)) == acc + sem + 256 + table + blocks
+
+
+def _visible_tile_pairs(lq, lk, bm, causal, window):
+    """(query tile of bm rows, 128-key tile) pairs in which some query row sees
+    some key, counted by brute force from the visibility rule of the header:
+    key j is visible to row i iff i + off - left <= j <= i + off + right
+    (off = lk - lq; causal sets right = 0; -1 / no window: unbounded)."""
+    import numpy as np
+    off = lk - lq
+    big = 1 << 40
+    left = window[0] if window is not None and window[0] >= 0 else big
+    right = 0 if causal else (window[1] if window is not None and window[1] >= 0 else big)
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    vis = (j >= i + off - left) & (j <= i + off + right)
+    nq, nk = -(-lq // bm), -(-lk // 128)
+    pad = np.zeros((nq * bm, nk * 128), bool)
+    pad[:lq, :lk] = vis
+    return int(pad.reshape(nq, bm, nk, 128).any(axis=(1, 3)).sum())
+
+
+@pytest.mark.parametrize("d,causal,window,lens", [
+    (128, True, None, None),
+    (64, True, None, None),
+    (128, False, None, None),
+    (128, False, (100, 40), None),
+    (64, True, (300, -1), None),
+    (128, True, None, ((300, 300), (1, 1), (700, 650), (0, 0), (129, 400))),
+    (64, True, (70, -1), ((65, 90), (200, 200), (33, 31))),
+])
+def test_stored_ds_workspace_is_exactly_the_visible_blocks(d, causal, window, lens):
+    """The stored-dS workspace holds one 32 x 128 block per 32-row block of
+    each (query tile, key tile) pair with a visible element, per q-head: dense
+    shapes, and varlen shapes whose offsets are also given in host memory."""
+    bm = 32 if d == 128 else 64
+    hq, hkv = 6, 3
+    kw = dict(num_heads_q=hq, num_heads_kv=hkv, head_dim=d, causal=int(causal), dq_algo=L.ATTN_DQ_STORED_DS)
+    if window is not None:
+        kw.update(local=1, window_left=window[0], window_right=window[1])
+    keep = []
+    if lens is None:
+        kw.update(batch=2, seqlen_q=700, seqlen_k=650)
+        seqs = [(700, 650)] * 2
+    else:
+        seqs = list(lens)
+        cq = (ctypes.c_int32 * (len(seqs) + 1))(*[sum(a for a, _ in seqs[:b]) for b in range(len(seqs) + 1)])
+        ck = (ctypes.c_int32 * (len(seqs) + 1))(*[sum(b_ for _, b_ in seqs[:b]) for b in range(len(seqs) + 1)])
+        keep += [cq, ck]
+        kw.update(batch=len(seqs), seqlen_q=max(a for a, _ in seqs), seqlen_k=max(b_ for _, b_ in seqs),
+                  total_q=cq[len(seqs)], total_k=ck[len(seqs)], cu_seqlens_q=0x1000, cu_seqlens_k=0x2000,
+                  cu_seqlens_q_host=ctypes.addressof(cq), cu_seqlens_k_host=ctypes.addressof(ck))
+    s = shape(**kw)
+    base = shape(**dict(kw, dq_algo=L.ATTN_DQ_SEPARATE))
+    pairs = sum(_visible_tile_pairs(a, b_, bm, causal, window) for a, b_ in seqs)
+    tiles = len(seqs) * -(-kw["seqlen_q"] // bm) if lens is None else s.total_q // bm + len(seqs)
+    table = (4 * (len(seqs) + 1 + tiles) + 255) // 256 * 256
+    assert ws_bytes(s) == ws_bytes(base) + table + hq * pairs * (bm // 32) * 32 * 128 * 2
+    if lens is not None:
+        # without the host offsets: every sequence's full rectangle, bounded
+        s.cu_seqlens_q_host = None
+        bound = (s.total_q // 32 + (bm // 32) * len(seqs)) * -(-s.seqlen_k // 128)
+        assert ws_bytes(s) == ws_bytes(base) + table + hq * bound * 32 * 128 * 2
+
+
+def test_workspace_cap_chunks_kv_heads_or_falls_back():
+    """max_workspace_bytes: the stored-dS blocks of as many whole kv-head
+    groups as fit, or the separate mode's workspace when not one does."""
+    kw = dict(batch=2, num_heads_q=8, num_heads_kv=4, seqlen_q=1000, seqlen_k=1000, causal=1,
+              dq_algo=L.ATTN_DQ_STORED_DS)
+    full = ws_bytes(shape(**kw))
+    sep = ws_bytes(shape(**dict(kw, dq_algo=L.ATTN_DQ_SEPARATE)))
+    pairs = 2 * _visible_tile_pairs(1000, 1000, 32, True, None)
+    per_group = 2 * pairs * 32 * 128 * 2          # G = 2 q-heads per kv-head
+    base = full - 4 * per_group
+    assert base > sep
+    assert ws_bytes(shape(**kw, max_workspace_bytes=full)) == full
+    assert ws_bytes(shape(**kw, max_workspace_bytes=full - 1)) == base + 3 * per_group
+    assert ws_bytes(shape(**kw, max_workspace_bytes=base + per_group)) == base + per_group
+    assert ws_bytes(shape(**kw, max_workspace_bytes=base + per_group - 1)) == sep
+    assert ws_bytes(shape(**kw, max_workspace_bytes=1)) == sep
+    assert ws_bytes(shape(**kw, max_workspace_bytes=-1)) == 0    # invalid
 
 
 @pytest.mark.parametrize("kw,status", [

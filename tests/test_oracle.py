@@ -979,3 +979,78 @@ def test_planted_mistakes_are_caught_by_finite_differences(mutant):
         assert rel_err(good[pos], fd) <= 1e-6
         worst = max(worst, rel_err(g, fd))
     assert worst > 1e-3, mutant.__name__
+
+
+# --------------------------------------------------------------------------
+# the row-blocked forward and the sampled backward (long sequences)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sq,sk,causal,block", [(7, 9, True, 3), (9, 7, True, 2), (7, 7, False, 4), (5, 8, True, 1)])
+def test_row_blocked_forward_matches_scalar_loops(sq, sk, causal, block):
+    """head_forward_rows against the scalar-loop definition, with row blocks
+    that split the sequence unevenly (rows that see no key included)."""
+    rng = np.random.default_rng(300 + sq * 10 + sk)
+    q, k, v = rand(rng, sq, 3), rand(rng, sk, 3), rand(rng, sk, 3)
+    o, lse = A.head_forward_rows(q, k, v, 0.7, causal, block=block)
+    bo, blse = brute_head_forward(q.tolist(), k.tolist(), v.tolist(), 0.7, causal)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    fin = np.isfinite(blse)
+    assert np.max(np.abs(lse[fin] - blse[fin])) <= 1e-12
+    assert np.max(np.abs(o - bo)) <= 1e-12
+
+
+@pytest.mark.parametrize("window,alibi", [((2, 1), None), (None, 0.3), ((3, -1), 0.5)])
+def test_row_blocked_forward_matches_head_forward_windows_alibi(window, alibi):
+    rng = np.random.default_rng(31)
+    q, k, v = rand(rng, 11, 4), rand(rng, 9, 4), rand(rng, 9, 4)
+    for causal in (False, True):
+        o, lse = A.head_forward_rows(q, k, v, 0.6, causal, window, alibi, block=4)
+        ro, rlse = A.head_forward(q, k, v, 0.6, causal, window, alibi)
+        assert np.array_equal(np.isinf(lse), np.isinf(rlse))
+        fin = np.isfinite(rlse)
+        assert np.max(np.abs(lse[fin] - rlse[fin])) <= 1e-12
+        assert np.max(np.abs(o - ro)) <= 1e-12
+
+
+@pytest.mark.parametrize("sq,sk,causal", [(6, 6, True), (6, 4, True), (4, 7, False), (5, 5, False)])
+def test_sampled_backward_finite_differences(sq, sk, causal):
+    """head_backward_rows at sampled rows and keys against central finite
+    differences of L = sum dO * O(Q, K, V), O from head_forward_rows."""
+    rng = np.random.default_rng(400 + sq * 10 + sk)
+    q, k, v, do = rand(rng, sq, 3), rand(rng, sk, 3), rand(rng, sk, 3), rand(rng, sq, 3)
+    scale = 0.8
+    o, lse = A.head_forward_rows(q, k, v, scale, causal, block=2)
+    rows, keys = [0, sq - 1, sq // 2], [0, sk - 1, 1]
+    dq, dk, dv = A.head_backward_rows(q, k, v, o, do, lse, scale, causal, rows, keys)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * A.head_forward_rows(qq, kk, vv, scale, causal, block=3)[0]))
+
+    h = 1e-5
+    for name, x, g, idx_rows in (("q", q, dq, rows), ("k", k, dk, keys), ("v", v, dv, keys)):
+        fd = np.zeros((len(idx_rows), x.shape[1]))
+        for a, r in enumerate(idx_rows):
+            for t in range(x.shape[1]):
+                xp, xm = x.copy(), x.copy()
+                xp[r, t] += h
+                xm[r, t] -= h
+                args_p, args_m = [q, k, v], [q, k, v]
+                args_p["qkv".index(name)], args_m["qkv".index(name)] = xp, xm
+                fd[a, t] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert rel_err(g, fd) <= 1e-6, (name, rel_err(g, fd))
+
+
+@pytest.mark.parametrize("window,alibi", [(None, None), ((3, 1), None), (None, 0.25), ((2, -1), 0.4)])
+def test_sampled_backward_equals_full_backward(window, alibi):
+    """The sampled rows and keys of head_backward_rows equal those rows of
+    head_backward (pinned above by finite differences and torch autograd)."""
+    rng = np.random.default_rng(57)
+    q, k, v, do = rand(rng, 13, 5), rand(rng, 10, 5), rand(rng, 10, 5), rand(rng, 13, 5)
+    for causal in (False, True):
+        o, lse = A.head_forward(q, k, v, 0.45, causal, window, alibi)
+        rows, keys = [0, 3, 12, 7], [9, 0, 4]
+        dq, dk, dv = A.head_backward_rows(q, k, v, o, do, lse, 0.45, causal, rows, keys, window, alibi)
+        fq, fk, fv = A.head_backward(q, k, v, o, do, lse, 0.45, causal, window=window, alibi=alibi)
+        assert np.max(np.abs(dq - fq[rows])) <= 1e-12
+        assert np.max(np.abs(dk - fk[keys])) <= 1e-12
+        assert np.max(np.abs(dv - fv[keys])) <= 1e-12
