@@ -18,6 +18,10 @@ ATTN_ERR_BAD_SHAPE = 2
 ATTN_ERR_UNSUPPORTED = 3
 ATTN_ERR_MISALIGNED = 4
 ATTN_ERR_HIP = 5
+ATTN_ERR_SCRATCH = 6
+
+# bytes of the no-allocation entry point's scratch memory (per GPU)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
@@ -35,6 +39,7 @@ EXPORTS = (
     "attn_bwd",
     "attn_bwd_dq_postprocess",
     "attn_bwd_full",
+    "attn_bwd_full_noalloc",
 )
 
 
@@ -118,6 +123,9 @@ def lib():
         L.attn_bwd_dq_postprocess.restype = i32
         L.attn_bwd_full.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         L.attn_bwd_full.restype = i32
+        if hasattr(L, "attn_bwd_full_noalloc"):   # absent from builds that predate it
+            L.attn_bwd_full_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.attn_bwd_full_noalloc.restype = i32
         _lib = L
     return _lib
 

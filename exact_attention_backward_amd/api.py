@@ -27,6 +27,7 @@ __all__ = [
     "attn_bwd",
     "attn_bwd_dq_postprocess",
     "attn_bwd_full",
+    "attn_bwd_full_noalloc",
     "forward",
     "backward",
     "BackwardPlan",
@@ -190,6 +191,14 @@ def attn_bwd_full(shape, q, k, v, do, lse, delta, workspace, dq, dk, dv):
     return _call("attn_bwd_full", shape, dict(q=q, k=k, v=v, dout=do, dq=dq, dk=dk, dv=dv),
                  _tptr(q), _tptr(k), _tptr(v), _tptr(do), _ptr(lse), _ptr(delta), _ptr(workspace),
                  workspace.numel(), _tptr(dq), _tptr(dk), _tptr(dv), _stream())
+
+
+def attn_bwd_full_noalloc(shape, q, k, v, o, do, lse, dq, dk, dv):
+    """attn_bwd_preprocess + attn_bwd_full with D and the workspace in the
+    library's fixed scratch memory (no allocation, no workspace argument)."""
+    return _call("attn_bwd_full_noalloc", shape, dict(q=q, k=k, v=v, o=o, dout=do, dq=dq, dk=dk, dv=dv),
+                 _tptr(q), _tptr(k), _tptr(v), _tptr(o), _tptr(do), _ptr(lse), _tptr(dq), _tptr(dk), _tptr(dv),
+                 _stream())
 
 
 def _lse_shape(shape, varlen):

@@ -6,10 +6,15 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "launch.h"
 
 using namespace attn;
+
+// Scratch memory of the no-allocation entry point (see scratch_base below).
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -240,6 +245,27 @@ int check_launch() {
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// ---- scratch memory of attn_bwd_full_noalloc: a static device array, one
+// copy per GPU, held from the library's load on that GPU to the process end.
+// In host code the array's name is not a device address; its address on
+// each device is looked up once, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+int scratch_base(char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+        g_scratch[dev] = reinterpret_cast<char*>(p);
+    }
+    *out = g_scratch[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +278,7 @@ const char* attn_status_string(int status) {
         case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or dq_algo";
         case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case ATTN_ERR_HIP: return "HIP runtime error";
+        case ATTN_ERR_SCRATCH: return "problem needs more than the no-allocation entry point's scratch memory";
         default: return "unknown status";
     }
 }
@@ -468,6 +495,32 @@ int attn_bwd_full(const attn_shape_t* s, const void* q, const void* k, const voi
     const Layout l = layout(s, true);
     enqueue_bwd(s, l, q, k, v, dout, lse, delta, workspace, dk, dv, dq, s->softmax_scale, hs);
     if (l.p.algo == ATTN_DQ_ATOMIC) enqueue_postprocess(s, l, workspace, dq, s->softmax_scale, hs);
+    return check_launch();
+}
+
+int attn_bwd_full_noalloc(const attn_shape_t* s, const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv, void* stream) {
+    int st = validate_bwd(s);
+    if (st) return st;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_MISALIGNED;
+    // scratch = [D, fp32 in the LSE layout][workspace without the accumulator
+    // unless dQ is added atomically]
+    const size_t d_bytes = align_up((size_t)rows_q(s) * s->num_heads_q * sizeof(float));
+    const Layout l = layout(s, plan(s).algo == ATTN_DQ_ATOMIC);
+    if (d_bytes + l.total > kScratchBytes) return ATTN_ERR_SCRATCH;
+    char* base = nullptr;
+    st = scratch_base(&base);
+    if (st) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
+    float* delta = reinterpret_cast<float*>(base);
+    void* ws = base + d_bytes;
+    enqueue_preprocess(s, l, o, dout, delta, ws, hs);
+    enqueue_bwd(s, l, q, k, v, dout, lse, delta, ws, dk, dv, dq, s->softmax_scale, hs);
+    if (l.p.algo == ATTN_DQ_ATOMIC) enqueue_postprocess(s, l, ws, dq, s->softmax_scale, hs);
     return check_launch();
 }
 

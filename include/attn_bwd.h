@@ -109,7 +109,9 @@ typedef enum attn_status {
                                   bias or dbias without ATTN_DQ_ATOMIC */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer or stride is not 16-byte aligned
                                   (cu_seqlens, seqused and alibi_slopes: 4-byte) */
-    ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+    ATTN_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+    ATTN_ERR_SCRATCH = 6       /* attn_bwd_full_noalloc: the problem needs more than the
+                                  library's fixed scratch memory */
 } attn_status_t;
 
 typedef enum attn_dtype {
@@ -286,6 +288,30 @@ int attn_bwd_full(const attn_shape_t* shape, const void* q, const void* k, const
                   const void* dout, const float* lse, const float* delta,
                   void* workspace, size_t workspace_bytes, void* dq, void* dk, void* dv,
                   void* stream);
+
+/* attn_bwd_preprocess + attn_bwd_full in one call that allocates nothing and
+ * takes no workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  D and the workspace live in a scratch array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * (from its first use there to the end of the process); the call uses the
+ * copy of the current device, so `stream` must belong to that device.  The
+ * scratch must hold D (4 bytes per query row and q-head, rounded up to 256)
+ * plus the workspace of shape->dq_algo without the fp32 dQ accumulator, which
+ * only ATTN_DQ_ATOMIC needs (it then takes 4 * head_dim bytes per query row
+ * and q-head); ATTN_DQ_STORED_DS also needs its dS blocks (see
+ * attn_bwd_workspace_bytes).  Larger problems return ATTN_ERR_SCRATCH and
+ * enqueue nothing.  Results equal those of attn_bwd_preprocess followed by
+ * attn_bwd_full with the same shape, bit for bit in the separate, stored-dS
+ * and deterministic atomic modes.  Every call on a GPU uses that GPU's one
+ * scratch array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller; each call clears what
+ * it needs cleared itself.
+ * q, k, v, o, dout, lse: inputs; dq, dk, dv: outputs (as attn_bwd_full). */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_bwd_full_noalloc(const attn_shape_t* shape, const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse,
+                          void* dq, void* dk, void* dv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert L.status_string(L.ATTN_OK) == "ok"
-    for code in (1, 2, 3, 4, 5):
+    for code in (1, 2, 3, 4, 5, 6):
         assert L.status_string(code) not in ("ok", "unknown status")
     assert L.status_string(99) == "unknown status"
 
@@ -325,3 +325,33 @@ def test_null_and_misaligned_pointers_rejected():
                              None) == L.ATTN_ERR_MISALIGNED
     assert lib.attn_bwd_full(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 16, fake, fake, fake,
                              None) == L.ATTN_ERR_BAD_SHAPE
+
+
+def test_noalloc_entry_point_validates_before_any_hip_call():
+    """attn_bwd_full_noalloc: null and misaligned pointers, and problems
+    larger than its fixed scratch, are rejected before any HIP call."""
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1008)
+    s = shape(dq_algo=L.ATTN_DQ_SEPARATE)
+    args = [fake] * 9
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_bwd_full_noalloc(ctypes.byref(s), *a, None) == L.ATTN_ERR_NULL_ARG, i
+        a[i] = bad
+        assert lib.attn_bwd_full_noalloc(ctypes.byref(s), *a, None) == L.ATTN_ERR_MISALIGNED, i
+    assert lib.attn_bwd_full_noalloc(None, *args, None) == L.ATTN_ERR_NULL_ARG
+    # D alone of 2^24 (row, head) pairs fills the 64 MiB scratch
+    big = shape(batch=64, seqlen_q=1 << 15, seqlen_k=1 << 15, num_heads_q=8, num_heads_kv=8,
+                dq_algo=L.ATTN_DQ_SEPARATE)
+    assert 4 * 64 * (1 << 15) * 8 >= L.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_full_noalloc(ctypes.byref(big), *args, None) == L.ATTN_ERR_SCRATCH
+    # the stored-dS blocks of B4 H16 S4096 (1 GiB) do not fit either, nor the
+    # atomic mode's accumulator at that size (128 MiB)
+    for algo in (L.ATTN_DQ_STORED_DS, L.ATTN_DQ_ATOMIC):
+        hs = shape(batch=4, seqlen_q=4096, seqlen_k=4096, num_heads_q=16, num_heads_kv=16, dq_algo=algo)
+        assert lib.attn_bwd_full_noalloc(ctypes.byref(hs), *args, None) == L.ATTN_ERR_SCRATCH
+    # invalid shapes keep their own status
+    assert lib.attn_bwd_full_noalloc(ctypes.byref(shape(head_dim=100)), *args, None) == L.ATTN_ERR_UNSUPPORTED
+    assert L.status_string(L.ATTN_ERR_SCRATCH) != "unknown status"
