@@ -388,8 +388,12 @@ void enqueue_preprocess(const attn_shape_t* s, const Layout& l, const void* o, c
     PreArgs a{o, dout, delta, rows_q(s) * s->num_heads_q, s->num_heads_q, s->seqlen_q, s->total_q, varlen(s),
               s->head_dim, to_kernel(d.o), to_kernel(d.dout), reinterpret_cast<u32x4*>(zero),
               (long long)(zero_bytes / 16)};
-    launch_preprocess(a, s->dtype, padded_hd(s), hs);
-    if (l.p.algo == ATTN_DQ_STORED_DS) launch_ds_table(bwd_args(s, l, workspace), ds_bm(s), masked(s), hs);
+    if (l.p.algo == ATTN_DQ_STORED_DS) {
+        const BwdArgs t = bwd_args(s, l, workspace);
+        launch_preprocess(a, s->dtype, padded_hd(s), &t, ds_bm(s), masked(s), hs);
+    } else {
+        launch_preprocess(a, s->dtype, padded_hd(s), nullptr, 0, false, hs);
+    }
 }
 
 // dq_out: the separate and stored-dS modes write dQ = T(dq_scale * sum)

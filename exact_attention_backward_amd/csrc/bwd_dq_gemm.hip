@@ -327,76 +327,6 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     }
 }
 
-// The stored-dS block table, one workgroup: first the exclusive prefix sum
-// of each sequence's query tiles (tile_base, batch + 1 entries), then that of
-// the dS blocks of every query tile over all sequences (prefix, one entry
-// per tile): the tile's first block within a q-head's region.  A tile whose
-// blocks would end past ds_head_blocks (only with malformed cu_seqlens,
-// whose clamped lengths can add up to more rows than total_q) gets -1: no dS
-// is stored or read for it.  Lengths are clamped as the kernels clamp them.
-__global__ __launch_bounds__(256) void ds_table_kernel(BwdArgs a, int bm, bool masked) {
-    __shared__ long long part[256];
-    int* tile_base = const_cast<int*>(a.ds_tile_base);
-    int* prefix = const_cast<int*>(a.ds_prefix);
-    auto scan = [&](long long v) {   // inclusive scan of v over the workgroup
-        part[threadIdx.x] = v;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const long long x = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
-            __syncthreads();
-            part[threadIdx.x] += x;
-            __syncthreads();
-        }
-        const long long r = part[threadIdx.x];
-        const long long total = part[255];
-        __syncthreads();
-        return make_longlong2(r, total);
-    };
-    long long carry = 0;
-    for (int c0 = 0; c0 < a.batch; c0 += 256) {
-        const int b = c0 + (int)threadIdx.x;
-        long long v = 0;
-        if (b < a.batch) {
-            const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
-                                        a.used_k);
-            v = (si.len_q + bm - 1) / bm;
-        }
-        const longlong2 r = scan(v);
-        if (b < a.batch) tile_base[b] = (int)min(carry + r.x - v, (long long)a.ds_ntiles);
-        carry += r.y;
-    }
-    if (threadIdx.x == 0) tile_base[a.batch] = (int)min(carry, (long long)a.ds_ntiles);
-    __syncthreads();
-    const int ntiles = (int)min(carry, (long long)a.ds_ntiles);
-    long long blocks = 0;
-    for (int t0 = 0; t0 < ntiles; t0 += 256) {
-        const int t = t0 + (int)threadIdx.x;
-        long long v = 0;
-        if (t < ntiles) {
-            // the sequence of tile t: the last b with tile_base[b] <= t
-            int lo = 0, hi = a.batch - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (tile_base[mid] <= t) lo = mid;
-                else hi = mid - 1;
-            }
-            const SeqInfo si = seq_info(lo, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
-                                        a.used_k);
-            v = ds_tile_blocks(t - tile_base[lo], bm, si.len_q, si.len_k, a.win_lo, a.win_hi, masked);
-        }
-        const longlong2 r = scan(v);
-        if (t < ntiles) {
-            const long long first = blocks + r.x - v;
-            prefix[t] = first + v <= a.ds_head_blocks ? (int)first : -1;
-        }
-        blocks += r.y;
-    }
-}
-
-void launch_ds_table(const BwdArgs& a, int bm, bool masked, hipStream_t st) {
-    ds_table_kernel<<<1, 256, 0, st>>>(a, bm, masked);
-}
-
 template <class T>
 static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool masked, hipStream_t st) {
     const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;

@@ -8,6 +8,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 // Index of (sequence row r, head h) in the [B, H, S] / [H, total] layouts of
@@ -128,10 +130,78 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
 // LDS as one contiguous 256-byte run of D, so no D line is shared between
 // workgroups (they would sit in different L2s and be written back partially).
 // ---------------------------------------------------------------------------
+// The stored-dS block table, built by one extra workgroup of the preprocess: first the exclusive prefix sum
+// of each sequence's query tiles (tile_base, batch + 1 entries), then that of
+// the dS blocks of every query tile over all sequences (prefix, one entry
+// per tile): the tile's first block within a q-head's region.  A tile whose
+// blocks would end past ds_head_blocks (only with malformed cu_seqlens,
+// whose clamped lengths can add up to more rows than total_q) gets -1: no dS
+// is stored or read for it.  Lengths are clamped as the kernels clamp them.
+__device__ __forceinline__ void ds_table_body(const BwdArgs& a, int bm, bool masked) {
+    __shared__ long long part[256];
+    int* tile_base = const_cast<int*>(a.ds_tile_base);
+    int* prefix = const_cast<int*>(a.ds_prefix);
+    auto scan = [&](long long v) {   // inclusive scan of v over the workgroup
+        part[threadIdx.x] = v;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const long long x = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
+            __syncthreads();
+            part[threadIdx.x] += x;
+            __syncthreads();
+        }
+        const long long r = part[threadIdx.x];
+        const long long total = part[255];
+        __syncthreads();
+        return make_longlong2(r, total);
+    };
+    long long carry = 0;
+    for (int c0 = 0; c0 < a.batch; c0 += 256) {
+        const int b = c0 + (int)threadIdx.x;
+        long long v = 0;
+        if (b < a.batch) {
+            const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
+                                        a.used_k);
+            v = (si.len_q + bm - 1) / bm;
+        }
+        const longlong2 r = scan(v);
+        if (b < a.batch) tile_base[b] = (int)min(carry + r.x - v, (long long)a.ds_ntiles);
+        carry += r.y;
+    }
+    if (threadIdx.x == 0) tile_base[a.batch] = (int)min(carry, (long long)a.ds_ntiles);
+    __syncthreads();
+    const int ntiles = (int)min(carry, (long long)a.ds_ntiles);
+    long long blocks = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += 256) {
+        const int t = t0 + (int)threadIdx.x;
+        long long v = 0;
+        if (t < ntiles) {
+            // the sequence of tile t: the last b with tile_base[b] <= t
+            int lo = 0, hi = a.batch - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tile_base[mid] <= t) lo = mid;
+                else hi = mid - 1;
+            }
+            const SeqInfo si = seq_info(lo, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q,
+                                        a.used_k);
+            v = ds_tile_blocks(t - tile_base[lo], bm, si.len_q, si.len_k, a.win_lo, a.win_hi, masked);
+        }
+        const longlong2 r = scan(v);
+        if (t < ntiles) {
+            const long long first = blocks + r.x - v;
+            prefix[t] = first + v <= a.ds_head_blocks ? (int)first : -1;
+        }
+        blocks += r.y;
+    }
+}
+
 constexpr int kPreTokens = 64;
 
-template <class T, int HD>
-__global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
+// TABLE: the grid's last workgroup builds the stored-dS block table instead
+// (it runs beside the D workgroups, so the table costs no launch of its own)
+template <class T, int HD, bool TABLE>
+__global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a, BwdArgs t, int bm, bool masked) {
     constexpr int LPR = HD / 8;
     constexpr int RPP = 256 / LPR;                 // rows per pass
     constexpr int PASSES = kPreTokens / RPP;
@@ -143,6 +213,10 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
              i += (long long)gridDim.x * blockDim.x)
             a.zero[i] = z;
     }
+    if (TABLE && blockIdx.x == gridDim.x - 1) {
+        ds_table_body(t, bm, masked);
+        return;
+    }
     const long long tokens = a.rows / a.h;
     const int h = (int)(blockIdx.x % (unsigned)a.h);
     const long long r0 = (long long)(blockIdx.x / (unsigned)a.h) * kPreTokens;
@@ -153,10 +227,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
     for (int p = 0; p < PASSES; ++p) {
         const long long r = min(r0 + p * RPP + slot, tokens - 1);
         if (live) {
-            load8(reinterpret_cast<const T*>(a.o) + flat_row_off(a.so, a.varlen, r, a.s) + (long long)h * a.so.h +
-                      part * 8, x[p]);
-            load8(reinterpret_cast<const T*>(a.dout) + flat_row_off(a.sdo, a.varlen, r, a.s) +
-                      (long long)h * a.sdo.h + part * 8, y[p]);
+            // O and dO are read once here: non-temporal loads
+            load8_nt(reinterpret_cast<const T*>(a.o) + flat_row_off(a.so, a.varlen, r, a.s) + (long long)h * a.so.h +
+                         part * 8, x[p]);
+            load8_nt(reinterpret_cast<const T*>(a.dout) + flat_row_off(a.sdo, a.varlen, r, a.s) +
+                         (long long)h * a.sdo.h + part * 8, y[p]);
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t) x[p][t] = y[p][t] = 0.f;
@@ -255,19 +330,27 @@ void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, 
     else zero_blocks_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<float*>(p), s, a);
 }
 
-void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st) {
+void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table, int bm, bool masked,
+                       hipStream_t st) {
     const long long tokens = a.rows / a.h;
-    const unsigned blocks = (unsigned)((tokens + kPreTokens - 1) / kPreTokens * a.h);
-    if (dtype == ATTN_DTYPE_BF16) {
-        if (hd == 64) preprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
-        else preprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
-    } else if (dtype == ATTN_DTYPE_F16) {
-        if (hd == 64) preprocess_kernel<f16_t, 64><<<blocks, 256, 0, st>>>(a);
-        else preprocess_kernel<f16_t, 128><<<blocks, 256, 0, st>>>(a);
-    } else {
-        if (hd == 64) preprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
-        else preprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);
-    }
+    const unsigned blocks = (unsigned)((tokens + kPreTokens - 1) / kPreTokens * a.h) + (table ? 1u : 0u);
+    const BwdArgs t = table ? *table : BwdArgs{};
+    auto go = [&](auto tc, auto hc, auto table_c) {
+        using T = decltype(tc);
+        constexpr int HD = decltype(hc)::value;
+        preprocess_kernel<T, HD, decltype(table_c)::value><<<blocks, 256, 0, st>>>(a, t, bm, masked);
+    };
+    auto by_hd = [&](auto tc, auto table_c) {
+        if (hd == 64) go(tc, std::integral_constant<int, 64>{}, table_c);
+        else go(tc, std::integral_constant<int, 128>{}, table_c);
+    };
+    auto by_table = [&](auto tc) {
+        if (table) by_hd(tc, std::true_type{});
+        else by_hd(tc, std::false_type{});
+    };
+    if (dtype == ATTN_DTYPE_BF16) by_table(bf16_t{});
+    else if (dtype == ATTN_DTYPE_F16) by_table(f16_t{});
+    else by_hd(float{}, std::false_type{});   // no stored dS in fp32
 }
 
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st) {

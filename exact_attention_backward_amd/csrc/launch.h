@@ -4,6 +4,8 @@
 
 #include "common.h"
 
+#include <type_traits>
+
 namespace attn {
 
 // Element strides of one tensor: between batch entries (dense layouts only),
@@ -200,16 +202,15 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st
 void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 // zero every sequence's [Hq, len_q, len_k] block of a [b, h, i, j] tensor with strides s
 void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st);
-void launch_preprocess(const PreArgs& a, int dtype, int hd, hipStream_t st);
+// table (stored-dS mode, else null): also build its block table (for query
+// tiles of bm rows) in an extra workgroup
+void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table, int bm, bool masked,
+                       hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
 void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, hipStream_t st);
 // stored-dS mode: dQ = dS K from the stored blocks (16-bit types), and the
 // per-sequence block table of varlen problems
 void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
-// the stored-dS block table: a.ds_tile_base and a.ds_prefix from the
-// sequence lengths (cu_seqlens / seqused of a, or the dense lengths), for
-// query tiles of bm rows
-void launch_ds_table(const BwdArgs& a, int bm, bool masked, hipStream_t st);
 // query-stationary dQ pass; a.nblk_m must count its query tiles (bwd_dq_block_m() rows each)
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 int bwd_dq_block_m();
@@ -253,6 +254,32 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
     for (int t = 0; t < 4; ++t) {
         x[t] = u[t];
         x[4 + t] = v[t];
+    }
+}
+// load8 with the non-temporal hint (data read once)
+template <class T>
+__device__ __forceinline__ void load8_nt(const T* p, float* x) {
+    if constexpr (sizeof(T) == 2) {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        if constexpr (std::is_same<T, f16_t>::value) {
+            const f32x8 f = __builtin_convertvector(__builtin_bit_cast(f16x8, w), f32x8);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = f[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[2 * t] = bf16_lo(w[t]);
+                x[2 * t + 1] = bf16_hi(w[t]);
+            }
+        }
+    } else {
+        const f32x4 u = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[t] = u[t];
+            x[4 + t] = v[t];
+        }
     }
 }
 __device__ __forceinline__ void store8(bf16_t* p, const float* x) {
