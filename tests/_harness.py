@@ -119,3 +119,73 @@ def assert_close(name, got, ref, dtype):
     err = rel_err(got, ref)
     assert err <= TOL[dtype], f"{name}: max|gpu-ref|/max|ref| = {err:.3e} > {TOL[dtype]}"
     return err
+
+
+# --------------------------------------------------------------------------
+# the fp64 oracle on every (sequence, kv-head) group of a full-size workload,
+# in worker processes (spawned: no GPU state; one BLAS thread each)
+# --------------------------------------------------------------------------
+
+def _oracle_group_job(args):
+    """Forward (O rounded to the I/O type, LSE to fp32: the values the GPU is
+    given) and backward of one kv-head group of one sequence."""
+    q, k, v, do, scale, causal, dtype, window, slopes = args
+    import numpy as np
+    import oracle as orc
+    g = q.shape[1] // k.shape[1]
+    outs = []
+    dk = np.zeros((k.shape[0], k.shape[2]))
+    dv = np.zeros_like(dk)
+    for j in range(q.shape[1]):
+        slope = None if slopes is None else float(slopes[j])
+        o, lse = orc.head_forward(q[:, j], k[:, 0], v[:, 0], scale, causal, window, slope)
+        o = round_like(o, dtype)
+        lse = lse.astype(np.float32).astype(np.float64)
+        dq, dkj, dvj = orc.head_backward(q[:, j], k[:, 0], v[:, 0], o, do[:, j], lse, scale, causal,
+                                         window=window, alibi=slope)
+        dk += dkj
+        dv += dvj
+        outs.append((o, lse, dq))
+    assert g == len(outs)
+    return outs, dk, dv
+
+
+def oracle_all_groups(p, x, window=None, slopes=None, workers=16):
+    """{(sequence, kv_head): ([(o, lse, dq) per q-head of the group], dk, dv)}
+    for every group of problem p with inputs x (as datagen.draw returns)."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    g = p.heads_q // p.heads_kv
+    cq, ck = p.cu_seqlens()
+    jobs, keys = [], []
+    for b in range(p.batch):
+        for hk in range(p.heads_kv):
+            hs = slice(hk * g, (hk + 1) * g)
+            if p.varlen:
+                q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+                q, do = x["q"][q0:q1, hs], x["do"][q0:q1, hs]
+                k, v = x["k"][k0:k1, hk:hk + 1], x["v"][k0:k1, hk:hk + 1]
+            else:
+                q, do = x["q"][b, :, hs], x["do"][b, :, hs]
+                k, v = x["k"][b, :, hk:hk + 1], x["v"][b, :, hk:hk + 1]
+            sl = None if slopes is None else np.asarray(slopes)[hs]
+            jobs.append((q, k, v, do, p.scale, p.causal, p.dtype, window, sl))
+            keys.append((b, hk))
+    env = {n: os.environ.get(n) for n in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS")}
+    os.environ["OPENBLAS_NUM_THREADS"] = os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        n = max(1, min(workers, len(jobs), os.cpu_count() or 1))
+        with ProcessPoolExecutor(n, mp_context=mp.get_context("spawn")) as ex:
+            res = {}
+            for i, r in enumerate(ex.map(_oracle_group_job, jobs, timeout=1500)):
+                res[keys[i]] = r
+                if (i + 1) % 16 == 0 or i + 1 == len(jobs):
+                    print(f"  oracle groups {i + 1}/{len(jobs)}", flush=True)
+    finally:
+        for k_, v_ in env.items():
+            if v_ is None:
+                os.environ.pop(k_, None)
+            else:
+                os.environ[k_] = v_
+    return res

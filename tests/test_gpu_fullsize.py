@@ -1,14 +1,15 @@
 """Parity at the five workloads' full sizes, in the launch configuration the
-benchmark times (BackwardPlan.run: preprocess -> main -> postprocess).
+benchmark times (attn_bwd_preprocess -> attn_bwd_full).
 
-The small workloads (fp32 B1 H2 S128 D64 and bf16 causal B2 H8 S1024 D64) are
-compared element by element in full.  For the large ones the oracle computes
-sampled (sequence, kv-head) groups one by one: their O and LSE come from the
-oracle forward (written into the device buffers, rounded to the I/O type),
-every other head uses the library forward, and the sampled heads' dQ, dK and
-dV are compared with the oracle backward.  Every head is also checked against
-the identity sum_j dV_j = sum_i dO_i (rows of P sum to one), which holds at any
-size.  The deterministic mode is checked bit for bit across repeated runs."""
+Every (sequence, kv-head) group of every workload is compared element by
+element with the fp64 oracle (run in worker processes): the two small
+workloads directly; for the three large ones O and LSE of every head come from
+the oracle forward (rounded to the I/O type and fp32, written into the device
+buffers) and dQ, dK and dV of every group from the oracle backward.  Extra
+configurations of the headline shape (a window with ALiBi, packed QKV) are
+checked on sampled groups plus the identity sum_j dV_j = sum_i dO_i over every
+head.  The deterministic and atomic-free modes are checked bit for bit across
+repeated runs."""
 
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ import torch
 
 import datagen
 import oracle
-from _harness import TOL, assert_close, rel_err, round_like, to_dev, to_host
+from _harness import TOL, assert_close, oracle_all_groups, rel_err, round_like, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +122,61 @@ def sampled_check(p, samples, deterministic=None, repeats=1, dq_algo="separate",
         assert rel_err(lhs, rhs) <= TOL[p.dtype]
 
 
+_ALL = {}
+
+
+def all_groups_check(name, dq_algo, deterministic=False, repeats=1):
+    """Every (sequence, kv-head) group of workload `name` against the fp64
+    oracle: O and LSE of every head from the oracle forward (rounded to the
+    I/O type and fp32), the backward in the benchmark's launch configuration,
+    dQ, dK and dV of every group compared element by element."""
+    from exact_attention_backward_amd import api
+    p = datagen.workload(name, deterministic=deterministic)
+    x, dev, kw, cu = setup(p)
+    if name not in _ALL:
+        print(f"{p.name}: oracle on every group", flush=True)
+        _ALL.clear()   # keep one workload's results at a time
+        _ALL[name] = oracle_all_groups(p, x)
+    ref = _ALL[name]
+    g = p.heads_q // p.heads_kv
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((p.heads_q, p.total_q) if p.varlen else (p.batch, p.heads_q, p.seqlen_q), dtype=torch.float32,
+                      device="cuda")
+    o_np = np.zeros(dev["q"].shape, np.float32)
+    lse_np = np.zeros(lse.shape, np.float32)
+    for (b, hk), (heads, _, _) in ref.items():
+        for j, (oh, lh, _) in enumerate(heads):
+            h = hk * g + j
+            if p.varlen:
+                q0, q1 = int(cu[0][b]), int(cu[0][b + 1])
+                o_np[q0:q1, h], lse_np[h, q0:q1] = oh, lh
+            else:
+                o_np[b, :, h], lse_np[b, h] = oh, lh
+    o.copy_(torch.from_numpy(o_np).to(o.dtype))
+    lse.copy_(torch.from_numpy(lse_np))
+    outs = [run_backward(p, dev, o, lse, kw, deterministic, dq_algo) for _ in range(repeats)]
+    for rep in outs[1:]:
+        for a, bb in zip(outs[0], rep):
+            assert torch.equal(a.view(torch.int16), bb.view(torch.int16)), "not bitwise reproducible"
+    dq, dk, dv = (to_host(t) for t in outs[0])
+    worst = {}
+    for (b, hk), (heads, rdk, rdv) in ref.items():
+        if p.varlen:
+            q0, q1, k0, k1 = int(cu[0][b]), int(cu[0][b + 1]), int(cu[1][b]), int(cu[1][b + 1])
+            gk, gv = dk[k0:k1, hk], dv[k0:k1, hk]
+            gq = [dq[q0:q1, hk * g + j] for j in range(g)]
+        else:
+            gk, gv = dk[b, :, hk], dv[b, :, hk]
+            gq = [dq[b, :, hk * g + j] for j in range(g)]
+        errs = {"dK": rel_err(gk, rdk), "dV": rel_err(gv, rdv)}
+        for j, (_, _, rdq) in enumerate(heads):
+            errs[f"dQ{j}"] = rel_err(gq[j], rdq)
+        for n, e in errs.items():
+            worst[n[:2]] = max(worst.get(n[:2], 0.0), e)
+            assert e <= TOL[p.dtype], f"seq {b} kv-head {hk} {n}: {e:.3e}"
+    print(f"{p.name} {dq_algo}: {len(ref)} groups, worst rel err {worst}", flush=True)
+
+
 @pytest.mark.parametrize("dq_algo", ["stored_ds", "separate"])
 def test_headline_window_alibi_sampled(dq_algo):
     """The headline shape with a causal sliding window of 1024 keys and ALiBi."""
@@ -166,38 +222,29 @@ def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
 
 
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
-def test_headline_causal_sampled(dq_algo):
-    sampled_check(datagen.workload("c3"), [(0, 0), (3, 15)], dq_algo=dq_algo)
+def test_headline_causal_all_groups(dq_algo):
+    all_groups_check("c3", dq_algo)
 
 
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
-def test_headline_shape_fp16_sampled(dq_algo):
+def test_headline_noncausal_all_groups(dq_algo):
+    all_groups_check("c3nc", dq_algo)
+
+
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
+def test_headline_shape_fp16_all_groups(dq_algo):
     """The causal B=4 H=16 S=4096 D=128 shape with fp16 I/O."""
-    sampled_check(datagen.workload("c3h"), [(0, 0), (2, 9)], dq_algo=dq_algo)
+    all_groups_check("c3h", dq_algo)
 
 
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
-def test_headline_noncausal_sampled(dq_algo):
-    sampled_check(datagen.workload("c3nc"), [(1, 7)], dq_algo=dq_algo)
+def test_varlen_all_groups(dq_algo):
+    all_groups_check("c4", dq_algo)
 
 
-@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
-def test_varlen_sampled(dq_algo):
-    p = datagen.workload("c4")
-    longest = int(np.argmax(p.lengths_q))
-    shortest = int(np.argmin(p.lengths_q))
-    sampled_check(p, [(shortest, 0), (longest, 31)], dq_algo=dq_algo)
-
-
-def test_gqa_atomic_sampled():
-    sampled_check(datagen.workload("c5"), [(0, 0)], dq_algo="atomic")
-
-
-def test_gqa_deterministic_sampled_and_reproducible():
-    """Ordered atomic dQ adds: bitwise identical over three runs."""
-    sampled_check(datagen.workload("c5", deterministic=True), [(0, 7)], repeats=3, dq_algo="atomic")
-
-
-@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
-def test_gqa_atomic_free_modes_sampled_and_reproducible(dq_algo):
-    sampled_check(datagen.workload("c5"), [(0, 3)], repeats=2, dq_algo=dq_algo)
+@pytest.mark.parametrize("dq_algo,deterministic,repeats",
+                         [("atomic", False, 1), ("atomic", True, 3), ("separate", False, 2), ("stored_ds", False, 2)])
+def test_gqa_all_groups(dq_algo, deterministic, repeats):
+    """GQA Hq32 Hkv8 S8192 in every dQ mode; the deterministic and the
+    atomic-free modes also bitwise reproducible."""
+    all_groups_check("c5", dq_algo, deterministic, repeats)
