@@ -94,12 +94,27 @@ int validate_shape(const attn_shape_t* s) {
     return ATTN_OK;
 }
 
-// the backward entry points: an elementwise bias or its gradient needs the
-// atomic dQ mode (the forward takes a bias whatever dq_algo says)
+// the backward entry points: outside the atomic dQ mode the kernels copy
+// the bias in 16-byte chunks (rows, batch and head steps and the base
+// 16-byte aligned) and address a tile of up to 64 bias or dBias rows with
+// 32-bit offsets
 int validate_bwd(const attn_shape_t* s) {
     const int st = validate_shape(s);
     if (st) return st;
-    if ((s->bias != nullptr || s->dbias != nullptr) && s->dq_algo != ATTN_DQ_ATOMIC) return ATTN_ERR_UNSUPPORTED;
+    if (s->dq_algo != ATTN_DQ_ATOMIC) {
+        const long long esz = s->dtype == ATTN_DTYPE_F32 ? 4 : 2;
+        if (s->bias != nullptr) {
+            const attn_tensor_strides_t& b = s->bias_strides;
+            if (reinterpret_cast<uintptr_t>(s->bias) % 16 || (b.batch * esz) % 16 || (b.head * esz) % 16 ||
+                (b.row * esz) % 16)
+                return ATTN_ERR_MISALIGNED;
+        }
+        const attn_tensor_strides_t* bs[] = {&s->bias_strides, &s->dbias_strides};
+        const void* bp[] = {s->bias, s->dbias};
+        for (int t = 0; t < 2; ++t)
+            if (bp[t] != nullptr && (65 * bs[t]->row + s->seqlen_k + 8) * esz >= kOobOff - (1LL << 20))
+                return ATTN_ERR_BAD_SHAPE;
+    }
     return ATTN_OK;
 }
 

@@ -43,7 +43,14 @@ struct DqCfg {
     static constexpr int BUF_K = 0, BUF_V = TILE;
     static constexpr int BUF_BYTES = 2 * TILE;
     static constexpr int LDS_BYTES = NS * BUF_BYTES;
-    static_assert(LDS_BYTES <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for 16-bit types)");
+    // elementwise bias: each wave's [32 rows][BN keys] block, two buffers
+    // (tile parity), copied one tile ahead
+    static constexpr int BIAS_W = 32 * BN * (int)sizeof(T);
+    static constexpr int BIAS_ROWB = BN * (int)sizeof(T);
+    static constexpr int BOPS = BIAS_W / 1024;       // copies per wave and tile
+    static constexpr int OFF_BIAS = LDS_BYTES;
+    static constexpr int LDS_BYTES_BIAS = OFF_BIAS + 2 * kWaves * BIAS_W;
+    static_assert(LDS_BYTES_BIAS <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for 16-bit types)");
     static constexpr int NC = HD / 16;       // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;      // 32-column blocks of the head dim
     static constexpr int NJB = BN / 32;      // 32-key blocks of a K tile
@@ -148,8 +155,9 @@ __device__ __forceinline__ void dq_wait_vmem_but(int n) {
 
 }  // namespace
 
-// dQ rows of query tile m (128 rows) of q-head hq in sequence b.
-template <class T, int HD, bool MASKED, bool ALIBI>
+// dQ rows of query tile m (128 rows) of q-head hq in sequence b.  BIAS: an
+// elementwise bias (and ALiBi too when slopes are given).
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS>
 __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                         char* smem) {
     using C = DqCfg<T, HD>;
@@ -219,10 +227,38 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
     }
     const float scale2 = a.scale * kLog2e;
     // ALiBi slope of this q-head, negated, in log2 units
-    const float nsl2 = ALIBI ? -a.alibi[hq] * kLog2e : 0.f;
+    const float nsl2 = ALIBI || (BIAS && a.alibi != nullptr) ? -a.alibi[hq] * kLog2e : 0.f;
     // key j is visible to this lane's row iff lim_lo <= j < lim
     const int lim = row_ok ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
     const int lim_lo = MASKED ? i + off - a.win_lo : 0;
+    // elementwise bias: each wave copies the [32 rows][BN keys] block of its
+    // rows for tile u + 1 during step u (LDS, two buffers), ahead of that
+    // step's tile copies, so the wait at the top of step u + 1 covers it.
+    // Lane L of copy k takes row (16-byte chunks per row CPB) k * 64 / CPB +
+    // L / CPB, chunk L % CPB.  The range ends with the last valid row, at its
+    // valid keys rounded up to 16 bytes (inside the row: bias rows are
+    // 16-byte aligned); later rows read zeros.
+    using bchunk_t = std::conditional_t<sizeof(T) == 2, u32x2, u32x4>;
+    constexpr int CPB = C::BIAS_ROWB / 16;
+    const long long sbr_b = a.sbias.r * (long long)sizeof(T);
+    const int bias_voff = BIAS ? (int)((lane / CPB) * sbr_b) + (lane % CPB) * 16 : 0;
+    const unsigned bias_lds = lds_addr(smem) + C::OFF_BIAS + w * C::BIAS_W;
+    const int rows_w = si.len_q - (i0 + 32 * w);   // this wave's valid rows (may be <= 0)
+    auto issue_bias = [&](int u) {
+        const int jt = (kt_b + u) * BN;
+        const char* base = reinterpret_cast<const char*>(a.bias) +
+                           ((long long)b * a.sbias.b + (long long)hq * a.sbias.h +
+                            (long long)(i0 + 32 * w) * a.sbias.r + jt) * (long long)sizeof(T);
+        const unsigned bytes = a.bias == nullptr || rows_w <= 0
+                                   ? 0u
+                                   : (unsigned)((min(rows_w, 32) - 1) * sbr_b) +
+                                         (unsigned)(((si.len_k - jt) * (int)sizeof(T) + 15) & ~15);
+        const i32x4 rb = rsrc_words(base, bytes);
+        const unsigned dst = bias_lds + (u & 1) * kWaves * C::BIAS_W;
+#pragma unroll
+        for (int k = 0; k < C::BOPS; ++k)
+            dma_to_lds16_so(rb, dst + k * 1024, bias_voff, (int)(k * (64 / CPB) * sbr_b));
+    };
 
     f32x16 dq[C::NDB];
 #pragma unroll
@@ -231,17 +267,33 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         for (int v = 0; v < 16; ++v) dq[d][v] = 0.f;
     }
 
-    // prologue: the first NS - 1 tiles in flight
+    // prologue: the first NS - 1 tiles in flight (after the first bias block)
+    if (BIAS && n_kt > 0) issue_bias(0);
     for (int u = 0; u < C::NS - 1 && u < n_kt; ++u) issue_tile(u);
     for (int u = 0; u < n_kt; ++u) {
         const char* buf = buf_of(u);
-        // tile u has landed once only the tiles issued after it may be in flight
-        dq_wait_vmem_but(kOpsPerTile * (min(u + C::NS - 2, n_kt - 1) - u));
+        // tile u has landed once only the tiles issued after it may be in
+        // flight; with a bias only the tile copied in the last step may (the
+        // bias of tile u went out just before it), and none when that tile
+        // is u itself (a ring of two)
+        if constexpr (BIAS)
+            dq_wait_vmem_but(C::NS >= 3 && u + C::NS - 2 < n_kt ? kOpsPerTile : 0);
+        else
+            dq_wait_vmem_but(kOpsPerTile * (min(u + C::NS - 2, n_kt - 1) - u));
         __syncthreads();   // tile u is visible to all waves; tile u-1's buffer is free
+        const int j0 = (kt_b + u) * BN;
+        // this tile's bias: this lane's row, keys 32 jb + 8 q4 + 4h .. + 3
+        bchunk_t bia[BIAS ? C::NJB * 4 : 1];
+        if constexpr (BIAS) {
+            const char* bl = smem + C::OFF_BIAS + (u & 1) * kWaves * C::BIAS_W + w * C::BIAS_W + l32 * C::BIAS_ROWB;
+#pragma unroll
+            for (int q = 0; q < C::NJB * 4; ++q)   // 32 jb + 8 q4 = 8 q
+                bia[q] = *reinterpret_cast<const bchunk_t*>(bl + (8 * q + 4 * h) * (int)sizeof(T));
+            if (u + 1 < n_kt) issue_bias(u + 1);
+        }
         if (u + C::NS - 1 < n_kt) issue_tile(u + C::NS - 1);
         const char* lk = buf + C::BUF_K;
         const char* lv = buf + C::BUF_V;
-        const int j0 = (kt_b + u) * BN;
         const bool edge = !((j0 + BN <= si.len_k) && (i0 + BQ <= si.len_q) &&
                             (!MASKED || (j0 + BN - 1 <= i0 + off + a.win_hi && j0 >= i0 + BQ - 1 + off - a.win_lo)));
 
@@ -278,8 +330,15 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     float x = st[jb][v] * scale2 - l2;
-                    if constexpr (ALIBI)
+                    if constexpr (ALIBI || BIAS)
                         x = fmaf(nsl2, fabsf(fdist + (float)(32 * jb + 8 * (v >> 2) + (v & 3))), x);
+                    if constexpr (BIAS) {
+                        const bchunk_t bq = bia[4 * jb + (v >> 2)];
+                        float bv;
+                        if constexpr (sizeof(T) == 2) bv = b16_elem<T>(bq, v & 3);
+                        else bv = __builtin_bit_cast(f32x4, bq)[v & 3];   // whole vector: a cast of one element reads element 0
+                        x = fmaf(bv, kLog2e, x);
+                    }
                     float p = __builtin_amdgcn_exp2f(x);
                     if constexpr (decltype(masked)::value) {
                         const int j = j0 + 32 * jb + acc_row(v, h);
@@ -346,9 +405,9 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 }
 
 
-template <class T, int HD, bool MASKED, bool ALIBI>
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[BIAS ? DqCfg<T, HD>::LDS_BYTES_BIAS : DqCfg<T, HD>::LDS_BYTES];
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
     // kv-head) run on one XCD, so their K/V reads share an L2.  Under a causal
     // mask the keys a query tile sees grow linearly with its index, so
@@ -377,25 +436,27 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
         const int m2 = nq - 1 - p;
         if (m2 > p) {
-            dq_tile<T, HD, MASKED, ALIBI>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            dq_tile<T, HD, MASKED, ALIBI, BIAS>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
             __syncthreads();   // its LDS ring is free again
         }
-        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI, BIAS>(p, a, b, hq, hkv, si, smem);
     } else {
-        dq_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+        dq_tile<T, HD, MASKED, ALIBI, BIAS>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
 static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
     const unsigned grid = (unsigned)((masked ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
-    const bool alibi = a.alibi != nullptr;
+    const bool alibi = a.alibi != nullptr, bias = a.bias != nullptr;
     if (masked) {
-        if (alibi) bwd_dq_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
-        else bwd_dq_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
+        if (bias) bwd_dq_kernel<T, HD, true, false, true><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) bwd_dq_kernel<T, HD, true, true, false><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, true, false, false><<<grid, kThreads, 0, st>>>(a);
     } else {
-        if (alibi) bwd_dq_kernel<T, HD, false, true><<<grid, kThreads, 0, st>>>(a);
-        else bwd_dq_kernel<T, HD, false, false><<<grid, kThreads, 0, st>>>(a);
+        if (bias) bwd_dq_kernel<T, HD, false, false, true><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) bwd_dq_kernel<T, HD, false, true, false><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, false, false, false><<<grid, kThreads, 0, st>>>(a);
     }
 }
 

@@ -454,6 +454,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             }
         }
 
+        if constexpr (!DQ_ATOMIC) {
+            // dBias = dS, straight from the registers (dQ comes from another
+            // pass; each step ends with a full wait for memory operations)
+            if (dbias_h != nullptr) {
+#pragma unroll
+                for (int mb = 0; mb < C::NMB; ++mb) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int ib = i0 + 32 * mb + acc_row(v, h);
+                        if (ib < si.len_q && j < si.len_k)
+                            store_elem(dbias_h, (long long)ib * a.sdbias.r + j, dp[mb][v]);
+                    }
+                }
+            }
+        }
         if constexpr (DQ_ATOMIC) {
         // ---- dS^T to LDS (row = key, column = query row)
         {
@@ -648,17 +663,26 @@ struct KvCfg {
     static constexpr int OFF_P = NBUF * BUF_BYTES;   // [pair][tile parity] P slots
     static constexpr int OFF_CONST = OFF_P + 4 * 2 * PSLOT;   // 16 bytes per wave, see kv_tile
     static constexpr int LDS_BYTES = OFF_CONST + kKvWaves * 16;
+    // elementwise bias: per P wave a [BM rows][32 keys] image (64-byte rows)
+    // in each of two buffers (tile parity), copied one tile ahead
+    static constexpr int BIAS_PAIR = BM * 64;
+    static constexpr int OFF_BIAS = (LDS_BYTES + 1023) / 1024 * 1024;
+    static constexpr int LDS_BYTES_BIAS = OFF_BIAS + 2 * 4 * BIAS_PAIR;
+    static constexpr int BOPS = BM / 16;             // bias copies per tile and P wave (16 rows each)
+    static constexpr int NDBS = BM / 2;              // dBias stores per tile and dS wave (one per element)
     static constexpr int NC = HD / 16;               // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;              // 32-column blocks of the head dim
     static constexpr int OPS = 3;                    // copy instructions per tile and wave
     static_assert(TileCopy<ROWB, BM, kKvWaves>::N == 1, "one segment per wave and tensor");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(LDS_BYTES_BIAS <= 160 * 1024, "LDS budget");
     static_assert(BUF_BYTES % 256 == 0 && TILE % 256 == 0, "XOR addressing needs 256-byte aligned tiles");
     static_assert(BM * 4 <= 256, "LSE/D tile in one 256-byte slot");
 };
 
-// All work of one key tile n of sequence b, kv-head hkv (the body of bwd_kv_kernel).
-template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI>
+// All work of one key tile n of sequence b, kv-head hkv (the body of
+// bwd_kv_kernel).  ALIBI: ALiBi slopes; BIAS: an elementwise bias (and ALiBi
+// too when slopes are given) and, when dbias is set, its gradient dS.
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
     static_assert(sizeof(T) == 2, "16-bit operand types");
     using C = KvCfg<HD>;
@@ -800,7 +824,33 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // ALiBi: lane g holds the slope of the group's q-head g (groups of up to
     // 64 q-heads; larger ones read the slope per tile)
     float slope_v = 0.f;
-    if (ALIBI && lane < G) slope_v = a.alibi[hkv * G + lane];
+    if ((ALIBI || (BIAS && a.alibi != nullptr)) && lane < G) slope_v = a.alibi[hkv * G + lane];
+
+    // ---- elementwise bias (P wave): the [BM rows][32 keys] block of tile
+    // t + 1 is copied during step t into the bias buffer of t + 1's parity,
+    // before the tile copies of that step, so the wait at the top of step
+    // t + 1 covers it.  Lane L copies row L / 4 (+ 16 per copy), keys
+    // 8 (L % 4) .. + 7 of the pair.  The range ends with the tile's last
+    // valid row, at its valid keys rounded up to a 16-byte chunk (inside the
+    // row: bias rows are 16-byte aligned); later rows read zeros.
+    const long long sbr_b = a.sbias.r * (long long)sizeof(T);
+    const int bias_voff = BIAS ? (int)((lane >> 2) * sbr_b) + pair * 64 + (lane & 3) * 16 : 0;
+    const unsigned bias_lds = lds0 + C::OFF_BIAS + pair * C::BIAS_PAIR;
+    auto issue_bias = [&](auto buf_c, int m, int g) {
+        constexpr unsigned BB = decltype(buf_c)::value * 4 * C::BIAS_PAIR;
+        const char* base = reinterpret_cast<const char*>(a.bias) +
+                           ((long long)b * a.sbias.b + (long long)(hkv * G + g) * a.sbias.h +
+                            (long long)m * BM * a.sbias.r + (long long)n * kBN) * (long long)sizeof(T);
+        const int rows = min(BM, si.len_q - m * BM);
+        const unsigned bytes = a.bias == nullptr ? 0u   // dBias without a bias: zeros
+                                                 : (unsigned)((rows - 1) * sbr_b) +
+                                                       (unsigned)(((si.len_k - n * kBN) * (int)sizeof(T) + 15) & ~15);
+        const i32x4 rb = rsrc_words(base, bytes);
+#pragma unroll
+        for (int k = 0; k < C::BOPS; ++k)
+            dma_to_lds16_so(rb, bias_lds + BB + k * 1024, bias_voff, (int)(k * 16 * sbr_b));
+    };
+    if (BIAS && role == 0 && n_tiles > 0) issue_bias(std::integral_constant<unsigned, 0>{}, m_begin, 0);
     wait_vmem();
 
     f32x16 acc[C::NDB];   // dV rows (P wave) or unscaled dK rows (dS wave) of this pair's keys
@@ -875,6 +925,20 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     };
     DsBlocks ds_last{ds_head, ds_cur.blk, ds_cur.cnt};   // tile t-1: what its stores need
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
+    constexpr int NDBS = BIAS ? C::NDBS : 0;      // dBias stores per dS-wave step
+    constexpr int NSTW = NST + NDBS;
+    // dBias (dS wave): element (row r of tile t-1, this lane's key j) goes to
+    // the tile's first row + r * row stride + j, one 16-bit store each.  Keys
+    // past the sequence take an offset past every range; rows past it fall
+    // outside the range (it ends at the last valid row's last key).
+    const long long sdbr_b = a.sdbias.r * (long long)sizeof(T);
+    const int db_voff = j < si.len_k ? (int)(4 * h * sdbr_b) + (32 * pair + l32) * (int)sizeof(T) : kOobOff;
+    int db_m = m_begin, db_g = 0;   // dS wave: query tile and q-head of tile t-1
+    // P wave's transposing reads of its bias image: lane (l32, h) gets key
+    // l32 of rows r0 + 4h + 0..3 (see lds_read_tr; source lane s of each
+    // 16-lane group points at row r0 + 4h + s / 4, keys 16 * (lane / 16 % 2) + 4 (s % 4))
+    const int bias_rd = C::OFF_BIAS + pair * C::BIAS_PAIR + (((lane & 15) >> 2) + 4 * h) * 64 +
+                        2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     // one step: tile t for the P wave, tiles t (first product) and t-1 for the dS wave
     auto step = [&](auto role_c, auto first_c, auto k_c, int t, f32x16* xc, f32x16* xp) {
@@ -890,22 +954,22 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // tiles may still fly); after the barrier all waves' have, P of tile
         // t-1 is in LDS, and every wave is done with tile t-2, whose buffer
         // receives tile t+3
-        // in the stored-dS mode each dS-wave step also issues NST stores,
-        // before its copies, so the copies of tile t are counted past the
-        // stores of the PD - 1 later steps (the first step has no dS; it
-        // stores an empty range instead, to keep the count)
-        if (STORE_DS && R == 1)
-            wait_vmem_but<C::OPS * (C::PD - 1) + NST * (C::PD - 1)>();
+        // in the stored-dS and bias variants each dS-wave step also issues
+        // NSTW stores (dS, dBias), before its copies, so the copies of tile t
+        // are counted past the stores of the PD - 1 later steps (the first
+        // step has no dS; it stores an empty range instead, to keep the count)
+        if (NSTW > 0 && R == 1)
+            wait_vmem_but<C::OPS * (C::PD - 1) + NSTW * (C::PD - 1)>();
         else
             wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
         const int i0 = cur_m * BM;
         // ALiBi slope of tile t's q-head, negated, in log2 units
         float nsl2 = 0.f;
-        if constexpr (ALIBI && R == 0) {
+        if constexpr ((ALIBI || BIAS) && R == 0) {
             const float sl = G <= 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                                      __builtin_bit_cast(int, slope_v), cur_g))
-                                     : a.alibi[hkv * G + cur_g];
+                                     : (a.alibi != nullptr ? a.alibi[hkv * G + cur_g] : 0.f);
             nsl2 = -sl * kLog2e;
         }
         // row statistics of the tile whose second product comes in this step,
@@ -917,6 +981,13 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         u32x4 pin[C::NIC];
 #pragma unroll
         for (int q = 0; q < NMB * 4; ++q) stat[q] = *reinterpret_cast<const f32x4*>(lst + 8 * q);
+        // the bias of tile t (P wave): rows 32 mb + 8 q4 + 4h + 0..3 of this lane's key
+        u32x2 bia[BIAS && R == 0 ? NMB * 4 : 1];
+        if constexpr (BIAS && R == 0) {
+#pragma unroll
+            for (int q = 0; q < NMB * 4; ++q)
+                bia[q] = lds_read_tr(smem, bias_rd + (K & 1) * 4 * C::BIAS_PAIR + q * 8 * 64);
+        }
         if constexpr (R == 1) {
             const int psr = pslots + ((K + 1) & 1) * C::PSLOT + lane * 16;   // slot of tile t-1
 #pragma unroll
@@ -929,7 +1000,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // dS-store work for tile t-1 goes first, while the P wave of the same
         // SIMD computes the exponentials of tile t (measured 1.8% faster with
         // the stores, 0.8% slower without them)
-        constexpr bool DS_LATE = R == 1 && STORE_DS;
+        constexpr bool DS_LATE = R == 1 && NSTW > 0;
         auto first_product = [&]() {
         if (t < n_tiles) {
             // the swizzle XOR touches only address bits 5-7, which are zero
@@ -950,11 +1021,25 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             __builtin_amdgcn_sched_group_barrier(0x100, NMB * C::NC, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NMB * C::NC, 0);
         }
+        if constexpr (BIAS && R == 0) {
+            // the bias of tile t + 1 (the q-head's next query tile, or the next
+            // q-head's first)
+            if (t + 1 < n_tiles) {
+                const bool wrap = cur_m + 1 == m_end;
+                issue_bias(std::integral_constant<unsigned, (K + 1) & 1>{}, wrap ? m_begin : cur_m + 1,
+                           wrap ? cur_g + 1 : cur_g);
+            }
+        }
         issue_next(std::integral_constant<unsigned, ISS>{});
         };
         if constexpr (!DS_LATE) first_product();
         const DsBlocks ds_prev = ds_last;           // dS blocks of tile t-1
         if (STORE_DS) ds_last = DsBlocks{ds_head, ds_cur.blk, ds_cur.cnt};
+        const int dbm = db_m, dbg = db_g;            // query tile and q-head of tile t-1
+        if (BIAS && R == 1) {
+            db_m = cur_m;
+            db_g = cur_g;
+        }
         bool new_head = false;
         if (++cur_m == m_end) {
             cur_m = m_begin;
@@ -980,11 +1065,11 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         // the tile whose second product this wave computes now
         const int tt = R == 0 ? t : t - 1;   // the dS wave's later steps always have a tile t-1
         if (FIRST || (R == 0 && tt >= n_tiles)) {
-            if (STORE_DS && FIRST) {   // the dS wave's first step: empty stores
-                const rsrc_t none = make_rsrc(a.ds, 0);
+            if (NSTW > 0 && FIRST) {   // the dS wave's first step: empty stores
+                const rsrc_t none = make_rsrc(STORE_DS ? a.ds : a.dbias, 0);
                 const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int k = 0; k < NST; ++k) __builtin_amdgcn_raw_buffer_store_b128(z, none, lane * 16, 0, 2);
+                for (int k = 0; k < NSTW; ++k) __builtin_amdgcn_raw_buffer_store_b128(z, none, lane * 16, 0, 2);
             }
             if constexpr (DS_LATE) first_product();
             advance_ds();
@@ -1009,6 +1094,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const int r = 32 * mb + 8 * q4;   // + 4h + e
                         const f32x4 lse = stat[mb * 4 + q4];
+                        constexpr bool XA = ALIBI || BIAS;   // an ALiBi term (slope 0 when absent)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int v = 4 * q4 + e;
@@ -1016,15 +1102,17 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                             if constexpr (decltype(masked)::value) {
                                 const float l2 = lse[e] == -INFINITY ? 0.f : lse[e] * kLog2e;
                                 float x = xc[mb][v] * scale2 - l2;
-                                if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                if constexpr (XA) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                if constexpr (BIAS) x = fmaf(b16_elem<T>(bia[mb * 4 + q4], e), kLog2e, x);
                                 p = __builtin_amdgcn_exp2f(x);
                                 // i + off - lo <= j <= i + off + hi, i = i0 + r + 4h + e
                                 bool vis = dj_hi <= r + e && dj_lo >= r + e;
-                                if constexpr (ALIBI) vis = vis && r + e < row_lim;
+                                if constexpr (XA) vis = vis && r + e < row_lim;
                                 p = vis ? p : 0.f;
                             } else {
                                 float x = fmaf(xc[mb][v], scale2, -lse[e] * kLog2e);
-                                if constexpr (ALIBI) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                if constexpr (XA) x = fmaf(nsl2, fabsf(fdj - (float)(r + e)), x);
+                                if constexpr (BIAS) x = fmaf(b16_elem<T>(bia[mb * 4 + q4], e), kLog2e, x);
                                 p = __builtin_amdgcn_exp2f(x);
                             }
                             xc[mb][v] = p;
@@ -1032,7 +1120,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                     }
                 }
             };
-            if ((MASKED && (i0 < diag_hi || i0 > diag_lo)) || (ALIBI && i0 + BM > si.len_q))
+            if ((MASKED && (i0 < diag_hi || i0 > diag_lo)) || ((ALIBI || BIAS) && i0 + BM > si.len_q))
                 softmax(std::true_type{});
             else
                 softmax(std::false_type{});
@@ -1146,6 +1234,29 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                 }
             }
         }
+        if (BIAS && R == 1) {
+            // dBias = dS of tile t-1 (16-bit, the value dK's product used),
+            // element (row 32 mb + 8 q4 + 4h + e, key j) of operand slice c =
+            // 2 mb + q4 / 2, element 4 (q4 % 2) + e; an empty range without dBias
+            const char* dbase = reinterpret_cast<const char*>(a.dbias) +
+                                ((long long)b * a.sdbias.b + (long long)(hkv * G + dbg) * a.sdbias.h +
+                                 (long long)dbm * BM * a.sdbias.r + (long long)n * kBN) * (long long)sizeof(T);
+            const int rows = min(BM, si.len_q - dbm * BM);
+            const unsigned bytes = a.dbias != nullptr ? (unsigned)((rows - 1) * sdbr_b) +
+                                                            (unsigned)((si.len_k - n * kBN) * (int)sizeof(T))
+                                                      : 0u;
+            const rsrc_t dst = make_rsrc(dbase, bytes);
+#pragma unroll
+            for (int c = 0; c < C::NIC; ++c) {
+                const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = 32 * (c >> 1) + 8 * (2 * (c & 1) + (u >> 2)) + (u & 3);   // + 4h
+                    const unsigned short x = (unsigned short)((u & 1) ? (wv[u >> 1] >> 16) : (wv[u >> 1] & 0xffffu));
+                    __builtin_amdgcn_raw_buffer_store_b16(x, dst, db_voff, (int)(r * sdbr_b), 2);
+                }
+            }
+        }
         if constexpr (DS_LATE) {
             __builtin_amdgcn_sched_barrier(0);
             first_product();
@@ -1206,9 +1317,9 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI>
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[KvCfg<HD>::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[BIAS ? KvCfg<HD>::LDS_BYTES_BIAS : KvCfg<HD>::LDS_BYTES];
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
     // a causal mask key tile n is seen by a number of query tiles that falls
     // linearly with n, so workgroup p takes the tiles p and (last - p), which
@@ -1237,10 +1348,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         const int cnt = (p <= n2) + (n2 > p);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, MASKED, STORE_DS, ALIBI>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
+            kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
-        kv_tile<T, HD, MASKED, STORE_DS, ALIBI>(a, b, hkv, p, si, smem);
+        kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS>(a, b, hkv, p, si, smem);
     }
 }
 
@@ -1250,15 +1361,17 @@ int bwd_block_m(int dtype, int head_dim) {
     return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 64>::BM : BwdCfg<bf16_t, 64>::BM;
 }
 
-// the dK/dV kernel's instantiation for (mask, stored dS, ALiBi)
-template <class T, int HD, bool M, bool S, bool A>
+// the dK/dV kernel's instantiation for (mask, stored dS, ALiBi, bias): the
+// bias variant also applies ALiBi slopes when given
+template <class T, int HD, bool M, bool S, bool A, bool B>
 static void launch_kv3(const BwdArgs& a, unsigned grid, hipStream_t st) {
-    bwd_kv_kernel<T, HD, M, S, A><<<grid, kKvThreads, 0, st>>>(a);
+    bwd_kv_kernel<T, HD, M, S, A, B><<<grid, kKvThreads, 0, st>>>(a);
 }
 template <class T, int HD, bool M, bool S>
 static void launch_kv2(const BwdArgs& a, bool alibi, unsigned grid, hipStream_t st) {
-    if (alibi) launch_kv3<T, HD, M, S, true>(a, grid, st);
-    else launch_kv3<T, HD, M, S, false>(a, grid, st);
+    if (a.bias != nullptr || a.dbias != nullptr) launch_kv3<T, HD, M, S, false, true>(a, grid, st);
+    else if (alibi) launch_kv3<T, HD, M, S, true, false>(a, grid, st);
+    else launch_kv3<T, HD, M, S, false, false>(a, grid, st);
 }
 template <class T, int HD, bool M>
 static void launch_kv1(const BwdArgs& a, bool store_ds, bool alibi, unsigned grid, hipStream_t st) {

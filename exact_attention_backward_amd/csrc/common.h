@@ -111,6 +111,17 @@ __device__ __forceinline__ void to_op(f32x8& o, const float* x) {
     for (int t = 0; t < 8; ++t) o[t] = x[t];
 }
 
+// Element e (0..3) of four 16-bit values of type T packed two per word, low
+// half first, in fp32 (exact).
+template <class T> __device__ __forceinline__ float b16_elem(u32x2 w, int e);
+template <> __device__ __forceinline__ float b16_elem<bf16_t>(u32x2 w, int e) {
+    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+}
+template <> __device__ __forceinline__ float b16_elem<f16_t>(u32x2 w, int e) {
+    const unsigned short u = (unsigned short)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+    return (float)__builtin_bit_cast(f16_t, u);
+}
+
 // MFMA operand of a 16-bit type -> its eight values in fp32 (exact).
 __device__ __forceinline__ void from_op(const bf16x8& o, float* x) {
     const u32x4 w = __builtin_bit_cast(u32x4, o);
@@ -228,24 +239,28 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(size_t)((__attribute__((address_space(3))) const char*)p));
 }
 // M0 (the LDS base of the copy) is an input operand bound to that register,
-// so the compiler sets it, knows it changed, and never sees it clobbered; the
-// s_nop is the wait state required between an M0 write and an LDS-DMA load.
+// so the compiler sets it, knows it changed, and never sees it clobbered.
+// The compiler does not insert hazard wait states around inline assembly,
+// so the s_nop provides them: one after an M0 write, and five after a VALU
+// instruction writes an SGPR that a vector memory instruction then reads
+// (the descriptor and scalar offset may come straight from v_readfirstlane
+// or from a v_readlane of a spilled SGPR).
 __device__ __forceinline__ void dma_to_lds16(i32x4 r, unsigned lds, int voff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 // The same with the non-temporal hint, for data read once (streams that
 // should not displace reused tiles from the L2).
 __device__ __forceinline__ void dma_to_lds16_nt(i32x4 r, unsigned lds, int voff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 // The same with a scalar offset added to the address; the range check
 // applies to the scalar plus the per-lane offset.
 __device__ __forceinline__ void dma_to_lds16_so(i32x4 r, unsigned lds, int voff, int soff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory");
 }
 __device__ __forceinline__ void dma_to_lds4_so(i32x4 r, unsigned lds, int voff, int soff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
+    asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, %3 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory");
 }
 // The scalar-offset copies to an LDS address given as an SGPR base plus a
@@ -264,7 +279,7 @@ __device__ __forceinline__ void dma_to_lds4_at(i32x4 r, unsigned base, int voff,
     dma_to_lds4_so(r, base + OFF, voff, soff);
 }
 __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 
 // ---------------------------------------------------------------------------

@@ -252,16 +252,31 @@ def test_alibi_slopes_alignment():
     assert rc == L.ATTN_ERR_MISALIGNED
 
 
-def test_bias_needs_the_atomic_mode():
+def test_bias_alignment_and_range_by_dq_mode():
+    """Every dQ mode takes a bias and dBias; outside the atomic mode the bias
+    is copied in 16-byte chunks (base, batch, head and row steps 16-byte
+    aligned) and 64 rows of bias or dBias must stay inside a 32-bit offset."""
     fake = ctypes.c_void_p(0x1000)
-    for algo, want in ((L.ATTN_DQ_SEPARATE, L.ATTN_ERR_UNSUPPORTED), (L.ATTN_DQ_STORED_DS, L.ATTN_ERR_UNSUPPORTED)):
-        for field in ("bias", "dbias"):
-            s = shape(dq_algo=algo, **{field: 0x1000})
-            assert ws_bytes(s) == 0
+    for algo in (L.ATTN_DQ_ATOMIC, L.ATTN_DQ_SEPARATE, L.ATTN_DQ_STORED_DS):
+        base = ws_bytes(shape(dq_algo=algo))
+        s = shape(dq_algo=algo, bias=0x1000, dbias=0x2000)
+        s.bias_strides.row = s.dbias_strides.row = 96
+        s.bias_strides.head = s.dbias_strides.head = 96 * 100
+        assert ws_bytes(s) == base
+        for field, value, aligned_ok in (("bias", 0x1008, False), ("dbias", 0x1002, True)):
+            s = shape(dq_algo=algo, **{field: value})
+            getattr(s, field + "_strides").row = 96
+            assert (ws_bytes(s) == base) == (algo == L.ATTN_DQ_ATOMIC or aligned_ok), (algo, field)
+        s = shape(dq_algo=algo, bias=0x1000)
+        s.bias_strides.row = 90   # 180 bytes: not a multiple of 16
+        want_ok = algo == L.ATTN_DQ_ATOMIC
+        assert (ws_bytes(s) == base) == want_ok
+        if not want_ok:
             rc = L.lib().attn_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, 1 << 40, fake, fake, None)
-            assert rc == want
-    s = shape(dq_algo=L.ATTN_DQ_ATOMIC, bias=0x1000, dbias=0x2000)
-    assert ws_bytes(s) == ws_bytes(shape(dq_algo=L.ATTN_DQ_ATOMIC))
+            assert rc == L.ATTN_ERR_MISALIGNED
+        s = shape(dq_algo=algo, dbias=0x1000)
+        s.dbias_strides.row = 1 << 24   # 64 rows of 32 MiB
+        assert (ws_bytes(s) == base) == (algo == L.ATTN_DQ_ATOMIC)
     s = shape(dq_algo=L.ATTN_DQ_ATOMIC, bias=0x1001)
     assert ws_bytes(s) == 0   # misaligned for bf16
     s = shape(dq_algo=L.ATTN_DQ_ATOMIC, dbias=0x1000)

@@ -503,7 +503,7 @@ def test_strided_layouts_match_contiguous_bitwise(case, dq_algo):
         assert_close(n, to_host(g.contiguous()), rr, p.dtype)
 
 
-# elementwise bias + dBias (atomic dQ mode): (dtype, B, Hq, Hkv, Sq, Sk, D, causal, lengths, window, broadcast)
+# elementwise bias + dBias: (dtype, B, Hq, Hkv, Sq, Sk, D, causal, lengths, window, broadcast)
 BIAS_CASES = [
     ("bf16", 2, 3, 3, 200, 200, 128, True, None, None, None),
     ("bf16", 1, 4, 2, 170, 260, 64, False, None, None, "heads"),     # one bias for every q-head
@@ -520,20 +520,31 @@ def _biasid(c):
     return f"{_id(c[:9])}{w}{bc}"
 
 
+@pytest.mark.parametrize("algo", ["atomic", "separate", "stored_ds"])
 @pytest.mark.parametrize("full", [False, True], ids=["three_calls", "bwd_full"])
 @pytest.mark.parametrize("case", BIAS_CASES, ids=_biasid)
-def test_bias_and_dbias_match_oracle(case, full):
-    """O and LSE with the bias, dQ/dK/dV and dBias = dS against the oracle;
-    dBias outside each sequence's block keeps its contents."""
+def test_bias_and_dbias_match_oracle(case, full, algo):
+    """O and LSE with the bias, dQ/dK/dV and dBias = dS against the oracle in
+    every dQ mode; dBias outside each sequence's block keeps its contents.
+    Outside the atomic mode bias rows are 16-byte aligned: the bias is a view
+    of rows padded to a multiple of 8 keys."""
     import datagen
     p = problem(case[:9])
+    if algo == "stored_ds" and p.dtype == "f32":
+        pytest.skip("the stored-dS mode is for 16-bit types")
     win, bcast = case[9], case[10]
     r = Run(p, oracle_o_lse=False, window=win)
     nb = len(case[8]) if case[8] else case[1]
     bias_np = datagen.draw_bias(p, 91, heads=1 if bcast == "heads" else None, batch=1 if bcast == "batch" else nb)
-    bias_dev = to_dev(bias_np, p.dtype).expand(nb, p.heads_q, p.seqlen_q, p.seqlen_k)
+    bias_dev = to_dev(bias_np, p.dtype)
+    if algo != "atomic":
+        skp = (p.seqlen_k + 7) // 8 * 8
+        padded = torch.full(bias_dev.shape[:3] + (skp,), float("nan"), dtype=bias_dev.dtype, device="cuda")
+        padded[..., :p.seqlen_k] = bias_dev
+        bias_dev = padded[..., :p.seqlen_k]
+    bias_dev = bias_dev.expand(nb, p.heads_q, p.seqlen_q, p.seqlen_k)
     bias_full = np.broadcast_to(bias_np, (nb, p.heads_q, p.seqlen_q, p.seqlen_k))
-    print(f"bias {_biasid(case)} full={full}", flush=True)
+    print(f"bias {_biasid(case)} full={full} algo={algo}", flush=True)
     d, kw = r.dev, r.kw()
     cq, ck = r.cu_np
     o, lse = api.forward(d["q"], d["k"], d["v"], p.scale, p.causal, window=win, bias=bias_dev, **kw)
@@ -548,7 +559,7 @@ def test_bias_and_dbias_match_oracle(case, full):
     r.set_o_lse(ro, rlse)
     sentinel = 9.0
     dbias = torch.full((nb, p.heads_q, p.seqlen_q, p.seqlen_k), sentinel, dtype=d["q"].dtype, device="cuda")
-    plan = api.BackwardPlan(d["q"], d["k"], p.scale, p.causal, False, dq_algo="atomic", window=win,
+    plan = api.BackwardPlan(d["q"], d["k"], p.scale, p.causal, False, dq_algo=algo, window=win,
                             bias=bias_dev, dbias=dbias, **kw)
     dq, dk, dv = (torch.empty_like(d[n]) for n in ("q", "k", "v"))
     (plan.run_full if full else plan.run)(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], dq, dk, dv)
