@@ -73,10 +73,11 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     key j iff i + off - left <= j <= i + off + right (off = len_k - len_q, -1
     for an unbounded side), intersected with the causal bound when causal.
     alibi_slopes: fp32 device tensor [Hq]; the logits get -slope_h |i + off - j|.
-    bias / dbias (atomic dQ mode): tensors indexed [b, h, i, j] (b the
-    sequence for varlen; keys contiguous, any batch/head/row strides, 0 to
-    broadcast the bias); the bias is added to the logits and dbias receives
-    dS.  max_workspace_bytes caps the stored-dS workspace (kv-head groups in
+    bias / dbias: tensors indexed [b, h, i, j] (b the sequence for varlen;
+    keys contiguous, batch/head/row strides of 0 broadcast the bias); the
+    bias is added to the logits and dbias receives dS.  Outside the atomic
+    dQ mode the bias needs 16-byte aligned rows and base (pad the key axis
+    to a multiple of 8 for 16-bit types).  max_workspace_bytes caps the stored-dS workspace (kv-head groups in
     chunks, or the separate mode when not even one fits).  cu_seqlens_host =
     (cu_q, cu_k): contiguous int32 CPU tensors holding the offsets, kept
     alive by the caller while the shape is used; with them the stored-dS
