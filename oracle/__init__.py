@@ -7,4 +7,8 @@ Every function carries "parity pinned" status in its own tests
 """
 
 from .attention import *  # noqa: F401,F403
-from .attention import __all__  # noqa: F401
+from .dropout import *  # noqa: F401,F403
+from .attention import __all__ as _a
+from .dropout import __all__ as _d
+
+__all__ = list(_a) + list(_d)

@@ -44,6 +44,15 @@ Readings taken where the pages are silent (each is listed in the design notes):
   with respect to the logit s q_i . k_j + bias_ij is exactly dS_ij, so dBias
   = dS; a bias broadcast over batch or heads is not summed here (the page
   writes one dBias tile per (batch, head) tile).
+* Dropout (``dropout`` arguments): P is computed as without dropout (the
+  LSE keeps every visible key); the output uses Z P / (1 - p) with Z the
+  keep mask of ``oracle.dropout``.  The gradient of that output is
+  dV = (Z P)^T dO / (1 - p), dP = Z (dO V^T) / (1 - p), dS = P (dP - D) with
+  D = rowsum(dO * O) of the dropped output.  The composable-kernel page forms
+  dS from the sign-marked P as P (dP' - D') on kept and -P D' on dropped
+  elements and then scales dS-derived results by rp_undrop; that is this
+  same gradient when its D' is D (1 - p), the reading taken for the D it
+  consumes but does not define.
 * GQA groups are contiguous: q-head h reads kv-head ``h // (Hq // Hkv)``, as in
   the head mapping of ``CollectiveEpilogueBwdGQA::store`` on the
   FlashAttention-3 page "flash-attention/hopper/epilogue_bwd.hpp"; dK and dV of
@@ -57,6 +66,8 @@ Layouts (all numpy arrays, any float dtype, computed in float64):
 """
 
 import numpy as np
+
+from .dropout import dropout_keep
 
 __all__ = [
     "visible",
@@ -130,13 +141,15 @@ def _logits(q, k, scale, alibi, bias=None):
     return s
 
 
-def head_forward(q, k, v, scale, causal, window=None, alibi=None, bias=None):
+def head_forward(q, k, v, scale, causal, window=None, alibi=None, bias=None, dropout=None):
     """Softmax attention for one head.
 
     q [sq, d], k [sk, d], v [sk, d] -> (o [sq, d], lse [sq]), float64.
     ``lse_i = log(sum_j exp(s * q_i . k_j + b_ij))`` over the visible keys
     (b the ALiBi bias of slope ``alibi``, or 0), ``o_i = sum_j softmax_ij
     v_j``.  Rows with no visible key give lse = -inf and o = 0.
+    ``dropout = (keep [sq, sk] bool, rp)``: ``o_i = rp sum_j keep_ij
+    softmax_ij v_j`` (the LSE is unchanged).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -154,6 +167,9 @@ def head_forward(q, k, v, scale, causal, window=None, alibi=None, bias=None):
     lse[has_key] = row_max[has_key] + np.log(total[has_key])
     p = np.zeros_like(s)
     p[has_key] = e[has_key] / total[has_key, None]
+    if dropout is not None:
+        keep, rp = dropout
+        p = rp * np.where(keep, p, 0.0)
     o = p @ v
     return o, lse
 
@@ -167,13 +183,16 @@ def _probabilities(q, k, lse, scale, causal, window=None, alibi=None, bias=None)
     return np.exp(np.where(ok, s - safe_lse[:, None], -np.inf))
 
 
-def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None, alibi=None, bias=None):
+def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None, alibi=None, bias=None,
+                  dropout=None):
     """Gradient of attention for one head, given O and LSE as saved by a forward.
 
     Returns (dq [sq, d], dk [sk, d], dv [sk, d]) in float64; with
     ``details=True`` also a dict holding P, dP, dS and D.  The ALiBi and
     elementwise biases only enter through P (they do not depend on Q or K);
     the gradient of the elementwise bias is dS (``details["ds"]``).
+    ``dropout = (keep [sq, sk] bool, rp)`` as in head_forward: dV =
+    rp (keep P)^T dO and dP = rp keep (dO V^T).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -184,7 +203,12 @@ def head_backward(q, k, v, o, do, lse, scale, causal, details=False, window=None
     p = _probabilities(q, k, lse, scale, causal, window, alibi, bias)  # stages 1-2
     delta = np.sum(do * o, axis=1)                        # D = rowsum(dO * O)
     dp = do @ v.T                                         # stage 4
-    dv = p.T @ do                                         # stage 3
+    if dropout is None:
+        dv = p.T @ do                                     # stage 3
+    else:
+        keep, rp = dropout
+        dv = (rp * np.where(keep, p, 0.0)).T @ do         # stage 3 on the kept P
+        dp = rp * np.where(keep, dp, 0.0)
     ds = p * (dp - delta[:, None])                        # stage 5
     dk = scale * (ds.T @ q)                               # stage 6 + final scale
     dq = scale * (ds @ k)                                 # stage 7 + dQ scale
@@ -367,13 +391,25 @@ def _bias_block(bias, seq, h, len_q, len_k):
     return None if bias is None else np.asarray(bias)[seq, h, :len_q, :len_k]
 
 
+def _dropout_block(dropout, seq, h, hq, len_q, len_k):
+    """(keep mask, 1 / (1 - p)) of one (sequence, q-head) for ``dropout =
+    (p, seed, offset)``, or None."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    return dropout_keep(seed, offset, seq * hq + h, len_q, len_k, p), 1.0 / (1.0 - float(p))
+
+
 def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_seqlens_k=None,
-                  seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None):
+                  seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None, dropout=None):
     """Forward for the q-heads of one kv-head group of one sequence.
 
     Returns {q_head: (o [len_q, d], lse [len_q])}.  ``alibi_slopes``: one
     slope per q-head, or None.  ``bias``: [nseq, Hq, Sq, Sk] (Sq, Sk the
     longest lengths), each sequence's block at its top left, or None.
+    ``dropout``: (p, seed, offset) or None; the keep mask of (sequence, q-head)
+    uses index sequence * Hq + q-head and the sequence's own row and key
+    positions.
     """
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
     g = hq // hkv
@@ -382,13 +418,14 @@ def group_forward(q, k, v, scale, causal, seq, kv_head, cu_seqlens_q=None, cu_se
     out = {}
     for h in range(kv_head * g, (kv_head + 1) * g):
         out[h] = head_forward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head], scale, causal, window,
-                              _slope(alibi_slopes, h), _bias_block(bias, seq, h, q1 - q0, k1 - k0))
+                              _slope(alibi_slopes, h), _bias_block(bias, seq, h, q1 - q0, k1 - k0),
+                              _dropout_block(dropout, seq, h, hq, q1 - q0, k1 - k0))
     return out
 
 
 def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
                    cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None, window=None,
-                   alibi_slopes=None, bias=None, dbias_out=None):
+                   alibi_slopes=None, bias=None, dbias_out=None, dropout=None):
     """Backward for one kv-head group of one sequence.
 
     Returns (dq {q_head: [len_q, d]}, dk [len_k, d], dv [len_k, d]); dk and dv
@@ -410,7 +447,8 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
         dqh, dkh, dvh, det = head_backward(qf[q0:q1, h], kf[k0:k1, kv_head], vf[k0:k1, kv_head],
                                            of[q0:q1, h], dof[q0:q1, h], lf[h, q0:q1], scale, causal, details=True,
                                            window=window, alibi=_slope(alibi_slopes, h),
-                                           bias=_bias_block(bias, seq, h, q1 - q0, k1 - k0))
+                                           bias=_bias_block(bias, seq, h, q1 - q0, k1 - k0),
+                                           dropout=_dropout_block(dropout, seq, h, hq, q1 - q0, k1 - k0))
         if dbias_out is not None:
             dbias_out[seq, h, :q1 - q0, :k1 - k0] = det["ds"]
         dq[h] = dqh
@@ -420,7 +458,7 @@ def group_backward(q, k, v, o, do, lse, scale, causal, seq, kv_head,
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None,
-            window=None, alibi_slopes=None, bias=None):
+            window=None, alibi_slopes=None, bias=None, dropout=None):
     """Full forward.  Returns (o, lse) in the layouts given in the module doc
     (rows past a sequence's used length are left at zero)."""
     varlen, nseq, sq, sk, hq, hkv = _geometry(q, k, cu_seqlens_q, cu_seqlens_k)
@@ -430,7 +468,8 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
     for b, (q0, q1, _, _) in enumerate(_ranges(nseq, sq, sk, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)):
         for g in range(hkv):
             for h, (oh, lh) in group_forward(q, k, v, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
-                                             seqused_q, seqused_k, window, alibi_slopes, bias).items():
+                                             seqused_q, seqused_k, window, alibi_slopes, bias,
+                                             dropout).items():
                 o[q0:q1, h] = oh
                 lse[h, q0:q1] = lh
     if varlen:
@@ -439,7 +478,8 @@ def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, sequse
 
 
 def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None,
-             seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None, want_dbias=False):
+             seqused_q=None, seqused_k=None, window=None, alibi_slopes=None, bias=None, want_dbias=False,
+             dropout=None):
     """Full backward.  Returns (dq, dk, dv) shaped like q, k, v (float64);
     rows past a sequence's used length are left at zero.  With
     ``want_dbias`` also dBias [nseq, Hq, Sq, Sk] (dS of each head; zero
@@ -460,7 +500,7 @@ def backward(q, k, v, o, do, lse, scale, causal, cu_seqlens_q=None, cu_seqlens_k
     for b, (q0, q1, k0, k1) in enumerate(ranges):
         for g in range(hkv):
             dqg, dkg, dvg = group_backward(q, k, v, o, do, lse, scale, causal, b, g, cu_seqlens_q, cu_seqlens_k,
-                                           seqused_q, seqused_k, window, alibi_slopes, bias, dbias)
+                                           seqused_q, seqused_k, window, alibi_slopes, bias, dbias, dropout)
             for h, x in dqg.items():
                 dq[q0:q1, h] = x
             dk[k0:k1, g] = dkg
