@@ -56,6 +56,8 @@ def parse():
                     help="dQ from dS stored by the dK/dV kernel (default for bf16/fp16), by a query-stationary "
                          "pass that recomputes S and dP (default for fp32), or by fp32 atomics")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="dropout of P with probability P (Philox4x32-10 keep mask, seed 1, offset 0)")
     ap.add_argument("--bias", action="store_true",
                     help="an elementwise bias [B, Hq, Sq, Sk] (seeded normal x 2) and its gradient dBias")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -185,9 +187,10 @@ def main():
         bshape = (p.batch, p.heads_q, p.seqlen_q, p.seqlen_k)
         bias = (2 * torch.randn(bshape, generator=gen, device="cuda")).to(dt)
         dbias = torch.empty_like(bias)
-    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=bias, **kw)
+    drop = (args.dropout, 1, 0) if args.dropout > 0 else None
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=bias, dropout=drop, **kw)
     plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, dq_algo=args.dq_algo,
-                            bias=bias, dbias=dbias, **kw)
+                            bias=bias, dbias=dbias, dropout=drop, **kw)
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
@@ -257,9 +260,9 @@ def main():
     post_bytes = rows_q * p.heads_q * p.head_dim * (4 + elem)
 
     out = {
-        "metric": METRIC if args.workload == "c3" and not args.bias else
-        f"attention-backward TFLOP/s ({p.dtype}, {p.name}{', elementwise bias and dBias' if args.bias else ''}) "
-        "and % of MFMA peak",
+        "metric": METRIC if args.workload == "c3" and not args.bias and not args.dropout else
+        f"attention-backward TFLOP/s ({p.dtype}, {p.name}{', elementwise bias and dBias' if args.bias else ''}"
+        f"{f', dropout {args.dropout}' if args.dropout else ''}) and % of MFMA peak",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -279,7 +282,7 @@ def main():
             "batch": p.batch, "heads_q": p.heads_q, "heads_kv": p.heads_kv, "seqlen_q": p.seqlen_q,
             "seqlen_k": p.seqlen_k, "head_dim": p.head_dim, "causal": p.causal,
             "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
-            "bias": bool(args.bias),
+            "bias": bool(args.bias), "dropout": args.dropout,
         },
         "roofline": {
             "kernel": ("attn_bwd (" if three else "attn_bwd_full (") + KERNEL_DESC[args.dq_algo] +
@@ -289,7 +292,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None if args.bias else traffic_entry(args.dq_algo, args.workload, args.api),
+            "traffic": None if args.bias or args.dropout else traffic_entry(args.dq_algo, args.workload, args.api),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,
         },

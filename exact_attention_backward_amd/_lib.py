@@ -88,6 +88,9 @@ class AttnShape(ctypes.Structure):
         ("max_workspace_bytes", ctypes.c_int64),
         ("cu_seqlens_q_host", ctypes.c_void_p),
         ("cu_seqlens_k_host", ctypes.c_void_p),
+        ("dropout_seed", ctypes.c_uint64),
+        ("dropout_p", ctypes.c_float),
+        ("dropout_offset", ctypes.c_uint32),
     ]
 
 

@@ -63,7 +63,7 @@ DQ_ALGOS = {"separate": L.ATTN_DQ_SEPARATE, "atomic": L.ATTN_DQ_ATOMIC, "stored_
 def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
                window=None, alibi_slopes=None, bias=None, dbias=None, max_workspace_bytes=0,
-               cu_seqlens_host=None):
+               cu_seqlens_host=None, dropout=None):
     """attn_shape_t for the given tensors (the dtype is q's).  dq_algo is
     "separate" (query-stationary dQ pass recomputing S and dP, no atomics),
     "stored_ds" (dS stored in the 16-bit I/O type by the dK/dV kernel, then
@@ -77,7 +77,10 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
     keys contiguous, batch/head/row strides of 0 broadcast the bias); the
     bias is added to the logits and dbias receives dS.  Outside the atomic
     dQ mode the bias needs 16-byte aligned rows and base (pad the key axis
-    to a multiple of 8 for 16-bit types).  max_workspace_bytes caps the stored-dS workspace (kv-head groups in
+    to a multiple of 8 for 16-bit types).  dropout = (p, seed, offset): drop
+    probability p in [0, 1) with the library's Philox4x32-10 keep mask (seed
+    the 64-bit key, offset the 32-bit counter word); forward and backward
+    must get the same triple.  max_workspace_bytes caps the stored-dS workspace (kv-head groups in
     chunks, or the separate mode when not even one fits).  cu_seqlens_host =
     (cu_q, cu_k): contiguous int32 CPU tensors holding the offsets, kept
     alive by the caller while the shape is used; with them the stored-dS
@@ -123,6 +126,11 @@ def make_shape(q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_s
                 raise ValueError("host cu_seqlens must be contiguous int32 CPU tensors")
             setattr(s, name, t.data_ptr())
     s.max_workspace_bytes = int(max_workspace_bytes)
+    if dropout is not None:
+        p, seed, offset = dropout
+        s.dropout_p = float(p)
+        s.dropout_seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        s.dropout_offset = int(offset) & 0xFFFFFFFF
     s.softmax_scale = float(scale)
     s.causal = int(bool(causal))
     s.deterministic = int(bool(deterministic))
@@ -209,12 +217,13 @@ def _lse_shape(shape, varlen):
 
 
 def forward(q, k, v, scale, causal, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
-            seqused_q=None, seqused_k=None, out=None, window=None, alibi_slopes=None, bias=None):
+            seqused_q=None, seqused_k=None, out=None, window=None, alibi_slopes=None, bias=None, dropout=None):
     """Plain forward: returns (o, lse).  ``out`` = (o, lse) writes into given
-    buffers (rows past the used lengths keep their contents)."""
+    buffers (rows past the used lengths keep their contents).  ``dropout`` =
+    (p, seed, offset): see make_shape."""
     shape = make_shape(q, k, scale, causal, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                        seqused_q=seqused_q, seqused_k=seqused_k, window=window, alibi_slopes=alibi_slopes,
-                       bias=bias)
+                       bias=bias, dropout=dropout)
     if out is not None:
         o, lse = out
     else:
@@ -234,14 +243,14 @@ class BackwardPlan:
     def __init__(self, q, k, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
                  max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
                  window=None, alibi_slopes=None, bias=None, dbias=None, max_workspace_bytes=0,
-                 host_offsets=True):
+                 host_offsets=True, dropout=None):
         # host copies of the offsets size the stored-dS workspace exactly
         host = None
         if cu_seqlens_q is not None and host_offsets:
             host = (cu_seqlens_q.to("cpu", torch.int32).contiguous(), cu_seqlens_k.to("cpu", torch.int32).contiguous())
         self.shape = make_shape(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k,
                                 max_seqlen_q, max_seqlen_k, dq_algo, seqused_q, seqused_k, window, alibi_slopes,
-                                bias, dbias, max_workspace_bytes, host)
+                                bias, dbias, max_workspace_bytes, host, dropout)
         self._keep = (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, alibi_slopes, bias, dbias, host)
         self.scale = float(scale)
         nbytes = attn_bwd_workspace_bytes(self.shape)
@@ -289,10 +298,10 @@ class BackwardPlan:
 
 def backward(q, k, v, o, do, lse, scale, causal, deterministic=False, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, dq_algo="separate", seqused_q=None, seqused_k=None,
-             window=None, alibi_slopes=None, bias=None, dbias=None):
+             window=None, alibi_slopes=None, bias=None, dbias=None, dropout=None):
     """Full backward: returns (dq, dk, dv) (and fills dbias when given)."""
     plan = BackwardPlan(q, k, scale, causal, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                        dq_algo, seqused_q, seqused_k, window, alibi_slopes, bias, dbias)
+                        dq_algo, seqused_q, seqused_k, window, alibi_slopes, bias, dbias, dropout=dropout)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     plan.run(q, k, v, o, do, lse, dq, dk, dv)
     return dq, dk, dv

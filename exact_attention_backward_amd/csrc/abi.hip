@@ -62,6 +62,7 @@ int validate_shape(const attn_shape_t* s) {
         return ATTN_ERR_UNSUPPORTED;
     if (s->dq_algo == ATTN_DQ_STORED_DS && s->dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
     if (s->max_workspace_bytes < 0) return ATTN_ERR_BAD_SHAPE;
+    if (!(s->dropout_p >= 0.f && s->dropout_p < 1.f)) return ATTN_ERR_BAD_SHAPE;   // NaN included
     // element counts must stay addressable with 64-bit offsets and 32-bit row counts
     const long long rows_q = s->cu_seqlens_q ? s->total_q : (long long)s->batch * s->seqlen_q;
     const long long rows_k = s->cu_seqlens_k ? s->total_k : (long long)s->batch * s->seqlen_k;
@@ -119,6 +120,22 @@ int validate_bwd(const attn_shape_t* s) {
 }
 
 bool varlen(const attn_shape_t* s) { return s->cu_seqlens_q != nullptr; }
+
+// The kernels' dropout parameters: keep iff the random byte >= round(256 p)
+// (at most 255), kept values scaled by 1 / (1 - p).
+Dropout dropout_args(const attn_shape_t* s) {
+    Dropout d{};
+    if (s->dropout_p > 0.f) {
+        const double p = s->dropout_p;
+        d.on = 1;
+        d.thr = (unsigned)std::min(255.0, std::floor(256.0 * p + 0.5));
+        d.k0 = (unsigned)(s->dropout_seed & 0xffffffffu);
+        d.k1 = (unsigned)(s->dropout_seed >> 32);
+        d.off = s->dropout_offset;
+        d.rp = (float)(1.0 / (1.0 - p));
+    }
+    return d;
+}
 
 // the head dim the kernels tile with: head_dim rounded up to 64 or 128
 int padded_hd(const attn_shape_t* s) { return s->head_dim <= 64 ? 64 : 128; }
@@ -325,9 +342,10 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.so = to_kernel(d.o);
     a.bias = s->bias;
     a.sbias = to_kernel(s->bias_strides);
-    // the MFMA forward for the 16-bit types; fp32 and the elementwise bias
-    // take the plain one
-    if (s->dtype != ATTN_DTYPE_F32 && s->bias == nullptr)
+    a.drop = dropout_args(s);
+    // the MFMA forward for the 16-bit types; fp32, the elementwise bias and
+    // dropout take the plain one
+    if (s->dtype != ATTN_DTYPE_F32 && s->bias == nullptr && !a.drop.on)
         launch_fwd_mfma(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     else
         launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
@@ -381,6 +399,7 @@ BwdArgs bwd_args(const attn_shape_t* s, const Layout& l, void* workspace) {
     a.dbias = s->dbias;
     a.sbias = to_kernel(s->bias_strides);
     a.sdbias = to_kernel(s->dbias_strides);
+    a.drop = dropout_args(s);
     if (l.p.algo == ATTN_DQ_STORED_DS) {
         a.ds_tile_base = reinterpret_cast<const int*>(ws + l.tab);
         a.ds_prefix = a.ds_tile_base + s->batch + 1;

@@ -156,8 +156,10 @@ __device__ __forceinline__ void dq_wait_vmem_but(int n) {
 }  // namespace
 
 // dQ rows of query tile m (128 rows) of q-head hq in sequence b.  BIAS: an
-// elementwise bias (and ALiBi too when slopes are given).
-template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS>
+// elementwise bias (and ALiBi too when slopes are given); DROP (with BIAS):
+// dropout of P as well (dS = P (dP / (1 - p) - D) on kept, -P D on dropped
+// elements).
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
 __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                         char* smem) {
     using C = DqCfg<T, HD>;
@@ -324,6 +326,16 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         // ALiBi distance of key j0 + 32 jb + acc_row(v, h) from this lane's
         // diagonal key i + off: fdist + 32 jb + 8 (v / 4) + v % 4
         const float fdist = (float)(j0 + 4 * h - i - off);
+        // dropout: this lane's row i of the 4 x 4 blocks (keys j0 + 8 q + 4h ..
+        // + 3, q = 4 jb + q4): word i % 4, byte (key % 4)
+        unsigned dword_[DROP ? C::NJB * 4 : 1];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int q = 0; q < C::NJB * 4; ++q)
+                dword_[q] = word_at(drop_block((unsigned)((j0 + 8 * q + 4 * h) >> 2), (unsigned)(i >> 2),
+                                               (unsigned)(b * a.hq + hq), a.drop.off, a.drop.k0, a.drop.k1),
+                                    i & 3);
+        }
         auto softmax_grad = [&](auto masked) {
 #pragma unroll
             for (int jb = 0; jb < C::NJB; ++jb) {
@@ -344,7 +356,12 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
                         const int j = j0 + 32 * jb + acc_row(v, h);
                         p = (j < lim && j >= lim_lo) ? p : 0.f;
                     }
-                    dpt[jb][v] = p * (dpt[jb][v] - dl);
+                    if constexpr (DROP) {
+                        const bool keep = drop_keep(dword_[4 * jb + (v >> 2)], v & 3, a.drop.thr);
+                        dpt[jb][v] = p * ((keep ? a.drop.rp * dpt[jb][v] : 0.f) - dl);
+                    } else {
+                        dpt[jb][v] = p * (dpt[jb][v] - dl);
+                    }
                 }
             }
         };
@@ -405,7 +422,7 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 }
 
 
-template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS>
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[BIAS ? DqCfg<T, HD>::LDS_BYTES_BIAS : DqCfg<T, HD>::LDS_BYTES];
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
@@ -436,27 +453,30 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
         const int m2 = nq - 1 - p;
         if (m2 > p) {
-            dq_tile<T, HD, MASKED, ALIBI, BIAS>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
             __syncthreads();   // its LDS ring is free again
         }
-        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI, BIAS>(p, a, b, hq, hkv, si, smem);
+        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     } else {
-        dq_tile<T, HD, MASKED, ALIBI, BIAS>(p, a, b, hq, hkv, si, smem);
+        dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
 static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
     const unsigned grid = (unsigned)((masked ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
-    const bool alibi = a.alibi != nullptr, bias = a.bias != nullptr;
+    // variants: plain, ALiBi, bias (+ ALiBi), dropout (+ bias, ALiBi)
+    const bool alibi = a.alibi != nullptr, bias = a.bias != nullptr, drop = a.drop.on;
     if (masked) {
-        if (bias) bwd_dq_kernel<T, HD, true, false, true><<<grid, kThreads, 0, st>>>(a);
-        else if (alibi) bwd_dq_kernel<T, HD, true, true, false><<<grid, kThreads, 0, st>>>(a);
-        else bwd_dq_kernel<T, HD, true, false, false><<<grid, kThreads, 0, st>>>(a);
+        if (drop) bwd_dq_kernel<T, HD, true, false, true, true><<<grid, kThreads, 0, st>>>(a);
+        else if (bias) bwd_dq_kernel<T, HD, true, false, true, false><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) bwd_dq_kernel<T, HD, true, true, false, false><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, true, false, false, false><<<grid, kThreads, 0, st>>>(a);
     } else {
-        if (bias) bwd_dq_kernel<T, HD, false, false, true><<<grid, kThreads, 0, st>>>(a);
-        else if (alibi) bwd_dq_kernel<T, HD, false, true, false><<<grid, kThreads, 0, st>>>(a);
-        else bwd_dq_kernel<T, HD, false, false, false><<<grid, kThreads, 0, st>>>(a);
+        if (drop) bwd_dq_kernel<T, HD, false, false, true, true><<<grid, kThreads, 0, st>>>(a);
+        else if (bias) bwd_dq_kernel<T, HD, false, false, true, false><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) bwd_dq_kernel<T, HD, false, true, false, false><<<grid, kThreads, 0, st>>>(a);
+        else bwd_dq_kernel<T, HD, false, false, false, false><<<grid, kThreads, 0, st>>>(a);
     }
 }
 

@@ -380,8 +380,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         T* dbias_h = a.dbias != nullptr ? reinterpret_cast<T*>(a.dbias) + (long long)b * a.sdbias.b +
                                               (long long)hq * a.sdbias.h
                                         : nullptr;
-        // extra: ALiBi and the bias (each present or not); rows and keys past
-        // the sequence read no bias
+        // extra: ALiBi, the bias and dropout (each present or not); rows and
+        // keys past the sequence read no bias.  Dropout: the rows r..r+3 of
+        // key j form one column of a 4 x 4 block; dropped elements leave dV
+        // (P zeroed) and enter dS as -P D
         auto softmax_grad = [&](auto masked, auto extra) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
@@ -390,6 +392,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                     const int r = 32 * mb + 8 * q4 + 4 * h;
                     const f32x4 lse = *reinterpret_cast<const f32x4*>(llse + r);
                     const f32x4 dl = *reinterpret_cast<const f32x4*>(ldl + r);
+                    u32x4 dw = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // keep all
+                    if constexpr (decltype(extra)::value) {
+                        if (a.drop.on)
+                            dw = drop_block((unsigned)(j >> 2), (unsigned)((i0 + r) >> 2), (unsigned)(b * a.hq + hq),
+                                            a.drop.off, a.drop.k0, a.drop.k1);
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * q4 + e;
@@ -409,13 +417,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                             const int lo = MASKED ? i + off - a.win_lo : 0;
                             p = (j < lim && j >= lo) ? p : 0.f;
                         }
+                        if constexpr (decltype(extra)::value) {
+                            if (a.drop.on) {
+                                const bool keep = drop_keep(word_at(dw, e), j & 3, a.drop.thr);
+                                s[mb][v] = keep ? p : 0.f;
+                                dp[mb][v] = p * ((keep ? a.drop.rp * dp[mb][v] : 0.f) - dl[e]);
+                                continue;
+                            }
+                        }
                         s[mb][v] = p;
                         dp[mb][v] = p * (dp[mb][v] - dl[e]);
                     }
                 }
             }
         };
-        if (a.alibi != nullptr || a.bias != nullptr) {
+        if (a.alibi != nullptr || a.bias != nullptr || a.drop.on) {
             if (edge)
                 softmax_grad(std::true_type{}, std::true_type{});
             else
@@ -597,7 +613,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             wait_vmem();
     }
 
-    // ---- epilogue: dK = s * sum dS^T Q, dV; rows past the sequence are not written
+    // ---- epilogue: dK = s * sum dS^T Q, dV (times 1 / (1 - p) under dropout);
+    // rows past the sequence are not written
+    const float dv_scale = a.drop.on ? a.drop.rp : 1.f;
     T* dkg = reinterpret_cast<T*>(a.dk) + seq_off(a.sdk, varlen, b, si.k0) + (long long)hkv * a.sdk.h;
     T* dvg = reinterpret_cast<T*>(a.dv) + seq_off(a.sdv, varlen, b, si.k0) + (long long)hkv * a.sdv.h;
 #pragma unroll
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
             const int jj = n * kBN + 32 * w + acc_row(v, h);
             if (jj < si.len_k && 32 * d + l32 < a.d) {
                 store_elem(dkg, (long long)jj * a.sdk.r + 32 * d + l32, dk[d][v] * a.scale);
-                store_elem(dvg, (long long)jj * a.sdv.r + 32 * d + l32, dv[d][v]);
+                store_elem(dvg, (long long)jj * a.sdv.r + 32 * d + l32, dv[d][v] * dv_scale);
             }
         }
     }
@@ -681,8 +699,12 @@ struct KvCfg {
 
 // All work of one key tile n of sequence b, kv-head hkv (the body of
 // bwd_kv_kernel).  ALIBI: ALiBi slopes; BIAS: an elementwise bias (and ALiBi
-// too when slopes are given) and, when dbias is set, its gradient dS.
-template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS>
+// too when slopes are given) and, when dbias is set, its gradient dS; DROP
+// (with BIAS): dropout of P as well.  Under dropout the P wave passes P to
+// its partner with the sign bit set on dropped elements (P >= 0 otherwise),
+// feeds the kept P to dV, and the dS wave forms P (dP / (1 - p) - D) on kept
+// and -P D on dropped elements.
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS, bool DROP>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n, const SeqInfo& si, char* smem) {
     static_assert(sizeof(T) == 2, "16-bit operand types");
     using C = KvCfg<HD>;
@@ -964,6 +986,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             wait_vmem_but<C::OPS * (C::PD - 1)>();
         __syncthreads();
         const int i0 = cur_m * BM;
+        const int g_t = cur_g;   // tile t's q-head within the group
         // ALiBi slope of tile t's q-head, negated, in log2 units
         float nsl2 = 0.f;
         if constexpr ((ALIBI || BIAS) && R == 0) {
@@ -1124,15 +1147,44 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                 softmax(std::true_type{});
             else
                 softmax(std::false_type{});
+            // dropout: bit 4 q + e of keep is element (rows r + e of 4 x 4 block
+            // q = 4 mb + q4, this lane's key j): byte j % 4 of word e
+            unsigned keep = 0xffffffffu;
+            if constexpr (DROP) {
+                keep = 0u;
+#pragma unroll
+                for (int q = 0; q < NMB * 4; ++q) {
+                    const u32x4 dw = drop_block((unsigned)(j >> 2), (unsigned)((i0 + 8 * q + 4 * h) >> 2),
+                                                (unsigned)(b * a.hq + hkv * G + g_t), a.drop.off, a.drop.k0,
+                                                a.drop.k1);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) keep |= (drop_keep(dw[e], j & 3, a.drop.thr) ? 1u : 0u) << (4 * q + e);
+                }
+            }
 #pragma unroll
             for (int c = 0; c < C::NIC; ++c) {
                 float tp[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tp[u] = xc[c >> 1][8 * (c & 1) + u];
-                to_op(opa[c], tp);
-                // P goes to the partner in the operand type it already has
-                // for P^T dO (half the LDS bytes of fp32)
-                lds_write(smem, ps + c * 1024, __builtin_bit_cast(u32x4, opa[c]));
+                if constexpr (DROP) {
+                    // element u of slice c: block q = 2c + u / 4, row e = u % 4
+                    float te[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const bool k = (keep >> (8 * c + u)) & 1u;
+                        te[u] = k ? tp[u] : -tp[u];
+                        tp[u] = k ? tp[u] : 0.f;
+                    }
+                    op_t enc;
+                    to_op(enc, te);
+                    to_op(opa[c], tp);
+                    lds_write(smem, ps + c * 1024, __builtin_bit_cast(u32x4, enc));
+                } else {
+                    to_op(opa[c], tp);
+                    // P goes to the partner in the operand type it already has
+                    // for P^T dO (half the LDS bytes of fp32)
+                    lds_write(smem, ps + c * 1024, __builtin_bit_cast(u32x4, opa[c]));
+                }
             }
         } else {
             // ---- dS = P (dP - D) with P from the partner wave (the value
@@ -1148,7 +1200,14 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * q4 + e;
-                        xp[mb][v] = pf[2 * mb + (v >> 3)][v & 7] * (xp[mb][v] - dl[e]);
+                        const float pv = pf[2 * mb + (v >> 3)][v & 7];
+                        if constexpr (DROP) {
+                            // sign bit set: dropped (P = -0 included)
+                            const bool kept = !__builtin_signbit(pv);
+                            xp[mb][v] = fabsf(pv) * ((kept ? a.drop.rp * xp[mb][v] : 0.f) - dl[e]);
+                        } else {
+                            xp[mb][v] = pv * (xp[mb][v] - dl[e]);
+                        }
                     }
                 }
             }
@@ -1305,7 +1364,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     // ---- epilogue: dV (P wave) or dK = s * sum dS^T Q (dS wave); rows past
     // the sequence are not written
     T* dst = reinterpret_cast<T*>(role == 0 ? a.dv : a.dk) + out_base;
-    const float f = role == 0 ? 1.f : a.scale;
+    const float f = role == 0 ? (DROP ? a.drop.rp : 1.f) : a.scale;
 #pragma unroll
     for (int d = 0; d < C::NDB; ++d) {
 #pragma unroll
@@ -1317,7 +1376,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS>
+template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[BIAS ? KvCfg<HD>::LDS_BYTES_BIAS : KvCfg<HD>::LDS_BYTES];
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
@@ -1348,10 +1407,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_kv_kernel(BwdArgs a) {
         const int cnt = (p <= n2) + (n2 > p);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
+            kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
-        kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS>(a, b, hkv, p, si, smem);
+        kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, p, si, smem);
     }
 }
 
@@ -1361,17 +1420,19 @@ int bwd_block_m(int dtype, int head_dim) {
     return dtype == ATTN_DTYPE_F32 ? BwdCfg<float, 64>::BM : BwdCfg<bf16_t, 64>::BM;
 }
 
-// the dK/dV kernel's instantiation for (mask, stored dS, ALiBi, bias): the
-// bias variant also applies ALiBi slopes when given
-template <class T, int HD, bool M, bool S, bool A, bool B>
+// the dK/dV kernel's instantiation for (mask, stored dS, ALiBi, bias,
+// dropout): the bias variant also applies ALiBi slopes when given, the
+// dropout variant a bias and ALiBi slopes when given
+template <class T, int HD, bool M, bool S, bool A, bool B, bool D>
 static void launch_kv3(const BwdArgs& a, unsigned grid, hipStream_t st) {
-    bwd_kv_kernel<T, HD, M, S, A, B><<<grid, kKvThreads, 0, st>>>(a);
+    bwd_kv_kernel<T, HD, M, S, A, B, D><<<grid, kKvThreads, 0, st>>>(a);
 }
 template <class T, int HD, bool M, bool S>
 static void launch_kv2(const BwdArgs& a, bool alibi, unsigned grid, hipStream_t st) {
-    if (a.bias != nullptr || a.dbias != nullptr) launch_kv3<T, HD, M, S, false, true>(a, grid, st);
-    else if (alibi) launch_kv3<T, HD, M, S, true, false>(a, grid, st);
-    else launch_kv3<T, HD, M, S, false, false>(a, grid, st);
+    if (a.drop.on) launch_kv3<T, HD, M, S, false, true, true>(a, grid, st);
+    else if (a.bias != nullptr || a.dbias != nullptr) launch_kv3<T, HD, M, S, false, true, false>(a, grid, st);
+    else if (alibi) launch_kv3<T, HD, M, S, true, false, false>(a, grid, st);
+    else launch_kv3<T, HD, M, S, false, false, false>(a, grid, st);
 }
 template <class T, int HD, bool M>
 static void launch_kv1(const BwdArgs& a, bool store_ds, bool alibi, unsigned grid, hipStream_t st) {

@@ -283,6 +283,45 @@ __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
 }
 
 // ---------------------------------------------------------------------------
+// dropout: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011).  Ten rounds on a 128-bit counter
+// under a 64-bit key; a round multiplies words 0 and 2 by two odd constants
+// into 64-bit products and mixes the halves with words 1 and 3 and the key,
+// which grows by two Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, unsigned k0, unsigned k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned long long p0 = (unsigned long long)0xD2511F53u * c[0];
+        const unsigned long long p1 = (unsigned long long)0xCD9E8D57u * c[2];
+        const u32x4 n = {(unsigned)(p1 >> 32) ^ c[1] ^ k0, (unsigned)p1, (unsigned)(p0 >> 32) ^ c[3] ^ k1,
+                         (unsigned)p0};
+        c = n;
+    }
+    return c;
+}
+
+// The random bytes of the 4 x 4 (row, key) block (4 i4 + r, 4 j4 + c) of the
+// (sequence, q-head) with index bh: byte c (least significant first) of word
+// r.  An element is kept iff its byte >= the threshold round(256 p).
+__device__ __forceinline__ u32x4 drop_block(unsigned j4, unsigned i4, unsigned bh, unsigned off, unsigned k0,
+                                            unsigned k1) {
+    const u32x4 c = {j4, i4, bh, off};
+    return philox4x32_10(c, k0, k1);
+}
+__device__ __forceinline__ bool drop_keep(unsigned word, int byte, unsigned thr) {
+    return ((word >> (8 * byte)) & 0xffu) >= thr;
+}
+// Word r (a run-time 0..3) of a generator output.
+__device__ __forceinline__ unsigned word_at(u32x4 w, int r) {
+    return r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+}
+
+// ---------------------------------------------------------------------------
 // problem geometry on the device
 // ---------------------------------------------------------------------------
 struct SeqInfo {

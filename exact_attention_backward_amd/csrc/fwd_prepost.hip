@@ -100,10 +100,20 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
             l *= corr;
 #pragma unroll
             for (int d = 0; d < HD; ++d) o[d] *= corr;
+            // dropout: this row's random word of each 4 x 4 block of the tile
+            unsigned dw[BK / 4];
+            if (a.drop.on) {
+#pragma unroll
+                for (int t = 0; t < BK / 4; ++t)
+                    dw[t] = word_at(drop_block((unsigned)(kt / 4 + t), (unsigned)(i >> 2), (unsigned)(b * a.hq + hq),
+                                               a.drop.off, a.drop.k0, a.drop.k1),
+                                    i & 3);
+            }
 #pragma unroll
             for (int jj = 0; jj < BK; ++jj) {
-                const float p = exp2f(s[jj] - mn);
-                l += p;
+                float p = exp2f(s[jj] - mn);
+                l += p;   // the sum (and LSE) over every visible key
+                if (a.drop.on && !drop_keep(dw[jj >> 2], jj & 3, a.drop.thr)) p = 0.f;
 #pragma unroll
                 for (int d = 0; d < HD; ++d) o[d] = fmaf(p, vs[jj][d], o[d]);
             }
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
         }
     }
     if (!row_ok) return;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? (a.drop.on ? a.drop.rp : 1.f) / l : 0.f;
     T* op = reinterpret_cast<T*>(a.o);
     const long long ob = seq_off(a.so, varlen, b, si.q0) + (long long)hq * a.so.h + (long long)i * a.so.r;
 #pragma unroll

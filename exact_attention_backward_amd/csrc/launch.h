@@ -26,6 +26,15 @@ __host__ __device__ __forceinline__ long long flat_row_off(const Strides& s, boo
     return b * s.b + (r - b * S) * s.r;
 }
 
+// Dropout of P (drop iff the element's random byte < thr; kept values are
+// scaled by rp = 1 / (1 - p)): the Philox4x32-10 key (k0, k1), the fourth
+// counter word, and on = 0 when there is no dropout.  See drop_block.
+struct Dropout {
+    int on;
+    unsigned thr, k0, k1, off;
+    float rp;
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -44,6 +53,7 @@ struct FwdArgs {
     Strides sq, sk, sv, so;
     const void* bias;        // elementwise bias [b, h, i, j] (I/O type), or null
     Strides sbias;           // its batch, row and head strides (columns contiguous)
+    Dropout drop;
 };
 
 struct PreArgs {
@@ -109,11 +119,12 @@ struct BwdArgs {
     int d;               // head dim (the kernels' HD is this rounded up to 64 or 128;
                          // columns from d on are zero in every tile)
     Strides sq, sk, sv, sdo, sdq, sdk, sdv;
-    // elementwise bias [b, h, i, j] added to the logits and its gradient dS
-    // (atomic dQ mode), or null; batch, row and head strides
+    // elementwise bias [b, h, i, j] added to the logits and its gradient dS,
+    // or null; batch, row and head strides
     const void* bias;
     void* dbias;
     Strides sbias, sdbias;
+    Dropout drop;
     int nblk_n;          // key tiles per sequence (of the longest sequence)
     int nblk_m;          // query tiles per sequence (of the longest sequence)
     float scale;

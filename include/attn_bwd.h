@@ -2,7 +2,7 @@
  * attn_bwd.h -- C ABI of the MI355X (gfx950) exact-attention backward library.
  *
  * The library computes the gradient of exact softmax attention,
- *     O = softmax(s * Q K^T [+ ALiBi] [+ bias] [+ causal / local mask]) V,
+ *     O = dropout(softmax(s * Q K^T [+ ALiBi] [+ bias] [+ causal / local mask])) V,
  * i.e. dQ, dK and dV from Q, K, V, O, dO and the per-row log-sum-exp LSE,
  * as a fused, tiled pass that recomputes the probabilities from LSE instead
  * of storing them.  The operation and its stages are those of the
@@ -67,16 +67,33 @@
  *    position encoding per (row, column) after the scale without its formula;
  *    this linear bias is the reading taken.  attn_fwd's LSE includes it and
  *    attn_bwd must get the same slopes.
- *  - Elementwise bias (ATTN_DQ_ATOMIC only; other modes return
- *    ATTN_ERR_UNSUPPORTED): with bias non-NULL the logit of query i, key j
- *    under q-head h of sequence b gets + bias[b * batch + h * head + i * row
- *    + j] (bias_strides, in elements; 0 broadcasts; keys contiguous), in
- *    natural-log units, in attn_fwd and attn_bwd alike.  With dbias non-NULL,
- *    attn_bwd / attn_bwd_full write dBias = dS (the gradient of the logit,
- *    rounded to the I/O type, as the composable-kernel pipeline's dBias
- *    tile) at the same positions with dbias_strides: every (i, j) of each
- *    sequence's len_q x len_k block of every q-head, zero where masked.
- *    dbias must not overlap other tensors or itself.
+ *  - Elementwise bias (every dQ mode): with bias non-NULL the logit of
+ *    query i, key j under q-head h of sequence b gets + bias[b * batch + h *
+ *    head + i * row + j] (bias_strides, in elements; 0 broadcasts; keys
+ *    contiguous), in natural-log units, in attn_fwd and attn_bwd alike.
+ *    Outside ATTN_DQ_ATOMIC the kernels copy the bias in 16-byte chunks: its
+ *    base and batch, head and row steps must be 16-byte aligned
+ *    (ATTN_ERR_MISALIGNED otherwise).  With dbias non-NULL, attn_bwd /
+ *    attn_bwd_full write dBias = dS (the gradient of the logit, rounded to
+ *    the I/O type, as the composable-kernel pipeline's dBias tile) at the
+ *    same positions with dbias_strides: every (i, j) of each sequence's
+ *    len_q x len_k block of every q-head, zero where masked.  dbias must not
+ *    overlap other tensors or itself.
+ *  - Dropout (dropout_p > 0): the composable-kernel pipeline page drops
+ *    elements of P after the softmax and rescales the kept ones by
+ *    rp_undrop = 1 / (1 - p) ("Dropout" in its stage 2; dV, dK, dQ and dBias
+ *    scaled by rp_undrop).  P and the LSE are those without dropout; O =
+ *    (Z P / (1 - p)) V, and the backward gives dV = (Z P)^T dO / (1 - p),
+ *    dS = P (Z dO V^T / (1 - p) - D), D = rowsum(dO * O).  The pages name no
+ *    generator; Z comes from Philox4x32-10 (Salmon et al., SC 2011): one
+ *    call per 4 x 4 block of (row, key) positions of a (sequence, q-head),
+ *    counter = (key / 4, row / 4, sequence * Hq + q-head, dropout_offset),
+ *    key = (low, high 32 bits of dropout_seed); element (row, key) takes
+ *    byte key % 4 (least significant first) of output word row % 4 and is
+ *    kept iff that byte >= round(256 p) (so p acts rounded to a multiple of
+ *    1/256; the rescale uses p as given).  Rows and keys are positions
+ *    within the sequence.  attn_fwd and attn_bwd must get the same p, seed
+ *    and offset; callers advance dropout_offset (or the seed) per step.
  *  - GQA: Hq must be a multiple of Hkv; q-head h uses kv-head h / (Hq / Hkv)
  *    (contiguous groups).  dK and dV of a kv-head are the sums over its
  *    q-heads.
@@ -103,10 +120,10 @@ typedef enum attn_status {
                                   cu_seqlens, workspace too small, more than 2^27
                                   (row, head) pairs in Q or K, a negative stride,
                                   about 2 GiB or more of one sequence's rows of a
-                                  tensor (seqlen x row stride), ... */
+                                  tensor (seqlen x row stride), dropout_p outside
+                                  [0, 1), ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not a multiple of 8 in
-                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32,
-                                  bias or dbias without ATTN_DQ_ATOMIC */
+                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer or stride is not 16-byte aligned
                                   (cu_seqlens, seqused and alibi_slopes: 4-byte) */
     ATTN_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
@@ -202,6 +219,9 @@ typedef struct attn_shape {
     const int32_t* cu_seqlens_q_host;  /* varlen, optional: HOST copies of cu_seqlens_q/_k, read */
     const int32_t* cu_seqlens_k_host;  /* during each call; with both (and no seqused) the
                                           stored-dS workspace is sized exactly from them */
+    uint64_t dropout_seed;   /* dropout: the generator key (see the conventions above) */
+    float dropout_p;         /* drop probability in [0, 1); 0 = no dropout */
+    uint32_t dropout_offset; /* dropout: the generator's fourth counter word */
 } attn_shape_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -284,6 +284,16 @@ def test_bias_alignment_and_range_by_dq_mode():
     assert ws_bytes(s) == 0
 
 
+def test_dropout_probability_validated():
+    base = ws_bytes(shape())
+    for p_drop, ok in ((0.0, True), (0.5, True), (0.999, True), (1.0, False), (-0.1, False), (float("nan"), False)):
+        s = shape(dropout_p=p_drop, dropout_seed=(1 << 63) + 5, dropout_offset=7)
+        assert (ws_bytes(s) == base) == ok, p_drop
+    fake = ctypes.c_void_p(0x1000)
+    s = shape(dropout_p=1.5)
+    assert L.lib().attn_fwd(ctypes.byref(s), fake, fake, fake, fake, fake, None) == L.ATTN_ERR_BAD_SHAPE
+
+
 def test_shape_struct_layout_matches_header(tmp_path):
     """The ctypes mirror of attn_shape_t has the C layout (compiled from the header)."""
     import shutil
