@@ -101,6 +101,9 @@ WORKLOADS = {
                   name="c5_bf16_gqa_causal"),
     "c3h": Problem("f16", 4, 16, 16, 4096, 4096, 128, True, 1 / math.sqrt(128), 3, do_scale=0.1,
                    name="c3_f16_causal"),
+    # head dim 256 at the headline's FLOPs (half the heads)
+    "c3w": Problem("bf16", 4, 8, 8, 4096, 4096, 256, True, 1 / 16, 3, do_scale=0.1,
+                   name="c3_bf16_causal_d256"),
 }
 
 

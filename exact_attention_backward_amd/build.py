@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattnbwd.so")
-SOURCES = ["abi.hip", "fwd_prepost.hip", "bwd_main.hip", "bwd_dq.hip", "bwd_dq_gemm.hip"]
+SOURCES = ["abi.hip", "fwd_prepost.hip", "bwd_main.hip", "bwd_kv_wide.hip", "bwd_dq.hip", "bwd_dq_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

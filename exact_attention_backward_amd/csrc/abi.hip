@@ -38,7 +38,8 @@ int validate_shape(const attn_shape_t* s) {
     if (s == nullptr) return ATTN_ERR_NULL_ARG;
     if (s->dtype != ATTN_DTYPE_F32 && s->dtype != ATTN_DTYPE_BF16 && s->dtype != ATTN_DTYPE_F16)
         return ATTN_ERR_UNSUPPORTED;
-    if (s->head_dim < 8 || s->head_dim > 128 || s->head_dim % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (s->head_dim < 8 || s->head_dim > 256 || s->head_dim % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (s->head_dim > 128 && s->dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
     if (s->batch <= 0 || s->num_heads_q <= 0 || s->num_heads_kv <= 0 || s->seqlen_q <= 0 || s->seqlen_k <= 0)
         return ATTN_ERR_BAD_SHAPE;
     if (s->num_heads_q % s->num_heads_kv != 0) return ATTN_ERR_BAD_SHAPE;
@@ -95,6 +96,13 @@ int validate_shape(const attn_shape_t* s) {
     return ATTN_OK;
 }
 
+// The dQ mode the kernels run: above head dim 128 the atomic mode runs as
+// the separate one (the key-stationary kernel that adds dQ with atomics keeps
+// a K/V tile per wave in registers, which does not fit at 256).
+int algo_of(const attn_shape_t* s) {
+    return s->dq_algo == ATTN_DQ_ATOMIC && s->head_dim > 128 ? ATTN_DQ_SEPARATE : s->dq_algo;
+}
+
 // the backward entry points: outside the atomic dQ mode the kernels copy
 // the bias in 16-byte chunks (rows, batch and head steps and the base
 // 16-byte aligned) and address a tile of up to 64 bias or dBias rows with
@@ -102,7 +110,7 @@ int validate_shape(const attn_shape_t* s) {
 int validate_bwd(const attn_shape_t* s) {
     const int st = validate_shape(s);
     if (st) return st;
-    if (s->dq_algo != ATTN_DQ_ATOMIC) {
+    if (algo_of(s) != ATTN_DQ_ATOMIC) {
         const long long esz = s->dtype == ATTN_DTYPE_F32 ? 4 : 2;
         if (s->bias != nullptr) {
             const attn_tensor_strides_t& b = s->bias_strides;
@@ -137,8 +145,8 @@ Dropout dropout_args(const attn_shape_t* s) {
     return d;
 }
 
-// the head dim the kernels tile with: head_dim rounded up to 64 or 128
-int padded_hd(const attn_shape_t* s) { return s->head_dim <= 64 ? 64 : 128; }
+// the head dim the kernels tile with: head_dim rounded up to 64, 128 or 256
+int padded_hd(const attn_shape_t* s) { return s->head_dim <= 64 ? 64 : s->head_dim <= 128 ? 128 : 256; }
 
 Strides to_kernel(const attn_tensor_strides_t& t) { return Strides{t.batch, t.row, t.head}; }
 
@@ -220,8 +228,8 @@ struct Plan {
 };
 size_t base_bytes(const attn_shape_t* s, int algo, bool with_accum);
 Plan plan(const attn_shape_t* s) {
-    Plan p{s->dq_algo, s->num_heads_kv, 0};
-    if (s->dq_algo != ATTN_DQ_STORED_DS) return p;
+    Plan p{algo_of(s), s->num_heads_kv, 0};
+    if (p.algo != ATTN_DQ_STORED_DS) return p;
     p.head_blocks = ds_head_blocks(s);
     // block indices are int32 in the table (a q-head's dS past 2^31 blocks,
     // 16 TiB, could not be allocated anyway): the separate mode instead
@@ -343,9 +351,9 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.bias = s->bias;
     a.sbias = to_kernel(s->bias_strides);
     a.drop = dropout_args(s);
-    // the MFMA forward for the 16-bit types; fp32, the elementwise bias and
-    // dropout take the plain one
-    if (s->dtype != ATTN_DTYPE_F32 && s->bias == nullptr && !a.drop.on)
+    // the MFMA forward for the 16-bit types up to head dim 128; fp32, the
+    // elementwise bias, dropout and wider heads take the plain one
+    if (s->dtype != ATTN_DTYPE_F32 && s->bias == nullptr && !a.drop.on && padded_hd(s) <= 128)
         launch_fwd_mfma(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     else
         launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));

@@ -37,12 +37,17 @@ template <class T, int HD>
 struct DqCfg {
     static constexpr int BQ = 32 * kWaves;   // query rows per workgroup
     static constexpr int BN = 32;            // keys per K/V tile
-    static constexpr int NS = sizeof(T) == 2 ? 4 : 2;   // K/V tiles in flight (LDS ring)
+    // K/V tiles in the LDS ring (the copies of NS - 2 later tiles stay in
+    // flight while one is consumed; at head dim 256 a tile's copies are
+    // twice as many and the ring is three deep)
+    static constexpr int NS = sizeof(T) == 2 ? (HD <= 128 ? 4 : 3) : 2;
     static constexpr int ROWB = HD * (int)sizeof(T);
     static constexpr int TILE = BN * ROWB;
     static constexpr int BUF_K = 0, BUF_V = TILE;
     static constexpr int BUF_BYTES = 2 * TILE;
     static constexpr int LDS_BYTES = NS * BUF_BYTES;
+    // workgroups per CU: two for the 16-bit types up to head dim 128, else one
+    static constexpr int WG_PER_CU = sizeof(T) == 2 && HD <= 128 ? 2 : 1;
     // elementwise bias: each wave's [32 rows][BN keys] block, two buffers
     // (tile parity), copied one tile ahead
     static constexpr int BIAS_W = 32 * BN * (int)sizeof(T);
@@ -50,7 +55,7 @@ struct DqCfg {
     static constexpr int BOPS = BIAS_W / 1024;       // copies per wave and tile
     static constexpr int OFF_BIAS = LDS_BYTES;
     static constexpr int LDS_BYTES_BIAS = OFF_BIAS + 2 * kWaves * BIAS_W;
-    static_assert(LDS_BYTES_BIAS <= (sizeof(T) == 2 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU for 16-bit types)");
+    static_assert(LDS_BYTES_BIAS <= 160 * 1024 / WG_PER_CU, "LDS budget");
     static constexpr int NC = HD / 16;       // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;      // 32-column blocks of the head dim
     static constexpr int NJB = BN / 32;      // 32-key blocks of a K tile
@@ -423,7 +428,7 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
 
 
 template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[BIAS ? DqCfg<T, HD>::LDS_BYTES_BIAS : DqCfg<T, HD>::LDS_BYTES];
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
     // kv-head) run on one XCD, so their K/V reads share an L2.  Under a causal
@@ -737,11 +742,13 @@ void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream
 void launch_bwd_dq(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_dq_t<bf16_t, 64>(a, masked, st);
-        else launch_dq_t<bf16_t, 128>(a, masked, st);
+        else if (hd == 128) launch_dq_t<bf16_t, 128>(a, masked, st);
+        else launch_dq_t<bf16_t, 256>(a, masked, st);
     } else if (dtype == ATTN_DTYPE_F16) {
         if (hd == 64) launch_dq_t<f16_t, 64>(a, masked, st);
-        else launch_dq_t<f16_t, 128>(a, masked, st);
-    } else {
+        else if (hd == 128) launch_dq_t<f16_t, 128>(a, masked, st);
+        else launch_dq_t<f16_t, 256>(a, masked, st);
+    } else {   // fp32: head dims up to 128
         if (hd == 64) launch_dq_t<float, 64>(a, masked, st);
         else launch_dq_t<float, 128>(a, masked, st);
     }

@@ -22,24 +22,25 @@ namespace {
 constexpr int kGWaves = 4;
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int kGXcds = 8;
-constexpr int kGRB = 2;   // 32-row dS blocks per wave
-
 template <int HD>
 struct DqgCfg {
-    static constexpr int BQ = kGWaves * kGRB * kDsRows;   // query rows per workgroup
+    // 32-row dS blocks per wave: two (their fp32 dQ rows are 2 x HD / 2
+    // registers per lane) up to head dim 128, one at 256
+    static constexpr int RB = HD <= 128 ? 2 : 1;
+    static constexpr int BQ = kGWaves * RB * kDsRows;   // query rows per workgroup
     static constexpr int BN = kDsKeys;              // keys per dS block
     static constexpr int BS = 32;                   // keys per pipeline stage
     static constexpr int SPB = BN / BS;             // stages per dS block
     static constexpr int ROWB = HD * 2;
     static constexpr int K_BYTES = BS * ROWB;
     static constexpr int DS_PART = kDsBlockBytes / SPB;   // one block's part per stage
-    static constexpr int STAGE = K_BYTES + kGWaves * kGRB * DS_PART;
+    static constexpr int STAGE = K_BYTES + kGWaves * RB * DS_PART;
     static constexpr int NS = 3;                    // ring of stages
     static constexpr int PD = NS - 1;               // stages in flight ahead
     static constexpr int LDS_BYTES = NS * STAGE;
     static constexpr int NDB = HD / 32;
     static constexpr int KOPS = BS * (ROWB / 16) / 64 / kGWaves;   // K copy instructions per wave and stage
-    static constexpr int OPS = KOPS + kGRB * DS_PART / 1024;        // copy instructions per wave and stage
+    static constexpr int OPS = KOPS + RB * DS_PART / 1024;          // copy instructions per wave and stage
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(BS * (ROWB / 16) % (64 * kGWaves) == 0, "K tile split");
     static_assert(OPS * (PD - 1) < 64, "vmcnt range");
@@ -73,6 +74,7 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
                                           char* smem) {
     using C = DqgCfg<HD>;
     constexpr int BQ = C::BQ, BN = C::BN;
+    constexpr int kGRB = C::RB;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;
@@ -117,8 +119,12 @@ __device__ __forceinline__ void gemm_tile(int m, const BwdArgs& a, int b, int hq
         n_last_b[r] = last_block(lq0 + r);
         n_first_b[r] = n_last_b[r] < 0 ? nblk_k : first_block(lq0 + r);
     }
-    const int n_first_w = min(n_first_b[0], n_first_b[kGRB - 1]);
-    const int n_last_w = max(n_last_b[0], n_last_b[kGRB - 1]);
+    int n_first_w = n_first_b[0], n_last_w = n_last_b[0];
+#pragma unroll
+    for (int r = 1; r < kGRB; ++r) {
+        n_first_w = min(n_first_w, n_first_b[r]);
+        n_last_w = max(n_last_w, n_last_b[r]);
+    }
     // the workgroup's key blocks: n_first .. n_last over its blocks with rows
     int n_first = nblk_k, n_last = -1;
     for (int lq = m * (BQ / kDsRows); lq < (m + 1) * (BQ / kDsRows); ++lq) {
@@ -327,19 +333,19 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     }
 }
 
-template <class T>
-static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool masked, hipStream_t st) {
-    const int nblk_q = (a.seqlen_q + DqgCfg<128>::BQ - 1) / DqgCfg<128>::BQ;
-    static_assert(DqgCfg<128>::BQ == DqgCfg<64>::BQ, "one query tiling");
+template <class T, int HD>
+static void launch_dq_gemm_hd(const BwdArgs& a, bool masked, hipStream_t st) {
+    const int nblk_q = (a.seqlen_q + DqgCfg<HD>::BQ - 1) / DqgCfg<HD>::BQ;
     const int n_pair = masked ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
     const unsigned grid = (unsigned)(n_pair * (a.hq / a.hkv) * a.hkv_n * a.batch);
-    if (hd == 64) {
-        if (masked) bwd_dq_gemm_kernel<T, 64, true><<<grid, kGThreads, 0, st>>>(a);
-        else bwd_dq_gemm_kernel<T, 64, false><<<grid, kGThreads, 0, st>>>(a);
-    } else {
-        if (masked) bwd_dq_gemm_kernel<T, 128, true><<<grid, kGThreads, 0, st>>>(a);
-        else bwd_dq_gemm_kernel<T, 128, false><<<grid, kGThreads, 0, st>>>(a);
-    }
+    if (masked) bwd_dq_gemm_kernel<T, HD, true><<<grid, kGThreads, 0, st>>>(a);
+    else bwd_dq_gemm_kernel<T, HD, false><<<grid, kGThreads, 0, st>>>(a);
+}
+template <class T>
+static void launch_dq_gemm_t(const BwdArgs& a, int hd, bool masked, hipStream_t st) {
+    if (hd == 64) launch_dq_gemm_hd<T, 64>(a, masked, st);
+    else if (hd == 128) launch_dq_gemm_hd<T, 128>(a, masked, st);
+    else launch_dq_gemm_hd<T, 256>(a, masked, st);
 }
 
 void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {

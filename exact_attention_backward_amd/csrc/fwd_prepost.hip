@@ -22,19 +22,26 @@ __device__ __forceinline__ long long lse_index(bool varlen, long long r, int h, 
 }
 
 // ---------------------------------------------------------------------------
-// forward: one thread per query row, K/V tiles of 32 keys staged in LDS,
-// online softmax in base 2.  Not performance-tracked.
+// forward: one thread per query row (two above head dim 128, each holding
+// half the row's columns and adding the other's dot-product half by a
+// shuffle), K/V tiles of 32 keys staged in LDS, online softmax in base 2.
+// Not performance-tracked.
 // ---------------------------------------------------------------------------
+template <int HD>
+constexpr int fwd_threads_per_row() { return HD > 128 ? 2 : 1; }
+
 template <class T, int HD, bool MASKED>
-__global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(128 * fwd_threads_per_row<HD>()) void fwd_kernel(FwdArgs a) {
     constexpr int BQ = 128, BK = 32;
+    constexpr int TPR = fwd_threads_per_row<HD>(), HDT = HD / TPR;   // threads per row, columns per thread
     __shared__ float ks[BK][HD];
     __shared__ float vs[BK][HD];
     const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (qb * BQ >= si.len_q) return;
     const int hkv = hq / (a.hq / a.hkv);
-    const int i = qb * BQ + threadIdx.x;
+    const int part = (int)threadIdx.x % TPR, c0 = part * HDT;   // this thread's columns c0 .. c0 + HDT - 1
+    const int i = qb * BQ + (int)threadIdx.x / TPR;
     const bool row_ok = i < si.len_q;
     const int off = si.len_k - si.len_q;
     const bool varlen = a.cu_q != nullptr;
@@ -46,11 +53,11 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     const long long vbase = seq_off(a.sv, varlen, b, si.k0) + (long long)hkv * a.sv.h;
 
     // columns from a.d on are zero (the head dim padded to HD)
-    float q[HD], o[HD];
+    float q[HDT], o[HDT];
     const float qs = a.scale * kLog2e;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) {
-        q[d] = row_ok && d < a.d ? (float)load_elem(qp, qrow + d) * qs : 0.f;
+    for (int d = 0; d < HDT; ++d) {
+        q[d] = row_ok && c0 + d < a.d ? (float)load_elem(qp, qrow + c0 + d) * qs : 0.f;
         o[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -88,7 +95,8 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
             const bool vis = row_ok && j < si.len_k && (!MASKED || (dj <= whi && dj >= -wlo));
             float acc = 0.f;
 #pragma unroll
-            for (int d = 0; d < HD; ++d) acc = fmaf(q[d], ks[jj][d], acc);
+            for (int d = 0; d < HDT; ++d) acc = fmaf(q[d], ks[jj][c0 + d], acc);
+            if constexpr (TPR == 2) acc += __shfl_xor(acc, 1);   // the row's other half
             float x = acc - sl2 * fabsf((float)dj);
             if (brow != nullptr && vis) x = fmaf((float)load_elem(brow, j), kLog2e, x);
             s[jj] = vis ? x : -INFINITY;
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
             const float corr = exp2f(m - mn);
             l *= corr;
 #pragma unroll
-            for (int d = 0; d < HD; ++d) o[d] *= corr;
+            for (int d = 0; d < HDT; ++d) o[d] *= corr;
             // dropout: this row's random word of each 4 x 4 block of the tile
             unsigned dw[BK / 4];
             if (a.drop.on) {
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
                 l += p;   // the sum (and LSE) over every visible key
                 if (a.drop.on && !drop_keep(dw[jj >> 2], jj & 3, a.drop.thr)) p = 0.f;
 #pragma unroll
-                for (int d = 0; d < HD; ++d) o[d] = fmaf(p, vs[jj][d], o[d]);
+                for (int d = 0; d < HDT; ++d) o[d] = fmaf(p, vs[jj][c0 + d], o[d]);
             }
             m = mn;
         }
@@ -125,12 +133,12 @@ __global__ __launch_bounds__(128) void fwd_kernel(FwdArgs a) {
     T* op = reinterpret_cast<T*>(a.o);
     const long long ob = seq_off(a.so, varlen, b, si.q0) + (long long)hq * a.so.h + (long long)i * a.so.r;
 #pragma unroll
-    for (int d = 0; d < HD; ++d) {
-        if (d < a.d) store_elem(op, ob + d, o[d] * inv);
+    for (int d = 0; d < HDT; ++d) {
+        if (c0 + d < a.d) store_elem(op, ob + c0 + d, o[d] * inv);
     }
     const long long li = varlen ? (long long)hq * a.total_q + si.q0 + i
                                 : ((long long)b * a.hq + hq) * a.seqlen_q + i;
-    a.lse[li] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    if (part == 0) a.lse[li] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -314,20 +322,23 @@ __global__ __launch_bounds__(256) void postprocess_kernel(PostArgs a) {
 template <class T, int HD>
 static void launch_fwd_t(const FwdArgs& a, bool masked, hipStream_t st) {
     dim3 grid((a.seqlen_q + 127) / 128, a.hq, a.batch);
+    constexpr int threads = 128 * fwd_threads_per_row<HD>();
     if (masked)
-        fwd_kernel<T, HD, true><<<grid, 128, 0, st>>>(a);
+        fwd_kernel<T, HD, true><<<grid, threads, 0, st>>>(a);
     else
-        fwd_kernel<T, HD, false><<<grid, 128, 0, st>>>(a);
+        fwd_kernel<T, HD, false><<<grid, threads, 0, st>>>(a);
 }
 
 void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_fwd_t<bf16_t, 64>(a, masked, st);
-        else launch_fwd_t<bf16_t, 128>(a, masked, st);
+        else if (hd == 128) launch_fwd_t<bf16_t, 128>(a, masked, st);
+        else launch_fwd_t<bf16_t, 256>(a, masked, st);
     } else if (dtype == ATTN_DTYPE_F16) {
         if (hd == 64) launch_fwd_t<f16_t, 64>(a, masked, st);
-        else launch_fwd_t<f16_t, 128>(a, masked, st);
-    } else {
+        else if (hd == 128) launch_fwd_t<f16_t, 128>(a, masked, st);
+        else launch_fwd_t<f16_t, 256>(a, masked, st);
+    } else {   // fp32: head dims up to 128
         if (hd == 64) launch_fwd_t<float, 64>(a, masked, st);
         else launch_fwd_t<float, 128>(a, masked, st);
     }
@@ -352,7 +363,8 @@ void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table
     };
     auto by_hd = [&](auto tc, auto table_c) {
         if (hd == 64) go(tc, std::integral_constant<int, 64>{}, table_c);
-        else go(tc, std::integral_constant<int, 128>{}, table_c);
+        else if (hd == 128 || sizeof(decltype(tc)) == 4) go(tc, std::integral_constant<int, 128>{}, table_c);
+        else go(tc, std::integral_constant<int, 256>{}, table_c);
     };
     auto by_table = [&](auto tc) {
         if (table) by_hd(tc, std::true_type{});
@@ -368,10 +380,12 @@ void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st) {
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) postprocess_kernel<bf16_t, 64><<<blocks, 256, 0, st>>>(a);
-        else postprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+        else if (hd == 128) postprocess_kernel<bf16_t, 128><<<blocks, 256, 0, st>>>(a);
+        else postprocess_kernel<bf16_t, 256><<<blocks, 256, 0, st>>>(a);
     } else if (dtype == ATTN_DTYPE_F16) {
         if (hd == 64) postprocess_kernel<f16_t, 64><<<blocks, 256, 0, st>>>(a);
-        else postprocess_kernel<f16_t, 128><<<blocks, 256, 0, st>>>(a);
+        else if (hd == 128) postprocess_kernel<f16_t, 128><<<blocks, 256, 0, st>>>(a);
+        else postprocess_kernel<f16_t, 256><<<blocks, 256, 0, st>>>(a);
     } else {
         if (hd == 64) postprocess_kernel<float, 64><<<blocks, 256, 0, st>>>(a);
         else postprocess_kernel<float, 128><<<blocks, 256, 0, st>>>(a);

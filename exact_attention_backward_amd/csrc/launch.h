@@ -159,7 +159,7 @@ constexpr int kDsBlockBytes = kDsRows * kDsKeys * 2;
 __host__ __device__ constexpr int ds_chunk(int g, int l) { return g * 64 + (l ^ ((l >> 5) << 2)); }
 
 // Query rows per tile of the stored-dS dK/dV kernel (kDsRows-row blocks each).
-__host__ __device__ constexpr int kv_block_m(int hd) { return hd == 128 ? 32 : 64; }
+__host__ __device__ constexpr int kv_block_m(int hd) { return hd >= 128 ? 32 : 64; }
 
 // The key tiles (kDsKeys keys each) whose dS the key-stationary kernel stores
 // for query tile m (bm rows) of a sequence with len_q query and len_k key
@@ -219,6 +219,8 @@ void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table
                        hipStream_t st);
 void launch_postprocess(const PostArgs& a, int dtype, int hd, hipStream_t st);
 void launch_bwd(const BwdArgs& a, int dtype, int hd, bool masked, int dq_algo, hipStream_t st);
+// dK/dV kernel for head dims above 128 (16-bit types, separate or stored-dS dQ)
+void launch_bwd_kv_wide(const BwdArgs& a, int dtype, bool masked, bool store_ds, hipStream_t st);
 // stored-dS mode: dQ = dS K from the stored blocks (16-bit types), and the
 // per-sequence block table of varlen problems
 void launch_bwd_dq_gemm(const BwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);

@@ -151,7 +151,8 @@ def test_workspace_cap_chunks_kv_heads_or_falls_back():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=100), L.ATTN_ERR_UNSUPPORTED),
-    (dict(head_dim=136), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=264), L.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim=136, dtype=L.ATTN_DTYPE_F32), L.ATTN_ERR_UNSUPPORTED),   # fp32: up to 128
     (dict(head_dim=0), L.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), L.ATTN_ERR_UNSUPPORTED),
     (dict(num_heads_kv=3), L.ATTN_ERR_BAD_SHAPE),
@@ -189,10 +190,15 @@ def test_seqused_needs_varlen_and_alignment():
 
 
 def test_head_dims_accepted_and_workspace_padded():
-    """Any multiple of 8 up to 128; the accumulator is sized for the padded
-    head dim (64 or 128)."""
-    for d, pad in ((8, 64), (40, 64), (64, 64), (72, 128), (96, 128), (128, 128)):
+    """Any multiple of 8 up to 256 (fp32: 128); the accumulator is sized for
+    the padded head dim (64, 128 or 256); above 128 the atomic mode runs (and
+    is sized) as the separate one."""
+    for d, pad in ((8, 64), (40, 64), (64, 64), (72, 128), (96, 128), (128, 128), (136, 256), (200, 256),
+                   (256, 256)):
         assert ws_bytes(shape(head_dim=d)) == ws_bytes(shape(head_dim=pad))
+    assert ws_bytes(shape(head_dim=256)) > ws_bytes(shape(head_dim=128))
+    for d in (136, 256):
+        assert ws_bytes(shape(head_dim=d, dq_algo=L.ATTN_DQ_ATOMIC)) == ws_bytes(shape(head_dim=d))
 
 
 def _strides(**over):

@@ -25,6 +25,7 @@ DROP_CASES = [
     ("f32", 1, 4, 2, 97, 96, 128, False, None, None, 0.4, True),
     ("bf16", 0, 4, 2, 0, 0, 128, True, (1, 64, 300), None, 0.15, False),   # varlen + GQA
     ("f16", 0, 2, 2, 0, 0, 64, False, (7, 129, 40), None, 0.35, True),    # varlen + bias
+    ("bf16", 1, 4, 2, 200, 200, 256, True, None, (90, 10), 0.2, True),    # head dim 256, window, bias
 ]
 
 

@@ -256,6 +256,7 @@ ALIBI_CASES = [
     ("f16", 1, 6, 2, 200, 333, 64, False, None, None),
     ("f32", 1, 2, 2, 150, 200, 64, True, None, None),
     ("f32", 0, 2, 2, 0, 0, 128, False, (5, 170, 33), None),
+    ("bf16", 1, 4, 2, 200, 260, 256, True, None, (64, -1)),   # head dim 256 with a window
 ]
 
 
@@ -379,8 +380,15 @@ def test_bwd_full_matches_three_calls_bitwise(fc, dq_algo):
         assert_close(n, to_host(g), ref, p.dtype)
 
 
-# head dims other than 64 and 128 (padded with zeros to 64 or 128 inside the kernels)
+# head dims other than 64 and 128 (padded with zeros to 64, 128 or 256 inside
+# the kernels); above 128 the dK/dV kernel runs with four waves and 64 keys
+# per workgroup and the atomic mode runs as the separate one
 HEADDIM_CASES = [
+    ("bf16", 1, 2, 2, 200, 200, 256, True, None),
+    ("bf16", 1, 4, 2, 150, 260, 192, False, None),   # GQA, Sq < Sk
+    ("f16", 2, 2, 2, 130, 130, 136, True, None),
+    ("bf16", 0, 4, 2, 0, 0, 256, True, (7, 128, 129, 300)),   # varlen + GQA
+    ("f16", 1, 2, 2, 300, 170, 248, True, None),     # Sq > Sk: rows that see no key
     ("bf16", 1, 2, 2, 200, 200, 8, True, None),
     ("bf16", 1, 3, 3, 150, 260, 40, False, None),
     ("bf16", 2, 4, 2, 130, 130, 72, True, None),     # GQA
