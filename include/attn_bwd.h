@@ -123,7 +123,8 @@ typedef enum attn_status {
                                   tensor (seqlen x row stride), dropout_p outside
                                   [0, 1), ... */
     ATTN_ERR_UNSUPPORTED = 3,  /* dtype not F32/BF16/F16, head_dim not a multiple of 8 in
-                                  [8, 128], unknown dq_algo, ATTN_DQ_STORED_DS with F32 */
+                                  [8, 256] ([8, 128] for F32), unknown dq_algo,
+                                  ATTN_DQ_STORED_DS with F32 */
     ATTN_ERR_MISALIGNED = 4,   /* a tensor pointer or stride is not 16-byte aligned
                                   (cu_seqlens, seqused and alibi_slopes: 4-byte) */
     ATTN_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
@@ -150,7 +151,8 @@ typedef enum attn_dtype {
  *    reproducible; seven contractions per tile pair instead of five.
  *  ATTN_DQ_ATOMIC: the key-stationary kernel adds dS K for each tile pair
  *    into the fp32 accumulator with global atomics (with deterministic = 1,
- *    in a fixed order per dQ tile).
+ *    in a fixed order per dQ tile); head dims up to 128 (wider heads run as
+ *    ATTN_DQ_SEPARATE).
  *  ATTN_DQ_STORED_DS (bf16 and fp16): the key-stationary kernel stores dS
  *    in the 16-bit I/O type (the operand type the pages' dQ = dS K product
  *    uses) in the workspace; a second pass forms dQ = dS K from it and writes every
@@ -187,8 +189,11 @@ typedef struct attn_shape {
     int32_t num_heads_kv;    /* Hkv, divides Hq */
     int32_t seqlen_q;        /* dense Sq, or the longest query sequence when varlen */
     int32_t seqlen_k;        /* dense Sk, or the longest key sequence when varlen */
-    int32_t head_dim;        /* D: a multiple of 8, 8..128 (the kernels pad it with zeros
-                                to 64 or 128 and compute at that size) */
+    int32_t head_dim;        /* D: a multiple of 8, 8..256 (F32: ..128); the kernels pad it
+                                with zeros to 64, 128 or 256 and compute at that size.
+                                Above 128 ATTN_DQ_ATOMIC runs as ATTN_DQ_SEPARATE (the
+                                atomic kernel keeps a K/V tile per wave in registers,
+                                which does not fit at 256) */
     int32_t total_q;         /* varlen only: rows of Q (= cu_seqlens_q[batch]) */
     int32_t total_k;         /* varlen only: rows of K (= cu_seqlens_k[batch]) */
     const int32_t* cu_seqlens_q;  /* device, [batch+1], or NULL for dense */
