@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="dropout of P with probability P (Philox4x32-10 keep mask, seed 1, offset 0)")
+    ap.add_argument("--alibi", action="store_true", help="ALiBi slopes 2^(-8 (h + 1) / Hq) per q-head")
     ap.add_argument("--bias", action="store_true",
                     help="an elementwise bias [B, Hq, Sq, Sk] (seeded normal x 2) and its gradient dBias")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -188,9 +189,14 @@ def main():
         bias = (2 * torch.randn(bshape, generator=gen, device="cuda")).to(dt)
         dbias = torch.empty_like(bias)
     drop = (args.dropout, 1, 0) if args.dropout > 0 else None
-    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=bias, dropout=drop, **kw)
+    slopes = None
+    if args.alibi:
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / p.heads_q) for h in range(p.heads_q)],
+                              dtype=torch.float32, device="cuda")
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=bias, dropout=drop,
+                         alibi_slopes=slopes, **kw)
     plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, dq_algo=args.dq_algo,
-                            bias=bias, dbias=dbias, dropout=drop, **kw)
+                            bias=bias, dbias=dbias, dropout=drop, alibi_slopes=slopes, **kw)
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
@@ -260,9 +266,10 @@ def main():
     post_bytes = rows_q * p.heads_q * p.head_dim * (4 + elem)
 
     out = {
-        "metric": METRIC if args.workload == "c3" and not args.bias and not args.dropout else
+        "metric": METRIC if args.workload == "c3" and not (args.bias or args.dropout or args.alibi) else
         f"attention-backward TFLOP/s ({p.dtype}, {p.name}{', elementwise bias and dBias' if args.bias else ''}"
-        f"{f', dropout {args.dropout}' if args.dropout else ''}) and % of MFMA peak",
+        f"{f', dropout {args.dropout}' if args.dropout else ''}{', ALiBi' if args.alibi else ''}) "
+        "and % of MFMA peak",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -282,7 +289,7 @@ def main():
             "batch": p.batch, "heads_q": p.heads_q, "heads_kv": p.heads_kv, "seqlen_q": p.seqlen_q,
             "seqlen_k": p.seqlen_k, "head_dim": p.head_dim, "causal": p.causal,
             "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
-            "bias": bool(args.bias), "dropout": args.dropout,
+            "bias": bool(args.bias), "dropout": args.dropout, "alibi": bool(args.alibi),
         },
         "roofline": {
             "kernel": ("attn_bwd (" if three else "attn_bwd_full (") + KERNEL_DESC[args.dq_algo] +
@@ -292,7 +299,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None if args.bias or args.dropout else traffic_entry(args.dq_algo, args.workload, args.api),
+            "traffic": None if args.bias or args.dropout or args.alibi
+            else traffic_entry(args.dq_algo, args.workload, args.api),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,
         },

@@ -282,6 +282,14 @@ __device__ __forceinline__ void dma_to_lds4(i32x4 r, unsigned lds, int voff) {
     asm volatile("s_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds" :: "{m0}"(lds), "v"(voff), "s"(r) : "memory");
 }
 
+// A read-only fp32 value at a wave-uniform index, loaded through the scalar
+// data cache (the constant address space): a scalar load counts against
+// lgkmcnt, not vmcnt, so waiting for it does not wait for the copies in flight.
+__device__ __forceinline__ float load_uniform_f32(const float* p, int i) {
+    typedef const __attribute__((address_space(4))) float cfloat;
+    return ((cfloat*)p)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // ---------------------------------------------------------------------------
 // dropout: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random
 // Numbers: As Easy as 1, 2, 3", SC 2011).  Ten rounds on a 128-bit counter

@@ -401,7 +401,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
         if constexpr ((ALIBI || BIAS) && R == 0) {
             const float sl = G <= 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                                      __builtin_bit_cast(int, slope_v), cur_g))
-                                     : (a.alibi != nullptr ? a.alibi[hkv * G + cur_g] : 0.f);
+                                     : (a.alibi != nullptr ? load_uniform_f32(a.alibi, hkv * G + cur_g) : 0.f);
             nsl2 = -sl * kLog2e;
         }
         // row statistics of the tile whose second product comes in this step,
