@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--alibi", action="store_true", help="ALiBi slopes 2^(-8 (h + 1) / Hq) per q-head")
     ap.add_argument("--bias", action="store_true",
                     help="an elementwise bias [B, Hq, Sq, Sk] (seeded normal x 2) and its gradient dBias")
+    ap.add_argument("--max-workspace-mib", type=int, default=0, metavar="MIB",
+                    help="cap the stored-dS workspace (kv-head groups in chunks whose dS fits; 0 = no cap)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (HBM counter calibration)")
     ap.add_argument("--cpu-pairs", type=int, default=64, help="(sequence, head) pairs in the CPU oracle sample")
@@ -196,7 +198,8 @@ def main():
     o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=bias, dropout=drop,
                          alibi_slopes=slopes, **kw)
     plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, p.deterministic, dq_algo=args.dq_algo,
-                            bias=bias, dbias=dbias, dropout=drop, alibi_slopes=slopes, **kw)
+                            bias=bias, dbias=dbias, dropout=drop, alibi_slopes=slopes,
+                            max_workspace_bytes=args.max_workspace_mib << 20, **kw)
     dq, dk, dv = torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     torch.cuda.synchronize()
@@ -290,6 +293,7 @@ def main():
             "seqlen_k": p.seqlen_k, "head_dim": p.head_dim, "causal": p.causal,
             "deterministic": p.deterministic, "dq_algo": args.dq_algo, "flops_per_step": flops,
             "bias": bool(args.bias), "dropout": args.dropout, "alibi": bool(args.alibi),
+            "max_workspace_mib": args.max_workspace_mib,
         },
         "roofline": {
             "kernel": ("attn_bwd (" if three else "attn_bwd_full (") + KERNEL_DESC[args.dq_algo] +
@@ -299,7 +303,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None if args.bias or args.dropout or args.alibi
+            "traffic": None if args.bias or args.dropout or args.alibi or args.max_workspace_mib
             else traffic_entry(args.dq_algo, args.workload, args.api),
             "avg_launch_ms": round(main_avg, 5),
             "algorithmic_flops_per_launch": flops,

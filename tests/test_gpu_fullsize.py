@@ -222,6 +222,25 @@ def test_bf16_causal_d64_workload_full(dq_algo, deterministic):
 
 
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
+def test_bf16_causal_d64_workload_end_to_end(dq_algo):
+    """The c2 workload as specified, O and LSE from the library forward: the
+    GPU chain (attn_fwd, then the backward on its O and LSE) against the
+    oracle chain (oracle forward, then the oracle backward on its own fp64 O
+    and LSE), so no oracle input comes from the GPU."""
+    from exact_attention_backward_amd import api
+    p = datagen.workload("c2")
+    x, dev, kw, cu = setup(p)
+    o_g, lse_g = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal)
+    dq, dk, dv = run_backward(p, dev, o_g, lse_g, kw, dq_algo=dq_algo)
+    ro, rlse = oracle.forward(x["q"], x["k"], x["v"], p.scale, p.causal)
+    assert_close("O", to_host(o_g), ro, "bf16")
+    assert np.max(np.abs(lse_g.cpu().numpy().astype(np.float64) - rlse)) <= 2e-4
+    rdq, rdk, rdv = oracle.backward(x["q"], x["k"], x["v"], ro, x["do"], rlse, p.scale, p.causal)
+    for n, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert_close(n, to_host(gg), r, "bf16")
+
+
+@pytest.mark.parametrize("dq_algo", ["separate", "stored_ds", "atomic"])
 def test_headline_causal_all_groups(dq_algo):
     all_groups_check("c3", dq_algo)
 
