@@ -608,12 +608,12 @@ template <class T, int HD>
 static void launch_bwd_t(const BwdArgs& a, bool masked, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
-        // masked: mostly one workgroup per pair of key tiles; the launch's kv-heads only
-        const unsigned kvg = kv_grid(masked, a.hkv_n * a.batch, a.nblk_n);
+        // masked: one workgroup per pair of key tiles; the launch's kv-heads only
+        const unsigned kv_grid = (unsigned)((masked ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE || dq_algo == ATTN_DQ_STORED_DS) {
-            launch_kv<T, HD>(a, masked, dq_algo == ATTN_DQ_STORED_DS, a.alibi != nullptr, kvg, st);
+            launch_kv<T, HD>(a, masked, dq_algo == ATTN_DQ_STORED_DS, a.alibi != nullptr, kv_grid, st);
             return;
         }
     }

@@ -786,26 +786,6 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
 }
 
 
-// Masked workgroups: when the (sequence, kv-head) groups split evenly over
-// the XCDs, each XCD runs its first groups' key tiles in pairs of equal cost
-// and its last groups' (about one round of its CUs) as single key tiles, the
-// most expensive first.  The last round's workgroups start at staggered
-// times; single tiles of falling cost let them end close together.
-constexpr int kCusPerXcd = 32;
-__host__ __device__ inline int kv_tail_groups(int gx, int per_group) {
-    const int t = (kCusPerXcd + per_group - 1) / per_group;
-    return t < gx ? t : gx;
-}
-// Grid of bwd_kv_kernel for `groups` (sequence, kv-head) groups of nblk_n
-// key tiles each.
-inline unsigned kv_grid(bool masked, int groups, int nblk_n) {
-    if (!masked) return (unsigned)(nblk_n * groups);
-    const int per_group = (nblk_n + 1) / 2;
-    if (groups % kXcds != 0) return (unsigned)(per_group * groups);
-    const int gx = groups / kXcds, tail = kv_tail_groups(gx, per_group);
-    return (unsigned)(kXcds * ((gx - tail) * per_group + tail * nblk_n));
-}
-
 template <class T, int HD, bool MASKED, bool STORE_DS, bool ALIBI, bool BIAS, bool DROP>
 __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[BIAS ? KvCfg<HD>::LDS_BYTES_BIAS : KvCfg<HD>::LDS_BYTES];
@@ -817,26 +797,15 @@ __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a
     // a causal mask key tile n is seen by a number of query tiles that falls
     // linearly with n, so workgroup p takes the tiles p and (last - p), which
     // together always cost about the same (under a window alone the pairs
-    // cost about the same anyway); the tail groups of an XCD (kv_grid) take
-    // single tiles instead, tile `single` for workgroup slot (single, group)
+    // cost about the same anyway).
     const int per_group = MASKED ? (a.nblk_n + 1) / 2 : a.nblk_n;
-    int grp, p, single = -1;
+    int grp, p;
     {
         const int groups = a.hkv_n * a.batch;
         if (groups % kXcds == 0) {
             const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-            const int gx = groups / kXcds;
-            const int tail = MASKED ? kv_tail_groups(gx, per_group) : 0;
-            const int paired = (gx - tail) * per_group;
-            if (slot < paired) {
-                grp = (slot / per_group) * kXcds + xcd;
-                p = slot % per_group;
-            } else {
-                const int s2 = slot - paired;
-                grp = (gx - tail + s2 % tail) * kXcds + xcd;
-                p = 0;
-                single = s2 / tail;
-            }
+            grp = (slot / per_group) * kXcds + xcd;
+            p = slot % per_group;
         } else {
             grp = blockIdx.x / per_group;
             p = blockIdx.x % per_group;
@@ -849,11 +818,10 @@ __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a
         const int nk = (si.len_k + KROUND * KBN - 1) / (KROUND * KBN) * KROUND;   // this sequence's key tiles
         const int n2 = nk - 1 - p;
         // one call site in a loop: a single copy of the (large) tile body
-        const int cnt = single >= 0 ? (single < nk ? 1 : 0) : (p <= n2) + (n2 > p);
-        const int first = single >= 0 ? single : (p <= n2 ? p : n2);
+        const int cnt = (p <= n2) + (n2 > p);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
-            kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, k == 0 ? first : n2, si, smem);
+            kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);
         }
     } else {
         kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, p, si, smem);
