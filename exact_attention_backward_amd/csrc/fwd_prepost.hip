@@ -278,14 +278,34 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a, BwdArgs t, i
         a.delta[lse_index(a.varlen, r, h, a.h, a.s, a.total)] = dsum[threadIdx.x];
 }
 
-// zero row i of (sequence b, q-head h) of a [b, h, i, j] tensor: its len_k elements
+// Zero the masked elements of a [b, h, i, j] tensor (dBias): in row i of
+// (sequence b, q-head h), the keys j < len_k outside i + off - lo <= j <=
+// i + off + hi.  The backward kernels write every visible element of the
+// rows i < len_q, so nothing else needs clearing.  kZeroRows rows per
+// workgroup, 64 lanes each; 16-byte stores where the row is 16-byte aligned.
+constexpr int kZeroRows = 4;
 template <class T>
-__global__ __launch_bounds__(256) void zero_blocks_kernel(T* p, Strides s, BwdArgs a) {
-    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(256) void zero_masked_kernel(T* p, Strides s, BwdArgs a) {
+    const int i = blockIdx.x * kZeroRows + (int)(threadIdx.x >> 6), h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x & 63;
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (i >= si.len_q) return;
     T* row = p + (long long)b * s.b + (long long)h * s.h + (long long)i * s.r;
-    for (int j = threadIdx.x; j < si.len_k; j += blockDim.x) store_elem(row, j, 0.f);
+    const int off = si.len_k - si.len_q;
+    const int lo = min(max(i + off - a.win_lo, 0), si.len_k);        // keys [0, lo) lie before the window
+    const int hi = min(max(i + off + a.win_hi + 1, 0), si.len_k);    // keys [hi, len_k) lie after it
+    constexpr int E = 16 / (int)sizeof(T);
+    const bool al = (reinterpret_cast<unsigned long long>(row) & 15) == 0;
+    auto zero_range = [&](int x0, int x1) {   // keys [x0, x1)
+        if (x0 >= x1) return;
+        const int a0 = al ? min((x0 + E - 1) / E * E, x1) : x1;   // first key of the 16-byte part
+        const int a1 = al ? max(x1 / E * E, a0) : x1;             // its end
+        for (int j = x0 + t; j < a0; j += 64) store_elem(row, j, 0.f);
+        for (int j = a1 + t; j < x1; j += 64) store_elem(row, j, 0.f);
+        for (int c = a0 / E + t; c < a1 / E; c += 64) reinterpret_cast<u32x4*>(row)[c] = u32x4{0u, 0u, 0u, 0u};
+    };
+    zero_range(0, lo);
+    zero_range(max(hi, lo), si.len_k);
 }
 
 // ---------------------------------------------------------------------------
@@ -352,11 +372,11 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st
     }
 }
 
-void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st) {
-    const dim3 grid((unsigned)a.seqlen_q, (unsigned)a.hq, (unsigned)a.batch);
-    if (dtype == ATTN_DTYPE_BF16) zero_blocks_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<bf16_t*>(p), s, a);
-    else if (dtype == ATTN_DTYPE_F16) zero_blocks_kernel<f16_t><<<grid, 256, 0, st>>>(reinterpret_cast<f16_t*>(p), s, a);
-    else zero_blocks_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<float*>(p), s, a);
+void launch_zero_masked(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st) {
+    const dim3 grid((unsigned)((a.seqlen_q + kZeroRows - 1) / kZeroRows), (unsigned)a.hq, (unsigned)a.batch);
+    if (dtype == ATTN_DTYPE_BF16) zero_masked_kernel<bf16_t><<<grid, 256, 0, st>>>(reinterpret_cast<bf16_t*>(p), s, a);
+    else if (dtype == ATTN_DTYPE_F16) zero_masked_kernel<f16_t><<<grid, 256, 0, st>>>(reinterpret_cast<f16_t*>(p), s, a);
+    else zero_masked_kernel<float><<<grid, 256, 0, st>>>(reinterpret_cast<float*>(p), s, a);
 }
 
 void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table, int bm, bool masked,

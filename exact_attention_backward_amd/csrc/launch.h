@@ -212,7 +212,7 @@ void launch_fwd(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st
 // the MFMA forward (bf16 and fp16, no elementwise bias)
 void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st);
 // zero every sequence's [Hq, len_q, len_k] block of a [b, h, i, j] tensor with strides s
-void launch_zero_blocks(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st);
+void launch_zero_masked(void* p, const Strides& s, int dtype, const BwdArgs& a, hipStream_t st);
 // table (stored-dS mode, else null): also build its block table (for query
 // tiles of bm rows) in an extra workgroup
 void launch_preprocess(const PreArgs& a, int dtype, int hd, const BwdArgs* table, int bm, bool masked,
