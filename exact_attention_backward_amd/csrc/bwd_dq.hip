@@ -332,14 +332,22 @@ __device__ __forceinline__ void dq_tile(int m, const BwdArgs& a, int b, int hq, 
         // diagonal key i + off: fdist + 32 jb + 8 (v / 4) + v % 4
         const float fdist = (float)(j0 + 4 * h - i - off);
         // dropout: this lane's row i of the 4 x 4 blocks (keys j0 + 8 q + 4h ..
-        // + 3, q = 4 jb + q4): word i % 4, byte (key % 4)
+        // + 3, q = 4 jb + q4): word i % 4, byte (key % 4).  The four lanes of
+        // a group of four rows (lanes 4k .. 4k + 3, i % 4 = lane % 4) need the
+        // same blocks: lane c draws block 4 jb + c and the group trades words.
         unsigned dword_[DROP ? C::NJB * 4 : 1];
         if constexpr (DROP) {
+            const int c = lane & 3;
 #pragma unroll
-            for (int q = 0; q < C::NJB * 4; ++q)
-                dword_[q] = word_at(drop_block((unsigned)((j0 + 8 * q + 4 * h) >> 2), (unsigned)(i >> 2),
-                                               (unsigned)(b * a.hq + hq), a.drop.off, a.drop.k0, a.drop.k1),
-                                    i & 3);
+            for (int jb = 0; jb < C::NJB; ++jb) {
+                const int q = 4 * jb + c;
+                const u32x4 w = quad_word_transpose(
+                    drop_block((unsigned)((j0 + 8 * q + 4 * h) >> 2), (unsigned)(i >> 2), (unsigned)(b * a.hq + hq),
+                               a.drop.off, a.drop.k0, a.drop.k1),
+                    c);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) dword_[4 * jb + q4] = w[q4];
+            }
         }
         auto softmax_grad = [&](auto masked) {
 #pragma unroll

@@ -353,17 +353,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
         auto softmax_grad = [&](auto masked, auto extra) {
 #pragma unroll
             for (int mb = 0; mb < C::NMB; ++mb) {
+                // dropout: bit 4 q4 + e of keep is element (row 32 mb + 8 q4 + 4h
+                // + e, key j).  The four lanes of a group of four keys (lanes
+                // 4k .. 4k + 3, j % 4 = lane % 4) need the same blocks: lane c
+                // draws block q4 = c and the group trades the decisions.
+                unsigned keep_m = 0xffffffffu;
+                if constexpr (decltype(extra)::value) {
+                    if (a.drop.on) {
+                        const int c = lane & 3;
+                        const unsigned m = drop_mask16(
+                            drop_block((unsigned)(j >> 2), (unsigned)((i0 + 32 * mb + 8 * c + 4 * h) >> 2),
+                                       (unsigned)(b * a.hq + hq), a.drop.off, a.drop.k0, a.drop.k1),
+                            a.drop.thr);
+                        const unsigned sh = 4u * (unsigned)c;
+                        keep_m = ((quad_bcast<0>(m) >> sh) & 0xfu) | (((quad_bcast<1>(m) >> sh) & 0xfu) << 4) |
+                                 (((quad_bcast<2>(m) >> sh) & 0xfu) << 8) | (((quad_bcast<3>(m) >> sh) & 0xfu) << 12);
+                    }
+                }
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int r = 32 * mb + 8 * q4 + 4 * h;
                     const f32x4 lse = *reinterpret_cast<const f32x4*>(llse + r);
                     const f32x4 dl = *reinterpret_cast<const f32x4*>(ldl + r);
-                    u32x4 dw = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};   // keep all
-                    if constexpr (decltype(extra)::value) {
-                        if (a.drop.on)
-                            dw = drop_block((unsigned)(j >> 2), (unsigned)((i0 + r) >> 2), (unsigned)(b * a.hq + hq),
-                                            a.drop.off, a.drop.k0, a.drop.k1);
-                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * q4 + e;
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs a) {
                         }
                         if constexpr (decltype(extra)::value) {
                             if (a.drop.on) {
-                                const bool keep = drop_keep(word_at(dw, e), j & 3, a.drop.thr);
+                                const bool keep = (keep_m >> (4 * q4 + e)) & 1u;
                                 s[mb][v] = keep ? p : 0.f;
                                 dp[mb][v] = p * ((keep ? a.drop.rp * dp[mb][v] : 0.f) - dl[e]);
                                 continue;

@@ -324,9 +324,42 @@ __device__ __forceinline__ u32x4 drop_block(unsigned j4, unsigned i4, unsigned b
 __device__ __forceinline__ bool drop_keep(unsigned word, int byte, unsigned thr) {
     return ((word >> (8 * byte)) & 0xffu) >= thr;
 }
+// The keep decisions of one generator output (a block of 4 rows x 4 keys):
+// bit 4 c + e is byte c of word e against the threshold, element (row e, key c).
+__device__ __forceinline__ unsigned drop_mask16(u32x4 w, unsigned thr) {
+    unsigned m = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m |= (((w[e] >> (8 * c)) & 0xffu) >= thr ? 1u : 0u) << (4 * c + e);
+    }
+    return m;
+}
+// v of lane Q of this lane's group of four consecutive lanes (a DPP quad broadcast)
+template <int Q>
+__device__ __forceinline__ unsigned quad_bcast(unsigned v) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)v, Q * 0x55, 0xf, 0xf, false);
+}
 // Word r (a run-time 0..3) of a generator output.
 __device__ __forceinline__ unsigned word_at(u32x4 w, int r) {
     return r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+}
+// A 4 x 4 transpose of words in a group of four consecutive lanes: lane s
+// holds the output w of block s; lane c (= its lane % 4) gets word c of the
+// block of lane q as element q.  Round r reads lane (c + r) % 4 (a DPP quad
+// rotation), which sends its word (s - r) % 4, that is c.
+__device__ __forceinline__ u32x4 quad_word_transpose(u32x4 w, int c) {
+    const unsigned g0 = word_at(w, c);
+    const unsigned g1 = (unsigned)__builtin_amdgcn_mov_dpp((int)word_at(w, (c + 3) & 3), 0x39, 0xf, 0xf, false);
+    const unsigned g2 = (unsigned)__builtin_amdgcn_mov_dpp((int)word_at(w, (c + 2) & 3), 0x4e, 0xf, 0xf, false);
+    const unsigned g3 = (unsigned)__builtin_amdgcn_mov_dpp((int)word_at(w, (c + 1) & 3), 0x93, 0xf, 0xf, false);
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = (q - c) & 3;   // g_r is word c of block (c + r) % 4
+        out[q] = r == 0 ? g0 : r == 1 ? g1 : r == 2 ? g2 : g3;
+    }
+    return out;
 }
 
 // ---------------------------------------------------------------------------

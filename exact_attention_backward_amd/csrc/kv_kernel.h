@@ -560,14 +560,24 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
             // q = 4 mb + q4, this lane's key j): byte j % 4 of word e
             unsigned keep = 0xffffffffu;
             if constexpr (DROP) {
+                // the four lanes of a group of four keys (lanes 4k .. 4k + 3,
+                // key j % 4 = lane % 4, the same rows) need the same generator
+                // blocks: lane c draws block 4 qq + c and the group trades the
+                // decisions, lane c taking key c's nibble of each block
                 keep = 0u;
+                const int c = lane & 3;
+                const unsigned sh = 4u * (unsigned)c;
 #pragma unroll
-                for (int q = 0; q < NMB * 4; ++q) {
+                for (int qq = 0; qq < NMB; ++qq) {
+                    const int q = 4 * qq + c;
                     const u32x4 dw = drop_block((unsigned)(j >> 2), (unsigned)((i0 + 8 * q + 4 * h) >> 2),
                                                 (unsigned)(b * a.hq + hkv * G + g_t), a.drop.off, a.drop.k0,
                                                 a.drop.k1);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) keep |= (drop_keep(dw[e], j & 3, a.drop.thr) ? 1u : 0u) << (4 * q + e);
+                    const unsigned m = drop_mask16(dw, a.drop.thr);
+                    keep |= ((quad_bcast<0>(m) >> sh) & 0xfu) << (16 * qq);
+                    keep |= ((quad_bcast<1>(m) >> sh) & 0xfu) << (16 * qq + 4);
+                    keep |= ((quad_bcast<2>(m) >> sh) & 0xfu) << (16 * qq + 8);
+                    keep |= ((quad_bcast<3>(m) >> sh) & 0xfu) << (16 * qq + 12);
                 }
             }
 #pragma unroll
