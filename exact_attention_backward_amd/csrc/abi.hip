@@ -438,11 +438,12 @@ void enqueue_preprocess(const attn_shape_t* s, const Layout& l, const void* o, c
     }
 }
 
-// ---- a second stream per device for the separate mode, whose dQ kernel
-// needs neither the dK/dV kernel nor its outputs: on small problems, where
-// neither fills the GPU alone, the two run side by side (measured 8% faster
-// on B=2 H=8 S=1024 D=64; on the full-size shapes 0.5-1.5% slower, so they
-// keep one stream: side_worth).  The side stream is
+// ---- a second stream per device for work that needs neither the dK/dV
+// kernel nor its outputs: the masked-dBias clear (1% on B=4 H=16 S=4096
+// causal with dBias) and the separate mode's dQ kernel on small problems,
+// where neither kernel fills the GPU alone (8% on B=2 H=8 S=1024 D=64; on
+// the full-size shapes 0.5-1.5% slower, so they keep one stream:
+// side_worth).  The side stream is
 // forked from the caller's stream after the work enqueued so far and joined
 // back before the call returns, so to the caller everything stays ordered on
 // its own stream.  Created once per device (default priority, non-blocking),
@@ -507,8 +508,22 @@ void enqueue_bwd(const attn_shape_t* s, const Layout& l, const void* q, const vo
     a.dv = dv;
     a.dq_out = l.p.algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
     a.dq_scale = dq_scale;
+    // On the side stream (when there is one to take): the masked-dBias clear
+    // (it writes only elements the kernels write as zero, if at all) and, on
+    // small problems, the separate mode's dQ kernel
+    const bool zero = s->dbias != nullptr && masked(s);
+    const bool sep_side = l.p.algo == ATTN_DQ_SEPARATE && side_worth(s);
+    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+    SideStream* ss = nullptr;
+    if (side && (zero || sep_side)) {
+        lock.lock();
+        if (side_stream(hs, &ss) != ATTN_OK || hipEventRecord(ss->fork, hs) != hipSuccess ||
+            hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+            ss = nullptr;   // one after the other on the caller's stream
+    }
+    const hipStream_t aux = ss != nullptr ? ss->s : hs;
     // masked dBias elements read zero (the kernels write the visible ones)
-    if (s->dbias != nullptr && masked(s)) launch_zero_masked(s->dbias, a.sdbias, s->dtype, a, hs);
+    if (zero) launch_zero_masked(s->dbias, a.sdbias, s->dtype, a, aux);
     if (l.p.algo == ATTN_DQ_STORED_DS) {
         // kv-head groups in chunks whose dS fits the workspace: the dK/dV
         // kernel stores the chunk's dS, the dQ pass consumes it
@@ -518,29 +533,23 @@ void enqueue_bwd(const attn_shape_t* s, const Layout& l, const void* q, const vo
             launch_bwd(a, s->dtype, padded_hd(s), masked(s), ATTN_DQ_STORED_DS, hs);
             launch_bwd_dq_gemm(a, s->dtype, padded_hd(s), masked(s), hs);
         }
-        return;
-    }
-    if (l.p.algo == ATTN_DQ_SEPARATE) {
+    } else if (l.p.algo == ATTN_DQ_SEPARATE) {
         BwdArgs e = a;
         e.nblk_m = (s->seqlen_q + bwd_dq_block_m() - 1) / bwd_dq_block_m();
-        if (side && side_worth(s)) {
-            std::lock_guard<std::mutex> lock(g_side_mu);
-            SideStream* ss = nullptr;
-            if (side_stream(hs, &ss) == ATTN_OK && hipEventRecord(ss->fork, hs) == hipSuccess &&
-                hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess) {
-                launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), ss->s);
-                launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
-                (void)hipEventRecord(ss->join, ss->s);      // a failure here is left for check_launch
-                (void)hipStreamWaitEvent(hs, ss->join, 0);
-                return;
-            }
+        if (sep_side && ss != nullptr) {
+            launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), aux);
+            launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
+        } else {
+            launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
+            launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), hs);
         }
-        // one after the other on the caller's stream
+    } else {
         launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
-        launch_bwd_dq(e, s->dtype, padded_hd(s), masked(s), hs);
-        return;
     }
-    launch_bwd(a, s->dtype, padded_hd(s), masked(s), l.p.algo, hs);
+    if (ss != nullptr) {
+        (void)hipEventRecord(ss->join, ss->s);   // a failure here is left for check_launch
+        (void)hipStreamWaitEvent(hs, ss->join, 0);
+    }
 }
 
 void enqueue_postprocess(const attn_shape_t* s, const Layout& l, const void* workspace, void* dq, float scale,

@@ -68,9 +68,15 @@ struct KvCfg {
     // in each of two buffers (tile parity), copied one tile ahead
     static constexpr int BIAS_PAIR = BM * 64;
     static constexpr int OFF_BIAS = (LDS_BYTES + 1023) / 1024 * 1024;
-    static constexpr int LDS_BYTES_BIAS = OFF_BIAS + 2 * NP * BIAS_PAIR;
+    // dBias (dS wave): the tile's dS, key-major (one key's BM rows, padded
+    // by 8 bytes against bank conflicts), read back row-major for 16-byte stores
+    static constexpr int DBIMG_ROWB = 2 * BM + 8;
+    static constexpr int DBIMG = 32 * DBIMG_ROWB;
+    static constexpr int OFF_DBIMG = OFF_BIAS + 2 * NP * BIAS_PAIR;
+    static constexpr int LDS_BYTES_BIAS = OFF_DBIMG + NP * DBIMG;
     static constexpr int BOPS = BM / 16;             // bias copies per tile and P wave (16 rows each)
-    static constexpr int NDBS = BM / 2;              // dBias stores per tile and dS wave (one per element)
+    static constexpr int NDBW = BM / 16;             // dBias stores per tile and dS wave (16 bytes each)
+    static constexpr int NDBS = BM / 2;              // the same one element each (unaligned dBias, ragged keys)
     static constexpr int NC = HD / 16;               // 16-wide chunks of the head dim
     static constexpr int NDB = HD / 32;              // 32-column blocks of the head dim
     static constexpr int SEG = TILE / 1024 / NW;     // 1 KiB segments of a Q or dO tile per wave
@@ -356,13 +362,23 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
     };
     DsBlocks ds_last{ds_head, ds_cur.blk, ds_cur.cnt};   // tile t-1: what its stores need
     constexpr int NST = STORE_DS ? 2 * NMB : 0;   // dS stores per dS-wave step
-    constexpr int NDBS = BIAS ? C::NDBS : 0;      // dBias stores per dS-wave step
-    constexpr int NSTW = NST + NDBS;
+    // dBias stores per dS-wave step: NDBW 16-byte stores, or NDBS element
+    // stores where dBias rows are not 16-byte aligned or the key tile is
+    // ragged.  The wait counts assume the smaller number: more stores issued
+    // after a tile's copies only make a wait stricter.
+    constexpr int NDB = BIAS ? C::NDBW : 0;
+    constexpr int NSTW = NST + NDB;
     // dBias (dS wave): element (row r of tile t-1, this lane's key j) goes to
     // the tile's first row + r * row stride + j, one 16-bit store each.  Keys
     // past the sequence take an offset past every range; rows past it fall
     // outside the range (it ends at the last valid row's last key).
     const long long sdbr_b = a.sdbias.r * (long long)sizeof(T);
+    // (not with dropout, whose kernel has no registers to spare for it)
+    const bool db_wide = BIAS && !DROP && a.dbias != nullptr && n * KBN + KBN <= si.len_k &&
+                         ((reinterpret_cast<unsigned long long>(a.dbias) |
+                           (unsigned long long)(a.sdbias.b * (long long)sizeof(T)) |
+                           (unsigned long long)(a.sdbias.h * (long long)sizeof(T)) | (unsigned long long)sdbr_b) &
+                          15) == 0;
     const int db_voff = j < si.len_k ? (int)(4 * h * sdbr_b) + (32 * pair + l32) * (int)sizeof(T) : kOobOff;
     int db_m = m_begin, db_g = 0;   // dS wave: query tile and q-head of tile t-1
     // P wave's transposing reads of its bias image: lane (l32, h) gets key
@@ -725,14 +741,43 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, int b, int hkv, int n,
                                                             (unsigned)(max(si.len_k - n * KBN, 0) * (int)sizeof(T))
                                                       : 0u;
             const rsrc_t dst = make_rsrc(dbase, bytes);
+            if (!DROP && db_wide) {
+                // through this wave's LDS image: lane (l32, h) leaves its key's
+                // rows 32 (c / 2) + 16 (c % 2) + 4h + 0..3 and + 8 .. 11, then
+                // transposing reads give lane u of 16-lane group g keys
+                // 8 kc .. + 7 of row 16 rb + u, (rb, kc) = (x / 4, x % 4) for
+                // x = 4 p + g: one 16-byte store each
+                const int img = C::OFF_DBIMG + pair * C::DBIMG;
 #pragma unroll
-            for (int c = 0; c < C::NIC; ++c) {
-                const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+                for (int c = 0; c < C::NIC; ++c) {
+                    const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+                    const int r0 = 32 * (c >> 1) + 16 * (c & 1) + 4 * h;
+                    *reinterpret_cast<u32x2*>(smem + img + l32 * C::DBIMG_ROWB + 2 * r0) = u32x2{wv[0], wv[1]};
+                    *reinterpret_cast<u32x2*>(smem + img + l32 * C::DBIMG_ROWB + 2 * (r0 + 8)) = u32x2{wv[2], wv[3]};
+                }
+                const int u16 = lane & 15, g = lane >> 4;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int r = 32 * (c >> 1) + 8 * (2 * (c & 1) + (u >> 2)) + (u & 3);   // + 4h
-                    const unsigned short x = (unsigned short)((u & 1) ? (wv[u >> 1] >> 16) : (wv[u >> 1] & 0xffffu));
-                    __builtin_amdgcn_raw_buffer_store_b16(x, dst, db_voff, (int)(r * sdbr_b), 2);
+                for (int p = 0; p < C::NDBW; ++p) {
+                    const int x = 4 * p + g, rb = x >> 2, kc = x & 3;
+                    // source lane u16 points at key 8 kc + u16 / 4, rows 16 rb + 4 (u16 % 4) .. + 3
+                    const int src = img + (8 * kc + (u16 >> 2)) * C::DBIMG_ROWB + 2 * (16 * rb + 4 * (u16 & 3));
+                    const u32x2 k0 = lds_read_tr(smem, src);
+                    const u32x2 k4 = lds_read_tr(smem, src + 4 * C::DBIMG_ROWB);
+                    const int row = 16 * rb + u16;
+                    const int voff = row < rows ? (int)(row * sdbr_b) + (32 * pair + 8 * kc) * (int)sizeof(T) : kOobOff;
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{k0[0], k0[1], k4[0], k4[1]}, dst, voff, 0, 2);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < C::NIC; ++c) {
+                    const u32x4 wv = __builtin_bit_cast(u32x4, opa[c]);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = 32 * (c >> 1) + 8 * (2 * (c & 1) + (u >> 2)) + (u & 3);   // + 4h
+                        const unsigned short x =
+                            (unsigned short)((u & 1) ? (wv[u >> 1] >> 16) : (wv[u >> 1] & 0xffffu));
+                        __builtin_amdgcn_raw_buffer_store_b16(x, dst, db_voff, (int)(r * sdbr_b), 2);
+                    }
                 }
             }
         }
