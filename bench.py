@@ -35,8 +35,11 @@ METRIC = "attention-backward TFLOP/s (bf16, causal, S=4096, D=128) and % of MFMA
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 TORCH_DT = {"bf16": "bfloat16", "f16": "float16", "f32": "float32"}
 PEAK_HBM_GBS = 8000.0
+# the sources the dK/dV and dQ kernels are compiled from: a change to any of
+# them voids the committed HBM counter summary
 MAIN_SRCS = [os.path.join(ROOT, "exact_attention_backward_amd", "csrc", f)
-             for f in ("bwd_main.hip", "bwd_dq.hip", "bwd_dq_gemm.hip")]
+             for f in ("bwd_main.hip", "kv_kernel.h", "bwd_shared.h", "common.h", "launch.h", "bwd_dq.hip",
+                       "bwd_dq_gemm.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_main_{}_{}.json")
 KERNEL_DESC = {
     "stored_ds": "key-stationary dK/dV kernel storing dS + dQ = dS K pass",

@@ -456,12 +456,13 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-// whether the dK/dV kernel leaves most of the GPU idle: at most two key
-// tiles (of 128 keys) per compute unit over all (sequence, kv-head) groups
+// whether the dK/dV kernel leaves most of the GPU idle: at most one key
+// tile (of 128 keys) per compute unit over all (sequence, kv-head) groups
+// (its workgroups take two tiles each under a causal mask)
 bool side_worth(const attn_shape_t* s) {
     constexpr long long kComputeUnits = 256;
     const long long tiles = (long long)((s->seqlen_k + 127) / 128) * s->num_heads_kv * s->batch;
-    return tiles <= 2 * kComputeUnits;
+    return tiles <= kComputeUnits;
 }
 
 // under g_side_mu.  Not created while `hs` is being captured into a graph
