@@ -98,6 +98,27 @@ def traffic_entry(dq_algo, workload, api):
     return t.get("hbm_bytes_per_launch")
 
 
+def device_peak(dtype):
+    """The dense MFMA peak from this device's own compute-unit count and
+    peak clock (hipDeviceGetAttribute), reported beside the published figure
+    the roofline uses; None where the runtime cannot be asked."""
+    import ctypes
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    khz = ctypes.c_int(0)
+    HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5   # hipDeviceAttributeClockRate: peak clock in kHz
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE,
+                                 torch.cuda.current_device()) != 0 or khz.value <= 0:
+        return None
+    per_clock = {"bf16": 4096, "f16": 4096, "f32": 256}[dtype]   # dense FLOP per clock per CU
+    return {"tflops": round(cus * khz.value * 1e3 * per_clock / 1e12, 1), "compute_units": cus,
+            "peak_clock_mhz": round(khz.value / 1e3, 1), "flop_per_clock_per_cu": per_clock}
+
+
 def cpu_baseline(p, x, n_pairs):
     """The fp64 oracle backward on the first n_pairs (sequence, q-head) pairs
     of the workload (sequence-major), each at full length, given O and LSE
@@ -304,6 +325,7 @@ def main():
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
+            "peak_from_device": device_peak(p.dtype),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": None if args.bias or args.dropout or args.alibi or args.max_workspace_mib

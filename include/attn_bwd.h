@@ -27,9 +27,17 @@
  *  - All tensor pointers are DEVICE pointers, 16-byte aligned, head
  *    dimension innermost and contiguous; rows, heads and batch entries are
  *    contiguous too unless shape->strides gives their strides.  The caller allocates and frees every buffer,
- *    the workspace included; the library never allocates, frees or
- *    synchronises.  Every call only enqueues work on `stream` (a hipStream_t,
- *    NULL = the default stream) and returns.
+ *    the workspace included; the library never allocates device memory,
+ *    frees or synchronises.  Every call only enqueues work on `stream` (a
+ *    hipStream_t, NULL = the default stream) and returns.  attn_bwd and
+ *    attn_bwd_full may run part of that work (the clear of masked dBias
+ *    elements; the separate dQ mode's dQ kernel on problems whose dK/dV grid
+ *    cannot fill the GPU) on a stream of the library's own, one per device,
+ *    created at first use (not while `stream` is being captured into a
+ *    graph) and held until the process ends: it is forked from `stream` by an
+ *    event after the work enqueued before the call and joined back by another
+ *    before the call returns, so all of it stays ordered on `stream` and the
+ *    call can be captured.  attn_bwd_full_noalloc never uses it.
  *  - Layouts (element type = shape->dtype for Q K V O dO dQ dK dV; fp32 for
  *    LSE and D):
  *        dense : Q, O, dO, dQ [B, Sq, Hq, D];  K, V, dK, dV [B, Sk, Hkv, D]
