@@ -438,12 +438,14 @@ void enqueue_preprocess(const attn_shape_t* s, const Layout& l, const void* o, c
     }
 }
 
-// ---- a second stream per device for work that needs neither the dK/dV
-// kernel nor its outputs: the masked-dBias clear (1% on B=4 H=16 S=4096
-// causal with dBias) and the separate mode's dQ kernel on small problems,
-// where neither kernel fills the GPU alone (8% on B=2 H=8 S=1024 D=64; on
-// the full-size shapes 0.5-1.5% slower, so they keep one stream:
-// side_worth).  The side stream is
+// ---- a second stream per device for the separate mode's dQ kernel, which
+// needs neither the dK/dV kernel nor its outputs: on small problems, where
+// neither kernel fills the GPU alone, the two run side by side (8% on B=2
+// H=8 S=1024 D=64; on the full-size shapes 0.5-1.5% slower, so they keep
+// one stream: side_worth).  (The masked-dBias clear stays on the caller's
+// stream, ahead of the kernels: beside them it gained 1%, but a masked
+// element inside a visited tile then got the clear's +0 or the kernel's
+// -0 (P = 0 times a negative dP - D) depending on timing.)  The side stream is
 // forked from the caller's stream after the work enqueued so far and joined
 // back before the call returns, so to the caller everything stays ordered on
 // its own stream.  Created once per device (default priority, non-blocking),
@@ -509,22 +511,21 @@ void enqueue_bwd(const attn_shape_t* s, const Layout& l, const void* q, const vo
     a.dv = dv;
     a.dq_out = l.p.algo == ATTN_DQ_ATOMIC ? nullptr : dq_out;
     a.dq_scale = dq_scale;
-    // On the side stream (when there is one to take): the masked-dBias clear
-    // (it writes only elements the kernels write as zero, if at all) and, on
-    // small problems, the separate mode's dQ kernel
-    const bool zero = s->dbias != nullptr && masked(s);
+    // masked dBias elements read zero (the kernels write the visible ones,
+    // and the masked ones of the tiles they visit, after this)
+    if (s->dbias != nullptr && masked(s)) launch_zero_masked(s->dbias, a.sdbias, s->dtype, a, hs);
+    // on small problems the separate mode's dQ kernel runs on the side
+    // stream (when there is one to take)
     const bool sep_side = l.p.algo == ATTN_DQ_SEPARATE && side_worth(s);
     std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
     SideStream* ss = nullptr;
-    if (side && (zero || sep_side)) {
+    if (side && sep_side) {
         lock.lock();
         if (side_stream(hs, &ss) != ATTN_OK || hipEventRecord(ss->fork, hs) != hipSuccess ||
             hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
             ss = nullptr;   // one after the other on the caller's stream
     }
     const hipStream_t aux = ss != nullptr ? ss->s : hs;
-    // masked dBias elements read zero (the kernels write the visible ones)
-    if (zero) launch_zero_masked(s->dbias, a.sdbias, s->dtype, a, aux);
     if (l.p.algo == ATTN_DQ_STORED_DS) {
         // kv-head groups in chunks whose dS fits the workspace: the dK/dV
         // kernel stores the chunk's dS, the dQ pass consumes it

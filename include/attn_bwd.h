@@ -30,9 +30,9 @@
  *    the workspace included; the library never allocates device memory,
  *    frees or synchronises.  Every call only enqueues work on `stream` (a
  *    hipStream_t, NULL = the default stream) and returns.  attn_bwd and
- *    attn_bwd_full may run part of that work (the clear of masked dBias
- *    elements; the separate dQ mode's dQ kernel on problems whose dK/dV grid
- *    cannot fill the GPU) on a stream of the library's own, one per device,
+ *    attn_bwd_full may run part of that work (the separate dQ mode's dQ
+ *    kernel on problems whose dK/dV grid cannot fill the GPU) on a stream of
+ *    the library's own, one per device,
  *    created at first use (not while `stream` is being captured into a
  *    graph) and held until the process ends: it is forked from `stream` by an
  *    event after the work enqueued before the call and joined back by another
