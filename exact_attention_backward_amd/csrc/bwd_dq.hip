@@ -443,7 +443,8 @@ __global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void bwd_dq_ke
     // mask the keys a query tile sees grow linearly with its index, so
     // workgroup p takes the tiles p and (last - p) (also under a window).
     const int G = a.hq / a.hkv;
-    const int n_pair = MASKED ? (a.nblk_m + 1) / 2 : a.nblk_m;
+    const bool pair = MASKED && a.pair_tiles;
+    const int n_pair = pair ? (a.nblk_m + 1) / 2 : a.nblk_m;
     const int per_group = n_pair * G;          // workgroups of one (sequence, kv-head)
     int grp, slot;
     {
@@ -464,20 +465,24 @@ __global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void bwd_dq_ke
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (MASKED) {
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
-        const int m2 = nq - 1 - p;
-        if (m2 > p) {
-            dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
-            __syncthreads();   // its LDS ring is free again
+        // paired: the longer tile m2 first, then p; one call site in a loop
+        // (a single copy of the tile body)
+        const int m2 = pair ? nq - 1 - p : p;
+        const int cnt = m2 > p ? 2 : (p < nq && p == m2 ? 1 : 0);
+        for (int k = 0; k < cnt; ++k) {
+            if (k) __syncthreads();   // the first tile's LDS ring is free again
+            dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(k == 0 ? m2 : p, a, b, hq, hkv, si, smem);
         }
-        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     } else {
         dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
-static void launch_dq_t(const BwdArgs& a, bool masked, hipStream_t st) {
-    const unsigned grid = (unsigned)((masked ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
+static void launch_dq_t(const BwdArgs& a0, bool masked, hipStream_t st) {
+    BwdArgs a = a0;   // pairs of query tiles on grids larger than the GPU
+    a.pair_tiles = masked && (long long)a.nblk_m * a.hq * a.batch > kComputeUnits;
+    const unsigned grid = (unsigned)((a.pair_tiles ? (a.nblk_m + 1) / 2 : a.nblk_m) * a.hq * a.batch);
     // variants: plain, ALiBi, bias (+ ALiBi), dropout (+ bias, ALiBi)
     const bool alibi = a.alibi != nullptr, bias = a.bias != nullptr, drop = a.drop.on;
     if (masked) {

@@ -299,7 +299,8 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const int nblk_q = (a.seqlen_q + BQ - 1) / BQ;
     // masked: workgroup p takes query tiles p and nblk_q - 1 - p, whose key
     // ranges add up to the same length for every p (balanced work)
-    const int n_pair = MASKED ? (nblk_q + 1) / 2 : nblk_q;
+    const bool pair = MASKED && a.pair_tiles;
+    const int n_pair = pair ? (nblk_q + 1) / 2 : nblk_q;
     const int per_group = n_pair * G;
     int grp, slot;
     {
@@ -320,23 +321,26 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     const int nblk_q_seq = (si.len_q + BQ - 1) / BQ;   // this sequence's query tiles
     if (MASKED) {
-        // the longer tile first, then its partner (once the first tile's LDS
-        // stages are no longer read)
-        const int m2 = nblk_q_seq - 1 - p;
-        if (m2 > p) {
-            gemm_tile<T, HD, MASKED>(m2, a, b, hq, hkv, si, smem);
-            __syncthreads();
+        // paired: the longer tile m2 first, then its partner p (once the
+        // first tile's LDS stages are no longer read); one call site in a loop
+        const int m2 = pair ? nblk_q_seq - 1 - p : p;
+        const int cnt = m2 > p ? 2 : (p < nblk_q_seq && p == m2 ? 1 : 0);
+        for (int k = 0; k < cnt; ++k) {
+            if (k) __syncthreads();
+            gemm_tile<T, HD, MASKED>(k == 0 ? m2 : p, a, b, hq, hkv, si, smem);
         }
-        if (p < nblk_q_seq && p <= m2) gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     } else {
         gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     }
 }
 
 template <class T, int HD>
-static void launch_dq_gemm_hd(const BwdArgs& a, bool masked, hipStream_t st) {
+static void launch_dq_gemm_hd(const BwdArgs& a0, bool masked, hipStream_t st) {
+    BwdArgs a = a0;
     const int nblk_q = (a.seqlen_q + DqgCfg<HD>::BQ - 1) / DqgCfg<HD>::BQ;
-    const int n_pair = masked ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
+    // pairs of query tiles on grids larger than the GPU
+    a.pair_tiles = masked && (long long)nblk_q * (a.hq / a.hkv) * a.hkv_n * a.batch > kComputeUnits;
+    const int n_pair = a.pair_tiles ? (nblk_q + 1) / 2 : nblk_q;   // workgroups per (sequence, q-head)
     const unsigned grid = (unsigned)(n_pair * (a.hq / a.hkv) * a.hkv_n * a.batch);
     if (masked) bwd_dq_gemm_kernel<T, HD, true><<<grid, kGThreads, 0, st>>>(a);
     else bwd_dq_gemm_kernel<T, HD, false><<<grid, kGThreads, 0, st>>>(a);

@@ -13,7 +13,8 @@ void launch_bwd_kv_wide(const BwdArgs& a0, int dtype, bool masked, bool store_ds
     // key tiles of the longest sequence (with the stored dS, whole dS blocks of them)
     const int round = store_ds ? C::KPB : 1;
     a.nblk_n = (a.seqlen_k + round * C::KBN - 1) / (round * C::KBN) * round;
-    const unsigned grid = (unsigned)((masked ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
+    a.pair_tiles = masked && (long long)a.nblk_n * a.hkv_n * a.batch > kComputeUnits;
+    const unsigned grid = (unsigned)((a.pair_tiles ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
     if (dtype == ATTN_DTYPE_BF16)
         launch_kv<bf16_t, 256>(a, masked, store_ds, a.alibi != nullptr, grid, st);
     else

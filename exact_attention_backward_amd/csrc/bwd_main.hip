@@ -619,12 +619,15 @@ template <class T, int HD>
 static void launch_bwd_t(const BwdArgs& a, bool masked, int dq_algo, hipStream_t st) {
     const unsigned grid = (unsigned)(a.nblk_n * a.hkv * a.batch);
     if constexpr (sizeof(T) == 2) {
-        // masked: one workgroup per pair of key tiles; the launch's kv-heads only
-        const unsigned kv_grid = (unsigned)((masked ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
+        // masked: one workgroup per pair of key tiles on grids larger than the
+        // GPU; the launch's kv-heads only
+        BwdArgs b = a;
+        b.pair_tiles = masked && (long long)a.nblk_n * a.hkv_n * a.batch > kComputeUnits;
+        const unsigned kv_grid = (unsigned)((b.pair_tiles ? (a.nblk_n + 1) / 2 : a.nblk_n) * a.hkv_n * a.batch);
         static_assert(KvCfg<HD>::BM == BwdCfg<T, HD, false>::BM, "one query tiling");
         static_assert(KvCfg<HD>::BM % kDsRows == 0, "query tiles hold whole dS blocks");
         if (dq_algo == ATTN_DQ_SEPARATE || dq_algo == ATTN_DQ_STORED_DS) {
-            launch_kv<T, HD>(a, masked, dq_algo == ATTN_DQ_STORED_DS, a.alibi != nullptr, kv_grid, st);
+            launch_kv<T, HD>(b, masked, dq_algo == ATTN_DQ_STORED_DS, a.alibi != nullptr, kv_grid, st);
             return;
         }
     }

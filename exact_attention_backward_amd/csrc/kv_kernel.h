@@ -853,7 +853,8 @@ __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a
     // linearly with n, so workgroup p takes the tiles p and (last - p), which
     // together always cost about the same (under a window alone the pairs
     // cost about the same anyway).
-    const int per_group = MASKED ? (a.nblk_n + 1) / 2 : a.nblk_n;
+    const bool pair = MASKED && a.pair_tiles;
+    const int per_group = pair ? (a.nblk_n + 1) / 2 : a.nblk_n;
     int grp, p;
     {
         const int groups = a.hkv_n * a.batch;
@@ -871,9 +872,9 @@ __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (MASKED) {
         const int nk = (si.len_k + KROUND * KBN - 1) / (KROUND * KBN) * KROUND;   // this sequence's key tiles
-        const int n2 = nk - 1 - p;
+        const int n2 = pair ? nk - 1 - p : p;
         // one call site in a loop: a single copy of the (large) tile body
-        const int cnt = (p <= n2) + (n2 > p);
+        const int cnt = pair ? (p <= n2) + (n2 > p) : (p < nk ? 1 : 0);
         for (int k = 0; k < cnt; ++k) {
             if (k) __syncthreads();   // the first tile's LDS ring and P slots are free again
             kv_tile<T, HD, MASKED, STORE_DS, ALIBI, BIAS, DROP>(a, b, hkv, k == 0 && p <= n2 ? p : n2, si, smem);

@@ -144,7 +144,15 @@ struct BwdArgs {
     // kv-heads: the launch's grid covers these groups; the stored-dS region
     // starts at q-head hkv0 * Hq / Hkv)
     int hkv0, hkv_n;
+    // masked launches of the dK/dV and dQ kernels: 1 = a workgroup takes two
+    // tiles of complementary cost (p and last - p), 0 = one tile each (set
+    // by each launcher: pairs only when single tiles would outnumber the
+    // compute units, since on a small grid a pair doubles the longest
+    // workgroup's work)
+    int pair_tiles;
 };
+
+constexpr int kComputeUnits = 256;   // of an MI355X
 
 // dS blocks of the stored-dS mode: 32 query rows x 128 keys of bf16 or fp16 (8 KiB),
 // in the register order of the key-stationary kernel's MFMA operands: 16-byte
