@@ -465,14 +465,12 @@ __global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void bwd_dq_ke
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     if (MASKED) {
         const int nq = (si.len_q + DqCfg<T, HD>::BQ - 1) / DqCfg<T, HD>::BQ;   // this sequence's query tiles
-        // paired: the longer tile m2 first, then p; one call site in a loop
-        // (a single copy of the tile body)
-        const int m2 = pair ? nq - 1 - p : p;
-        const int cnt = m2 > p ? 2 : (p < nq && p == m2 ? 1 : 0);
-        for (int k = 0; k < cnt; ++k) {
-            if (k) __syncthreads();   // the first tile's LDS ring is free again
-            dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(k == 0 ? m2 : p, a, b, hq, hkv, si, smem);
+        const int m2 = pair ? nq - 1 - p : p;   // unpaired: tile p alone
+        if (m2 > p) {
+            dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(m2, a, b, hq, hkv, si, smem);   // the longer tile first
+            __syncthreads();   // its LDS ring is free again
         }
+        if (p < nq && p <= m2) dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     } else {
         dq_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     }

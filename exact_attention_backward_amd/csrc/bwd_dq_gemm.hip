@@ -321,14 +321,14 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     const SeqInfo si = seq_info(b, a.seqlen_q, a.seqlen_k, a.total_q, a.total_k, a.cu_q, a.cu_k, a.used_q, a.used_k);
     const int nblk_q_seq = (si.len_q + BQ - 1) / BQ;   // this sequence's query tiles
     if (MASKED) {
-        // paired: the longer tile m2 first, then its partner p (once the
-        // first tile's LDS stages are no longer read); one call site in a loop
+        // the longer tile first, then its partner (once the first tile's LDS
+        // stages are no longer read); unpaired: tile p alone
         const int m2 = pair ? nblk_q_seq - 1 - p : p;
-        const int cnt = m2 > p ? 2 : (p < nblk_q_seq && p == m2 ? 1 : 0);
-        for (int k = 0; k < cnt; ++k) {
-            if (k) __syncthreads();
-            gemm_tile<T, HD, MASKED>(k == 0 ? m2 : p, a, b, hq, hkv, si, smem);
+        if (m2 > p) {
+            gemm_tile<T, HD, MASKED>(m2, a, b, hq, hkv, si, smem);
+            __syncthreads();
         }
+        if (p < nblk_q_seq && p <= m2) gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     } else {
         gemm_tile<T, HD, MASKED>(p, a, b, hq, hkv, si, smem);
     }
