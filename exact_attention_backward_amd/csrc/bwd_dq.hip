@@ -441,7 +441,8 @@ __global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void bwd_dq_ke
     // ---- which query tiles: all query tiles of all q-heads of one (sequence,
     // kv-head) run on one XCD, so their K/V reads share an L2.  Under a causal
     // mask the keys a query tile sees grow linearly with its index, so
-    // workgroup p takes the tiles p and (last - p) (also under a window).
+    // workgroup p takes the tiles p and (last - p) (also under a window), on
+    // grids larger than the GPU (pair_tiles); else each takes one tile.
     const int G = a.hq / a.hkv;
     const bool pair = MASKED && a.pair_tiles;
     const int n_pair = pair ? (a.nblk_m + 1) / 2 : a.nblk_m;

@@ -297,8 +297,9 @@ __global__ __launch_bounds__(kGThreads, 1) void bwd_dq_gemm_kernel(BwdArgs a) {
     // kv-head) on one XCD, so their K reads share an L2
     const int G = a.hq / a.hkv;
     const int nblk_q = (a.seqlen_q + BQ - 1) / BQ;
-    // masked: workgroup p takes query tiles p and nblk_q - 1 - p, whose key
-    // ranges add up to the same length for every p (balanced work)
+    // masked, on grids larger than the GPU (pair_tiles): workgroup p takes
+    // query tiles p and nblk_q - 1 - p, whose key ranges add up to the same
+    // length for every p (balanced work); else one tile each
     const bool pair = MASKED && a.pair_tiles;
     const int n_pair = pair ? (nblk_q + 1) / 2 : nblk_q;
     const int per_group = n_pair * G;

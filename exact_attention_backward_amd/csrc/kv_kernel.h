@@ -850,9 +850,10 @@ __global__ __launch_bounds__(KvCfg<HD>::NW * 64, 1) void bwd_kv_kernel(BwdArgs a
     constexpr int KROUND = STORE_DS ? KvCfg<HD>::KPB : 1;
     // ---- key tiles: all those of one (sequence, kv-head) on one XCD.  Under
     // a causal mask key tile n is seen by a number of query tiles that falls
-    // linearly with n, so workgroup p takes the tiles p and (last - p), which
-    // together always cost about the same (under a window alone the pairs
-    // cost about the same anyway).
+    // linearly with n, so on grids larger than the GPU (pair_tiles)
+    // workgroup p takes the tiles p and (last - p), which together always
+    // cost about the same (under a window alone the pairs cost about the
+    // same anyway); on smaller ones each workgroup takes one tile.
     const bool pair = MASKED && a.pair_tiles;
     const int per_group = pair ? (a.nblk_n + 1) / 2 : a.nblk_n;
     int grp, p;
