@@ -508,9 +508,13 @@ int bwd_dq_block_m() { return 32 * kWaves; }
 // P (rounded to the operand type) straight from the S^T registers.  The O^T
 // accumulator's column is again this lane's query, so the rescale by the
 // change of the row maximum is one scalar per lane.  Not part of the
-// backward; it produces O and LSE for it.
+// backward; it produces O and LSE for it.  BIAS: an elementwise bias added to
+// the scaled logits (and ALiBi too when slopes are given); DROP (with BIAS):
+// dropout of P with the backward's Philox stream, so O sums the kept
+// probabilities times 1 / (1 - p) while the row sum and LSE take every
+// visible key.
 // ---------------------------------------------------------------------------
-template <class T, int HD, bool MASKED, bool ALIBI>
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
 __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq, int hkv, const SeqInfo& si,
                                          char* smem) {
     using C = DqCfg<T, HD>;
@@ -562,9 +566,24 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
         for (int c = 0; c < C::NC; ++c) qreg[c] = dq_load_global<T>(qg + 16 * c + 8 * h, row_ok && 16 * c + 8 * h < a.d);
     }
     const float scale2 = a.scale * kLog2e;
-    const float nsl2 = ALIBI ? -a.alibi[hq] * kLog2e : 0.f;
+    const float nsl2 = ALIBI || (BIAS && a.alibi != nullptr) ? -a.alibi[hq] * kLog2e : 0.f;
     const int lim = row_ok ? (MASKED ? min(si.len_k, i + off + a.win_hi + 1) : si.len_k) : 0;
     const int lim_lo = MASKED ? i + off - a.win_lo : 0;
+    // elementwise bias: this lane's row, or null (no bias, or a row past the
+    // sequence).  Each element is used once, by one lane, so it is read
+    // straight from memory: 4 keys per load where the row's 4-key groups are
+    // 8-byte aligned, else one element at a time; keys past the sequence read
+    // as zero.
+    const uint16_t* brow = nullptr;
+    bool bvec = false;
+    if constexpr (BIAS) {
+        if (a.bias != nullptr && row_ok) {
+            brow = reinterpret_cast<const uint16_t*>(a.bias) + (long long)b * a.sbias.b + (long long)hq * a.sbias.h +
+                   (long long)i * a.sbias.r;
+            bvec = (reinterpret_cast<uintptr_t>(a.bias) & 7) == 0 && (a.sbias.b & 3) == 0 && (a.sbias.h & 3) == 0 &&
+                   (a.sbias.r & 3) == 0;
+        }
+    }
 
     f32x16 o[C::NDB];   // O^T: rows = head-dim columns, column = this lane's query
 #pragma unroll
@@ -586,6 +605,43 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
         const bool edge = !((j0 + BN <= si.len_k) && (i0 + BQ <= si.len_q) &&
                             (!MASKED || (j0 + BN - 1 <= i0 + off + a.win_hi && j0 >= i0 + BQ - 1 + off - a.win_lo)));
 
+        // this tile's bias: keys 32 jb + 8 q4 + 4h .. + 3 of this lane's row (q = 4 jb + q4)
+        u32x2 bia[BIAS ? C::NJB * 4 : 1];
+        if constexpr (BIAS) {
+#pragma unroll
+            for (int q = 0; q < C::NJB * 4; ++q) {
+                const int jc = j0 + 8 * q + 4 * h;
+                u32x2 wv = {0u, 0u};
+                if (brow != nullptr) {
+                    if (bvec && jc + 4 <= si.len_k) {
+                        wv = *reinterpret_cast<const u32x2*>(brow + jc);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (jc + e < si.len_k) wv[e >> 1] |= (unsigned)brow[jc + e] << (16 * (e & 1));
+                    }
+                }
+                bia[q] = wv;
+            }
+        }
+        // dropout: lane c of each group of four rows draws block 4 jb + c of
+        // the tile (keys j0 + 8 q + 4h .. + 3) and the group trades words so
+        // that each lane holds its own row's word of every block
+        unsigned dword_[DROP ? C::NJB * 4 : 1];
+        if constexpr (DROP) {
+            const int c = lane & 3;
+#pragma unroll
+            for (int jb = 0; jb < C::NJB; ++jb) {
+                const int q = 4 * jb + c;
+                const u32x4 wd = quad_word_transpose(
+                    drop_block((unsigned)((j0 + 8 * q + 4 * h) >> 2), (unsigned)(i >> 2), (unsigned)(b * a.hq + hq),
+                               a.drop.off, a.drop.k0, a.drop.k1),
+                    c);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) dword_[4 * jb + q4] = wd[q4];
+            }
+        }
+
         f32x16 st[C::NJB];
 #pragma unroll
         for (int jb = 0; jb < C::NJB; ++jb) {
@@ -606,8 +662,9 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     float x = st[jb][v] * scale2;
-                    if constexpr (ALIBI)
+                    if constexpr (ALIBI || BIAS)
                         x = fmaf(nsl2, fabsf(fdist + (float)(32 * jb + 8 * (v >> 2) + (v & 3))), x);
+                    if constexpr (BIAS) x = fmaf(b16_elem<T>(bia[4 * jb + (v >> 2)], v & 3), kLog2e, x);
                     if constexpr (decltype(masked)::value) {
                         const int j = j0 + 32 * jb + acc_row(v, h);
                         x = (j < lim && j >= lim_lo) ? x : -INFINITY;
@@ -643,8 +700,11 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float p = __builtin_amdgcn_exp2f(st[jb][v] - mref);
-                lsum += p;
-                st[jb][v] = p;
+                lsum += p;   // the row sum (and LSE) over every visible key
+                if constexpr (DROP)
+                    st[jb][v] = drop_keep(dword_[4 * jb + (v >> 2)], v & 3, a.drop.thr) ? p : 0.f;
+                else
+                    st[jb][v] = p;
             }
         }
         mrow = mnew;
@@ -669,7 +729,7 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
     // ---- epilogue: O = O^T / l (this lane's query row), LSE = (m + log2 l) ln 2
     const float ltot = lsum + __shfl_xor(lsum, 32);
     if (!row_ok) return;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float inv = ltot > 0.f ? (DROP ? a.drop.rp : 1.f) / ltot : 0.f;
     T* orow = reinterpret_cast<T*>(a.o) + seq_off(a.so, varlen, b, si.q0) + (long long)hq * a.so.h +
               (long long)i * a.so.r;
 #pragma unroll
@@ -686,7 +746,7 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
     }
 }
 
-template <class T, int HD, bool MASKED, bool ALIBI>
+template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
     // all query tiles of all q-heads of one (sequence, kv-head) on one XCD;
@@ -717,12 +777,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
         const int nq = (si.len_q + BQ - 1) / BQ;
         const int m2 = nq - 1 - p;
         if (m2 > p) {
-            fwd_tile<T, HD, MASKED, ALIBI>(m2, a, b, hq, hkv, si, smem);
+            fwd_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(m2, a, b, hq, hkv, si, smem);
             __syncthreads();
         }
-        if (p < nq && p <= m2) fwd_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+        if (p < nq && p <= m2) fwd_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     } else {
-        fwd_tile<T, HD, MASKED, ALIBI>(p, a, b, hq, hkv, si, smem);
+        fwd_tile<T, HD, MASKED, ALIBI, BIAS, DROP>(p, a, b, hq, hkv, si, smem);
     }
 }
 
@@ -731,13 +791,18 @@ static void launch_fwd_mfma_t(const FwdArgs& a, bool masked, hipStream_t st) {
     constexpr int BQ = DqCfg<T, HD>::BQ;
     const int nblk_m = (a.seqlen_q + BQ - 1) / BQ;
     const unsigned grid = (unsigned)((masked ? (nblk_m + 1) / 2 : nblk_m) * a.hq * a.batch);
-    const bool alibi = a.alibi != nullptr;
+    // variants: plain, ALiBi, bias (+ ALiBi), dropout (+ bias, ALiBi)
+    const bool alibi = a.alibi != nullptr, bias = a.bias != nullptr, drop = a.drop.on;
     if (masked) {
-        if (alibi) fwd_mfma_kernel<T, HD, true, true><<<grid, kThreads, 0, st>>>(a);
-        else fwd_mfma_kernel<T, HD, true, false><<<grid, kThreads, 0, st>>>(a);
+        if (drop) fwd_mfma_kernel<T, HD, true, false, true, true><<<grid, kThreads, 0, st>>>(a);
+        else if (bias) fwd_mfma_kernel<T, HD, true, false, true, false><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) fwd_mfma_kernel<T, HD, true, true, false, false><<<grid, kThreads, 0, st>>>(a);
+        else fwd_mfma_kernel<T, HD, true, false, false, false><<<grid, kThreads, 0, st>>>(a);
     } else {
-        if (alibi) fwd_mfma_kernel<T, HD, false, true><<<grid, kThreads, 0, st>>>(a);
-        else fwd_mfma_kernel<T, HD, false, false><<<grid, kThreads, 0, st>>>(a);
+        if (drop) fwd_mfma_kernel<T, HD, false, false, true, true><<<grid, kThreads, 0, st>>>(a);
+        else if (bias) fwd_mfma_kernel<T, HD, false, false, true, false><<<grid, kThreads, 0, st>>>(a);
+        else if (alibi) fwd_mfma_kernel<T, HD, false, true, false, false><<<grid, kThreads, 0, st>>>(a);
+        else fwd_mfma_kernel<T, HD, false, false, false, false><<<grid, kThreads, 0, st>>>(a);
     }
 }
 

@@ -20,7 +20,7 @@
  * or two: attn_bwd_preprocess, then attn_bwd_full (dK, dV and dQ, the latter
  * written in the I/O type by the dQ pass itself where that pass owns whole
  * rows).
- * attn_fwd is a plain forward used only to produce O and LSE inputs.
+ * attn_fwd is a forward (O and LSE) that produces the backward's inputs.
  *
  * Conventions shared by every entry point
  * ---------------------------------------

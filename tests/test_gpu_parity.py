@@ -586,6 +586,41 @@ def test_bias_and_dbias_match_oracle(case, full, algo):
     assert np.all(gdb[~inside] == sentinel)
 
 
+# (dtype, Hq, Hkv, Sq, Sk, D, causal, element offset of the bias view, padded row length)
+FWD_BIAS_LAYOUTS = [
+    ("bf16", 4, 2, 200, 261, 128, True, 1, 265),    # odd base offset and row stride
+    ("f16", 2, 2, 150, 77, 64, False, 0, 80),       # aligned rows, ragged 4-key tail
+    ("bf16", 2, 1, 130, 130, 64, True, 2, 134),     # 4-byte aligned base, stride 2 mod 4
+    ("f16", 3, 3, 97, 300, 128, False, 3, 303),
+]
+
+
+@pytest.mark.parametrize("case", FWD_BIAS_LAYOUTS, ids=lambda c: f"{c[0]}-s{c[3]}x{c[4]}-d{c[5]}-off{c[7]}-row{c[8]}")
+def test_bias_forward_any_row_layout_matches_oracle(case):
+    """The forward reads a bias whose rows start anywhere (base and row
+    stride not multiples of 4 elements) one element at a time and aligned
+    rows four keys per load; no element past a row's keys is read (the
+    padding holds NaN, which would reach O)."""
+    import datagen
+    dt, hq, hkv, sq, sk, d, causal, off, row = case
+    p = small_problem(dt, 2, hq, hkv, sq, sk, d, causal, 4100 + off)
+    r = Run(p, oracle_o_lse=False)
+    bias_np = datagen.draw_bias(p, 97, batch=2)
+    big = torch.full((2, hq, sq, row), float("nan"), dtype=to_dev(bias_np[:1, :1, :1], dt).dtype, device="cuda")
+    big[..., off:off + sk] = to_dev(bias_np, dt)
+    bias_dev = big[..., off:off + sk]
+    print(f"forward bias layout {case}", flush=True)
+    d_ = r.dev
+    o, lse = api.forward(d_["q"], d_["k"], d_["v"], p.scale, p.causal, bias=bias_dev)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.forward(r.x["q"], r.x["k"], r.x["v"], p.scale, p.causal, bias=bias_np)
+    assert_close("O", to_host(o), ro, p.dtype)
+    fin = np.isfinite(rlse)
+    g = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert np.max(np.abs(g[fin] - rlse[fin]), initial=0) <= 2e-4
+
+
 SEQUSED_CASES = [
     # (dtype, Hq, Hkv, D, causal, lengths_q, lengths_k, used_q, used_k)
     ("bf16", 4, 2, 128, True, (70, 300, 129, 1), (90, 260, 129, 40), (70, 211, 0, 1), (33, 260, 100, 40)),
