@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--api", default="full", choices=["full", "three"],
                     help="full: attn_bwd_preprocess + attn_bwd_full (default); three: attn_bwd_preprocess + "
                          "attn_bwd + attn_bwd_dq_postprocess")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one HIP graph that holds a step's launches (for small "
+                         "problems, where the host's launch cost per step exceeds the kernels'); the per-launch "
+                         "HIP-event timing behind the roofline still runs on its own eager steps first")
     ap.add_argument("--settle", type=float, default=0.5, metavar="SECONDS",
                     help="untimed steps before the warm-up, until this much time has passed: after idle the GPU "
                          "takes about 20 calls (~25 ms) to reach its steady clock")
@@ -271,6 +275,29 @@ def main():
         e[3].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    eager_ms_per_step = wall * 1e3 / args.steps
+
+    if args.graph:
+        # one step (the same calls as run above) captured once, then replayed:
+        # the host issues one graph launch per step instead of every kernel's
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):   # a step on a non-default stream before the capture
+            run(q, k, v, o, do, lse, dq, dk, dv)
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run(q, k, v, o, do, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     main_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
@@ -304,6 +331,8 @@ def main():
         "warmup": args.warmup,
         "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
+        "launch": "hip_graph" if args.graph else "eager",
+        "ms_per_step_eager": round(eager_ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
