@@ -351,9 +351,8 @@ int attn_fwd(const attn_shape_t* s, const void* q, const void* k, const void* v,
     a.bias = s->bias;
     a.sbias = to_kernel(s->bias_strides);
     a.drop = dropout_args(s);
-    // the MFMA forward for the 16-bit types up to head dim 128; fp32 and
-    // wider heads take the plain one
-    if (s->dtype != ATTN_DTYPE_F32 && padded_hd(s) <= 128)
+    // the MFMA forward for the 16-bit types; fp32 takes the plain one
+    if (s->dtype != ATTN_DTYPE_F32)
         launch_fwd_mfma(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));
     else
         launch_fwd(a, s->dtype, padded_hd(s), masked(s), reinterpret_cast<hipStream_t>(stream));

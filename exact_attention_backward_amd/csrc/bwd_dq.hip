@@ -747,7 +747,7 @@ __device__ __forceinline__ void fwd_tile(int m, const FwdArgs& a, int b, int hq,
 }
 
 template <class T, int HD, bool MASKED, bool ALIBI, bool BIAS, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (DqCfg<T, HD>::WG_PER_CU)) void fwd_mfma_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[DqCfg<T, HD>::LDS_BYTES];
     // all query tiles of all q-heads of one (sequence, kv-head) on one XCD;
     // masked: workgroup p takes the tiles p and (last - p)
@@ -809,10 +809,12 @@ static void launch_fwd_mfma_t(const FwdArgs& a, bool masked, hipStream_t st) {
 void launch_fwd_mfma(const FwdArgs& a, int dtype, int hd, bool masked, hipStream_t st) {
     if (dtype == ATTN_DTYPE_BF16) {
         if (hd == 64) launch_fwd_mfma_t<bf16_t, 64>(a, masked, st);
-        else launch_fwd_mfma_t<bf16_t, 128>(a, masked, st);
+        else if (hd == 128) launch_fwd_mfma_t<bf16_t, 128>(a, masked, st);
+        else launch_fwd_mfma_t<bf16_t, 256>(a, masked, st);
     } else {
         if (hd == 64) launch_fwd_mfma_t<f16_t, 64>(a, masked, st);
-        else launch_fwd_mfma_t<f16_t, 128>(a, masked, st);
+        else if (hd == 128) launch_fwd_mfma_t<f16_t, 128>(a, masked, st);
+        else launch_fwd_mfma_t<f16_t, 256>(a, masked, st);
     }
 }
 
