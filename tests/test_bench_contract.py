@@ -29,10 +29,14 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_only_from_counters_of_the_current_sources():
-    # committed counters of the headline workload, taken on the current kernel sources
+    """The committed counters' figure while the kernel sources hash as when
+    they were taken, else none."""
+    current = "+".join(bench.source_hash(p) for p in bench.MAIN_SRCS)
     for algo in ("stored_ds", "separate"):
-        t = bench.traffic_entry(algo, "c3", "full")
-        assert isinstance(t, int) and t > 0
+        path = bench.TRAFFIC_FILE.format("c3", algo)
+        t = json.load(open(path))
+        expected = t["hbm_bytes_per_launch"] if t["kernel_source_sha256_16"] == current else None
+        assert bench.traffic_entry(algo, "c3", "full") == expected
     # none for the three-call path, a workload or mode without counters
     assert bench.traffic_entry("stored_ds", "c3", "three") is None
     assert bench.traffic_entry("atomic", "c3", "full") is None
