@@ -105,3 +105,109 @@ def test_combined_backward_matches_oracle(case, algo):
         inside[bb, :, :lq[bb], :lk[bb]] = True
     assert_close("dBias", gdb[inside], res[3][inside], p.dtype)
     assert np.all(gdb[~inside] == 9.0)
+
+
+# (dtype, Hq, Hkv, D, causal, lengths_q, lengths_k, used_q, used_k, dropout p or 0)
+SEQUSED_COMBINED = [
+    ("bf16", 4, 2, 128, True, (70, 300, 129), (90, 260, 129), (70, 211, 100), (33, 260, 64), 0.2),
+    ("f16", 2, 2, 64, False, (200, 65), (150, 300), (199, 1), (150, 129), 0.0),
+]
+
+
+@pytest.mark.parametrize("algo", ["separate", "stored_ds", "atomic"])
+@pytest.mark.parametrize("case", SEQUSED_COMBINED,
+                         ids=lambda c: f"{c[0]}-h{c[1]}/{c[2]}-d{c[3]}-{'causal' if c[4] else 'full'}-p{c[9]}")
+def test_combined_with_used_lengths(case, algo):
+    """Used lengths with ALiBi, bias/dBias and dropout: used rows and keys
+    match the oracle; rows past a used length, and dBias outside each
+    sequence's used block, keep what the buffers held."""
+    import math
+    from _harness import round_like
+    dt, hq, hkv, d, causal, lq, lk, uq, uk, pd = case
+    p = datagen.Problem(dt, len(lq), hq, hkv, max(lq), max(lk), d, causal, 1 / math.sqrt(d), 91,
+                        lengths_q=tuple(lq), lengths_k=tuple(lk), name="seqused_combined")
+    x = datagen.draw(p)
+    cq, ck = p.cu_seqlens()
+    uq_np, uk_np = np.array(uq, np.int32), np.array(uk, np.int32)
+    dev = {n: to_dev(v, dt) for n, v in x.items()}
+    cu = dict(cu_seqlens_q=torch.from_numpy(cq).cuda(), cu_seqlens_k=torch.from_numpy(ck).cuda(),
+              max_seqlen_q=p.seqlen_q, max_seqlen_k=p.seqlen_k,
+              seqused_q=torch.from_numpy(uq_np).cuda(), seqused_k=torch.from_numpy(uk_np).cuda())
+    nb = len(lq)
+    used_q = np.zeros(cq[-1], bool)
+    used_k = np.zeros(ck[-1], bool)
+    for b in range(nb):
+        used_q[cq[b]:cq[b] + uq[b]] = True
+        used_k[ck[b]:ck[b] + uk[b]] = True
+    slopes = _slopes(hq)
+    slopes_dev = torch.from_numpy(slopes).cuda()
+    bias_np = datagen.draw_bias(p, 61, batch=nb)
+    skp = (p.seqlen_k + 7) // 8 * 8
+    padded = torch.full(bias_np.shape[:3] + (skp,), float("nan"), dtype=dev["q"].dtype, device="cuda")
+    padded[..., :p.seqlen_k] = to_dev(bias_np, dt)
+    bias_dev = padded[..., :p.seqlen_k]
+    drop = (float(np.float32(pd)), 0xBEEF + hq, 3) if pd > 0 else None
+    print(f"combined seqused {case} {algo}", flush=True)
+    feats = dict(alibi_slopes=slopes, bias=bias_np, dropout=drop)
+    ro, rlse = oracle.forward(x["q"], x["k"], x["v"], p.scale, causal, cq, ck, uq_np, uk_np, **feats)
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, causal, alibi_slopes=slopes_dev, bias=bias_dev,
+                         dropout=drop, **cu)
+    torch.cuda.synchronize()
+    assert_close("O", to_host(o)[used_q], ro[used_q], dt)
+    gl = lse.cpu().numpy().astype(np.float64)[:, used_q]
+    fin = np.isfinite(rlse[:, used_q])
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.max(np.abs(gl[fin] - rlse[:, used_q][fin]), initial=0) <= 2e-4
+    # backward from the oracle's O and LSE on the used rows
+    o_in = round_like(np.where(used_q[:, None, None], ro, 0.0), dt)
+    lse_in = np.where(used_q[None, :], rlse, 0.0).astype(np.float32)
+    sentinel = 3.0
+    dbias = torch.full((nb, hq, p.seqlen_q, p.seqlen_k), sentinel, dtype=dev["q"].dtype, device="cuda")
+    plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, causal, False, dq_algo=algo, alibi_slopes=slopes_dev,
+                            bias=bias_dev, dbias=dbias, dropout=drop, **cu)
+    dq = torch.full_like(dev["q"], sentinel)
+    dk = torch.full_like(dev["k"], sentinel)
+    dv = torch.full_like(dev["v"], sentinel)
+    plan.run_full(dev["q"], dev["k"], dev["v"], to_dev(o_in, dt), dev["do"], torch.from_numpy(lse_in).cuda(),
+                  dq, dk, dv)
+    torch.cuda.synchronize()
+    res = oracle.backward(x["q"], x["k"], x["v"], o_in, x["do"], lse_in.astype(np.float64), p.scale, causal, cq, ck,
+                          uq_np, uk_np, want_dbias=True, **feats)
+    for n, g, ref, used in (("dQ", dq, res[0], used_q), ("dK", dk, res[1], used_k), ("dV", dv, res[2], used_k)):
+        gh = to_host(g)
+        assert_close(n, gh[used], ref[used], dt)
+        assert np.all(gh[~used] == sentinel), f"{n}: a row past the used length was written"
+    gdb = to_host(dbias)
+    inside = np.zeros(gdb.shape, bool)
+    for bb in range(nb):
+        inside[bb, :, :uq[bb], :uk[bb]] = True
+    assert_close("dBias", gdb[inside], res[3][inside], dt)
+    assert np.all(gdb[~inside] == sentinel)
+
+
+@pytest.mark.parametrize("case", [COMBINED_CASES[0], COMBINED_CASES[2]], ids=_id)
+def test_ordered_mode_reproducible_with_features(case):
+    """The ordered (deterministic) mode with ALiBi, bias/dBias and dropout:
+    two runs, with other GPU work between them, agree bit for bit."""
+    p, r, nb, bias_np, bias_dev, drop = _setup(case)
+    if drop is None:
+        drop = (0.15, 4242, 1)
+    print(f"ordered reproducible {_id(case)}", flush=True)
+    cq, ck = r.cu_np
+    ro, rlse = oracle.forward(r.x["q"], r.x["k"], r.x["v"], p.scale, p.causal, cq, ck, window=r.window,
+                              alibi_slopes=r.alibi, bias=bias_np, dropout=drop)
+    r.set_o_lse(ro, rlse)
+    d, kw = r.dev, r.kw()
+    outs = []
+    for rep in range(2):
+        dbias = torch.zeros((nb, p.heads_q, p.seqlen_q, p.seqlen_k), dtype=d["q"].dtype, device="cuda")
+        plan = api.BackwardPlan(d["q"], d["k"], p.scale, p.causal, True, dq_algo="atomic", window=r.window,
+                                alibi_slopes=r.slopes, bias=bias_dev, dbias=dbias, dropout=drop, **kw)
+        g = [torch.empty_like(d[n]) for n in ("q", "k", "v")]
+        plan.run_full(d["q"], d["k"], d["v"], d["o"], d["do"], d["lse"], *g)
+        torch.randn(1 << 20, device="cuda").mul_(2.0)   # other work between the runs
+        torch.cuda.synchronize()
+        assert plan.error_flag() == 0
+        outs.append([t.clone() for t in g] + [dbias])
+    for n, a, b in zip(("dQ", "dK", "dV", "dBias"), outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n

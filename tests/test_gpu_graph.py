@@ -16,9 +16,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("bias", [False, True], ids=["plain", "bias_dbias"])
+@pytest.mark.parametrize("dropout", [False, True], ids=["no_dropout", "dropout"])
 @pytest.mark.parametrize("dq_algo", ["separate", "stored_ds"])
-def test_captured_backward_replays_match_eager(dq_algo, bias):
-    """With bias and dBias the masked-dBias clear also runs on the side stream."""
+def test_captured_backward_replays_match_eager(dq_algo, dropout, bias):
+    """With bias and dBias the clear of dBias's masked elements is captured too;
+    with dropout every replay draws the same keep mask (fixed seed and offset)."""
     p = datagen.Problem("bf16", 2, 4, 2, 300, 300, 64, True, 1 / 8, 17, name="graph")
     x = datagen.draw(p)
     dev = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
@@ -31,11 +33,14 @@ def test_captured_backward_replays_match_eager(dq_algo, bias):
         bpad[..., :p.seqlen_k] = torch.from_numpy(datagen.draw_bias(p, 5)).to(torch.bfloat16).cuda()
         dbias = torch.full_like(bpad, 7.0)[..., :p.seqlen_k]
         kw = dict(bias=bpad[..., :p.seqlen_k], dbias=dbias)
-    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=kw.get("bias"))
+    if dropout:
+        kw["dropout"] = (0.2, 0x1234ABCD, 7)
+    o, lse = api.forward(dev["q"], dev["k"], dev["v"], p.scale, p.causal, bias=kw.get("bias"),
+                         dropout=kw.get("dropout"))
     plan = api.BackwardPlan(dev["q"], dev["k"], p.scale, p.causal, False, dq_algo=dq_algo, **kw)
     outs = [torch.empty_like(dev[n]) for n in ("q", "k", "v")] + ([dbias] if bias else [])
     args = (dev["q"], dev["k"], dev["v"], o, dev["do"], lse)
-    print(f"graph capture {dq_algo} bias={bias}", flush=True)
+    print(f"graph capture {dq_algo} bias={bias} dropout={dropout}", flush=True)
     grads = outs[:3]
     plan.run_full(*args, *grads)   # eager (also creates the side stream before any capture)
     torch.cuda.synchronize()
