@@ -211,3 +211,70 @@ def test_ordered_mode_reproducible_with_features(case):
         outs.append([t.clone() for t in g] + [dbias])
     for n, a, b in zip(("dQ", "dK", "dV", "dBias"), outs[0], outs[1]):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+
+
+# (dtype, B, H, S, D, varlen lengths)
+STRIDED_COMBINED = [
+    ("bf16", 2, 3, 260, 128, None),
+    ("f16", 1, 4, 333, 64, None),
+    ("bf16", 0, 2, 0, 128, (1, 64, 300, 129)),
+]
+
+
+@pytest.mark.parametrize("dq_algo", ["stored_ds", "separate", "ordered"])
+@pytest.mark.parametrize("case", STRIDED_COMBINED,
+                         ids=lambda c: f"{c[0]}-{'lens' + '-'.join(map(str, c[5])) if c[5] else f'b{c[1]}s{c[3]}'}-h{c[2]}-d{c[4]}")
+def test_strided_layouts_with_features_match_contiguous_bitwise(case, dq_algo):
+    """Q, K, V as views of one packed [.., 3, H, D] tensor, dO head-major, O in
+    a row-padded buffer and dQ/dK/dV in a packed gradient tensor, with ALiBi,
+    bias/dBias and dropout: O, LSE, dQ, dK, dV and dBias equal the contiguous
+    run's bit for bit (the ordered mode stands for the atomic one, whose
+    order of additions varies)."""
+    dt, b, h, s_len, d, lens = case
+    p = small_problem(dt, b, h, h, s_len, s_len, d, True, 71, lengths=lens)
+    r = Run(p, oracle_o_lse=False, alibi=_slopes(h))
+    dev, kw = r.dev, r.kw()
+    nb = len(lens) if lens else b
+    bias_np = datagen.draw_bias(p, 29, batch=nb)
+    skp = (p.seqlen_k + 7) // 8 * 8
+    padded = torch.full(bias_np.shape[:3] + (skp,), float("nan"), dtype=dev["q"].dtype, device="cuda")
+    padded[..., :p.seqlen_k] = to_dev(bias_np, dt)
+    bias_dev = padded[..., :p.seqlen_k]
+    drop = (float(np.float32(0.2)), 0xABC, 9)
+    det = dq_algo == "ordered"
+    algo = "atomic" if det else dq_algo
+    feats = dict(alibi_slopes=r.slopes, bias=bias_dev, dropout=drop)
+    print(f"strided combined {case} {dq_algo}", flush=True)
+
+    def backward(q, k, v, o, do, lse, grads):
+        dbias = torch.full((nb, h, p.seqlen_q, p.seqlen_k), 5.0, dtype=dev["q"].dtype, device="cuda")
+        plan = api.BackwardPlan(q, k, p.scale, True, det, dq_algo=algo, dbias=dbias, **feats, **kw)
+        plan.run_full(q, k, v, o, do, lse, *grads)
+        torch.cuda.synchronize()
+        if det:
+            assert plan.error_flag() == 0
+        return dbias
+
+    o_c, lse_c = api.forward(dev["q"], dev["k"], dev["v"], p.scale, True, **feats, **kw)
+    ref = [torch.empty_like(dev[n]) for n in ("q", "k", "v")]
+    dbias_c = backward(dev["q"], dev["k"], dev["v"], o_c, dev["do"], lse_c, ref)
+    lead = dev["q"].shape[:-2]
+    nl = len(lead)
+    qkv = torch.empty(*lead, 3, h, d, dtype=dev["q"].dtype, device="cuda")
+    for slot, n in enumerate(("q", "k", "v")):
+        qkv.select(nl, slot).copy_(dev[n])
+    q, k, v = (qkv.select(nl, slot) for slot in range(3))
+    do = dev["do"].movedim(nl, 0).contiguous().movedim(0, nl)
+    o_pad = torch.full((*lead, h, d + 8), -3.0, dtype=dev["q"].dtype, device="cuda")
+    o = o_pad[..., :d]
+    lse = torch.empty_like(lse_c)
+    api.forward(q, k, v, p.scale, True, out=(o, lse), **feats, **kw)
+    dqkv = torch.full((*lead, 3, h, d), -3.0, dtype=dev["q"].dtype, device="cuda")
+    grads = [dqkv.select(nl, slot) for slot in range(3)]
+    dbias_s = backward(q, k, v, o, do, lse, grads)
+    assert torch.equal(o.contiguous().view(torch.int16), o_c.view(torch.int16))
+    assert torch.equal(lse, lse_c)
+    assert bool((o_pad[..., d:] == -3.0).all())
+    for n, g, c in zip(("dQ", "dK", "dV"), grads, ref):
+        assert torch.equal(g.contiguous().view(torch.int16), c.view(torch.int16)), n
+    assert torch.equal(dbias_s.view(torch.int16), dbias_c.view(torch.int16))
